@@ -1,0 +1,333 @@
+/*
+ * Kamera reuse operator: plain fp64 CPU oracle.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark load this library. The GPU library never links, includes
+ * or calls it, and it shares no source with the GPU library.
+ *
+ * Sources cited below (web summaries of two papers):
+ *   [K]  "Kamera: KV Cache Multimodal Unificado e Invariante a Posicao para Reuso
+ *        sem Treinamento", gist.science/pt/paper/2606.23581, and its Korean twin
+ *        at gist.science/ko/paper/2606.23581, which agrees on every point used here.
+ *   [N]  "Modelos Tomam Notas no Prefill: O Cache KV Pode Ser Editavel e
+ *        Componivel", gist.science/pt/paper/2606.17107.
+ *
+ * What the oracle computes, per layer l, channel c, chunk j, token t of chunk j,
+ * head h and dim d of that head (feature f = h*D + d):
+ *
+ *     out = round( [R(delta_j) x](h, d)  +  sum_{k<m} U[l][t][k] * V[l][j][f][k] )
+ *
+ *   - [K §2, reuse equation]: the reused KV is the relocated canonical KV plus a
+ *     rank-m patch U_m V_m^T, with U_m indexed by token and V_m by feature.
+ *   - [K §2, "Relocacao"]: keys are turned by the RoPE phase shift of the new
+ *     position; it is an exact rotation, not a network pass.
+ *   - [K §2, architecture list]: MHA/GQA rotate the whole key; MLA rotates only
+ *     the 64-dim decoupled k_rope and keeps c_KV as it is; the patch goes on
+ *     both channels.
+ *   - [K §3, sliding-window survival] and [N §3B, composable KV]: with no patch,
+ *     only the keys move and the values are carried over unchanged.
+ *
+ * Readings taken where the pages are silent (the pages give no RoPE formula):
+ *   - NeoX half-split pairing: dim i pairs with dim i + r/2 (i < r/2), where r
+ *     is the number of rotated dims of a head; dims >= r are not rotated.
+ *   - Pair frequency omega_i = theta^(-2i/r); angle delta * omega_i; the pair
+ *     (a, b) turns to (a cos - b sin, b cos + a sin).  Positive delta moves the
+ *     chunk to a later position.
+ *   - The patch is added after the rotation and is not itself rotated.
+ *   - R(0) is the identity matrix: a chunk with delta 0 is not rotated at all.
+ *   - The result is rounded once, from fp64, to the storage type (bf16 or fp32)
+ *     with round-to-nearest-even.
+ *   - With no patch (m = 0), elements the rotation does not move (channels with
+ *     r = 0, dims >= r, chunks with delta = 0) keep their exact bits.
+ *
+ * Everything is plain loops over the definition; rows are independent, so an
+ * OpenMP loop spreads rows over host threads without changing any arithmetic.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_BF16 0
+#define ORC_F32 1
+
+/* ---------------------------------------------------------------- numbers */
+
+/* bf16 bits -> exact double value. */
+double orc_bf16_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* double -> bf16 bits, round to nearest, ties to even, straight from the double
+ * (no detour through fp32, which would round twice).  bf16 keeps 8 significant
+ * bits and the fp32 exponent range: normal numbers from 2^-126, subnormal
+ * quantum 2^-133, largest finite (2 - 2^-7) * 2^127.  Reading [K §3,
+ * production deployment]: the rebuilt KV is compared at bf16 rounding. */
+uint16_t orc_bf16_from_double(double y) {
+    uint16_t sign = signbit(y) ? 0x8000u : 0u;
+    if (isnan(y)) return (uint16_t)(sign | 0x7FC0u);
+    if (isinf(y)) return (uint16_t)(sign | 0x7F80u);
+    double a = fabs(y);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                 /* a = f * 2^e, 0.5 <= f < 1 */
+    int qexp = e - 8;             /* weight of the last kept bit */
+    if (qexp < -133) qexp = -133; /* subnormal range: fixed quantum */
+    double q = nearbyint(ldexp(a, -qexp)); /* default mode: ties to even */
+    double r = ldexp(q, qexp);
+    if (r >= 0x1p128) return (uint16_t)(sign | 0x7F80u);
+    float rf = (float)r;          /* exact: r has <= 8 significant bits */
+    uint32_t bits;
+    memcpy(&bits, &rf, sizeof bits);
+    return (uint16_t)(sign | (bits >> 16));
+}
+
+void orc_round_bf16_array(const double* y, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_from_double(y[i]);
+}
+
+static double load_elem(int dtype, const void* base, int64_t i) {
+    if (dtype == ORC_BF16) return orc_bf16_to_double(((const uint16_t*)base)[i]);
+    return (double)((const float*)base)[i];
+}
+
+static void store_elem(int dtype, void* base, int64_t i, double y) {
+    if (dtype == ORC_BF16) ((uint16_t*)base)[i] = orc_bf16_from_double(y);
+    else ((float*)base)[i] = (float)y; /* C conversion: round to nearest even */
+}
+
+static void copy_elem(int dtype, void* dst, int64_t i, const void* src, int64_t k) {
+    if (dtype == ORC_BF16) ((uint16_t*)dst)[i] = ((const uint16_t*)src)[k];
+    else memcpy((float*)dst + i, (const float*)src + k, sizeof(float));
+}
+
+/* ------------------------------------------------------------- relocation */
+
+/* Angular frequency of rotary pair i in a head that rotates r dims:
+ * theta^(-2i/r) (reading: the pages name RoPE but print no formula). */
+double orc_freq(double theta, int r, int i) {
+    return pow(theta, -2.0 * (double)i / (double)r);
+}
+
+/* y = R(delta) x for one head of `dim` values, in fp64 ([K §2, "Relocacao"]).
+ * Dim i < r/2 pairs with dim i + r/2; dims >= r are copied. */
+void orc_rotate_head_f64(const double* x, double* y, int dim, int r,
+                         double theta, int64_t delta) {
+    for (int d = 0; d < dim; ++d) y[d] = x[d];
+    if (delta == 0 || r == 0) return;
+    int half = r / 2;
+    for (int i = 0; i < half; ++i) {
+        double phi = (double)delta * orc_freq(theta, r, i);
+        double cs = cos(phi), sn = sin(phi);
+        double a = x[i], b = x[i + half];
+        y[i] = a * cs - b * sn;
+        y[i + half] = b * cs + a * sn;
+    }
+}
+
+/* y[f] += sum_k u[k] * V[f][k] for f < F: one token row of U_m V_m^T
+ * ([K §2, reuse equation and "Aplicacao de Patch"]). V is [F][m]. */
+void orc_patch_row_f64(double* y, int F, int m, const double* u, const double* V) {
+    for (int f = 0; f < F; ++f) {
+        double s = 0.0;
+        for (int k = 0; k < m; ++k) s += u[k] * V[(int64_t)f * m + k];
+        y[f] += s;
+    }
+}
+
+/* One token row of one channel (heads x dim values, head-major), in fp64:
+ * rotate every head, then add the patch row (m may be 0). */
+void orc_row_f64(const double* x, double* y, int heads, int dim, int r, double theta,
+                 int64_t delta, int m, const double* u, const double* V) {
+    for (int h = 0; h < heads; ++h)
+        orc_rotate_head_f64(x + (int64_t)h * dim, y + (int64_t)h * dim, dim, r, theta, delta);
+    if (m > 0) orc_patch_row_f64(y, heads * dim, m, u, V);
+}
+
+/* One token row in storage format (dtype 0 = bf16 bits, 1 = fp32): x_in and out
+ * hold heads*dim contiguous elements, u holds m, V holds [heads*dim][m], all of
+ * the same dtype.  out may equal x_in.  With m = 0, every element the rotation
+ * does not move keeps its bits. Returns 0, or -1 on bad arguments. */
+int orc_row(int dtype, const void* x_in, void* out, int heads, int dim, int r,
+            double theta, int64_t delta, int m, const void* u, const void* V) {
+    if ((dtype != ORC_BF16 && dtype != ORC_F32) || heads < 1 || dim < 1 || r < 0 ||
+        r > dim || (r & 1) || m < 0)
+        return -1;
+    int64_t F = (int64_t)heads * dim;
+    double* x = (double*)malloc(sizeof(double) * F);
+    double* y = (double*)malloc(sizeof(double) * F);
+    double* ud = (double*)malloc(sizeof(double) * (m > 0 ? m : 1));
+    double* vd = (double*)malloc(sizeof(double) * (m > 0 ? F * m : 1));
+    if (!x || !y || !ud || !vd) { free(x); free(y); free(ud); free(vd); return -1; }
+    for (int64_t f = 0; f < F; ++f) x[f] = load_elem(dtype, x_in, f);
+    for (int k = 0; k < m; ++k) ud[k] = load_elem(dtype, u, k);
+    for (int64_t i = 0; i < F * m; ++i) vd[i] = load_elem(dtype, V, i);
+    orc_row_f64(x, y, heads, dim, r, theta, delta, m, ud, vd);
+    for (int64_t f = 0; f < F; ++f) {
+        int d = (int)(f % dim);
+        int moved = m > 0 || (delta != 0 && d < r);
+        if (moved) store_elem(dtype, out, f, y[f]);
+        else if (out != x_in) copy_elem(dtype, out, f, x_in, f);
+    }
+    free(x); free(y); free(ud); free(vd);
+    return 0;
+}
+
+/* ---------------------------------------------------------- whole operator */
+
+typedef struct {
+    void* data;               /* element (layer 0, slot 0, head 0, dim 0) */
+    int32_t heads, dim, rope_dim;
+    int32_t pad_;
+    int64_t layer_stride, slot_stride, head_stride, page_stride; /* elements */
+    const void* U;            /* [layers][total_tokens][m] or NULL when m = 0 */
+    const void* V;            /* [layers][chunks][heads*dim][m] or NULL */
+} orc_channel;
+
+typedef struct {
+    int32_t dtype, num_layers, num_channels, page_size;
+    orc_channel ch[2];
+    double theta;
+    const int32_t* block_table; /* [ceil(total_tokens / page_size)] when paged */
+    int64_t total_tokens;
+    const int64_t* offsets;     /* [num_chunks + 1], 0 = o_0 <= ... = total */
+    const int64_t* delta;       /* [num_chunks] */
+    int32_t num_chunks, rank;
+} orc_problem;
+
+/* Element offset of (layer, logical token t, head h, dim 0).  Contiguous: the
+ * slot is the token.  Paged with page size P: the logical page t / P is looked
+ * up in the block table and t mod P is the slot inside that pool page. */
+int64_t orc_row_offset(const orc_channel* c, int32_t page_size, const int32_t* bt,
+                       int64_t layer, int64_t t, int64_t h) {
+    int64_t slot;
+    if (page_size > 0)
+        slot = (int64_t)bt[t / page_size] * c->page_stride + (t % page_size) * c->slot_stride;
+    else
+        slot = t * c->slot_stride;
+    return layer * c->layer_stride + slot + h * c->head_stride;
+}
+
+static int64_t chunk_of(const orc_problem* p, int64_t t) {
+    for (int32_t j = 0; j < p->num_chunks; ++j)
+        if (t >= p->offsets[j] && t < p->offsets[j + 1]) return j;
+    return -1;
+}
+
+/* Sum of the magnitudes of the terms that make each fp64 row value: for a rotated
+ * pair |a cos| + |b sin| (and |b cos| + |a sin|), |x| for an unrotated dim, plus
+ * sum_k |u_k V[f][k]| for the patch.  It bounds the fp32 evaluation error of any
+ * ordering of the same terms; the parity tolerance near cancellation scales with it. */
+void orc_row_magnitude_f64(const double* x, double* s, int heads, int dim, int r,
+                           double theta, int64_t delta, int m, const double* u,
+                           const double* V) {
+    int half = r / 2;
+    for (int h = 0; h < heads; ++h) {
+        const double* xh = x + (int64_t)h * dim;
+        double* sh = s + (int64_t)h * dim;
+        for (int d = 0; d < dim; ++d) sh[d] = fabs(xh[d]);
+        if (delta == 0 || r == 0) continue;
+        for (int i = 0; i < half; ++i) {
+            double phi = (double)delta * orc_freq(theta, r, i);
+            double cs = fabs(cos(phi)), sn = fabs(sin(phi));
+            double a = fabs(xh[i]), b = fabs(xh[i + half]);
+            sh[i] = a * cs + b * sn;
+            sh[i + half] = b * cs + a * sn;
+        }
+    }
+    int64_t F = (int64_t)heads * dim;
+    for (int64_t f = 0; f < F; ++f)
+        for (int k = 0; k < m; ++k) s[f] += fabs(u[k] * V[f * m + k]);
+}
+
+/* The reuse operator over a whole problem, in place on host memory.  When y_out[c]
+ * (and s_out[c]) are given, they are fp64 arrays laid out exactly like channel c's
+ * elements (same offsets from the channel's data pointer); every element the call
+ * computes gets its unrounded value there (and its magnitude bound), every other
+ * element is left as the caller filled it.  Returns 0, or -1 on bad arguments. */
+int orc_relocate_patch_ex(const orc_problem* p, double* const* y_out, double* const* s_out) {
+    if (!p || p->num_channels < 1 || p->num_channels > 2 || p->rank < 0 ||
+        (p->dtype != ORC_BF16 && p->dtype != ORC_F32))
+        return -1;
+    int64_t T = p->total_tokens, L = p->num_layers;
+    if (T == 0 || L == 0 || p->num_chunks == 0) return 0;
+    int es = p->dtype == ORC_BF16 ? 2 : 4;
+    int m = p->rank;
+    int bad = 0;
+    for (int c = 0; c < p->num_channels; ++c) {
+        const orc_channel* ch = &p->ch[c];
+        int64_t F = (int64_t)ch->heads * ch->dim;
+        double* yo = y_out ? y_out[c] : NULL;
+        double* so = s_out ? s_out[c] : NULL;
+        if (m == 0 && ch->rope_dim == 0) continue; /* never read nor written */
+#pragma omp parallel for collapse(2) schedule(dynamic, 64) reduction(|:bad)
+        for (int64_t l = 0; l < L; ++l) {
+            for (int64_t t = 0; t < T; ++t) {
+                int64_t j = chunk_of(p, t);
+                if (j < 0) { bad = 1; continue; }
+                int64_t dj = p->delta[j];
+                if (m == 0 && dj == 0) continue;
+                char* row = (char*)malloc((size_t)(F * es));
+                double* x = (double*)malloc(sizeof(double) * F);
+                double* y = (double*)malloc(sizeof(double) * F);
+                double* s = (double*)malloc(sizeof(double) * F);
+                double* ud = (double*)malloc(sizeof(double) * (m > 0 ? m : 1));
+                double* vd = (double*)malloc(sizeof(double) * (m > 0 ? F * m : 1));
+                int64_t* offs = (int64_t*)malloc(sizeof(int64_t) * ch->heads);
+                for (int64_t h = 0; h < ch->heads; ++h) {
+                    offs[h] = orc_row_offset(ch, p->page_size, p->block_table, l, t, h);
+                    memcpy(row + h * ch->dim * es, (char*)ch->data + offs[h] * es, (size_t)ch->dim * es);
+                }
+                const void* u = NULL;
+                const void* V = NULL;
+                if (m > 0) {
+                    u = (const char*)ch->U + ((l * T + t) * m) * es;
+                    V = (const char*)ch->V + ((l * p->num_chunks + j) * F * m) * es;
+                    for (int k = 0; k < m; ++k) ud[k] = load_elem(p->dtype, u, k);
+                    for (int64_t i = 0; i < F * m; ++i) vd[i] = load_elem(p->dtype, V, i);
+                }
+                if (yo) {
+                    for (int64_t f = 0; f < F; ++f) x[f] = load_elem(p->dtype, row, f);
+                    orc_row_f64(x, y, ch->heads, ch->dim, ch->rope_dim, p->theta, dj, m, ud, vd);
+                    orc_row_magnitude_f64(x, s, ch->heads, ch->dim, ch->rope_dim, p->theta, dj, m, ud, vd);
+                }
+                if (orc_row(p->dtype, row, row, ch->heads, ch->dim, ch->rope_dim, p->theta,
+                            dj, m, u, V) != 0)
+                    bad = 1;
+                for (int64_t h = 0; h < ch->heads; ++h) {
+                    memcpy((char*)ch->data + offs[h] * es, row + h * ch->dim * es, (size_t)ch->dim * es);
+                    if (yo) {
+                        for (int d = 0; d < ch->dim; ++d) {
+                            int moved = m > 0 || d < ch->rope_dim;
+                            if (!moved) continue;
+                            yo[offs[h] + d] = y[h * ch->dim + d];
+                            if (so) so[offs[h] + d] = s[h * ch->dim + d];
+                        }
+                    }
+                }
+                free(row); free(x); free(y); free(s); free(ud); free(vd); free(offs);
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+int orc_relocate_patch(const orc_problem* p) { return orc_relocate_patch_ex(p, NULL, NULL); }
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+int orc_struct_sizes(int which) {
+    return which == 0 ? (int)sizeof(orc_channel) : (int)sizeof(orc_problem);
+}

@@ -1,0 +1,263 @@
+"""ctypes front end of the fp64 CPU oracle (kamera_oracle.c).
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` import this module.  It shares no code with
+the GPU library: it has its own C source, its own structs and its own loader.
+
+Every array argument is a numpy array in storage format: bf16 values travel as
+``uint16`` bit patterns, fp32 values as ``float32``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "kamera_oracle.c")
+LIB = os.path.join(HERE, "libkamera_oracle.so")
+
+BF16 = 0
+F32 = 1
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (IEEE fp64, no FMA contraction, OpenMP)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math",
+                               "-fopenmp", "-shared", "-fPIC", "-Wall", SRC,
+                               "-o", tmp, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+class _Channel(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("heads", C.c_int32), ("dim", C.c_int32),
+                ("rope_dim", C.c_int32), ("pad_", C.c_int32),
+                ("layer_stride", C.c_int64), ("slot_stride", C.c_int64),
+                ("head_stride", C.c_int64), ("page_stride", C.c_int64),
+                ("U", C.c_void_p), ("V", C.c_void_p)]
+
+
+class _Problem(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("num_layers", C.c_int32),
+                ("num_channels", C.c_int32), ("page_size", C.c_int32),
+                ("ch", _Channel * 2), ("theta", C.c_double),
+                ("block_table", C.c_void_p), ("total_tokens", C.c_int64),
+                ("offsets", C.c_void_p), ("delta", C.c_void_p),
+                ("num_chunks", C.c_int32), ("rank", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = C.CDLL(LIB)
+        L.orc_bf16_from_double.restype = C.c_uint16
+        L.orc_bf16_from_double.argtypes = [C.c_double]
+        L.orc_bf16_to_double.restype = C.c_double
+        L.orc_bf16_to_double.argtypes = [C.c_uint16]
+        L.orc_round_bf16_array.argtypes = [C.c_void_p, C.c_void_p, C.c_int64]
+        L.orc_freq.restype = C.c_double
+        L.orc_freq.argtypes = [C.c_double, C.c_int, C.c_int]
+        L.orc_rotate_head_f64.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int,
+                                          C.c_double, C.c_int64]
+        L.orc_row_f64.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
+                                  C.c_double, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
+        L.orc_row.restype = C.c_int
+        L.orc_row.argtypes = [C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
+                              C.c_double, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
+        L.orc_relocate_patch.restype = C.c_int
+        L.orc_relocate_patch.argtypes = [C.POINTER(_Problem)]
+        L.orc_relocate_patch_ex.restype = C.c_int
+        L.orc_relocate_patch_ex.argtypes = [C.POINTER(_Problem), C.POINTER(C.c_void_p),
+                                            C.POINTER(C.c_void_p)]
+        L.orc_row_magnitude_f64.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
+                                            C.c_double, C.c_int64, C.c_int, C.c_void_p,
+                                            C.c_void_p]
+        L.orc_row_offset.restype = C.c_int64
+        L.orc_row_offset.argtypes = [C.POINTER(_Channel), C.c_int32, C.c_void_p,
+                                     C.c_int64, C.c_int64, C.c_int64]
+        L.orc_num_threads.restype = C.c_int
+        L.orc_struct_sizes.restype = C.c_int
+        L.orc_struct_sizes.argtypes = [C.c_int]
+        assert L.orc_struct_sizes(0) == C.sizeof(_Channel)
+        assert L.orc_struct_sizes(1) == C.sizeof(_Problem)
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError("storage arrays are uint16 (bf16 bits) or float32")
+
+
+# ----------------------------------------------------------------- numbers
+
+def round_bf16(y) -> np.ndarray:
+    """fp64 -> bf16 bits, round to nearest even, in one step."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.empty(y.shape, dtype=np.uint16)
+    lib().orc_round_bf16_array(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bits -> exact fp64 values."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def freq(theta: float, r: int, i: int) -> float:
+    return lib().orc_freq(theta, r, i)
+
+
+# ------------------------------------------------------------- fp64 forms
+
+def rotate_head_f64(x, r: int, theta: float, delta: int) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    lib().orc_rotate_head_f64(_ptr(x), _ptr(y), x.size, r, theta, int(delta))
+    return y
+
+
+def row_f64(x, heads: int, dim: int, r: int, theta: float, delta: int,
+            u=None, V=None) -> np.ndarray:
+    """One token row (heads*dim values) in fp64: rotation, then the patch row."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    assert x.size == heads * dim
+    y = np.empty_like(x)
+    m = 0 if u is None else int(np.asarray(u).size)
+    uu = None if u is None else np.ascontiguousarray(u, dtype=np.float64)
+    vv = None if V is None else np.ascontiguousarray(V, dtype=np.float64)
+    if m:
+        assert vv.shape == (heads * dim, m)
+    lib().orc_row_f64(_ptr(x), _ptr(y), heads, dim, r, theta, int(delta), m, _ptr(uu), _ptr(vv))
+    return y
+
+
+def row_magnitude_f64(x, heads: int, dim: int, r: int, theta: float, delta: int,
+                      u=None, V=None) -> np.ndarray:
+    """Per element, the sum of |terms| that make the fp64 row value."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    s = np.empty_like(x)
+    m = 0 if u is None else int(np.asarray(u).size)
+    uu = None if u is None else np.ascontiguousarray(u, dtype=np.float64)
+    vv = None if V is None else np.ascontiguousarray(V, dtype=np.float64)
+    lib().orc_row_magnitude_f64(_ptr(x), _ptr(s), heads, dim, r, theta, int(delta), m,
+                                _ptr(uu), _ptr(vv))
+    return s
+
+
+def row(x, heads: int, dim: int, r: int, theta: float, delta: int,
+        u=None, V=None) -> np.ndarray:
+    """One token row in storage format (uint16 bf16 bits or float32)."""
+    x = np.ascontiguousarray(x)
+    code = _dtype_code(x)
+    out = np.empty_like(x)
+    m = 0 if u is None else int(np.asarray(u).size)
+    uu = None if u is None else np.ascontiguousarray(u, dtype=x.dtype)
+    vv = None if V is None else np.ascontiguousarray(V, dtype=x.dtype)
+    rc = lib().orc_row(code, _ptr(x), _ptr(out), heads, dim, r, theta, int(delta), m,
+                       _ptr(uu), _ptr(vv))
+    if rc != 0:
+        raise ValueError("oracle rejected the row arguments")
+    return out
+
+
+# ---------------------------------------------------------- whole operator
+
+def row_offset(ch: dict, page_size: int, block_table, layer: int, t: int, h: int) -> int:
+    c = _Channel()
+    c.layer_stride, c.slot_stride = ch["layer_stride"], ch["slot_stride"]
+    c.head_stride, c.page_stride = ch["head_stride"], ch.get("page_stride", 0)
+    bt = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
+    return lib().orc_row_offset(C.byref(c), page_size, _ptr(bt), layer, t, h)
+
+
+def relocate_patch(channels, *, num_layers: int, theta: float, offsets, delta,
+                   rank: int = 0, page_size: int = 0, block_table=None,
+                   y_out=None, s_out=None) -> None:
+    """The reuse operator over host arrays, in place.
+
+    ``channels`` is a list of one or two dicts with keys ``data`` (a flat numpy
+    buffer, uint16 or float32, element 0 = layer 0 slot 0 head 0 dim 0),
+    ``offset`` (element offset of that first element inside ``data``, default
+    0), ``heads``, ``dim``, ``rope_dim``, ``layer_stride``, ``slot_stride``,
+    ``head_stride``, ``page_stride`` (elements) and, when ``rank > 0``, ``U``
+    ([layers][tokens][rank]) and ``V`` ([layers][chunks][heads*dim][rank]).
+
+    ``y_out`` / ``s_out``: optional lists (one per channel) of float64 buffers shaped
+    like that channel's ``data``; every element the call computes receives its
+    unrounded fp64 value / its sum of term magnitudes, at the same element offset.
+    """
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    delta = np.ascontiguousarray(delta, dtype=np.int64)
+    bt = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
+    p = _Problem()
+    keep = [offsets, delta, bt]
+    code = None
+    for i, ch in enumerate(channels):
+        data = ch["data"]
+        assert data.flags["C_CONTIGUOUS"] and data.flags["WRITEABLE"]
+        c = _dtype_code(data)
+        if code is None:
+            code = c
+        assert code == c
+        es = data.itemsize
+        p.ch[i].data = data.ctypes.data + es * int(ch.get("offset", 0))
+        p.ch[i].heads, p.ch[i].dim, p.ch[i].rope_dim = ch["heads"], ch["dim"], ch["rope_dim"]
+        p.ch[i].layer_stride = ch["layer_stride"]
+        p.ch[i].slot_stride = ch["slot_stride"]
+        p.ch[i].head_stride = ch["head_stride"]
+        p.ch[i].page_stride = ch.get("page_stride", 0)
+        if rank > 0:
+            U = np.ascontiguousarray(ch["U"])
+            V = np.ascontiguousarray(ch["V"])
+            assert U.dtype == data.dtype and V.dtype == data.dtype
+            keep += [U, V]
+            p.ch[i].U, p.ch[i].V = U.ctypes.data, V.ctypes.data
+    p.dtype = code
+    p.num_layers = num_layers
+    p.num_channels = len(channels)
+    p.page_size = page_size
+    p.theta = theta
+    p.block_table = _ptr(bt)
+    p.total_tokens = int(offsets[-1]) if offsets.size else 0
+    p.offsets = _ptr(offsets)
+    p.delta = _ptr(delta)
+    p.num_chunks = int(delta.size)
+    p.rank = rank
+    ys = (C.c_void_p * 2)()
+    ss = (C.c_void_p * 2)()
+    if y_out is not None:
+        for i, ch in enumerate(channels):
+            yb, sb = y_out[i], s_out[i]
+            assert yb.dtype == np.float64 and sb.dtype == np.float64
+            assert yb.size == ch["data"].size and sb.size == ch["data"].size
+            ys[i] = yb.ctypes.data + 8 * int(ch.get("offset", 0))
+            ss[i] = sb.ctypes.data + 8 * int(ch.get("offset", 0))
+        rc = lib().orc_relocate_patch_ex(C.byref(p), ys, ss)
+    else:
+        rc = lib().orc_relocate_patch(C.byref(p))
+    del keep
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
