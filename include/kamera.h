@@ -1,0 +1,172 @@
+/*
+ * kamera.h: C ABI of the Kamera relocate + patch operator on AMD Instinct MI355X (gfx950).
+ *
+ * The operator rebuilds a reused KV chunk at a new position
+ * ("Kamera: KV Cache Multimodal Unificado e Invariante a Posicao para Reuso sem
+ * Treinamento", gist.science/pt/paper/2606.23581, §2, reuse equation):
+ *
+ *     KV(B|A)  ~=  R(delta) * KV(B|empty)  +  U_m V_m^T
+ *
+ *   - R(delta): the cached keys, stored rotated at their old positions, are turned
+ *     by the RoPE phase shift delta = new position - old position (same page, §2,
+ *     "Relocacao": an exact rotation, no network pass).  Values and the MLA latent
+ *     c_KV have no position and are not rotated (same page, §2, architecture list;
+ *     and "Modelos Tomam Notas no Prefill", gist.science/pt/paper/2606.17107, §3B:
+ *     keys are re-rotated, values are carried over unchanged).
+ *   - U_m V_m^T: a rank-m conditioning patch, token factor U_m [T, m] and feature
+ *     factor V_m [F, m], added to every patched channel (same Kamera page, §2,
+ *     "Aplicacao de Patch"; MLA patches both of its channels, §2 architecture list).
+ *   - With m = 0 the call is the rotation-only path that serves sliding-window
+ *     survival (same page, §3, "Sobrevivencia de Janela Deslizante").
+ *
+ * Readings fixed by this library where the pages print no formula:
+ *   - NeoX half-split pairing: in a head whose first rope_dim dims rotate, dim i
+ *     pairs with dim i + rope_dim/2; pair i turns by angle delta * theta^(-2i/rope_dim);
+ *     (a, b) -> (a cos - b sin, b cos + a sin).  Dims >= rope_dim do not rotate.
+ *   - The patch is added after the rotation; it is not rotated.
+ *   - delta == 0 means R = identity exactly.
+ *   - Each output element is rounded once to the storage type (round to nearest even).
+ *     Angles are formed and reduced in fp64; the sums run in fp32.
+ *
+ * Conventions for every entry point:
+ *   - In place: the KV buffers named by the descriptor are read and overwritten.
+ *   - Ownership: the caller owns every buffer (KV, block table, chunk offsets,
+ *     deltas, factors).  The library allocates no memory, keeps no per-call state
+ *     and returns as soon as the work is enqueued on `stream` (stream order; no
+ *     host synchronisation).  Work is safe to capture in a HIP graph.
+ *   - Pointers marked "device" must be device-accessible (hipMalloc or torch CUDA
+ *     tensors).  Descriptor structs themselves are host memory and are read only
+ *     during the call.
+ *   - Errors: every host-checkable argument error is reported before any HIP call
+ *     is made, as a kamera_status; kamera_last_error() then holds a message for the
+ *     calling thread.  A failed launch returns KAMERA_E_HIP.  Device-array
+ *     preconditions (listed per field) are not checked; whatever their values, the
+ *     kernels only address tokens in [0, total_tokens), chunks in [0, num_chunks)
+ *     and pool pages in [0, num_pages).
+ *   - Threading: reentrant; calls on different streams are independent.  Calls that
+ *     touch the same KV elements must be ordered by the caller.
+ */
+#ifndef KAMERA_H
+#define KAMERA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef KAMERA_API
+#define KAMERA_API __attribute__((visibility("default")))
+#endif
+
+#define KAMERA_ABI_VERSION 1
+#define KAMERA_MAX_RANK 256   /* largest patch rank m accepted */
+
+typedef enum {
+  KAMERA_OK = 0,
+  KAMERA_E_NULL = 1,        /* a required pointer is NULL */
+  KAMERA_E_SHAPE = 2,       /* a size, stride, rank or rope_dim is out of range */
+  KAMERA_E_UNSUPPORTED = 3, /* dtype or pairing this library does not implement */
+  KAMERA_E_ALIGN = 4,       /* a pointer is not aligned to its element size */
+  KAMERA_E_ALIAS = 5,       /* factor memory overlaps KV memory */
+  KAMERA_E_HIP = 6          /* the HIP runtime reported an error at launch */
+} kamera_status;
+
+typedef enum { KAMERA_BF16 = 0, KAMERA_F32 = 1 } kamera_dtype;
+
+typedef enum {
+  KAMERA_NEOX_HALF = 0 /* dim i pairs with dim i + rope_dim/2 */
+} kamera_pairing;
+
+/* flags of kamera_kv_desc */
+#define KAMERA_FLAG_GENERIC 1u /* run the plain per-row kernel instead of the tuned ones */
+
+/* One cache channel: K or V (MHA/GQA); c_KV or k_rope (MLA).
+ * Element (layer l, slot s, head h, dim d) sits at
+ *     data + l*layer_stride + s*slot_stride + h*head_stride + d          (contiguous)
+ *     data + l*layer_stride + p*page_stride + s*slot_stride + h*head_stride + d (paged:
+ *           logical token t lives in pool page p = block_table[t / page_size],
+ *           slot s = t mod page_size)
+ * Strides are in elements and must be >= 0.  The element sets of distinct rows,
+ * heads and channels must not overlap (precondition).  The MLA combined row
+ * [c_KV(512) | k_rope(64)] is two channels over one buffer: data and data + 512,
+ * slot_stride 576. */
+typedef struct {
+  void* data;          /* device; element (layer 0, slot 0, head 0, dim 0) */
+  int32_t heads;       /* >= 1 */
+  int32_t dim;         /* head dim D >= 1; feature width F = heads * dim */
+  int32_t rope_dim;    /* even, 0 <= rope_dim <= dim; 0 = this channel never rotates */
+  int32_t reserved0;   /* must be 0 */
+  int64_t layer_stride, slot_stride, head_stride, page_stride;
+} kamera_channel;
+
+typedef struct {
+  int32_t dtype;         /* kamera_dtype of the KV elements and of the factors */
+  int32_t num_layers;    /* >= 0 */
+  int32_t num_channels;  /* 1 or 2 */
+  int32_t pairing;       /* kamera_pairing */
+  kamera_channel ch[2];  /* MHA/GQA: {K, V}; MLA: {c_KV, k_rope} */
+  double rope_theta;     /* RoPE base, finite and > 0 when any rope_dim > 0 */
+  int32_t page_size;     /* 0 = contiguous (slot = token); > 0 = paged */
+  uint32_t flags;        /* KAMERA_FLAG_* */
+  int64_t num_pages;     /* paged: pool pages per layer; block-table entries lie in [0, num_pages) */
+  const int32_t* block_table; /* device [ceil(total_tokens / page_size)] when paged, else ignored.
+                                 Precondition: entries pairwise distinct.  Tokens whose entry
+                                 lies outside [0, num_pages) are left untouched. */
+} kamera_kv_desc;
+
+/* The chunks being moved.  Chunk j owns logical tokens [token_offsets[j], token_offsets[j+1]). */
+typedef struct {
+  int32_t num_chunks;      /* >= 0; 0 requires total_tokens == 0 */
+  int32_t reserved0;       /* must be 0 */
+  int64_t total_tokens;    /* host copy of token_offsets[num_chunks]; sizes the launch */
+  const int64_t* token_offsets; /* device [num_chunks + 1]; precondition: 0 = o_0 <= o_1 <= ... = total_tokens */
+  const int64_t* delta;    /* device [num_chunks]; new position - old position; precondition |delta| < 2^53 */
+} kamera_chunks;
+
+/* The rank-m patch, one factor pair per channel, in the KV dtype, dense row-major:
+ *   U[c]: [num_layers][total_tokens][rank]           token factor U_m, per layer
+ *   V[c]: [num_layers][num_chunks][heads*dim][rank]  feature factor V_m, per layer and chunk
+ * The same pointers may be passed for both channels when their shapes agree. */
+typedef struct {
+  int32_t rank;            /* 0 <= m <= KAMERA_MAX_RANK; 0 = no patch */
+  int32_t reserved0;       /* must be 0 */
+  const void* U[2];        /* device, read only; NULL allowed only when rank == 0 */
+  const void* V[2];        /* device, read only; NULL allowed only when rank == 0 */
+} kamera_patch;
+
+/* Rotation only (m = 0).  Rotates dims [0, rope_dim) of every head of every channel
+ * with rope_dim > 0, for every chunk with delta != 0.  Nothing else is read or
+ * written: channels with rope_dim == 0 (V, c_KV), dims >= rope_dim and chunks with
+ * delta == 0 keep their exact bits.  Kamera page §3, sliding-window survival. */
+KAMERA_API kamera_status kamera_relocate(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                              hipStream_t stream);
+
+/* Relocate and patch: every element of every channel becomes
+ * round(R(delta_j) x + sum_k U[c][l][t][k] * V[c][l][j][f][k]).  Kamera page §2,
+ * reuse equation.  patch == NULL or patch->rank == 0 behaves as kamera_relocate. */
+KAMERA_API kamera_status kamera_relocate_patch(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                                    const kamera_patch* patch, hipStream_t stream);
+
+/* Which kernels a call would launch, without launching anything (no HIP call).
+ * Fills `out` and returns the status the call itself would return before launching. */
+typedef struct {
+  int32_t kernel[2];       /* per channel: 0 none, 1 rotate (tuned), 2 rotate+patch MFMA (tuned),
+                              3 generic */
+  int32_t launches;        /* kernel launches the call would make */
+  int32_t tokens_per_unit; /* tokens one wavefront streams per unit of work (tuned kernels) */
+  int64_t units;           /* wavefront work units of the tuned launch */
+} kamera_plan_info;
+
+KAMERA_API kamera_status kamera_plan(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                          const kamera_patch* patch, kamera_plan_info* out);
+
+KAMERA_API const char* kamera_status_str(kamera_status s);
+KAMERA_API const char* kamera_last_error(void); /* this thread's last failure message ("" if none) */
+KAMERA_API int kamera_abi_version(void);        /* KAMERA_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KAMERA_H */

@@ -1,0 +1,342 @@
+// Host side of the C ABI declared in include/kamera.h: argument checks (no HIP call
+// before they pass), kernel choice, launch on the caller's stream.
+#include <stdint.h>
+#include <string.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kamera.h"
+#include "kamera_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kamera_status fail(kamera_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+kamera_status fail(kamera_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+enum Kernel { K_NONE = 0, K_ROTATE = 1, K_MFMA = 2, K_GENERIC = 3 };
+
+constexpr int kMfmaMaxRank = 128;
+constexpr int64_t kMaxTunedTokens = (int64_t)1 << 30;  // token ids stay in 32 bits
+constexpr int64_t kTargetWaves = 256 * 16;              // 256 CUs, 16 wavefronts each
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Exclusive end (bytes) of the KV memory a channel can touch, from its base.
+// Returns false on int64 overflow.
+bool kv_extent(const kamera_channel& c, int64_t layers, int64_t slots, int32_t page_size,
+               int64_t pages, int64_t es, int64_t* out) {
+  __int128 last = (__int128)(layers - 1) * c.layer_stride + (__int128)(c.heads - 1) * c.head_stride +
+                  (c.dim - 1);
+  if (page_size > 0)
+    last += (__int128)(pages - 1) * c.page_stride + (__int128)(page_size - 1) * c.slot_stride;
+  else
+    last += (__int128)(slots - 1) * c.slot_stride;
+  const __int128 end = (last + 1) * es;
+  if (end > (__int128)INT64_MAX) return false;
+  *out = (int64_t)end;
+  return true;
+}
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+struct Plan {
+  int kernel[2] = {K_NONE, K_NONE};
+  int launches = 0;
+  int range_tokens = 0;
+  int tasks_per_wave = 0;
+  int64_t units = 0;
+  bool mfma_both = false;
+};
+
+bool rotate_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, int64_t T) {
+  const int r = c.rope_dim;
+  const bool shape = r % 16 == 0 && (r == 16 || r == 32 || r == 64 || r == 128 || r == 256);
+  return kv.dtype == KAMERA_BF16 && !(kv.flags & KAMERA_FLAG_GENERIC) && shape &&
+         T < kMaxTunedTokens && aligned(c.data, 16) && c.layer_stride % 8 == 0 &&
+         c.slot_stride % 8 == 0 && c.head_stride % 8 == 0 && c.page_stride % 8 == 0;
+}
+
+bool mfma_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, const kamera_patch& p,
+                   int ci, int64_t T) {
+  return kv.dtype == KAMERA_BF16 && !(kv.flags & KAMERA_FLAG_GENERIC) && p.rank <= kMfmaMaxRank &&
+         c.dim % 64 == 0 && c.rope_dim % 64 == 0 && T < kMaxTunedTokens && aligned(c.data, 16) &&
+         aligned(p.U[ci], 16) && aligned(p.V[ci], 16) && c.layer_stride % 8 == 0 &&
+         c.slot_stride % 8 == 0 && c.head_stride % 8 == 0 && c.page_stride % 8 == 0 &&
+         (int64_t)c.heads * c.dim < (1 << 24);
+}
+
+// Wavefront units for a given tokens-per-unit.
+int64_t mfma_units(const kamera_kv_desc& kv, const kamera_chunks& ch, int nt, int rt,
+                   const bool* use) {
+  const int64_t nranges = (ch.total_tokens + rt - 1) / rt;
+  int64_t u = 0;
+  for (int c = 0; c < kv.num_channels; ++c) {
+    if (!use[c]) continue;
+    const int64_t tasks = (int64_t)kv.ch[c].heads * (kv.ch[c].dim / 64);
+    u += (tasks + nt - 1) / nt * nranges;
+  }
+  return u * kv.num_layers;
+}
+
+// Checks every host-visible argument.  No HIP call is made here.
+kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamera_patch* p,
+                       Plan* plan) {
+  if (!kv) return fail(KAMERA_E_NULL, "kv descriptor is NULL");
+  if (!ch) return fail(KAMERA_E_NULL, "chunks descriptor is NULL");
+  if (kv->dtype != KAMERA_BF16 && kv->dtype != KAMERA_F32)
+    return fail(KAMERA_E_UNSUPPORTED, "dtype %d is not bf16 (0) or fp32 (1)", kv->dtype);
+  if (kv->pairing != KAMERA_NEOX_HALF)
+    return fail(KAMERA_E_UNSUPPORTED, "pairing %d: only NeoX half-split (0) is implemented",
+                kv->pairing);
+  if (kv->flags & ~KAMERA_FLAG_GENERIC) return fail(KAMERA_E_SHAPE, "unknown flags 0x%x", kv->flags);
+  if (kv->num_layers < 0) return fail(KAMERA_E_SHAPE, "num_layers %d < 0", kv->num_layers);
+  if (kv->num_channels < 1 || kv->num_channels > 2)
+    return fail(KAMERA_E_SHAPE, "num_channels %d is not 1 or 2", kv->num_channels);
+  if (ch->num_chunks < 0) return fail(KAMERA_E_SHAPE, "num_chunks %d < 0", ch->num_chunks);
+  if (ch->total_tokens < 0) return fail(KAMERA_E_SHAPE, "total_tokens < 0");
+  if (ch->reserved0 != 0) return fail(KAMERA_E_SHAPE, "chunks.reserved0 must be 0");
+  if (ch->num_chunks == 0 && ch->total_tokens != 0)
+    return fail(KAMERA_E_SHAPE, "total_tokens > 0 with no chunks");
+  if (ch->total_tokens >= ((int64_t)1 << 40)) return fail(KAMERA_E_SHAPE, "total_tokens too large");
+  const int m = p ? p->rank : 0;
+  if (p && p->reserved0 != 0) return fail(KAMERA_E_SHAPE, "patch.reserved0 must be 0");
+  if (m < 0 || m > KAMERA_MAX_RANK)
+    return fail(KAMERA_E_SHAPE, "rank %d outside [0, %d]", m, KAMERA_MAX_RANK);
+  const int64_t es = kv->dtype == KAMERA_BF16 ? 2 : 4;
+  const bool empty = kv->num_layers == 0 || ch->total_tokens == 0;
+  bool any_rope = false;
+  for (int c = 0; c < kv->num_channels; ++c) {
+    const kamera_channel& k = kv->ch[c];
+    if (k.heads < 1 || k.dim < 1)
+      return fail(KAMERA_E_SHAPE, "channel %d: heads %d and dim %d must be >= 1", c, k.heads, k.dim);
+    if (k.rope_dim < 0 || k.rope_dim > k.dim || (k.rope_dim & 1))
+      return fail(KAMERA_E_SHAPE, "channel %d: rope_dim %d must be even and in [0, dim=%d]", c,
+                  k.rope_dim, k.dim);
+    if (k.reserved0 != 0) return fail(KAMERA_E_SHAPE, "channel %d: reserved0 must be 0", c);
+    if (k.layer_stride < 0 || k.slot_stride < 0 || k.head_stride < 0 || k.page_stride < 0)
+      return fail(KAMERA_E_SHAPE, "channel %d: strides must be >= 0", c);
+    if ((int64_t)k.heads * k.dim > ((int64_t)1 << 30))
+      return fail(KAMERA_E_SHAPE, "channel %d: heads * dim too large", c);
+    any_rope = any_rope || k.rope_dim > 0;
+    if (!empty && !k.data) return fail(KAMERA_E_NULL, "channel %d: data is NULL", c);
+    if (!aligned(k.data, es))
+      return fail(KAMERA_E_ALIGN, "channel %d: data not aligned to %d bytes", c, (int)es);
+  }
+  if (any_rope && !(std::isfinite(kv->rope_theta) && kv->rope_theta > 0))
+    return fail(KAMERA_E_SHAPE, "rope_theta must be finite and > 0");
+  if (kv->page_size < 0) return fail(KAMERA_E_SHAPE, "page_size %d < 0", kv->page_size);
+  if (kv->page_size > 0) {
+    if (kv->num_pages < 1) return fail(KAMERA_E_SHAPE, "paged layout with num_pages < 1");
+    if (!empty && !kv->block_table) return fail(KAMERA_E_NULL, "paged layout with no block table");
+    if (!aligned(kv->block_table, 4)) return fail(KAMERA_E_ALIGN, "block table not 4-byte aligned");
+  }
+  if (!empty) {
+    if (!ch->token_offsets) return fail(KAMERA_E_NULL, "token_offsets is NULL");
+    if (!ch->delta) return fail(KAMERA_E_NULL, "delta is NULL");
+    if (!aligned(ch->token_offsets, 8) || !aligned(ch->delta, 8))
+      return fail(KAMERA_E_ALIGN, "token_offsets / delta not 8-byte aligned");
+  }
+  if (m > 0) {
+    for (int c = 0; c < kv->num_channels; ++c) {
+      if (!empty && (!p->U[c] || !p->V[c]))
+        return fail(KAMERA_E_NULL, "channel %d: rank %d with a NULL factor", c, m);
+      if (!aligned(p->U[c], es) || !aligned(p->V[c], es))
+        return fail(KAMERA_E_ALIGN, "channel %d: factor not aligned to %d bytes", c, (int)es);
+    }
+  }
+  // Factors must not overlap any KV memory the call writes.
+  if (m > 0 && !empty) {
+    for (int c = 0; c < kv->num_channels; ++c) {
+      int64_t kend;
+      if (!kv_extent(kv->ch[c], kv->num_layers, ch->total_tokens, kv->page_size, kv->num_pages, es,
+                     &kend))
+        return fail(KAMERA_E_SHAPE, "channel %d: KV extent overflows", c);
+      for (int f = 0; f < kv->num_channels; ++f) {
+        const int64_t F = (int64_t)kv->ch[f].heads * kv->ch[f].dim;
+        const __int128 ub = (__int128)kv->num_layers * ch->total_tokens * m * es;
+        const __int128 vb = (__int128)kv->num_layers * ch->num_chunks * F * m * es;
+        if (ub > INT64_MAX || vb > INT64_MAX) return fail(KAMERA_E_SHAPE, "factor size overflows");
+        if (overlaps(kv->ch[c].data, kend, p->U[f], (int64_t)ub) ||
+            overlaps(kv->ch[c].data, kend, p->V[f], (int64_t)vb))
+          return fail(KAMERA_E_ALIAS, "factors of channel %d overlap KV of channel %d", f, c);
+      }
+    }
+  }
+
+  // Kernel choice.
+  if (empty) return KAMERA_OK;
+  const int64_t T = ch->total_tokens;
+  if (m == 0) {
+    int64_t rt = 256;
+    while (rt > 16 && (int64_t)kv->num_layers * ((T + rt - 1) / rt) < kTargetWaves) rt /= 2;
+    plan->range_tokens = (int)rt;
+    for (int c = 0; c < kv->num_channels; ++c) {
+      if (kv->ch[c].rope_dim == 0) continue;
+      plan->kernel[c] = rotate_tuned_ok(*kv, kv->ch[c], T) ? K_ROTATE : K_GENERIC;
+      plan->launches++;
+      if (plan->kernel[c] == K_ROTATE) plan->units += (int64_t)kv->num_layers * ((T + rt - 1) / rt);
+    }
+    return KAMERA_OK;
+  }
+  bool use[2] = {false, false};
+  for (int c = 0; c < kv->num_channels; ++c) {
+    use[c] = mfma_tuned_ok(*kv, kv->ch[c], *p, c, T);
+    plan->kernel[c] = use[c] ? K_MFMA : K_GENERIC;
+    if (!use[c]) plan->launches++;
+  }
+  if (use[0] || use[1]) {
+    plan->launches++;
+    const int mk = (m + 31) / 32;
+    plan->tasks_per_wave = 1;
+    (void)mk;
+    int64_t rt = 256;
+    while (rt > 16 && mfma_units(*kv, *ch, plan->tasks_per_wave, (int)rt, use) < kTargetWaves) rt /= 2;
+    plan->range_tokens = (int)rt;
+    plan->units = mfma_units(*kv, *ch, plan->tasks_per_wave, (int)rt, use);
+  }
+  return KAMERA_OK;
+}
+
+kamera::CommonArgs common_args(const kamera_kv_desc& kv, const kamera_chunks& ch, int m, int rt) {
+  kamera::CommonArgs a;
+  memset(&a, 0, sizeof a);
+  a.offsets = ch.token_offsets;
+  a.delta = ch.delta;
+  a.block_table = kv.block_table;
+  a.total_tokens = ch.total_tokens;
+  a.num_pages = kv.num_pages;
+  a.range_tokens = rt > 0 ? rt : 256;
+  a.nranges = (ch.total_tokens + a.range_tokens - 1) / a.range_tokens;
+  a.theta = kv.rope_theta;
+  a.num_chunks = ch.num_chunks;
+  a.page_size = kv.page_size;
+  a.num_layers = kv.num_layers;
+  a.rank = m;
+  return a;
+}
+
+kamera::ChanArgs chan_args(const kamera_channel& c, const kamera_patch* p, int ci) {
+  kamera::ChanArgs a;
+  memset(&a, 0, sizeof a);
+  a.data = c.data;
+  a.layer_stride = c.layer_stride;
+  a.slot_stride = c.slot_stride;
+  a.head_stride = c.head_stride;
+  a.page_stride = c.page_stride;
+  a.U = p ? p->U[ci] : nullptr;
+  a.V = p ? p->V[ci] : nullptr;
+  a.heads = c.heads;
+  a.dim = c.dim;
+  a.rope_dim = c.rope_dim;
+  return a;
+}
+
+kamera_status hip_fail(hipError_t e, const char* what) {
+  return fail(KAMERA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+kamera_status run(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamera_patch* p,
+                  hipStream_t stream) {
+  g_last_error.clear();
+  Plan plan;
+  kamera_status st = validate(kv, ch, p, &plan);
+  if (st != KAMERA_OK || plan.launches == 0) return st;
+  const int m = p ? p->rank : 0;
+  const kamera::CommonArgs cm = common_args(*kv, *ch, m, plan.range_tokens);
+  if (m == 0) {
+    for (int c = 0; c < kv->num_channels; ++c) {
+      if (plan.kernel[c] == K_NONE) continue;
+      const kamera::ChanArgs a = chan_args(kv->ch[c], nullptr, c);
+      const hipError_t e = plan.kernel[c] == K_ROTATE ? kamera::launch_rotate_bf16(a, cm, stream)
+                                                      : kamera::launch_generic(a, cm, kv->dtype, stream);
+      if (e != hipSuccess) return hip_fail(e, "rotation launch");
+    }
+    return KAMERA_OK;
+  }
+  kamera::ChanArgs tuned[2];
+  int ntuned = 0;
+  for (int c = 0; c < kv->num_channels; ++c) {
+    kamera::ChanArgs a = chan_args(kv->ch[c], p, c);
+    if (plan.kernel[c] == K_MFMA) {
+      a.tasks_per_head = a.dim / 64;
+      const int ntask = a.heads * a.tasks_per_head;
+      a.groups = (ntask + plan.tasks_per_wave - 1) / plan.tasks_per_wave;
+      a.units = (int64_t)a.groups * cm.nranges;
+      tuned[ntuned++] = a;
+    } else {
+      const hipError_t e = kamera::launch_generic(a, cm, kv->dtype, stream);
+      if (e != hipSuccess) return hip_fail(e, "generic launch");
+    }
+  }
+  if (ntuned > 0) {
+    const hipError_t e = kamera::launch_relocate_patch_mfma(tuned, ntuned, cm, plan.tasks_per_wave, stream);
+    if (e != hipSuccess) return hip_fail(e, "relocate+patch launch");
+  }
+  return KAMERA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kamera_status kamera_relocate(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                              hipStream_t stream) {
+  return run(kv, chunks, nullptr, stream);
+}
+
+kamera_status kamera_relocate_patch(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                                    const kamera_patch* patch, hipStream_t stream) {
+  return run(kv, chunks, patch, stream);
+}
+
+kamera_status kamera_plan(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                          const kamera_patch* patch, kamera_plan_info* out) {
+  g_last_error.clear();
+  if (!out) return fail(KAMERA_E_NULL, "plan output is NULL");
+  memset(out, 0, sizeof *out);
+  Plan plan;
+  const kamera_status st = validate(kv, chunks, patch, &plan);
+  if (st != KAMERA_OK) return st;
+  out->kernel[0] = plan.kernel[0];
+  out->kernel[1] = plan.kernel[1];
+  out->launches = plan.launches;
+  out->tokens_per_unit = plan.range_tokens;
+  out->units = plan.units;
+  return KAMERA_OK;
+}
+
+const char* kamera_status_str(kamera_status s) {
+  switch (s) {
+    case KAMERA_OK: return "ok";
+    case KAMERA_E_NULL: return "null pointer";
+    case KAMERA_E_SHAPE: return "bad shape, stride, rank or rope_dim";
+    case KAMERA_E_UNSUPPORTED: return "unsupported dtype or pairing";
+    case KAMERA_E_ALIGN: return "misaligned pointer";
+    case KAMERA_E_ALIAS: return "factor memory overlaps KV memory";
+    case KAMERA_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* kamera_last_error(void) { return g_last_error.c_str(); }
+
+int kamera_abi_version(void) { return KAMERA_ABI_VERSION; }
+
+}  // extern "C"

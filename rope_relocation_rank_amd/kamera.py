@@ -1,0 +1,199 @@
+"""ctypes binding of libkamera.so (include/kamera.h): argument marshalling only.
+
+The entry points keep their C names: ``kamera_relocate``, ``kamera_relocate_patch``,
+``kamera_plan``, ``kamera_status_str``, ``kamera_last_error``, ``kamera_abi_version``.
+Descriptors are the ctypes mirrors of the C structs.  ``desc_from_tensors`` and the
+``relocate_`` / ``relocate_patch_`` helpers fill them from torch tensors (device
+memory and streams are all torch is used for); every step of the operator runs in
+the library's HIP kernels.  A missing library raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkamera.so")
+
+KAMERA_OK, KAMERA_E_NULL, KAMERA_E_SHAPE, KAMERA_E_UNSUPPORTED = 0, 1, 2, 3
+KAMERA_E_ALIGN, KAMERA_E_ALIAS, KAMERA_E_HIP = 4, 5, 6
+KAMERA_BF16, KAMERA_F32 = 0, 1
+KAMERA_NEOX_HALF = 0
+KAMERA_FLAG_GENERIC = 1
+KAMERA_MAX_RANK = 256
+KERNEL_NAMES = {0: "none", 1: "rotate", 2: "rotate+patch mfma", 3: "generic"}
+
+EXPORTED = ["kamera_relocate", "kamera_relocate_patch", "kamera_plan", "kamera_status_str",
+            "kamera_last_error", "kamera_abi_version"]
+
+
+class kamera_channel(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("heads", C.c_int32), ("dim", C.c_int32),
+                ("rope_dim", C.c_int32), ("reserved0", C.c_int32),
+                ("layer_stride", C.c_int64), ("slot_stride", C.c_int64),
+                ("head_stride", C.c_int64), ("page_stride", C.c_int64)]
+
+
+class kamera_kv_desc(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("num_layers", C.c_int32), ("num_channels", C.c_int32),
+                ("pairing", C.c_int32), ("ch", kamera_channel * 2), ("rope_theta", C.c_double),
+                ("page_size", C.c_int32), ("flags", C.c_uint32), ("num_pages", C.c_int64),
+                ("block_table", C.c_void_p)]
+
+
+class kamera_chunks(C.Structure):
+    _fields_ = [("num_chunks", C.c_int32), ("reserved0", C.c_int32),
+                ("total_tokens", C.c_int64), ("token_offsets", C.c_void_p),
+                ("delta", C.c_void_p)]
+
+
+class kamera_patch(C.Structure):
+    _fields_ = [("rank", C.c_int32), ("reserved0", C.c_int32),
+                ("U", C.c_void_p * 2), ("V", C.c_void_p * 2)]
+
+
+class kamera_plan_info(C.Structure):
+    _fields_ = [("kernel", C.c_int32 * 2), ("launches", C.c_int32),
+                ("tokens_per_unit", C.c_int32), ("units", C.c_int64)]
+
+
+class KameraError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"kamera status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+
+def lib():
+    """Load libkamera.so from the package directory (built by build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = C.CDLL(LIB_PATH)
+        L.kamera_relocate.restype = C.c_int
+        L.kamera_relocate.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks), C.c_void_p]
+        L.kamera_relocate_patch.restype = C.c_int
+        L.kamera_relocate_patch.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
+                                            C.POINTER(kamera_patch), C.c_void_p]
+        L.kamera_plan.restype = C.c_int
+        L.kamera_plan.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
+                                  C.POINTER(kamera_patch), C.POINTER(kamera_plan_info)]
+        L.kamera_status_str.restype = C.c_char_p
+        L.kamera_status_str.argtypes = [C.c_int]
+        L.kamera_last_error.restype = C.c_char_p
+        L.kamera_last_error.argtypes = []
+        L.kamera_abi_version.restype = C.c_int
+        L.kamera_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------- C entry points
+
+def kamera_relocate(kv: kamera_kv_desc, chunks: kamera_chunks, stream) -> int:
+    return lib().kamera_relocate(C.byref(kv), C.byref(chunks), stream)
+
+
+def kamera_relocate_patch(kv: kamera_kv_desc, chunks: kamera_chunks, patch, stream) -> int:
+    return lib().kamera_relocate_patch(C.byref(kv), C.byref(chunks),
+                                       None if patch is None else C.byref(patch), stream)
+
+
+def kamera_plan(kv, chunks, patch=None):
+    info = kamera_plan_info()
+    st = lib().kamera_plan(None if kv is None else C.byref(kv),
+                           None if chunks is None else C.byref(chunks),
+                           None if patch is None else C.byref(patch), C.byref(info))
+    return st, info
+
+
+def kamera_status_str(status: int) -> str:
+    return lib().kamera_status_str(status).decode()
+
+
+def kamera_last_error() -> str:
+    return lib().kamera_last_error().decode()
+
+
+def kamera_abi_version() -> int:
+    return lib().kamera_abi_version()
+
+
+def check(status: int) -> None:
+    if status != KAMERA_OK:
+        raise KameraError(status, kamera_last_error() or kamera_status_str(status))
+
+
+# ------------------------------------------------------------- torch helpers
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KAMERA_BF16
+    if t.dtype == torch.float32:
+        return KAMERA_F32
+    raise TypeError(f"unsupported KV dtype {t.dtype}")
+
+
+def channel(data, *, heads: int, dim: int, rope_dim: int, layer_stride: int,
+            slot_stride: int, head_stride: int, page_stride: int = 0,
+            element_offset: int = 0) -> kamera_channel:
+    """Channel view over a tensor's storage; strides in elements."""
+    c = kamera_channel()
+    c.data = data.data_ptr() + element_offset * data.element_size()
+    c.heads, c.dim, c.rope_dim, c.reserved0 = heads, dim, rope_dim, 0
+    c.layer_stride, c.slot_stride = layer_stride, slot_stride
+    c.head_stride, c.page_stride = head_stride, page_stride
+    return c
+
+
+def kv_desc(channels, *, dtype: int, num_layers: int, rope_theta: float, page_size: int = 0,
+            num_pages: int = 0, block_table=None, flags: int = 0) -> kamera_kv_desc:
+    d = kamera_kv_desc()
+    d.dtype, d.num_layers, d.num_channels = dtype, num_layers, len(channels)
+    d.pairing = KAMERA_NEOX_HALF
+    for i, c in enumerate(channels):
+        d.ch[i] = c
+    d.rope_theta = rope_theta
+    d.page_size, d.flags, d.num_pages = page_size, flags, num_pages
+    d.block_table = None if block_table is None else block_table.data_ptr()
+    return d
+
+
+def chunks_desc(offsets, delta, total_tokens: int) -> kamera_chunks:
+    """offsets: int64 device tensor [n+1]; delta: int64 device tensor [n]."""
+    c = kamera_chunks()
+    c.num_chunks = int(delta.numel())
+    c.reserved0 = 0
+    c.total_tokens = int(total_tokens)
+    c.token_offsets = offsets.data_ptr() if offsets.numel() else None
+    c.delta = delta.data_ptr() if delta.numel() else None
+    return c
+
+
+def patch_desc(rank: int, U=(None, None), V=(None, None)) -> kamera_patch:
+    p = kamera_patch()
+    p.rank, p.reserved0 = rank, 0
+    for i in range(2):
+        p.U[i] = None if U[i] is None else U[i].data_ptr()
+        p.V[i] = None if V[i] is None else V[i].data_ptr()
+    return p
+
+
+def current_stream():
+    import torch
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def relocate_patch_(kv: kamera_kv_desc, chunks: kamera_chunks, patch=None, stream=None) -> None:
+    """Enqueue the operator on `stream` (default: torch's current stream); raise on error."""
+    s = current_stream() if stream is None else stream
+    if patch is None or patch.rank == 0:
+        check(kamera_relocate(kv, chunks, s))
+    else:
+        check(kamera_relocate_patch(kv, chunks, patch, s))

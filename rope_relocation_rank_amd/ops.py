@@ -1,0 +1,52 @@
+"""Torch front end: builds the C descriptors for a problem held in torch tensors and
+enqueues the library call.  Argument marshalling only; the HIP kernels do all work."""
+from __future__ import annotations
+
+from . import kamera as K
+
+
+def descriptors(buffers, layouts, *, dtype_code: int, num_layers: int, theta: float,
+                offsets_t, delta_t, total_tokens: int, rank: int = 0, U=(), V=(),
+                page_size: int = 0, num_pages: int = 0, block_table_t=None, flags: int = 0):
+    """Descriptors for channels laid out as `layouts` (dicts with buffer, offset,
+    heads, dim, rope_dim and element strides) over the KV tensors in `buffers`."""
+    chans = []
+    for lay in layouts:
+        chans.append(K.channel(buffers[lay["buffer"]], heads=lay["heads"], dim=lay["dim"],
+                               rope_dim=lay["rope_dim"], layer_stride=lay["layer_stride"],
+                               slot_stride=lay["slot_stride"], head_stride=lay["head_stride"],
+                               page_stride=lay.get("page_stride", 0),
+                               element_offset=lay.get("offset", 0)))
+    kv = K.kv_desc(chans, dtype=dtype_code, num_layers=num_layers, rope_theta=theta,
+                   page_size=page_size, num_pages=num_pages, block_table=block_table_t,
+                   flags=flags)
+    ch = K.chunks_desc(offsets_t, delta_t, total_tokens)
+    Us = list(U) + [None] * (2 - len(U))
+    Vs = list(V) + [None] * (2 - len(V))
+    patch = K.patch_desc(rank, Us, Vs) if rank > 0 else None
+    return kv, ch, patch
+
+
+def descriptors_for(inp, flags: int = 0):
+    """Descriptors for a synth.Inputs instance."""
+    import torch
+    w = inp.workload
+    code = K.KAMERA_BF16 if inp.buffers[0].dtype == torch.bfloat16 else K.KAMERA_F32
+    return descriptors(inp.buffers, inp.layouts, dtype_code=code, num_layers=w.layers,
+                       theta=w.theta, offsets_t=inp.offsets_t, delta_t=inp.delta_t,
+                       total_tokens=inp.struct.total_tokens, rank=inp.rank, U=inp.U, V=inp.V,
+                       page_size=w.page_size, num_pages=inp.pool_pages,
+                       block_table_t=inp.block_table_t, flags=flags)
+
+
+def run(inp, stream=None, flags: int = 0) -> None:
+    """Apply the operator in place to the tensors of `inp` on `stream`."""
+    kv, ch, patch = descriptors_for(inp, flags)
+    K.relocate_patch_(kv, ch, patch, stream)
+
+
+def plan(inp, flags: int = 0):
+    kv, ch, patch = descriptors_for(inp, flags)
+    st, info = K.kamera_plan(kv, ch, patch)
+    K.check(st)
+    return info

@@ -1,0 +1,296 @@
+"""Seeded synthetic workloads: shapes, layouts, chunk structure and input values.
+
+This module holds no step of the operator.  It draws the inputs that both the HIP
+path and the CPU oracle consume, describes where every element lives (strides,
+block table), and counts the bytes an ideal in-place pass moves.
+
+Inputs stand in for real model KV of the named shapes (no weights or datasets are
+used).  Values: KV ~ N(0, 1); patch factors ~ N(0, s^2) with s^2 = 0.1 / sqrt(m),
+so every entry of U V^T has standard deviation 0.1 whatever m is; all drawn in fp32
+and rounded to the storage dtype.  Seeds derive from (workload id, kind, layer,
+channel) through numpy's SeedSequence; kind 0 = KV, 1 = U, 2 = V, 3 = structure.
+The structure stream draws chunk lengths, then deltas, then the block-table
+permutation, then outlier feature indices.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+KIND_KV, KIND_U, KIND_V, KIND_STRUCT = 0, 1, 2, 3
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    wid: int
+    family: str                 # "mha", "gqa" or "mla"
+    layers: int
+    heads: int                  # KV heads (1 for MLA)
+    head_dim: int               # GQA/MHA head dim; MLA latent width (c_KV)
+    theta: float
+    rank: int                   # patch rank of the patched pass
+    passes: tuple = (None,)     # ranks run per step; None = `rank`
+    tokens: int = 0             # fixed chunk length (single chunk) when chunk_len is None
+    n_chunks: int = 1
+    chunk_len: tuple | None = None   # (lo, hi) inclusive, drawn per chunk
+    delta: int = 0
+    delta_range: tuple | None = None  # (lo, hi) inclusive, drawn per chunk
+    rope_mla: int = 64          # MLA decoupled k_rope width
+    page_size: int = 0
+    pool_pages: int = 0         # pages per layer in the pool (paged only)
+    outliers: int = 0           # feature indices scaled by outlier_scale in K and V
+    outlier_scale: float = 8.0
+    dtype: str = "bf16"
+    note: str = ""
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def rank_passes(self) -> tuple:
+        return tuple(self.rank if r is None else r for r in self.passes)
+
+    @property
+    def elem_size(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+
+WORKLOADS = {
+    "tiny_mha": Workload(
+        key="tiny_mha", wid=0, family="mha", layers=1, heads=8, head_dim=64, theta=1e4,
+        rank=4, tokens=256, delta=37,
+        note="tiny MHA, 1 layer, T=256, 8 heads x 64, delta +37, rank-4 patch on K and V"),
+    "qwen25vl7b_segment": Workload(
+        key="qwen25vl7b_segment", wid=1, family="gqa", layers=28, heads=4, head_dim=128,
+        theta=1e6, rank=32, passes=(0, 32), tokens=4096, delta=-1536, outliers=4,
+        note="Qwen2.5-VL-7B-shaped video segment: 28 layers, 4 KV heads x 128, T=4096, "
+             "delta -1536; rotation-only pass then rank-32 patch pass"),
+    "llama3_8b_reorder": Workload(
+        key="llama3_8b_reorder", wid=2, family="gqa", layers=32, heads=8, head_dim=128,
+        theta=5e5, rank=16, n_chunks=64, chunk_len=(256, 2048), delta_range=(-32768, 32768),
+        note="Llama-3-8B-shaped reorder batch: 32 layers, 8 KV heads x 128, 64 chunks of "
+             "256..2048 tokens, per-chunk delta in [-32768, 32768], rank-16 per chunk"),
+    "deepseek_v3_mla": Workload(
+        key="deepseek_v3_mla", wid=3, family="mla", layers=61, heads=1, head_dim=512,
+        theta=1e4, rank=64, tokens=8192, delta=100000,
+        note="DeepSeek-V3-shaped MLA: 61 layers, rows c_KV(512) | k_rope(64), T=8192, "
+             "delta +100000, rank-64 on both channels"),
+    "long_video_72b_paged": Workload(
+        key="long_video_72b_paged", wid=4, family="gqa", layers=80, heads=8, head_dim=128,
+        theta=1e6, rank=64, tokens=32768, delta=65536, page_size=16, pool_pages=2048,
+        note="72B-shaped long-video paged cache: 80 layers, 8 KV heads x 128, T=32768 in "
+             "16-token pages scattered by a random block table, delta +65536, rank-64"),
+}
+
+
+def get(key: str) -> Workload:
+    return WORKLOADS[key]
+
+
+def seed_of(wid: int, kind: int, layer: int = 0, channel: int = 0) -> int:
+    ss = np.random.SeedSequence([wid, kind, layer, channel])
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
+def factor_std(m: int) -> float:
+    return math.sqrt(0.1 / math.sqrt(m)) if m > 0 else 0.0
+
+
+# ------------------------------------------------------------------ structure
+
+@dataclass
+class Structure:
+    offsets: np.ndarray            # int64 [n+1]
+    delta: np.ndarray              # int64 [n]
+    block_table: np.ndarray | None  # int32 [ceil(T / P)]
+    outlier_features: np.ndarray   # int64 [k]
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.offsets[-1])
+
+    @property
+    def num_chunks(self) -> int:
+        return int(self.delta.size)
+
+
+def structure(w: Workload) -> Structure:
+    rng = np.random.default_rng(np.random.SeedSequence([w.wid, KIND_STRUCT]))
+    if w.chunk_len is not None:
+        lens = rng.integers(w.chunk_len[0], w.chunk_len[1] + 1, size=w.n_chunks)
+    else:
+        lens = np.full(w.n_chunks, w.tokens, dtype=np.int64)
+    offsets = np.zeros(w.n_chunks + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(lens)
+    if w.delta_range is not None:
+        delta = rng.integers(w.delta_range[0], w.delta_range[1] + 1, size=w.n_chunks).astype(np.int64)
+    else:
+        delta = np.full(w.n_chunks, w.delta, dtype=np.int64)
+    T = int(offsets[-1])
+    bt = None
+    if w.page_size > 0:
+        need = -(-T // w.page_size)
+        pool = max(w.pool_pages, need)
+        bt = rng.permutation(pool)[:need].astype(np.int32)
+    F = feature_width(w)[0]
+    outl = np.sort(rng.choice(F, size=w.outliers, replace=False)) if w.outliers else np.zeros(0, np.int64)
+    return Structure(offsets, delta, bt, outl.astype(np.int64))
+
+
+# ------------------------------------------------------------------ layouts
+
+def feature_width(w: Workload) -> list:
+    """Feature width F = heads * dim of each channel."""
+    if w.family == "mla":
+        return [w.head_dim, w.rope_mla]
+    return [w.heads * w.head_dim, w.heads * w.head_dim]
+
+
+def channel_layouts(w: Workload, total_tokens: int, pool_pages: int = 0) -> list:
+    """Per channel: buffer index, element offset, heads, dim, rope_dim and strides."""
+    if w.family == "mla":
+        row = w.head_dim + w.rope_mla
+        ls = total_tokens * row
+        return [
+            dict(buffer=0, offset=0, heads=1, dim=w.head_dim, rope_dim=0, layer_stride=ls,
+                 slot_stride=row, head_stride=w.head_dim, page_stride=0),
+            dict(buffer=0, offset=w.head_dim, heads=1, dim=w.rope_mla, rope_dim=w.rope_mla,
+                 layer_stride=ls, slot_stride=row, head_stride=w.rope_mla, page_stride=0),
+        ]
+    H, D = w.heads, w.head_dim
+    if w.page_size > 0:
+        P = w.page_size
+        ps = P * H * D
+        return [dict(buffer=b, offset=0, heads=H, dim=D, rope_dim=D if b == 0 else 0,
+                     layer_stride=pool_pages * ps, slot_stride=H * D, head_stride=D,
+                     page_stride=ps) for b in (0, 1)]
+    return [dict(buffer=b, offset=0, heads=H, dim=D, rope_dim=D if b == 0 else 0,
+                 layer_stride=total_tokens * H * D, slot_stride=H * D, head_stride=D,
+                 page_stride=0) for b in (0, 1)]
+
+
+def buffer_shapes(w: Workload, total_tokens: int, pool_pages: int = 0) -> list:
+    """Shape of each KV buffer (MLA: one combined buffer; GQA/MHA: K and V)."""
+    if w.family == "mla":
+        return [(w.layers, total_tokens, w.head_dim + w.rope_mla)]
+    if w.page_size > 0:
+        return [(w.layers, pool_pages, w.page_size, w.heads, w.head_dim)] * 2
+    return [(w.layers, total_tokens, w.heads, w.head_dim)] * 2
+
+
+# ------------------------------------------------------------------ values
+
+@dataclass
+class Inputs:
+    """One problem instance.  All tensors live on `device`."""
+    workload: Workload
+    rank: int
+    struct: Structure
+    pool_pages: int
+    buffers: list                  # KV buffers (torch)
+    layouts: list                  # per channel layout dicts
+    U: list = field(default_factory=list)   # per channel [L][T][m] (torch) or []
+    V: list = field(default_factory=list)   # per channel [L][n][F][m]
+    offsets_t: object = None
+    delta_t: object = None
+    block_table_t: object = None
+
+
+def _torch_dtype(w: Workload):
+    import torch
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+def _normal(shape, seed: int, std: float, device, dtype):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(dtype)
+
+
+def make_inputs(w: Workload, rank: int, device="cpu", pass_id: int = 0) -> Inputs:
+    """Draw every input of one call.  `pass_id` shifts the seeds so that a second
+    pass of the same workload gets fresh values."""
+    import torch
+    st = structure(w)
+    T = st.total_tokens
+    pool = 0
+    if w.page_size > 0:
+        pool = max(w.pool_pages, -(-T // w.page_size))
+    dt = _torch_dtype(w)
+    wid = w.wid + 1000 * pass_id
+    shapes = buffer_shapes(w, T, pool)
+    buffers = []
+    for b, shp in enumerate(shapes):
+        buf = torch.empty(shp, dtype=dt, device=device)
+        for l in range(w.layers):
+            buf[l] = _normal(shp[1:], seed_of(wid, KIND_KV, l, b), 1.0, device, dt)
+        buffers.append(buf)
+    layouts = channel_layouts(w, T, pool)
+    if st.outlier_features.size and w.family != "mla":
+        idx = torch.as_tensor(st.outlier_features, device=device)
+        for buf in buffers:
+            flat = buf.view(w.layers, -1, w.heads * w.head_dim)
+            flat[:, :, idx] = flat[:, :, idx] * w.outlier_scale
+    U, V = [], []
+    if rank > 0:
+        s = factor_std(rank)
+        for c, F in enumerate(feature_width(w)):
+            u = torch.empty((w.layers, T, rank), dtype=dt, device=device)
+            v = torch.empty((w.layers, st.num_chunks, F, rank), dtype=dt, device=device)
+            for l in range(w.layers):
+                u[l] = _normal((T, rank), seed_of(wid, KIND_U, l, c), s, device, dt)
+                v[l] = _normal((st.num_chunks, F, rank), seed_of(wid, KIND_V, l, c), s, device, dt)
+            U.append(u)
+            V.append(v)
+    inp = Inputs(w, rank, st, pool, buffers, layouts, U, V)
+    inp.offsets_t = torch.as_tensor(st.offsets, device=device)
+    inp.delta_t = torch.as_tensor(st.delta, device=device)
+    if st.block_table is not None:
+        inp.block_table_t = torch.as_tensor(st.block_table, device=device)
+    return inp
+
+
+# ------------------------------------------------------------------ accounting
+
+def algorithmic_bytes(w: Workload, rank: int, total_tokens: int | None = None,
+                      num_chunks: int | None = None) -> int:
+    """Bytes an ideal in-place pass moves: every touched KV element read once and
+    written once, every factor element read once.  With rank 0 only the rotated
+    dims of rotating channels move (chunks with delta 0 would move nothing; no
+    workload here has one).  Block table, offsets and deltas are not counted."""
+    if total_tokens is None or num_chunks is None:
+        st = structure(w)
+        total_tokens, num_chunks = st.total_tokens, st.num_chunks
+    es = w.elem_size
+    T, L, n = total_tokens, w.layers, num_chunks
+    lay = channel_layouts(w, T, 0)
+    total = 0
+    for c in lay:
+        F = c["heads"] * c["dim"]
+        if rank == 0:
+            total += 2 * es * c["heads"] * c["rope_dim"] * T * L
+        else:
+            total += L * (2 * es * F * T + es * rank * T + es * F * rank * n)
+    return total
+
+
+def patch_flops(w: Workload, rank: int) -> int:
+    st = structure(w)
+    return sum(2 * rank * F * st.total_tokens * w.layers for F in feature_width(w))
+
+
+def patch_to_kv_ratio(w: Workload, rank: int) -> float:
+    """Bytes of the stored patch (U and V) over bytes of the segment's KV."""
+    st = structure(w)
+    es, T, n = w.elem_size, st.total_tokens, st.num_chunks
+    kv = sum(F * T * es for F in feature_width(w))
+    pat = sum(es * rank * (T + F * n) for F in feature_width(w))
+    return pat / kv

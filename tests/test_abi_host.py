@@ -1,0 +1,274 @@
+"""Host-side tests of the C ABI: load, exported symbols, struct layout, argument
+checks and kernel choice.  No kernel is launched: every call into an entry point
+that could launch is made with arguments the host checks reject (asserted first
+through kamera_plan), or with an empty problem."""
+import ctypes as C
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from rope_relocation_rank_amd import kamera as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kamera.h")
+
+FAKE = 0x7F0000000000  # 4 KiB-aligned address that is never dereferenced
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"KAMERA_API\s+[\w\s\*]+?\b(kamera_\w+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_every_declared_function():
+    L = K.lib()
+    names = header_functions()
+    assert set(names) == set(K.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+    assert not [e for e in exported if "launch" in e], "internal symbols leak"
+    assert K.kamera_abi_version() == 1
+
+
+def test_struct_layout_matches_header():
+    fields = {
+        "kamera_channel": [f[0] for f in K.kamera_channel._fields_],
+        "kamera_kv_desc": [f[0] for f in K.kamera_kv_desc._fields_],
+        "kamera_chunks": [f[0] for f in K.kamera_chunks._fields_],
+        "kamera_patch": [f[0] for f in K.kamera_patch._fields_],
+        "kamera_plan_info": [f[0] for f in K.kamera_plan_info._fields_],
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "kamera.h"', "int main(void){"]
+    for s, fs in fields.items():
+        lines.append(f'printf("{s} %zu\\n", sizeof({s}));')
+        for f in fs:
+            lines.append(f'printf("{s}.{f} %zu\\n", offsetof({s}, {f}));')
+    lines.append("return 0;}")
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "l.c"), os.path.join(d, "l")
+        open(src, "w").write("\n".join(lines))
+        subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    got = dict(l.rsplit(" ", 1) for l in out.splitlines())
+    for s, fs in fields.items():
+        cls = getattr(K, s)
+        assert int(got[s]) == C.sizeof(cls), s
+        for f in fs:
+            assert int(got[f"{s}.{f}"]) == getattr(cls, f).offset, f"{s}.{f}"
+
+
+# ----------------------------------------------------------------- descriptors
+
+class FakeTensor:
+    def __init__(self, addr, es=2):
+        self.addr, self.es = addr, es
+
+    def data_ptr(self):
+        return self.addr
+
+    def element_size(self):
+        return self.es
+
+    def numel(self):
+        return 1
+
+
+def gqa(T=4096, L=28, H=4, D=128, r=128, m=32, dtype=K.KAMERA_BF16, kv_addr=FAKE,
+        paged=False, pages=0, flags=0, n=1):
+    es = 2 if dtype == K.KAMERA_BF16 else 4
+    chans = []
+    for c in range(2):
+        base = kv_addr + c * (1 << 36)
+        chans.append(K.channel(FakeTensor(base, es), heads=H, dim=D, rope_dim=r if c == 0 else 0,
+                               layer_stride=(pages * 16 if paged else T) * H * D,
+                               slot_stride=H * D, head_stride=D,
+                               page_stride=16 * H * D if paged else 0))
+    kv = K.kv_desc(chans, dtype=dtype, num_layers=L, rope_theta=1e6,
+                   page_size=16 if paged else 0, num_pages=pages,
+                   block_table=FakeTensor(FAKE + (1 << 40)) if paged else None, flags=flags)
+    ch = K.kamera_chunks()
+    ch.num_chunks, ch.total_tokens = n, T
+    ch.token_offsets, ch.delta = FAKE + (3 << 38), FAKE + (3 << 38) + 4096
+    p = K.patch_desc(m) if m else None
+    if m:
+        for c in range(2):
+            p.U[c] = FAKE + (1 << 39) + c * (1 << 34)
+            p.V[c] = FAKE + (1 << 39) + (1 << 33) + c * (1 << 34)
+    return kv, ch, p
+
+
+def plan_names(kv, ch, p):
+    st, info = K.kamera_plan(kv, ch, p)
+    assert st == K.KAMERA_OK, K.kamera_last_error()
+    return [K.KERNEL_NAMES[k] for k in info.kernel], info
+
+
+def expect_status(status, kv, ch, p=None):
+    st, _ = K.kamera_plan(kv, ch, p)
+    assert st == status, (st, K.kamera_last_error())
+    assert K.kamera_last_error()
+    # The entry points reject the same arguments before any HIP call.
+    assert K.kamera_relocate_patch(kv, ch, p, None) == status
+    if p is None or p.rank == 0:
+        assert K.kamera_relocate(kv, ch, None) == status
+
+
+# ----------------------------------------------------------------- argument checks
+
+def test_null_descriptors():
+    kv, ch, p = gqa()
+    st, _ = K.kamera_plan(None, ch, p)
+    assert st == K.KAMERA_E_NULL
+    st, _ = K.kamera_plan(kv, None, p)
+    assert st == K.KAMERA_E_NULL
+    assert K.lib().kamera_relocate(None, None, None) == K.KAMERA_E_NULL
+    assert "NULL" in K.kamera_last_error()
+
+
+def test_bad_dtype_and_pairing():
+    kv, ch, p = gqa()
+    kv.dtype = 7
+    expect_status(K.KAMERA_E_UNSUPPORTED, kv, ch, p)
+    kv, ch, p = gqa()
+    kv.pairing = 1
+    expect_status(K.KAMERA_E_UNSUPPORTED, kv, ch, p)
+
+
+@pytest.mark.parametrize("mutate", [
+    lambda kv, ch, p: setattr(kv, "num_channels", 0),
+    lambda kv, ch, p: setattr(kv, "num_channels", 3),
+    lambda kv, ch, p: setattr(kv, "num_layers", -1),
+    lambda kv, ch, p: setattr(kv.ch[0], "heads", 0),
+    lambda kv, ch, p: setattr(kv.ch[1], "dim", 0),
+    lambda kv, ch, p: setattr(kv.ch[0], "rope_dim", 127),
+    lambda kv, ch, p: setattr(kv.ch[0], "rope_dim", 130),
+    lambda kv, ch, p: setattr(kv.ch[0], "rope_dim", -2),
+    lambda kv, ch, p: setattr(kv.ch[1], "slot_stride", -8),
+    lambda kv, ch, p: setattr(kv.ch[0], "reserved0", 1),
+    lambda kv, ch, p: setattr(kv, "flags", 2),
+    lambda kv, ch, p: setattr(kv, "rope_theta", 0.0),
+    lambda kv, ch, p: setattr(kv, "rope_theta", float("nan")),
+    lambda kv, ch, p: setattr(kv, "page_size", -1),
+    lambda kv, ch, p: setattr(p, "rank", 257),
+    lambda kv, ch, p: setattr(p, "rank", -1),
+    lambda kv, ch, p: setattr(p, "reserved0", 3),
+    lambda kv, ch, p: setattr(ch, "num_chunks", 0),
+    lambda kv, ch, p: setattr(ch, "num_chunks", -1),
+    lambda kv, ch, p: setattr(ch, "total_tokens", -5),
+    lambda kv, ch, p: setattr(ch, "reserved0", 1),
+])
+def test_shape_errors(mutate):
+    kv, ch, p = gqa()
+    mutate(kv, ch, p)
+    expect_status(K.KAMERA_E_SHAPE, kv, ch, p)
+
+
+@pytest.mark.parametrize("mutate", [
+    lambda kv, ch, p: setattr(kv.ch[0], "data", None),
+    lambda kv, ch, p: p.U.__setitem__(1, None),
+    lambda kv, ch, p: p.V.__setitem__(0, None),
+    lambda kv, ch, p: setattr(ch, "token_offsets", None),
+    lambda kv, ch, p: setattr(ch, "delta", None),
+])
+def test_null_pointers(mutate):
+    kv, ch, p = gqa()
+    mutate(kv, ch, p)
+    expect_status(K.KAMERA_E_NULL, kv, ch, p)
+
+
+def test_paged_without_table_or_pages():
+    kv, ch, p = gqa(paged=True, pages=256)
+    kv.block_table = None
+    expect_status(K.KAMERA_E_NULL, kv, ch, p)
+    kv, ch, p = gqa(paged=True, pages=256)
+    kv.num_pages = 0
+    expect_status(K.KAMERA_E_SHAPE, kv, ch, p)
+
+
+def test_misaligned_pointers():
+    kv, ch, p = gqa()
+    kv.ch[0].data = FAKE + 1
+    expect_status(K.KAMERA_E_ALIGN, kv, ch, p)
+    kv, ch, p = gqa(dtype=K.KAMERA_F32)
+    kv.ch[1].data = FAKE + (1 << 36) + 2
+    expect_status(K.KAMERA_E_ALIGN, kv, ch, p)
+    kv, ch, p = gqa()
+    p.U[0] = p.U[0] + 1
+    expect_status(K.KAMERA_E_ALIGN, kv, ch, p)
+    kv, ch, p = gqa()
+    ch.delta = ch.delta + 4
+    expect_status(K.KAMERA_E_ALIGN, kv, ch, p)
+
+
+def test_factors_overlapping_kv():
+    kv, ch, p = gqa(T=4096, L=2)
+    p.U[0] = kv.ch[1].data + 1024  # inside V's KV range
+    expect_status(K.KAMERA_E_ALIAS, kv, ch, p)
+    kv, ch, p = gqa(T=4096, L=2)
+    p.V[1] = kv.ch[0].data + 2 * (2 * 4096 * 4 * 128) - 64  # tail of K's last layer
+    expect_status(K.KAMERA_E_ALIAS, kv, ch, p)
+
+
+def test_empty_problems_are_ok_without_launch():
+    for L, T, n in [(0, 4096, 1), (28, 0, 0), (28, 0, 3)]:
+        kv, ch, p = gqa(L=L, T=T, n=n)
+        ch.total_tokens = T
+        st, info = K.kamera_plan(kv, ch, p)
+        assert st == K.KAMERA_OK and info.launches == 0
+        assert K.kamera_relocate_patch(kv, ch, p, None) == K.KAMERA_OK
+        assert K.kamera_relocate(kv, ch, None) == K.KAMERA_OK
+
+
+def test_status_strings():
+    for s in range(7):
+        assert K.kamera_status_str(s)
+    assert K.kamera_status_str(99) == "unknown status"
+
+
+# ----------------------------------------------------------------- kernel choice
+
+def test_kernel_choice():
+    names, info = plan_names(*gqa(m=32))
+    assert names == ["rotate+patch mfma"] * 2 and info.launches == 1
+    names, info = plan_names(*gqa(m=0))
+    assert names == ["rotate", "none"] and info.launches == 1
+    names, _ = plan_names(*gqa(D=96, r=96, m=8))
+    assert names == ["generic", "generic"]
+    names, _ = plan_names(*gqa(D=128, r=32, m=8))
+    assert names == ["generic", "rotate+patch mfma"]
+    names, _ = plan_names(*gqa(D=128, r=32, m=0))
+    assert names == ["rotate", "none"]
+    names, _ = plan_names(*gqa(D=128, r=48, m=0))
+    assert names == ["generic", "none"]
+    names, _ = plan_names(*gqa(dtype=K.KAMERA_F32, m=8))
+    assert names == ["generic", "generic"]
+    names, _ = plan_names(*gqa(flags=K.KAMERA_FLAG_GENERIC, m=8))
+    assert names == ["generic", "generic"]
+    names, _ = plan_names(*gqa(m=129))
+    assert names == ["generic", "generic"]
+    names, _ = plan_names(*gqa(m=128))
+    assert names == ["rotate+patch mfma"] * 2
+    kv, ch, p = gqa(m=8)
+    kv.ch[0].data = FAKE + 2  # element-aligned but not 16-byte aligned
+    names, info = plan_names(kv, ch, p)
+    assert names == ["generic", "rotate+patch mfma"] and info.launches == 2
+    names, _ = plan_names(*gqa(paged=True, pages=256, m=64))
+    assert names == ["rotate+patch mfma"] * 2
+
+
+def test_mfma_unit_count():
+    # One wavefront unit = one 64-feature task of one channel over tokens_per_unit tokens.
+    kv, ch, p = gqa(T=32768, L=80, H=8, D=128, m=64, paged=True, pages=2048)
+    names, info = plan_names(kv, ch, p)
+    rt = info.tokens_per_unit
+    assert rt % 16 == 0
+    assert info.units == 80 * 2 * (8 * 128 // 64) * (-(-32768 // rt))
