@@ -1,0 +1,269 @@
+"""Throughput of the Kamera relocate + patch operator on one MI355X.
+
+One step = one pass of the whole operator over one batch of synthetic input.  The
+default workload is the Qwen2.5-VL-7B-shaped video segment (28 layers, 4 KV heads x
+128, 4096 tokens, delta -1536, theta 1e6): a rotation-only pass (m = 0, keys only)
+followed by a rank-32 relocate+patch pass on K and V.  Inputs are resident in HBM
+before the timed region; steps cycle through `--copies` independent input copies
+(about 2 GB) so that no step finds its data in the 256 MB last-level cache.
+
+Prints one JSON line.  value = algorithmic bytes moved per step (every touched KV
+element read once and written once, every factor element read once) x steps / wall
+time, in GB/s (1e9).  roofline = the dominant kernel (the relocate+patch launch)
+timed with HIP events on its stream.  cpu_baseline = the fp64 CPU oracle on the host
+cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "relocate+patch GB/s (read+write) and % HBM peak; tokens relocated/s"
+KERNEL_SRC = os.path.join(ROOT, "rope_relocation_rank_amd", "csrc", "kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str, bytes_per_launch: int):
+    """Measured HBM bytes per launch of the dominant kernel from committed counter
+    summaries (FETCH_SIZE and WRITE_SIZE, scaled by a copy-kernel calibration); None
+    when absent or when the kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return int(round((d["fetch_kib"] * d["fetch_scale"] + d["write_kib"] * d["write_scale"]) * 1024))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="qwen25vl7b_segment")
+    ap.add_argument("--copies", type=int, default=0, help="input copies (0 = enough for >= 2 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=1024)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the operator "
+              "needs no collective, and every run here uses a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from rope_relocation_rank_amd import kamera as K
+    from rope_relocation_rank_amd import ops, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K.lib()
+    dev = torch.device("cuda:0")
+    w = synth.get(args.workload)
+    ranks = w.rank_passes
+    dominant = max(range(len(ranks)), key=lambda i: synth.algorithmic_bytes(w, ranks[i]))
+    bytes_pass = [synth.algorithmic_bytes(w, r) for r in ranks]
+    bytes_step = sum(bytes_pass)
+    per_copy = max(bytes_pass)
+    copies = args.copies or max(1, min(16, -(-2_000_000_000 // per_copy)))
+    print(f"[bench] workload {w.key}: {w.note}", file=sys.stderr, flush=True)
+    print(f"[bench] passes m={list(ranks)} bytes/step={bytes_step} copies={copies}",
+          file=sys.stderr, flush=True)
+
+    # Inputs: one instance per (pass, copy); copies share values (the traffic does not
+    # depend on them) but live at distinct addresses.
+    insts = []
+    for pi, r in enumerate(ranks):
+        base = synth.make_inputs(w, r, device=dev, pass_id=pi)
+        row = [base]
+        for _ in range(copies - 1):
+            c = synth.Inputs(base.workload, base.rank, base.struct, base.pool_pages,
+                             [b.clone() for b in base.buffers], base.layouts,
+                             [u.clone() for u in base.U], [v.clone() for v in base.V],
+                             base.offsets_t, base.delta_t, base.block_table_t)
+            row.append(c)
+        insts.append(row)
+    descs = [[ops.descriptors_for(c) for c in row] for row in insts]
+    plan_info = [ops.plan(row[0]) for row in insts]
+    lib = K.lib()
+    import ctypes as C
+
+    stream = torch.cuda.current_stream(dev)
+    s_ptr = C.c_void_p(stream.cuda_stream)
+
+    def launch(pi, ci):
+        kv, ch, p = descs[pi][ci]
+        if p is None:
+            st = lib.kamera_relocate(C.byref(kv), C.byref(ch), s_ptr)
+        else:
+            st = lib.kamera_relocate_patch(C.byref(kv), C.byref(ch), C.byref(p), s_ptr)
+        if st != 0:
+            raise K.KameraError(st, K.kamera_last_error())
+
+    # Copy-kernel reference of known size (also the counter calibration point).
+    nb = args.copy_calibration_mib << 20
+    src = torch.empty(nb, dtype=torch.uint8, device=dev).random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    # Warmup.
+    for s in range(args.warmup):
+        for pi in range(len(ranks)):
+            launch(pi, s % copies)
+    torch.cuda.synchronize()
+
+    # Timed region: events bracket every launch of every pass on the launch stream.
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)] for _ in ranks]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for pi in range(len(ranks)):
+            a, b = ev[pi][s]
+            a.record(stream)
+            launch(pi, s % copies)
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pass_ms = [sum(a.elapsed_time(b) for a, b in ev[pi]) / args.steps for pi in range(len(ranks))]
+
+    ms_step = wall * 1e3 / args.steps
+    value = bytes_step * args.steps / wall / 1e9
+    dom_ms = pass_ms[dominant]
+    achieved = bytes_pass[dominant] / (dom_ms * 1e-3) / 1e9
+    traffic = load_traffic(w.key, bytes_pass[dominant])
+    st = synth.structure(w)
+    tokens_step = st.total_tokens * len(ranks)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, ranks, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.key,
+            "description": w.note,
+            "layers": w.layers, "kv_heads": w.heads, "head_dim": w.head_dim,
+            "tokens": st.total_tokens, "chunks": st.num_chunks,
+            "theta": w.theta, "passes_rank": list(ranks), "page_size": w.page_size,
+            "bytes_per_step": bytes_step, "input_copies": copies,
+            "parallelism": "single GPU",
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "tokens_relocated_per_s": round(tokens_step * args.steps / wall, 1),
+        "pass_kernel_ms": [round(x, 5) for x in pass_ms],
+        "pass_gbps": [round(bytes_pass[i] / (pass_ms[i] * 1e-3) / 1e9, 1) for i in range(len(ranks))],
+        "kernels": [[K.KERNEL_NAMES[k] for k in pi.kernel] for pi in plan_info],
+        "copy_kernel_gbps": round(copy_gbps, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "relocate_patch_mfma" if ranks[dominant] > 0 else "rotate_bf16",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": bytes_pass[dominant],
+            "avg_launch_ms": round(dom_ms, 5),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, ranks, seconds: float):
+    """The fp64 oracle on the host cores over a bounded sample of the same workload:
+    whole steps (every pass, every layer, every token) repeated until `seconds` of
+    compute have passed; for workloads too large for that, leading layers only."""
+    import numpy as np
+    import torch
+
+    from oracle import oracle as orc
+    from rope_relocation_rank_amd import synth
+
+    print("[bench] cpu baseline: oracle on host cores", file=sys.stderr, flush=True)
+
+    def prepare(ww):
+        probs = []
+        for pi, r in enumerate(ranks):
+            inp = synth.make_inputs(ww, r, device="cpu", pass_id=pi)
+            bufs = [b.view(torch.int16).numpy().view(np.uint16).ravel() for b in inp.buffers]
+            chans = []
+            for c, lay in enumerate(inp.layouts):
+                d = dict(lay)
+                d["data"] = bufs[lay["buffer"]]
+                if r > 0:
+                    d["U"] = inp.U[c].view(torch.int16).numpy().view(np.uint16)
+                    d["V"] = inp.V[c].view(torch.int16).numpy().view(np.uint16)
+                chans.append(d)
+            probs.append((r, inp, chans))
+        return probs
+
+    def step(ww, probs):
+        t0 = time.perf_counter()
+        for r, inp, chans in probs:
+            orc.relocate_patch(chans, num_layers=ww.layers, theta=w.theta,
+                               offsets=inp.struct.offsets, delta=inp.struct.delta, rank=r,
+                               page_size=w.page_size, block_table=inp.struct.block_table)
+        return time.perf_counter() - t0
+
+    # One layer first, to size the sample.
+    w1 = w.with_(layers=1)
+    t1 = step(w1, prepare(w1))
+    layers = int(max(1, min(w.layers, seconds / max(t1, 1e-6))))
+    ww = w.with_(layers=layers)
+    probs = prepare(ww)
+    reps, t = 0, 0.0
+    while reps < 10 and (reps == 0 or t < seconds):
+        t += step(ww, probs)
+        reps += 1
+    b = reps * sum(synth.algorithmic_bytes(ww, r) for r in ranks)
+    return {
+        "value": round(b / t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": orc.num_threads(),
+        "kind": "oracle",
+        "sample": f"{reps} x ({layers} of {w.layers} layers of every pass m={list(ranks)}, all "
+                  f"tokens); {t:.1f} s of compute, input generation excluded",
+    }
+
+
+if __name__ == "__main__":
+    main()

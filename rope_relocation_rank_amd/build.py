@@ -17,6 +17,8 @@ FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared", "-fvisibility=hidden",
     # packed fp32 VALU ops stay off: the compiler must not form v_pk_* fp32 ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators stay in VGPRs (no AGPR copies around every MFMA)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-result",
 ]
 

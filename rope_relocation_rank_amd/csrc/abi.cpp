@@ -5,7 +5,9 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "kamera.h"
@@ -31,7 +33,6 @@ enum Kernel { K_NONE = 0, K_ROTATE = 1, K_MFMA = 2, K_GENERIC = 3 };
 
 constexpr int kMfmaMaxRank = 128;
 constexpr int64_t kMaxTunedTokens = (int64_t)1 << 30;  // token ids stay in 32 bits
-constexpr int64_t kTargetWaves = 256 * 16;              // 256 CUs, 16 wavefronts each
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -56,44 +57,61 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
 }
 
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v && *v ? atoi(v) : dflt;
+}
+
 struct Plan {
   int kernel[2] = {K_NONE, K_NONE};
   int launches = 0;
-  int range_tokens = 0;
-  int tasks_per_wave = 0;
-  int64_t units = 0;
-  bool mfma_both = false;
+  int block_tokens = 0;
+  int tiles_per_wave = 0;
+  int rotate_unroll = 2;
+  int tile_unroll = 1;
+  int64_t units = 0;  // workgroups of the tuned launch(es)
 };
 
+bool strides_ok(const kamera_channel& c) {
+  return c.layer_stride % 8 == 0 && c.slot_stride % 8 == 0 && c.head_stride % 8 == 0 &&
+         c.page_stride % 8 == 0;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Largest element offset inside one layer that a channel can touch, plus one.
+__int128 layer_extent(const kamera_channel& c, int64_t T, int32_t page_size, int64_t pages) {
+  __int128 last = (__int128)(c.heads - 1) * c.head_stride + (c.dim - 1);
+  if (page_size > 0)
+    last += (__int128)(pages - 1) * c.page_stride + (__int128)(page_size - 1) * c.slot_stride;
+  else
+    last += (__int128)(T - 1) * c.slot_stride;
+  return last + 1;
+}
+
+// Rotation-only kernel: 16-byte lanes over the rotated dims of each row.
 bool rotate_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, int64_t T) {
   const int r = c.rope_dim;
-  const bool shape = r % 16 == 0 && (r == 16 || r == 32 || r == 64 || r == 128 || r == 256);
-  return kv.dtype == KAMERA_BF16 && !(kv.flags & KAMERA_FLAG_GENERIC) && shape &&
-         T < kMaxTunedTokens && aligned(c.data, 16) && c.layer_stride % 8 == 0 &&
-         c.slot_stride % 8 == 0 && c.head_stride % 8 == 0 && c.page_stride % 8 == 0;
+  return kv.dtype == KAMERA_BF16 && !(kv.flags & KAMERA_FLAG_GENERIC) &&
+         (r == 16 || r == 32 || r == 64 || r == 128) && T < kMaxTunedTokens &&
+         aligned(c.data, 16) && strides_ok(c);
 }
 
+// Rotate+patch kernel: 128-feature blocks hold whole heads (or whole blocks of one
+// head), a NeoX partner sits r/16 lanes away, rank <= 128.
 bool mfma_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, const kamera_patch& p,
                    int ci, int64_t T) {
+  const int r = c.rope_dim, D = c.dim;
+  const bool rope_ok = r == 0 || ((r == 16 || r == 32 || r == 64 || r == 128) && D % r == 0);
+  const bool dim_ok = D % 8 == 0 && (D % 128 == 0 || 128 % D == 0);
+  // row offsets inside a layer are kept in 32 bits
+  const bool extent_ok = layer_extent(c, T, kv.page_size, kv.num_pages) < ((__int128)1 << 31);
   return kv.dtype == KAMERA_BF16 && !(kv.flags & KAMERA_FLAG_GENERIC) && p.rank <= kMfmaMaxRank &&
-         c.dim % 64 == 0 && c.rope_dim % 64 == 0 && T < kMaxTunedTokens && aligned(c.data, 16) &&
-         aligned(p.U[ci], 16) && aligned(p.V[ci], 16) && c.layer_stride % 8 == 0 &&
-         c.slot_stride % 8 == 0 && c.head_stride % 8 == 0 && c.page_stride % 8 == 0 &&
-         (int64_t)c.heads * c.dim < (1 << 24);
+         rope_ok && dim_ok && extent_ok && T < kMaxTunedTokens && aligned(c.data, 16) &&
+         aligned(p.U[ci], 16) && aligned(p.V[ci], 16) && strides_ok(c) &&
+         (int64_t)c.heads * D < (1 << 24);
 }
 
-// Wavefront units for a given tokens-per-unit.
-int64_t mfma_units(const kamera_kv_desc& kv, const kamera_chunks& ch, int nt, int rt,
-                   const bool* use) {
-  const int64_t nranges = (ch.total_tokens + rt - 1) / rt;
-  int64_t u = 0;
-  for (int c = 0; c < kv.num_channels; ++c) {
-    if (!use[c]) continue;
-    const int64_t tasks = (int64_t)kv.ch[c].heads * (kv.ch[c].dim / 64);
-    u += (tasks + nt - 1) / nt * nranges;
-  }
-  return u * kv.num_layers;
-}
 
 // Checks every host-visible argument.  No HIP call is made here.
 kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamera_patch* p,
@@ -184,14 +202,22 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
   if (empty) return KAMERA_OK;
   const int64_t T = ch->total_tokens;
   if (m == 0) {
-    int64_t rt = 256;
-    while (rt > 16 && (int64_t)kv->num_layers * ((T + rt - 1) / rt) < kTargetWaves) rt /= 2;
-    plan->range_tokens = (int)rt;
     for (int c = 0; c < kv->num_channels; ++c) {
-      if (kv->ch[c].rope_dim == 0) continue;
-      plan->kernel[c] = rotate_tuned_ok(*kv, kv->ch[c], T) ? K_ROTATE : K_GENERIC;
+      const kamera_channel& k = kv->ch[c];
+      if (k.rope_dim == 0) continue;
+      plan->kernel[c] = rotate_tuned_ok(*kv, k, T) ? K_ROTATE : K_GENERIC;
       plan->launches++;
-      if (plan->kernel[c] == K_ROTATE) plan->units += (int64_t)kv->num_layers * ((T + rt - 1) / rt);
+      if (plan->kernel[c] == K_ROTATE) {
+        // A workgroup covers 4 waves x `unroll` row groups of 64 / (rope_dim / 8) rows.
+        int unroll = env_int("KAMERA_ROTATE_UNROLL", 4);
+        if (unroll != 1 && unroll != 2 && unroll != 4) unroll = 4;
+        const int rows = 4 * unroll * (64 / (k.rope_dim / 8));
+        const int bt = (int)std::min<int64_t>(kamera::kMaxBlockTokens,
+                                              std::max<int64_t>(1, rows / k.heads));
+        plan->rotate_unroll = unroll;
+        plan->block_tokens = bt;
+        plan->units += (int64_t)kv->num_layers * ceil_div(T, bt);
+      }
     }
     return KAMERA_OK;
   }
@@ -203,18 +229,21 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
   }
   if (use[0] || use[1]) {
     plan->launches++;
-    const int mk = (m + 31) / 32;
-    plan->tasks_per_wave = 1;
-    (void)mk;
-    int64_t rt = 256;
-    while (rt > 16 && mfma_units(*kv, *ch, plan->tasks_per_wave, (int)rt, use) < kTargetWaves) rt /= 2;
-    plan->range_tokens = (int)rt;
-    plan->units = mfma_units(*kv, *ch, plan->tasks_per_wave, (int)rt, use);
+    // Each of the 4 wavefronts of a workgroup streams `tpw` 16-token tiles.
+    int tpw = env_int("KAMERA_TILES_PER_WAVE", 4);
+    if (tpw < 1 || tpw > kamera::kMaxBlockTokens / 64) tpw = 4;
+    plan->tiles_per_wave = tpw;
+    plan->tile_unroll = env_int("KAMERA_TILE_UNROLL", 1) == 2 ? 2 : 1;
+    plan->block_tokens = 64 * tpw;
+    for (int c = 0; c < kv->num_channels; ++c)
+      if (use[c])
+        plan->units += (int64_t)kv->num_layers * ceil_div(T, plan->block_tokens) *
+                       ceil_div((int64_t)kv->ch[c].heads * kv->ch[c].dim, 128);
   }
   return KAMERA_OK;
 }
 
-kamera::CommonArgs common_args(const kamera_kv_desc& kv, const kamera_chunks& ch, int m, int rt) {
+kamera::CommonArgs common_args(const kamera_kv_desc& kv, const kamera_chunks& ch, int m, int bt) {
   kamera::CommonArgs a;
   memset(&a, 0, sizeof a);
   a.offsets = ch.token_offsets;
@@ -222,17 +251,21 @@ kamera::CommonArgs common_args(const kamera_kv_desc& kv, const kamera_chunks& ch
   a.block_table = kv.block_table;
   a.total_tokens = ch.total_tokens;
   a.num_pages = kv.num_pages;
-  a.range_tokens = rt > 0 ? rt : 256;
-  a.nranges = (ch.total_tokens + a.range_tokens - 1) / a.range_tokens;
+  a.block_tokens = bt > 0 ? bt : 64;
+  a.token_groups = ceil_div(ch.total_tokens, a.block_tokens);
   a.theta = kv.rope_theta;
   a.num_chunks = ch.num_chunks;
   a.page_size = kv.page_size;
   a.num_layers = kv.num_layers;
   a.rank = m;
+  a.page_shift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if (kv.page_size == (1 << sh)) a.page_shift = sh;
   return a;
 }
 
-kamera::ChanArgs chan_args(const kamera_channel& c, const kamera_patch* p, int ci) {
+kamera::ChanArgs chan_args(const kamera_kv_desc& kv, int ci, const kamera_patch* p) {
+  const kamera_channel& c = kv.ch[ci];
   kamera::ChanArgs a;
   memset(&a, 0, sizeof a);
   a.data = c.data;
@@ -245,6 +278,10 @@ kamera::ChanArgs chan_args(const kamera_channel& c, const kamera_patch* p, int c
   a.heads = c.heads;
   a.dim = c.dim;
   a.rope_dim = c.rope_dim;
+  // Pair frequencies theta^(-2i/r) in fp64, the same expression the reference form uses.
+  const int half = c.rope_dim / 2;
+  for (int i = 0; i < half && i < kamera::kMaxTunedHalf; ++i)
+    a.omega[i] = pow(kv.rope_theta, -2.0 * (double)i / (double)c.rope_dim);
   return a;
 }
 
@@ -259,12 +296,13 @@ kamera_status run(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamer
   kamera_status st = validate(kv, ch, p, &plan);
   if (st != KAMERA_OK || plan.launches == 0) return st;
   const int m = p ? p->rank : 0;
-  const kamera::CommonArgs cm = common_args(*kv, *ch, m, plan.range_tokens);
+  const kamera::CommonArgs cm = common_args(*kv, *ch, m, plan.block_tokens);
   if (m == 0) {
     for (int c = 0; c < kv->num_channels; ++c) {
       if (plan.kernel[c] == K_NONE) continue;
-      const kamera::ChanArgs a = chan_args(kv->ch[c], nullptr, c);
-      const hipError_t e = plan.kernel[c] == K_ROTATE ? kamera::launch_rotate_bf16(a, cm, stream)
+      const kamera::ChanArgs a = chan_args(*kv, c, nullptr);
+      const hipError_t e = plan.kernel[c] == K_ROTATE
+                               ? kamera::launch_rotate_rows(a, cm, plan.rotate_unroll, stream)
                                                       : kamera::launch_generic(a, cm, kv->dtype, stream);
       if (e != hipSuccess) return hip_fail(e, "rotation launch");
     }
@@ -273,12 +311,10 @@ kamera_status run(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamer
   kamera::ChanArgs tuned[2];
   int ntuned = 0;
   for (int c = 0; c < kv->num_channels; ++c) {
-    kamera::ChanArgs a = chan_args(kv->ch[c], p, c);
+    kamera::ChanArgs a = chan_args(*kv, c, p);
     if (plan.kernel[c] == K_MFMA) {
-      a.tasks_per_head = a.dim / 64;
-      const int ntask = a.heads * a.tasks_per_head;
-      a.groups = (ntask + plan.tasks_per_wave - 1) / plan.tasks_per_wave;
-      a.units = (int64_t)a.groups * cm.nranges;
+      a.fblocks = (int)ceil_div((int64_t)a.heads * a.dim, 128);
+      a.blocks = cm.token_groups * a.fblocks;
       tuned[ntuned++] = a;
     } else {
       const hipError_t e = kamera::launch_generic(a, cm, kv->dtype, stream);
@@ -286,7 +322,8 @@ kamera_status run(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamer
     }
   }
   if (ntuned > 0) {
-    const hipError_t e = kamera::launch_relocate_patch_mfma(tuned, ntuned, cm, plan.tasks_per_wave, stream);
+    const hipError_t e =
+        kamera::launch_relocate_patch_rows(tuned, ntuned, cm, plan.tile_unroll, stream);
     if (e != hipSuccess) return hip_fail(e, "relocate+patch launch");
   }
   return KAMERA_OK;
@@ -317,7 +354,7 @@ kamera_status kamera_plan(const kamera_kv_desc* kv, const kamera_chunks* chunks,
   out->kernel[0] = plan.kernel[0];
   out->kernel[1] = plan.kernel[1];
   out->launches = plan.launches;
-  out->tokens_per_unit = plan.range_tokens;
+  out->tokens_per_unit = plan.block_tokens;
   out->units = plan.units;
   return KAMERA_OK;
 }

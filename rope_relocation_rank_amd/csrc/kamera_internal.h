@@ -6,6 +6,9 @@
 
 namespace kamera {
 
+constexpr int kMaxTunedHalf = 64;     // tuned kernels rotate at most 128 dims per head
+constexpr int kMaxBlockTokens = 512;  // tokens one tuned workgroup covers, at most
+
 // One channel as the kernels see it.  Pointers are device pointers; strides are in
 // elements of the storage type.
 struct ChanArgs {
@@ -14,10 +17,10 @@ struct ChanArgs {
   const void* U;  // [layers][tokens][rank]
   const void* V;  // [layers][chunks][heads*dim][rank]
   int32_t heads, dim, rope_dim;
-  int32_t tasks_per_head;  // rotate+patch kernel: dim / 64
-  int32_t groups;          // rotate+patch kernel: ceil(heads * tasks_per_head / tasks_per_wave)
-  int32_t pad_;
-  int64_t units;           // wavefront units of this channel per layer
+  int32_t fblocks;   // rotate+patch kernel: 128-feature blocks per token row
+  int64_t blocks;    // tuned kernels: workgroups of this channel per layer
+  // Pair frequencies theta^(-2i/rope_dim), i < rope_dim/2, formed on the host in fp64.
+  double omega[kMaxTunedHalf];
 };
 
 struct CommonArgs {
@@ -26,23 +29,26 @@ struct CommonArgs {
   const int32_t* block_table;
   int64_t total_tokens;
   int64_t num_pages;
-  int64_t nranges;          // ceil(total_tokens / range_tokens)
+  int64_t token_groups;     // ceil(total_tokens / block_tokens)
   double theta;
   int32_t num_chunks;
   int32_t page_size;
   int32_t num_layers;
   int32_t rank;
-  int32_t range_tokens;     // tokens per wavefront unit (multiple of 16)
-  int32_t pad_;
+  int32_t block_tokens;     // tokens one workgroup covers (tuned kernels)
+  int32_t page_shift;       // log2(page_size) when it is a power of two, else -1
 };
 
-// Rotation only, bf16, 16-byte rows: half = rope_dim / 2 in {8, 16, 32, 64, 128}.
-hipError_t launch_rotate_bf16(const ChanArgs& ch, const CommonArgs& cm, hipStream_t s);
+// Rotation only, bf16, 16-byte accesses: rope_dim in {16, 32, 64, 128}.
+// `unroll` row groups per wavefront (1, 2 or 4).
+hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unroll,
+                              hipStream_t s);
 
-// Rotation + rank-m patch with MFMA, bf16: dim % 64 == 0, rope_dim % 64 == 0, rank <= 128.
+// Rotation + rank-m patch on MFMA, bf16: see kernels.hip for the shape conditions.
 // Covers nch (1 or 2) channels in one launch.
-hipError_t launch_relocate_patch_mfma(const ChanArgs* ch, int nch, const CommonArgs& cm,
-                                      int tasks_per_wave, hipStream_t s);
+// `tile_unroll` 16-token tiles (1 or 2) are loaded together by each wavefront.
+hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonArgs& cm,
+                                      int tile_unroll, hipStream_t s);
 
 // Plain per-row kernel: any dim, even rope_dim, rank <= KAMERA_MAX_RANK, bf16 or fp32,
 // element-aligned pointers.  With rank 0 it only touches rotated dims.

@@ -9,17 +9,25 @@
 // "Aplicacao de Patch").
 //
 // Three kernels:
-//   rotate_bf16            m = 0: only the rotated dims of rotating channels are read and
-//                          written (§3, sliding-window survival: no patch is needed).
-//   relocate_patch_mfma    m > 0: rotation fused with the patch in one HBM pass; the
-//                          patch is a [16 x m] x [m x 16] product per tile on MFMA.
-//   generic_rows           any shape, bf16 or fp32: one thread per (layer, token, head).
+//   rotate_rows          m = 0: only the rotated dims of rotating channels are read and
+//                        written (§3, sliding-window survival: no patch is needed).
+//   relocate_patch_rows  m > 0: rotation fused with the patch in one HBM pass; the
+//                        patch of a 16-token x 128-feature tile is 8 MFMA
+//                        16x16x32 bf16 tiles per 32 k.
+//   generic_rows         any shape, bf16 or fp32: one thread per (layer, token, head).
 //
-// Memory: each KV element is read once and written once, in place.  A wavefront owns
-// whole 128-byte lines of the rows it writes.  Angles are formed in fp64 (delta up to
-// 2^53 times a frequency near 1 needs fp64 to keep the phase error far below fp32
-// rounding) and rounded to fp32 once per chunk; all element arithmetic is fp32.
+// Memory shape of the tuned kernels (what streams well on MI355X HBM3E): every load
+// and store is a 16-byte nontemporal access; 16 consecutive lanes cover one 256-byte
+// row of 128 features (or LPR lanes cover the rotated part of a row), so each wave
+// instruction touches whole 128-byte lines; a wavefront handles one or two 16-token
+// tiles and exits, so the lines in flight across the chip stay within a small
+// address window.  Per-chunk state (phases, feature factor V) is built once per
+// workgroup in LDS.  Angles: delta * omega_i is formed in fp64 with omega_i from the
+// host, reduced by 2 pi in fp64, and its cos and sin are rounded to fp32; all element
+// arithmetic is fp32 with one rounding to bf16 at the end.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kamera_internal.h"
 
@@ -30,6 +38,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = 64 * kWavesPerBlock;
@@ -39,7 +48,7 @@ constexpr int kBlock = 64 * kWavesPerBlock;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ void unpack8(const uint4& v, float (&x)[8]) {
+__device__ __forceinline__ void unpack8(const u32x4_t& v, float (&x)[8]) {
   x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
   x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
   x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
@@ -52,8 +61,20 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-__device__ __forceinline__ uint4 pack8(const float (&y)[8]) {
-  return make_uint4(pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7]));
+__device__ __forceinline__ u32x4_t pack8(const float (&y)[8]) {
+  u32x4_t r;
+  r.x = pack2(y[0], y[1]);
+  r.y = pack2(y[2], y[3]);
+  r.z = pack2(y[4], y[5]);
+  r.w = pack2(y[6], y[7]);
+  return r;
+}
+
+__device__ __forceinline__ u32x4_t load_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load((const u32x4_t*)p);
+}
+__device__ __forceinline__ void store_nt(uint16_t* p, const u32x4_t& v) {
+  __builtin_nontemporal_store(v, (u32x4_t*)p);
 }
 
 __device__ __forceinline__ float load_f(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
@@ -63,9 +84,79 @@ __device__ __forceinline__ void store_f(uint16_t* p, float y) {
 }
 __device__ __forceinline__ void store_f(float* p, float y) { *p = y; }
 
+// Value of lane (l ^ X) within each 16-lane row, X in {1, 2, 4, 8}.  Every lane of the
+// wavefront must execute it.
+template <int X>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (X == 1)  // quad_perm [1,0,3,2]
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);
+  else if constexpr (X == 2)  // quad_perm [2,3,0,1]
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);
+  else if constexpr (X == 8)  // row_ror:8 swaps the two 8-lane halves of a row
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, true);
+  else  // swizzle bit mode: and 0x1f, or 0, xor 4
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);
+}
+
+template <int X>
+__device__ __forceinline__ u32x4_t lane_xor4(const u32x4_t& v) {
+  u32x4_t r;
+  r.x = lane_xor<X>(v.x);
+  r.y = lane_xor<X>(v.y);
+  r.z = lane_xor<X>(v.z);
+  r.w = lane_xor<X>(v.w);
+  return r;
+}
+
+__device__ __forceinline__ u32x4_t lane_xor4_rt(const u32x4_t& v, int x) {
+  switch (x) {
+    case 1: return lane_xor4<1>(v);
+    case 2: return lane_xor4<2>(v);
+    case 4: return lane_xor4<4>(v);
+    default: return lane_xor4<8>(v);
+  }
+}
+
 // ------------------------------------------------------------------ index helpers
 
-// Chunk that owns token t: the last j with offsets[j] <= t (offsets[0] == 0 <= t).
+// Chunk that owns token t: the last j with offsets[j] <= t (offsets[0] == 0 <= t), with
+// its end offsets[j + 1] and its delta, in one round of loads: lane l reads
+// offsets[base + l + 1] and delta[base + l], a ballot counts the chunks that start at
+// or before t, and the owner's values come back by lane shuffle.  j lies in [0, n)
+// whatever the offsets hold.  All lanes must call it.
+struct ChunkRef {
+  int j;
+  int64_t end;
+  int64_t delta;
+};
+
+__device__ __forceinline__ ChunkRef find_chunk_wave(const int64_t* off, const int64_t* delta,
+                                                    int n, int64_t t, int from = 0) {
+  const int lane = threadIdx.x & 63;
+  ChunkRef c{from, 0, 0};
+  for (int base = from; base < n; base += 64) {
+    const int k = base + lane;
+    const int64_t e = k < n ? off[k + 1] : INT64_MAX;
+    const int64_t d = k < n ? delta[k] : 0;
+    const unsigned long long le = __ballot(e <= t);  // chunks that end at or before t
+    const int cnt = __popcll(le);
+    if (cnt < 64 || base + 64 >= n) {
+      const int src = cnt < 64 ? cnt : 63;
+      c.j = min(base + src, n - 1);
+      c.end = __shfl(e, src);
+      c.delta = __shfl(d, src);
+      if (base + src >= n) {  // past the last chunk: clamp to it
+        c.j = n - 1;
+        c.end = off[n];
+        c.delta = delta[n - 1];
+      }
+      break;
+    }
+  }
+  return c;
+}
+
+// Chunk of token t for a single thread (generic kernel).
 __device__ __forceinline__ int find_chunk(const int64_t* off, int n, int64_t t) {
   int lo = 0, hi = n;
   while (hi - lo > 1) {
@@ -75,25 +166,42 @@ __device__ __forceinline__ int find_chunk(const int64_t* off, int n, int64_t t) 
   return lo;
 }
 
-// Element offset of logical token t's slot inside one layer.  Paged: the block table
-// maps logical page t / P to a pool page; a page id outside [0, num_pages) leaves
-// the row untouched (ok = false) instead of touching memory outside the pool.
-__device__ __forceinline__ int64_t slot_offset(const ChanArgs& ch, const CommonArgs& cm,
-                                               int64_t t, bool& ok) {
-  if (cm.page_size > 0) {
-    const int tt = (int)t;
-    const int64_t pg = cm.block_table[tt / cm.page_size];
-    ok = pg >= 0 && pg < cm.num_pages;
-    return pg * ch.page_stride + (int64_t)(tt % cm.page_size) * ch.slot_stride;
-  }
-  ok = true;
-  return t * ch.slot_stride;
+// cos and sin of phi = delta * omega, rounded to fp32.  phi is formed in fp64 and
+// reduced by pi/2 with the two-constant Cody-Waite method (inside the FMA the first
+// product is exact for |phi| < 2^53); on the reduced |r| <= pi/4 the Taylor series of
+// sin (through r^11) and cos (through r^12) are summed in fp64, whose truncation error
+// (< 2e-9 relative) stays far below fp32 rounding; the quadrant picks signs and order.
+__device__ __forceinline__ float2 phase_of(double omega, int64_t delta) {
+  const double kPio2a = 0x1.921fb54442d18p+0;    // pi/2 rounded to a double
+  const double kPio2b = 0x1.1a62633145c07p-54;   // pi/2 minus the above
+  const double kTwoOverPi = 0x1.45f306dc9c883p-1;
+  const double phi = (double)delta * omega;
+  const double k = rint(phi * kTwoOverPi);
+  double r = fma(-k, kPio2a, phi);
+  r = fma(-k, kPio2b, r);
+  const double r2 = r * r;
+  double sp = -1.0 / 39916800.0;
+  sp = fma(sp, r2, 1.0 / 362880.0);
+  sp = fma(sp, r2, -1.0 / 5040.0);
+  sp = fma(sp, r2, 1.0 / 120.0);
+  sp = fma(sp, r2, -1.0 / 6.0);
+  const double sr = fma(r * r2, sp, r);
+  double cp = 1.0 / 479001600.0;
+  cp = fma(cp, r2, -1.0 / 3628800.0);
+  cp = fma(cp, r2, 1.0 / 40320.0);
+  cp = fma(cp, r2, -1.0 / 720.0);
+  cp = fma(cp, r2, 1.0 / 24.0);
+  cp = fma(cp, r2, -0.5);
+  const double cr = fma(r2, cp, 1.0);
+  const int qd = (int)((int64_t)k & 3);
+  const double c = qd == 0 ? cr : qd == 1 ? -sr : qd == 2 ? -cr : sr;
+  const double s = qd == 0 ? sr : qd == 1 ? cr : qd == 2 ? -sr : -cr;
+  return make_float2((float)c, (float)s);
 }
 
-// cos and sin of delta * theta^(-2i/r): the angle is formed and reduced in fp64, then
-// rounded to fp32.
-__device__ __forceinline__ void phase(double theta, int r, int i, int64_t delta,
-                                      float& c, float& s) {
+// Generic-kernel phase: plain fp64 pow and sincos per element pair.
+__device__ __forceinline__ void phase_generic(double theta, int r, int i, int64_t delta,
+                                              float& c, float& s) {
   const double w = pow(theta, -2.0 * (double)i / (double)r);
   const double phi = (double)delta * w;
   double sd, cd;
@@ -104,98 +212,127 @@ __device__ __forceinline__ void phase(double theta, int r, int i, int64_t delta,
 
 // ------------------------------------------------------------------ rotation only
 
-// One wavefront streams the rows (token, head) of `range_tokens` tokens of one layer.
-// A row's rotated part is r = 16 * LPR dims: LPR lanes each own 8 dims of the first
-// half and their 8 partners in the second half (two 16-byte loads, two 16-byte
-// stores), so 64 / LPR rows move per wavefront step.  Dims >= r are never touched.
-template <int LPR>
-__global__ __launch_bounds__(kBlock) void rotate_bf16(ChanArgs ch, CommonArgs cm) {
-  constexpr int HALF = 8 * LPR;
-  constexpr int RPW = 64 / LPR;
-  constexpr int NS = (HALF + 63) / 64;
-  constexpr int UNR = 4;
-  const int lane = threadIdx.x & 63;
-  const int64_t unit = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (unit >= (int64_t)cm.num_layers * cm.nranges) return;
-  const int64_t layer = unit / cm.nranges;
-  int64_t t0 = (unit - layer * cm.nranges) * cm.range_tokens;
-  const int64_t t1 = min(t0 + (int64_t)cm.range_tokens, cm.total_tokens);
-  const int q = lane % LPR;
-  const int rho = lane / LPR;
-  const int H = ch.heads;
-  uint16_t* base = (uint16_t*)ch.data + layer * ch.layer_stride;
-  int j = find_chunk(cm.offsets, cm.num_chunks, t0);
-  while (t0 < t1 && j < cm.num_chunks) {
-    const int64_t seg_end = min(t1, cm.offsets[j + 1]);
-    const int64_t dj = cm.delta[j];
-    if (seg_end > t0 && dj != 0) {
-      // Lane l forms pair frequency l (and l + 64); lanes then gather their 8.
-      float cown[NS], sown[NS];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int i = lane + 64 * s;
-        cown[s] = 1.f;
-        sown[s] = 0.f;
-        if (i < HALF) phase(cm.theta, 2 * HALF, i, dj, cown[s], sown[s]);
-      }
-      float cs[8], sn[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = 8 * q + e;
-        float c = __shfl(cown[0], i & 63);
-        float s = __shfl(sown[0], i & 63);
-#pragma unroll
-        for (int k = 1; k < NS; ++k) {
-          const float c1 = __shfl(cown[k], i & 63);
-          const float s1 = __shfl(sown[k], i & 63);
-          if ((i >> 6) == k) { c = c1; s = s1; }
-        }
-        cs[e] = c;
-        sn[e] = s;
-      }
-      const int nrows = (int)(seg_end - t0) * H;
-      for (int r0 = 0; r0 < nrows; r0 += RPW * UNR) {
-        uint4 va[UNR], vb[UNR];
-        uint16_t* rowp[UNR];
-        bool ok[UNR];
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-          const int R = r0 + u * RPW + rho;
-          ok[u] = R < nrows;
-          rowp[u] = base;
-          if (ok[u]) {
-            const int tl = R / H;
-            const int h = R - tl * H;
-            bool pok;
-            const int64_t so = slot_offset(ch, cm, t0 + tl, pok);
-            ok[u] = pok;
-            rowp[u] = base + so + (int64_t)h * ch.head_stride + 8 * q;
-          }
-          if (ok[u]) {
-            va[u] = *(const uint4*)rowp[u];
-            vb[u] = *(const uint4*)(rowp[u] + HALF);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-          if (!ok[u]) continue;
-          float a[8], b[8];
-          unpack8(va[u], a);
-          unpack8(vb[u], b);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float an = fmaf(a[e], cs[e], -(b[e] * sn[e]));
-            const float bn = fmaf(b[e], cs[e], a[e] * sn[e]);
-            a[e] = an;
-            b[e] = bn;
-          }
-          *(uint4*)rowp[u] = pack8(a);
-          *(uint4*)(rowp[u] + HALF) = pack8(b);
-        }
-      }
+// Block-table entries a workgroup needs, staged once in LDS: pages [p0, p0 + n) cover
+// tokens [tb0, t1).  Entries outside [0, num_pages) become -1 (their tokens are left
+// untouched).  Returns p0.  The caller synchronises before reading `sbt`.
+__device__ __forceinline__ int stage_block_table(const CommonArgs& cm, int64_t tb0, int64_t t1,
+                                                 int* sbt) {
+  const int P = cm.page_size;
+  const int p0 = (int)(tb0 / P);
+  const int n = (int)((t1 - 1) / P) + 1 - p0;
+  for (int k = threadIdx.x; k < n; k += kBlock) {
+    const int64_t pg = cm.block_table[p0 + k];
+    sbt[k] = (pg >= 0 && pg < cm.num_pages) ? (int)pg : -1;
+  }
+  return p0;
+}
+
+// Element offset, inside one layer, of the slot of token t (-1: token left untouched).
+__device__ __forceinline__ int64_t slot_staged(const CommonArgs& cm, const int* sbt, int p0,
+                                               int64_t page_stride, int64_t slot_stride,
+                                               int64_t t) {
+  if (cm.page_size > 0) {
+    const int tt = (int)t;
+    int pi, si;
+    if (cm.page_shift >= 0) {
+      pi = tt >> cm.page_shift;
+      si = tt & (cm.page_size - 1);
+    } else {
+      pi = tt / cm.page_size;
+      si = tt - pi * cm.page_size;
     }
-    t0 = max(t0, seg_end);
-    ++j;
+    const int pg = sbt[pi - p0];
+    return pg < 0 ? -1 : (int64_t)pg * page_stride + (int64_t)si * slot_stride;
+  }
+  return t * slot_stride;
+}
+
+// Workgroup = `block_tokens` tokens of one layer, every head, taken as rows (token,
+// head) in order.  LPR lanes cover the rotated part of a row (8 dims each); a lane's
+// NeoX partner dims sit LPR/2 lanes away and arrive by a lane exchange; one wave
+// instruction covers 64/LPR consecutive rows.  Wave w takes row groups w, w + 4, ...
+// (UNR of them per pass) and issues all their loads before it looks up the chunk and
+// waits for the phases.  Dims >= rope_dim are never touched; rows of chunks with
+// delta == 0 are not written.
+template <int LPR, int UNR>
+__global__ __launch_bounds__(kBlock) void rotate_rows(ChanArgs ch, CommonArgs cm) {
+  constexpr int RPI = 64 / LPR;
+  constexpr int HX = LPR / 2;
+  constexpr int HALF = 8 * HX;
+  constexpr int ROWS = kWavesPerBlock * UNR * RPI;  // rows one pass of the block covers
+  __shared__ float2 sph[HALF];
+  __shared__ int sbt[kMaxBlockTokens + 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t layer = blockIdx.x / cm.token_groups;
+  const int64_t tg = blockIdx.x - layer * cm.token_groups;
+  const int64_t tb0 = tg * cm.block_tokens;
+  const int64_t t1 = min(tb0 + (int64_t)cm.block_tokens, cm.total_tokens);
+  const int q = lane % LPR;
+  const int rr = lane / LPR;
+  const int fi0 = (q % HX) * 8;
+  const float sgn = q < HX ? -1.f : 1.f;
+  const int H = ch.heads;
+  const int nrows = (int)(t1 - tb0) * H;
+  uint16_t* base = (uint16_t*)ch.data + layer * ch.layer_stride + 8 * q;
+  int p0 = 0;
+  if (cm.page_size > 0) {
+    p0 = stage_block_table(cm, tb0, t1, sbt);
+    __syncthreads();
+  }
+  for (int rbase = 0; rbase < nrows; rbase += ROWS) {
+    u32x4_t xv[UNR];
+    uint16_t* ptr[UNR];
+    int64_t tok[UNR];
+    bool ok[UNR];
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const int R = rbase + (wave + kWavesPerBlock * k) * RPI + rr;
+      ok[k] = R < nrows;
+      ptr[k] = base;
+      tok[k] = tb0;
+      xv[k] = u32x4_t{0u, 0u, 0u, 0u};
+      if (ok[k]) {
+        const int tl = R / H;
+        const int h = R - tl * H;
+        tok[k] = tb0 + tl;
+        const int64_t so = slot_staged(cm, sbt, p0, ch.page_stride, ch.slot_stride, tok[k]);
+        ok[k] = so >= 0;
+        ptr[k] = base + so + (int64_t)h * ch.head_stride;
+      }
+      if (ok[k]) xv[k] = load_nt(ptr[k]);
+    }
+    int64_t t0 = tb0 + rbase / H;
+    const int64_t rt1 = min(t1, tb0 + (rbase + ROWS + H - 1) / H);
+    ChunkRef c = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0);
+    while (true) {
+      const int64_t s1 = min(rt1, c.end);
+      if (s1 > t0 && c.delta != 0) {
+        __syncthreads();
+        if (threadIdx.x < HALF) sph[threadIdx.x] = phase_of(ch.omega[threadIdx.x], c.delta);
+        __syncthreads();
+        float cs[8], sn[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 v = sph[fi0 + e];
+          cs[e] = v.x;
+          sn[e] = sgn * v.y;
+        }
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+          const u32x4_t pv = lane_xor4<HX>(xv[k]);
+          float a[8], b[8], y[8];
+          unpack8(xv[k], a);
+          unpack8(pv, b);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = fmaf(a[e], cs[e], b[e] * sn[e]);
+          if (ok[k] && tok[k] >= t0 && tok[k] < s1) store_nt(ptr[k], pack8(y));
+        }
+      }
+      t0 = max(t0, s1);
+      if (t0 >= rt1 || c.j + 1 >= cm.num_chunks) break;
+      c = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0, c.j + 1);
+    }
   }
 }
 
@@ -203,207 +340,234 @@ __global__ __launch_bounds__(kBlock) void rotate_bf16(ChanArgs ch, CommonArgs cm
 
 // Patch fragment of 8 consecutive k (bf16): a 16-byte load when all 8 lie below m and
 // rows are 16-byte aligned (m % 8 == 0), else element loads with zero fill.
-__device__ __forceinline__ bf16x8_t load_frag(const uint16_t* row, int k0, int m, bool m8) {
-  if (m8 && k0 + 8 <= m) return __builtin_bit_cast(bf16x8_t, *(const uint4*)(row + k0));
+__device__ __forceinline__ u32x4_t load_frag(const uint16_t* row, int k0, int m, bool m8) {
+  if (m8 && k0 + 8 <= m) return *(const u32x4_t*)(row + k0);
   uint16_t v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = (k0 + e < m) ? row[k0 + e] : (uint16_t)0;
-  uint4 w = make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
-                       v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
-  return __builtin_bit_cast(bf16x8_t, w);
+  u32x4_t w;
+  w.x = v[0] | ((uint32_t)v[1] << 16);
+  w.y = v[2] | ((uint32_t)v[3] << 16);
+  w.z = v[4] | ((uint32_t)v[5] << 16);
+  w.w = v[6] | ((uint32_t)v[7] << 16);
+  return w;
 }
 
-// Work unit of one wavefront: NT "tasks" of one channel and layer, over `range_tokens`
-// tokens, 16 tokens per step.  A task is 64 features of one head, kept as two 32-wide
-// slabs: a rotating pair task holds dims [32i, 32i+32) and their partners
-// [r/2 + 32i, r/2 + 32i + 32); a plain task holds dims [r + 64i', r + 64i' + 64).
+// Per-workgroup constants of the rotate+patch kernel that the tile loop reads.
+struct PatchCtx {
+  uint16_t* base;       // lane's element (layer, slot 0, head h, dim d0)
+  const uint16_t* Ul;   // U of this layer and channel
+  const int* sbt;       // staged block table (paged)
+  int64_t page_stride, slot_stride;
+  int64_t tb0, t1;
+  int p0, m;
+  int lane, wave, c16, g;
+  int fi0;
+  float sgn;
+  bool lane_on, rot_lane;
+};
+
+// Tiles of this wave (16-token tile kt with kt = wave mod 4) that meet [t0, s1): TU tiles
+// are loaded together (4 x 16 B of KV and MK x 16 B of U per lane each), then rotated,
+// patched and stored.  HX is the partner lane distance (0: no rotation).  Lane l holds
+// features fb + 8c + n (c = l & 15, n < 8) of tokens 4g .. 4g + 3 (g = l >> 4).
 //
-// Lane l works on token (l & 15) of the step and on dims 8g..8g+7 (g = l >> 4) of each
-// slab: a NeoX pair never leaves the lane.  The patch of one slab is two MFMA
-// 16x16x32 bf16 tiles per 32 k:  D[f][t] = C[f][t] + sum_k V[f][k] U[t][k], with
-// A = V rows (features), B = U rows (tokens).  The MFMA output layout gives lane l
-// rows 4g..4g+3 of column l & 15; the A rows are ordered so that output row 4g+i of
-// tile p is feature 8g + 4p + i of the slab.  The lane's own rotated values are thus
-// the C operand, and the output lands in the lane that stores it.
-template <int NT, int MK>
-__global__ __launch_bounds__(kBlock) void relocate_patch_mfma(ChanArgs ch0, ChanArgs ch1,
-                                                              CommonArgs cm,
-                                                              int64_t units_per_layer) {
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 15;
-  const int g = lane >> 4;
-  const int64_t unit = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (unit >= (int64_t)cm.num_layers * units_per_layer) return;
-  const int64_t layer = unit / units_per_layer;
-  int64_t rem = unit - layer * units_per_layer;
-  const bool second = rem >= ch0.units;
-  if (second) rem -= ch0.units;
-  const ChanArgs ch = second ? ch1 : ch0;
-  const int64_t range = rem / ch.groups;
-  const int group = (int)(rem - range * ch.groups);
-
-  const int m = cm.rank;
-  const bool m8 = (m & 7) == 0;
-  const int F = ch.heads * ch.dim;
-  const int r = ch.rope_dim;
-  const int npair = r >> 6;
-  const int ntask = ch.heads * ch.tasks_per_head;
-
-  bool tv[NT], tp[NT];
-  int ti[NT], dd[NT][2], fb[NT][2];
-  int64_t hoff[NT];
+// Patch on MFMA 16x16x32 bf16: D[t][col] = C[t][col] + sum_k A[t][k] B[k][col] with
+// A = U rows (tokens), B = V^T.  Column col of MFMA tile n is feature fb + 8 col + n,
+// so the output layout (lane l holds rows 4g..4g+3 of column l & 15) is the lane's own
+// feature n of its 4 tokens: the rotated values are the C operand and the result is
+// already where it is stored.  Output tiles go two at a time (features 2p, 2p + 1 form
+// one packed bf16 pair), so only 8 accumulators are live.
+template <int MK, bool M8, int HX, int TU>
+__device__ __forceinline__ void patch_tiles(const PatchCtx& c, const CommonArgs& cm,
+                                            const u32x4_t* sV, const float4* sph2,
+                                            int64_t t0, int64_t s1) {
+  const int k_lo = (int)((t0 - c.tb0) >> 4);
+  const int k_hi = (int)((s1 - c.tb0 + 15) >> 4);
+  int kt = k_lo + ((c.wave - k_lo) % kWavesPerBlock + kWavesPerBlock) % kWavesPerBlock;
+  for (; kt < k_hi; kt += kWavesPerBlock * TU) {
+    u32x4_t x[TU][4];
+    int32_t off[TU][4];
+    u32x4_t a[TU][MK];
 #pragma unroll
-  for (int k = 0; k < NT; ++k) {
-    const int tau = group * NT + k;
-    tv[k] = tau < ntask;
-    const int h = tau / ch.tasks_per_head;
-    const int i = tau - h * ch.tasks_per_head;
-    tp[k] = i < npair;
-    ti[k] = i;
-    dd[k][0] = tp[k] ? 32 * i : r + 64 * (i - npair);
-    dd[k][1] = tp[k] ? (r >> 1) + 32 * i : dd[k][0] + 32;
-    fb[k][0] = h * ch.dim + dd[k][0];
-    fb[k][1] = h * ch.dim + dd[k][1];
-    hoff[k] = (int64_t)h * ch.head_stride;
-  }
-
-  const uint16_t* Ul = (const uint16_t*)ch.U + layer * cm.total_tokens * m;
-  const uint16_t* Vl = (const uint16_t*)ch.V + layer * (int64_t)cm.num_chunks * F * m;
-  uint16_t* base = (uint16_t*)ch.data + layer * ch.layer_stride;
-
-  int64_t t0 = range * cm.range_tokens;
-  const int64_t t1 = min(t0 + (int64_t)cm.range_tokens, cm.total_tokens);
-  int j = find_chunk(cm.offsets, cm.num_chunks, t0);
-  while (t0 < t1 && j < cm.num_chunks) {
-    const int64_t seg_end = min(t1, cm.offsets[j + 1]);
-    if (seg_end > t0) {
-      const int64_t dj = cm.delta[j];
-      // Feature factor of chunk j, resident in registers for the whole segment.
-      const uint16_t* Vj = Vl + (int64_t)j * F * m;
-      bf16x8_t vf[NT][2][2][MK];
+    for (int u = 0; u < TU; ++u) {
+      const int64_t ts = c.tb0 + 16 * (int64_t)(kt + kWavesPerBlock * u);
+      const bool tile_on = kt + kWavesPerBlock * u < k_hi;
 #pragma unroll
-      for (int k = 0; k < NT; ++k)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int ks = 0; ks < MK; ++ks) {
-              const int f = fb[k][s] + 8 * (col >> 2) + 4 * p + (col & 3);
-              vf[k][s][p][ks] = tv[k] ? load_frag(Vj + (int64_t)f * m, 32 * ks + 8 * g, m, m8)
-                                      : load_frag(Vj, 0, 0, m8);
-            }
-      // Phase of the lane's 8 pairs per rotating task.
-      float cs[NT][8], sn[NT][8];
-      const bool rot = dj != 0;
-#pragma unroll
-      for (int k = 0; k < NT; ++k) {
-        float c = 1.f, s = 0.f;
-        if (rot && tv[k] && tp[k]) phase(cm.theta, r, 32 * ti[k] + (lane & 31), dj, c, s);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          cs[k][e] = __shfl(c, 8 * g + e);
-          sn[k][e] = __shfl(s, 8 * g + e);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = ts + 4 * c.g + i;
+        off[u][i] = -1;
+        x[u][i] = u32x4_t{0u, 0u, 0u, 0u};
+        if (tile_on && c.lane_on && t >= t0 && t < s1)
+          off[u][i] = (int32_t)slot_staged(cm, c.sbt, c.p0, c.page_stride, c.slot_stride, t);
+        if (off[u][i] >= 0) x[u][i] = load_nt(c.base + off[u][i]);
       }
-
-      uint4 xc[NT][2], xn[NT][2];
-      bf16x8_t uc[MK], un[MK];
-      uint16_t* rc[NT];
-      uint16_t* rn[NT];
-      bool okc, okn;
-      auto load_tile = [&](int64_t ts, uint4 (&xv)[NT][2], bf16x8_t (&uf)[MK],
-                           uint16_t* (&rp)[NT], bool& ok) {
-        const int64_t tok = ts + col;
-        ok = tok < seg_end;
-        int64_t so = 0;
-        if (ok) {
-          bool pok;
-          so = slot_offset(ch, cm, tok, pok);
-          ok = pok;
-        }
+      const int64_t tu = ts + c.c16;
+      const bool uok = tile_on && tu < c.t1;
+      const uint16_t* urow = c.Ul + (uok ? tu : 0) * c.m;
 #pragma unroll
-        for (int k = 0; k < NT; ++k) {
-          rp[k] = base + so + hoff[k];
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            xv[k][s] = make_uint4(0, 0, 0, 0);
-            if (ok && tv[k]) xv[k][s] = *(const uint4*)(rp[k] + dd[k][s] + 8 * g);
-          }
-        }
-        const uint16_t* urow = Ul + (ok ? tok : 0) * m;
-#pragma unroll
-        for (int ks = 0; ks < MK; ++ks) {
-          uf[ks] = load_frag(urow, 0, 0, m8);
-          if (ok) uf[ks] = load_frag(urow, 32 * ks + 8 * g, m, m8);
-        }
-      };
-
-      load_tile(t0, xc, uc, rc, okc);
-      for (int64_t ts = t0; ts < seg_end; ts += 16) {
-        const bool more = ts + 16 < seg_end;
-        if (more) load_tile(ts + 16, xn, un, rn, okn);
-
-        f32x4_t acc[NT][2][2];
-#pragma unroll
-        for (int k = 0; k < NT; ++k) {
-          float a[8], b[8];
-          unpack8(xc[k][0], a);
-          unpack8(xc[k][1], b);
-          if (rot && tp[k]) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float an = fmaf(a[e], cs[k][e], -(b[e] * sn[k][e]));
-              const float bn = fmaf(b[e], cs[k][e], a[e] * sn[k][e]);
-              a[e] = an;
-              b[e] = bn;
-            }
-          }
-          acc[k][0][0] = f32x4_t{a[0], a[1], a[2], a[3]};
-          acc[k][0][1] = f32x4_t{a[4], a[5], a[6], a[7]};
-          acc[k][1][0] = f32x4_t{b[0], b[1], b[2], b[3]};
-          acc[k][1][1] = f32x4_t{b[4], b[5], b[6], b[7]};
-        }
-#pragma unroll
-        for (int ks = 0; ks < MK; ++ks)
-#pragma unroll
-          for (int k = 0; k < NT; ++k)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-              for (int p = 0; p < 2; ++p)
-                acc[k][s][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[k][s][p][ks], uc[ks],
-                                                                       acc[k][s][p], 0, 0, 0);
-        if (okc) {
-#pragma unroll
-          for (int k = 0; k < NT; ++k) {
-            if (!tv[k]) continue;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              float y[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) y[e] = acc[k][s][e >> 2][e & 3];
-              *(uint4*)(rc[k] + dd[k][s] + 8 * g) = pack8(y);
-            }
-          }
-        }
-        if (more) {
-#pragma unroll
-          for (int k = 0; k < NT; ++k) {
-            xc[k][0] = xn[k][0];
-            xc[k][1] = xn[k][1];
-            rc[k] = rn[k];
-          }
-#pragma unroll
-          for (int ks = 0; ks < MK; ++ks) uc[ks] = un[ks];
-          okc = okn;
-        }
+      for (int ks = 0; ks < MK; ++ks) {
+        a[u][ks] = u32x4_t{0u, 0u, 0u, 0u};
+        if (uok) a[u][ks] = load_frag(urow, 32 * ks + 8 * c.g, c.m, M8);
       }
     }
-    t0 = max(t0, seg_end);
-    ++j;
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      u32x4_t out[4];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {  // features 2pp, 2pp + 1 of the lane's 8
+        float4 ph = make_float4(1.f, 0.f, 1.f, 0.f);
+        if constexpr (HX > 0) ph = sph2[(c.fi0 >> 1) + pp];
+        f32x4_t acc0, acc1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = x[u][i][pp];
+          float a0 = bf16_lo(w), a1 = bf16_hi(w);
+          if constexpr (HX > 0) {
+            const uint32_t pw = lane_xor<HX>(w);
+            const float y0 = fmaf(a0, ph.x, bf16_lo(pw) * (c.sgn * ph.y));
+            const float y1 = fmaf(a1, ph.z, bf16_hi(pw) * (c.sgn * ph.w));
+            a0 = c.rot_lane ? y0 : a0;
+            a1 = c.rot_lane ? y1 : a1;
+          }
+          acc0[i] = a0;
+          acc1[i] = a1;
+        }
+#pragma unroll
+        for (int ks = 0; ks < MK; ++ks) {
+          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, a[u][ks]);
+          const bf16x8_t B0 = __builtin_bit_cast(bf16x8_t, sV[((2 * pp) * MK + ks) * 64 + c.lane]);
+          const bf16x8_t B1 =
+              __builtin_bit_cast(bf16x8_t, sV[((2 * pp + 1) * MK + ks) * 64 + c.lane]);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B0, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i][pp] = pack2(acc0[i], acc1[i]);
+        // Keep the scheduler from hoisting every feature pair's LDS reads at once (it
+        // would hold all B fragments live and halve the occupancy).
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (off[u][i] >= 0) store_nt(c.base + off[u][i], out[i]);
+    }
   }
 }
+
+// Workgroup = one 128-feature block of one channel and layer over `block_tokens` tokens;
+// wave w takes the 16-token tiles w, w + 4, ....  Each chunk the workgroup meets is
+// staged once in LDS (the B fragments of its feature factor, the phases of its delta),
+// then the waves stream their tiles of that chunk.  Workgroups are numbered so that all
+// feature blocks of one token group run on the same XCD (consecutive workgroup ids go
+// to consecutive XCDs), where they share the token group's U rows in that XCD's L2.
+template <int MK, bool M8, int TU>
+__global__ __launch_bounds__(kBlock) void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1,
+                                                              CommonArgs cm,
+                                                              int64_t blocks_per_layer,
+                                                              int xcd_group) {
+  __shared__ u32x4_t sV[8 * MK * 64];
+  __shared__ float4 sph2[kMaxTunedHalf / 2];  // (cos, sin) of pairs 2p and 2p + 1
+  __shared__ int sbt[kMaxBlockTokens + 1];
+  const int lane = threadIdx.x & 63;
+
+  // Logical workgroup index: groups of 8 * xcd_group ids are permuted so that XCD x
+  // gets xcd_group consecutive logical blocks (one token group's feature blocks).
+  int64_t bid = blockIdx.x;
+  if (xcd_group > 0) {
+    const int64_t G = 8 * (int64_t)xcd_group;
+    const int64_t full = ((int64_t)gridDim.x / G) * G;
+    if (bid < full) {
+      const int64_t i = bid % G;
+      bid = bid - i + (i % 8) * xcd_group + i / 8;
+    }
+  }
+  const int64_t layer = bid / blocks_per_layer;
+  int64_t b = bid - layer * blocks_per_layer;
+  const bool second = b >= ch0.blocks;
+  if (second) b -= ch0.blocks;
+  // Field-wise choice of the channel (a reference to either argument would copy both
+  // to scratch memory).
+#define KAMERA_CH(f) (second ? ch1.f : ch0.f)
+  const int fblocks = KAMERA_CH(fblocks);
+  const int64_t tg = b / fblocks;
+  const int fbk = (int)(b - tg * fblocks);
+
+  PatchCtx c;
+  c.lane = lane;
+  c.wave = threadIdx.x >> 6;
+  c.c16 = lane & 15;
+  c.g = lane >> 4;
+  c.m = cm.rank;
+  const int m = cm.rank;
+  const int D = KAMERA_CH(dim);
+  const int r = KAMERA_CH(rope_dim);
+  const int F = KAMERA_CH(heads) * D;
+  const int fb = fbk * 128;
+  const int f0 = fb + 8 * c.c16;
+  c.lane_on = f0 < F;
+  const int h = f0 / D;
+  const int d0 = f0 - h * D;
+  c.rot_lane = c.lane_on && d0 < r;
+  c.fi0 = d0 < (r >> 1) ? d0 : d0 - (r >> 1);
+  c.sgn = d0 < (r >> 1) ? -1.f : 1.f;
+  const int hx = r >> 4;  // partner lane distance: half / 8
+
+  c.slot_stride = KAMERA_CH(slot_stride);
+  c.page_stride = KAMERA_CH(page_stride);
+  c.base = (uint16_t*)KAMERA_CH(data) + layer * KAMERA_CH(layer_stride) +
+           (int64_t)h * KAMERA_CH(head_stride) + d0;
+  c.Ul = (const uint16_t*)KAMERA_CH(U) + layer * cm.total_tokens * m;
+  const uint16_t* Vl = (const uint16_t*)KAMERA_CH(V) + layer * (int64_t)cm.num_chunks * F * m;
+
+  c.tb0 = tg * cm.block_tokens;
+  c.t1 = min(c.tb0 + (int64_t)cm.block_tokens, cm.total_tokens);
+  c.p0 = 0;
+  c.sbt = sbt;
+  if (cm.page_size > 0) c.p0 = stage_block_table(cm, c.tb0, c.t1, sbt);
+
+  int64_t t0 = c.tb0;
+  ChunkRef ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0);
+  while (true) {
+    const int64_t s1 = min(c.t1, ck.end);
+    if (s1 > t0) {
+      const bool rotate = r > 0 && ck.delta != 0;
+      __syncthreads();
+      {
+        const uint16_t* Vj = Vl + (int64_t)ck.j * F * m;
+#pragma unroll
+        for (int u = 0; u < 2 * MK; ++u) {
+          const int it = threadIdx.x + kBlock * u;
+          const int l = it & 63;
+          const int nk = it >> 6;  // n * MK + ks
+          const int n = nk / MK;
+          const int ks = nk - n * MK;
+          const int f = fb + 8 * (l & 15) + n;
+          u32x4_t v = {0u, 0u, 0u, 0u};
+          if (f < F) v = load_frag(Vj + (int64_t)f * m, 32 * ks + 8 * (l >> 4), m, M8);
+          sV[it] = v;
+        }
+      }
+      if (rotate && threadIdx.x < (r >> 2)) {
+        const float2 q0 = phase_of(KAMERA_CH(omega[2 * threadIdx.x]), ck.delta);
+        const float2 q1 = phase_of(KAMERA_CH(omega[2 * threadIdx.x + 1]), ck.delta);
+        sph2[threadIdx.x] = make_float4(q0.x, q0.y, q1.x, q1.y);
+      }
+      __syncthreads();
+      switch (rotate ? hx : 0) {
+        case 1: patch_tiles<MK, M8, 1, TU>(c, cm, sV, sph2, t0, s1); break;
+        case 2: patch_tiles<MK, M8, 2, TU>(c, cm, sV, sph2, t0, s1); break;
+        case 4: patch_tiles<MK, M8, 4, TU>(c, cm, sV, sph2, t0, s1); break;
+        case 8: patch_tiles<MK, M8, 8, TU>(c, cm, sV, sph2, t0, s1); break;
+        default: patch_tiles<MK, M8, 0, TU>(c, cm, sV, sph2, t0, s1); break;
+      }
+    }
+    t0 = max(t0, s1);
+    if (t0 >= c.t1 || ck.j + 1 >= cm.num_chunks) break;
+    ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0, ck.j + 1);
+  }
+}
+#undef KAMERA_CH
 
 // ------------------------------------------------------------------ generic rows
 
@@ -447,7 +611,7 @@ __global__ __launch_bounds__(kBlock) void generic_rows(ChanArgs ch, CommonArgs c
       float a = load_f(row + i), b = load_f(row + i + half);
       if (dj != 0) {
         float c, s;
-        phase(cm.theta, r, i, dj, c, s);
+        phase_generic(cm.theta, r, i, dj, c, s);
         const float an = fmaf(a, c, -(b * s));
         const float bn = fmaf(b, c, a * s);
         a = an;
@@ -469,38 +633,49 @@ __global__ __launch_bounds__(kBlock) void generic_rows(ChanArgs ch, CommonArgs c
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_rotate_bf16(const ChanArgs& ch, const CommonArgs& cm, hipStream_t s) {
-  const int64_t units = (int64_t)cm.num_layers * cm.nranges;
-  const dim3 grid((unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock));
-  switch (ch.rope_dim / 16) {
-    case 1: hipLaunchKernelGGL(rotate_bf16<1>, grid, dim3(kBlock), 0, s, ch, cm); break;
-    case 2: hipLaunchKernelGGL(rotate_bf16<2>, grid, dim3(kBlock), 0, s, ch, cm); break;
-    case 4: hipLaunchKernelGGL(rotate_bf16<4>, grid, dim3(kBlock), 0, s, ch, cm); break;
-    case 8: hipLaunchKernelGGL(rotate_bf16<8>, grid, dim3(kBlock), 0, s, ch, cm); break;
-    case 16: hipLaunchKernelGGL(rotate_bf16<16>, grid, dim3(kBlock), 0, s, ch, cm); break;
+hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unroll,
+                              hipStream_t s) {
+  const int64_t blocks = (int64_t)cm.num_layers * cm.token_groups;
+  const dim3 grid((unsigned)blocks);
+#define KAMERA_LAUNCH_ROT(LPR)                                                              \
+  do {                                                                                      \
+    if (unroll == 1) hipLaunchKernelGGL((rotate_rows<LPR, 1>), grid, dim3(kBlock), 0, s, ch, cm); \
+    else if (unroll == 2) hipLaunchKernelGGL((rotate_rows<LPR, 2>), grid, dim3(kBlock), 0, s, ch, cm); \
+    else hipLaunchKernelGGL((rotate_rows<LPR, 4>), grid, dim3(kBlock), 0, s, ch, cm);       \
+  } while (0)
+  switch (ch.rope_dim) {
+    case 16: KAMERA_LAUNCH_ROT(2); break;
+    case 32: KAMERA_LAUNCH_ROT(4); break;
+    case 64: KAMERA_LAUNCH_ROT(8); break;
+    case 128: KAMERA_LAUNCH_ROT(16); break;
     default: return hipErrorInvalidValue;
   }
+#undef KAMERA_LAUNCH_ROT
   return hipGetLastError();
 }
 
-hipError_t launch_relocate_patch_mfma(const ChanArgs* ch, int nch, const CommonArgs& cm,
-                                      int tasks_per_wave, hipStream_t s) {
+hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonArgs& cm,
+                                      int tile_unroll, hipStream_t s) {
   ChanArgs c0 = ch[0];
   ChanArgs c1 = nch > 1 ? ch[1] : ch[0];
-  if (nch == 1) c1.units = 0;
-  const int64_t upl = c0.units + c1.units;
-  const int64_t units = (int64_t)cm.num_layers * upl;
-  const dim3 grid((unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock));
+  if (nch == 1) c1.blocks = 0;
+  const int64_t bpl = c0.blocks + c1.blocks;
+  const dim3 grid((unsigned)((int64_t)cm.num_layers * bpl));
+  // XCD grouping needs one feature-block count for every channel of the launch.
+  const int xg = (nch == 1 || c0.fblocks == c1.fblocks) ? c0.fblocks : 0;
   const int mk = (cm.rank + 31) / 32;
-  if (tasks_per_wave != 1) return hipErrorInvalidValue;
-  if (mk == 1)
-    hipLaunchKernelGGL((relocate_patch_mfma<1, 1>), grid, dim3(kBlock), 0, s, c0, c1, cm, upl);
-  else if (mk == 2)
-    hipLaunchKernelGGL((relocate_patch_mfma<1, 2>), grid, dim3(kBlock), 0, s, c0, c1, cm, upl);
-  else if (mk <= 4)
-    hipLaunchKernelGGL((relocate_patch_mfma<1, 4>), grid, dim3(kBlock), 0, s, c0, c1, cm, upl);
-  else
-    return hipErrorInvalidValue;
+  const bool m8 = cm.rank % 8 == 0;
+#define KAMERA_LAUNCH_PATCH(MK)                                                               \
+  do {                                                                                        \
+    if (m8 && tile_unroll == 2) hipLaunchKernelGGL((relocate_patch_rows<MK, true, 2>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, xg); \
+    else if (m8) hipLaunchKernelGGL((relocate_patch_rows<MK, true, 1>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, xg); \
+    else hipLaunchKernelGGL((relocate_patch_rows<MK, false, 1>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, xg); \
+  } while (0)
+  if (mk == 1) KAMERA_LAUNCH_PATCH(1);
+  else if (mk == 2) KAMERA_LAUNCH_PATCH(2);
+  else if (mk <= 4) KAMERA_LAUNCH_PATCH(4);
+  else return hipErrorInvalidValue;
+#undef KAMERA_LAUNCH_PATCH
   return hipGetLastError();
 }
 

@@ -40,6 +40,9 @@ class Workload:
     delta: int = 0
     delta_range: tuple | None = None  # (lo, hi) inclusive, drawn per chunk
     rope_mla: int = 64          # MLA decoupled k_rope width
+    rope_dim: int = 0           # GQA/MHA rotated dims per key head (0 = the whole head)
+    lens: tuple | None = None   # explicit chunk lengths (overrides tokens / chunk_len)
+    deltas: tuple | None = None  # explicit per-chunk deltas (overrides delta / delta_range)
     page_size: int = 0
     pool_pages: int = 0         # pages per layer in the pool (paged only)
     outliers: int = 0           # feature indices scaled by outlier_scale in K and V
@@ -120,16 +123,22 @@ class Structure:
 
 def structure(w: Workload) -> Structure:
     rng = np.random.default_rng(np.random.SeedSequence([w.wid, KIND_STRUCT]))
-    if w.chunk_len is not None:
+    if w.lens is not None:
+        lens = np.asarray(w.lens, dtype=np.int64)
+    elif w.chunk_len is not None:
         lens = rng.integers(w.chunk_len[0], w.chunk_len[1] + 1, size=w.n_chunks)
     else:
         lens = np.full(w.n_chunks, w.tokens, dtype=np.int64)
-    offsets = np.zeros(w.n_chunks + 1, dtype=np.int64)
+    n = len(lens)
+    offsets = np.zeros(n + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(lens)
-    if w.delta_range is not None:
-        delta = rng.integers(w.delta_range[0], w.delta_range[1] + 1, size=w.n_chunks).astype(np.int64)
+    if w.deltas is not None:
+        delta = np.asarray(w.deltas, dtype=np.int64)
+        assert delta.size == n
+    elif w.delta_range is not None:
+        delta = rng.integers(w.delta_range[0], w.delta_range[1] + 1, size=n).astype(np.int64)
     else:
-        delta = np.full(w.n_chunks, w.delta, dtype=np.int64)
+        delta = np.full(n, w.delta, dtype=np.int64)
     T = int(offsets[-1])
     bt = None
     if w.page_size > 0:
@@ -162,13 +171,14 @@ def channel_layouts(w: Workload, total_tokens: int, pool_pages: int = 0) -> list
                  layer_stride=ls, slot_stride=row, head_stride=w.rope_mla, page_stride=0),
         ]
     H, D = w.heads, w.head_dim
+    rk = w.rope_dim or D
     if w.page_size > 0:
         P = w.page_size
         ps = P * H * D
-        return [dict(buffer=b, offset=0, heads=H, dim=D, rope_dim=D if b == 0 else 0,
+        return [dict(buffer=b, offset=0, heads=H, dim=D, rope_dim=rk if b == 0 else 0,
                      layer_stride=pool_pages * ps, slot_stride=H * D, head_stride=D,
                      page_stride=ps) for b in (0, 1)]
-    return [dict(buffer=b, offset=0, heads=H, dim=D, rope_dim=D if b == 0 else 0,
+    return [dict(buffer=b, offset=0, heads=H, dim=D, rope_dim=rk if b == 0 else 0,
                  layer_stride=total_tokens * H * D, slot_stride=H * D, head_stride=D,
                  page_stride=0) for b in (0, 1)]
 

@@ -244,7 +244,15 @@ def test_kernel_choice():
     names, _ = plan_names(*gqa(D=96, r=96, m=8))
     assert names == ["generic", "generic"]
     names, _ = plan_names(*gqa(D=128, r=32, m=8))
+    assert names == ["rotate+patch mfma"] * 2
+    names, _ = plan_names(*gqa(D=128, r=48, m=8))
     assert names == ["generic", "rotate+patch mfma"]
+    names, _ = plan_names(*gqa(D=256, r=256, m=8))
+    assert names == ["generic", "rotate+patch mfma"]
+    names, _ = plan_names(*gqa(D=256, r=128, m=8))
+    assert names == ["rotate+patch mfma"] * 2
+    names, _ = plan_names(*gqa(D=256, r=256, m=0))
+    assert names == ["generic", "none"]
     names, _ = plan_names(*gqa(D=128, r=32, m=0))
     assert names == ["rotate", "none"]
     names, _ = plan_names(*gqa(D=128, r=48, m=0))
@@ -265,10 +273,11 @@ def test_kernel_choice():
     assert names == ["rotate+patch mfma"] * 2
 
 
-def test_mfma_unit_count():
-    # One wavefront unit = one 64-feature task of one channel over tokens_per_unit tokens.
+def test_mfma_workgroup_count():
+    # One workgroup = one 128-feature block of one channel and layer over
+    # tokens_per_unit tokens (a multiple of the 64 tokens four 16-token tiles cover).
     kv, ch, p = gqa(T=32768, L=80, H=8, D=128, m=64, paged=True, pages=2048)
     names, info = plan_names(kv, ch, p)
-    rt = info.tokens_per_unit
-    assert rt % 16 == 0
-    assert info.units == 80 * 2 * (8 * 128 // 64) * (-(-32768 // rt))
+    bt = info.tokens_per_unit
+    assert bt % 64 == 0
+    assert info.units == 80 * 2 * (8 * 128 // 128) * (-(-32768 // bt))

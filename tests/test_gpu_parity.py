@@ -93,3 +93,55 @@ def test_generic_kernel(key, rank):
 def test_fp32_mode():
     w = synth.get("tiny_mha").with_(dtype="fp32")
     _run_case(w, w.rank, expect=["generic", "generic"])
+
+
+# ----------------------------------------------------------------- shapes and edge cases
+
+def _gqa(**kw):
+    base = dict(key="shape", wid=50, family="gqa", layers=2, heads=2, head_dim=128, theta=1e4,
+                rank=8, tokens=100)
+    base.update(kw)
+    return synth.Workload(**base)
+
+
+@pytest.mark.parametrize("D,r,H,m,T", [
+    (128, 32, 2, 8, 100),     # partial rotary, partner 2 lanes away
+    (64, 16, 4, 3, 77),       # partner 1 lane away, odd rank (element loads)
+    (256, 128, 2, 24, 50),    # head spans two feature blocks
+    (128, 64, 3, 96, 130),    # rank padded to 128 (4 k-steps)
+    (32, 32, 4, 128, 41),     # four heads per feature block, largest tuned rank
+    (128, 128, 1, 1, 17),     # rank 1
+    (64, 64, 3, 5, 1),        # one token; F = 192 leaves half a block idle
+    (96, 32, 2, 8, 40),       # dim 96: generic kernel
+])
+def test_shapes(D, r, H, m, T):
+    w = _gqa(head_dim=D, rope_dim=r, heads=H, tokens=T, rank=m)
+    _run_case(w, m, label=f"D={D} r={r} H={H} m={m} T={T}")
+    if r in (16, 32, 64, 128):
+        _run_case(w, 0, label=f"rotation D={D} r={r} H={H} T={T}")
+
+
+@pytest.mark.parametrize("rank", [0, 16])
+def test_chunk_edges(rank):
+    # empty chunks, one-token chunks, delta 0 / +-1 / +-2^20, chunks not aligned to tiles
+    w = _gqa(lens=(1, 0, 17, 1, 64, 0, 33, 1, 200),
+             deltas=(5, 7, 0, -1, 1 << 20, 3, -(1 << 20), 0, 1), rank=16)
+    _run_case(w, rank, label=f"chunk edges rank={rank}")
+
+
+def test_paged_chunk_edges():
+    w = _gqa(lens=(5, 0, 40, 1, 70), deltas=(1, 2, -3, 0, 99999), page_size=16, pool_pages=20,
+             heads=4)
+    _run_case(w, 32, label="paged chunk edges")
+    _run_case(w, 0, label="paged chunk edges rotation")
+
+
+def test_delta_zero_rotation_only_is_untouched():
+    w = _gqa(lens=(50, 30), deltas=(0, 0))
+    inp = synth.make_inputs(w, 0, device=DEV)
+    before = [parity.host_bits(b) for b in inp.buffers]
+    ops.run(inp)
+    torch.cuda.synchronize()
+    after = [parity.host_bits(b) for b in inp.buffers]
+    for a, b in zip(after, before):
+        assert np.array_equal(a, b)
