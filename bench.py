@@ -194,7 +194,7 @@ def main():
         "copy_kernel_gbps": round(copy_gbps, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "relocate_patch_mfma" if ranks[dominant] > 0 else "rotate_bf16",
+            "kernel": "relocate_patch_rows" if ranks[dominant] > 0 else "rotate_rows",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -251,7 +251,7 @@ def cpu_baseline(w, ranks, seconds: float):
     ww = w.with_(layers=layers)
     probs = prepare(ww)
     reps, t = 0, 0.0
-    while reps < 10 and (reps == 0 or t < seconds):
+    while reps < 40 and (reps == 0 or t < seconds):
         t += step(ww, probs)
         reps += 1
     b = reps * sum(synth.algorithmic_bytes(ww, r) for r in ranks)

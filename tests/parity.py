@@ -152,3 +152,90 @@ def check_problem(inp, run, flags: int = 0) -> Report:
     for g, o, yy, ss in zip(after, out, y, s):
         compare(g, o, yy, ss, inp.rank, rep)
     return rep
+
+
+def _element_index(inp, c, layer, t, h):
+    """Flat element index of (layer, token t, head h, dim 0) of channel c in its buffer,
+    from the oracle's addressing."""
+    from oracle import oracle as orc
+    lay = inp.layouts[c]
+    w = inp.workload
+    return int(lay.get("offset", 0)) + orc.row_offset(lay, w.page_size, inp.struct.block_table,
+                                                      layer, t, h)
+
+
+def sample_rows(inp, n, seed=0):
+    """(layer, token) pairs: random ones plus the first and last tokens, chunk edges and
+    the last layer."""
+    rng = np.random.default_rng(seed)
+    w, st = inp.workload, inp.struct
+    T, L = st.total_tokens, w.layers
+    rows = {(0, 0), (L - 1, T - 1), (L - 1, 0), (0, T - 1)}
+    for j in range(min(st.num_chunks, 16)):
+        a, b = int(st.offsets[j]), int(st.offsets[j + 1])
+        if b > a:
+            rows.add((int(rng.integers(L)), a))
+            rows.add((int(rng.integers(L)), b - 1))
+    while len(rows) < n:
+        rows.add((int(rng.integers(L)), int(rng.integers(T))))
+    return sorted(rows)
+
+
+def sampled_check(inp, run, n=1024, seed=0) -> Report:
+    """Run `run(inp)` at full size and check sampled rows of every computed channel
+    against the oracle, row by row."""
+    import torch
+    from oracle import oracle as orc
+    w, st = inp.workload, inp.struct
+    rows = sample_rows(inp, n, seed)
+    chans = [c for c, lay in enumerate(inp.layouts) if inp.rank > 0 or lay["rope_dim"] > 0]
+    idx = {}
+    for c in chans:
+        lay = inp.layouts[c]
+        D, H = lay["dim"], lay["heads"]
+        ii = np.empty((len(rows), H * D), dtype=np.int64)
+        for k, (l, t) in enumerate(rows):
+            for h in range(H):
+                ii[k, h * D:(h + 1) * D] = _element_index(inp, c, l, t, h) + np.arange(D)
+        idx[c] = ii
+
+    def gather(c):
+        buf = inp.buffers[inp.layouts[c]["buffer"]].view(-1)
+        g = buf[torch.as_tensor(idx[c].ravel(), device=buf.device)].view(len(rows), -1)
+        return host_bits(g).reshape(len(rows), -1)
+
+    before = {c: gather(c) for c in chans}
+    us, vs = {}, {}
+    if inp.rank > 0:
+        li = torch.as_tensor([l for l, _ in rows], device=inp.U[0].device)
+        ti = torch.as_tensor([t for _, t in rows], device=inp.U[0].device)
+        for c in chans:
+            us[c] = host_bits(inp.U[c][li, ti]).reshape(len(rows), -1)
+            vs[c] = host_bits(inp.V[c]).reshape(w.layers, st.num_chunks, -1, inp.rank)
+    run(inp)
+    torch.cuda.synchronize()
+    after = {c: gather(c) for c in chans}
+    rep = Report()
+    for c in chans:
+        lay = inp.layouts[c]
+        for k, (l, t) in enumerate(rows):
+            j = int(np.searchsorted(st.offsets, t, side="right") - 1)
+            d = int(st.delta[j])
+            u = us[c][k] if inp.rank > 0 else None
+            V = vs[c][l, j] if inp.rank > 0 else None
+            x = before[c][k]
+            o = orc.row(x, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, u, V)
+            xf = bf16_value(x)
+            uf = None if u is None else bf16_value(u)
+            Vf = None if V is None else bf16_value(V)
+            y = orc.row_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, uf, Vf)
+            s = orc.row_magnitude_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d,
+                                      uf, Vf)
+            if inp.rank == 0:  # only rotated dims of chunks that move are computed
+                moved = np.zeros(lay["heads"] * lay["dim"], bool)
+                if d != 0:
+                    for h in range(lay["heads"]):
+                        moved[h * lay["dim"]:h * lay["dim"] + lay["rope_dim"]] = True
+                s = np.where(moved, s, -1.0)
+            compare(after[c][k], o, y, s, inp.rank, rep)
+    return rep

@@ -1,0 +1,34 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times
+(the library's default plan): sampled rows of every computed channel are checked
+against the CPU oracle row by row; rows include first/last tokens and chunk edges."""
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from rope_relocation_rank_amd import kamera, ops, synth  # noqa: E402
+
+import parity  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+CASES = [("tiny_mha", 4), ("qwen25vl7b_segment", 0), ("qwen25vl7b_segment", 32),
+         ("llama3_8b_reorder", 16), ("deepseek_v3_mla", 64), ("long_video_72b_paged", 64)]
+
+
+@pytest.mark.parametrize("key,rank", CASES)
+def test_full_size_sampled(key, rank):
+    w = synth.get(key)
+    print(f"\n[full] {w.note} rank={rank}", flush=True)
+    inp = synth.make_inputs(w, rank, device="cuda:0", pass_id=1 if rank == 0 and key.startswith("qwen") else 0)
+    info = ops.plan(inp)
+    untouched = None
+    if rank == 0:
+        untouched = [b.clone() for c, b in enumerate(inp.buffers) if inp.layouts[c]["rope_dim"] == 0]
+    rep = parity.sampled_check(inp, ops.run, n=1024 if w.layers > 1 else 256)
+    print(f"[full] kernels={[kamera.KERNEL_NAMES[k] for k in info.kernel]} {rep}", flush=True)
+    assert rep.ok(), str(rep)
+    assert rep.band_only <= max(2, rep.computed // 10000), str(rep)
+    if untouched:  # rotation only: the value channel is bit-for-bit unchanged
+        vb = [b for c, b in enumerate(inp.buffers) if inp.layouts[c]["rope_dim"] == 0]
+        for a, b in zip(untouched, vb):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
