@@ -229,9 +229,13 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
   }
   if (use[0] || use[1]) {
     plan->launches++;
-    // Each of the 4 wavefronts of a workgroup streams `tpw` 16-token tiles.
-    int tpw = env_int("KAMERA_TILES_PER_WAVE", 4);
-    if (tpw < 1 || tpw > kamera::kMaxBlockTokens / 64) tpw = 4;
+    // Each of the 4 wavefronts of a workgroup streams `tpw` 16-token tiles.  The
+    // workgroup stages 8 KB of feature factor per 32 ranks once per chunk, so larger
+    // ranks take more tiles per wave (measured best: 2 tiles at rank <= 32, 4 at 64).
+    const int mk = (m + 31) / 32;
+    const int dflt = std::min(8, 2 * (mk == 3 ? 4 : mk));
+    int tpw = env_int("KAMERA_TILES_PER_WAVE", dflt);
+    if (tpw < 1 || tpw > kamera::kMaxBlockTokens / 64) tpw = dflt;
     plan->tiles_per_wave = tpw;
     plan->tile_unroll = env_int("KAMERA_TILE_UNROLL", 1) == 2 ? 2 : 1;
     plan->block_tokens = 64 * tpw;

@@ -247,20 +247,43 @@ __device__ __forceinline__ int64_t slot_staged(const CommonArgs& cm, const int* 
   return t * slot_stride;
 }
 
+// Same as slot_staged in 32-bit arithmetic, for channels whose per-layer extent is
+// below 2^31 elements; PAGED selects the addressing at compile time.
+template <bool PAGED>
+__device__ __forceinline__ int32_t slot32(const CommonArgs& cm, const int* sbt, int p0,
+                                          int32_t page_stride, int32_t slot_stride, int t) {
+  if constexpr (PAGED) {
+    int pi, si;
+    if (cm.page_shift >= 0) {
+      pi = t >> cm.page_shift;
+      si = t & (cm.page_size - 1);
+    } else {
+      pi = t / cm.page_size;
+      si = t - pi * cm.page_size;
+    }
+    const int pg = sbt[pi - p0];
+    return pg < 0 ? -1 : pg * page_stride + si * slot_stride;
+  } else {
+    return t * slot_stride;
+  }
+}
+
 // Workgroup = `block_tokens` tokens of one layer, every head, taken as rows (token,
 // head) in order.  LPR lanes cover the rotated part of a row (8 dims each); a lane's
 // NeoX partner dims sit LPR/2 lanes away and arrive by a lane exchange; one wave
 // instruction covers 64/LPR consecutive rows.  Wave w takes row groups w, w + 4, ...
-// (UNR of them per pass) and issues all their loads before it looks up the chunk and
-// waits for the phases.  Dims >= rope_dim are never touched; rows of chunks with
-// delta == 0 are not written.
-template <int LPR, int UNR>
-__global__ __launch_bounds__(kBlock) void rotate_rows(ChanArgs ch, CommonArgs cm) {
+// (UNR of them per pass) and issues all their loads first.  Each wavefront then works
+// on its own: it finds the chunks its rows belong to, forms that chunk's phases (one
+// pair frequency per lane, gathered by lane shuffles) and finishes the rows.  Only a
+// paged cache needs a workgroup barrier, once, for the staged block table.  Dims
+// >= rope_dim are never touched; rows of chunks with delta == 0 are not written.
+template <int LPR, int UNR, bool PAGED>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(UNR == 4 ? 4 : 1)))
+void rotate_rows(ChanArgs ch, CommonArgs cm) {
   constexpr int RPI = 64 / LPR;
   constexpr int HX = LPR / 2;
   constexpr int HALF = 8 * HX;
   constexpr int ROWS = kWavesPerBlock * UNR * RPI;  // rows one pass of the block covers
-  __shared__ float2 sph[HALF];
   __shared__ int sbt[kMaxBlockTokens + 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -276,7 +299,7 @@ __global__ __launch_bounds__(kBlock) void rotate_rows(ChanArgs ch, CommonArgs cm
   const int nrows = (int)(t1 - tb0) * H;
   uint16_t* base = (uint16_t*)ch.data + layer * ch.layer_stride + 8 * q;
   int p0 = 0;
-  if (cm.page_size > 0) {
+  if (PAGED) {
     p0 = stage_block_table(cm, tb0, t1, sbt);
     __syncthreads();
   }
@@ -296,27 +319,34 @@ __global__ __launch_bounds__(kBlock) void rotate_rows(ChanArgs ch, CommonArgs cm
         const int tl = R / H;
         const int h = R - tl * H;
         tok[k] = tb0 + tl;
-        const int64_t so = slot_staged(cm, sbt, p0, ch.page_stride, ch.slot_stride, tok[k]);
-        ok[k] = so >= 0;
+        int64_t so;
+        if (PAGED) {
+          so = slot_staged(cm, sbt, p0, ch.page_stride, ch.slot_stride, tok[k]);
+          ok[k] = so >= 0;
+        } else {
+          so = tok[k] * ch.slot_stride;
+        }
         ptr[k] = base + so + (int64_t)h * ch.head_stride;
       }
       if (ok[k]) xv[k] = load_nt(ptr[k]);
     }
-    int64_t t0 = tb0 + rbase / H;
-    const int64_t rt1 = min(t1, tb0 + (rbase + ROWS + H - 1) / H);
+    // Token span of this wave's rows in this pass.
+    const int r_first = rbase + wave * RPI;
+    if (r_first >= nrows) continue;
+    const int r_last = min(nrows - 1, rbase + (wave + kWavesPerBlock * (UNR - 1)) * RPI + RPI - 1);
+    int64_t t0 = tb0 + r_first / H;
+    const int64_t tw1 = tb0 + r_last / H + 1;
     ChunkRef c = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0);
     while (true) {
-      const int64_t s1 = min(rt1, c.end);
+      const int64_t s1 = min(tw1, c.end);
       if (s1 > t0 && c.delta != 0) {
-        __syncthreads();
-        if (threadIdx.x < HALF) sph[threadIdx.x] = phase_of(ch.omega[threadIdx.x], c.delta);
-        __syncthreads();
+        float2 own = make_float2(1.f, 0.f);
+        if (lane < HALF) own = phase_of(ch.omega[lane], c.delta);
         float cs[8], sn[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float2 v = sph[fi0 + e];
-          cs[e] = v.x;
-          sn[e] = sgn * v.y;
+          cs[e] = __shfl(own.x, fi0 + e);
+          sn[e] = sgn * __shfl(own.y, fi0 + e);
         }
 #pragma unroll
         for (int k = 0; k < UNR; ++k) {
@@ -330,7 +360,7 @@ __global__ __launch_bounds__(kBlock) void rotate_rows(ChanArgs ch, CommonArgs cm
         }
       }
       t0 = max(t0, s1);
-      if (t0 >= rt1 || c.j + 1 >= cm.num_chunks) break;
+      if (t0 >= tw1 || c.j + 1 >= cm.num_chunks) break;
       c = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0, c.j + 1);
     }
   }
@@ -358,7 +388,7 @@ struct PatchCtx {
   uint16_t* base;       // lane's element (layer, slot 0, head h, dim d0)
   const uint16_t* Ul;   // U of this layer and channel
   const int* sbt;       // staged block table (paged)
-  int64_t page_stride, slot_stride;
+  int32_t page_stride, slot_stride;
   int64_t tb0, t1;
   int p0, m;
   int lane, wave, c16, g;
@@ -367,10 +397,46 @@ struct PatchCtx {
   bool lane_on, rot_lane;
 };
 
-// Tiles of this wave (16-token tile kt with kt = wave mod 4) that meet [t0, s1): TU tiles
-// are loaded together (4 x 16 B of KV and MK x 16 B of U per lane each), then rotated,
-// patched and stored.  HX is the partner lane distance (0: no rotation).  Lane l holds
-// features fb + 8c + n (c = l & 15, n < 8) of tokens 4g .. 4g + 3 (g = l >> 4).
+// KV, row offsets and U fragments of the TU tiles a wave loads together.
+template <int MK, int TU>
+struct TileSet {
+  u32x4_t x[TU][4];
+  int32_t off[TU][4];  // element offset from the lane's base, -1 = no load / no store
+  u32x4_t a[TU][MK];
+};
+
+// Loads tiles kt, kt + 4, ... (TU of them, those below k_hi), keeping tokens in [t0, s1).
+template <int MK, bool M8, bool PAGED, int TU>
+__device__ __forceinline__ void load_tiles(const PatchCtx& c, const CommonArgs& cm, int kt,
+                                           int k_hi, int64_t t0, int64_t s1,
+                                           TileSet<MK, TU>& T) {
+#pragma unroll
+  for (int u = 0; u < TU; ++u) {
+    const int64_t ts = c.tb0 + 16 * (int64_t)(kt + kWavesPerBlock * u);
+    const bool tile_on = kt + kWavesPerBlock * u < k_hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = ts + 4 * c.g + i;
+      T.off[u][i] = -1;
+      T.x[u][i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (tile_on && c.lane_on && t >= t0 && t < s1)
+        T.off[u][i] = slot32<PAGED>(cm, c.sbt, c.p0, c.page_stride, c.slot_stride, (int)t);
+      if (T.off[u][i] >= 0) T.x[u][i] = load_nt(c.base + T.off[u][i]);
+    }
+    const int64_t tu = ts + c.c16;
+    const bool uok = tile_on && tu < c.t1;
+    const uint16_t* urow = c.Ul + (uok ? tu : 0) * c.m;
+#pragma unroll
+    for (int ks = 0; ks < MK; ++ks) {
+      T.a[u][ks] = u32x4_t{0u, 0u, 0u, 0u};
+      if (uok) T.a[u][ks] = load_frag(urow, 32 * ks + 8 * c.g, c.m, M8);
+    }
+  }
+}
+
+// Rotates, patches and stores loaded tiles.  HX is the partner lane distance (0: no
+// rotation).  Lane l holds features fb + 8c + n (c = l & 15, n < 8) of tokens
+// 4g .. 4g + 3 (g = l >> 4).
 //
 // Patch on MFMA 16x16x32 bf16: D[t][col] = C[t][col] + sum_k A[t][k] B[k][col] with
 // A = U rows (tokens), B = V^T.  Column col of MFMA tile n is feature fb + 8 col + n,
@@ -378,80 +444,71 @@ struct PatchCtx {
 // feature n of its 4 tokens: the rotated values are the C operand and the result is
 // already where it is stored.  Output tiles go two at a time (features 2p, 2p + 1 form
 // one packed bf16 pair), so only 8 accumulators are live.
-template <int MK, bool M8, int HX, int TU>
+template <int MK, int HX, int TU>
+__device__ __forceinline__ void finish_tiles(const PatchCtx& c, const u32x4_t* sV,
+                                             const float4* sph2, const TileSet<MK, TU>& T) {
+#pragma unroll
+  for (int u = 0; u < TU; ++u) {
+    u32x4_t out[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {  // features 2pp, 2pp + 1 of the lane's 8
+      float4 ph = make_float4(1.f, 0.f, 1.f, 0.f);
+      if constexpr (HX > 0) ph = sph2[(c.fi0 >> 1) + pp];
+      f32x4_t acc0, acc1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = T.x[u][i][pp];
+        float a0 = bf16_lo(w), a1 = bf16_hi(w);
+        if constexpr (HX > 0) {
+          const uint32_t pw = lane_xor<HX>(w);
+          const float y0 = fmaf(a0, ph.x, bf16_lo(pw) * (c.sgn * ph.y));
+          const float y1 = fmaf(a1, ph.z, bf16_hi(pw) * (c.sgn * ph.w));
+          a0 = c.rot_lane ? y0 : a0;
+          a1 = c.rot_lane ? y1 : a1;
+        }
+        acc0[i] = a0;
+        acc1[i] = a1;
+      }
+#pragma unroll
+      for (int ks = 0; ks < MK; ++ks) {
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, T.a[u][ks]);
+        const bf16x8_t B0 = __builtin_bit_cast(bf16x8_t, sV[((2 * pp) * MK + ks) * 64 + c.lane]);
+        const bf16x8_t B1 =
+            __builtin_bit_cast(bf16x8_t, sV[((2 * pp + 1) * MK + ks) * 64 + c.lane]);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc1, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[i][pp] = pack2(acc0[i], acc1[i]);
+      // Keep the scheduler from hoisting every feature pair's LDS reads at once (it
+      // would hold all B fragments live and lower the occupancy).
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (T.off[u][i] >= 0) store_nt(c.base + T.off[u][i], out[i]);
+  }
+}
+
+// The wave's tiles (16-token tile kt with kt = wave mod 4) that meet [t0, s1), TU at a
+// time; only tokens in [t0, s1) are loaded and stored.  When `use_pre`, `pre` already
+// holds the wave's first group of tiles (loaded before the workgroup staged the chunk).
+template <int MK, bool M8, bool PAGED, int HX, int TU>
 __device__ __forceinline__ void patch_tiles(const PatchCtx& c, const CommonArgs& cm,
                                             const u32x4_t* sV, const float4* sph2,
-                                            int64_t t0, int64_t s1) {
+                                            int64_t t0, int64_t s1,
+                                            const TileSet<MK, TU>& pre, bool use_pre) {
   const int k_lo = (int)((t0 - c.tb0) >> 4);
   const int k_hi = (int)((s1 - c.tb0 + 15) >> 4);
   int kt = k_lo + ((c.wave - k_lo) % kWavesPerBlock + kWavesPerBlock) % kWavesPerBlock;
+  if (use_pre) {
+    finish_tiles<MK, HX, TU>(c, sV, sph2, pre);
+    kt += kWavesPerBlock * TU;
+  }
   for (; kt < k_hi; kt += kWavesPerBlock * TU) {
-    u32x4_t x[TU][4];
-    int32_t off[TU][4];
-    u32x4_t a[TU][MK];
-#pragma unroll
-    for (int u = 0; u < TU; ++u) {
-      const int64_t ts = c.tb0 + 16 * (int64_t)(kt + kWavesPerBlock * u);
-      const bool tile_on = kt + kWavesPerBlock * u < k_hi;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = ts + 4 * c.g + i;
-        off[u][i] = -1;
-        x[u][i] = u32x4_t{0u, 0u, 0u, 0u};
-        if (tile_on && c.lane_on && t >= t0 && t < s1)
-          off[u][i] = (int32_t)slot_staged(cm, c.sbt, c.p0, c.page_stride, c.slot_stride, t);
-        if (off[u][i] >= 0) x[u][i] = load_nt(c.base + off[u][i]);
-      }
-      const int64_t tu = ts + c.c16;
-      const bool uok = tile_on && tu < c.t1;
-      const uint16_t* urow = c.Ul + (uok ? tu : 0) * c.m;
-#pragma unroll
-      for (int ks = 0; ks < MK; ++ks) {
-        a[u][ks] = u32x4_t{0u, 0u, 0u, 0u};
-        if (uok) a[u][ks] = load_frag(urow, 32 * ks + 8 * c.g, c.m, M8);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < TU; ++u) {
-      u32x4_t out[4];
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {  // features 2pp, 2pp + 1 of the lane's 8
-        float4 ph = make_float4(1.f, 0.f, 1.f, 0.f);
-        if constexpr (HX > 0) ph = sph2[(c.fi0 >> 1) + pp];
-        f32x4_t acc0, acc1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = x[u][i][pp];
-          float a0 = bf16_lo(w), a1 = bf16_hi(w);
-          if constexpr (HX > 0) {
-            const uint32_t pw = lane_xor<HX>(w);
-            const float y0 = fmaf(a0, ph.x, bf16_lo(pw) * (c.sgn * ph.y));
-            const float y1 = fmaf(a1, ph.z, bf16_hi(pw) * (c.sgn * ph.w));
-            a0 = c.rot_lane ? y0 : a0;
-            a1 = c.rot_lane ? y1 : a1;
-          }
-          acc0[i] = a0;
-          acc1[i] = a1;
-        }
-#pragma unroll
-        for (int ks = 0; ks < MK; ++ks) {
-          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, a[u][ks]);
-          const bf16x8_t B0 = __builtin_bit_cast(bf16x8_t, sV[((2 * pp) * MK + ks) * 64 + c.lane]);
-          const bf16x8_t B1 =
-              __builtin_bit_cast(bf16x8_t, sV[((2 * pp + 1) * MK + ks) * 64 + c.lane]);
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B0, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc1, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i][pp] = pack2(acc0[i], acc1[i]);
-        // Keep the scheduler from hoisting every feature pair's LDS reads at once (it
-        // would hold all B fragments live and halve the occupancy).
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (off[u][i] >= 0) store_nt(c.base + off[u][i], out[i]);
-    }
+    TileSet<MK, TU> T;
+    load_tiles<MK, M8, PAGED, TU>(c, cm, kt, k_hi, t0, s1, T);
+    finish_tiles<MK, HX, TU>(c, sV, sph2, T);
   }
 }
 
@@ -461,8 +518,9 @@ __device__ __forceinline__ void patch_tiles(const PatchCtx& c, const CommonArgs&
 // then the waves stream their tiles of that chunk.  Workgroups are numbered so that all
 // feature blocks of one token group run on the same XCD (consecutive workgroup ids go
 // to consecutive XCDs), where they share the token group's U rows in that XCD's L2.
-template <int MK, bool M8, int TU>
-__global__ __launch_bounds__(kBlock) void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1,
+template <int MK, bool M8, bool PAGED, int TU>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MK == 1 && TU == 1 ? 4 : 1)))
+void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1,
                                                               CommonArgs cm,
                                                               int64_t blocks_per_layer,
                                                               int xcd_group) {
@@ -513,8 +571,8 @@ __global__ __launch_bounds__(kBlock) void relocate_patch_rows(ChanArgs ch0, Chan
   c.sgn = d0 < (r >> 1) ? -1.f : 1.f;
   const int hx = r >> 4;  // partner lane distance: half / 8
 
-  c.slot_stride = KAMERA_CH(slot_stride);
-  c.page_stride = KAMERA_CH(page_stride);
+  c.slot_stride = (int32_t)KAMERA_CH(slot_stride);
+  c.page_stride = (int32_t)KAMERA_CH(page_stride);
   c.base = (uint16_t*)KAMERA_CH(data) + layer * KAMERA_CH(layer_stride) +
            (int64_t)h * KAMERA_CH(head_stride) + d0;
   c.Ul = (const uint16_t*)KAMERA_CH(U) + layer * cm.total_tokens * m;
@@ -524,48 +582,73 @@ __global__ __launch_bounds__(kBlock) void relocate_patch_rows(ChanArgs ch0, Chan
   c.t1 = min(c.tb0 + (int64_t)cm.block_tokens, cm.total_tokens);
   c.p0 = 0;
   c.sbt = sbt;
-  if (cm.page_size > 0) c.p0 = stage_block_table(cm, c.tb0, c.t1, sbt);
+  if (PAGED) c.p0 = stage_block_table(cm, c.tb0, c.t1, sbt);
 
+  // Stages chunk j's B fragments (and, when rotating, its phases) in LDS.
+  auto stage = [&](const ChunkRef& ck, bool rotate) {
+    const uint16_t* Vj = Vl + (int64_t)ck.j * F * m;
+#pragma unroll
+    for (int u = 0; u < 2 * MK; ++u) {
+      const int it = threadIdx.x + kBlock * u;
+      const int l = it & 63;
+      const int nk = it >> 6;  // n * MK + ks
+      const int n = nk / MK;
+      const int ks = nk - n * MK;
+      const int f = fb + 8 * (l & 15) + n;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (f < F) v = load_frag(Vj + (int64_t)f * m, 32 * ks + 8 * (l >> 4), m, M8);
+      sV[it] = v;
+    }
+    if (rotate && threadIdx.x < (r >> 2)) {
+      const float2 q0 = phase_of(KAMERA_CH(omega[2 * threadIdx.x]), ck.delta);
+      const float2 q1 = phase_of(KAMERA_CH(omega[2 * threadIdx.x + 1]), ck.delta);
+      sph2[threadIdx.x] = make_float4(q0.x, q0.y, q1.x, q1.y);
+    }
+  };
+#define KAMERA_PATCH_SWITCH(PRE, USE)                                                           \
+  switch (rotate ? hx : 0) {                                                                    \
+    case 1: patch_tiles<MK, M8, PAGED, 1, TU>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
+    case 2: patch_tiles<MK, M8, PAGED, 2, TU>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
+    case 4: patch_tiles<MK, M8, PAGED, 4, TU>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
+    case 8: patch_tiles<MK, M8, PAGED, 8, TU>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
+    default: patch_tiles<MK, M8, PAGED, 0, TU>(c, cm, sV, sph2, t0, s1, PRE, USE); break;      \
+  }
+
+  // The wave's first tiles are loaded before anything else, so their HBM latency
+  // overlaps the chunk lookup, the LDS staging and the barrier.
+  const int ntiles = (int)((c.t1 - c.tb0 + 15) >> 4);
+  if (PAGED) __syncthreads();  // staged block table
+  TileSet<MK, TU> pre;
+  load_tiles<MK, M8, PAGED, TU>(c, cm, c.wave, ntiles, c.tb0, c.t1, pre);
+
+  ChunkRef ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, c.tb0);
+  if (ck.end >= c.t1) {
+    // The whole token range lies in one chunk (the common case).
+    const int64_t t0 = c.tb0, s1 = c.t1;
+    const bool rotate = r > 0 && ck.delta != 0;
+    stage(ck, rotate);
+    __syncthreads();
+    KAMERA_PATCH_SWITCH(pre, true)
+    return;
+  }
+  // Several chunks: chunk by chunk, tiles reloaded per chunk.
   int64_t t0 = c.tb0;
-  ChunkRef ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0);
+  bool staged = false;
   while (true) {
     const int64_t s1 = min(c.t1, ck.end);
     if (s1 > t0) {
       const bool rotate = r > 0 && ck.delta != 0;
+      if (staged) __syncthreads();  // LDS still read by the previous chunk's tiles
+      staged = true;
+      stage(ck, rotate);
       __syncthreads();
-      {
-        const uint16_t* Vj = Vl + (int64_t)ck.j * F * m;
-#pragma unroll
-        for (int u = 0; u < 2 * MK; ++u) {
-          const int it = threadIdx.x + kBlock * u;
-          const int l = it & 63;
-          const int nk = it >> 6;  // n * MK + ks
-          const int n = nk / MK;
-          const int ks = nk - n * MK;
-          const int f = fb + 8 * (l & 15) + n;
-          u32x4_t v = {0u, 0u, 0u, 0u};
-          if (f < F) v = load_frag(Vj + (int64_t)f * m, 32 * ks + 8 * (l >> 4), m, M8);
-          sV[it] = v;
-        }
-      }
-      if (rotate && threadIdx.x < (r >> 2)) {
-        const float2 q0 = phase_of(KAMERA_CH(omega[2 * threadIdx.x]), ck.delta);
-        const float2 q1 = phase_of(KAMERA_CH(omega[2 * threadIdx.x + 1]), ck.delta);
-        sph2[threadIdx.x] = make_float4(q0.x, q0.y, q1.x, q1.y);
-      }
-      __syncthreads();
-      switch (rotate ? hx : 0) {
-        case 1: patch_tiles<MK, M8, 1, TU>(c, cm, sV, sph2, t0, s1); break;
-        case 2: patch_tiles<MK, M8, 2, TU>(c, cm, sV, sph2, t0, s1); break;
-        case 4: patch_tiles<MK, M8, 4, TU>(c, cm, sV, sph2, t0, s1); break;
-        case 8: patch_tiles<MK, M8, 8, TU>(c, cm, sV, sph2, t0, s1); break;
-        default: patch_tiles<MK, M8, 0, TU>(c, cm, sV, sph2, t0, s1); break;
-      }
+      KAMERA_PATCH_SWITCH(pre, false)
     }
     t0 = max(t0, s1);
     if (t0 >= c.t1 || ck.j + 1 >= cm.num_chunks) break;
     ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0, ck.j + 1);
   }
+#undef KAMERA_PATCH_SWITCH
 }
 #undef KAMERA_CH
 
@@ -637,11 +720,16 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
                               hipStream_t s) {
   const int64_t blocks = (int64_t)cm.num_layers * cm.token_groups;
   const dim3 grid((unsigned)blocks);
-#define KAMERA_LAUNCH_ROT(LPR)                                                              \
-  do {                                                                                      \
-    if (unroll == 1) hipLaunchKernelGGL((rotate_rows<LPR, 1>), grid, dim3(kBlock), 0, s, ch, cm); \
-    else if (unroll == 2) hipLaunchKernelGGL((rotate_rows<LPR, 2>), grid, dim3(kBlock), 0, s, ch, cm); \
-    else hipLaunchKernelGGL((rotate_rows<LPR, 4>), grid, dim3(kBlock), 0, s, ch, cm);       \
+#define KAMERA_LAUNCH_ROT2(LPR, PG)                                                              \
+  do {                                                                                           \
+    if (unroll == 1) hipLaunchKernelGGL((rotate_rows<LPR, 1, PG>), grid, dim3(kBlock), 0, s, ch, cm); \
+    else if (unroll == 2) hipLaunchKernelGGL((rotate_rows<LPR, 2, PG>), grid, dim3(kBlock), 0, s, ch, cm); \
+    else hipLaunchKernelGGL((rotate_rows<LPR, 4, PG>), grid, dim3(kBlock), 0, s, ch, cm);       \
+  } while (0)
+#define KAMERA_LAUNCH_ROT(LPR)                                  \
+  do {                                                          \
+    if (cm.page_size > 0) KAMERA_LAUNCH_ROT2(LPR, true);       \
+    else KAMERA_LAUNCH_ROT2(LPR, false);                        \
   } while (0)
   switch (ch.rope_dim) {
     case 16: KAMERA_LAUNCH_ROT(2); break;
@@ -651,6 +739,7 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
     default: return hipErrorInvalidValue;
   }
 #undef KAMERA_LAUNCH_ROT
+#undef KAMERA_LAUNCH_ROT2
   return hipGetLastError();
 }
 
@@ -665,17 +754,23 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
   const int xg = (nch == 1 || c0.fblocks == c1.fblocks) ? c0.fblocks : 0;
   const int mk = (cm.rank + 31) / 32;
   const bool m8 = cm.rank % 8 == 0;
-#define KAMERA_LAUNCH_PATCH(MK)                                                               \
+#define KAMERA_LAUNCH_PATCH2(MK, PG)                                                          \
   do {                                                                                        \
-    if (m8 && tile_unroll == 2) hipLaunchKernelGGL((relocate_patch_rows<MK, true, 2>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, xg); \
-    else if (m8) hipLaunchKernelGGL((relocate_patch_rows<MK, true, 1>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, xg); \
-    else hipLaunchKernelGGL((relocate_patch_rows<MK, false, 1>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, xg); \
+    if (m8 && tile_unroll == 2) hipLaunchKernelGGL((relocate_patch_rows<MK, true, PG, 2>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, xg); \
+    else if (m8) hipLaunchKernelGGL((relocate_patch_rows<MK, true, PG, 1>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, xg); \
+    else hipLaunchKernelGGL((relocate_patch_rows<MK, false, PG, 1>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, xg); \
+  } while (0)
+#define KAMERA_LAUNCH_PATCH(MK)                        \
+  do {                                                 \
+    if (cm.page_size > 0) KAMERA_LAUNCH_PATCH2(MK, true); \
+    else KAMERA_LAUNCH_PATCH2(MK, false);               \
   } while (0)
   if (mk == 1) KAMERA_LAUNCH_PATCH(1);
   else if (mk == 2) KAMERA_LAUNCH_PATCH(2);
   else if (mk <= 4) KAMERA_LAUNCH_PATCH(4);
   else return hipErrorInvalidValue;
 #undef KAMERA_LAUNCH_PATCH
+#undef KAMERA_LAUNCH_PATCH2
   return hipGetLastError();
 }
 
