@@ -154,9 +154,11 @@ KAMERA_API kamera_status kamera_relocate_patch(const kamera_kv_desc* kv, const k
 typedef struct {
   int32_t kernel[2];       /* per channel: 0 none, 1 rotate (tuned), 2 rotate+patch MFMA (tuned),
                               3 generic */
-  int32_t launches;        /* kernel launches the call would make */
-  int32_t tokens_per_unit; /* tokens one wavefront streams per unit of work (tuned kernels) */
-  int64_t units;           /* wavefront work units of the tuned launch */
+  int32_t launches;        /* kernel launches the call would make (the rotate+patch kernel
+                              takes a second launch for the token groups that chunk
+                              boundaries cut when num_chunks > 1) */
+  int32_t tokens_per_unit; /* tokens one workgroup of a tuned kernel covers */
+  int64_t units;           /* workgroups of the tuned launches */
 } kamera_plan_info;
 
 KAMERA_API kamera_status kamera_plan(const kamera_kv_desc* kv, const kamera_chunks* chunks,

@@ -239,9 +239,14 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
     plan->tiles_per_wave = tpw;
     plan->tile_unroll = env_int("KAMERA_TILE_UNROLL", 1) == 2 ? 2 : 1;
     plan->block_tokens = 64 * tpw;
+    // A second launch covers the token groups that chunk boundaries cut.
+    const int64_t groups = ceil_div(T, plan->block_tokens);
+    const int64_t tail_units =
+        ch->num_chunks < 2 ? 0 : std::min<int64_t>((int64_t)ch->num_chunks - 1, groups);
+    if (tail_units > 0) plan->launches++;
     for (int c = 0; c < kv->num_channels; ++c)
       if (use[c])
-        plan->units += (int64_t)kv->num_layers * ceil_div(T, plan->block_tokens) *
+        plan->units += (int64_t)kv->num_layers * (groups + tail_units) *
                        ceil_div((int64_t)kv->ch[c].heads * kv->ch[c].dim, 128);
   }
   return KAMERA_OK;

@@ -37,6 +37,7 @@ struct CommonArgs {
   int32_t rank;
   int32_t block_tokens;     // tokens one workgroup covers (tuned kernels)
   int32_t page_shift;       // log2(page_size) when it is a power of two, else -1
+  int32_t tail_mode;        // rotate+patch tail launch: 1 by boundary, 2 by token group
 };
 
 // Rotation only, bf16, 16-byte accesses: rope_dim in {16, 32, 64, 128}.
@@ -45,7 +46,8 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
                               hipStream_t s);
 
 // Rotation + rank-m patch on MFMA, bf16: see kernels.hip for the shape conditions.
-// Covers nch (1 or 2) channels in one launch.
+// Covers nch (1 or 2) channels in one launch, plus a second launch for the token groups
+// that chunk boundaries cut when there is more than one chunk.
 // `tile_unroll` 16-token tiles (1 or 2) are loaded together by each wavefront.
 hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonArgs& cm,
                                       int tile_unroll, hipStream_t s);

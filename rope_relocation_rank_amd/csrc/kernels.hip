@@ -108,15 +108,6 @@ __device__ __forceinline__ u32x4_t lane_xor4(const u32x4_t& v) {
   return r;
 }
 
-__device__ __forceinline__ u32x4_t lane_xor4_rt(const u32x4_t& v, int x) {
-  switch (x) {
-    case 1: return lane_xor4<1>(v);
-    case 2: return lane_xor4<2>(v);
-    case 4: return lane_xor4<4>(v);
-    default: return lane_xor4<8>(v);
-  }
-}
-
 // ------------------------------------------------------------------ index helpers
 
 // Chunk that owns token t: the last j with offsets[j] <= t (offsets[0] == 0 <= t), with
@@ -513,17 +504,23 @@ __device__ __forceinline__ void patch_tiles(const PatchCtx& c, const CommonArgs&
 }
 
 // Workgroup = one 128-feature block of one channel and layer over `block_tokens` tokens;
-// wave w takes the 16-token tiles w, w + 4, ....  Each chunk the workgroup meets is
+// wave w takes the 16-token tiles w, w + 4, ....  The chunk the workgroup works on is
 // staged once in LDS (the B fragments of its feature factor, the phases of its delta),
 // then the waves stream their tiles of that chunk.  Workgroups are numbered so that all
 // feature blocks of one token group run on the same XCD (consecutive workgroup ids go
 // to consecutive XCDs), where they share the token group's U rows in that XCD's L2.
-template <int MK, bool M8, bool PAGED, int TU>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MK == 1 && TU == 1 ? 4 : 1)))
-void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1,
-                                                              CommonArgs cm,
-                                                              int64_t blocks_per_layer,
-                                                              int xcd_group) {
+//
+// TAIL = false covers every token group from its first token to the end of the chunk
+// that holds it (all of it in the common case of a group inside one chunk).  TAIL =
+// true covers the rest of the groups that a chunk boundary cuts: the grid then runs
+// over boundaries (cm.tail_mode == 1: unit k handles boundary offsets[k + 1] when it is
+// the first boundary inside its group) or over groups (cm.tail_mode == 2, when chunks
+// outnumber groups).  Keeping that rarer loop over chunks in its own kernel keeps the
+// common kernel's register count (and so its occupancy) down.
+template <int MK, bool M8, bool PAGED, int TU, bool TAIL>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(!TAIL && MK <= 2 && TU == 1 ? 4 : 1)))
+void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t blocks_per_layer,
+                         int xcd_group) {
   __shared__ u32x4_t sV[8 * MK * 64];
   __shared__ float4 sph2[kMaxTunedHalf / 2];  // (cos, sin) of pairs 2p and 2p + 1
   __shared__ int sbt[kMaxBlockTokens + 1];
@@ -578,8 +575,33 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1,
   c.Ul = (const uint16_t*)KAMERA_CH(U) + layer * cm.total_tokens * m;
   const uint16_t* Vl = (const uint16_t*)KAMERA_CH(V) + layer * (int64_t)cm.num_chunks * F * m;
 
-  c.tb0 = tg * cm.block_tokens;
-  c.t1 = min(c.tb0 + (int64_t)cm.block_tokens, cm.total_tokens);
+  // Token group and the first token this workgroup works on.
+  [[maybe_unused]] int64_t start;
+  [[maybe_unused]] int from = 0;  // chunk index to search from
+  if constexpr (TAIL) {
+    if (cm.tail_mode == 1) {
+      const int k = (int)tg + 1;  // boundary offsets[k], 1 <= k < num_chunks
+      const int64_t o = cm.offsets[k];
+      const int64_t g = o / cm.block_tokens;
+      c.tb0 = g * cm.block_tokens;
+      c.t1 = min(c.tb0 + (int64_t)cm.block_tokens, cm.total_tokens);
+      // Only the first boundary strictly inside the group starts work there.
+      if (!(o > c.tb0 && o < c.t1) || cm.offsets[k - 1] > c.tb0) return;
+      start = o;
+      from = k;
+    } else {
+      c.tb0 = tg * cm.block_tokens;
+      c.t1 = min(c.tb0 + (int64_t)cm.block_tokens, cm.total_tokens);
+      const ChunkRef first = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, c.tb0);
+      if (first.end <= c.tb0 || first.end >= c.t1) return;  // no boundary inside
+      start = first.end;
+      from = first.j + 1;
+    }
+  } else {
+    c.tb0 = tg * cm.block_tokens;
+    c.t1 = min(c.tb0 + (int64_t)cm.block_tokens, cm.total_tokens);
+    start = c.tb0;
+  }
   c.p0 = 0;
   c.sbt = sbt;
   if (PAGED) c.p0 = stage_block_table(cm, c.tb0, c.t1, sbt);
@@ -599,11 +621,9 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1,
       if (f < F) v = load_frag(Vj + (int64_t)f * m, 32 * ks + 8 * (l >> 4), m, M8);
       sV[it] = v;
     }
-    if (rotate && threadIdx.x < (r >> 2)) {
-      const float2 q0 = phase_of(KAMERA_CH(omega[2 * threadIdx.x]), ck.delta);
-      const float2 q1 = phase_of(KAMERA_CH(omega[2 * threadIdx.x + 1]), ck.delta);
-      sph2[threadIdx.x] = make_float4(q0.x, q0.y, q1.x, q1.y);
-    }
+    // One pair frequency per thread; (cos, sin) of pairs 2p and 2p + 1 are adjacent.
+    if (rotate && threadIdx.x < (r >> 1))
+      reinterpret_cast<float2*>(sph2)[threadIdx.x] = phase_of(KAMERA_CH(omega[threadIdx.x]), ck.delta);
   };
 #define KAMERA_PATCH_SWITCH(PRE, USE)                                                           \
   switch (rotate ? hx : 0) {                                                                    \
@@ -614,39 +634,46 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1,
     default: patch_tiles<MK, M8, PAGED, 0, TU>(c, cm, sV, sph2, t0, s1, PRE, USE); break;      \
   }
 
-  // The wave's first tiles are loaded before anything else, so their HBM latency
-  // overlaps the chunk lookup, the LDS staging and the barrier.
-  const int ntiles = (int)((c.t1 - c.tb0 + 15) >> 4);
   if (PAGED) __syncthreads();  // staged block table
-  TileSet<MK, TU> pre;
-  load_tiles<MK, M8, PAGED, TU>(c, cm, c.wave, ntiles, c.tb0, c.t1, pre);
-
-  ChunkRef ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, c.tb0);
-  if (ck.end >= c.t1) {
-    // The whole token range lies in one chunk (the common case).
-    const int64_t t0 = c.tb0, s1 = c.t1;
+  if constexpr (!TAIL) {
+    const int ntiles = (int)((c.t1 - c.tb0 + 15) >> 4);
+    // The wave's first tiles are loaded before anything else, so their HBM latency
+    // overlaps the chunk lookup, the LDS staging and the barrier.
+    TileSet<MK, TU> pre;
+    load_tiles<MK, M8, PAGED, TU>(c, cm, c.wave, ntiles, c.tb0, c.t1, pre);
+    const ChunkRef ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, c.tb0);
+    const int64_t t0 = c.tb0, s1 = min(c.t1, ck.end);
+    if (s1 <= t0) return;  // offsets that do not cover the group: nothing here
+    // Tokens past the chunk's end belong to the tail kernel.
+#pragma unroll
+    for (int u = 0; u < TU; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (c.tb0 + 16 * (c.wave + kWavesPerBlock * u) + 4 * c.g + i >= s1) pre.off[u][i] = -1;
     const bool rotate = r > 0 && ck.delta != 0;
     stage(ck, rotate);
     __syncthreads();
     KAMERA_PATCH_SWITCH(pre, true)
-    return;
-  }
-  // Several chunks: chunk by chunk, tiles reloaded per chunk.
-  int64_t t0 = c.tb0;
-  bool staged = false;
-  while (true) {
-    const int64_t s1 = min(c.t1, ck.end);
-    if (s1 > t0) {
-      const bool rotate = r > 0 && ck.delta != 0;
-      if (staged) __syncthreads();  // LDS still read by the previous chunk's tiles
-      staged = true;
-      stage(ck, rotate);
-      __syncthreads();
-      KAMERA_PATCH_SWITCH(pre, false)
+  } else {
+    // The remaining chunks of the group, one after the other.
+    TileSet<MK, TU> none;
+    int64_t t0 = start;
+    ChunkRef ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0, from);
+    bool staged = false;
+    while (true) {
+      const int64_t s1 = min(c.t1, ck.end);
+      if (s1 > t0) {
+        const bool rotate = r > 0 && ck.delta != 0;
+        if (staged) __syncthreads();  // LDS still read by the previous chunk's tiles
+        staged = true;
+        stage(ck, rotate);
+        __syncthreads();
+        KAMERA_PATCH_SWITCH(none, false)
+      }
+      t0 = max(t0, s1);
+      if (t0 >= c.t1 || ck.j + 1 >= cm.num_chunks) break;
+      ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0, ck.j + 1);
     }
-    t0 = max(t0, s1);
-    if (t0 >= c.t1 || ck.j + 1 >= cm.num_chunks) break;
-    ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0, ck.j + 1);
   }
 #undef KAMERA_PATCH_SWITCH
 }
@@ -743,32 +770,51 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
   return hipGetLastError();
 }
 
-hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonArgs& cm,
+hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonArgs& cm_in,
                                       int tile_unroll, hipStream_t s) {
   ChanArgs c0 = ch[0];
   ChanArgs c1 = nch > 1 ? ch[1] : ch[0];
   if (nch == 1) c1.blocks = 0;
-  const int64_t bpl = c0.blocks + c1.blocks;
-  const dim3 grid((unsigned)((int64_t)cm.num_layers * bpl));
+  CommonArgs cm = cm_in;
+  cm.tail_mode = 0;
+  int64_t bpl = c0.blocks + c1.blocks;
+  dim3 grid((unsigned)((int64_t)cm.num_layers * bpl));
   // XCD grouping needs one feature-block count for every channel of the launch.
   const int xg = (nch == 1 || c0.fblocks == c1.fblocks) ? c0.fblocks : 0;
   const int mk = (cm.rank + 31) / 32;
   const bool m8 = cm.rank % 8 == 0;
-#define KAMERA_LAUNCH_PATCH2(MK, PG)                                                          \
-  do {                                                                                        \
-    if (m8 && tile_unroll == 2) hipLaunchKernelGGL((relocate_patch_rows<MK, true, PG, 2>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, xg); \
-    else if (m8) hipLaunchKernelGGL((relocate_patch_rows<MK, true, PG, 1>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, xg); \
-    else hipLaunchKernelGGL((relocate_patch_rows<MK, false, PG, 1>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, xg); \
+#define KAMERA_LAUNCH_PATCH2(MK, PG, TL, XG)                                                   \
+  do {                                                                                         \
+    if (m8 && tile_unroll == 2 && !TL) hipLaunchKernelGGL((relocate_patch_rows<MK, true, PG, 2, false>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, XG); \
+    else if (m8) hipLaunchKernelGGL((relocate_patch_rows<MK, true, PG, 1, TL>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, XG); \
+    else hipLaunchKernelGGL((relocate_patch_rows<MK, false, PG, 1, TL>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, XG); \
   } while (0)
-#define KAMERA_LAUNCH_PATCH(MK)                        \
+#define KAMERA_LAUNCH_PATCH(MK, TL, XG)                        \
+  do {                                                         \
+    if (cm.page_size > 0) KAMERA_LAUNCH_PATCH2(MK, true, TL, XG); \
+    else KAMERA_LAUNCH_PATCH2(MK, false, TL, XG);               \
+  } while (0)
+#define KAMERA_LAUNCH_MK(TL, XG)                       \
   do {                                                 \
-    if (cm.page_size > 0) KAMERA_LAUNCH_PATCH2(MK, true); \
-    else KAMERA_LAUNCH_PATCH2(MK, false);               \
+    if (mk == 1) KAMERA_LAUNCH_PATCH(1, TL, XG);       \
+    else if (mk == 2) KAMERA_LAUNCH_PATCH(2, TL, XG);  \
+    else if (mk <= 4) KAMERA_LAUNCH_PATCH(4, TL, XG);  \
+    else return hipErrorInvalidValue;                  \
   } while (0)
-  if (mk == 1) KAMERA_LAUNCH_PATCH(1);
-  else if (mk == 2) KAMERA_LAUNCH_PATCH(2);
-  else if (mk <= 4) KAMERA_LAUNCH_PATCH(4);
-  else return hipErrorInvalidValue;
+  KAMERA_LAUNCH_MK(false, xg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || cm.num_chunks < 2) return e;
+  // Groups that a chunk boundary cuts: indexed by boundary, or by group when chunks
+  // outnumber groups.
+  const int64_t nb = (int64_t)cm.num_chunks - 1;
+  cm.tail_mode = nb <= cm.token_groups ? 1 : 2;
+  const int64_t units = cm.tail_mode == 1 ? nb : cm.token_groups;
+  c0.blocks = units * c0.fblocks;
+  c1.blocks = nch > 1 ? units * c1.fblocks : 0;
+  bpl = c0.blocks + c1.blocks;
+  grid = dim3((unsigned)((int64_t)cm.num_layers * bpl));
+  KAMERA_LAUNCH_MK(true, 0);
+#undef KAMERA_LAUNCH_MK
 #undef KAMERA_LAUNCH_PATCH
 #undef KAMERA_LAUNCH_PATCH2
   return hipGetLastError();

@@ -281,3 +281,22 @@ def test_mfma_workgroup_count():
     bt = info.tokens_per_unit
     assert bt % 64 == 0
     assert info.units == 80 * 2 * (8 * 128 // 128) * (-(-32768 // bt))
+
+
+def test_chunk_boundary_tail_launch():
+    # With more than one chunk a second launch covers the token groups that chunk
+    # boundaries cut: one unit per boundary, or per token group when chunks outnumber
+    # the groups.
+    _, info1 = plan_names(*gqa(T=4096, m=32, n=1))
+    assert info1.launches == 1
+    bt = info1.tokens_per_unit
+    groups = -(-4096 // bt)
+    fb = 4 * 128 // 128
+    _, info = plan_names(*gqa(T=4096, m=32, n=5))
+    assert info.launches == 2
+    assert info.units == 28 * 2 * fb * (groups + 4)
+    _, info = plan_names(*gqa(T=4096, m=32, n=groups + 100))
+    assert info.launches == 2
+    assert info.units == 28 * 2 * fb * (2 * groups)
+    _, info = plan_names(*gqa(T=4096, m=0, n=5))  # rotation only: one kernel, no tail
+    assert info.launches == 1

@@ -129,6 +129,24 @@ def test_chunk_edges(rank):
     _run_case(w, rank, label=f"chunk edges rank={rank}")
 
 
+@pytest.mark.parametrize("rank", [8, 64, 100])
+def test_chunk_boundary_groups(rank):
+    # Token groups that chunk boundaries cut go to a second launch.  Boundaries here:
+    # one on a group start (512 is a multiple of every group size), several inside one
+    # group, an empty chunk; then many tiny chunks, so that boundaries outnumber groups.
+    lens = (512, 3, 0, 250, 1, 1, 700, 40)
+    deltas = (3, -5, 9, 0, 1 << 16, -7, 11, 2)
+    _run_case(_gqa(lens=lens, deltas=deltas, rank=rank), rank,
+              label=f"boundaries by boundary rank={rank}")
+    _run_case(_gqa(lens=lens, deltas=deltas, rank=rank, page_size=16, pool_pages=110), rank,
+              label=f"boundaries by boundary, paged, rank={rank}")
+    rng = np.random.default_rng(rank)
+    lens2 = tuple(int(x) for x in rng.integers(0, 10, size=40))
+    deltas2 = tuple(int(x) for x in rng.integers(-1000, 1000, size=40))
+    _run_case(_gqa(lens=lens2, deltas=deltas2, rank=rank), rank,
+              label=f"boundaries by group rank={rank}")
+
+
 def test_paged_chunk_edges():
     w = _gqa(lens=(5, 0, 40, 1, 70), deltas=(1, 2, -3, 0, 99999), page_size=16, pool_pages=20,
              heads=4)
