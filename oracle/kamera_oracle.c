@@ -320,6 +320,89 @@ int orc_relocate_patch_ex(const orc_problem* p, double* const* y_out, double* co
 
 int orc_relocate_patch(const orc_problem* p) { return orc_relocate_patch_ex(p, NULL, NULL); }
 
+/* Recall, the reversible eviction of [K §3, the three cheap window operations]: an
+ * evicted chunk is rebuilt from its canonical store with a patch for its new context.
+ * Out of place: each row is read from `src` (its layout, block table, chunks, deltas,
+ * factors and rank) and the whole result row goes to the same token of `dst`, of
+ * which only the channel data pointers, strides, page size and block table are read.
+ * Every element of the row is written; elements that neither the rotation nor the
+ * patch changes are copied bit for bit, so a chunk with delta 0 and no patch is a
+ * plain copy.  src is never written.  y_out / s_out are laid out like dst; the
+ * computed elements get their fp64 value and magnitude bound there.  Returns 0, or -1
+ * on bad arguments. */
+int orc_recall_patch_ex(const orc_problem* src, const orc_problem* dst, double* const* y_out,
+                        double* const* s_out) {
+    if (!src || !dst || src->num_channels < 1 || src->num_channels > 2 || src->rank < 0 ||
+        (src->dtype != ORC_BF16 && src->dtype != ORC_F32) || dst->dtype != src->dtype ||
+        dst->num_channels != src->num_channels || dst->num_layers != src->num_layers)
+        return -1;
+    for (int c = 0; c < src->num_channels; ++c)
+        if (dst->ch[c].heads != src->ch[c].heads || dst->ch[c].dim != src->ch[c].dim)
+            return -1;
+    int64_t T = src->total_tokens, L = src->num_layers;
+    if (T == 0 || L == 0 || src->num_chunks == 0) return 0;
+    int es = src->dtype == ORC_BF16 ? 2 : 4;
+    int m = src->rank;
+    int bad = 0;
+    for (int c = 0; c < src->num_channels; ++c) {
+        const orc_channel* sc = &src->ch[c];
+        const orc_channel* dc = &dst->ch[c];
+        int64_t F = (int64_t)sc->heads * sc->dim;
+        double* yo = y_out ? y_out[c] : NULL;
+        double* so = s_out ? s_out[c] : NULL;
+#pragma omp parallel for collapse(2) schedule(dynamic, 64) reduction(|:bad)
+        for (int64_t l = 0; l < L; ++l) {
+            for (int64_t t = 0; t < T; ++t) {
+                int64_t j = chunk_of(src, t);
+                if (j < 0) { bad = 1; continue; }
+                int64_t dj = src->delta[j];
+                char* row = (char*)malloc((size_t)(F * es));
+                char* out = (char*)malloc((size_t)(F * es));
+                double* x = (double*)malloc(sizeof(double) * F);
+                double* y = (double*)malloc(sizeof(double) * F);
+                double* s = (double*)malloc(sizeof(double) * F);
+                double* ud = (double*)malloc(sizeof(double) * (m > 0 ? m : 1));
+                double* vd = (double*)malloc(sizeof(double) * (m > 0 ? F * m : 1));
+                for (int64_t h = 0; h < sc->heads; ++h) {
+                    int64_t o = orc_row_offset(sc, src->page_size, src->block_table, l, t, h);
+                    memcpy(row + h * sc->dim * es, (const char*)sc->data + o * es, (size_t)sc->dim * es);
+                }
+                const void* u = NULL;
+                const void* V = NULL;
+                if (m > 0) {
+                    u = (const char*)sc->U + ((l * T + t) * m) * es;
+                    V = (const char*)sc->V + ((l * src->num_chunks + j) * F * m) * es;
+                    for (int k = 0; k < m; ++k) ud[k] = load_elem(src->dtype, u, k);
+                    for (int64_t i = 0; i < F * m; ++i) vd[i] = load_elem(src->dtype, V, i);
+                }
+                if (yo) {
+                    for (int64_t f = 0; f < F; ++f) x[f] = load_elem(src->dtype, row, f);
+                    orc_row_f64(x, y, sc->heads, sc->dim, sc->rope_dim, src->theta, dj, m, ud, vd);
+                    orc_row_magnitude_f64(x, s, sc->heads, sc->dim, sc->rope_dim, src->theta, dj, m,
+                                          ud, vd);
+                }
+                if (orc_row(src->dtype, row, out, sc->heads, sc->dim, sc->rope_dim, src->theta, dj,
+                            m, u, V) != 0)
+                    bad = 1;
+                for (int64_t h = 0; h < sc->heads; ++h) {
+                    int64_t o = orc_row_offset(dc, dst->page_size, dst->block_table, l, t, h);
+                    memcpy((char*)dc->data + o * es, out + h * sc->dim * es, (size_t)sc->dim * es);
+                    if (yo) {
+                        for (int d = 0; d < sc->dim; ++d) {
+                            int moved = m > 0 || (dj != 0 && d < sc->rope_dim);
+                            if (!moved) continue;
+                            yo[o + d] = y[h * sc->dim + d];
+                            if (so) so[o + d] = s[h * sc->dim + d];
+                        }
+                    }
+                }
+                free(row); free(out); free(x); free(y); free(s); free(ud); free(vd);
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

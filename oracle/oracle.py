@@ -79,6 +79,9 @@ def lib():
         L.orc_relocate_patch_ex.restype = C.c_int
         L.orc_relocate_patch_ex.argtypes = [C.POINTER(_Problem), C.POINTER(C.c_void_p),
                                             C.POINTER(C.c_void_p)]
+        L.orc_recall_patch_ex.restype = C.c_int
+        L.orc_recall_patch_ex.argtypes = [C.POINTER(_Problem), C.POINTER(_Problem),
+                                          C.POINTER(C.c_void_p), C.POINTER(C.c_void_p)]
         L.orc_row_magnitude_f64.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
                                             C.c_double, C.c_int64, C.c_int, C.c_void_p,
                                             C.c_void_p]
@@ -189,22 +192,9 @@ def row_offset(ch: dict, page_size: int, block_table, layer: int, t: int, h: int
     return lib().orc_row_offset(C.byref(c), page_size, _ptr(bt), layer, t, h)
 
 
-def relocate_patch(channels, *, num_layers: int, theta: float, offsets, delta,
-                   rank: int = 0, page_size: int = 0, block_table=None,
-                   y_out=None, s_out=None) -> None:
-    """The reuse operator over host arrays, in place.
-
-    ``channels`` is a list of one or two dicts with keys ``data`` (a flat numpy
-    buffer, uint16 or float32, element 0 = layer 0 slot 0 head 0 dim 0),
-    ``offset`` (element offset of that first element inside ``data``, default
-    0), ``heads``, ``dim``, ``rope_dim``, ``layer_stride``, ``slot_stride``,
-    ``head_stride``, ``page_stride`` (elements) and, when ``rank > 0``, ``U``
-    ([layers][tokens][rank]) and ``V`` ([layers][chunks][heads*dim][rank]).
-
-    ``y_out`` / ``s_out``: optional lists (one per channel) of float64 buffers shaped
-    like that channel's ``data``; every element the call computes receives its
-    unrounded fp64 value / its sum of term magnitudes, at the same element offset.
-    """
+def _problem(channels, *, num_layers, theta, offsets, delta, rank, page_size, block_table,
+             shape_from=None):
+    """Fills an orc_problem from channel dicts; returns (problem, arrays to keep alive)."""
     offsets = np.ascontiguousarray(offsets, dtype=np.int64)
     delta = np.ascontiguousarray(delta, dtype=np.int64)
     bt = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
@@ -219,13 +209,15 @@ def relocate_patch(channels, *, num_layers: int, theta: float, offsets, delta,
             code = c
         assert code == c
         es = data.itemsize
+        shape = shape_from[i] if shape_from is not None else ch
         p.ch[i].data = data.ctypes.data + es * int(ch.get("offset", 0))
-        p.ch[i].heads, p.ch[i].dim, p.ch[i].rope_dim = ch["heads"], ch["dim"], ch["rope_dim"]
+        p.ch[i].heads, p.ch[i].dim = shape["heads"], shape["dim"]
+        p.ch[i].rope_dim = shape["rope_dim"]
         p.ch[i].layer_stride = ch["layer_stride"]
         p.ch[i].slot_stride = ch["slot_stride"]
         p.ch[i].head_stride = ch["head_stride"]
         p.ch[i].page_stride = ch.get("page_stride", 0)
-        if rank > 0:
+        if rank > 0 and shape_from is None:
             U = np.ascontiguousarray(ch["U"])
             V = np.ascontiguousarray(ch["V"])
             assert U.dtype == data.dtype and V.dtype == data.dtype
@@ -242,19 +234,68 @@ def relocate_patch(channels, *, num_layers: int, theta: float, offsets, delta,
     p.delta = _ptr(delta)
     p.num_chunks = int(delta.size)
     p.rank = rank
+    return p, keep
+
+
+def _out_arrays(channels, y_out, s_out):
     ys = (C.c_void_p * 2)()
     ss = (C.c_void_p * 2)()
+    for i, ch in enumerate(channels):
+        yb, sb = y_out[i], s_out[i]
+        assert yb.dtype == np.float64 and sb.dtype == np.float64
+        assert yb.size == ch["data"].size and sb.size == ch["data"].size
+        ys[i] = yb.ctypes.data + 8 * int(ch.get("offset", 0))
+        ss[i] = sb.ctypes.data + 8 * int(ch.get("offset", 0))
+    return ys, ss
+
+
+def relocate_patch(channels, *, num_layers: int, theta: float, offsets, delta,
+                   rank: int = 0, page_size: int = 0, block_table=None,
+                   y_out=None, s_out=None) -> None:
+    """The reuse operator over host arrays, in place.
+
+    ``channels`` is a list of one or two dicts with keys ``data`` (a flat numpy
+    buffer, uint16 or float32, element 0 = layer 0 slot 0 head 0 dim 0),
+    ``offset`` (element offset of that first element inside ``data``, default
+    0), ``heads``, ``dim``, ``rope_dim``, ``layer_stride``, ``slot_stride``,
+    ``head_stride``, ``page_stride`` (elements) and, when ``rank > 0``, ``U``
+    ([layers][tokens][rank]) and ``V`` ([layers][chunks][heads*dim][rank]).
+
+    ``y_out`` / ``s_out``: optional lists (one per channel) of float64 buffers shaped
+    like that channel's ``data``; every element the call computes receives its
+    unrounded fp64 value / its sum of term magnitudes, at the same element offset.
+    """
+    p, keep = _problem(channels, num_layers=num_layers, theta=theta, offsets=offsets,
+                       delta=delta, rank=rank, page_size=page_size, block_table=block_table)
     if y_out is not None:
-        for i, ch in enumerate(channels):
-            yb, sb = y_out[i], s_out[i]
-            assert yb.dtype == np.float64 and sb.dtype == np.float64
-            assert yb.size == ch["data"].size and sb.size == ch["data"].size
-            ys[i] = yb.ctypes.data + 8 * int(ch.get("offset", 0))
-            ss[i] = sb.ctypes.data + 8 * int(ch.get("offset", 0))
+        ys, ss = _out_arrays(channels, y_out, s_out)
         rc = lib().orc_relocate_patch_ex(C.byref(p), ys, ss)
     else:
         rc = lib().orc_relocate_patch(C.byref(p))
     del keep
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+
+
+def recall_patch(src_channels, dst_channels, *, num_layers: int, theta: float, offsets, delta,
+                 rank: int = 0, src_page_size: int = 0, src_block_table=None,
+                 dst_page_size: int = 0, dst_block_table=None, y_out=None, s_out=None) -> None:
+    """Recall (out of place): rows read through ``src_channels`` (dicts as in
+    ``relocate_patch``, with the factors), whole result rows written through
+    ``dst_channels`` (dicts with ``data``, ``offset`` and the four strides; heads,
+    dim and rope_dim come from the source).  ``y_out`` / ``s_out`` are shaped like
+    the destination buffers."""
+    sp, keep = _problem(src_channels, num_layers=num_layers, theta=theta, offsets=offsets,
+                        delta=delta, rank=rank, page_size=src_page_size,
+                        block_table=src_block_table)
+    dp, keep2 = _problem(dst_channels, num_layers=num_layers, theta=theta, offsets=offsets,
+                         delta=delta, rank=rank, page_size=dst_page_size,
+                         block_table=dst_block_table, shape_from=src_channels)
+    ys = ss = None
+    if y_out is not None:
+        ys, ss = _out_arrays(dst_channels, y_out, s_out)
+    rc = lib().orc_recall_patch_ex(C.byref(sp), C.byref(dp), ys, ss)
+    del keep, keep2
     if rc != 0:
         raise ValueError("oracle rejected the problem")
 
