@@ -29,7 +29,8 @@
  *     Angles are formed and reduced in fp64; the sums run in fp32.
  *
  * Conventions for every entry point:
- *   - In place: the KV buffers named by the descriptor are read and overwritten.
+ *   - In place: the KV buffers named by the descriptor are read and overwritten
+ *     (kamera_recall_patch alone writes a separate destination instead).
  *   - Ownership: the caller owns every buffer (KV, block table, chunk offsets,
  *     deltas, factors).  The library allocates no memory, keeps no per-call state
  *     and returns as soon as the work is enqueued on `stream` (stream order; no
@@ -69,7 +70,8 @@ typedef enum {
   KAMERA_E_SHAPE = 2,       /* a size, stride, rank or rope_dim is out of range */
   KAMERA_E_UNSUPPORTED = 3, /* dtype or pairing this library does not implement */
   KAMERA_E_ALIGN = 4,       /* a pointer is not aligned to its element size */
-  KAMERA_E_ALIAS = 5,       /* factor memory overlaps KV memory */
+  KAMERA_E_ALIAS = 5,       /* factor memory overlaps KV memory, or a recall destination
+                               overlaps its source or the factors */
   KAMERA_E_HIP = 6          /* the HIP runtime reported an error at launch */
 } kamera_status;
 
@@ -149,6 +151,30 @@ KAMERA_API kamera_status kamera_relocate(const kamera_kv_desc* kv, const kamera_
 KAMERA_API kamera_status kamera_relocate_patch(const kamera_kv_desc* kv, const kamera_chunks* chunks,
                                     const kamera_patch* patch, hipStream_t stream);
 
+/* Recall, out of place: rebuild chunks from their canonical store into other cache
+ * slots.  Kamera page §3, the three cheap window operations, recall (reversible
+ * eviction): an evicted chunk is rehydrated from the canonical store with a patch for
+ * its new context, without re-encoding it.
+ *
+ * Every row (layer l, token t, each head) of every channel is read through `src` and
+ * the whole result row is written to the same (l, t) through `dst`:
+ *     dst element = round(R(delta_j) x + sum_k U[c][l][t][k] * V[c][l][j][f][k])
+ * Elements that neither the rotation nor the patch changes (rank 0 and rope_dim 0,
+ * dims >= rope_dim, chunks with delta 0 at rank 0) are copied bit for bit.
+ *   src: the canonical store (contiguous or paged); read only.  It is checked as the
+ *        kv argument of kamera_relocate_patch is (factors overlapping it are rejected
+ *        too).
+ *   dst: the cache being filled.  dtype, num_layers, num_channels, pairing and each
+ *        channel's heads, dim and rope_dim must equal src's; data, strides,
+ *        page_size, num_pages and block_table are its own (destination tokens whose
+ *        page id lies outside [0, num_pages) are skipped).  rope_theta is not read.
+ *        Its memory must not overlap the source or the factors (KAMERA_E_ALIAS).
+ *   patch == NULL or rank 0: rotation and copy only.
+ * chunks, stream and errors as for kamera_relocate_patch. */
+KAMERA_API kamera_status kamera_recall_patch(const kamera_kv_desc* src, const kamera_kv_desc* dst,
+                                  const kamera_chunks* chunks, const kamera_patch* patch,
+                                  hipStream_t stream);
+
 /* Which kernels a call would launch, without launching anything (no HIP call).
  * Fills `out` and returns the status the call itself would return before launching. */
 typedef struct {
@@ -163,6 +189,11 @@ typedef struct {
 
 KAMERA_API kamera_status kamera_plan(const kamera_kv_desc* kv, const kamera_chunks* chunks,
                           const kamera_patch* patch, kamera_plan_info* out);
+
+/* Same for kamera_recall_patch (which launches every channel: each is written whole). */
+KAMERA_API kamera_status kamera_recall_plan(const kamera_kv_desc* src, const kamera_kv_desc* dst,
+                                 const kamera_chunks* chunks, const kamera_patch* patch,
+                                 kamera_plan_info* out);
 
 KAMERA_API const char* kamera_status_str(kamera_status s);
 KAMERA_API const char* kamera_last_error(void); /* this thread's last failure message ("" if none) */

@@ -113,6 +113,32 @@ bool mfma_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, const kame
 }
 
 
+// Launch shape of the rotate+patch kernel for the channels in `use`.
+void plan_mfma(const kamera_kv_desc& kv, const kamera_chunks& ch, int m, const bool* use,
+               Plan* plan) {
+  plan->launches++;
+  // Each of the 4 wavefronts of a workgroup streams `tpw` 16-token tiles.  The
+  // workgroup stages 8 KB of feature factor per 32 ranks once per chunk, so larger
+  // ranks take more tiles per wave (measured best: 2 tiles at rank <= 32, 4 at 64).
+  const int mk = std::max(1, (m + 31) / 32);
+  const int dflt = std::min(8, 2 * (mk == 3 ? 4 : mk));
+  int tpw = env_int("KAMERA_TILES_PER_WAVE", dflt);
+  if (tpw < 1 || tpw > kamera::kMaxBlockTokens / 64) tpw = dflt;
+  plan->tiles_per_wave = tpw;
+  plan->tile_unroll = env_int("KAMERA_TILE_UNROLL", 1) == 2 ? 2 : 1;
+  plan->block_tokens = 64 * tpw;
+  // A second launch covers the token groups that chunk boundaries cut.
+  const int64_t T = ch.total_tokens;
+  const int64_t groups = ceil_div(T, plan->block_tokens);
+  const int64_t tail_units =
+      ch.num_chunks < 2 ? 0 : std::min<int64_t>((int64_t)ch.num_chunks - 1, groups);
+  if (tail_units > 0) plan->launches++;
+  for (int c = 0; c < kv.num_channels; ++c)
+    if (use[c])
+      plan->units += (int64_t)kv.num_layers * (groups + tail_units) *
+                     ceil_div((int64_t)kv.ch[c].heads * kv.ch[c].dim, 128);
+}
+
 // Checks every host-visible argument.  No HIP call is made here.
 kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamera_patch* p,
                        Plan* plan) {
@@ -227,28 +253,7 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
     plan->kernel[c] = use[c] ? K_MFMA : K_GENERIC;
     if (!use[c]) plan->launches++;
   }
-  if (use[0] || use[1]) {
-    plan->launches++;
-    // Each of the 4 wavefronts of a workgroup streams `tpw` 16-token tiles.  The
-    // workgroup stages 8 KB of feature factor per 32 ranks once per chunk, so larger
-    // ranks take more tiles per wave (measured best: 2 tiles at rank <= 32, 4 at 64).
-    const int mk = (m + 31) / 32;
-    const int dflt = std::min(8, 2 * (mk == 3 ? 4 : mk));
-    int tpw = env_int("KAMERA_TILES_PER_WAVE", dflt);
-    if (tpw < 1 || tpw > kamera::kMaxBlockTokens / 64) tpw = dflt;
-    plan->tiles_per_wave = tpw;
-    plan->tile_unroll = env_int("KAMERA_TILE_UNROLL", 1) == 2 ? 2 : 1;
-    plan->block_tokens = 64 * tpw;
-    // A second launch covers the token groups that chunk boundaries cut.
-    const int64_t groups = ceil_div(T, plan->block_tokens);
-    const int64_t tail_units =
-        ch->num_chunks < 2 ? 0 : std::min<int64_t>((int64_t)ch->num_chunks - 1, groups);
-    if (tail_units > 0) plan->launches++;
-    for (int c = 0; c < kv->num_channels; ++c)
-      if (use[c])
-        plan->units += (int64_t)kv->num_layers * (groups + tail_units) *
-                       ceil_div((int64_t)kv->ch[c].heads * kv->ch[c].dim, 128);
-  }
+  if (use[0] || use[1]) plan_mfma(*kv, *ch, m, use, plan);
   return KAMERA_OK;
 }
 
@@ -270,6 +275,7 @@ kamera::CommonArgs common_args(const kamera_kv_desc& kv, const kamera_chunks& ch
   a.page_shift = -1;
   for (int sh = 0; sh < 31; ++sh)
     if (kv.page_size == (1 << sh)) a.page_shift = sh;
+  a.out_page_shift = -1;
   return a;
 }
 
@@ -338,9 +344,171 @@ kamera_status run(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamer
   return KAMERA_OK;
 }
 
+// Out-of-place (recall) kernel: the rotate+patch kernel with a destination layout;
+// ranks that are multiples of 8 (0 included), both layouts 16-byte addressable.
+bool recall_tuned_ok(const kamera_kv_desc& src, const kamera_kv_desc& dst, const kamera_patch* p,
+                     int ci, int64_t T) {
+  const kamera_channel& c = src.ch[ci];
+  const kamera_channel& d = dst.ch[ci];
+  const int m = p ? p->rank : 0;
+  const int r = c.rope_dim, D = c.dim;
+  const bool rope_ok = r == 0 || ((r == 16 || r == 32 || r == 64 || r == 128) && D % r == 0);
+  const bool dim_ok = D % 8 == 0 && (D % 128 == 0 || 128 % D == 0);
+  const bool extent_ok =
+      layer_extent(c, T, src.page_size, src.num_pages) < ((__int128)1 << 31) &&
+      layer_extent(d, T, dst.page_size, dst.num_pages) < ((__int128)1 << 31);
+  const bool factors_ok = m == 0 || (aligned(p->U[ci], 16) && aligned(p->V[ci], 16));
+  return src.dtype == KAMERA_BF16 && !((src.flags | dst.flags) & KAMERA_FLAG_GENERIC) &&
+         m <= kMfmaMaxRank && m % 8 == 0 && rope_ok && dim_ok && extent_ok &&
+         T < kMaxTunedTokens && aligned(c.data, 16) && aligned(d.data, 16) && factors_ok &&
+         strides_ok(c) && strides_ok(d) && (int64_t)c.heads * D < (1 << 24);
+}
+
+// Checks every host-visible argument of a recall: the source side as for the in-place
+// call, then the destination.  No HIP call is made here.
+kamera_status validate_recall(const kamera_kv_desc* src, const kamera_kv_desc* dst,
+                              const kamera_chunks* ch, const kamera_patch* p, Plan* plan) {
+  Plan src_plan;
+  const kamera_status st = validate(src, ch, p, &src_plan);
+  if (st != KAMERA_OK) return st;
+  if (!dst) return fail(KAMERA_E_NULL, "destination descriptor is NULL");
+  if (dst->dtype != src->dtype)
+    return fail(KAMERA_E_SHAPE, "destination dtype %d differs from source dtype %d", dst->dtype,
+                src->dtype);
+  if (dst->num_layers != src->num_layers || dst->num_channels != src->num_channels)
+    return fail(KAMERA_E_SHAPE, "destination layers/channels differ from the source");
+  if (dst->pairing != src->pairing)
+    return fail(KAMERA_E_SHAPE, "destination pairing differs from the source");
+  if (dst->flags & ~KAMERA_FLAG_GENERIC)
+    return fail(KAMERA_E_SHAPE, "unknown destination flags 0x%x", dst->flags);
+  const int64_t es = src->dtype == KAMERA_BF16 ? 2 : 4;
+  const int m = p ? p->rank : 0;
+  const int64_t T = ch->total_tokens;
+  const bool empty = src->num_layers == 0 || T == 0;
+  for (int c = 0; c < dst->num_channels; ++c) {
+    const kamera_channel& d = dst->ch[c];
+    const kamera_channel& k = src->ch[c];
+    if (d.heads != k.heads || d.dim != k.dim || d.rope_dim != k.rope_dim)
+      return fail(KAMERA_E_SHAPE, "destination channel %d: heads/dim/rope_dim differ", c);
+    if (d.reserved0 != 0) return fail(KAMERA_E_SHAPE, "destination channel %d: reserved0 must be 0", c);
+    if (d.layer_stride < 0 || d.slot_stride < 0 || d.head_stride < 0 || d.page_stride < 0)
+      return fail(KAMERA_E_SHAPE, "destination channel %d: strides must be >= 0", c);
+    if (!empty && !d.data) return fail(KAMERA_E_NULL, "destination channel %d: data is NULL", c);
+    if (!aligned(d.data, es))
+      return fail(KAMERA_E_ALIGN, "destination channel %d: data not aligned to %d bytes", c, (int)es);
+  }
+  if (dst->page_size < 0) return fail(KAMERA_E_SHAPE, "destination page_size %d < 0", dst->page_size);
+  if (dst->page_size > 0) {
+    if (dst->num_pages < 1) return fail(KAMERA_E_SHAPE, "paged destination with num_pages < 1");
+    if (!empty && !dst->block_table)
+      return fail(KAMERA_E_NULL, "paged destination with no block table");
+    if (!aligned(dst->block_table, 4))
+      return fail(KAMERA_E_ALIGN, "destination block table not 4-byte aligned");
+  }
+  if (empty) return KAMERA_OK;
+  // The destination must not overlap the source or the factors.
+  for (int c = 0; c < dst->num_channels; ++c) {
+    int64_t dend;
+    if (!kv_extent(dst->ch[c], dst->num_layers, T, dst->page_size, dst->num_pages, es, &dend))
+      return fail(KAMERA_E_SHAPE, "destination channel %d: extent overflows", c);
+    for (int f = 0; f < src->num_channels; ++f) {
+      int64_t send;
+      if (!kv_extent(src->ch[f], src->num_layers, T, src->page_size, src->num_pages, es, &send))
+        return fail(KAMERA_E_SHAPE, "channel %d: KV extent overflows", f);
+      if (overlaps(dst->ch[c].data, dend, src->ch[f].data, send))
+        return fail(KAMERA_E_ALIAS, "destination channel %d overlaps source channel %d", c, f);
+      if (m > 0) {
+        const int64_t F = (int64_t)src->ch[f].heads * src->ch[f].dim;
+        const int64_t ub = (int64_t)src->num_layers * T * m * es;
+        const int64_t vb = (int64_t)src->num_layers * ch->num_chunks * F * m * es;
+        if (overlaps(dst->ch[c].data, dend, p->U[f], ub) ||
+            overlaps(dst->ch[c].data, dend, p->V[f], vb))
+          return fail(KAMERA_E_ALIAS, "factors of channel %d overlap destination channel %d", f, c);
+      }
+    }
+  }
+  // Every channel is written whole, so every channel is launched.
+  bool use[2] = {false, false};
+  for (int c = 0; c < src->num_channels; ++c) {
+    use[c] = recall_tuned_ok(*src, *dst, p, c, T);
+    plan->kernel[c] = use[c] ? K_MFMA : K_GENERIC;
+    if (!use[c]) plan->launches++;
+  }
+  if (use[0] || use[1]) plan_mfma(*src, *ch, m, use, plan);
+  return KAMERA_OK;
+}
+
+int exact_log2(int v) {
+  for (int sh = 0; sh < 31; ++sh)
+    if (v == (1 << sh)) return sh;
+  return -1;
+}
+
+kamera_status run_recall(const kamera_kv_desc* src, const kamera_kv_desc* dst,
+                         const kamera_chunks* ch, const kamera_patch* p, hipStream_t stream) {
+  g_last_error.clear();
+  Plan plan;
+  kamera_status st = validate_recall(src, dst, ch, p, &plan);
+  if (st != KAMERA_OK || plan.launches == 0) return st;
+  const int m = p ? p->rank : 0;
+  kamera::CommonArgs cm = common_args(*src, *ch, m, plan.block_tokens);
+  cm.out_block_table = dst->block_table;
+  cm.out_num_pages = dst->num_pages;
+  cm.out_page_size = dst->page_size;
+  cm.out_page_shift = exact_log2(dst->page_size);
+  kamera::ChanArgs tuned[2];
+  int ntuned = 0;
+  for (int c = 0; c < src->num_channels; ++c) {
+    kamera::ChanArgs a = chan_args(*src, c, m > 0 ? p : nullptr);
+    const kamera_channel& d = dst->ch[c];
+    a.out = d.data;
+    a.out_layer_stride = d.layer_stride;
+    a.out_slot_stride = d.slot_stride;
+    a.out_head_stride = d.head_stride;
+    a.out_page_stride = d.page_stride;
+    if (plan.kernel[c] == K_MFMA) {
+      a.fblocks = (int)ceil_div((int64_t)a.heads * a.dim, 128);
+      a.blocks = cm.token_groups * a.fblocks;
+      tuned[ntuned++] = a;
+    } else {
+      const hipError_t e = kamera::launch_generic(a, cm, src->dtype, stream);
+      if (e != hipSuccess) return hip_fail(e, "generic recall launch");
+    }
+  }
+  if (ntuned > 0) {
+    const hipError_t e = kamera::launch_relocate_patch_rows(tuned, ntuned, cm, 1, stream);
+    if (e != hipSuccess) return hip_fail(e, "recall launch");
+  }
+  return KAMERA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+kamera_status kamera_recall_patch(const kamera_kv_desc* src, const kamera_kv_desc* dst,
+                                  const kamera_chunks* chunks, const kamera_patch* patch,
+                                  hipStream_t stream) {
+  return run_recall(src, dst, chunks, patch, stream);
+}
+
+kamera_status kamera_recall_plan(const kamera_kv_desc* src, const kamera_kv_desc* dst,
+                                 const kamera_chunks* chunks, const kamera_patch* patch,
+                                 kamera_plan_info* out) {
+  g_last_error.clear();
+  if (!out) return fail(KAMERA_E_NULL, "plan output is NULL");
+  memset(out, 0, sizeof *out);
+  Plan plan;
+  const kamera_status st = validate_recall(src, dst, chunks, patch, &plan);
+  if (st != KAMERA_OK) return st;
+  out->kernel[0] = plan.kernel[0];
+  out->kernel[1] = plan.kernel[1];
+  out->launches = plan.launches;
+  out->tokens_per_unit = plan.block_tokens;
+  out->units = plan.units;
+  return KAMERA_OK;
+}
+
 
 kamera_status kamera_relocate(const kamera_kv_desc* kv, const kamera_chunks* chunks,
                               hipStream_t stream) {
@@ -375,7 +543,7 @@ const char* kamera_status_str(kamera_status s) {
     case KAMERA_E_SHAPE: return "bad shape, stride, rank or rope_dim";
     case KAMERA_E_UNSUPPORTED: return "unsupported dtype or pairing";
     case KAMERA_E_ALIGN: return "misaligned pointer";
-    case KAMERA_E_ALIAS: return "factor memory overlaps KV memory";
+    case KAMERA_E_ALIAS: return "overlapping memory (factors and KV, or recall source and destination)";
     case KAMERA_E_HIP: return "HIP runtime error";
   }
   return "unknown status";

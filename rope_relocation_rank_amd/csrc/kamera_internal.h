@@ -14,6 +14,10 @@ constexpr int kMaxBlockTokens = 512;  // tokens one tuned workgroup covers, at m
 struct ChanArgs {
   void* data;
   int64_t layer_stride, slot_stride, head_stride, page_stride;
+  // Out-of-place destination (recall): whole result rows go here, through its own
+  // strides and the destination block table.  nullptr: in place.
+  void* out;
+  int64_t out_layer_stride, out_slot_stride, out_head_stride, out_page_stride;
   const void* U;  // [layers][tokens][rank]
   const void* V;  // [layers][chunks][heads*dim][rank]
   int32_t heads, dim, rope_dim;
@@ -38,6 +42,11 @@ struct CommonArgs {
   int32_t block_tokens;     // tokens one workgroup covers (tuned kernels)
   int32_t page_shift;       // log2(page_size) when it is a power of two, else -1
   int32_t tail_mode;        // rotate+patch tail launch: 1 by boundary, 2 by token group
+  // Destination paging (out of place only).
+  const int32_t* out_block_table;
+  int64_t out_num_pages;
+  int32_t out_page_size;
+  int32_t out_page_shift;
 };
 
 // Rotation only, bf16, 16-byte accesses: rope_dim in {16, 32, 64, 128}.
@@ -46,6 +55,7 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
                               hipStream_t s);
 
 // Rotation + rank-m patch on MFMA, bf16: see kernels.hip for the shape conditions.
+// With ChanArgs::out set it runs out of place (rank % 8 == 0; rank 0 allowed).
 // Covers nch (1 or 2) channels in one launch, plus a second launch for the token groups
 // that chunk boundaries cut when there is more than one chunk.
 // `tile_unroll` 16-token tiles (1 or 2) are loaded together by each wavefront.
@@ -53,7 +63,8 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
                                       int tile_unroll, hipStream_t s);
 
 // Plain per-row kernel: any dim, even rope_dim, rank <= KAMERA_MAX_RANK, bf16 or fp32,
-// element-aligned pointers.  With rank 0 it only touches rotated dims.
+// element-aligned pointers.  In place with rank 0 it only touches rotated dims; out of
+// place (ChanArgs::out set) it writes whole rows.
 hipError_t launch_generic(const ChanArgs& ch, const CommonArgs& cm, int dtype, hipStream_t s);
 
 }  // namespace kamera

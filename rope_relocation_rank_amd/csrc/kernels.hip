@@ -206,16 +206,20 @@ __device__ __forceinline__ void phase_generic(double theta, int r, int i, int64_
 // Block-table entries a workgroup needs, staged once in LDS: pages [p0, p0 + n) cover
 // tokens [tb0, t1).  Entries outside [0, num_pages) become -1 (their tokens are left
 // untouched).  Returns p0.  The caller synchronises before reading `sbt`.
-__device__ __forceinline__ int stage_block_table(const CommonArgs& cm, int64_t tb0, int64_t t1,
-                                                 int* sbt) {
-  const int P = cm.page_size;
+__device__ __forceinline__ int stage_table(const int32_t* table, int64_t num_pages, int P,
+                                           int64_t tb0, int64_t t1, int* sbt) {
   const int p0 = (int)(tb0 / P);
   const int n = (int)((t1 - 1) / P) + 1 - p0;
   for (int k = threadIdx.x; k < n; k += kBlock) {
-    const int64_t pg = cm.block_table[p0 + k];
-    sbt[k] = (pg >= 0 && pg < cm.num_pages) ? (int)pg : -1;
+    const int64_t pg = table[p0 + k];
+    sbt[k] = (pg >= 0 && pg < num_pages) ? (int)pg : -1;
   }
   return p0;
+}
+
+__device__ __forceinline__ int stage_block_table(const CommonArgs& cm, int64_t tb0, int64_t t1,
+                                                 int* sbt) {
+  return stage_table(cm.block_table, cm.num_pages, cm.page_size, tb0, t1, sbt);
 }
 
 // Element offset, inside one layer, of the slot of token t (-1: token left untouched).
@@ -241,16 +245,16 @@ __device__ __forceinline__ int64_t slot_staged(const CommonArgs& cm, const int* 
 // Same as slot_staged in 32-bit arithmetic, for channels whose per-layer extent is
 // below 2^31 elements; PAGED selects the addressing at compile time.
 template <bool PAGED>
-__device__ __forceinline__ int32_t slot32(const CommonArgs& cm, const int* sbt, int p0,
+__device__ __forceinline__ int32_t slot32(int page_size, int page_shift, const int* sbt, int p0,
                                           int32_t page_stride, int32_t slot_stride, int t) {
   if constexpr (PAGED) {
     int pi, si;
-    if (cm.page_shift >= 0) {
-      pi = t >> cm.page_shift;
-      si = t & (cm.page_size - 1);
+    if (page_shift >= 0) {
+      pi = t >> page_shift;
+      si = t & (page_size - 1);
     } else {
-      pi = t / cm.page_size;
-      si = t - pi * cm.page_size;
+      pi = t / page_size;
+      si = t - pi * page_size;
     }
     const int pg = sbt[pi - p0];
     return pg < 0 ? -1 : pg * page_stride + si * slot_stride;
@@ -377,11 +381,14 @@ __device__ __forceinline__ u32x4_t load_frag(const uint16_t* row, int k0, int m,
 // Per-workgroup constants of the rotate+patch kernel that the tile loop reads.
 struct PatchCtx {
   uint16_t* base;       // lane's element (layer, slot 0, head h, dim d0)
+  uint16_t* obase;      // same element of the destination (out of place)
   const uint16_t* Ul;   // U of this layer and channel
   const int* sbt;       // staged block table (paged)
+  const int* osbt;      // staged destination block table (paged destination)
   int32_t page_stride, slot_stride;
+  int32_t opage_stride, oslot_stride;
   int64_t tb0, t1;
-  int p0, m;
+  int p0, op0, m;
   int lane, wave, c16, g;
   int fi0;
   float sgn;
@@ -392,12 +399,16 @@ struct PatchCtx {
 template <int MK, int TU>
 struct TileSet {
   u32x4_t x[TU][4];
-  int32_t off[TU][4];  // element offset from the lane's base, -1 = no load / no store
-  u32x4_t a[TU][MK];
+  // Element offset of the row to store, -1 = none: from the lane's base in place, from
+  // the lane's destination base out of place.
+  int32_t off[TU][4];
+  u32x4_t a[TU][MK > 0 ? MK : 1];
 };
 
 // Loads tiles kt, kt + 4, ... (TU of them, those below k_hi), keeping tokens in [t0, s1).
-template <int MK, bool M8, bool PAGED, int TU>
+// OUT: 0 in place, 1 contiguous destination, 2 paged destination; a row is loaded
+// only when both its source and its destination slot exist.
+template <int MK, bool M8, bool PAGED, int TU, int OUT>
 __device__ __forceinline__ void load_tiles(const PatchCtx& c, const CommonArgs& cm, int kt,
                                            int k_hi, int64_t t0, int64_t s1,
                                            TileSet<MK, TU>& T) {
@@ -410,17 +421,28 @@ __device__ __forceinline__ void load_tiles(const PatchCtx& c, const CommonArgs& 
       const int64_t t = ts + 4 * c.g + i;
       T.off[u][i] = -1;
       T.x[u][i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (tile_on && c.lane_on && t >= t0 && t < s1)
-        T.off[u][i] = slot32<PAGED>(cm, c.sbt, c.p0, c.page_stride, c.slot_stride, (int)t);
-      if (T.off[u][i] >= 0) T.x[u][i] = load_nt(c.base + T.off[u][i]);
+      if (tile_on && c.lane_on && t >= t0 && t < s1) {
+        int32_t so = slot32<PAGED>(cm.page_size, cm.page_shift, c.sbt, c.p0, c.page_stride,
+                                   c.slot_stride, (int)t);
+        if constexpr (OUT > 0) {
+          const int32_t dso = slot32<OUT == 2>(cm.out_page_size, cm.out_page_shift, c.osbt, c.op0,
+                                               c.opage_stride, c.oslot_stride, (int)t);
+          if (dso < 0) so = -1;
+          if (so >= 0) T.x[u][i] = load_nt(c.base + so);
+          T.off[u][i] = so >= 0 ? dso : -1;
+        } else {
+          T.off[u][i] = so;
+        }
+      }
+      if (OUT == 0 && T.off[u][i] >= 0) T.x[u][i] = load_nt(c.base + T.off[u][i]);
     }
     const int64_t tu = ts + c.c16;
     const bool uok = tile_on && tu < c.t1;
     const uint16_t* urow = c.Ul + (uok ? tu : 0) * c.m;
 #pragma unroll
-    for (int ks = 0; ks < MK; ++ks) {
+    for (int ks = 0; ks < (MK > 0 ? MK : 1); ++ks) {
       T.a[u][ks] = u32x4_t{0u, 0u, 0u, 0u};
-      if (uok) T.a[u][ks] = load_frag(urow, 32 * ks + 8 * c.g, c.m, M8);
+      if (MK > 0 && uok) T.a[u][ks] = load_frag(urow, 32 * ks + 8 * c.g, c.m, M8);
     }
   }
 }
@@ -435,7 +457,7 @@ __device__ __forceinline__ void load_tiles(const PatchCtx& c, const CommonArgs& 
 // feature n of its 4 tokens: the rotated values are the C operand and the result is
 // already where it is stored.  Output tiles go two at a time (features 2p, 2p + 1 form
 // one packed bf16 pair), so only 8 accumulators are live.
-template <int MK, int HX, int TU>
+template <int MK, int HX, int TU, int OUT>
 __device__ __forceinline__ void finish_tiles(const PatchCtx& c, const u32x4_t* sV,
                                              const float4* sph2, const TileSet<MK, TU>& T) {
 #pragma unroll
@@ -445,46 +467,62 @@ __device__ __forceinline__ void finish_tiles(const PatchCtx& c, const u32x4_t* s
     for (int pp = 0; pp < 4; ++pp) {  // features 2pp, 2pp + 1 of the lane's 8
       float4 ph = make_float4(1.f, 0.f, 1.f, 0.f);
       if constexpr (HX > 0) ph = sph2[(c.fi0 >> 1) + pp];
-      f32x4_t acc0, acc1;
+      if constexpr (MK == 0) {
+        // No patch (out of place only): rotated dims are rounded once, every other
+        // element is copied bit for bit.
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = T.x[u][i][pp];
-        float a0 = bf16_lo(w), a1 = bf16_hi(w);
-        if constexpr (HX > 0) {
-          const uint32_t pw = lane_xor<HX>(w);
-          const float y0 = fmaf(a0, ph.x, bf16_lo(pw) * (c.sgn * ph.y));
-          const float y1 = fmaf(a1, ph.z, bf16_hi(pw) * (c.sgn * ph.w));
-          a0 = c.rot_lane ? y0 : a0;
-          a1 = c.rot_lane ? y1 : a1;
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = T.x[u][i][pp];
+          out[i][pp] = w;
+          if constexpr (HX > 0) {
+            const uint32_t pw = lane_xor<HX>(w);
+            const float y0 = fmaf(bf16_lo(w), ph.x, bf16_lo(pw) * (c.sgn * ph.y));
+            const float y1 = fmaf(bf16_hi(w), ph.z, bf16_hi(pw) * (c.sgn * ph.w));
+            if (c.rot_lane) out[i][pp] = pack2(y0, y1);
+          }
         }
-        acc0[i] = a0;
-        acc1[i] = a1;
-      }
+      } else {
+        f32x4_t acc0, acc1;
 #pragma unroll
-      for (int ks = 0; ks < MK; ++ks) {
-        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, T.a[u][ks]);
-        const bf16x8_t B0 = __builtin_bit_cast(bf16x8_t, sV[((2 * pp) * MK + ks) * 64 + c.lane]);
-        const bf16x8_t B1 =
-            __builtin_bit_cast(bf16x8_t, sV[((2 * pp + 1) * MK + ks) * 64 + c.lane]);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc1, 0, 0, 0);
-      }
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = T.x[u][i][pp];
+          float a0 = bf16_lo(w), a1 = bf16_hi(w);
+          if constexpr (HX > 0) {
+            const uint32_t pw = lane_xor<HX>(w);
+            const float y0 = fmaf(a0, ph.x, bf16_lo(pw) * (c.sgn * ph.y));
+            const float y1 = fmaf(a1, ph.z, bf16_hi(pw) * (c.sgn * ph.w));
+            a0 = c.rot_lane ? y0 : a0;
+            a1 = c.rot_lane ? y1 : a1;
+          }
+          acc0[i] = a0;
+          acc1[i] = a1;
+        }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out[i][pp] = pack2(acc0[i], acc1[i]);
+        for (int ks = 0; ks < MK; ++ks) {
+          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, T.a[u][ks]);
+          const bf16x8_t B0 = __builtin_bit_cast(bf16x8_t, sV[((2 * pp) * MK + ks) * 64 + c.lane]);
+          const bf16x8_t B1 =
+              __builtin_bit_cast(bf16x8_t, sV[((2 * pp + 1) * MK + ks) * 64 + c.lane]);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B0, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i][pp] = pack2(acc0[i], acc1[i]);
+      }
       // Keep the scheduler from hoisting every feature pair's LDS reads at once (it
       // would hold all B fragments live and lower the occupancy).
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (T.off[u][i] >= 0) store_nt(c.base + T.off[u][i], out[i]);
+      if (T.off[u][i] >= 0) store_nt((OUT > 0 ? c.obase : c.base) + T.off[u][i], out[i]);
   }
 }
 
 // The wave's tiles (16-token tile kt with kt = wave mod 4) that meet [t0, s1), TU at a
 // time; only tokens in [t0, s1) are loaded and stored.  When `use_pre`, `pre` already
 // holds the wave's first group of tiles (loaded before the workgroup staged the chunk).
-template <int MK, bool M8, bool PAGED, int HX, int TU>
+template <int MK, bool M8, bool PAGED, int HX, int TU, int OUT>
 __device__ __forceinline__ void patch_tiles(const PatchCtx& c, const CommonArgs& cm,
                                             const u32x4_t* sV, const float4* sph2,
                                             int64_t t0, int64_t s1,
@@ -493,13 +531,13 @@ __device__ __forceinline__ void patch_tiles(const PatchCtx& c, const CommonArgs&
   const int k_hi = (int)((s1 - c.tb0 + 15) >> 4);
   int kt = k_lo + ((c.wave - k_lo) % kWavesPerBlock + kWavesPerBlock) % kWavesPerBlock;
   if (use_pre) {
-    finish_tiles<MK, HX, TU>(c, sV, sph2, pre);
+    finish_tiles<MK, HX, TU, OUT>(c, sV, sph2, pre);
     kt += kWavesPerBlock * TU;
   }
   for (; kt < k_hi; kt += kWavesPerBlock * TU) {
     TileSet<MK, TU> T;
-    load_tiles<MK, M8, PAGED, TU>(c, cm, kt, k_hi, t0, s1, T);
-    finish_tiles<MK, HX, TU>(c, sV, sph2, T);
+    load_tiles<MK, M8, PAGED, TU, OUT>(c, cm, kt, k_hi, t0, s1, T);
+    finish_tiles<MK, HX, TU, OUT>(c, sV, sph2, T);
   }
 }
 
@@ -517,13 +555,18 @@ __device__ __forceinline__ void patch_tiles(const PatchCtx& c, const CommonArgs&
 // the first boundary inside its group) or over groups (cm.tail_mode == 2, when chunks
 // outnumber groups).  Keeping that rarer loop over chunks in its own kernel keeps the
 // common kernel's register count (and so its occupancy) down.
-template <int MK, bool M8, bool PAGED, int TU, bool TAIL>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(!TAIL && MK <= 2 && TU == 1 ? 4 : 1)))
+//
+// OUT != 0 is the out-of-place form (recall): rows are read through the source layout
+// and whole result rows written through the destination layout (OUT 1 contiguous, 2
+// paged); MK = 0 is its no-patch form.
+template <int MK, bool M8, bool PAGED, int TU, bool TAIL, int OUT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(!TAIL && TU == 1 && (MK <= 1 || (MK == 2 && OUT == 0)) ? 4 : 1)))
 void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t blocks_per_layer,
                          int xcd_group) {
-  __shared__ u32x4_t sV[8 * MK * 64];
+  __shared__ u32x4_t sV[8 * (MK > 0 ? MK : 1) * 64];
   __shared__ float4 sph2[kMaxTunedHalf / 2];  // (cos, sin) of pairs 2p and 2p + 1
   __shared__ int sbt[kMaxBlockTokens + 1];
+  __shared__ int osbt[OUT == 2 ? kMaxBlockTokens + 1 : 1];
   const int lane = threadIdx.x & 63;
 
   // Logical workgroup index: groups of 8 * xcd_group ids are permuted so that XCD x
@@ -572,6 +615,14 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
   c.page_stride = (int32_t)KAMERA_CH(page_stride);
   c.base = (uint16_t*)KAMERA_CH(data) + layer * KAMERA_CH(layer_stride) +
            (int64_t)h * KAMERA_CH(head_stride) + d0;
+  c.obase = nullptr;
+  c.opage_stride = c.oslot_stride = 0;
+  if constexpr (OUT > 0) {
+    c.obase = (uint16_t*)KAMERA_CH(out) + layer * KAMERA_CH(out_layer_stride) +
+              (int64_t)h * KAMERA_CH(out_head_stride) + d0;
+    c.oslot_stride = (int32_t)KAMERA_CH(out_slot_stride);
+    c.opage_stride = (int32_t)KAMERA_CH(out_page_stride);
+  }
   c.Ul = (const uint16_t*)KAMERA_CH(U) + layer * cm.total_tokens * m;
   const uint16_t* Vl = (const uint16_t*)KAMERA_CH(V) + layer * (int64_t)cm.num_chunks * F * m;
 
@@ -603,18 +654,22 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
     start = c.tb0;
   }
   c.p0 = 0;
+  c.op0 = 0;
   c.sbt = sbt;
+  c.osbt = osbt;
   if (PAGED) c.p0 = stage_block_table(cm, c.tb0, c.t1, sbt);
+  if (OUT == 2)
+    c.op0 = stage_table(cm.out_block_table, cm.out_num_pages, cm.out_page_size, c.tb0, c.t1, osbt);
 
   // Stages chunk j's B fragments (and, when rotating, its phases) in LDS.
   auto stage = [&](const ChunkRef& ck, bool rotate) {
     const uint16_t* Vj = Vl + (int64_t)ck.j * F * m;
 #pragma unroll
-    for (int u = 0; u < 2 * MK; ++u) {
+    for (int u = 0; u < 2 * MK; ++u) {  // none when MK == 0
       const int it = threadIdx.x + kBlock * u;
       const int l = it & 63;
       const int nk = it >> 6;  // n * MK + ks
-      const int n = nk / MK;
+      const int n = nk / (MK > 0 ? MK : 1);
       const int ks = nk - n * MK;
       const int f = fb + 8 * (l & 15) + n;
       u32x4_t v = {0u, 0u, 0u, 0u};
@@ -627,20 +682,20 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
   };
 #define KAMERA_PATCH_SWITCH(PRE, USE)                                                           \
   switch (rotate ? hx : 0) {                                                                    \
-    case 1: patch_tiles<MK, M8, PAGED, 1, TU>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
-    case 2: patch_tiles<MK, M8, PAGED, 2, TU>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
-    case 4: patch_tiles<MK, M8, PAGED, 4, TU>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
-    case 8: patch_tiles<MK, M8, PAGED, 8, TU>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
-    default: patch_tiles<MK, M8, PAGED, 0, TU>(c, cm, sV, sph2, t0, s1, PRE, USE); break;      \
+    case 1: patch_tiles<MK, M8, PAGED, 1, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
+    case 2: patch_tiles<MK, M8, PAGED, 2, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
+    case 4: patch_tiles<MK, M8, PAGED, 4, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
+    case 8: patch_tiles<MK, M8, PAGED, 8, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
+    default: patch_tiles<MK, M8, PAGED, 0, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;      \
   }
 
-  if (PAGED) __syncthreads();  // staged block table
+  if (PAGED || OUT == 2) __syncthreads();  // staged block tables
   if constexpr (!TAIL) {
     const int ntiles = (int)((c.t1 - c.tb0 + 15) >> 4);
     // The wave's first tiles are loaded before anything else, so their HBM latency
     // overlaps the chunk lookup, the LDS staging and the barrier.
     TileSet<MK, TU> pre;
-    load_tiles<MK, M8, PAGED, TU>(c, cm, c.wave, ntiles, c.tb0, c.t1, pre);
+    load_tiles<MK, M8, PAGED, TU, OUT>(c, cm, c.wave, ntiles, c.tb0, c.t1, pre);
     const ChunkRef ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, c.tb0);
     const int64_t t0 = c.tb0, s1 = min(c.t1, ck.end);
     if (s1 <= t0) return;  // offsets that do not cover the group: nothing here
@@ -688,8 +743,30 @@ __device__ __forceinline__ float dot_patch(const T* u, const T* v, int m) {
   return s;
 }
 
-// One thread per (layer, token, head) row; any dim, any even rope_dim, any rank.
+// Slot offset of token t in one layer of a (possibly paged) channel; false when its
+// page id is out of range.
+__device__ __forceinline__ bool slot_of(int64_t t, int page_size, const int32_t* table,
+                                        int64_t num_pages, int64_t page_stride,
+                                        int64_t slot_stride, int64_t* so) {
+  if (page_size > 0) {
+    const int64_t pg = table[t / page_size];
+    *so = pg * page_stride + (t % page_size) * slot_stride;
+    return pg >= 0 && pg < num_pages;
+  }
+  *so = t * slot_stride;
+  return true;
+}
+
 template <typename T>
+__device__ __forceinline__ void copy_bits(T* dst, const T* src) {
+  if constexpr (sizeof(T) == 2) *(uint16_t*)dst = *(const uint16_t*)src;
+  else *(uint32_t*)dst = *(const uint32_t*)src;
+}
+
+// One thread per (layer, token, head) row; any dim, any even rope_dim, any rank.
+// OUT: the row is read through the channel's layout and written through its
+// destination layout, whole (elements the call leaves alone are copied bit for bit).
+template <typename T, bool OUT>
 __global__ __launch_bounds__(kBlock) void generic_rows(ChanArgs ch, CommonArgs cm) {
   const int64_t H = ch.heads, Tt = cm.total_tokens;
   const int64_t nrows = (int64_t)cm.num_layers * Tt * H;
@@ -703,22 +780,25 @@ __global__ __launch_bounds__(kBlock) void generic_rows(ChanArgs ch, CommonArgs c
     const int64_t layer = rest / Tt;
     const int j = find_chunk(cm.offsets, cm.num_chunks, t);
     const int64_t dj = cm.delta[j];
-    if (m == 0 && (dj == 0 || r == 0)) continue;
-    bool ok = true;
-    int64_t so;
-    if (cm.page_size > 0) {
-      const int64_t pg = cm.block_table[t / cm.page_size];
-      ok = pg >= 0 && pg < cm.num_pages;
-      so = pg * ch.page_stride + (t % cm.page_size) * ch.slot_stride;
-    } else {
-      so = t * ch.slot_stride;
+    if (!OUT && m == 0 && (dj == 0 || r == 0)) continue;
+    int64_t so, dso = 0;
+    if (!slot_of(t, cm.page_size, cm.block_table, cm.num_pages, ch.page_stride, ch.slot_stride,
+                 &so))
+      continue;
+    if (OUT && !slot_of(t, cm.out_page_size, cm.out_block_table, cm.out_num_pages,
+                        ch.out_page_stride, ch.out_slot_stride, &dso))
+      continue;
+    const T* src = (const T*)ch.data + layer * ch.layer_stride + so + h * ch.head_stride;
+    T* dst = OUT ? (T*)ch.out + layer * ch.out_layer_stride + dso + h * ch.out_head_stride
+                 : (T*)src;
+    if (OUT && m == 0 && (dj == 0 || r == 0)) {
+      for (int d = 0; d < D; ++d) copy_bits(dst + d, src + d);
+      continue;
     }
-    if (!ok) continue;
-    T* row = (T*)ch.data + layer * ch.layer_stride + so + h * ch.head_stride;
     const T* u = (const T*)ch.U + (layer * Tt + t) * m;
     const T* vr = (const T*)ch.V + ((layer * cm.num_chunks + j) * F + h * D) * m;
     for (int i = 0; i < half; ++i) {
-      float a = load_f(row + i), b = load_f(row + i + half);
+      float a = load_f(src + i), b = load_f(src + i + half);
       if (dj != 0) {
         float c, s;
         phase_generic(cm.theta, r, i, dj, c, s);
@@ -731,11 +811,13 @@ __global__ __launch_bounds__(kBlock) void generic_rows(ChanArgs ch, CommonArgs c
         a += dot_patch(u, vr + (int64_t)i * m, m);
         b += dot_patch(u, vr + (int64_t)(i + half) * m, m);
       }
-      store_f(row + i, a);
-      store_f(row + i + half, b);
+      store_f(dst + i, a);
+      store_f(dst + i + half, b);
     }
     if (m > 0)
-      for (int d = r; d < D; ++d) store_f(row + d, load_f(row + d) + dot_patch(u, vr + (int64_t)d * m, m));
+      for (int d = r; d < D; ++d) store_f(dst + d, load_f(src + d) + dot_patch(u, vr + (int64_t)d * m, m));
+    else if (OUT)
+      for (int d = r; d < D; ++d) copy_bits(dst + d, src + d);
   }
 }
 
@@ -783,23 +865,43 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
   const int xg = (nch == 1 || c0.fblocks == c1.fblocks) ? c0.fblocks : 0;
   const int mk = (cm.rank + 31) / 32;
   const bool m8 = cm.rank % 8 == 0;
-#define KAMERA_LAUNCH_PATCH2(MK, PG, TL, XG)                                                   \
+  // Out of place (recall): 1 contiguous destination, 2 paged destination.
+  const int out = c0.out == nullptr ? 0 : (cm.out_page_size > 0 ? 2 : 1);
+  if (out > 0 && (!m8 || (nch > 1 && c1.out == nullptr))) return hipErrorInvalidValue;
+  if (out == 0 && mk == 0) return hipErrorInvalidValue;
+#define KAMERA_LAUNCH_K(MK, M8, PG, TU, TL, OUT, XG)                                           \
+  hipLaunchKernelGGL((relocate_patch_rows<MK, M8, PG, TU, TL, OUT>), grid, dim3(kBlock), 0, s, \
+                     c0, c1, cm, bpl, XG)
+#define KAMERA_LAUNCH_IN(MK, PG, TL, XG)                                                       \
   do {                                                                                         \
-    if (m8 && tile_unroll == 2 && !TL) hipLaunchKernelGGL((relocate_patch_rows<MK, true, PG, 2, false>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, XG); \
-    else if (m8) hipLaunchKernelGGL((relocate_patch_rows<MK, true, PG, 1, TL>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, XG); \
-    else hipLaunchKernelGGL((relocate_patch_rows<MK, false, PG, 1, TL>), grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, XG); \
+    if (m8 && tile_unroll == 2 && !TL) KAMERA_LAUNCH_K(MK, true, PG, 2, false, 0, XG);         \
+    else if (m8) KAMERA_LAUNCH_K(MK, true, PG, 1, TL, 0, XG);                                  \
+    else KAMERA_LAUNCH_K(MK, false, PG, 1, TL, 0, XG);                                         \
   } while (0)
-#define KAMERA_LAUNCH_PATCH(MK, TL, XG)                        \
-  do {                                                         \
-    if (cm.page_size > 0) KAMERA_LAUNCH_PATCH2(MK, true, TL, XG); \
-    else KAMERA_LAUNCH_PATCH2(MK, false, TL, XG);               \
+#define KAMERA_LAUNCH_OUT(MK, PG, TL, XG)                                     \
+  do {                                                                        \
+    if (out == 1) KAMERA_LAUNCH_K(MK, true, PG, 1, TL, 1, XG);                \
+    else KAMERA_LAUNCH_K(MK, true, PG, 1, TL, 2, XG);                         \
   } while (0)
-#define KAMERA_LAUNCH_MK(TL, XG)                       \
-  do {                                                 \
-    if (mk == 1) KAMERA_LAUNCH_PATCH(1, TL, XG);       \
-    else if (mk == 2) KAMERA_LAUNCH_PATCH(2, TL, XG);  \
-    else if (mk <= 4) KAMERA_LAUNCH_PATCH(4, TL, XG);  \
-    else return hipErrorInvalidValue;                  \
+#define KAMERA_LAUNCH_PG(MK, TL, XG)                                          \
+  do {                                                                        \
+    if (out > 0) {                                                            \
+      if (cm.page_size > 0) KAMERA_LAUNCH_OUT(MK, true, TL, XG);              \
+      else KAMERA_LAUNCH_OUT(MK, false, TL, XG);                              \
+    } else {                                                                  \
+      if (cm.page_size > 0) KAMERA_LAUNCH_IN(MK, true, TL, XG);               \
+      else KAMERA_LAUNCH_IN(MK, false, TL, XG);                               \
+    }                                                                         \
+  } while (0)
+#define KAMERA_LAUNCH_MK(TL, XG)                                              \
+  do {                                                                        \
+    if (mk == 0) {                                                            \
+      if (cm.page_size > 0) KAMERA_LAUNCH_OUT(0, true, TL, XG);               \
+      else KAMERA_LAUNCH_OUT(0, false, TL, XG);                               \
+    } else if (mk == 1) KAMERA_LAUNCH_PG(1, TL, XG);                          \
+    else if (mk == 2) KAMERA_LAUNCH_PG(2, TL, XG);                            \
+    else if (mk <= 4) KAMERA_LAUNCH_PG(4, TL, XG);                            \
+    else return hipErrorInvalidValue;                                         \
   } while (0)
   KAMERA_LAUNCH_MK(false, xg);
   hipError_t e = hipGetLastError();
@@ -815,8 +917,10 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
   grid = dim3((unsigned)((int64_t)cm.num_layers * bpl));
   KAMERA_LAUNCH_MK(true, 0);
 #undef KAMERA_LAUNCH_MK
-#undef KAMERA_LAUNCH_PATCH
-#undef KAMERA_LAUNCH_PATCH2
+#undef KAMERA_LAUNCH_PG
+#undef KAMERA_LAUNCH_OUT
+#undef KAMERA_LAUNCH_IN
+#undef KAMERA_LAUNCH_K
   return hipGetLastError();
 }
 
@@ -825,10 +929,15 @@ hipError_t launch_generic(const ChanArgs& ch, const CommonArgs& cm, int dtype, h
   int64_t blocks = (nrows + kBlock - 1) / kBlock;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  if (dtype == 0)
-    hipLaunchKernelGGL(generic_rows<uint16_t>, dim3((unsigned)blocks), dim3(kBlock), 0, s, ch, cm);
+  const bool out = ch.out != nullptr;
+  if (dtype == 0 && out)
+    hipLaunchKernelGGL((generic_rows<uint16_t, true>), dim3((unsigned)blocks), dim3(kBlock), 0, s, ch, cm);
+  else if (dtype == 0)
+    hipLaunchKernelGGL((generic_rows<uint16_t, false>), dim3((unsigned)blocks), dim3(kBlock), 0, s, ch, cm);
+  else if (out)
+    hipLaunchKernelGGL((generic_rows<float, true>), dim3((unsigned)blocks), dim3(kBlock), 0, s, ch, cm);
   else
-    hipLaunchKernelGGL(generic_rows<float>, dim3((unsigned)blocks), dim3(kBlock), 0, s, ch, cm);
+    hipLaunchKernelGGL((generic_rows<float, false>), dim3((unsigned)blocks), dim3(kBlock), 0, s, ch, cm);
   return hipGetLastError();
 }
 

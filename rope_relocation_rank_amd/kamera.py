@@ -23,8 +23,8 @@ KAMERA_FLAG_GENERIC = 1
 KAMERA_MAX_RANK = 256
 KERNEL_NAMES = {0: "none", 1: "rotate", 2: "rotate+patch mfma", 3: "generic"}
 
-EXPORTED = ["kamera_relocate", "kamera_relocate_patch", "kamera_plan", "kamera_status_str",
-            "kamera_last_error", "kamera_abi_version"]
+EXPORTED = ["kamera_relocate", "kamera_relocate_patch", "kamera_recall_patch", "kamera_plan",
+            "kamera_recall_plan", "kamera_status_str", "kamera_last_error", "kamera_abi_version"]
 
 
 class kamera_channel(C.Structure):
@@ -83,6 +83,14 @@ def lib():
         L.kamera_plan.restype = C.c_int
         L.kamera_plan.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
                                   C.POINTER(kamera_patch), C.POINTER(kamera_plan_info)]
+        L.kamera_recall_patch.restype = C.c_int
+        L.kamera_recall_patch.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_kv_desc),
+                                          C.POINTER(kamera_chunks), C.POINTER(kamera_patch),
+                                          C.c_void_p]
+        L.kamera_recall_plan.restype = C.c_int
+        L.kamera_recall_plan.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_kv_desc),
+                                         C.POINTER(kamera_chunks), C.POINTER(kamera_patch),
+                                         C.POINTER(kamera_plan_info)]
         L.kamera_status_str.restype = C.c_char_p
         L.kamera_status_str.argtypes = [C.c_int]
         L.kamera_last_error.restype = C.c_char_p
@@ -109,6 +117,21 @@ def kamera_plan(kv, chunks, patch=None):
     st = lib().kamera_plan(None if kv is None else C.byref(kv),
                            None if chunks is None else C.byref(chunks),
                            None if patch is None else C.byref(patch), C.byref(info))
+    return st, info
+
+
+def _ref(x):
+    return None if x is None else C.byref(x)
+
+
+def kamera_recall_patch(src: kamera_kv_desc, dst: kamera_kv_desc, chunks: kamera_chunks, patch,
+                        stream) -> int:
+    return lib().kamera_recall_patch(_ref(src), _ref(dst), _ref(chunks), _ref(patch), stream)
+
+
+def kamera_recall_plan(src, dst, chunks, patch=None):
+    info = kamera_plan_info()
+    st = lib().kamera_recall_plan(_ref(src), _ref(dst), _ref(chunks), _ref(patch), C.byref(info))
     return st, info
 
 
@@ -197,3 +220,10 @@ def relocate_patch_(kv: kamera_kv_desc, chunks: kamera_chunks, patch=None, strea
         check(kamera_relocate(kv, chunks, s))
     else:
         check(kamera_relocate_patch(kv, chunks, patch, s))
+
+
+def recall_patch(src: kamera_kv_desc, dst: kamera_kv_desc, chunks: kamera_chunks, patch=None,
+                 stream=None) -> None:
+    """Enqueue a recall (out of place) on `stream` (default: torch's current stream)."""
+    s = current_stream() if stream is None else stream
+    check(kamera_recall_patch(src, dst, chunks, patch, s))

@@ -50,3 +50,35 @@ def plan(inp, flags: int = 0):
     st, info = K.kamera_plan(kv, ch, patch)
     K.check(st)
     return info
+
+
+def recall_descriptors(rinp, flags: int = 0):
+    """(src, dst, chunks, patch) descriptors for a synth.RecallInputs instance."""
+    import torch
+    src, ch, patch = descriptors_for(rinp.src, flags)
+    w = rinp.workload
+    code = K.KAMERA_BF16 if rinp.dst_buffers[0].dtype == torch.bfloat16 else K.KAMERA_F32
+    chans = []
+    for lay in rinp.dst_layouts:
+        chans.append(K.channel(rinp.dst_buffers[lay["buffer"]], heads=lay["heads"], dim=lay["dim"],
+                               rope_dim=lay["rope_dim"], layer_stride=lay["layer_stride"],
+                               slot_stride=lay["slot_stride"], head_stride=lay["head_stride"],
+                               page_stride=lay.get("page_stride", 0),
+                               element_offset=lay.get("offset", 0)))
+    dst = K.kv_desc(chans, dtype=code, num_layers=w.layers, rope_theta=w.theta,
+                    page_size=rinp.dst_page_size, num_pages=rinp.dst_pool_pages,
+                    block_table=rinp.dst_block_table_t, flags=flags)
+    return src, dst, ch, patch
+
+
+def run_recall(rinp, stream=None, flags: int = 0) -> None:
+    """Recall: rebuild the chunks of `rinp.src` into `rinp`'s destination on `stream`."""
+    src, dst, ch, patch = recall_descriptors(rinp, flags)
+    K.recall_patch(src, dst, ch, patch, stream)
+
+
+def recall_plan(rinp, flags: int = 0):
+    src, dst, ch, patch = recall_descriptors(rinp, flags)
+    st, info = K.kamera_recall_plan(src, dst, ch, patch)
+    K.check(st)
+    return info

@@ -8,9 +8,15 @@ Inputs stand in for real model KV of the named shapes (no weights or datasets ar
 used).  Values: KV ~ N(0, 1); patch factors ~ N(0, s^2) with s^2 = 0.1 / sqrt(m),
 so every entry of U V^T has standard deviation 0.1 whatever m is; all drawn in fp32
 and rounded to the storage dtype.  Seeds derive from (workload id, kind, layer,
-channel) through numpy's SeedSequence; kind 0 = KV, 1 = U, 2 = V, 3 = structure.
-The structure stream draws chunk lengths, then deltas, then the block-table
-permutation, then outlier feature indices.
+channel) through numpy's SeedSequence; kind 0 = KV, 1 = U, 2 = V, 3 = structure,
+4 = recall destination.  The structure stream draws chunk lengths, then deltas, then
+the block-table permutation, then outlier feature indices; the destination stream
+draws the destination block-table permutation.
+
+Recall workloads (out of place) read a canonical store laid out as the workload says
+and write into a destination cache, paged with its own random block table or
+contiguous; destination slots are pre-filled with a NaN sentinel so that any slot the
+call must not write is checked bit for bit.
 """
 from __future__ import annotations
 
@@ -20,7 +26,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-KIND_KV, KIND_U, KIND_V, KIND_STRUCT = 0, 1, 2, 3
+KIND_KV, KIND_U, KIND_V, KIND_STRUCT, KIND_DST = 0, 1, 2, 3, 4
+DST_SENTINEL = 0x7FC1  # bf16 NaN with a payload the operator never produces
 
 
 @dataclass(frozen=True)
@@ -49,6 +56,9 @@ class Workload:
     outlier_scale: float = 8.0
     dtype: str = "bf16"
     note: str = ""
+    recall: bool = False        # out of place: canonical store -> destination cache
+    dst_page_size: int = 0      # recall destination: 0 contiguous, > 0 paged
+    dst_pool_pages: int = 0     # recall destination pool pages per layer (paged)
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -87,6 +97,13 @@ WORKLOADS = {
         theta=1e6, rank=64, tokens=32768, delta=65536, page_size=16, pool_pages=2048,
         note="72B-shaped long-video paged cache: 80 layers, 8 KV heads x 128, T=32768 in "
              "16-token pages scattered by a random block table, delta +65536, rank-64"),
+    "recall_72b_paged": Workload(
+        key="recall_72b_paged", wid=5, family="gqa", layers=80, heads=8, head_dim=128,
+        theta=1e6, rank=64, tokens=32768, delta=65536, recall=True, dst_page_size=16,
+        dst_pool_pages=2048,
+        note="recall of a 72B-shaped long-video segment: canonical contiguous store "
+             "(80 layers, 8 KV heads x 128, T=32768) rebuilt with delta +65536 and a rank-64 "
+             "patch into a paged cache of 16-token pages under a random block table"),
 }
 
 
@@ -183,6 +200,40 @@ def channel_layouts(w: Workload, total_tokens: int, pool_pages: int = 0) -> list
                  page_stride=0) for b in (0, 1)]
 
 
+def dst_geometry(w: Workload, total_tokens: int):
+    """Recall destination: (page_size, pool pages per layer, block table or None)."""
+    P = w.dst_page_size
+    if P <= 0:
+        return 0, 0, None
+    need = -(-total_tokens // P)
+    pool = max(w.dst_pool_pages, need)
+    rng = np.random.default_rng(np.random.SeedSequence([w.wid, KIND_DST]))
+    return P, pool, rng.permutation(pool)[:need].astype(np.int32)
+
+
+def dst_layouts(w: Workload, total_tokens: int) -> list:
+    """Recall destination layout per channel (same keys as channel_layouts)."""
+    P, pool, _ = dst_geometry(w, total_tokens)
+    if w.family == "mla":
+        row = w.head_dim + w.rope_mla
+        slots = pool * P if P else total_tokens
+        ps = P * row if P else 0
+        return [dict(buffer=0, offset=0, heads=1, dim=w.head_dim, rope_dim=0,
+                     layer_stride=slots * row, slot_stride=row, head_stride=w.head_dim,
+                     page_stride=ps),
+                dict(buffer=0, offset=w.head_dim, heads=1, dim=w.rope_mla, rope_dim=w.rope_mla,
+                     layer_stride=slots * row, slot_stride=row, head_stride=w.rope_mla,
+                     page_stride=ps)]
+    return channel_layouts(w.with_(page_size=P), total_tokens, pool)
+
+
+def dst_buffer_shapes(w: Workload, total_tokens: int) -> list:
+    P, pool, _ = dst_geometry(w, total_tokens)
+    if w.family == "mla":
+        return [(w.layers, (pool * P) if P else total_tokens, w.head_dim + w.rope_mla)]
+    return buffer_shapes(w.with_(page_size=P), total_tokens, pool)
+
+
 def buffer_shapes(w: Workload, total_tokens: int, pool_pages: int = 0) -> list:
     """Shape of each KV buffer (MLA: one combined buffer; GQA/MHA: K and V)."""
     if w.family == "mla":
@@ -268,14 +319,57 @@ def make_inputs(w: Workload, rank: int, device="cpu", pass_id: int = 0) -> Input
     return inp
 
 
+@dataclass
+class RecallInputs:
+    """A recall problem: the canonical store (with chunks and factors) and the
+    destination cache."""
+    src: Inputs
+    dst_buffers: list
+    dst_layouts: list
+    dst_page_size: int
+    dst_pool_pages: int
+    dst_block_table: np.ndarray | None
+    dst_block_table_t: object = None
+
+    @property
+    def workload(self) -> Workload:
+        return self.src.workload
+
+    @property
+    def rank(self) -> int:
+        return self.src.rank
+
+
+def make_recall_inputs(w: Workload, rank: int, device="cpu", pass_id: int = 0) -> RecallInputs:
+    """Canonical store as make_inputs draws it, and a destination pre-filled with
+    DST_SENTINEL (or 0x7FC00001 for fp32)."""
+    import torch
+    src = make_inputs(w, rank, device, pass_id)
+    T = src.struct.total_tokens
+    P, pool, table = dst_geometry(w, T)
+    dt = _torch_dtype(w)
+    bufs = []
+    for shp in dst_buffer_shapes(w, T):
+        if dt == torch.bfloat16:
+            b = torch.full(shp, DST_SENTINEL, dtype=torch.int16, device=device).view(torch.bfloat16)
+        else:
+            b = torch.full(shp, 0x7FC00001, dtype=torch.int32, device=device).view(torch.float32)
+        bufs.append(b)
+    r = RecallInputs(src, bufs, dst_layouts(w, T), P, pool, table)
+    if table is not None:
+        r.dst_block_table_t = torch.as_tensor(table, device=device)
+    return r
+
+
 # ------------------------------------------------------------------ accounting
 
 def algorithmic_bytes(w: Workload, rank: int, total_tokens: int | None = None,
                       num_chunks: int | None = None) -> int:
-    """Bytes an ideal in-place pass moves: every touched KV element read once and
-    written once, every factor element read once.  With rank 0 only the rotated
-    dims of rotating channels move (chunks with delta 0 would move nothing; no
-    workload here has one).  Block table, offsets and deltas are not counted."""
+    """Bytes an ideal pass moves: every touched KV element read once and written once,
+    every factor element read once.  In place with rank 0 only the rotated dims of
+    rotating channels move (chunks with delta 0 would move nothing; no workload here
+    has one); a recall reads every source row and writes every destination row whole.
+    Block tables, offsets and deltas are not counted."""
     if total_tokens is None or num_chunks is None:
         st = structure(w)
         total_tokens, num_chunks = st.total_tokens, st.num_chunks
@@ -285,7 +379,9 @@ def algorithmic_bytes(w: Workload, rank: int, total_tokens: int | None = None,
     total = 0
     for c in lay:
         F = c["heads"] * c["dim"]
-        if rank == 0:
+        if rank == 0 and w.recall:  # recall copies every row whole
+            total += 2 * es * F * T * L
+        elif rank == 0:
             total += 2 * es * c["heads"] * c["rope_dim"] * T * L
         else:
             total += L * (2 * es * F * T + es * rank * T + es * F * rank * n)

@@ -36,7 +36,8 @@ def bf16_ordinal(bits: np.ndarray) -> np.ndarray:
 
 
 def bf16_value(bits: np.ndarray) -> np.ndarray:
-    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # signalling NaN patterns widen quietly
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def bf16_ulp(y: np.ndarray) -> np.ndarray:
@@ -238,4 +239,119 @@ def sampled_check(inp, run, n=1024, seed=0) -> Report:
                         moved[h * lay["dim"]:h * lay["dim"] + lay["rope_dim"]] = True
                 s = np.where(moved, s, -1.0)
             compare(after[c][k], o, y, s, inp.rank, rep)
+    return rep
+
+
+# ----------------------------------------------------------------- recall (out of place)
+
+def _dicts(layouts, bufs, factors=None, rank=0):
+    out = []
+    for c, lay in enumerate(layouts):
+        d = dict(lay)
+        d["data"] = bufs[lay["buffer"]]
+        if factors is not None and rank > 0:
+            d["U"], d["V"] = factors[0][c], factors[1][c]
+        out.append(d)
+    return out
+
+
+def check_recall(rinp, run) -> tuple:
+    """Run the recall `run(rinp)` on the GPU and compare the whole destination with the
+    oracle's recall (and the source with its state before).  Returns (report, src_ok)."""
+    import torch
+    from oracle import oracle as orc
+    src = rinp.src
+    w = rinp.workload
+    s_before = [host_bits(b) for b in src.buffers]
+    d_before = [host_bits(b) for b in rinp.dst_buffers]
+    factors = ([host_bits(u) for u in src.U], [host_bits(v) for v in src.V])
+    run(rinp)
+    torch.cuda.synchronize()
+    s_after = [host_bits(b) for b in src.buffers]
+    d_after = [host_bits(b) for b in rinp.dst_buffers]
+    out = [b.copy() for b in d_before]
+    if out[0].dtype == np.uint16:
+        y = [bf16_value(b) for b in d_before]
+    else:
+        y = [b.astype(np.float64) for b in d_before]
+    s = [np.full(b.size, -1.0) for b in d_before]
+    orc.recall_patch(_dicts(src.layouts, [b.copy() for b in s_before], factors, src.rank),
+                     _dicts(rinp.dst_layouts, out), num_layers=w.layers, theta=w.theta,
+                     offsets=src.struct.offsets, delta=src.struct.delta, rank=src.rank,
+                     src_page_size=w.page_size, src_block_table=src.struct.block_table,
+                     dst_page_size=rinp.dst_page_size, dst_block_table=rinp.dst_block_table,
+                     y_out=[y[lay["buffer"]] for lay in rinp.dst_layouts],
+                     s_out=[s[lay["buffer"]] for lay in rinp.dst_layouts])
+    rep = Report()
+    for g, o, yy, ss in zip(d_after, out, y, s):
+        compare(g, o, yy, ss, src.rank, rep)
+    src_ok = all(np.array_equal(a, b) for a, b in zip(s_after, s_before))
+    return rep, src_ok
+
+
+def sampled_check_recall(rinp, run, n=1024, seed=0) -> Report:
+    """Run a full-size recall and check sampled destination rows against the oracle's
+    row function applied to the source rows."""
+    import torch
+    from oracle import oracle as orc
+    src = rinp.src
+    w, st = src.workload, src.struct
+    rows = sample_rows(src, n, seed)
+
+    def idx_for(layouts, page_size, table, c):
+        lay = layouts[c]
+        D, H = lay["dim"], lay["heads"]
+        ii = np.empty((len(rows), H * D), dtype=np.int64)
+        for k, (l, t) in enumerate(rows):
+            for h in range(H):
+                ii[k, h * D:(h + 1) * D] = (int(lay.get("offset", 0)) +
+                                            orc.row_offset(lay, page_size, table, l, t, h) +
+                                            np.arange(D))
+        return ii
+
+    def gather(bufs, layouts, ii, c):
+        buf = bufs[layouts[c]["buffer"]].view(-1)
+        g = buf[torch.as_tensor(ii.ravel(), device=buf.device)].view(len(rows), -1)
+        return host_bits(g).reshape(len(rows), -1)
+
+    chans = range(len(src.layouts))
+    sidx = {c: idx_for(src.layouts, w.page_size, st.block_table, c) for c in chans}
+    didx = {c: idx_for(rinp.dst_layouts, rinp.dst_page_size, rinp.dst_block_table, c)
+            for c in chans}
+    before = {c: gather(src.buffers, src.layouts, sidx[c], c) for c in chans}
+    us, vs = {}, {}
+    if src.rank > 0:
+        li = torch.as_tensor([l for l, _ in rows], device=src.U[0].device)
+        ti = torch.as_tensor([t for _, t in rows], device=src.U[0].device)
+        for c in chans:
+            us[c] = host_bits(src.U[c][li, ti]).reshape(len(rows), -1)
+            vs[c] = host_bits(src.V[c]).reshape(w.layers, st.num_chunks, -1, src.rank)
+    run(rinp)
+    torch.cuda.synchronize()
+    rep = Report()
+    for c in chans:
+        lay = src.layouts[c]
+        got = gather(rinp.dst_buffers, rinp.dst_layouts, didx[c], c)
+        src_after = gather(src.buffers, src.layouts, sidx[c], c)
+        assert np.array_equal(src_after, before[c]), "recall wrote its source"
+        for k, (l, t) in enumerate(rows):
+            j = int(np.searchsorted(st.offsets, t, side="right") - 1)
+            d = int(st.delta[j])
+            u = us[c][k] if src.rank > 0 else None
+            V = vs[c][l, j] if src.rank > 0 else None
+            x = before[c][k]
+            o = orc.row(x, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, u, V)
+            xf = bf16_value(x)
+            uf = None if u is None else bf16_value(u)
+            Vf = None if V is None else bf16_value(V)
+            y = orc.row_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, uf, Vf)
+            s = orc.row_magnitude_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d,
+                                      uf, Vf)
+            if src.rank == 0:  # copied elements must match bit for bit
+                moved = np.zeros(lay["heads"] * lay["dim"], bool)
+                if d != 0:
+                    for h in range(lay["heads"]):
+                        moved[h * lay["dim"]:h * lay["dim"] + lay["rope_dim"]] = True
+                s = np.where(moved, s, -1.0)
+            compare(got[k], o, y, s, src.rank, rep)
     return rep

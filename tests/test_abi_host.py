@@ -300,3 +300,81 @@ def test_chunk_boundary_tail_launch():
     assert info.units == 28 * 2 * fb * (2 * groups)
     _, info = plan_names(*gqa(T=4096, m=0, n=5))  # rotation only: one kernel, no tail
     assert info.launches == 1
+
+
+# ----------------------------------------------------------------- recall (out of place)
+
+def recall_dst(T=4096, L=28, H=4, D=128, r=128, pages=300, addr=FAKE + (5 << 40), dtype=None):
+    """A paged destination cache matching gqa()'s source shape."""
+    es = 2 if dtype in (None, K.KAMERA_BF16) else 4
+    chans = [K.channel(FakeTensor(addr + c * (1 << 36), es), heads=H, dim=D,
+                       rope_dim=r if c == 0 else 0, layer_stride=pages * 16 * H * D,
+                       slot_stride=H * D, head_stride=D, page_stride=16 * H * D)
+             for c in range(2)]
+    return K.kv_desc(chans, dtype=K.KAMERA_BF16 if dtype is None else dtype, num_layers=L,
+                     rope_theta=0.0, page_size=16, num_pages=pages,
+                     block_table=FakeTensor(FAKE + (6 << 40)))
+
+
+def recall_plan_names(src, dst, ch, p):
+    st, info = K.kamera_recall_plan(src, dst, ch, p)
+    assert st == K.KAMERA_OK, K.kamera_last_error()
+    return [K.KERNEL_NAMES[k] for k in info.kernel], info
+
+
+def test_recall_kernel_choice():
+    # Every channel is written whole, so both launch, rank 0 included.
+    for m in (0, 8, 32, 64, 128):
+        src, ch, p = gqa(m=m)
+        names, info = recall_plan_names(src, recall_dst(), ch, p)
+        assert names == ["rotate+patch mfma"] * 2 and info.launches == 1, m
+    src, ch, p = gqa(m=32, n=3)
+    _, info = recall_plan_names(src, recall_dst(), ch, p)
+    assert info.launches == 2
+    src, ch, p = gqa(m=12)  # rank not a multiple of 8
+    names, _ = recall_plan_names(src, recall_dst(), ch, p)
+    assert names == ["generic", "generic"]
+    src, ch, p = gqa(m=8, dtype=K.KAMERA_F32)
+    names, _ = recall_plan_names(src, recall_dst(dtype=K.KAMERA_F32), ch, p)
+    assert names == ["generic", "generic"]
+    src, ch, p = gqa(m=8)
+    dst = recall_dst()
+    dst.ch[1].data = FAKE + (5 << 40) + (1 << 36) + 2  # element-aligned only
+    names, info = recall_plan_names(src, dst, ch, p)
+    assert names == ["rotate+patch mfma", "generic"] and info.launches == 2
+
+
+def test_recall_argument_errors():
+    src, ch, p = gqa(m=8)
+    st, _ = K.kamera_recall_plan(src, None, ch, p)
+    assert st == K.KAMERA_E_NULL
+    st, _ = K.kamera_recall_plan(src, recall_dst(dtype=K.KAMERA_F32), ch, p)
+    assert st == K.KAMERA_E_SHAPE
+    st, _ = K.kamera_recall_plan(src, recall_dst(H=8), ch, p)
+    assert st == K.KAMERA_E_SHAPE
+    st, _ = K.kamera_recall_plan(src, recall_dst(r=64), ch, p)
+    assert st == K.KAMERA_E_SHAPE
+    st, _ = K.kamera_recall_plan(src, recall_dst(L=27), ch, p)
+    assert st == K.KAMERA_E_SHAPE
+    dst = recall_dst()
+    dst.block_table = None
+    st, _ = K.kamera_recall_plan(src, dst, ch, p)
+    assert st == K.KAMERA_E_NULL
+    dst = recall_dst()
+    dst.ch[0].data = None
+    st, _ = K.kamera_recall_plan(src, dst, ch, p)
+    assert st == K.KAMERA_E_NULL
+    # destination overlapping the source, or a factor
+    st, _ = K.kamera_recall_plan(src, recall_dst(addr=FAKE + 4096), ch, p)
+    assert st == K.KAMERA_E_ALIAS
+    st, _ = K.kamera_recall_plan(src, recall_dst(addr=p.U[1] - 4096), ch, p)
+    assert st == K.KAMERA_E_ALIAS
+    # source-side errors are the in-place call's
+    src2, ch2, p2 = gqa(m=8)
+    src2.ch[0].rope_dim = 3
+    st, _ = K.kamera_recall_plan(src2, recall_dst(), ch2, p2)
+    assert st == K.KAMERA_E_SHAPE
+    # empty problem: nothing to launch, but still checked
+    src, ch, p = gqa(m=8, T=0, n=0)
+    names, info = recall_plan_names(src, recall_dst(), ch, p)
+    assert info.launches == 0
