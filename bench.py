@@ -12,6 +12,10 @@ element read once and written once, every factor element read once) x steps / wa
 time, in GB/s (1e9).  roofline = the dominant kernel (the relocate+patch launch)
 timed with HIP events on its stream.  cpu_baseline = the fp64 CPU oracle on the host
 cores over a bounded sample of the same workload.
+
+`--workload recall_72b_paged` measures the out-of-place recall entry point instead:
+a canonical contiguous store rebuilt into a paged cache (same metric, same roofline
+kernel template in its out-of-place form).
 """
 from __future__ import annotations
 
@@ -87,19 +91,33 @@ def main():
 
     # Inputs: one instance per (pass, copy); copies share values (the traffic does not
     # depend on them) but live at distinct addresses.
+    def clone(base):
+        c = synth.Inputs(base.workload, base.rank, base.struct, base.pool_pages,
+                         [b.clone() for b in base.buffers], base.layouts,
+                         [u.clone() for u in base.U], [v.clone() for v in base.V],
+                         base.offsets_t, base.delta_t, base.block_table_t)
+        return c
+
     insts = []
     for pi, r in enumerate(ranks):
-        base = synth.make_inputs(w, r, device=dev, pass_id=pi)
-        row = [base]
-        for _ in range(copies - 1):
-            c = synth.Inputs(base.workload, base.rank, base.struct, base.pool_pages,
-                             [b.clone() for b in base.buffers], base.layouts,
-                             [u.clone() for u in base.U], [v.clone() for v in base.V],
-                             base.offsets_t, base.delta_t, base.block_table_t)
-            row.append(c)
+        if w.recall:
+            base = synth.make_recall_inputs(w, r, device=dev, pass_id=pi)
+            row = [base]
+            for _ in range(copies - 1):
+                row.append(synth.RecallInputs(clone(base.src), [b.clone() for b in base.dst_buffers],
+                                              base.dst_layouts, base.dst_page_size,
+                                              base.dst_pool_pages, base.dst_block_table,
+                                              base.dst_block_table_t))
+        else:
+            base = synth.make_inputs(w, r, device=dev, pass_id=pi)
+            row = [base] + [clone(base) for _ in range(copies - 1)]
         insts.append(row)
-    descs = [[ops.descriptors_for(c) for c in row] for row in insts]
-    plan_info = [ops.plan(row[0]) for row in insts]
+    if w.recall:
+        descs = [[ops.recall_descriptors(c) for c in row] for row in insts]
+        plan_info = [ops.recall_plan(row[0]) for row in insts]
+    else:
+        descs = [[ops.descriptors_for(c) for c in row] for row in insts]
+        plan_info = [ops.plan(row[0]) for row in insts]
     lib = K.lib()
     import ctypes as C
 
@@ -107,11 +125,16 @@ def main():
     s_ptr = C.c_void_p(stream.cuda_stream)
 
     def launch(pi, ci):
-        kv, ch, p = descs[pi][ci]
-        if p is None:
-            st = lib.kamera_relocate(C.byref(kv), C.byref(ch), s_ptr)
+        if w.recall:
+            src, dst, ch, p = descs[pi][ci]
+            st = lib.kamera_recall_patch(C.byref(src), C.byref(dst), C.byref(ch),
+                                         None if p is None else C.byref(p), s_ptr)
         else:
-            st = lib.kamera_relocate_patch(C.byref(kv), C.byref(ch), C.byref(p), s_ptr)
+            kv, ch, p = descs[pi][ci]
+            if p is None:
+                st = lib.kamera_relocate(C.byref(kv), C.byref(ch), s_ptr)
+            else:
+                st = lib.kamera_relocate_patch(C.byref(kv), C.byref(ch), C.byref(p), s_ptr)
         if st != 0:
             raise K.KameraError(st, K.kamera_last_error())
 
@@ -183,6 +206,8 @@ def main():
             "layers": w.layers, "kv_heads": w.heads, "head_dim": w.head_dim,
             "tokens": st.total_tokens, "chunks": st.num_chunks,
             "theta": w.theta, "passes_rank": list(ranks), "page_size": w.page_size,
+            "entry_point": "kamera_recall_patch" if w.recall else "kamera_relocate_patch",
+            "dst_page_size": w.dst_page_size if w.recall else None,
             "bytes_per_step": bytes_step, "input_copies": copies,
             "parallelism": "single GPU",
         },
@@ -220,28 +245,43 @@ def cpu_baseline(w, ranks, seconds: float):
 
     print("[bench] cpu baseline: oracle on host cores", file=sys.stderr, flush=True)
 
+    def host(t):
+        return t.view(torch.int16).numpy().view(np.uint16)
+
     def prepare(ww):
         probs = []
         for pi, r in enumerate(ranks):
-            inp = synth.make_inputs(ww, r, device="cpu", pass_id=pi)
-            bufs = [b.view(torch.int16).numpy().view(np.uint16).ravel() for b in inp.buffers]
+            rinp = synth.make_recall_inputs(ww, r, device="cpu", pass_id=pi) if w.recall else None
+            inp = rinp.src if w.recall else synth.make_inputs(ww, r, device="cpu", pass_id=pi)
+            bufs = [host(b).ravel() for b in inp.buffers]
             chans = []
             for c, lay in enumerate(inp.layouts):
                 d = dict(lay)
                 d["data"] = bufs[lay["buffer"]]
                 if r > 0:
-                    d["U"] = inp.U[c].view(torch.int16).numpy().view(np.uint16)
-                    d["V"] = inp.V[c].view(torch.int16).numpy().view(np.uint16)
+                    d["U"] = host(inp.U[c])
+                    d["V"] = host(inp.V[c])
                 chans.append(d)
-            probs.append((r, inp, chans))
+            dchans = None
+            if w.recall:
+                dbufs = [host(b).ravel() for b in rinp.dst_buffers]
+                dchans = [dict(lay, data=dbufs[lay["buffer"]]) for lay in rinp.dst_layouts]
+            probs.append((r, inp, chans, rinp, dchans))
         return probs
 
     def step(ww, probs):
         t0 = time.perf_counter()
-        for r, inp, chans in probs:
-            orc.relocate_patch(chans, num_layers=ww.layers, theta=w.theta,
-                               offsets=inp.struct.offsets, delta=inp.struct.delta, rank=r,
-                               page_size=w.page_size, block_table=inp.struct.block_table)
+        for r, inp, chans, rinp, dchans in probs:
+            if w.recall:
+                orc.recall_patch(chans, dchans, num_layers=ww.layers, theta=w.theta,
+                                 offsets=inp.struct.offsets, delta=inp.struct.delta, rank=r,
+                                 src_page_size=w.page_size, src_block_table=inp.struct.block_table,
+                                 dst_page_size=rinp.dst_page_size,
+                                 dst_block_table=rinp.dst_block_table)
+            else:
+                orc.relocate_patch(chans, num_layers=ww.layers, theta=w.theta,
+                                   offsets=inp.struct.offsets, delta=inp.struct.delta, rank=r,
+                                   page_size=w.page_size, block_table=inp.struct.block_table)
         return time.perf_counter() - t0
 
     # One layer first, to size the sample.
