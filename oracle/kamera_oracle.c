@@ -28,11 +28,17 @@
  *     only the keys move and the values are carried over unchanged.
  *
  * Readings taken where the pages are silent (the pages give no RoPE formula):
- *   - NeoX half-split pairing: dim i pairs with dim i + r/2 (i < r/2), where r
- *     is the number of rotated dims of a head; dims >= r are not rotated.
+ *   - NeoX half-split pairing: rotary pair i (i < r/2) is dims (i, i + r/2), where
+ *     r is the number of rotated dims of a head; dims >= r are not rotated.  The
+ *     interleaved variant pairs dims (2i, 2i + 1) instead.
  *   - Pair frequency omega_i = theta^(-2i/r); angle delta * omega_i; the pair
  *     (a, b) turns to (a cos - b sin, b cos + a sin).  Positive delta moves the
  *     chunk to a later position.
+ *   - Multimodal rotary positions (M-RoPE, named in [N §4, composition: image KV
+ *     transplanted with M-RoPE re-rotation]): a position is a vector of up to 4
+ *     components and the pairs are cut, in pair order, into as many sections; pair
+ *     i of section s turns by delta[s] * omega_i.  A pair whose section delta is 0
+ *     does not move.  One section is plain RoPE.
  *   - The patch is added after the rotation and is not itself rotated.
  *   - R(0) is the identity matrix: a chunk with delta 0 is not rotated at all.
  *   - The result is rounded once, from fp64, to the storage type (bf16 or fp32)
@@ -115,20 +121,70 @@ double orc_freq(double theta, int r, int i) {
     return pow(theta, -2.0 * (double)i / (double)r);
 }
 
-/* y = R(delta) x for one head of `dim` values, in fp64 ([K §2, "Relocacao"]).
- * Dim i < r/2 pairs with dim i + r/2; dims >= r are copied. */
-void orc_rotate_head_f64(const double* x, double* y, int dim, int r,
-                         double theta, int64_t delta) {
+/* Positional variant of the rotation: pairing and M-RoPE sections. */
+typedef struct {
+    int32_t pairing;          /* 0: NeoX half-split (i, i + r/2); 1: interleaved (2i, 2i + 1) */
+    int32_t num_sections;     /* 0 or 1: one delta per chunk; 2..4: M-RoPE sections */
+    int32_t section_pairs[4]; /* pairs per section, in pair order; they sum to r/2 */
+} orc_rope;
+
+static int rope_sections(const orc_rope* q) {
+    return (q && q->num_sections > 1) ? q->num_sections : 1;
+}
+
+/* Section of rotary pair i. */
+static int section_of(const orc_rope* q, int i) {
+    int S = rope_sections(q), end = 0;
+    for (int s = 0; s < S; ++s) {
+        end += (S == 1) ? (1 << 30) : q->section_pairs[s];
+        if (i < end) return s;
+    }
+    return S - 1;
+}
+
+/* Dims of rotary pair i in a head that rotates r dims. */
+static void pair_dims(const orc_rope* q, int r, int i, int* d0, int* d1) {
+    if (q && q->pairing == 1) { *d0 = 2 * i; *d1 = 2 * i + 1; }
+    else { *d0 = i; *d1 = i + r / 2; }
+}
+
+/* Rotary pair that dim d (< r) belongs to. */
+static int pair_of_dim(const orc_rope* q, int r, int d) {
+    if (q && q->pairing == 1) return d / 2;
+    return d < r / 2 ? d : d - r / 2;
+}
+
+/* Whether dim d of a head moves under the per-section deltas. */
+static int dim_moves(const orc_rope* q, int r, int d, const int64_t* delta) {
+    if (d >= r) return 0;
+    return delta[section_of(q, pair_of_dim(q, r, d))] != 0;
+}
+
+/* y = R(delta) x for one head of `dim` values, in fp64 ([K §2, "Relocacao"]), with
+ * the pairing and sections of `q` (NULL: NeoX, one section).  delta holds one value
+ * per section.  Pairs whose section delta is 0 and dims >= r are copied. */
+void orc_rotate_head_spec_f64(const double* x, double* y, int dim, int r, double theta,
+                              const int64_t* delta, const orc_rope* q) {
     for (int d = 0; d < dim; ++d) y[d] = x[d];
-    if (delta == 0 || r == 0) return;
+    if (r == 0) return;
     int half = r / 2;
     for (int i = 0; i < half; ++i) {
-        double phi = (double)delta * orc_freq(theta, r, i);
+        int64_t dl = delta[section_of(q, i)];
+        if (dl == 0) continue;
+        int d0, d1;
+        pair_dims(q, r, i, &d0, &d1);
+        double phi = (double)dl * orc_freq(theta, r, i);
         double cs = cos(phi), sn = sin(phi);
-        double a = x[i], b = x[i + half];
-        y[i] = a * cs - b * sn;
-        y[i + half] = b * cs + a * sn;
+        double a = x[d0], b = x[d1];
+        y[d0] = a * cs - b * sn;
+        y[d1] = b * cs + a * sn;
     }
+}
+
+/* The plain form: NeoX pairing, one delta.  Dim i < r/2 pairs with dim i + r/2. */
+void orc_rotate_head_f64(const double* x, double* y, int dim, int r,
+                         double theta, int64_t delta) {
+    orc_rotate_head_spec_f64(x, y, dim, r, theta, &delta, NULL);
 }
 
 /* y[f] += sum_k u[k] * V[f][k] for f < F: one token row of U_m V_m^T
@@ -143,22 +199,39 @@ void orc_patch_row_f64(double* y, int F, int m, const double* u, const double* V
 
 /* One token row of one channel (heads x dim values, head-major), in fp64:
  * rotate every head, then add the patch row (m may be 0). */
+void orc_row_spec_f64(const double* x, double* y, int heads, int dim, int r, double theta,
+                      const int64_t* delta, const orc_rope* q, int m, const double* u,
+                      const double* V) {
+    for (int h = 0; h < heads; ++h)
+        orc_rotate_head_spec_f64(x + (int64_t)h * dim, y + (int64_t)h * dim, dim, r, theta,
+                                 delta, q);
+    if (m > 0) orc_patch_row_f64(y, heads * dim, m, u, V);
+}
+
 void orc_row_f64(const double* x, double* y, int heads, int dim, int r, double theta,
                  int64_t delta, int m, const double* u, const double* V) {
-    for (int h = 0; h < heads; ++h)
-        orc_rotate_head_f64(x + (int64_t)h * dim, y + (int64_t)h * dim, dim, r, theta, delta);
-    if (m > 0) orc_patch_row_f64(y, heads * dim, m, u, V);
+    orc_row_spec_f64(x, y, heads, dim, r, theta, &delta, NULL, m, u, V);
 }
 
 /* One token row in storage format (dtype 0 = bf16 bits, 1 = fp32): x_in and out
  * hold heads*dim contiguous elements, u holds m, V holds [heads*dim][m], all of
  * the same dtype.  out may equal x_in.  With m = 0, every element the rotation
  * does not move keeps its bits. Returns 0, or -1 on bad arguments. */
-int orc_row(int dtype, const void* x_in, void* out, int heads, int dim, int r,
-            double theta, int64_t delta, int m, const void* u, const void* V) {
+int orc_row_spec(int dtype, const void* x_in, void* out, int heads, int dim, int r,
+                 double theta, const int64_t* delta, const orc_rope* q, int m, const void* u,
+                 const void* V) {
     if ((dtype != ORC_BF16 && dtype != ORC_F32) || heads < 1 || dim < 1 || r < 0 ||
         r > dim || (r & 1) || m < 0)
         return -1;
+    if (q && q->num_sections > 1) {
+        int sum = 0;
+        if (q->num_sections > 4) return -1;
+        for (int k = 0; k < q->num_sections; ++k) {
+            if (q->section_pairs[k] < 0) return -1;
+            sum += q->section_pairs[k];
+        }
+        if (r > 0 && sum != r / 2) return -1;
+    }
     int64_t F = (int64_t)heads * dim;
     double* x = (double*)malloc(sizeof(double) * F);
     double* y = (double*)malloc(sizeof(double) * F);
@@ -168,15 +241,20 @@ int orc_row(int dtype, const void* x_in, void* out, int heads, int dim, int r,
     for (int64_t f = 0; f < F; ++f) x[f] = load_elem(dtype, x_in, f);
     for (int k = 0; k < m; ++k) ud[k] = load_elem(dtype, u, k);
     for (int64_t i = 0; i < F * m; ++i) vd[i] = load_elem(dtype, V, i);
-    orc_row_f64(x, y, heads, dim, r, theta, delta, m, ud, vd);
+    orc_row_spec_f64(x, y, heads, dim, r, theta, delta, q, m, ud, vd);
     for (int64_t f = 0; f < F; ++f) {
         int d = (int)(f % dim);
-        int moved = m > 0 || (delta != 0 && d < r);
+        int moved = m > 0 || dim_moves(q, r, d, delta);
         if (moved) store_elem(dtype, out, f, y[f]);
         else if (out != x_in) copy_elem(dtype, out, f, x_in, f);
     }
     free(x); free(y); free(ud); free(vd);
     return 0;
+}
+
+int orc_row(int dtype, const void* x_in, void* out, int heads, int dim, int r,
+            double theta, int64_t delta, int m, const void* u, const void* V) {
+    return orc_row_spec(dtype, x_in, out, heads, dim, r, theta, &delta, NULL, m, u, V);
 }
 
 /* ---------------------------------------------------------- whole operator */
@@ -197,8 +275,9 @@ typedef struct {
     const int32_t* block_table; /* [ceil(total_tokens / page_size)] when paged */
     int64_t total_tokens;
     const int64_t* offsets;     /* [num_chunks + 1], 0 = o_0 <= ... = total */
-    const int64_t* delta;       /* [num_chunks] */
+    const int64_t* delta;       /* [num_chunks][sections] (sections = 1 without M-RoPE) */
     int32_t num_chunks, rank;
+    orc_rope rope;              /* pairing and M-RoPE sections */
 } orc_problem;
 
 /* Element offset of (layer, logical token t, head h, dim 0).  Contiguous: the
@@ -224,26 +303,35 @@ static int64_t chunk_of(const orc_problem* p, int64_t t) {
  * pair |a cos| + |b sin| (and |b cos| + |a sin|), |x| for an unrotated dim, plus
  * sum_k |u_k V[f][k]| for the patch.  It bounds the fp32 evaluation error of any
  * ordering of the same terms; the parity tolerance near cancellation scales with it. */
-void orc_row_magnitude_f64(const double* x, double* s, int heads, int dim, int r,
-                           double theta, int64_t delta, int m, const double* u,
-                           const double* V) {
+void orc_row_magnitude_spec_f64(const double* x, double* s, int heads, int dim, int r,
+                                double theta, const int64_t* delta, const orc_rope* q, int m,
+                                const double* u, const double* V) {
     int half = r / 2;
     for (int h = 0; h < heads; ++h) {
         const double* xh = x + (int64_t)h * dim;
         double* sh = s + (int64_t)h * dim;
         for (int d = 0; d < dim; ++d) sh[d] = fabs(xh[d]);
-        if (delta == 0 || r == 0) continue;
         for (int i = 0; i < half; ++i) {
-            double phi = (double)delta * orc_freq(theta, r, i);
+            int64_t dl = delta[section_of(q, i)];
+            if (dl == 0) continue;
+            int d0, d1;
+            pair_dims(q, r, i, &d0, &d1);
+            double phi = (double)dl * orc_freq(theta, r, i);
             double cs = fabs(cos(phi)), sn = fabs(sin(phi));
-            double a = fabs(xh[i]), b = fabs(xh[i + half]);
-            sh[i] = a * cs + b * sn;
-            sh[i + half] = b * cs + a * sn;
+            double a = fabs(xh[d0]), b = fabs(xh[d1]);
+            sh[d0] = a * cs + b * sn;
+            sh[d1] = b * cs + a * sn;
         }
     }
     int64_t F = (int64_t)heads * dim;
     for (int64_t f = 0; f < F; ++f)
         for (int k = 0; k < m; ++k) s[f] += fabs(u[k] * V[f * m + k]);
+}
+
+void orc_row_magnitude_f64(const double* x, double* s, int heads, int dim, int r,
+                           double theta, int64_t delta, int m, const double* u,
+                           const double* V) {
+    orc_row_magnitude_spec_f64(x, s, heads, dim, r, theta, &delta, NULL, m, u, V);
 }
 
 /* The reuse operator over a whole problem, in place on host memory.  When y_out[c]
@@ -271,8 +359,10 @@ int orc_relocate_patch_ex(const orc_problem* p, double* const* y_out, double* co
             for (int64_t t = 0; t < T; ++t) {
                 int64_t j = chunk_of(p, t);
                 if (j < 0) { bad = 1; continue; }
-                int64_t dj = p->delta[j];
-                if (m == 0 && dj == 0) continue;
+                const int64_t* dj = p->delta + j * rope_sections(&p->rope);
+                int any = 0;
+                for (int k = 0; k < rope_sections(&p->rope); ++k) any |= dj[k] != 0;
+                if (m == 0 && !any) continue;
                 char* row = (char*)malloc((size_t)(F * es));
                 double* x = (double*)malloc(sizeof(double) * F);
                 double* y = (double*)malloc(sizeof(double) * F);
@@ -294,17 +384,19 @@ int orc_relocate_patch_ex(const orc_problem* p, double* const* y_out, double* co
                 }
                 if (yo) {
                     for (int64_t f = 0; f < F; ++f) x[f] = load_elem(p->dtype, row, f);
-                    orc_row_f64(x, y, ch->heads, ch->dim, ch->rope_dim, p->theta, dj, m, ud, vd);
-                    orc_row_magnitude_f64(x, s, ch->heads, ch->dim, ch->rope_dim, p->theta, dj, m, ud, vd);
+                    orc_row_spec_f64(x, y, ch->heads, ch->dim, ch->rope_dim, p->theta, dj, &p->rope,
+                                     m, ud, vd);
+                    orc_row_magnitude_spec_f64(x, s, ch->heads, ch->dim, ch->rope_dim, p->theta, dj,
+                                               &p->rope, m, ud, vd);
                 }
-                if (orc_row(p->dtype, row, row, ch->heads, ch->dim, ch->rope_dim, p->theta,
-                            dj, m, u, V) != 0)
+                if (orc_row_spec(p->dtype, row, row, ch->heads, ch->dim, ch->rope_dim, p->theta,
+                                 dj, &p->rope, m, u, V) != 0)
                     bad = 1;
                 for (int64_t h = 0; h < ch->heads; ++h) {
                     memcpy((char*)ch->data + offs[h] * es, row + h * ch->dim * es, (size_t)ch->dim * es);
                     if (yo) {
                         for (int d = 0; d < ch->dim; ++d) {
-                            int moved = m > 0 || d < ch->rope_dim;
+                            int moved = m > 0 || dim_moves(&p->rope, ch->rope_dim, d, dj);
                             if (!moved) continue;
                             yo[offs[h] + d] = y[h * ch->dim + d];
                             if (so) so[offs[h] + d] = s[h * ch->dim + d];
@@ -355,7 +447,7 @@ int orc_recall_patch_ex(const orc_problem* src, const orc_problem* dst, double* 
             for (int64_t t = 0; t < T; ++t) {
                 int64_t j = chunk_of(src, t);
                 if (j < 0) { bad = 1; continue; }
-                int64_t dj = src->delta[j];
+                const int64_t* dj = src->delta + j * rope_sections(&src->rope);
                 char* row = (char*)malloc((size_t)(F * es));
                 char* out = (char*)malloc((size_t)(F * es));
                 double* x = (double*)malloc(sizeof(double) * F);
@@ -377,19 +469,20 @@ int orc_recall_patch_ex(const orc_problem* src, const orc_problem* dst, double* 
                 }
                 if (yo) {
                     for (int64_t f = 0; f < F; ++f) x[f] = load_elem(src->dtype, row, f);
-                    orc_row_f64(x, y, sc->heads, sc->dim, sc->rope_dim, src->theta, dj, m, ud, vd);
-                    orc_row_magnitude_f64(x, s, sc->heads, sc->dim, sc->rope_dim, src->theta, dj, m,
-                                          ud, vd);
+                    orc_row_spec_f64(x, y, sc->heads, sc->dim, sc->rope_dim, src->theta, dj,
+                                     &src->rope, m, ud, vd);
+                    orc_row_magnitude_spec_f64(x, s, sc->heads, sc->dim, sc->rope_dim, src->theta,
+                                               dj, &src->rope, m, ud, vd);
                 }
-                if (orc_row(src->dtype, row, out, sc->heads, sc->dim, sc->rope_dim, src->theta, dj,
-                            m, u, V) != 0)
+                if (orc_row_spec(src->dtype, row, out, sc->heads, sc->dim, sc->rope_dim, src->theta,
+                                 dj, &src->rope, m, u, V) != 0)
                     bad = 1;
                 for (int64_t h = 0; h < sc->heads; ++h) {
                     int64_t o = orc_row_offset(dc, dst->page_size, dst->block_table, l, t, h);
                     memcpy((char*)dc->data + o * es, out + h * sc->dim * es, (size_t)sc->dim * es);
                     if (yo) {
                         for (int d = 0; d < sc->dim; ++d) {
-                            int moved = m > 0 || (dj != 0 && d < sc->rope_dim);
+                            int moved = m > 0 || dim_moves(&src->rope, sc->rope_dim, d, dj);
                             if (!moved) continue;
                             yo[o + d] = y[h * sc->dim + d];
                             if (so) so[o + d] = s[h * sc->dim + d];

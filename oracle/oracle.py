@@ -42,13 +42,40 @@ class _Channel(C.Structure):
                 ("U", C.c_void_p), ("V", C.c_void_p)]
 
 
+class _Rope(C.Structure):
+    _fields_ = [("pairing", C.c_int32), ("num_sections", C.c_int32),
+                ("section_pairs", C.c_int32 * 4)]
+
+
 class _Problem(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("num_layers", C.c_int32),
                 ("num_channels", C.c_int32), ("page_size", C.c_int32),
                 ("ch", _Channel * 2), ("theta", C.c_double),
                 ("block_table", C.c_void_p), ("total_tokens", C.c_int64),
                 ("offsets", C.c_void_p), ("delta", C.c_void_p),
-                ("num_chunks", C.c_int32), ("rank", C.c_int32)]
+                ("num_chunks", C.c_int32), ("rank", C.c_int32),
+                ("rope", _Rope)]
+
+
+NEOX = 0
+INTERLEAVED = 1
+
+
+def _rope(pairing: int = NEOX, sections=()) -> _Rope:
+    """Pairing (0 NeoX half-split, 1 interleaved) and M-RoPE sections (pairs per
+    section, in pair order; empty or one entry = plain RoPE)."""
+    q = _Rope()
+    q.pairing = pairing
+    sec = list(sections)
+    assert len(sec) <= 4
+    q.num_sections = len(sec) if len(sec) > 1 else 0
+    for k, v in enumerate(sec):
+        q.section_pairs[k] = v
+    return q
+
+
+def _delta_vec(delta) -> np.ndarray:
+    return np.ascontiguousarray(np.atleast_1d(np.asarray(delta, dtype=np.int64)))
 
 
 _lib = None
@@ -82,6 +109,19 @@ def lib():
         L.orc_recall_patch_ex.restype = C.c_int
         L.orc_recall_patch_ex.argtypes = [C.POINTER(_Problem), C.POINTER(_Problem),
                                           C.POINTER(C.c_void_p), C.POINTER(C.c_void_p)]
+        L.orc_rotate_head_spec_f64.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int,
+                                               C.c_double, C.c_void_p, C.POINTER(_Rope)]
+        L.orc_row_spec_f64.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
+                                       C.c_double, C.c_void_p, C.POINTER(_Rope), C.c_int,
+                                       C.c_void_p, C.c_void_p]
+        L.orc_row_spec.restype = C.c_int
+        L.orc_row_spec.argtypes = [C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
+                                   C.c_double, C.c_void_p, C.POINTER(_Rope), C.c_int,
+                                   C.c_void_p, C.c_void_p]
+        L.orc_row_magnitude_spec_f64.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int,
+                                                 C.c_int, C.c_double, C.c_void_p,
+                                                 C.POINTER(_Rope), C.c_int, C.c_void_p,
+                                                 C.c_void_p]
         L.orc_row_magnitude_f64.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
                                             C.c_double, C.c_int64, C.c_int, C.c_void_p,
                                             C.c_void_p]
@@ -131,15 +171,22 @@ def freq(theta: float, r: int, i: int) -> float:
 
 # ------------------------------------------------------------- fp64 forms
 
-def rotate_head_f64(x, r: int, theta: float, delta: int) -> np.ndarray:
+def rotate_head_f64(x, r: int, theta: float, delta, pairing: int = NEOX,
+                    sections=()) -> np.ndarray:
+    """One head in fp64; `delta` is one value, or one per M-RoPE section."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     y = np.empty_like(x)
-    lib().orc_rotate_head_f64(_ptr(x), _ptr(y), x.size, r, theta, int(delta))
+    if pairing == NEOX and not len(sections) > 1 and np.ndim(delta) == 0:
+        lib().orc_rotate_head_f64(_ptr(x), _ptr(y), x.size, r, theta, int(delta))
+    else:
+        dv = _delta_vec(delta)
+        q = _rope(pairing, sections)
+        lib().orc_rotate_head_spec_f64(_ptr(x), _ptr(y), x.size, r, theta, _ptr(dv), C.byref(q))
     return y
 
 
-def row_f64(x, heads: int, dim: int, r: int, theta: float, delta: int,
-            u=None, V=None) -> np.ndarray:
+def row_f64(x, heads: int, dim: int, r: int, theta: float, delta,
+            u=None, V=None, pairing: int = NEOX, sections=()) -> np.ndarray:
     """One token row (heads*dim values) in fp64: rotation, then the patch row."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     assert x.size == heads * dim
@@ -149,25 +196,30 @@ def row_f64(x, heads: int, dim: int, r: int, theta: float, delta: int,
     vv = None if V is None else np.ascontiguousarray(V, dtype=np.float64)
     if m:
         assert vv.shape == (heads * dim, m)
-    lib().orc_row_f64(_ptr(x), _ptr(y), heads, dim, r, theta, int(delta), m, _ptr(uu), _ptr(vv))
+    dv = _delta_vec(delta)
+    q = _rope(pairing, sections)
+    lib().orc_row_spec_f64(_ptr(x), _ptr(y), heads, dim, r, theta, _ptr(dv), C.byref(q), m,
+                           _ptr(uu), _ptr(vv))
     return y
 
 
-def row_magnitude_f64(x, heads: int, dim: int, r: int, theta: float, delta: int,
-                      u=None, V=None) -> np.ndarray:
+def row_magnitude_f64(x, heads: int, dim: int, r: int, theta: float, delta,
+                      u=None, V=None, pairing: int = NEOX, sections=()) -> np.ndarray:
     """Per element, the sum of |terms| that make the fp64 row value."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     s = np.empty_like(x)
     m = 0 if u is None else int(np.asarray(u).size)
     uu = None if u is None else np.ascontiguousarray(u, dtype=np.float64)
     vv = None if V is None else np.ascontiguousarray(V, dtype=np.float64)
-    lib().orc_row_magnitude_f64(_ptr(x), _ptr(s), heads, dim, r, theta, int(delta), m,
-                                _ptr(uu), _ptr(vv))
+    dv = _delta_vec(delta)
+    q = _rope(pairing, sections)
+    lib().orc_row_magnitude_spec_f64(_ptr(x), _ptr(s), heads, dim, r, theta, _ptr(dv),
+                                     C.byref(q), m, _ptr(uu), _ptr(vv))
     return s
 
 
-def row(x, heads: int, dim: int, r: int, theta: float, delta: int,
-        u=None, V=None) -> np.ndarray:
+def row(x, heads: int, dim: int, r: int, theta: float, delta,
+        u=None, V=None, pairing: int = NEOX, sections=()) -> np.ndarray:
     """One token row in storage format (uint16 bf16 bits or float32)."""
     x = np.ascontiguousarray(x)
     code = _dtype_code(x)
@@ -175,8 +227,10 @@ def row(x, heads: int, dim: int, r: int, theta: float, delta: int,
     m = 0 if u is None else int(np.asarray(u).size)
     uu = None if u is None else np.ascontiguousarray(u, dtype=x.dtype)
     vv = None if V is None else np.ascontiguousarray(V, dtype=x.dtype)
-    rc = lib().orc_row(code, _ptr(x), _ptr(out), heads, dim, r, theta, int(delta), m,
-                       _ptr(uu), _ptr(vv))
+    dv = _delta_vec(delta)
+    q = _rope(pairing, sections)
+    rc = lib().orc_row_spec(code, _ptr(x), _ptr(out), heads, dim, r, theta, _ptr(dv),
+                            C.byref(q), m, _ptr(uu), _ptr(vv))
     if rc != 0:
         raise ValueError("oracle rejected the row arguments")
     return out
@@ -193,10 +247,16 @@ def row_offset(ch: dict, page_size: int, block_table, layer: int, t: int, h: int
 
 
 def _problem(channels, *, num_layers, theta, offsets, delta, rank, page_size, block_table,
-             shape_from=None):
-    """Fills an orc_problem from channel dicts; returns (problem, arrays to keep alive)."""
+             shape_from=None, pairing=NEOX, sections=()):
+    """Fills an orc_problem from channel dicts; returns (problem, arrays to keep alive).
+    `delta` is [chunks] or, with M-RoPE sections, [chunks][sections]."""
     offsets = np.ascontiguousarray(offsets, dtype=np.int64)
     delta = np.ascontiguousarray(delta, dtype=np.int64)
+    nsec = len(sections) if len(sections) > 1 else 1
+    if delta.ndim == 2:
+        assert delta.shape[1] == nsec
+    else:
+        assert nsec == 1
     bt = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
     p = _Problem()
     keep = [offsets, delta, bt]
@@ -232,8 +292,9 @@ def _problem(channels, *, num_layers, theta, offsets, delta, rank, page_size, bl
     p.total_tokens = int(offsets[-1]) if offsets.size else 0
     p.offsets = _ptr(offsets)
     p.delta = _ptr(delta)
-    p.num_chunks = int(delta.size)
+    p.num_chunks = int(delta.shape[0]) if delta.ndim else 1
     p.rank = rank
+    p.rope = _rope(pairing, sections)
     return p, keep
 
 
@@ -251,7 +312,7 @@ def _out_arrays(channels, y_out, s_out):
 
 def relocate_patch(channels, *, num_layers: int, theta: float, offsets, delta,
                    rank: int = 0, page_size: int = 0, block_table=None,
-                   y_out=None, s_out=None) -> None:
+                   y_out=None, s_out=None, pairing: int = NEOX, sections=()) -> None:
     """The reuse operator over host arrays, in place.
 
     ``channels`` is a list of one or two dicts with keys ``data`` (a flat numpy
@@ -264,9 +325,13 @@ def relocate_patch(channels, *, num_layers: int, theta: float, offsets, delta,
     ``y_out`` / ``s_out``: optional lists (one per channel) of float64 buffers shaped
     like that channel's ``data``; every element the call computes receives its
     unrounded fp64 value / its sum of term magnitudes, at the same element offset.
+
+    ``pairing`` (NEOX or INTERLEAVED) and ``sections`` (M-RoPE pairs per section;
+    then ``delta`` is [chunks][sections]) select the positional variant.
     """
     p, keep = _problem(channels, num_layers=num_layers, theta=theta, offsets=offsets,
-                       delta=delta, rank=rank, page_size=page_size, block_table=block_table)
+                       delta=delta, rank=rank, page_size=page_size, block_table=block_table,
+                       pairing=pairing, sections=sections)
     if y_out is not None:
         ys, ss = _out_arrays(channels, y_out, s_out)
         rc = lib().orc_relocate_patch_ex(C.byref(p), ys, ss)
@@ -279,7 +344,8 @@ def relocate_patch(channels, *, num_layers: int, theta: float, offsets, delta,
 
 def recall_patch(src_channels, dst_channels, *, num_layers: int, theta: float, offsets, delta,
                  rank: int = 0, src_page_size: int = 0, src_block_table=None,
-                 dst_page_size: int = 0, dst_block_table=None, y_out=None, s_out=None) -> None:
+                 dst_page_size: int = 0, dst_block_table=None, y_out=None, s_out=None,
+                 pairing: int = NEOX, sections=()) -> None:
     """Recall (out of place): rows read through ``src_channels`` (dicts as in
     ``relocate_patch``, with the factors), whole result rows written through
     ``dst_channels`` (dicts with ``data``, ``offset`` and the four strides; heads,
@@ -287,7 +353,7 @@ def recall_patch(src_channels, dst_channels, *, num_layers: int, theta: float, o
     the destination buffers."""
     sp, keep = _problem(src_channels, num_layers=num_layers, theta=theta, offsets=offsets,
                         delta=delta, rank=rank, page_size=src_page_size,
-                        block_table=src_block_table)
+                        block_table=src_block_table, pairing=pairing, sections=sections)
     dp, keep2 = _problem(dst_channels, num_layers=num_layers, theta=theta, offsets=offsets,
                          delta=delta, rank=rank, page_size=dst_page_size,
                          block_table=dst_block_table, shape_from=src_channels)
