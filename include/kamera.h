@@ -20,9 +20,15 @@
  *     survival (same page, §3, "Sobrevivencia de Janela Deslizante").
  *
  * Readings fixed by this library where the pages print no formula:
- *   - NeoX half-split pairing: in a head whose first rope_dim dims rotate, dim i
- *     pairs with dim i + rope_dim/2; pair i turns by angle delta * theta^(-2i/rope_dim);
- *     (a, b) -> (a cos - b sin, b cos + a sin).  Dims >= rope_dim do not rotate.
+ *   - NeoX half-split pairing: in a head whose first rope_dim dims rotate, rotary
+ *     pair i (i < rope_dim/2) is dims (i, i + rope_dim/2); it turns by angle
+ *     delta * theta^(-2i/rope_dim); (a, b) -> (a cos - b sin, b cos + a sin).  Dims >=
+ *     rope_dim do not rotate.  KAMERA_INTERLEAVED pairs dims (2i, 2i + 1) instead.
+ *   - M-RoPE ("Modelos Tomam Notas no Prefill", gist.science/pt/paper/2606.17107, §4:
+ *     image KV is transplanted with M-RoPE re-rotation): positions are vectors of up
+ *     to 4 components; the rotary pairs are cut, in pair order, into that many
+ *     sections, and pair i of section s turns by delta[s] * theta^(-2i/rope_dim).  A
+ *     pair whose section delta is 0 does not move.
  *   - The patch is added after the rotation; it is not rotated.
  *   - delta == 0 means R = identity exactly.
  *   - Each output element is rounded once to the storage type (round to nearest even).
@@ -61,7 +67,7 @@ extern "C" {
 #define KAMERA_API __attribute__((visibility("default")))
 #endif
 
-#define KAMERA_ABI_VERSION 1
+#define KAMERA_ABI_VERSION 2
 #define KAMERA_MAX_RANK 256   /* largest patch rank m accepted */
 
 typedef enum {
@@ -78,8 +84,11 @@ typedef enum {
 typedef enum { KAMERA_BF16 = 0, KAMERA_F32 = 1 } kamera_dtype;
 
 typedef enum {
-  KAMERA_NEOX_HALF = 0 /* dim i pairs with dim i + rope_dim/2 */
+  KAMERA_NEOX_HALF = 0,   /* rotary pair i is dims (i, i + rope_dim/2) */
+  KAMERA_INTERLEAVED = 1  /* rotary pair i is dims (2i, 2i + 1) */
 } kamera_pairing;
+
+#define KAMERA_MAX_SECTIONS 4  /* M-RoPE position components */
 
 /* flags of kamera_kv_desc */
 #define KAMERA_FLAG_GENERIC 1u /* run the plain per-row kernel instead of the tuned ones */
@@ -116,6 +125,11 @@ typedef struct {
   const int32_t* block_table; /* device [ceil(total_tokens / page_size)] when paged, else ignored.
                                  Precondition: entries pairwise distinct.  Tokens whose entry
                                  lies outside [0, num_pages) are left untouched. */
+  int32_t num_sections;  /* 0 or 1: one delta per chunk; 2..KAMERA_MAX_SECTIONS: M-RoPE */
+  int32_t section_pairs[KAMERA_MAX_SECTIONS]; /* M-RoPE: rotary pairs per section, in pair
+                                 order, each >= 0, summing to rope_dim/2 of every channel
+                                 with rope_dim > 0; entries past num_sections are ignored */
+  int32_t reserved1;     /* must be 0 */
 } kamera_kv_desc;
 
 /* The chunks being moved.  Chunk j owns logical tokens [token_offsets[j], token_offsets[j+1]). */
@@ -124,7 +138,9 @@ typedef struct {
   int32_t reserved0;       /* must be 0 */
   int64_t total_tokens;    /* host copy of token_offsets[num_chunks]; sizes the launch */
   const int64_t* token_offsets; /* device [num_chunks + 1]; precondition: 0 = o_0 <= o_1 <= ... = total_tokens */
-  const int64_t* delta;    /* device [num_chunks]; new position - old position; precondition |delta| < 2^53 */
+  const int64_t* delta;    /* device [num_chunks][S], S = max(1, kv.num_sections): new position -
+                              old position, one value per M-RoPE section; precondition
+                              |delta| < 2^53 */
 } kamera_chunks;
 
 /* The rank-m patch, one factor pair per channel, in the KV dtype, dense row-major:
@@ -139,9 +155,10 @@ typedef struct {
 } kamera_patch;
 
 /* Rotation only (m = 0).  Rotates dims [0, rope_dim) of every head of every channel
- * with rope_dim > 0, for every chunk with delta != 0.  Nothing else is read or
- * written: channels with rope_dim == 0 (V, c_KV), dims >= rope_dim and chunks with
- * delta == 0 keep their exact bits.  Kamera page §3, sliding-window survival. */
+ * with rope_dim > 0, for every chunk with delta != 0.  Nothing else is written:
+ * channels with rope_dim == 0 (V, c_KV), dims >= rope_dim, chunks with delta == 0 and
+ * (M-RoPE) the pairs of sections whose delta is 0 keep their exact bits.  Kamera page
+ * §3, sliding-window survival. */
 KAMERA_API kamera_status kamera_relocate(const kamera_kv_desc* kv, const kamera_chunks* chunks,
                               hipStream_t stream);
 
@@ -164,10 +181,11 @@ KAMERA_API kamera_status kamera_relocate_patch(const kamera_kv_desc* kv, const k
  *   src: the canonical store (contiguous or paged); read only.  It is checked as the
  *        kv argument of kamera_relocate_patch is (factors overlapping it are rejected
  *        too).
- *   dst: the cache being filled.  dtype, num_layers, num_channels, pairing and each
- *        channel's heads, dim and rope_dim must equal src's; data, strides,
- *        page_size, num_pages and block_table are its own (destination tokens whose
- *        page id lies outside [0, num_pages) are skipped).  rope_theta is not read.
+ *   dst: the cache being filled.  dtype, num_layers, num_channels and each channel's
+ *        heads, dim and rope_dim must equal src's; data, strides, page_size,
+ *        num_pages and block_table are its own (destination tokens whose page id lies
+ *        outside [0, num_pages) are skipped).  Its rope_theta, pairing and sections
+ *        are not read: the source's apply.
  *        Its memory must not overlap the source or the factors (KAMERA_E_ALIAS).
  *   patch == NULL or rank 0: rotation and copy only.
  * chunks, stream and errors as for kamera_relocate_patch. */

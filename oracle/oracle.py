@@ -356,7 +356,8 @@ def recall_patch(src_channels, dst_channels, *, num_layers: int, theta: float, o
                         block_table=src_block_table, pairing=pairing, sections=sections)
     dp, keep2 = _problem(dst_channels, num_layers=num_layers, theta=theta, offsets=offsets,
                          delta=delta, rank=rank, page_size=dst_page_size,
-                         block_table=dst_block_table, shape_from=src_channels)
+                         block_table=dst_block_table, shape_from=src_channels,
+                         pairing=pairing, sections=sections)
     ys = ss = None
     if y_out is not None:
         ys, ss = _out_arrays(dst_channels, y_out, s_out)

@@ -146,9 +146,13 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
   if (!ch) return fail(KAMERA_E_NULL, "chunks descriptor is NULL");
   if (kv->dtype != KAMERA_BF16 && kv->dtype != KAMERA_F32)
     return fail(KAMERA_E_UNSUPPORTED, "dtype %d is not bf16 (0) or fp32 (1)", kv->dtype);
-  if (kv->pairing != KAMERA_NEOX_HALF)
-    return fail(KAMERA_E_UNSUPPORTED, "pairing %d: only NeoX half-split (0) is implemented",
+  if (kv->pairing != KAMERA_NEOX_HALF && kv->pairing != KAMERA_INTERLEAVED)
+    return fail(KAMERA_E_UNSUPPORTED, "pairing %d is not NeoX half-split (0) or interleaved (1)",
                 kv->pairing);
+  if (kv->num_sections < 0 || kv->num_sections > KAMERA_MAX_SECTIONS)
+    return fail(KAMERA_E_SHAPE, "num_sections %d outside [0, %d]", kv->num_sections,
+                KAMERA_MAX_SECTIONS);
+  if (kv->reserved1 != 0) return fail(KAMERA_E_SHAPE, "kv.reserved1 must be 0");
   if (kv->flags & ~KAMERA_FLAG_GENERIC) return fail(KAMERA_E_SHAPE, "unknown flags 0x%x", kv->flags);
   if (kv->num_layers < 0) return fail(KAMERA_E_SHAPE, "num_layers %d < 0", kv->num_layers);
   if (kv->num_channels < 1 || kv->num_channels > 2)
@@ -185,6 +189,18 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
   }
   if (any_rope && !(std::isfinite(kv->rope_theta) && kv->rope_theta > 0))
     return fail(KAMERA_E_SHAPE, "rope_theta must be finite and > 0");
+  if (kv->num_sections > 1) {
+    int sum = 0;
+    for (int s = 0; s < kv->num_sections; ++s) {
+      if (kv->section_pairs[s] < 0)
+        return fail(KAMERA_E_SHAPE, "section_pairs[%d] = %d < 0", s, kv->section_pairs[s]);
+      sum += kv->section_pairs[s];
+    }
+    for (int c = 0; c < kv->num_channels; ++c)
+      if (kv->ch[c].rope_dim > 0 && sum != kv->ch[c].rope_dim / 2)
+        return fail(KAMERA_E_SHAPE, "sections hold %d pairs but channel %d rotates %d", sum, c,
+                    kv->ch[c].rope_dim / 2);
+  }
   if (kv->page_size < 0) return fail(KAMERA_E_SHAPE, "page_size %d < 0", kv->page_size);
   if (kv->page_size > 0) {
     if (kv->num_pages < 1) return fail(KAMERA_E_SHAPE, "paged layout with num_pages < 1");
@@ -235,8 +251,11 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
       plan->launches++;
       if (plan->kernel[c] == K_ROTATE) {
         // A workgroup covers 4 waves x `unroll` row groups of 64 / (rope_dim / 8) rows.
-        int unroll = env_int("KAMERA_ROTATE_UNROLL", 4);
-        if (unroll != 1 && unroll != 2 && unroll != 4) unroll = 4;
+        // Interleaved rows keep more values live per row group: two groups fit the
+        // register budget of four waves per SIMD, four would spill.
+        const int udflt = kv->pairing == KAMERA_INTERLEAVED ? 2 : 4;
+        int unroll = env_int("KAMERA_ROTATE_UNROLL", udflt);
+        if (unroll != 1 && unroll != 2 && unroll != 4) unroll = udflt;
         const int rows = 4 * unroll * (64 / (k.rope_dim / 8));
         const int bt = (int)std::min<int64_t>(kamera::kMaxBlockTokens,
                                               std::max<int64_t>(1, rows / k.heads));
@@ -276,6 +295,13 @@ kamera::CommonArgs common_args(const kamera_kv_desc& kv, const kamera_chunks& ch
   for (int sh = 0; sh < 31; ++sh)
     if (kv.page_size == (1 << sh)) a.page_shift = sh;
   a.out_page_shift = -1;
+  a.pairing = kv.pairing;
+  a.num_sections = kv.num_sections > 1 ? kv.num_sections : 1;
+  int end = 0;
+  for (int s = 0; s < 4; ++s) {
+    end += s < kv.num_sections ? kv.section_pairs[s] : 0;
+    a.sec_end[s] = kv.num_sections > 1 ? end : (1 << 30);
+  }
   return a;
 }
 
@@ -377,8 +403,7 @@ kamera_status validate_recall(const kamera_kv_desc* src, const kamera_kv_desc* d
                 src->dtype);
   if (dst->num_layers != src->num_layers || dst->num_channels != src->num_channels)
     return fail(KAMERA_E_SHAPE, "destination layers/channels differ from the source");
-  if (dst->pairing != src->pairing)
-    return fail(KAMERA_E_SHAPE, "destination pairing differs from the source");
+  if (dst->reserved1 != 0) return fail(KAMERA_E_SHAPE, "destination reserved1 must be 0");
   if (dst->flags & ~KAMERA_FLAG_GENERIC)
     return fail(KAMERA_E_SHAPE, "unknown destination flags 0x%x", dst->flags);
   const int64_t es = src->dtype == KAMERA_BF16 ? 2 : 4;

@@ -42,6 +42,12 @@ struct CommonArgs {
   int32_t block_tokens;     // tokens one workgroup covers (tuned kernels)
   int32_t page_shift;       // log2(page_size) when it is a power of two, else -1
   int32_t tail_mode;        // rotate+patch tail launch: 1 by boundary, 2 by token group
+  // Positional variant: pairing 0 = NeoX half-split (i, i + r/2), 1 = interleaved
+  // (2i, 2i + 1); delta holds num_sections values per chunk (M-RoPE when > 1), and
+  // rotary pair i belongs to the first section s with i < sec_end[s].
+  int32_t pairing;
+  int32_t num_sections;
+  int32_t sec_end[4];
   // Destination paging (out of place only).
   const int32_t* out_block_table;
   int64_t out_num_pages;

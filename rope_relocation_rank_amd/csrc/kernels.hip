@@ -108,6 +108,14 @@ __device__ __forceinline__ u32x4_t lane_xor4(const u32x4_t& v) {
   return r;
 }
 
+// Word of results `y` with the halves flagged in `keep_lo` / `keep_hi` taken bit for
+// bit from `x` (pairs whose section delta is 0 do not move).
+__device__ __forceinline__ uint32_t keep_halves(uint32_t y, uint32_t x, bool keep_lo,
+                                                bool keep_hi) {
+  const uint32_t m = (keep_lo ? 0x0000ffffu : 0u) | (keep_hi ? 0xffff0000u : 0u);
+  return (y & ~m) | (x & m);
+}
+
 // ------------------------------------------------------------------ index helpers
 
 // Chunk that owns token t: the last j with offsets[j] <= t (offsets[0] == 0 <= t), with
@@ -121,14 +129,28 @@ struct ChunkRef {
   int64_t delta;
 };
 
-__device__ __forceinline__ ChunkRef find_chunk_wave(const int64_t* off, const int64_t* delta,
-                                                    int n, int64_t t, int from = 0) {
+// Whether chunk k moves at all: its delta, or any of its section deltas, is nonzero.
+__device__ __forceinline__ int64_t chunk_moves(const CommonArgs& cm, int k) {
+  if (cm.num_sections <= 1) return cm.delta[k];
+  int64_t any = 0;
+  for (int s = 0; s < cm.num_sections; ++s) any |= cm.delta[(int64_t)k * cm.num_sections + s];
+  return any;
+}
+
+// The chunk holding token t, searched from chunk `from` on, by the whole wave: lane k
+// reads the end and the motion of chunk base + k, a ballot counts the chunks that end
+// at or before t.  ChunkRef::delta is nonzero iff the chunk moves (with sections it is
+// not itself a delta: pair_delta gives those).
+__device__ __forceinline__ ChunkRef find_chunk_wave(const CommonArgs& cm, int64_t t,
+                                                    int from = 0) {
   const int lane = threadIdx.x & 63;
+  const int n = cm.num_chunks;
+  const int64_t* off = cm.offsets;
   ChunkRef c{from, 0, 0};
   for (int base = from; base < n; base += 64) {
     const int k = base + lane;
     const int64_t e = k < n ? off[k + 1] : INT64_MAX;
-    const int64_t d = k < n ? delta[k] : 0;
+    const int64_t d = k < n ? chunk_moves(cm, k) : 0;
     const unsigned long long le = __ballot(e <= t);  // chunks that end at or before t
     const int cnt = __popcll(le);
     if (cnt < 64 || base + 64 >= n) {
@@ -139,12 +161,26 @@ __device__ __forceinline__ ChunkRef find_chunk_wave(const int64_t* off, const in
       if (base + src >= n) {  // past the last chunk: clamp to it
         c.j = n - 1;
         c.end = off[n];
-        c.delta = delta[n - 1];
+        c.delta = chunk_moves(cm, n - 1);
       }
       break;
     }
   }
   return c;
+}
+
+// Section of rotary pair i (0 without M-RoPE).
+__device__ __forceinline__ int section_of(const CommonArgs& cm, int i) {
+  int s = 0;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) s += (k + 1 < cm.num_sections && i >= cm.sec_end[k]) ? 1 : 0;
+  return s;
+}
+
+// Delta that turns rotary pair i of chunk c.
+__device__ __forceinline__ int64_t pair_delta(const CommonArgs& cm, const ChunkRef& c, int i) {
+  if (cm.num_sections <= 1) return c.delta;
+  return cm.delta[(int64_t)c.j * cm.num_sections + section_of(cm, i)];
 }
 
 // Chunk of token t for a single thread (generic kernel).
@@ -264,20 +300,22 @@ __device__ __forceinline__ int32_t slot32(int page_size, int page_shift, const i
 }
 
 // Workgroup = `block_tokens` tokens of one layer, every head, taken as rows (token,
-// head) in order.  LPR lanes cover the rotated part of a row (8 dims each); a lane's
-// NeoX partner dims sit LPR/2 lanes away and arrive by a lane exchange; one wave
-// instruction covers 64/LPR consecutive rows.  Wave w takes row groups w, w + 4, ...
-// (UNR of them per pass) and issues all their loads first.  Each wavefront then works
-// on its own: it finds the chunks its rows belong to, forms that chunk's phases (one
-// pair frequency per lane, gathered by lane shuffles) and finishes the rows.  Only a
-// paged cache needs a workgroup barrier, once, for the staged block table.  Dims
-// >= rope_dim are never touched; rows of chunks with delta == 0 are not written.
-template <int LPR, int UNR, bool PAGED>
+// head) in order.  LPR lanes cover the rotated part of a row (8 dims each); one wave
+// instruction covers 64/LPR consecutive rows.  NeoX partner dims sit LPR/2 lanes away
+// and arrive by a lane exchange; interleaved (IL) partners are the other half of the
+// same 32-bit word.  Wave w takes row groups w, w + 4, ... (UNR of them per pass) and
+// issues all their loads first.  Each wavefront then works on its own: it finds the
+// chunks its rows belong to, forms that chunk's phases (one rotary pair per lane,
+// gathered by lane shuffles) and finishes the rows.  Only a paged cache needs a
+// workgroup barrier, once, for the staged block table.  Dims >= rope_dim are never
+// touched; rows of chunks that do not move are not written; with M-RoPE sections, the
+// dims of pairs whose section delta is 0 keep their bits.
+template <int LPR, int UNR, bool PAGED, bool IL>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(UNR == 4 ? 4 : 1)))
 void rotate_rows(ChanArgs ch, CommonArgs cm) {
   constexpr int RPI = 64 / LPR;
   constexpr int HX = LPR / 2;
-  constexpr int HALF = 8 * HX;
+  constexpr int HALF = 4 * LPR;  // rotary pairs of a head: rope_dim / 2
   constexpr int ROWS = kWavesPerBlock * UNR * RPI;  // rows one pass of the block covers
   __shared__ int sbt[kMaxBlockTokens + 1];
   const int lane = threadIdx.x & 63;
@@ -288,8 +326,10 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
   const int64_t t1 = min(tb0 + (int64_t)cm.block_tokens, cm.total_tokens);
   const int q = lane % LPR;
   const int rr = lane / LPR;
-  const int fi0 = (q % HX) * 8;
+  // Rotary pair of each of the lane's 8 dims, and the sign of its partner term.
+  const int fi0 = IL ? 4 * q : (q % HX) * 8;
   const float sgn = q < HX ? -1.f : 1.f;
+  const bool mixed = cm.num_sections > 1;
   const int H = ch.heads;
   const int nrows = (int)(t1 - tb0) * H;
   uint16_t* base = (uint16_t*)ch.data + layer * ch.layer_stride + 8 * q;
@@ -331,32 +371,44 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
     const int r_last = min(nrows - 1, rbase + (wave + kWavesPerBlock * (UNR - 1)) * RPI + RPI - 1);
     int64_t t0 = tb0 + r_first / H;
     const int64_t tw1 = tb0 + r_last / H + 1;
-    ChunkRef c = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0);
+    ChunkRef c = find_chunk_wave(cm, t0);
     while (true) {
       const int64_t s1 = min(tw1, c.end);
       if (s1 > t0 && c.delta != 0) {
         float2 own = make_float2(1.f, 0.f);
-        if (lane < HALF) own = phase_of(ch.omega[lane], c.delta);
+        if (lane < HALF) own = phase_of(ch.omega[lane], pair_delta(cm, c, lane));
         float cs[8], sn[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          cs[e] = __shfl(own.x, fi0 + e);
-          sn[e] = sgn * __shfl(own.y, fi0 + e);
+          const int pi = IL ? fi0 + (e >> 1) : fi0 + e;
+          cs[e] = __shfl(own.x, pi);
+          sn[e] = (IL ? ((e & 1) ? 1.f : -1.f) : sgn) * __shfl(own.y, pi);
         }
 #pragma unroll
         for (int k = 0; k < UNR; ++k) {
-          const u32x4_t pv = lane_xor4<HX>(xv[k]);
           float a[8], b[8], y[8];
           unpack8(xv[k], a);
-          unpack8(pv, b);
+          if constexpr (IL) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[e] = a[e ^ 1];
+          } else {
+            unpack8(lane_xor4<HX>(xv[k]), b);
+          }
 #pragma unroll
           for (int e = 0; e < 8; ++e) y[e] = fmaf(a[e], cs[e], b[e] * sn[e]);
-          if (ok[k] && tok[k] >= t0 && tok[k] < s1) store_nt(ptr[k], pack8(y));
+          u32x4_t o = pack8(y);
+          if (mixed) {
+            o.x = keep_halves(o.x, xv[k].x, sn[0] == 0.f, sn[1] == 0.f);
+            o.y = keep_halves(o.y, xv[k].y, sn[2] == 0.f, sn[3] == 0.f);
+            o.z = keep_halves(o.z, xv[k].z, sn[4] == 0.f, sn[5] == 0.f);
+            o.w = keep_halves(o.w, xv[k].w, sn[6] == 0.f, sn[7] == 0.f);
+          }
+          if (ok[k] && tok[k] >= t0 && tok[k] < s1) store_nt(ptr[k], o);
         }
       }
       t0 = max(t0, s1);
       if (t0 >= tw1 || c.j + 1 >= cm.num_chunks) break;
-      c = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0, c.j + 1);
+      c = find_chunk_wave(cm, t0, c.j + 1);
     }
   }
 }
@@ -390,9 +442,10 @@ struct PatchCtx {
   int64_t tb0, t1;
   int p0, op0, m;
   int lane, wave, c16, g;
-  int fi0;
+  int fi0;              // rotary pair of the lane's first dim (NeoX), or its first dim (IL)
   float sgn;
   bool lane_on, rot_lane;
+  bool mixed;           // M-RoPE sections: some pairs may not turn
 };
 
 // KV, row offsets and U fragments of the TU tiles a wave loads together.
@@ -447,8 +500,9 @@ __device__ __forceinline__ void load_tiles(const PatchCtx& c, const CommonArgs& 
   }
 }
 
-// Rotates, patches and stores loaded tiles.  HX is the partner lane distance (0: no
-// rotation).  Lane l holds features fb + 8c + n (c = l & 15, n < 8) of tokens
+// Rotates, patches and stores loaded tiles.  HX is the NeoX partner lane distance, -1
+// for interleaved pairs (partner in the other half of the same word), 0 for no
+// rotation.  Lane l holds features fb + 8c + n (c = l & 15, n < 8) of tokens
 // 4g .. 4g + 3 (g = l >> 4).
 //
 // Patch on MFMA 16x16x32 bf16: D[t][col] = C[t][col] + sum_k A[t][k] B[k][col] with
@@ -457,45 +511,56 @@ __device__ __forceinline__ void load_tiles(const PatchCtx& c, const CommonArgs& 
 // feature n of its 4 tokens: the rotated values are the C operand and the result is
 // already where it is stored.  Output tiles go two at a time (features 2p, 2p + 1 form
 // one packed bf16 pair), so only 8 accumulators are live.
+//
+// Phases sit in LDS as (cos, sin) per rotary pair.  With M-RoPE sections a pair whose
+// section delta is 0 has sin exactly 0 and is not rotated.
 template <int MK, int HX, int TU, int OUT>
 __device__ __forceinline__ void finish_tiles(const PatchCtx& c, const u32x4_t* sV,
                                              const float4* sph2, const TileSet<MK, TU>& T) {
+  const float2* sph = reinterpret_cast<const float2*>(sph2);
 #pragma unroll
   for (int u = 0; u < TU; ++u) {
     u32x4_t out[4];
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {  // features 2pp, 2pp + 1 of the lane's 8
+      // (cos, sin) of the pairs of the two features, and whether each one turns.
       float4 ph = make_float4(1.f, 0.f, 1.f, 0.f);
       if constexpr (HX > 0) ph = sph2[(c.fi0 >> 1) + pp];
+      if constexpr (HX < 0) {
+        const float2 q = sph[(c.fi0 >> 1) + pp];
+        ph = make_float4(q.x, q.y, q.x, q.y);
+      }
+      const bool turn0 = HX != 0 && c.rot_lane && !(c.mixed && ph.y == 0.f);
+      const bool turn1 = HX != 0 && c.rot_lane && !(c.mixed && ph.w == 0.f);
+      float r0[4], r1[4];  // rotated (or unrotated) values of the two features
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = T.x[u][i][pp];
+        const float a0 = bf16_lo(w), a1 = bf16_hi(w);
+        float y0 = a0, y1 = a1;
+        if constexpr (HX > 0) {
+          const uint32_t pw = lane_xor<HX>(w);
+          y0 = fmaf(a0, ph.x, bf16_lo(pw) * (c.sgn * ph.y));
+          y1 = fmaf(a1, ph.z, bf16_hi(pw) * (c.sgn * ph.w));
+        } else if constexpr (HX < 0) {
+          y0 = fmaf(a0, ph.x, -(a1 * ph.y));
+          y1 = fmaf(a1, ph.x, a0 * ph.y);
+        }
+        r0[i] = turn0 ? y0 : a0;
+        r1[i] = turn1 ? y1 : a1;
+      }
       if constexpr (MK == 0) {
         // No patch (out of place only): rotated dims are rounded once, every other
         // element is copied bit for bit.
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = T.x[u][i][pp];
-          out[i][pp] = w;
-          if constexpr (HX > 0) {
-            const uint32_t pw = lane_xor<HX>(w);
-            const float y0 = fmaf(bf16_lo(w), ph.x, bf16_lo(pw) * (c.sgn * ph.y));
-            const float y1 = fmaf(bf16_hi(w), ph.z, bf16_hi(pw) * (c.sgn * ph.w));
-            if (c.rot_lane) out[i][pp] = pack2(y0, y1);
-          }
-        }
+        for (int i = 0; i < 4; ++i)
+          out[i][pp] = keep_halves(pack2(r0[i], r1[i]), T.x[u][i][pp], !turn0, !turn1);
       } else {
         f32x4_t acc0, acc1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t w = T.x[u][i][pp];
-          float a0 = bf16_lo(w), a1 = bf16_hi(w);
-          if constexpr (HX > 0) {
-            const uint32_t pw = lane_xor<HX>(w);
-            const float y0 = fmaf(a0, ph.x, bf16_lo(pw) * (c.sgn * ph.y));
-            const float y1 = fmaf(a1, ph.z, bf16_hi(pw) * (c.sgn * ph.w));
-            a0 = c.rot_lane ? y0 : a0;
-            a1 = c.rot_lane ? y1 : a1;
-          }
-          acc0[i] = a0;
-          acc1[i] = a1;
+          acc0[i] = r0[i];
+          acc1[i] = r1[i];
         }
 #pragma unroll
         for (int ks = 0; ks < MK; ++ks) {
@@ -607,9 +672,11 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
   const int h = f0 / D;
   const int d0 = f0 - h * D;
   c.rot_lane = c.lane_on && d0 < r;
-  c.fi0 = d0 < (r >> 1) ? d0 : d0 - (r >> 1);
+  const bool il = cm.pairing == 1;
+  c.fi0 = il ? d0 : (d0 < (r >> 1) ? d0 : d0 - (r >> 1));
   c.sgn = d0 < (r >> 1) ? -1.f : 1.f;
-  const int hx = r >> 4;  // partner lane distance: half / 8
+  c.mixed = cm.num_sections > 1;
+  const int hx = il ? -1 : r >> 4;  // NeoX partner lane distance half / 8; -1 interleaved
 
   c.slot_stride = (int32_t)KAMERA_CH(slot_stride);
   c.page_stride = (int32_t)KAMERA_CH(page_stride);
@@ -643,7 +710,7 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
     } else {
       c.tb0 = tg * cm.block_tokens;
       c.t1 = min(c.tb0 + (int64_t)cm.block_tokens, cm.total_tokens);
-      const ChunkRef first = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, c.tb0);
+      const ChunkRef first = find_chunk_wave(cm, c.tb0);
       if (first.end <= c.tb0 || first.end >= c.t1) return;  // no boundary inside
       start = first.end;
       from = first.j + 1;
@@ -678,7 +745,8 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
     }
     // One pair frequency per thread; (cos, sin) of pairs 2p and 2p + 1 are adjacent.
     if (rotate && threadIdx.x < (r >> 1))
-      reinterpret_cast<float2*>(sph2)[threadIdx.x] = phase_of(KAMERA_CH(omega[threadIdx.x]), ck.delta);
+      reinterpret_cast<float2*>(sph2)[threadIdx.x] =
+          phase_of(KAMERA_CH(omega[threadIdx.x]), pair_delta(cm, ck, threadIdx.x));
   };
 #define KAMERA_PATCH_SWITCH(PRE, USE)                                                           \
   switch (rotate ? hx : 0) {                                                                    \
@@ -686,6 +754,7 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
     case 2: patch_tiles<MK, M8, PAGED, 2, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
     case 4: patch_tiles<MK, M8, PAGED, 4, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
     case 8: patch_tiles<MK, M8, PAGED, 8, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
+    case -1: patch_tiles<MK, M8, PAGED, -1, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;     \
     default: patch_tiles<MK, M8, PAGED, 0, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;      \
   }
 
@@ -696,7 +765,7 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
     // overlaps the chunk lookup, the LDS staging and the barrier.
     TileSet<MK, TU> pre;
     load_tiles<MK, M8, PAGED, TU, OUT>(c, cm, c.wave, ntiles, c.tb0, c.t1, pre);
-    const ChunkRef ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, c.tb0);
+    const ChunkRef ck = find_chunk_wave(cm, c.tb0);
     const int64_t t0 = c.tb0, s1 = min(c.t1, ck.end);
     if (s1 <= t0) return;  // offsets that do not cover the group: nothing here
     // Tokens past the chunk's end belong to the tail kernel.
@@ -713,7 +782,7 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
     // The remaining chunks of the group, one after the other.
     TileSet<MK, TU> none;
     int64_t t0 = start;
-    ChunkRef ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0, from);
+    ChunkRef ck = find_chunk_wave(cm, t0, from);
     bool staged = false;
     while (true) {
       const int64_t s1 = min(c.t1, ck.end);
@@ -727,7 +796,7 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
       }
       t0 = max(t0, s1);
       if (t0 >= c.t1 || ck.j + 1 >= cm.num_chunks) break;
-      ck = find_chunk_wave(cm.offsets, cm.delta, cm.num_chunks, t0, ck.j + 1);
+      ck = find_chunk_wave(cm, t0, ck.j + 1);
     }
   }
 #undef KAMERA_PATCH_SWITCH
@@ -779,8 +848,8 @@ __global__ __launch_bounds__(kBlock) void generic_rows(ChanArgs ch, CommonArgs c
     const int64_t t = rest % Tt;
     const int64_t layer = rest / Tt;
     const int j = find_chunk(cm.offsets, cm.num_chunks, t);
-    const int64_t dj = cm.delta[j];
-    if (!OUT && m == 0 && (dj == 0 || r == 0)) continue;
+    const int64_t moves = chunk_moves(cm, j);
+    if (!OUT && m == 0 && (moves == 0 || r == 0)) continue;
     int64_t so, dso = 0;
     if (!slot_of(t, cm.page_size, cm.block_table, cm.num_pages, ch.page_stride, ch.slot_stride,
                  &so))
@@ -791,28 +860,40 @@ __global__ __launch_bounds__(kBlock) void generic_rows(ChanArgs ch, CommonArgs c
     const T* src = (const T*)ch.data + layer * ch.layer_stride + so + h * ch.head_stride;
     T* dst = OUT ? (T*)ch.out + layer * ch.out_layer_stride + dso + h * ch.out_head_stride
                  : (T*)src;
-    if (OUT && m == 0 && (dj == 0 || r == 0)) {
+    if (OUT && m == 0 && (moves == 0 || r == 0)) {
       for (int d = 0; d < D; ++d) copy_bits(dst + d, src + d);
       continue;
     }
     const T* u = (const T*)ch.U + (layer * Tt + t) * m;
     const T* vr = (const T*)ch.V + ((layer * cm.num_chunks + j) * F + h * D) * m;
     for (int i = 0; i < half; ++i) {
-      float a = load_f(src + i), b = load_f(src + i + half);
-      if (dj != 0) {
+      const int d0 = cm.pairing == 1 ? 2 * i : i;
+      const int d1 = cm.pairing == 1 ? 2 * i + 1 : i + half;
+      const int64_t di = cm.num_sections > 1
+                             ? cm.delta[(int64_t)j * cm.num_sections + section_of(cm, i)]
+                             : moves;
+      if (di == 0 && m == 0) {  // this pair does not move
+        if (OUT) {
+          copy_bits(dst + d0, src + d0);
+          copy_bits(dst + d1, src + d1);
+        }
+        continue;
+      }
+      float a = load_f(src + d0), b = load_f(src + d1);
+      if (di != 0) {
         float c, s;
-        phase_generic(cm.theta, r, i, dj, c, s);
+        phase_generic(cm.theta, r, i, di, c, s);
         const float an = fmaf(a, c, -(b * s));
         const float bn = fmaf(b, c, a * s);
         a = an;
         b = bn;
       }
       if (m > 0) {
-        a += dot_patch(u, vr + (int64_t)i * m, m);
-        b += dot_patch(u, vr + (int64_t)(i + half) * m, m);
+        a += dot_patch(u, vr + (int64_t)d0 * m, m);
+        b += dot_patch(u, vr + (int64_t)d1 * m, m);
       }
-      store_f(dst + i, a);
-      store_f(dst + i + half, b);
+      store_f(dst + d0, a);
+      store_f(dst + d1, b);
     }
     if (m > 0)
       for (int d = r; d < D; ++d) store_f(dst + d, load_f(src + d) + dot_patch(u, vr + (int64_t)d * m, m));
@@ -829,11 +910,17 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
                               hipStream_t s) {
   const int64_t blocks = (int64_t)cm.num_layers * cm.token_groups;
   const dim3 grid((unsigned)blocks);
-#define KAMERA_LAUNCH_ROT2(LPR, PG)                                                              \
-  do {                                                                                           \
-    if (unroll == 1) hipLaunchKernelGGL((rotate_rows<LPR, 1, PG>), grid, dim3(kBlock), 0, s, ch, cm); \
-    else if (unroll == 2) hipLaunchKernelGGL((rotate_rows<LPR, 2, PG>), grid, dim3(kBlock), 0, s, ch, cm); \
-    else hipLaunchKernelGGL((rotate_rows<LPR, 4, PG>), grid, dim3(kBlock), 0, s, ch, cm);       \
+  const bool il = cm.pairing == 1;
+#define KAMERA_LAUNCH_ROT3(LPR, PG, IL)                                                              \
+  do {                                                                                               \
+    if (unroll == 1) hipLaunchKernelGGL((rotate_rows<LPR, 1, PG, IL>), grid, dim3(kBlock), 0, s, ch, cm); \
+    else if (unroll == 2) hipLaunchKernelGGL((rotate_rows<LPR, 2, PG, IL>), grid, dim3(kBlock), 0, s, ch, cm); \
+    else hipLaunchKernelGGL((rotate_rows<LPR, 4, PG, IL>), grid, dim3(kBlock), 0, s, ch, cm);       \
+  } while (0)
+#define KAMERA_LAUNCH_ROT2(LPR, PG)                 \
+  do {                                              \
+    if (il) KAMERA_LAUNCH_ROT3(LPR, PG, true);      \
+    else KAMERA_LAUNCH_ROT3(LPR, PG, false);        \
   } while (0)
 #define KAMERA_LAUNCH_ROT(LPR)                                  \
   do {                                                          \
@@ -849,6 +936,7 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
   }
 #undef KAMERA_LAUNCH_ROT
 #undef KAMERA_LAUNCH_ROT2
+#undef KAMERA_LAUNCH_ROT3
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ KAMERA_OK, KAMERA_E_NULL, KAMERA_E_SHAPE, KAMERA_E_UNSUPPORTED = 0, 1, 2, 3
 KAMERA_E_ALIGN, KAMERA_E_ALIAS, KAMERA_E_HIP = 4, 5, 6
 KAMERA_BF16, KAMERA_F32 = 0, 1
 KAMERA_NEOX_HALF = 0
+KAMERA_INTERLEAVED = 1
 KAMERA_FLAG_GENERIC = 1
 KAMERA_MAX_RANK = 256
 KERNEL_NAMES = {0: "none", 1: "rotate", 2: "rotate+patch mfma", 3: "generic"}
@@ -38,7 +39,8 @@ class kamera_kv_desc(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("num_layers", C.c_int32), ("num_channels", C.c_int32),
                 ("pairing", C.c_int32), ("ch", kamera_channel * 2), ("rope_theta", C.c_double),
                 ("page_size", C.c_int32), ("flags", C.c_uint32), ("num_pages", C.c_int64),
-                ("block_table", C.c_void_p)]
+                ("block_table", C.c_void_p), ("num_sections", C.c_int32),
+                ("section_pairs", C.c_int32 * 4), ("reserved1", C.c_int32)]
 
 
 class kamera_chunks(C.Structure):
@@ -176,10 +178,19 @@ def channel(data, *, heads: int, dim: int, rope_dim: int, layer_stride: int,
 
 
 def kv_desc(channels, *, dtype: int, num_layers: int, rope_theta: float, page_size: int = 0,
-            num_pages: int = 0, block_table=None, flags: int = 0) -> kamera_kv_desc:
+            num_pages: int = 0, block_table=None, flags: int = 0,
+            pairing: int = 0, sections=()) -> kamera_kv_desc:
+    """KV descriptor.  `pairing`: KAMERA_NEOX_HALF or KAMERA_INTERLEAVED; `sections`:
+    M-RoPE rotary pairs per section (then the chunk deltas are [chunks][sections])."""
     d = kamera_kv_desc()
     d.dtype, d.num_layers, d.num_channels = dtype, num_layers, len(channels)
-    d.pairing = KAMERA_NEOX_HALF
+    d.pairing = pairing
+    sec = list(sections)
+    if len(sec) > 4:
+        raise ValueError("at most 4 M-RoPE sections")
+    d.num_sections = len(sec) if len(sec) > 1 else 0
+    for k, v in enumerate(sec):
+        d.section_pairs[k] = v
     for i, c in enumerate(channels):
         d.ch[i] = c
     d.rope_theta = rope_theta
@@ -189,9 +200,10 @@ def kv_desc(channels, *, dtype: int, num_layers: int, rope_theta: float, page_si
 
 
 def chunks_desc(offsets, delta, total_tokens: int) -> kamera_chunks:
-    """offsets: int64 device tensor [n+1]; delta: int64 device tensor [n]."""
+    """offsets: int64 device tensor [n+1]; delta: int64 device tensor [n], or [n][S]
+    with M-RoPE sections (contiguous)."""
     c = kamera_chunks()
-    c.num_chunks = int(delta.numel())
+    c.num_chunks = int(delta.shape[0]) if delta.dim() else 1
     c.reserved0 = 0
     c.total_tokens = int(total_tokens)
     c.token_offsets = offsets.data_ptr() if offsets.numel() else None

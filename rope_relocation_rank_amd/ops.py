@@ -7,7 +7,8 @@ from . import kamera as K
 
 def descriptors(buffers, layouts, *, dtype_code: int, num_layers: int, theta: float,
                 offsets_t, delta_t, total_tokens: int, rank: int = 0, U=(), V=(),
-                page_size: int = 0, num_pages: int = 0, block_table_t=None, flags: int = 0):
+                page_size: int = 0, num_pages: int = 0, block_table_t=None, flags: int = 0,
+                pairing: int = 0, sections=()):
     """Descriptors for channels laid out as `layouts` (dicts with buffer, offset,
     heads, dim, rope_dim and element strides) over the KV tensors in `buffers`."""
     chans = []
@@ -19,7 +20,7 @@ def descriptors(buffers, layouts, *, dtype_code: int, num_layers: int, theta: fl
                                element_offset=lay.get("offset", 0)))
     kv = K.kv_desc(chans, dtype=dtype_code, num_layers=num_layers, rope_theta=theta,
                    page_size=page_size, num_pages=num_pages, block_table=block_table_t,
-                   flags=flags)
+                   flags=flags, pairing=pairing, sections=sections)
     ch = K.chunks_desc(offsets_t, delta_t, total_tokens)
     Us = list(U) + [None] * (2 - len(U))
     Vs = list(V) + [None] * (2 - len(V))
@@ -36,7 +37,8 @@ def descriptors_for(inp, flags: int = 0):
                        theta=w.theta, offsets_t=inp.offsets_t, delta_t=inp.delta_t,
                        total_tokens=inp.struct.total_tokens, rank=inp.rank, U=inp.U, V=inp.V,
                        page_size=w.page_size, num_pages=inp.pool_pages,
-                       block_table_t=inp.block_table_t, flags=flags)
+                       block_table_t=inp.block_table_t, flags=flags, pairing=w.pairing,
+                       sections=w.sections)
 
 
 def run(inp, stream=None, flags: int = 0) -> None:

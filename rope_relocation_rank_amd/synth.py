@@ -56,6 +56,9 @@ class Workload:
     outlier_scale: float = 8.0
     dtype: str = "bf16"
     note: str = ""
+    pairing: int = 0            # 0 NeoX half-split, 1 interleaved
+    sections: tuple = ()        # M-RoPE rotary pairs per section (empty: plain RoPE)
+    delta_vec: tuple | None = None  # M-RoPE: the same per-section delta for every chunk
     recall: bool = False        # out of place: canonical store -> destination cache
     dst_page_size: int = 0      # recall destination: 0 contiguous, > 0 paged
     dst_pool_pages: int = 0     # recall destination pool pages per layer (paged)
@@ -135,7 +138,7 @@ class Structure:
 
     @property
     def num_chunks(self) -> int:
-        return int(self.delta.size)
+        return int(self.delta.shape[0])
 
 
 def structure(w: Workload) -> Structure:
@@ -149,13 +152,16 @@ def structure(w: Workload) -> Structure:
     n = len(lens)
     offsets = np.zeros(n + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(lens)
+    S = len(w.sections) if len(w.sections) > 1 else 1
+    shape = (n, S) if S > 1 else (n,)
     if w.deltas is not None:
-        delta = np.asarray(w.deltas, dtype=np.int64)
-        assert delta.size == n
+        delta = np.asarray(w.deltas, dtype=np.int64).reshape(shape)
     elif w.delta_range is not None:
-        delta = rng.integers(w.delta_range[0], w.delta_range[1] + 1, size=n).astype(np.int64)
+        delta = rng.integers(w.delta_range[0], w.delta_range[1] + 1, size=shape).astype(np.int64)
+    elif w.delta_vec is not None:
+        delta = np.tile(np.asarray(w.delta_vec, dtype=np.int64), (n, 1)).reshape(shape)
     else:
-        delta = np.full(n, w.delta, dtype=np.int64)
+        delta = np.full(shape, w.delta, dtype=np.int64)
     T = int(offsets[-1])
     bt = None
     if w.page_size > 0:

@@ -134,7 +134,8 @@ def oracle_on_host(inp, before: list, factors: tuple | None = None):
         chans.append(d)
     orc.relocate_patch(chans, num_layers=w.layers, theta=w.theta, offsets=inp.struct.offsets,
                        delta=inp.struct.delta, rank=inp.rank, page_size=w.page_size,
-                       block_table=inp.struct.block_table,
+                       block_table=inp.struct.block_table, pairing=w.pairing,
+                       sections=w.sections,
                        y_out=[y[lay["buffer"]] for lay in inp.layouts],
                        s_out=[s[lay["buffer"]] for lay in inp.layouts])
     return out, y, s
@@ -221,25 +222,43 @@ def sampled_check(inp, run, n=1024, seed=0) -> Report:
         lay = inp.layouts[c]
         for k, (l, t) in enumerate(rows):
             j = int(np.searchsorted(st.offsets, t, side="right") - 1)
-            d = int(st.delta[j])
-            u = us[c][k] if inp.rank > 0 else None
-            V = vs[c][l, j] if inp.rank > 0 else None
-            x = before[c][k]
-            o = orc.row(x, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, u, V)
-            xf = bf16_value(x)
-            uf = None if u is None else bf16_value(u)
-            Vf = None if V is None else bf16_value(V)
-            y = orc.row_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, uf, Vf)
-            s = orc.row_magnitude_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d,
-                                      uf, Vf)
-            if inp.rank == 0:  # only rotated dims of chunks that move are computed
-                moved = np.zeros(lay["heads"] * lay["dim"], bool)
-                if d != 0:
-                    for h in range(lay["heads"]):
-                        moved[h * lay["dim"]:h * lay["dim"] + lay["rope_dim"]] = True
-                s = np.where(moved, s, -1.0)
-            compare(after[c][k], o, y, s, inp.rank, rep)
+            compare(after[c][k], *_row_expect(w, lay, st.delta[j], before[c][k],
+                                              us[c][k] if inp.rank > 0 else None,
+                                              vs[c][l, j] if inp.rank > 0 else None),
+                    inp.rank, rep)
     return rep
+
+
+def moved_dims(lay, d, pairing=0, sections=()) -> np.ndarray:
+    """Elements of one row that the rotation moves (rank 0): rotated dims of pairs
+    whose (section) delta is nonzero."""
+    H, D, r = lay["heads"], lay["dim"], lay["rope_dim"]
+    d = np.atleast_1d(np.asarray(d, dtype=np.int64))
+    half = r // 2
+    pair_sec = (np.repeat(np.arange(len(sections)), sections) if len(sections) > 1
+                else np.zeros(half, np.int64))
+    moves = d[pair_sec] != 0 if half else np.zeros(0, bool)
+    head = np.zeros(D, bool)
+    for i in range(half):
+        a, b = (2 * i, 2 * i + 1) if pairing == 1 else (i, i + half)
+        head[a] = head[b] = moves[i]
+    return np.tile(head, H)
+
+
+def _row_expect(w, lay, d, x, u, V):
+    """(oracle storage, fp64 value, magnitude or -1 where bits must match) of one row."""
+    from oracle import oracle as orc
+    kw = dict(pairing=w.pairing, sections=w.sections)
+    o = orc.row(x, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, u, V, **kw)
+    xf = bf16_value(x)
+    uf = None if u is None else bf16_value(u)
+    Vf = None if V is None else bf16_value(V)
+    y = orc.row_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, uf, Vf, **kw)
+    s = orc.row_magnitude_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, uf,
+                              Vf, **kw)
+    if u is None:  # rank 0: only moved dims are computed
+        s = np.where(moved_dims(lay, d, w.pairing, w.sections), s, -1.0)
+    return o, y, s
 
 
 # ----------------------------------------------------------------- recall (out of place)
@@ -280,6 +299,7 @@ def check_recall(rinp, run) -> tuple:
                      offsets=src.struct.offsets, delta=src.struct.delta, rank=src.rank,
                      src_page_size=w.page_size, src_block_table=src.struct.block_table,
                      dst_page_size=rinp.dst_page_size, dst_block_table=rinp.dst_block_table,
+                     pairing=w.pairing, sections=w.sections,
                      y_out=[y[lay["buffer"]] for lay in rinp.dst_layouts],
                      s_out=[s[lay["buffer"]] for lay in rinp.dst_layouts])
     rep = Report()
@@ -336,22 +356,8 @@ def sampled_check_recall(rinp, run, n=1024, seed=0) -> Report:
         assert np.array_equal(src_after, before[c]), "recall wrote its source"
         for k, (l, t) in enumerate(rows):
             j = int(np.searchsorted(st.offsets, t, side="right") - 1)
-            d = int(st.delta[j])
-            u = us[c][k] if src.rank > 0 else None
-            V = vs[c][l, j] if src.rank > 0 else None
-            x = before[c][k]
-            o = orc.row(x, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, u, V)
-            xf = bf16_value(x)
-            uf = None if u is None else bf16_value(u)
-            Vf = None if V is None else bf16_value(V)
-            y = orc.row_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, uf, Vf)
-            s = orc.row_magnitude_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d,
-                                      uf, Vf)
-            if src.rank == 0:  # copied elements must match bit for bit
-                moved = np.zeros(lay["heads"] * lay["dim"], bool)
-                if d != 0:
-                    for h in range(lay["heads"]):
-                        moved[h * lay["dim"]:h * lay["dim"] + lay["rope_dim"]] = True
-                s = np.where(moved, s, -1.0)
-            compare(got[k], o, y, s, src.rank, rep)
+            compare(got[k], *_row_expect(w, lay, st.delta[j], before[c][k],
+                                         us[c][k] if src.rank > 0 else None,
+                                         vs[c][l, j] if src.rank > 0 else None),
+                    src.rank, rep)
     return rep

@@ -35,7 +35,7 @@ def test_library_loads_and_exports_every_declared_function():
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     assert set(names) <= exported
     assert not [e for e in exported if "launch" in e], "internal symbols leak"
-    assert K.kamera_abi_version() == 1
+    assert K.kamera_abi_version() == 2
 
 
 def test_struct_layout_matches_header():
@@ -139,8 +139,40 @@ def test_bad_dtype_and_pairing():
     kv.dtype = 7
     expect_status(K.KAMERA_E_UNSUPPORTED, kv, ch, p)
     kv, ch, p = gqa()
-    kv.pairing = 1
+    kv.pairing = 2
     expect_status(K.KAMERA_E_UNSUPPORTED, kv, ch, p)
+
+
+def test_positional_variants():
+    # Interleaved pairing and M-RoPE sections take the same kernels.
+    kv, ch, p = gqa(m=32)
+    kv.pairing = K.KAMERA_INTERLEAVED
+    names, _ = plan_names(kv, ch, p)
+    assert names == ["rotate+patch mfma"] * 2
+    kv, ch, p = gqa(m=0)
+    kv.pairing = K.KAMERA_INTERLEAVED
+    names, _ = plan_names(kv, ch, p)
+    assert names == ["rotate", "none"]
+    for m in (0, 16):
+        kv, ch, p = gqa(m=m)
+        kv.num_sections = 3
+        kv.section_pairs[0], kv.section_pairs[1], kv.section_pairs[2] = 16, 24, 24
+        names, _ = plan_names(kv, ch, p)
+        assert names[0] in ("rotate", "rotate+patch mfma")
+    # sections must cover the rotary pairs of every rotating channel
+    kv, ch, p = gqa(m=16)
+    kv.num_sections = 3
+    kv.section_pairs[0], kv.section_pairs[1], kv.section_pairs[2] = 16, 24, 23
+    expect_status(K.KAMERA_E_SHAPE, kv, ch, p)
+    kv.section_pairs[2] = 24
+    kv.section_pairs[1] = -1
+    expect_status(K.KAMERA_E_SHAPE, kv, ch, p)
+    kv, ch, p = gqa(m=16)
+    kv.num_sections = 5
+    expect_status(K.KAMERA_E_SHAPE, kv, ch, p)
+    kv, ch, p = gqa(m=16)
+    kv.reserved1 = 1
+    expect_status(K.KAMERA_E_SHAPE, kv, ch, p)
 
 
 @pytest.mark.parametrize("mutate", [
