@@ -255,7 +255,7 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
         // register budget of four waves per SIMD, four would spill.
         const int udflt = kv->pairing == KAMERA_INTERLEAVED ? 2 : 4;
         int unroll = env_int("KAMERA_ROTATE_UNROLL", udflt);
-        if (unroll != 1 && unroll != 2 && unroll != 4) unroll = udflt;
+        if (unroll != 2 && unroll != 4) unroll = udflt;
         const int rows = 4 * unroll * (64 / (k.rope_dim / 8));
         const int bt = (int)std::min<int64_t>(kamera::kMaxBlockTokens,
                                               std::max<int64_t>(1, rows / k.heads));

@@ -56,7 +56,7 @@ struct CommonArgs {
 };
 
 // Rotation only, bf16, 16-byte accesses: rope_dim in {16, 32, 64, 128}.
-// `unroll` row groups per wavefront (1, 2 or 4).
+// `unroll` row groups per wavefront (2 or 4).
 hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unroll,
                               hipStream_t s);
 

@@ -141,6 +141,8 @@ __device__ __forceinline__ int64_t chunk_moves(const CommonArgs& cm, int k) {
 // reads the end and the motion of chunk base + k, a ballot counts the chunks that end
 // at or before t.  ChunkRef::delta is nonzero iff the chunk moves (with sections it is
 // not itself a delta: pair_delta gives those).
+// SEC: 1 sections known present, 0 known absent, -1 decided at run time.
+template <int SEC = -1>
 __device__ __forceinline__ ChunkRef find_chunk_wave(const CommonArgs& cm, int64_t t,
                                                     int from = 0) {
   const int lane = threadIdx.x & 63;
@@ -150,7 +152,8 @@ __device__ __forceinline__ ChunkRef find_chunk_wave(const CommonArgs& cm, int64_
   for (int base = from; base < n; base += 64) {
     const int k = base + lane;
     const int64_t e = k < n ? off[k + 1] : INT64_MAX;
-    const int64_t d = k < n ? chunk_moves(cm, k) : 0;
+    int64_t d = 0;
+    if (k < n) d = SEC == 0 ? cm.delta[k] : chunk_moves(cm, k);
     const unsigned long long le = __ballot(e <= t);  // chunks that end at or before t
     const int cnt = __popcll(le);
     if (cnt < 64 || base + 64 >= n) {
@@ -161,7 +164,7 @@ __device__ __forceinline__ ChunkRef find_chunk_wave(const CommonArgs& cm, int64_
       if (base + src >= n) {  // past the last chunk: clamp to it
         c.j = n - 1;
         c.end = off[n];
-        c.delta = chunk_moves(cm, n - 1);
+        c.delta = SEC == 0 ? cm.delta[n - 1] : chunk_moves(cm, n - 1);
       }
       break;
     }
@@ -310,7 +313,7 @@ __device__ __forceinline__ int32_t slot32(int page_size, int page_shift, const i
 // workgroup barrier, once, for the staged block table.  Dims >= rope_dim are never
 // touched; rows of chunks that do not move are not written; with M-RoPE sections, the
 // dims of pairs whose section delta is 0 keep their bits.
-template <int LPR, int UNR, bool PAGED, bool IL>
+template <int LPR, int UNR, bool PAGED, bool IL, bool SEC>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(UNR == 4 ? 4 : 1)))
 void rotate_rows(ChanArgs ch, CommonArgs cm) {
   constexpr int RPI = 64 / LPR;
@@ -329,7 +332,6 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
   // Rotary pair of each of the lane's 8 dims, and the sign of its partner term.
   const int fi0 = IL ? 4 * q : (q % HX) * 8;
   const float sgn = q < HX ? -1.f : 1.f;
-  const bool mixed = cm.num_sections > 1;
   const int H = ch.heads;
   const int nrows = (int)(t1 - tb0) * H;
   uint16_t* base = (uint16_t*)ch.data + layer * ch.layer_stride + 8 * q;
@@ -371,12 +373,12 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
     const int r_last = min(nrows - 1, rbase + (wave + kWavesPerBlock * (UNR - 1)) * RPI + RPI - 1);
     int64_t t0 = tb0 + r_first / H;
     const int64_t tw1 = tb0 + r_last / H + 1;
-    ChunkRef c = find_chunk_wave(cm, t0);
+    ChunkRef c = find_chunk_wave<SEC ? 1 : 0>(cm, t0);
     while (true) {
       const int64_t s1 = min(tw1, c.end);
       if (s1 > t0 && c.delta != 0) {
         float2 own = make_float2(1.f, 0.f);
-        if (lane < HALF) own = phase_of(ch.omega[lane], pair_delta(cm, c, lane));
+        if (lane < HALF) own = phase_of(ch.omega[lane], SEC ? pair_delta(cm, c, lane) : c.delta);
         float cs[8], sn[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -397,7 +399,7 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) y[e] = fmaf(a[e], cs[e], b[e] * sn[e]);
           u32x4_t o = pack8(y);
-          if (mixed) {
+          if constexpr (SEC) {
             o.x = keep_halves(o.x, xv[k].x, sn[0] == 0.f, sn[1] == 0.f);
             o.y = keep_halves(o.y, xv[k].y, sn[2] == 0.f, sn[3] == 0.f);
             o.z = keep_halves(o.z, xv[k].z, sn[4] == 0.f, sn[5] == 0.f);
@@ -408,7 +410,7 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
       }
       t0 = max(t0, s1);
       if (t0 >= tw1 || c.j + 1 >= cm.num_chunks) break;
-      c = find_chunk_wave(cm, t0, c.j + 1);
+      c = find_chunk_wave<SEC ? 1 : 0>(cm, t0, c.j + 1);
     }
   }
 }
@@ -911,11 +913,16 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
   const int64_t blocks = (int64_t)cm.num_layers * cm.token_groups;
   const dim3 grid((unsigned)blocks);
   const bool il = cm.pairing == 1;
-#define KAMERA_LAUNCH_ROT3(LPR, PG, IL)                                                              \
+  const bool sec = cm.num_sections > 1;
+#define KAMERA_LAUNCH_ROT4(LPR, PG, IL, SC)                                                          \
   do {                                                                                               \
-    if (unroll == 1) hipLaunchKernelGGL((rotate_rows<LPR, 1, PG, IL>), grid, dim3(kBlock), 0, s, ch, cm); \
-    else if (unroll == 2) hipLaunchKernelGGL((rotate_rows<LPR, 2, PG, IL>), grid, dim3(kBlock), 0, s, ch, cm); \
-    else hipLaunchKernelGGL((rotate_rows<LPR, 4, PG, IL>), grid, dim3(kBlock), 0, s, ch, cm);       \
+    if (unroll == 2) hipLaunchKernelGGL((rotate_rows<LPR, 2, PG, IL, SC>), grid, dim3(kBlock), 0, s, ch, cm); \
+    else hipLaunchKernelGGL((rotate_rows<LPR, 4, PG, IL, SC>), grid, dim3(kBlock), 0, s, ch, cm);   \
+  } while (0)
+#define KAMERA_LAUNCH_ROT3(LPR, PG, IL)                 \
+  do {                                                  \
+    if (sec) KAMERA_LAUNCH_ROT4(LPR, PG, IL, true);     \
+    else KAMERA_LAUNCH_ROT4(LPR, PG, IL, false);        \
   } while (0)
 #define KAMERA_LAUNCH_ROT2(LPR, PG)                 \
   do {                                              \
@@ -937,6 +944,7 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
 #undef KAMERA_LAUNCH_ROT
 #undef KAMERA_LAUNCH_ROT2
 #undef KAMERA_LAUNCH_ROT3
+#undef KAMERA_LAUNCH_ROT4
   return hipGetLastError();
 }
 
