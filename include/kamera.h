@@ -193,6 +193,54 @@ KAMERA_API kamera_status kamera_recall_patch(const kamera_kv_desc* src, const ka
                                   const kamera_chunks* chunks, const kamera_patch* patch,
                                   hipStream_t stream);
 
+/* ------------------------------------------------------------------ patch formation
+ *
+ * The step before the reuse operator: Kamera page §2, "Aplicacao de Patch" forms the
+ * patch once, from one conditioned forward pass over [A, B] and an SVD that keeps the
+ * top-m factors.  The forward pass is the caller's.  Given the deficit
+ * Delta = KV(B|A) - KV(B|empty) of every layer and chunk of a channel, this writes
+ * U_m = U[:, :m] diag(s[:m]) and V_m = V[:, :m] of each chunk's SVD Delta_j = U diag(s) V^T,
+ * in the layouts kamera_patch takes, so U_m V_m^T is the best rank-m approximation of
+ * Delta_j (Eckart-Young).  Singular vectors are unique only up to sign (and within
+ * repeated singular values); their product is what the operator uses.
+ *
+ * Method: Gram matrix Delta_j^T Delta_j on MFMA (bf16 products, fp32 sums), subspace
+ * iteration in fp32 with k = min(m + 16 rounded up to even, width, 128) columns,
+ * Rayleigh-Ritz with a Jacobi eigensolver, U_m = Delta_j V_m.  Its error falls like
+ * (lambda_{k+1} / lambda_i)^iterations for eigenvalue lambda_i = s_i^2; a chunk whose
+ * singular values past m fall off is solved to fp32 precision in a few iterations.
+ * Outputs are rounded to bf16 (sigma stays fp32). */
+#define KAMERA_FORM_MAX_RANK 112
+
+typedef struct {
+  int32_t dtype;          /* KAMERA_BF16 (deficit and factors) */
+  int32_t num_layers;     /* >= 0 */
+  int32_t num_channels;   /* 1 or 2 */
+  int32_t rank;           /* m, 1 <= m <= KAMERA_FORM_MAX_RANK */
+  int32_t width[2];       /* F of each channel (heads * dim): a multiple of 64 in [64, 1024] */
+  int32_t iterations;     /* subspace iterations after the first; 0 = 8; at most 64 */
+  int32_t reserved0;      /* must be 0 */
+  const void* delta[2];   /* device [num_layers][total_tokens][width] bf16, row-major, 16-byte
+                             aligned; read only */
+  void* U[2];             /* device out [num_layers][total_tokens][rank] bf16 */
+  void* V[2];             /* device out [num_layers][num_chunks][width][rank] bf16 */
+  float* sigma[2];        /* device out [num_layers][num_chunks][rank] fp32, or NULL */
+} kamera_form_desc;
+
+/* Bytes of workspace kamera_form_patch can use to hold up to 64 (layer, chunk)
+ * problems at a time; any workspace of at least one problem's share works (in more
+ * batches).  Checks the descriptor like kamera_form_patch. */
+KAMERA_API kamera_status kamera_form_workspace(const kamera_form_desc* desc,
+                                    const kamera_chunks* chunks, int64_t* bytes);
+
+/* Forms the patch of every layer and chunk of every channel.  chunks: offsets and
+ * total_tokens as for kamera_relocate_patch (its delta is not read).  The workspace is
+ * caller-owned device memory, 256-byte aligned, overwritten; nothing else is
+ * allocated.  The outputs must not overlap the deficit, each other or the workspace
+ * (KAMERA_E_ALIAS).  Stream-ordered, like every entry point. */
+KAMERA_API kamera_status kamera_form_patch(const kamera_form_desc* desc, const kamera_chunks* chunks,
+                                void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
 /* Which kernels a call would launch, without launching anything (no HIP call).
  * Fills `out` and returns the status the call itself would return before launching. */
 typedef struct {

@@ -507,9 +507,136 @@ kamera_status run_recall(const kamera_kv_desc* src, const kamera_kv_desc* dst,
   return KAMERA_OK;
 }
 
+// ------------------------------------------------------------------ patch formation
+
+constexpr int kFormBatch = 64;
+
+int form_k(int m, int F) { return std::min(std::min((m + 17) & ~1, F), 128); }
+
+int64_t form_problem_bytes(const kamera_form_desc& d, int c) {
+  return 4 * kamera::form_workspace_floats(d.width[c], form_k(d.rank, d.width[c]));
+}
+
+kamera_status validate_form(const kamera_form_desc* d, const kamera_chunks* ch, bool* empty) {
+  if (!d) return fail(KAMERA_E_NULL, "form descriptor is NULL");
+  if (!ch) return fail(KAMERA_E_NULL, "chunks descriptor is NULL");
+  if (d->dtype != KAMERA_BF16) return fail(KAMERA_E_UNSUPPORTED, "patch formation takes bf16 only");
+  if (d->num_layers < 0) return fail(KAMERA_E_SHAPE, "num_layers %d < 0", d->num_layers);
+  if (d->num_channels < 1 || d->num_channels > 2)
+    return fail(KAMERA_E_SHAPE, "num_channels %d is not 1 or 2", d->num_channels);
+  if (d->rank < 1 || d->rank > KAMERA_FORM_MAX_RANK)
+    return fail(KAMERA_E_SHAPE, "rank %d outside [1, %d]", d->rank, KAMERA_FORM_MAX_RANK);
+  if (d->iterations < 0 || d->iterations > 64)
+    return fail(KAMERA_E_SHAPE, "iterations %d outside [0, 64]", d->iterations);
+  if (d->reserved0 != 0) return fail(KAMERA_E_SHAPE, "form.reserved0 must be 0");
+  if (ch->num_chunks < 0 || ch->total_tokens < 0 || ch->reserved0 != 0)
+    return fail(KAMERA_E_SHAPE, "bad chunks descriptor");
+  if (ch->num_chunks == 0 && ch->total_tokens != 0)
+    return fail(KAMERA_E_SHAPE, "total_tokens > 0 with no chunks");
+  if (ch->total_tokens >= ((int64_t)1 << 31)) return fail(KAMERA_E_SHAPE, "total_tokens too large");
+  *empty = d->num_layers == 0 || ch->total_tokens == 0;
+  for (int c = 0; c < d->num_channels; ++c) {
+    const int F = d->width[c];
+    if (F < 64 || F > 1024 || F % 64 != 0)
+      return fail(KAMERA_E_SHAPE, "channel %d: width %d is not a multiple of 64 in [64, 1024]", c, F);
+    if (!*empty && (!d->delta[c] || !d->U[c] || !d->V[c]))
+      return fail(KAMERA_E_NULL, "channel %d: delta, U and V are required", c);
+    if (!aligned(d->delta[c], 16))
+      return fail(KAMERA_E_ALIGN, "channel %d: delta not 16-byte aligned", c);
+    if (!aligned(d->U[c], 2) || !aligned(d->V[c], 2) || !aligned(d->sigma[c], 4))
+      return fail(KAMERA_E_ALIGN, "channel %d: misaligned output", c);
+  }
+  if (!*empty && !ch->token_offsets) return fail(KAMERA_E_NULL, "token_offsets is NULL");
+  if (!aligned(ch->token_offsets, 8)) return fail(KAMERA_E_ALIGN, "token_offsets not 8-byte aligned");
+  return KAMERA_OK;
+}
+
+kamera_status run_form(const kamera_form_desc* d, const kamera_chunks* ch, void* ws, int64_t ws_bytes,
+                       hipStream_t stream) {
+  g_last_error.clear();
+  bool empty = true;
+  kamera_status st = validate_form(d, ch, &empty);
+  if (st != KAMERA_OK || empty) return st;
+  if (!ws) return fail(KAMERA_E_NULL, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(KAMERA_E_ALIGN, "workspace not 256-byte aligned");
+  const int64_t T = ch->total_tokens, L = d->num_layers, n = ch->num_chunks, m = d->rank;
+  // Outputs must not overlap the inputs, each other or the workspace.
+  struct Range { const void* p; int64_t n; };
+  Range in[5], out[6];
+  int nin = 0, nout = 0;
+  in[nin++] = {ws, ws_bytes};
+  for (int c = 0; c < d->num_channels; ++c) {
+    const int64_t F = d->width[c];
+    in[nin++] = {d->delta[c], L * T * F * 2};
+    out[nout++] = {d->U[c], L * T * m * 2};
+    out[nout++] = {d->V[c], L * n * F * m * 2};
+    if (d->sigma[c]) out[nout++] = {d->sigma[c], L * n * m * 4};
+  }
+  for (int a = 0; a < nout; ++a) {
+    for (int b = 0; b < nin; ++b)
+      if (overlaps(out[a].p, out[a].n, in[b].p, in[b].n))
+        return fail(KAMERA_E_ALIAS, "a patch-formation output overlaps its input or the workspace");
+    for (int b = a + 1; b < nout; ++b)
+      if (overlaps(out[a].p, out[a].n, out[b].p, out[b].n))
+        return fail(KAMERA_E_ALIAS, "patch-formation outputs overlap each other");
+  }
+  const int64_t problems = L * n;
+  for (int c = 0; c < d->num_channels; ++c) {
+    const int64_t per = form_problem_bytes(*d, c);
+    if (ws_bytes < per)
+      return fail(KAMERA_E_SHAPE, "workspace of %lld bytes holds no problem (needs %lld)",
+                  (long long)ws_bytes, (long long)per);
+  }
+  for (int c = 0; c < d->num_channels; ++c) {
+    kamera::FormArgs a;
+    memset(&a, 0, sizeof a);
+    a.delta = (const uint16_t*)d->delta[c];
+    a.offsets = ch->token_offsets;
+    a.ws = (float*)ws;
+    a.U_out = (uint16_t*)d->U[c];
+    a.V_out = (uint16_t*)d->V[c];
+    a.sigma_out = d->sigma[c];
+    a.total_tokens = T;
+    a.num_chunks = (int32_t)n;
+    a.F = d->width[c];
+    a.k = form_k(d->rank, d->width[c]);
+    a.m = d->rank;
+    a.iters = d->iterations > 0 ? d->iterations : 8;
+    const int64_t batch = std::min<int64_t>({(int64_t)kFormBatch, problems,
+                                             ws_bytes / form_problem_bytes(*d, c)});
+    for (int64_t p0 = 0; p0 < problems; p0 += batch) {
+      const int count = (int)std::min<int64_t>(batch, problems - p0);
+      const hipError_t e = kamera::launch_form_batch(a, p0, count, stream);
+      if (e != hipSuccess) return hip_fail(e, "patch-formation launch");
+    }
+  }
+  return KAMERA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+kamera_status kamera_form_workspace(const kamera_form_desc* desc, const kamera_chunks* chunks,
+                                    int64_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(KAMERA_E_NULL, "bytes is NULL");
+  *bytes = 0;
+  bool empty = true;
+  const kamera_status st = validate_form(desc, chunks, &empty);
+  if (st != KAMERA_OK) return st;
+  const int64_t problems = (int64_t)desc->num_layers * chunks->num_chunks;
+  int64_t per = 0;
+  for (int c = 0; c < desc->num_channels; ++c) per = std::max(per, form_problem_bytes(*desc, c));
+  *bytes = empty ? 0 : per * std::min<int64_t>(kFormBatch, std::max<int64_t>(1, problems));
+  return KAMERA_OK;
+}
+
+kamera_status kamera_form_patch(const kamera_form_desc* desc, const kamera_chunks* chunks,
+                                void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return run_form(desc, chunks, workspace, workspace_bytes, stream);
+}
+
 
 kamera_status kamera_recall_patch(const kamera_kv_desc* src, const kamera_kv_desc* dst,
                                   const kamera_chunks* chunks, const kamera_patch* patch,

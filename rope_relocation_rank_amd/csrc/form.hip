@@ -1,0 +1,488 @@
+// gfx950 kernels of patch formation: the top-m factors of the reuse deficit.
+//
+// "Kamera: KV Cache Multimodal Unificado e Invariante a Posicao para Reuso sem
+// Treinamento" (gist.science/pt/paper/2606.23581), §2, "Aplicacao de Patch": the patch
+// is formed once, from one conditioned forward pass and an SVD that keeps the top-m
+// factors.  The forward pass is the caller's; this file takes the deficit
+// Delta = KV(B|A) - KV(B|empty) of every (layer, chunk) of a channel, [T_j, F] in bf16,
+// and writes U_m = U diag(s) [T_j, m] and V_m [F, m] (bf16, the layouts the reuse
+// operator reads) and the singular values s (fp32).
+//
+// Method, per problem (layer, chunk):
+//   1. G = Delta^T Delta (F x F, fp32) on MFMA 16x16x32 bf16: a dense contraction over
+//      the chunk's tokens, upper-triangular 64 x 64 tiles, mirrored.
+//   2. Subspace iteration on G with k = m + 16 columns (at most 128, at most F):
+//      Q <- orth(G Q) from a fixed pseudo-random start, `iters` times (fp32 tiled GEMM,
+//      classical Gram-Schmidt with one reorthogonalization per column).
+//   3. Rayleigh-Ritz: B = Q^T G Q (k x k), eigenpairs of B by cyclic Jacobi in LDS,
+//      sorted; V_m = Q E[:, :m], s_i = sqrt(lambda_i).
+//   4. U_m = Delta V_m (= U_m diag(s) of the SVD), rounded to bf16 with V_m.
+// The top-m right singular vectors of Delta are the top-m eigenvectors of G; the error
+// of the subspace iteration shrinks like (lambda_{k+1} / lambda_i)^iters.
+#include <hip/hip_runtime.h>
+
+#include "kamera_internal.h"
+
+namespace kamera {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kMaxK = 128;
+
+__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ uint16_t f2bf16(float y) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(y));  // round to nearest even
+}
+
+// Workspace of one problem (floats): G [F][F], Q [F][k], Z [F][k], B [k][k], E [k][k],
+// lambda [k].
+struct WsLayout {
+  int64_t G, Q, Z, B, E, lam, stride;
+};
+
+__host__ __device__ inline WsLayout ws_layout(int F, int k) {
+  WsLayout w;
+  w.G = 0;
+  w.Q = w.G + (int64_t)F * F;
+  w.Z = w.Q + (int64_t)F * k;
+  w.B = w.Z + (int64_t)F * k;
+  w.E = w.B + (int64_t)k * k;
+  w.lam = w.E + (int64_t)k * k;
+  w.stride = (w.lam + k + 63) / 64 * 64;
+  return w;
+}
+
+// ------------------------------------------------------------------ 1. Gram on MFMA
+
+// One 64 x 64 tile (ti <= tj) of G = Delta_j^T Delta_j.  Per 32-token step the
+// workgroup stages both 64-feature column blocks of Delta transposed in LDS
+// ([feature][token]), so each lane reads the 8 consecutive tokens of one feature that
+// an MFMA operand row holds.  Wave w owns the 32 x 32 quadrant (w >> 1, w & 1): 2 x 2
+// MFMA 16x16x32 tiles.  G[i][j] = sum_t A[i][t] B[t][j] with A = Delta^T, B = Delta.
+__global__ __launch_bounds__(kThreads) void gram_tiles(FormArgs P, int64_t p0) {
+  const int ntile = P.F / 64;
+  int rem = blockIdx.x, ti = 0;
+  while (rem >= ntile - ti) {
+    rem -= ntile - ti;
+    ++ti;
+  }
+  const int tj = ti + rem;
+  const int64_t p = p0 + blockIdx.y;
+  const int64_t layer = p / P.num_chunks;
+  const int j = (int)(p - layer * P.num_chunks);
+  // Rows [a, b) of the chunk, kept inside [0, total_tokens) whatever the offsets hold.
+  const int64_t a = min(max(P.offsets[j], (int64_t)0), P.total_tokens);
+  const int64_t b = min(max(P.offsets[j + 1], a), P.total_tokens);
+  const WsLayout W = ws_layout(P.F, P.k);
+  float* G = P.ws + (int64_t)blockIdx.y * W.stride + W.G;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sA[64][40];  // 32 tokens + 8 pad
+  __shared__ __attribute__((aligned(16))) uint16_t sB[64][40];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  const int tl = tid >> 3, c8 = (tid & 7) * 8;
+  const uint16_t* D = P.delta + layer * P.total_tokens * P.F;
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t t0 = a; t0 < b; t0 += 32) {
+    const int64_t tt = t0 + tl;
+    u32x4_t va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
+    if (tt < b) {
+      va = *(const u32x4_t*)(D + tt * P.F + ti * 64 + c8);
+      vb = *(const u32x4_t*)(D + tt * P.F + tj * 64 + c8);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sA[c8 + 2 * e][tl] = (uint16_t)(va[e] & 0xffffu);
+      sA[c8 + 2 * e + 1][tl] = (uint16_t)(va[e] >> 16);
+      sB[c8 + 2 * e][tl] = (uint16_t)(vb[e] & 0xffffu);
+      sB[c8 + 2 * e + 1][tl] = (uint16_t)(vb[e] >> 16);
+    }
+    __syncthreads();
+    const int g = lane >> 4, r16 = lane & 15;
+    bf16x8_t fa[2], fb[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      fa[x] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)&sA[wi * 32 + x * 16 + r16][8 * g]);
+      fb[x] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)&sB[wj * 32 + x * 16 + r16][8 * g]);
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    __syncthreads();
+  }
+  // D layout: lane holds rows 4g .. 4g + 3 of column lane & 15.
+  const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gi = ti * 64 + wi * 32 + x * 16 + 4 * g + r;
+        const int gj = tj * 64 + wj * 32 + y * 16 + c;
+        G[(int64_t)gi * P.F + gj] = acc[x][y][r];
+        if (ti != tj) G[(int64_t)gj * P.F + gi] = acc[x][y][r];
+      }
+}
+
+// ------------------------------------------------------------------ 2. dense fp32 algebra
+
+// Fixed pseudo-random start: entry e of Q (row-major F x k) is a 32-bit integer hash of
+// e (a multiply-xorshift mixer) scaled to [-1, 1); the same for every problem.
+__global__ __launch_bounds__(kThreads) void init_start(FormArgs P) {
+  const WsLayout W = ws_layout(P.F, P.k);
+  float* Q = P.ws + (int64_t)blockIdx.y * W.stride + W.Q;
+  const int n = P.F * P.k;
+  for (int e = blockIdx.x * kThreads + threadIdx.x; e < n; e += gridDim.x * kThreads) {
+    uint32_t h = (uint32_t)e * 0x9E3779B9u + 0x7F4A7C15u;
+    h ^= h >> 16;
+    h *= 0x7feb352du;
+    h ^= h >> 15;
+    h *= 0x846ca68bu;
+    h ^= h >> 16;
+    Q[e] = (float)(int32_t)h * 0x1p-31f;
+  }
+}
+
+// C = op(A) B for every problem of the batch (blockIdx.z): op(A) is M x K (A row-major
+// M x K, or with TA row-major K x M), B row-major K x N, C row-major M x N; fp32 with
+// 64 x 64 output tiles, 16-deep LDS steps, 4 x 4 outputs per thread.  Offsets are
+// element offsets inside each problem's workspace.
+template <bool TA>
+__global__ __launch_bounds__(kThreads) void gemm_ws(FormArgs P, int64_t a_off, int lda,
+                                                     int64_t b_off, int ldb, int64_t c_off,
+                                                     int ldc, int M, int N, int K) {
+  const WsLayout W = ws_layout(P.F, P.k);
+  float* base = P.ws + (int64_t)blockIdx.z * W.stride;
+  const float* A = base + a_off;
+  const float* B = base + b_off;
+  float* C = base + c_off;
+  __shared__ float sA[16][64 + 4];
+  __shared__ float sB[16][64 + 4];
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int ty = tid >> 4, tx = tid & 15;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + kThreads * q;
+      int r, kk;
+      if (TA) {
+        kk = idx >> 6;
+        r = idx & 63;
+      } else {
+        r = idx >> 4;
+        kk = idx & 15;
+      }
+      const int gm = m0 + r, gk = k0 + kk;
+      float v = 0.f;
+      if (gm < M && gk < K) v = TA ? A[(int64_t)gk * lda + gm] : A[(int64_t)gm * lda + gk];
+      sA[kk][r] = v;
+      const int bk = idx >> 6, bc = idx & 63;
+      const int gbk = k0 + bk, gn = n0 + bc;
+      sB[bk][bc] = (gbk < K && gn < N) ? B[(int64_t)gbk * ldb + gn] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = sA[kk][ty * 4 + i];
+        bv[i] = sB[kk][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = fmaf(av[i], bv[jj], acc[i][jj]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int gm = m0 + ty * 4 + i, gn = n0 + tx * 4 + jj;
+      if (gm < M && gn < N) C[(int64_t)gm * ldc + gn] = acc[i][jj];
+    }
+}
+
+// Block reduction of one float over the workgroup (result in every thread).
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// Q = orth(Z): classical Gram-Schmidt with one reorthogonalization per column, column
+// by column; Z (F x k) is read, Q (F x k) written.  A column whose remainder falls
+// below 1e-6 of its norm (a direction the chunk does not span) becomes zero.
+__global__ __launch_bounds__(kThreads) void orthonormalize(FormArgs P) {
+  const WsLayout W = ws_layout(P.F, P.k);
+  float* base = P.ws + (int64_t)blockIdx.x * W.stride;
+  const float* Z = base + W.Z;
+  float* Q = base + W.Q;
+  const int F = P.F, k = P.k, tid = threadIdx.x;
+  __shared__ float z[1024];
+  __shared__ float rc[kMaxK];
+  __shared__ float red[4];
+  for (int c = 0; c < k; ++c) {
+    float n0 = 0.f;
+    for (int f = tid; f < F; f += kThreads) {
+      const float v = Z[(int64_t)f * k + c];
+      z[f] = v;
+      n0 += v * v;
+    }
+    n0 = block_sum(n0, red);
+    for (int pass = 0; pass < 2; ++pass) {
+      __syncthreads();
+      if (tid < c) {  // r_p = Q[:, p] . z
+        float s = 0.f;
+        for (int f = 0; f < F; ++f) s = fmaf(Q[(int64_t)f * k + tid], z[f], s);
+        rc[tid] = s;
+      }
+      __syncthreads();
+      for (int f = tid; f < F; f += kThreads) {  // z -= Q[:, :c] r
+        float s = z[f];
+        for (int q = 0; q < c; ++q) s = fmaf(-Q[(int64_t)f * k + q], rc[q], s);
+        z[f] = s;
+      }
+    }
+    __syncthreads();
+    float n1 = 0.f;
+    for (int f = tid; f < F; f += kThreads) n1 += z[f] * z[f];
+    n1 = block_sum(n1, red);
+    const float inv = (n1 > 1e-12f * n0 && n1 > 0.f) ? rsqrtf(n1) : 0.f;
+    for (int f = tid; f < F; f += kThreads) Q[(int64_t)f * k + c] = z[f] * inv;
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ 3. Jacobi on B
+
+// Eigenpairs of the symmetric k x k matrix B by cyclic Jacobi in LDS (round-robin
+// ordering: k/2 disjoint rotations per step, k - 1 steps per sweep, sweeps until the
+// off-diagonal squared mass is below 1e-10 of the total, at most 30; fp32 rounding
+// keeps it near (k eps)^2 of the total, below that bound).  Writes the eigenvectors
+// sorted by decreasing eigenvalue to E (k x k, column c = c-th) and the eigenvalues to
+// lambda.
+__global__ __launch_bounds__(kThreads) void jacobi_eig(FormArgs P) {
+  const WsLayout W = ws_layout(P.F, P.k);
+  float* base = P.ws + (int64_t)blockIdx.x * W.stride;
+  const int k = P.k, tid = threadIdx.x;
+  __shared__ float A[kMaxK][kMaxK + 1];
+  __shared__ float V[kMaxK][kMaxK + 1];
+  __shared__ float cs[kMaxK / 2], sn[kMaxK / 2];
+  __shared__ int pp[kMaxK / 2], qq[kMaxK / 2];
+  __shared__ float red[4];
+  __shared__ int rank_of[kMaxK];
+  for (int e = tid; e < k * k; e += kThreads) {
+    const int i = e / k, j = e % k;
+    // symmetrize: B = Q^T G Q is symmetric up to rounding
+    A[i][j] = 0.5f * (base[W.B + (int64_t)i * k + j] + base[W.B + (int64_t)j * k + i]);
+    V[i][j] = i == j ? 1.f : 0.f;
+  }
+  __syncthreads();
+  const int half = k / 2;
+  for (int sweep = 0; sweep < 30; ++sweep) {
+    float off = 0.f, tot = 0.f;
+    for (int e = tid; e < k * k; e += kThreads) {
+      const int i = e / k, j = e % k;
+      const float v = A[i][j] * A[i][j];
+      tot += v;
+      if (i != j) off += v;
+    }
+    off = block_sum(off, red);
+    tot = block_sum(tot, red);
+    if (!(off > 1e-10f * tot) || tot == 0.f) break;
+    for (int step = 0; step < k - 1; ++step) {
+      // Round-robin pairs: player 0 fixed, the others rotate by `step`.
+      if (tid < half) {
+        int a = tid == 0 ? 0 : 1 + (tid - 1 + step) % (k - 1);
+        int b = 1 + (k - 2 - tid + step) % (k - 1);
+        if (a > b) {
+          const int t = a;
+          a = b;
+          b = t;
+        }
+        pp[tid] = a;
+        qq[tid] = b;
+        const float apq = A[a][b];
+        float c = 1.f, s = 0.f;
+        if (apq != 0.f) {
+          const float theta = (A[b][b] - A[a][a]) / (2.f * apq);
+          const float t = copysignf(1.f, theta) / (fabsf(theta) + sqrtf(fmaf(theta, theta, 1.f)));
+          c = rsqrtf(fmaf(t, t, 1.f));
+          s = t * c;
+        }
+        cs[tid] = c;
+        sn[tid] = s;
+      }
+      __syncthreads();
+      // rows p, q of A
+      for (int e = tid; e < half * k; e += kThreads) {
+        const int r = e / k, j = e % k;
+        const int p = pp[r], q = qq[r];
+        const float c = cs[r], s = sn[r];
+        const float ap = A[p][j], aq = A[q][j];
+        A[p][j] = c * ap - s * aq;
+        A[q][j] = s * ap + c * aq;
+      }
+      __syncthreads();
+      // columns p, q of A and of V
+      for (int e = tid; e < half * k; e += kThreads) {
+        const int r = e / k, i = e % k;
+        const int p = pp[r], q = qq[r];
+        const float c = cs[r], s = sn[r];
+        const float ap = A[i][p], aq = A[i][q];
+        A[i][p] = c * ap - s * aq;
+        A[i][q] = s * ap + c * aq;
+        const float vp = V[i][p], vq = V[i][q];
+        V[i][p] = c * vp - s * vq;
+        V[i][q] = s * vp + c * vq;
+      }
+      __syncthreads();
+    }
+  }
+  // Sort by decreasing eigenvalue (ties by index).
+  for (int i = tid; i < k; i += kThreads) {
+    const float li = A[i][i];
+    int r = 0;
+    for (int j = 0; j < k; ++j) {
+      const float lj = A[j][j];
+      r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+    }
+    rank_of[i] = r;
+  }
+  __syncthreads();
+  for (int e = tid; e < k * k; e += kThreads) {
+    const int i = e / k, j = e % k;  // V[i][j]: component i of eigenvector j
+    base[W.E + (int64_t)i * k + rank_of[j]] = V[i][j];
+  }
+  for (int j = tid; j < k; j += kThreads) base[W.lam + rank_of[j]] = A[j][j];
+}
+
+// ------------------------------------------------------------------ 4. outputs
+
+// V_m (bf16, [F][m] of this layer and chunk) from Z's first m columns, where the
+// caller put Q E; s = sqrt(max(lambda, 0)).
+__global__ __launch_bounds__(kThreads) void write_v(FormArgs P, int64_t p0) {
+  const WsLayout W = ws_layout(P.F, P.k);
+  const float* base = P.ws + (int64_t)blockIdx.y * W.stride;
+  const int64_t p = p0 + blockIdx.y;
+  uint16_t* Vo = P.V_out + p * (int64_t)P.F * P.m;
+  for (int e = blockIdx.x * kThreads + threadIdx.x; e < P.F * P.m; e += gridDim.x * kThreads) {
+    const int f = e / P.m, c = e % P.m;
+    Vo[e] = f2bf16(c < P.k ? base[W.Z + (int64_t)f * P.k + c] : 0.f);
+  }
+  if (blockIdx.x == 0 && P.sigma_out != nullptr)
+    for (int c = threadIdx.x; c < P.m; c += kThreads)
+      P.sigma_out[p * P.m + c] = c < P.k ? sqrtf(fmaxf(base[W.lam + c], 0.f)) : 0.f;
+}
+
+// U_m = Delta V_m for the chunk's tokens: 64 tokens per workgroup (blockIdx.x), each
+// thread 4 tokens x 4 of the m columns; V_m (fp32, in Z) and Delta rows staged in LDS
+// 16 features at a time.  Rounded to bf16 into U [layer][t][m].
+__global__ __launch_bounds__(kThreads) void write_u(FormArgs P, int64_t p0) {
+  const WsLayout W = ws_layout(P.F, P.k);
+  const float* Vm = P.ws + (int64_t)blockIdx.y * W.stride + W.Z;
+  const int64_t p = p0 + blockIdx.y;
+  const int64_t layer = p / P.num_chunks;
+  const int j = (int)(p - layer * P.num_chunks);
+  const int64_t a = min(max(P.offsets[j], (int64_t)0), P.total_tokens);
+  const int64_t b = min(max(P.offsets[j + 1], a), P.total_tokens);
+  const int64_t t0 = a + (int64_t)blockIdx.x * 64;
+  if (t0 >= b) return;
+  const uint16_t* D = P.delta + layer * P.total_tokens * P.F;
+  uint16_t* Uo = P.U_out + layer * P.total_tokens * P.m;
+  __shared__ float sD[16][64 + 4];
+  __shared__ float sV[16][kMaxK + 4];
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int k = P.k, m = P.m;
+  for (int c0 = 0; c0 < m; c0 += 64) {
+    float acc[4][4] = {};
+    for (int f0 = 0; f0 < P.F; f0 += 16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int idx = tid + kThreads * q;
+        const int r = idx >> 4, ff = idx & 15;  // token r, feature ff
+        const int64_t t = t0 + r;
+        sD[ff][r] = (t < b) ? bf16f(D[t * P.F + f0 + ff]) : 0.f;
+        const int vf = idx >> 6, vc = idx & 63;  // feature vf, column vc
+        sV[vf][vc] = (c0 + vc < m && c0 + vc < k) ? Vm[(int64_t)(f0 + vf) * k + c0 + vc] : 0.f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ff = 0; ff < 16; ++ff) {
+        float dv[4], vv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dv[i] = sD[ff][ty * 4 + i];
+          vv[i] = sV[ff][tx * 4 + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) acc[i][jj] = fmaf(dv[i], vv[jj], acc[i][jj]);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t t = t0 + ty * 4 + i;
+        const int c = c0 + tx * 4 + jj;
+        if (t < b && c < m) Uo[t * m + c] = f2bf16(acc[i][jj]);
+      }
+  }
+}
+
+}  // namespace
+
+int64_t form_workspace_floats(int F, int k) { return ws_layout(F, k).stride; }
+
+// One channel's problems [p0, p0 + count) (problem = layer * num_chunks + chunk), with
+// the workspace holding `count` problems.
+hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream_t s) {
+  const WsLayout W = ws_layout(P.F, P.k);
+  const int F = P.F, k = P.k;
+  const int nt = F / 64;
+  const dim3 blk(kThreads);
+  hipLaunchKernelGGL(gram_tiles, dim3(nt * (nt + 1) / 2, count), blk, 0, s, P, p0);
+  hipLaunchKernelGGL(init_start, dim3((F * k + kThreads - 1) / kThreads, count), blk, 0, s, P);
+  const dim3 gFk((k + 63) / 64, (F + 63) / 64, count);
+  const dim3 gkk((k + 63) / 64, (k + 63) / 64, count);
+  // Z = G Q, Q = orth(Z), `iters` + 1 times (the first from the random start).
+  for (int it = 0; it <= P.iters; ++it) {
+    hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, W.G, F, W.Q, k, W.Z, k, F, k, F);
+    hipLaunchKernelGGL(orthonormalize, dim3(count), blk, 0, s, P);
+  }
+  // Rayleigh-Ritz: Z = G Q, B = Q^T Z, eigenpairs of B, then Z = Q E (V_m in its first
+  // m columns).
+  hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, W.G, F, W.Q, k, W.Z, k, F, k, F);
+  hipLaunchKernelGGL((gemm_ws<true>), gkk, blk, 0, s, P, W.Q, k, W.Z, k, W.B, k, k, k, F);
+  hipLaunchKernelGGL(jacobi_eig, dim3(count), blk, 0, s, P);
+  hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, W.Q, k, W.E, k, W.Z, k, F, k, k);
+  hipLaunchKernelGGL(write_v, dim3((F * P.m + kThreads - 1) / kThreads, count), blk, 0, s, P, p0);
+  const int64_t ttiles = (P.total_tokens + 63) / 64;
+  hipLaunchKernelGGL(write_u, dim3((unsigned)ttiles, count), blk, 0, s, P, p0);
+  return hipGetLastError();
+}
+
+}  // namespace kamera

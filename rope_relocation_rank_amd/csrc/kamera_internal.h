@@ -55,6 +55,27 @@ struct CommonArgs {
   int32_t out_page_shift;
 };
 
+// Patch formation for one channel: top-m factors of each (layer, chunk) deficit.
+struct FormArgs {
+  const uint16_t* delta;    // [layers][total_tokens][F] bf16
+  const int64_t* offsets;   // [num_chunks + 1]
+  float* ws;                // workspace of the current batch
+  uint16_t* U_out;          // [layers][total_tokens][m] bf16
+  uint16_t* V_out;          // [layers][num_chunks][F][m] bf16
+  float* sigma_out;         // [layers][num_chunks][m] or nullptr
+  int64_t total_tokens;
+  int32_t num_chunks;
+  int32_t F;                // feature width, a multiple of 64, at most 1024
+  int32_t k;                // subspace width: min(m + 16, F, 128), even
+  int32_t m;
+  int32_t iters;            // subspace iterations after the first
+};
+
+// Floats of workspace one problem needs.
+int64_t form_workspace_floats(int F, int k);
+// Problems [p0, p0 + count) of one channel (problem = layer * num_chunks + chunk).
+hipError_t launch_form_batch(const FormArgs& a, int64_t p0, int count, hipStream_t s);
+
 // Rotation only, bf16, 16-byte accesses: rope_dim in {16, 32, 64, 128}.
 // `unroll` row groups per wavefront (2 or 4).
 hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unroll,

@@ -25,7 +25,9 @@ KAMERA_MAX_RANK = 256
 KERNEL_NAMES = {0: "none", 1: "rotate", 2: "rotate+patch mfma", 3: "generic"}
 
 EXPORTED = ["kamera_relocate", "kamera_relocate_patch", "kamera_recall_patch", "kamera_plan",
-            "kamera_recall_plan", "kamera_status_str", "kamera_last_error", "kamera_abi_version"]
+            "kamera_recall_plan", "kamera_form_workspace", "kamera_form_patch",
+            "kamera_status_str", "kamera_last_error", "kamera_abi_version"]
+KAMERA_FORM_MAX_RANK = 112
 
 
 class kamera_channel(C.Structure):
@@ -52,6 +54,13 @@ class kamera_chunks(C.Structure):
 class kamera_patch(C.Structure):
     _fields_ = [("rank", C.c_int32), ("reserved0", C.c_int32),
                 ("U", C.c_void_p * 2), ("V", C.c_void_p * 2)]
+
+
+class kamera_form_desc(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("num_layers", C.c_int32), ("num_channels", C.c_int32),
+                ("rank", C.c_int32), ("width", C.c_int32 * 2), ("iterations", C.c_int32),
+                ("reserved0", C.c_int32), ("delta", C.c_void_p * 2), ("U", C.c_void_p * 2),
+                ("V", C.c_void_p * 2), ("sigma", C.c_void_p * 2)]
 
 
 class kamera_plan_info(C.Structure):
@@ -93,6 +102,12 @@ def lib():
         L.kamera_recall_plan.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_kv_desc),
                                          C.POINTER(kamera_chunks), C.POINTER(kamera_patch),
                                          C.POINTER(kamera_plan_info)]
+        L.kamera_form_workspace.restype = C.c_int
+        L.kamera_form_workspace.argtypes = [C.POINTER(kamera_form_desc), C.POINTER(kamera_chunks),
+                                            C.POINTER(C.c_int64)]
+        L.kamera_form_patch.restype = C.c_int
+        L.kamera_form_patch.argtypes = [C.POINTER(kamera_form_desc), C.POINTER(kamera_chunks),
+                                        C.c_void_p, C.c_int64, C.c_void_p]
         L.kamera_status_str.restype = C.c_char_p
         L.kamera_status_str.argtypes = [C.c_int]
         L.kamera_last_error.restype = C.c_char_p
@@ -239,3 +254,32 @@ def recall_patch(src: kamera_kv_desc, dst: kamera_kv_desc, chunks: kamera_chunks
     """Enqueue a recall (out of place) on `stream` (default: torch's current stream)."""
     s = current_stream() if stream is None else stream
     check(kamera_recall_patch(src, dst, chunks, patch, s))
+
+
+def form_desc(deltas, U, V, *, num_layers: int, rank: int, sigma=None,
+              iterations: int = 0) -> kamera_form_desc:
+    """Patch-formation descriptor over torch tensors: deltas [L][T][F] bf16 per channel,
+    U [L][T][m], V [L][n][F][m] (bf16) and optional sigma [L][n][m] (fp32) outputs."""
+    d = kamera_form_desc()
+    d.dtype, d.num_layers, d.num_channels, d.rank = KAMERA_BF16, num_layers, len(deltas), rank
+    d.iterations, d.reserved0 = iterations, 0
+    for c, t in enumerate(deltas):
+        d.width[c] = int(t.shape[-1])
+        d.delta[c] = t.data_ptr()
+        d.U[c] = U[c].data_ptr()
+        d.V[c] = V[c].data_ptr()
+        d.sigma[c] = None if sigma is None else sigma[c].data_ptr()
+    return d
+
+
+def kamera_form_workspace(desc, chunks):
+    n = C.c_int64(0)
+    st = lib().kamera_form_workspace(_ref(desc), _ref(chunks), C.byref(n))
+    return st, n.value
+
+
+def form_patch(desc: kamera_form_desc, chunks: kamera_chunks, workspace, stream=None) -> None:
+    """Enqueue patch formation; `workspace` is a torch uint8 tensor (256-byte aligned)."""
+    s = current_stream() if stream is None else stream
+    check(lib().kamera_form_patch(C.byref(desc), C.byref(chunks), workspace.data_ptr(),
+                                  workspace.numel(), s))

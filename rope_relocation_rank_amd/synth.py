@@ -367,6 +367,44 @@ def make_recall_inputs(w: Workload, rank: int, device="cpu", pass_id: int = 0) -
     return r
 
 
+# ------------------------------------------------------------------ patch formation input
+
+KIND_DEFICIT = 5
+
+
+def make_deficit(w: Workload, device="cpu", directions: int = 32, decay: float = 0.85,
+                 rms: float = 0.1, noise: float = 0.005) -> list:
+    """Synthetic reuse deficits Delta [L][T][F] (one bf16 tensor per channel): per layer
+    and chunk, sum_k s_k a_k b_k^T over `directions` feature directions plus N(0, noise^2)
+    entries, with s_k falling geometrically by `decay` and the signal scaled to `rms`
+    per entry.  The Kamera summary (section 3) reports the deficit's energy concentrated
+    in about 32 feature directions; a_k and b_k are Gaussian columns scaled to unit
+    expected norm (nearly orthonormal for T, F >> directions)."""
+    import torch
+    st = structure(w)
+    T = st.total_tokens
+    out = []
+    for c, F in enumerate(feature_width(w)):
+        buf = torch.zeros((w.layers, T, F), dtype=torch.bfloat16, device=device)
+        for l in range(w.layers):
+            g = torch.Generator(device=device)
+            g.manual_seed(seed_of(w.wid, KIND_DEFICIT, l, c))
+            for j in range(st.num_chunks):
+                a, b = int(st.offsets[j]), int(st.offsets[j + 1])
+                Tj = b - a
+                if Tj == 0:
+                    continue
+                r = min(directions, Tj, F)
+                s = decay ** torch.arange(r, dtype=torch.float32, device=device)
+                s *= rms * math.sqrt(Tj * F) / float(torch.linalg.vector_norm(s))
+                A = torch.randn((Tj, r), generator=g, device=device) / math.sqrt(Tj)
+                B = torch.randn((F, r), generator=g, device=device) / math.sqrt(F)
+                d = (A * s) @ B.T + noise * torch.randn((Tj, F), generator=g, device=device)
+                buf[l, a:b] = d.to(torch.bfloat16)
+        out.append(buf)
+    return out
+
+
 # ------------------------------------------------------------------ accounting
 
 def algorithmic_bytes(w: Workload, rank: int, total_tokens: int | None = None,
