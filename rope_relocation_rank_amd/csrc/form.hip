@@ -12,8 +12,8 @@
 //   1. G = Delta^T Delta (F x F, fp32) on MFMA 16x16x32 bf16: a dense contraction over
 //      the chunk's tokens, upper-triangular 64 x 64 tiles, mirrored.
 //   2. Subspace iteration on G with k = m + 16 columns (at most 128, at most F):
-//      Q <- orth(G Q) from a fixed pseudo-random start, `iters` times (fp32 tiled GEMM,
-//      classical Gram-Schmidt with one reorthogonalization per column).
+//      Q <- orth(G Q) from a fixed pseudo-random start, `iters` times (fp32 tiled GEMM;
+//      orth = Cholesky QR twice, Gram and Cholesky in fp64).
 //   3. Rayleigh-Ritz: B = Q^T G Q (k x k), eigenpairs of B by cyclic Jacobi in LDS,
 //      sorted; V_m = Q E[:, :m], s_i = sqrt(lambda_i).
 //   4. U_m = Delta V_m (= U_m diag(s) of the SVD), rounded to bf16 with V_m.
@@ -229,47 +229,94 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-// Q = orth(Z): classical Gram-Schmidt with one reorthogonalization per column, column
-// by column; Z (F x k) is read, Q (F x k) written.  A column whose remainder falls
-// below 1e-6 of its norm (a direction the chunk does not span) becomes zero.
-__global__ __launch_bounds__(kThreads) void orthonormalize(FormArgs P) {
+// W = X^T X in fp64 for the F x k matrix X (Z or Q) of every problem: one 32 x 32 tile
+// of W per workgroup, 16 rows of X staged per step, 2 x 2 outputs per thread.  W
+// occupies the B and E regions of the workspace (2 k^2 floats = k^2 doubles).
+__global__ __launch_bounds__(kThreads) void gram64(FormArgs P, int64_t x_off) {
+  const WsLayout W = ws_layout(P.F, P.k);
+  float* base = P.ws + (int64_t)blockIdx.z * W.stride;
+  const float* X = base + x_off;
+  double* Wd = reinterpret_cast<double*>(base + W.B);
+  const int k = P.k, tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+  __shared__ float si[16][33], sj[16][33];
+  double acc[2][2] = {};
+  for (int f0 = 0; f0 < P.F; f0 += 16) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + kThreads * q;
+      const int r = idx >> 5, c = idx & 31;
+      si[r][c] = (i0 + c < k) ? X[(int64_t)(f0 + r) * k + i0 + c] : 0.f;
+      sj[r][c] = (j0 + c < k) ? X[(int64_t)(f0 + r) * k + j0 + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = fma((double)si[r][2 * ty + a], (double)sj[r][2 * tx + b], acc[a][b]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int i = i0 + 2 * ty + a, jj = j0 + 2 * tx + b;
+      if (i < k && jj < k) Wd[(int64_t)i * k + jj] = acc[a][b];
+    }
+}
+
+// R^-1 of the Cholesky QR of one problem: W = X^T X (fp64, from gram64) is factored
+// W = L L^T column by column in LDS, in fp64; a column whose pivot falls below 1e-12 of
+// its diagonal (its remainder after projection is under 1e-6 of its norm: a direction
+// the chunk does not span) is dropped.  L is then inverted in place (columns from the
+// last, each from the already inverted trailing block), and R^-1 = L^-T is written as
+// fp32 k x k into the B region, so that X R^-1 has orthonormal (or zero) columns.
+__global__ __launch_bounds__(kThreads) void chol_rinv(FormArgs P) {
   const WsLayout W = ws_layout(P.F, P.k);
   float* base = P.ws + (int64_t)blockIdx.x * W.stride;
-  const float* Z = base + W.Z;
-  float* Q = base + W.Q;
-  const int F = P.F, k = P.k, tid = threadIdx.x;
-  __shared__ float z[1024];
-  __shared__ float rc[kMaxK];
-  __shared__ float red[4];
-  for (int c = 0; c < k; ++c) {
-    float n0 = 0.f;
-    for (int f = tid; f < F; f += kThreads) {
-      const float v = Z[(int64_t)f * k + c];
-      z[f] = v;
-      n0 += v * v;
-    }
-    n0 = block_sum(n0, red);
-    for (int pass = 0; pass < 2; ++pass) {
-      __syncthreads();
-      if (tid < c) {  // r_p = Q[:, p] . z
-        float s = 0.f;
-        for (int f = 0; f < F; ++f) s = fmaf(Q[(int64_t)f * k + tid], z[f], s);
-        rc[tid] = s;
-      }
-      __syncthreads();
-      for (int f = tid; f < F; f += kThreads) {  // z -= Q[:, :c] r
-        float s = z[f];
-        for (int q = 0; q < c; ++q) s = fmaf(-Q[(int64_t)f * k + q], rc[q], s);
-        z[f] = s;
-      }
+  const double* Wd = reinterpret_cast<const double*>(base + W.B);
+  float* Rinv = base + W.B;
+  const int k = P.k, tid = threadIdx.x;
+  __shared__ double L[kMaxK][kMaxK + 1];
+  __shared__ double col[kMaxK];
+  for (int e = tid; e < k * k; e += kThreads) L[e / k][e % k] = Wd[e];
+  __syncthreads();
+  for (int i = tid; i < k; i += kThreads) col[i] = L[i][i];  // diagonal of W
+  __syncthreads();
+  for (int j = 0; j < k; ++j) {
+    const double d = L[j][j];
+    const bool keep = d > 1e-12 * col[j] && d > 0.0;
+    const double inv = keep ? 1.0 / sqrt(d) : 0.0;
+    __syncthreads();
+    for (int i = j + 1 + tid; i < k; i += kThreads) L[i][j] *= inv;
+    if (tid == 0) L[j][j] = keep ? sqrt(d) : 0.0;
+    __syncthreads();
+    const int n = k - j - 1;  // trailing update: L[i][c] -= L[i][j] L[c][j], j < c <= i
+    for (int e = tid; e < n * n; e += kThreads) {
+      const int ii = j + 1 + e / n, cc = j + 1 + e % n;
+      if (cc <= ii) L[ii][cc] -= L[ii][j] * L[cc][j];
     }
     __syncthreads();
-    float n1 = 0.f;
-    for (int f = tid; f < F; f += kThreads) n1 += z[f] * z[f];
-    n1 = block_sum(n1, red);
-    const float inv = (n1 > 1e-12f * n0 && n1 > 0.f) ? rsqrtf(n1) : 0.f;
-    for (int f = tid; f < F; f += kThreads) Q[(int64_t)f * k + c] = z[f] * inv;
+  }
+  // In-place inverse of the lower-triangular L (dropped columns stay zero).
+  for (int j = k - 1; j >= 0; --j) {
+    const double djj = L[j][j] > 0.0 ? 1.0 / L[j][j] : 0.0;
+    for (int i = j + 1 + tid; i < k; i += kThreads) {  // -(Linv[i][j+1..i] . L[j+1..i][j]) djj
+      double s = 0.0;
+      for (int p2 = j + 1; p2 <= i; ++p2) s += L[i][p2] * L[p2][j];
+      col[i] = -s * djj;
+    }
     __syncthreads();
+    for (int i = j + 1 + tid; i < k; i += kThreads) L[i][j] = col[i];
+    if (tid == 0) L[j][j] = djj;
+    __syncthreads();
+  }
+  for (int e = tid; e < k * k; e += kThreads) {  // R^-1[i][j] = Linv[j][i]
+    const int i = e / k, jj = e % k;
+    Rinv[e] = jj >= i ? (float)L[jj][i] : 0.f;
   }
 }
 
@@ -379,16 +426,16 @@ __global__ __launch_bounds__(kThreads) void jacobi_eig(FormArgs P) {
 
 // ------------------------------------------------------------------ 4. outputs
 
-// V_m (bf16, [F][m] of this layer and chunk) from Z's first m columns, where the
-// caller put Q E; s = sqrt(max(lambda, 0)).
-__global__ __launch_bounds__(kThreads) void write_v(FormArgs P, int64_t p0) {
+// V_m (bf16, [F][m] of this layer and chunk) from the first m columns of the F x k
+// array at v_off, where the caller put Q E; s = sqrt(max(lambda, 0)).
+__global__ __launch_bounds__(kThreads) void write_v(FormArgs P, int64_t p0, int64_t v_off) {
   const WsLayout W = ws_layout(P.F, P.k);
   const float* base = P.ws + (int64_t)blockIdx.y * W.stride;
   const int64_t p = p0 + blockIdx.y;
   uint16_t* Vo = P.V_out + p * (int64_t)P.F * P.m;
   for (int e = blockIdx.x * kThreads + threadIdx.x; e < P.F * P.m; e += gridDim.x * kThreads) {
     const int f = e / P.m, c = e % P.m;
-    Vo[e] = f2bf16(c < P.k ? base[W.Z + (int64_t)f * P.k + c] : 0.f);
+    Vo[e] = f2bf16(c < P.k ? base[v_off + (int64_t)f * P.k + c] : 0.f);
   }
   if (blockIdx.x == 0 && P.sigma_out != nullptr)
     for (int c = threadIdx.x; c < P.m; c += kThreads)
@@ -396,11 +443,11 @@ __global__ __launch_bounds__(kThreads) void write_v(FormArgs P, int64_t p0) {
 }
 
 // U_m = Delta V_m for the chunk's tokens: 64 tokens per workgroup (blockIdx.x), each
-// thread 4 tokens x 4 of the m columns; V_m (fp32, in Z) and Delta rows staged in LDS
-// 16 features at a time.  Rounded to bf16 into U [layer][t][m].
-__global__ __launch_bounds__(kThreads) void write_u(FormArgs P, int64_t p0) {
+// thread 4 tokens x 4 of the m columns; V_m (fp32, F x k at v_off) and Delta rows
+// staged in LDS 16 features at a time.  Rounded to bf16 into U [layer][t][m].
+__global__ __launch_bounds__(kThreads) void write_u(FormArgs P, int64_t p0, int64_t v_off) {
   const WsLayout W = ws_layout(P.F, P.k);
-  const float* Vm = P.ws + (int64_t)blockIdx.y * W.stride + W.Z;
+  const float* Vm = P.ws + (int64_t)blockIdx.y * W.stride + v_off;
   const int64_t p = p0 + blockIdx.y;
   const int64_t layer = p / P.num_chunks;
   const int j = (int)(p - layer * P.num_chunks);
@@ -468,20 +515,37 @@ hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream
   hipLaunchKernelGGL(init_start, dim3((F * k + kThreads - 1) / kThreads, count), blk, 0, s, P);
   const dim3 gFk((k + 63) / 64, (F + 63) / 64, count);
   const dim3 gkk((k + 63) / 64, (k + 63) / 64, count);
-  // Z = G Q, Q = orth(Z), `iters` + 1 times (the first from the random start).
+  const dim3 g32((k + 31) / 32, (k + 31) / 32, count);
+  // Z = G Q, Q = orth(Z), `iters` + 1 times (the first from the random start).  orth is
+  // Cholesky QR; the last basis gets a second pass, which restores the orthogonality
+  // lost in fp32 (the iteration itself only needs the columns kept apart).  The basis
+  // and the scratch columns alternate between the Q and Z regions.
+  int64_t basis = W.Q, tmp = W.Z;
+  auto cholqr = [&](int64_t from, int64_t to) {  // to = from R^-1
+    hipLaunchKernelGGL(gram64, g32, blk, 0, s, P, from);
+    hipLaunchKernelGGL(chol_rinv, dim3(count), blk, 0, s, P);
+    hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, from, k, W.B, k, to, k, F, k, k);
+  };
   for (int it = 0; it <= P.iters; ++it) {
-    hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, W.G, F, W.Q, k, W.Z, k, F, k, F);
-    hipLaunchKernelGGL(orthonormalize, dim3(count), blk, 0, s, P);
+    hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, W.G, F, basis, k, tmp, k, F, k, F);
+    cholqr(tmp, basis);
+    if (it == P.iters) {  // the basis Rayleigh-Ritz uses is orthonormalized twice
+      cholqr(basis, tmp);
+      const int64_t t = basis;
+      basis = tmp;
+      tmp = t;
+    }
   }
-  // Rayleigh-Ritz: Z = G Q, B = Q^T Z, eigenpairs of B, then Z = Q E (V_m in its first
-  // m columns).
-  hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, W.G, F, W.Q, k, W.Z, k, F, k, F);
-  hipLaunchKernelGGL((gemm_ws<true>), gkk, blk, 0, s, P, W.Q, k, W.Z, k, W.B, k, k, k, F);
+  // Rayleigh-Ritz: tmp = G basis, B = basis^T tmp, eigenpairs of B, then tmp = basis E
+  // (V_m in its first m columns).
+  hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, W.G, F, basis, k, tmp, k, F, k, F);
+  hipLaunchKernelGGL((gemm_ws<true>), gkk, blk, 0, s, P, basis, k, tmp, k, W.B, k, k, k, F);
   hipLaunchKernelGGL(jacobi_eig, dim3(count), blk, 0, s, P);
-  hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, W.Q, k, W.E, k, W.Z, k, F, k, k);
-  hipLaunchKernelGGL(write_v, dim3((F * P.m + kThreads - 1) / kThreads, count), blk, 0, s, P, p0);
+  hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, basis, k, W.E, k, tmp, k, F, k, k);
+  hipLaunchKernelGGL(write_v, dim3((F * P.m + kThreads - 1) / kThreads, count), blk, 0, s, P, p0,
+                     tmp);
   const int64_t ttiles = (P.total_tokens + 63) / 64;
-  hipLaunchKernelGGL(write_u, dim3((unsigned)ttiles, count), blk, 0, s, P, p0);
+  hipLaunchKernelGGL(write_u, dim3((unsigned)ttiles, count), blk, 0, s, P, p0, tmp);
   return hipGetLastError();
 }
 
