@@ -26,6 +26,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -61,6 +63,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=1024)
+    ap.add_argument("--form", action="store_true",
+                    help="measure patch formation (kamera_form_patch) on the workload's shape")
     return ap.parse_args()
 
 
@@ -79,6 +83,8 @@ def main():
     K.lib()
     dev = torch.device("cuda:0")
     w = synth.get(args.workload)
+    if args.form:
+        return bench_form(args, w, dev)
     ranks = w.rank_passes
     dominant = max(range(len(ranks)), key=lambda i: synth.algorithmic_bytes(w, ranks[i]))
     bytes_pass = [synth.algorithmic_bytes(w, r) for r in ranks]
@@ -231,6 +237,120 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_form(args, w, dev):
+    """Patch formation on the workload's shape: synthetic deficits (32 dominant feature
+    directions), rank = the workload's patch rank.  value = (layer, chunk, channel)
+    problems formed per second over whole kamera_form_patch calls; roofline = the Gram
+    stage (kamera_form_gram) on MFMA, timed with HIP events around each launch."""
+    import torch
+
+    from rope_relocation_rank_amd import kamera as K
+    from rope_relocation_rank_amd import synth
+
+    m = w.rank
+    st = synth.structure(w)
+    T, n, L = st.total_tokens, st.num_chunks, w.layers
+    print(f"[bench] form {w.key}: rank {m}, {L} layers x {n} chunks", file=sys.stderr, flush=True)
+    deltas = synth.make_deficit(w, device=dev)
+    Fs = [d.shape[-1] for d in deltas]
+    U = [torch.zeros((L, T, m), dtype=torch.bfloat16, device=dev) for _ in Fs]
+    V = [torch.zeros((L, n, F, m), dtype=torch.bfloat16, device=dev) for F in Fs]
+    offs = torch.as_tensor(st.offsets, device=dev)
+    ch = K.chunks_desc(offs, torch.zeros(n, dtype=torch.int64, device=dev), T)
+    d = K.form_desc(deltas, U, V, num_layers=L, rank=m)
+    K.check(K.kamera_form_workspace(d, ch)[0])
+    ws = torch.empty(K.kamera_form_workspace(d, ch)[1], dtype=torch.uint8, device=dev)
+    G = [torch.empty((L, n, F, F), dtype=torch.float32, device=dev) for F in Fs]
+    stream = torch.cuda.current_stream(dev)
+    steps, warm = max(1, min(args.steps, 50)), max(1, min(args.warmup, 5))
+    for _ in range(warm):
+        K.form_patch(d, ch, ws)
+        K.form_gram(d, ch, G)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    gv = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        K.form_patch(d, ch, ws)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for i in range(steps):
+        gv[i][0].record(stream)
+        K.form_gram(d, ch, G)
+        gv[i][1].record(stream)
+    torch.cuda.synchronize()
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    gram_ms = sum(a.elapsed_time(b) for a, b in gv) / steps
+    problems = L * n * len(Fs)
+    # Algorithmic Gram flops: 2 T_j per entry of the upper triangle (the matrix is
+    # symmetric), over every layer, chunk and channel.
+    lens = np.diff(st.offsets)
+    gram_flops = sum(int(L * (2 * lens * F * (F + 1) // 2).sum()) for F in Fs)
+    achieved = gram_flops / (gram_ms * 1e-3) / 1e12
+    cpu = None if args.no_cpu_baseline else cpu_baseline_form(w, m, args.cpu_seconds)
+    line = {
+        "metric": "patch formation (top-m SVD factors of the deficit): problems per second",
+        "value": round(problems * steps / wall, 3),
+        "unit": "problems/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(wall * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp32 compute",
+        "data": "synthetic",
+        "config": {"workload": w.key + " (patch formation)", "rank": m, "layers": L,
+                   "chunks": n, "tokens": T, "widths": Fs, "problems_per_step": problems,
+                   "parallelism": "single GPU"},
+        "call_ms_events": round(call_ms, 4),
+        "roofline": {"bound": "mfma", "kernel": "gram_tiles", "achieved": round(achieved, 2),
+                     "peak": 2500.0, "unit": "TFLOP/s", "frac": round(achieved / 2500.0, 5),
+                     "traffic": None, "algorithmic_flops_per_launch": gram_flops,
+                     "avg_launch_ms": round(gram_ms, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_form(w, m, seconds: float):
+    """The oracle's exact SVD (numpy LAPACK, fp64) on the host, over as many (layer,
+    chunk, channel) problems of the same deficits as fit in `seconds`."""
+    import torch
+
+    from oracle import patch_form as pf
+    from rope_relocation_rank_amd import synth
+
+    ww = w.with_(layers=1)
+    deltas = synth.make_deficit(ww, device="cpu")
+    st = synth.structure(ww)
+    done, t = 0, 0.0
+    while t < seconds and done < 10000:
+        for d in deltas:
+            x = d[0].float().numpy().astype(np.float64)
+            for j in range(st.num_chunks):
+                a, b = int(st.offsets[j]), int(st.offsets[j + 1])
+                t0 = time.perf_counter()
+                pf.top_m_factors(x[a:b], m)
+                t += time.perf_counter() - t0
+                done += 1
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()
+                     if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = int(torch.get_num_threads())
+    return {"value": round(done / t, 3), "unit": "problems/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{done} (layer, chunk, channel) problems of layer 0, exact fp64 SVD; "
+                      f"{t:.1f} s of compute"}
 
 
 def cpu_baseline(w, ranks, seconds: float):

@@ -241,6 +241,14 @@ KAMERA_API kamera_status kamera_form_workspace(const kamera_form_desc* desc,
 KAMERA_API kamera_status kamera_form_patch(const kamera_form_desc* desc, const kamera_chunks* chunks,
                                 void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
+/* The first stage of kamera_form_patch on its own: the Gram matrix
+ * G_j = Delta_j^T Delta_j (fp32 [width][width]) of every layer and chunk of every
+ * channel, a dense contraction over the chunk's tokens on MFMA (bf16 products, fp32
+ * sums).  G[c]: device out [num_layers][num_chunks][width][width] fp32, must not
+ * overlap a deficit.  desc.rank, U, V, sigma and iterations are not read. */
+KAMERA_API kamera_status kamera_form_gram(const kamera_form_desc* desc, const kamera_chunks* chunks,
+                               float* const G[2], hipStream_t stream);
+
 /* Which kernels a call would launch, without launching anything (no HIP call).
  * Fills `out` and returns the status the call itself would return before launching. */
 typedef struct {

@@ -517,14 +517,15 @@ int64_t form_problem_bytes(const kamera_form_desc& d, int c) {
   return 4 * kamera::form_workspace_floats(d.width[c], form_k(d.rank, d.width[c]));
 }
 
-kamera_status validate_form(const kamera_form_desc* d, const kamera_chunks* ch, bool* empty) {
+kamera_status validate_form(const kamera_form_desc* d, const kamera_chunks* ch, bool* empty,
+                            bool gram_only = false) {
   if (!d) return fail(KAMERA_E_NULL, "form descriptor is NULL");
   if (!ch) return fail(KAMERA_E_NULL, "chunks descriptor is NULL");
   if (d->dtype != KAMERA_BF16) return fail(KAMERA_E_UNSUPPORTED, "patch formation takes bf16 only");
   if (d->num_layers < 0) return fail(KAMERA_E_SHAPE, "num_layers %d < 0", d->num_layers);
   if (d->num_channels < 1 || d->num_channels > 2)
     return fail(KAMERA_E_SHAPE, "num_channels %d is not 1 or 2", d->num_channels);
-  if (d->rank < 1 || d->rank > KAMERA_FORM_MAX_RANK)
+  if (!gram_only && (d->rank < 1 || d->rank > KAMERA_FORM_MAX_RANK))
     return fail(KAMERA_E_SHAPE, "rank %d outside [1, %d]", d->rank, KAMERA_FORM_MAX_RANK);
   if (d->iterations < 0 || d->iterations > 64)
     return fail(KAMERA_E_SHAPE, "iterations %d outside [0, 64]", d->iterations);
@@ -539,7 +540,7 @@ kamera_status validate_form(const kamera_form_desc* d, const kamera_chunks* ch, 
     const int F = d->width[c];
     if (F < 64 || F > 1024 || F % 64 != 0)
       return fail(KAMERA_E_SHAPE, "channel %d: width %d is not a multiple of 64 in [64, 1024]", c, F);
-    if (!*empty && (!d->delta[c] || !d->U[c] || !d->V[c]))
+    if (!*empty && (!d->delta[c] || (!gram_only && (!d->U[c] || !d->V[c]))))
       return fail(KAMERA_E_NULL, "channel %d: delta, U and V are required", c);
     if (!aligned(d->delta[c], 16))
       return fail(KAMERA_E_ALIGN, "channel %d: delta not 16-byte aligned", c);
@@ -602,6 +603,7 @@ kamera_status run_form(const kamera_form_desc* d, const kamera_chunks* ch, void*
     a.k = form_k(d->rank, d->width[c]);
     a.m = d->rank;
     a.iters = d->iterations > 0 ? d->iterations : 8;
+    a.num_layers = (int32_t)L;
     const int64_t batch = std::min<int64_t>({(int64_t)kFormBatch, problems,
                                              ws_bytes / form_problem_bytes(*d, c)});
     for (int64_t p0 = 0; p0 < problems; p0 += batch) {
@@ -635,6 +637,37 @@ kamera_status kamera_form_workspace(const kamera_form_desc* desc, const kamera_c
 kamera_status kamera_form_patch(const kamera_form_desc* desc, const kamera_chunks* chunks,
                                 void* workspace, int64_t workspace_bytes, hipStream_t stream) {
   return run_form(desc, chunks, workspace, workspace_bytes, stream);
+}
+
+kamera_status kamera_form_gram(const kamera_form_desc* desc, const kamera_chunks* chunks,
+                               float* const G[2], hipStream_t stream) {
+  g_last_error.clear();
+  bool empty = true;
+  kamera_status st = validate_form(desc, chunks, &empty, true);
+  if (st != KAMERA_OK || empty) return st;
+  if (!G) return fail(KAMERA_E_NULL, "G is NULL");
+  const int64_t L = desc->num_layers, T = chunks->total_tokens, n = chunks->num_chunks;
+  for (int c = 0; c < desc->num_channels; ++c) {
+    const int64_t F = desc->width[c];
+    if (!G[c]) return fail(KAMERA_E_NULL, "G[%d] is NULL", c);
+    if (!aligned(G[c], 4)) return fail(KAMERA_E_ALIGN, "G[%d] not 4-byte aligned", c);
+    for (int f = 0; f < desc->num_channels; ++f)
+      if (overlaps(G[c], L * n * F * F * 4, desc->delta[f], L * T * desc->width[f] * 2))
+        return fail(KAMERA_E_ALIAS, "G[%d] overlaps a deficit", c);
+  }
+  for (int c = 0; c < desc->num_channels; ++c) {
+    kamera::FormArgs a;
+    memset(&a, 0, sizeof a);
+    a.delta = (const uint16_t*)desc->delta[c];
+    a.offsets = chunks->token_offsets;
+    a.total_tokens = T;
+    a.num_chunks = (int32_t)n;
+    a.num_layers = (int32_t)L;
+    a.F = desc->width[c];
+    const hipError_t e = kamera::launch_form_gram(a, G[c], stream);
+    if (e != hipSuccess) return hip_fail(e, "Gram launch");
+  }
+  return KAMERA_OK;
 }
 
 

@@ -63,7 +63,8 @@ __host__ __device__ inline WsLayout ws_layout(int F, int k) {
 // ([feature][token]), so each lane reads the 8 consecutive tokens of one feature that
 // an MFMA operand row holds.  Wave w owns the 32 x 32 quadrant (w >> 1, w & 1): 2 x 2
 // MFMA 16x16x32 tiles.  G[i][j] = sum_t A[i][t] B[t][j] with A = Delta^T, B = Delta.
-__global__ __launch_bounds__(kThreads) void gram_tiles(FormArgs P, int64_t p0) {
+__global__ __launch_bounds__(kThreads) void gram_tiles(FormArgs P, int64_t p0, float* Gbase,
+                                                       int64_t gstride) {
   const int ntile = P.F / 64;
   int rem = blockIdx.x, ti = 0;
   while (rem >= ntile - ti) {
@@ -77,8 +78,7 @@ __global__ __launch_bounds__(kThreads) void gram_tiles(FormArgs P, int64_t p0) {
   // Rows [a, b) of the chunk, kept inside [0, total_tokens) whatever the offsets hold.
   const int64_t a = min(max(P.offsets[j], (int64_t)0), P.total_tokens);
   const int64_t b = min(max(P.offsets[j + 1], a), P.total_tokens);
-  const WsLayout W = ws_layout(P.F, P.k);
-  float* G = P.ws + (int64_t)blockIdx.y * W.stride + W.G;
+  float* G = Gbase + (int64_t)blockIdx.y * gstride;
 
   __shared__ __attribute__((aligned(16))) uint16_t sA[64][40];  // 32 tokens + 8 pad
   __shared__ __attribute__((aligned(16))) uint16_t sB[64][40];
@@ -511,7 +511,8 @@ hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream
   const int F = P.F, k = P.k;
   const int nt = F / 64;
   const dim3 blk(kThreads);
-  hipLaunchKernelGGL(gram_tiles, dim3(nt * (nt + 1) / 2, count), blk, 0, s, P, p0);
+  hipLaunchKernelGGL(gram_tiles, dim3(nt * (nt + 1) / 2, count), blk, 0, s, P, p0, P.ws + W.G,
+                     W.stride);
   hipLaunchKernelGGL(init_start, dim3((F * k + kThreads - 1) / kThreads, count), blk, 0, s, P);
   const dim3 gFk((k + 63) / 64, (F + 63) / 64, count);
   const dim3 gkk((k + 63) / 64, (k + 63) / 64, count);
@@ -546,6 +547,18 @@ hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream
                      tmp);
   const int64_t ttiles = (P.total_tokens + 63) / 64;
   hipLaunchKernelGGL(write_u, dim3((unsigned)ttiles, count), blk, 0, s, P, p0, tmp);
+  return hipGetLastError();
+}
+
+hipError_t launch_form_gram(const FormArgs& P, float* G, hipStream_t s) {
+  const int nt = P.F / 64;
+  const int64_t problems = (int64_t)P.num_layers * P.num_chunks;
+  const int64_t gs = (int64_t)P.F * P.F;
+  for (int64_t p0 = 0; p0 < problems; p0 += 65535) {
+    const int count = (int)min(problems - p0, (int64_t)65535);
+    hipLaunchKernelGGL(gram_tiles, dim3(nt * (nt + 1) / 2, count), dim3(kThreads), 0, s, P, p0,
+                       G + p0 * gs, gs);
+  }
   return hipGetLastError();
 }
 

@@ -69,12 +69,15 @@ struct FormArgs {
   int32_t k;                // subspace width: min(m + 16, F, 128), even
   int32_t m;
   int32_t iters;            // subspace iterations after the first
+  int32_t num_layers;
 };
 
 // Floats of workspace one problem needs.
 int64_t form_workspace_floats(int F, int k);
 // Problems [p0, p0 + count) of one channel (problem = layer * num_chunks + chunk).
 hipError_t launch_form_batch(const FormArgs& a, int64_t p0, int count, hipStream_t s);
+// Gram matrices of every problem of one channel into G [problems][F][F].
+hipError_t launch_form_gram(const FormArgs& a, float* G, hipStream_t s);
 
 // Rotation only, bf16, 16-byte accesses: rope_dim in {16, 32, 64, 128}.
 // `unroll` row groups per wavefront (2 or 4).

@@ -25,7 +25,7 @@ KAMERA_MAX_RANK = 256
 KERNEL_NAMES = {0: "none", 1: "rotate", 2: "rotate+patch mfma", 3: "generic"}
 
 EXPORTED = ["kamera_relocate", "kamera_relocate_patch", "kamera_recall_patch", "kamera_plan",
-            "kamera_recall_plan", "kamera_form_workspace", "kamera_form_patch",
+            "kamera_recall_plan", "kamera_form_workspace", "kamera_form_patch", "kamera_form_gram",
             "kamera_status_str", "kamera_last_error", "kamera_abi_version"]
 KAMERA_FORM_MAX_RANK = 112
 
@@ -108,6 +108,9 @@ def lib():
         L.kamera_form_patch.restype = C.c_int
         L.kamera_form_patch.argtypes = [C.POINTER(kamera_form_desc), C.POINTER(kamera_chunks),
                                         C.c_void_p, C.c_int64, C.c_void_p]
+        L.kamera_form_gram.restype = C.c_int
+        L.kamera_form_gram.argtypes = [C.POINTER(kamera_form_desc), C.POINTER(kamera_chunks),
+                                       C.POINTER(C.c_void_p), C.c_void_p]
         L.kamera_status_str.restype = C.c_char_p
         L.kamera_status_str.argtypes = [C.c_int]
         L.kamera_last_error.restype = C.c_char_p
@@ -283,3 +286,10 @@ def form_patch(desc: kamera_form_desc, chunks: kamera_chunks, workspace, stream=
     s = current_stream() if stream is None else stream
     check(lib().kamera_form_patch(C.byref(desc), C.byref(chunks), workspace.data_ptr(),
                                   workspace.numel(), s))
+
+
+def form_gram(desc: kamera_form_desc, chunks: kamera_chunks, G, stream=None) -> None:
+    """Enqueue the Gram stage: G[c] fp32 tensors [L][n][F][F]."""
+    s = current_stream() if stream is None else stream
+    arr = (C.c_void_p * 2)(*[g.data_ptr() for g in G] + [None] * (2 - len(G)))
+    check(lib().kamera_form_gram(C.byref(desc), C.byref(chunks), arr, s))

@@ -410,3 +410,63 @@ def test_recall_argument_errors():
     src, ch, p = gqa(m=8, T=0, n=0)
     names, info = recall_plan_names(src, recall_dst(), ch, p)
     assert info.launches == 0
+
+
+# ----------------------------------------------------------------- patch formation
+
+def form(L=28, T=4096, F=(512, 512), m=32, n=1, iters=0):
+    d = K.kamera_form_desc()
+    d.dtype, d.num_layers, d.num_channels, d.rank = K.KAMERA_BF16, L, len(F), m
+    d.iterations = iters
+    for c, f in enumerate(F):
+        d.width[c] = f
+        d.delta[c] = FAKE + c * (1 << 36)
+        d.U[c] = FAKE + (1 << 39) + c * (1 << 34)
+        d.V[c] = FAKE + (1 << 39) + (1 << 33) + c * (1 << 34)
+    ch = K.kamera_chunks()
+    ch.num_chunks, ch.total_tokens = n, T
+    ch.token_offsets, ch.delta = FAKE + (3 << 38), 0
+    return d, ch
+
+
+def test_form_workspace_and_errors():
+    d, ch = form()
+    st, nb = K.kamera_form_workspace(d, ch)
+    assert st == K.KAMERA_OK
+    k = 48  # m + 16
+    per = 512 * 512 + 2 * 512 * k + 2 * k * k + k
+    per = -(-per // 64) * 64 * 4
+    assert nb == per * 28  # 28 problems (< 64 per batch)
+    for mutate, status in [
+        (lambda d, ch: setattr(d, "rank", 0), K.KAMERA_E_SHAPE),
+        (lambda d, ch: setattr(d, "rank", K.KAMERA_FORM_MAX_RANK + 1), K.KAMERA_E_SHAPE),
+        (lambda d, ch: d.width.__setitem__(0, 100), K.KAMERA_E_SHAPE),
+        (lambda d, ch: d.width.__setitem__(1, 2048), K.KAMERA_E_SHAPE),
+        (lambda d, ch: setattr(d, "dtype", K.KAMERA_F32), K.KAMERA_E_UNSUPPORTED),
+        (lambda d, ch: d.delta.__setitem__(0, None), K.KAMERA_E_NULL),
+        (lambda d, ch: d.delta.__setitem__(0, FAKE + 8), K.KAMERA_E_ALIGN),
+        (lambda d, ch: setattr(d, "iterations", 65), K.KAMERA_E_SHAPE),
+        (lambda d, ch: setattr(d, "num_channels", 3), K.KAMERA_E_SHAPE),
+    ]:
+        d, ch = form()
+        mutate(d, ch)
+        st, _ = K.kamera_form_workspace(d, ch)
+        assert st == status, (status, K.kamera_last_error())
+
+
+def test_form_patch_checks_before_launch():
+    # Host-checkable errors come back before any HIP call (the pointers are fake).
+    import ctypes as C
+    L_ = K.lib()
+    d, ch = form()
+    # outputs overlapping the deficit
+    d.U[0] = d.delta[0] + 4096
+    st = L_.kamera_form_patch(C.byref(d), C.byref(ch), C.c_void_p(FAKE + (7 << 40)), 1 << 30, None)
+    assert st == K.KAMERA_E_ALIAS
+    d, ch = form()
+    st = L_.kamera_form_patch(C.byref(d), C.byref(ch), None, 1 << 30, None)
+    assert st == K.KAMERA_E_NULL
+    st = L_.kamera_form_patch(C.byref(d), C.byref(ch), C.c_void_p(FAKE + (7 << 40) + 8), 1 << 30, None)
+    assert st == K.KAMERA_E_ALIGN
+    st = L_.kamera_form_patch(C.byref(d), C.byref(ch), C.c_void_p(FAKE + (7 << 40)), 1024, None)
+    assert st == K.KAMERA_E_SHAPE  # workspace too small for one problem

@@ -157,3 +157,30 @@ def test_form_full_size_qwen():
             opt = np.sqrt((s[32:] ** 2).sum())
             assert opt * (1 - 1e-9) <= got <= opt + 2.0 ** -8 * np.linalg.norm(Uo @ Vo.T) + 1e-3 * opt
     print(f"\n[case] form full size qwen ok", flush=True)
+
+
+def test_form_gram_stage():
+    # G_j = Delta_j^T Delta_j on MFMA: bf16 products are exact in fp32, so every entry is
+    # within the fp32 summation bound T_j 2^-24 sum_t |Delta_ti Delta_tj| of the exact sum.
+    w = _w(lens=(100, 0, 37, 300), heads=2)
+    st = synth.structure(w)
+    deltas = synth.make_deficit(w, device=DEV)
+    L, n = w.layers, st.num_chunks
+    Fs = [d.shape[-1] for d in deltas]
+    G = [torch.full((L, n, F, F), float("nan"), dtype=torch.float32, device=DEV) for F in Fs]
+    offs = torch.as_tensor(st.offsets, device=DEV)
+    ch = kamera.chunks_desc(offs, torch.zeros(n, dtype=torch.int64, device=DEV), st.total_tokens)
+    d = kamera.form_desc(deltas, [torch.empty(0, device=DEV)] * 2, [torch.empty(0, device=DEV)] * 2,
+                         num_layers=L, rank=1)
+    kamera.form_gram(d, ch, G)
+    torch.cuda.synchronize()
+    for c, F in enumerate(Fs):
+        D = parity.bf16_value(parity.host_bits(deltas[c])).reshape(L, -1, F)
+        g = G[c].cpu().numpy().astype(np.float64)
+        for l in range(L):
+            for j in range(n):
+                a, b = int(st.offsets[j]), int(st.offsets[j + 1])
+                x = D[l, a:b]
+                exact = x.T @ x
+                bound = max(b - a, 1) * 2.0 ** -24 * (np.abs(x).T @ np.abs(x)) + 1e-30
+                assert (np.abs(g[l, j] - exact) <= bound).all(), (c, l, j)
