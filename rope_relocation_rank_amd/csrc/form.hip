@@ -136,6 +136,112 @@ __global__ __launch_bounds__(kThreads) void gram_tiles(FormArgs P, int64_t p0, f
       }
 }
 
+// The same for widths that are multiples of 128, with 128 x 128 tiles: wave w owns the
+// 64 x 64 quadrant (w >> 1, w & 1), 4 x 4 MFMA tiles, so each 64-token step issues 32
+// MFMAs per wave between barriers.  The next step's rows are loaded into registers
+// before the current step's MFMAs; rows go to LDS transposed two tokens at a time
+// (one 32-bit word holds a feature's pair of tokens).
+__global__ __launch_bounds__(kThreads) void gram_tiles128(FormArgs P, int64_t p0, float* Gbase,
+                                                          int64_t gstride) {
+  const int ntile = P.F / 128;
+  int rem = blockIdx.x, ti = 0;
+  while (rem >= ntile - ti) {
+    rem -= ntile - ti;
+    ++ti;
+  }
+  const int tj = ti + rem;
+  const int64_t p = p0 + blockIdx.y;
+  const int64_t layer = p / P.num_chunks;
+  const int j = (int)(p - layer * P.num_chunks);
+  const int64_t a = min(max(P.offsets[j], (int64_t)0), P.total_tokens);
+  const int64_t b = min(max(P.offsets[j + 1], a), P.total_tokens);
+  float* G = Gbase + (int64_t)blockIdx.y * gstride;
+
+  constexpr int KS = 64;           // tokens per LDS step
+  constexpr int RS = KS / 2 + 4;   // 32-bit words per LDS row (token pairs + pad)
+  __shared__ __attribute__((aligned(16))) uint32_t sA[128][RS];
+  __shared__ __attribute__((aligned(16))) uint32_t sB[128][RS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  const uint16_t* D = P.delta + layer * P.total_tokens * P.F;
+  // Work item q (2 per thread): token pair tp = q & 31, feature group fg = q >> 5.
+  auto load = [&](int64_t t0, int col0, u32x4_t (&r)[2][2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = tid + kThreads * h;
+      const int tp = q & 31, fg = q >> 5;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t t = t0 + 2 * tp + u;
+        r[h][u] = u32x4_t{0u, 0u, 0u, 0u};
+        if (t < b) r[h][u] = *(const u32x4_t*)(D + t * P.F + col0 + fg * 8);
+      }
+    }
+  };
+  auto store = [&](uint32_t (*S)[RS], const u32x4_t (&r)[2][2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = tid + kThreads * h;
+      const int tp = q & 31, fg = q >> 5;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // features 2e, 2e + 1 of the group
+        const uint32_t w0 = r[h][0][e], w1 = r[h][1][e];
+        S[fg * 8 + 2 * e][tp] = (w0 & 0xffffu) | (w1 << 16);
+        S[fg * 8 + 2 * e + 1][tp] = (w0 >> 16) | (w1 & 0xffff0000u);
+      }
+    }
+  };
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t ra[2][2], rb[2][2];
+  if (a < b) {
+    load(a, ti * 128, ra);
+    load(a, tj * 128, rb);
+  }
+  const int g = lane >> 4, r16 = lane & 15;
+  for (int64_t t0 = a; t0 < b; t0 += KS) {
+    __syncthreads();  // the previous step's fragments are read
+    store(sA, ra);
+    store(sB, rb);
+    __syncthreads();
+    if (t0 + KS < b) {
+      load(t0 + KS, ti * 128, ra);
+      load(t0 + KS, tj * 128, rb);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS / 32; ++ks) {
+      bf16x8_t fa[4], fb[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        fa[x] = __builtin_bit_cast(bf16x8_t,
+                                   *(const u32x4_t*)&sA[wi * 64 + x * 16 + r16][ks * 16 + 4 * g]);
+        fb[x] = __builtin_bit_cast(bf16x8_t,
+                                   *(const u32x4_t*)&sB[wj * 64 + x * 16 + r16][ks * 16 + 4 * g]);
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    }
+  }
+  const int c = lane & 15;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gi = ti * 128 + wi * 64 + x * 16 + 4 * g + r;
+        const int gj = tj * 128 + wj * 64 + y * 16 + c;
+        G[(int64_t)gi * P.F + gj] = acc[x][y][r];
+        if (ti != tj) G[(int64_t)gj * P.F + gi] = acc[x][y][r];
+      }
+}
+
 // ------------------------------------------------------------------ 2. dense fp32 algebra
 
 // Fixed pseudo-random start: entry e of Q (row-major F x k) is a 32-bit integer hash of
@@ -511,8 +617,14 @@ hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream
   const int F = P.F, k = P.k;
   const int nt = F / 64;
   const dim3 blk(kThreads);
-  hipLaunchKernelGGL(gram_tiles, dim3(nt * (nt + 1) / 2, count), blk, 0, s, P, p0, P.ws + W.G,
-                     W.stride);
+  if (F % 128 == 0) {
+    const int n2 = F / 128;
+    hipLaunchKernelGGL(gram_tiles128, dim3(n2 * (n2 + 1) / 2, count), blk, 0, s, P, p0,
+                       P.ws + W.G, W.stride);
+  } else {
+    hipLaunchKernelGGL(gram_tiles, dim3(nt * (nt + 1) / 2, count), blk, 0, s, P, p0,
+                       P.ws + W.G, W.stride);
+  }
   hipLaunchKernelGGL(init_start, dim3((F * k + kThreads - 1) / kThreads, count), blk, 0, s, P);
   const dim3 gFk((k + 63) / 64, (F + 63) / 64, count);
   const dim3 gkk((k + 63) / 64, (k + 63) / 64, count);
@@ -556,8 +668,14 @@ hipError_t launch_form_gram(const FormArgs& P, float* G, hipStream_t s) {
   const int64_t gs = (int64_t)P.F * P.F;
   for (int64_t p0 = 0; p0 < problems; p0 += 65535) {
     const int count = (int)min(problems - p0, (int64_t)65535);
-    hipLaunchKernelGGL(gram_tiles, dim3(nt * (nt + 1) / 2, count), dim3(kThreads), 0, s, P, p0,
-                       G + p0 * gs, gs);
+    if (P.F % 128 == 0) {
+      const int n2 = P.F / 128;
+      hipLaunchKernelGGL(gram_tiles128, dim3(n2 * (n2 + 1) / 2, count), dim3(kThreads), 0, s, P,
+                         p0, G + p0 * gs, gs);
+    } else {
+      hipLaunchKernelGGL(gram_tiles, dim3(nt * (nt + 1) / 2, count), dim3(kThreads), 0, s, P, p0,
+                         G + p0 * gs, gs);
+    }
   }
   return hipGetLastError();
 }
