@@ -3,17 +3,23 @@
 // Operator ("Kamera: KV Cache Multimodal Unificado e Invariante a Posicao para Reuso
 // sem Treinamento", gist.science/pt/paper/2606.23581, §2, reuse equation):
 //     out = round( R(delta_j) x + U_m V_m^T )
-// applied in place to every layer, channel and chunk of a KV cache.  R(delta) turns
-// each NeoX pair (i, i + r/2) of a head by angle delta * theta^(-2i/r) (§2,
-// "Relocacao"); the rank-m patch adds sum_k U[t][k] * V[f][k] to element (t, f) (§2,
-// "Aplicacao de Patch").
+// for every layer, channel and chunk of a KV cache, in place or (recall) from a
+// source cache into a destination cache.  R(delta) turns each rotary pair of a head
+// by angle delta * theta^(-2i/r) (§2, "Relocacao"): NeoX half-split pairs
+// (i, i + r/2) or interleaved pairs (2i, 2i + 1), and with M-RoPE sections each pair
+// takes the delta of its section.  The rank-m patch adds sum_k U[t][k] * V[f][k] to
+// element (t, f) (§2, "Aplicacao de Patch").
 //
-// Three kernels:
-//   rotate_rows          m = 0: only the rotated dims of rotating channels are read and
-//                        written (§3, sliding-window survival: no patch is needed).
-//   relocate_patch_rows  m > 0: rotation fused with the patch in one HBM pass; the
-//                        patch of a 16-token x 128-feature tile is 8 MFMA
-//                        16x16x32 bf16 tiles per 32 k.
+// Kernels:
+//   rotate_rows          m = 0 in place: only the rotated dims of rotating channels
+//                        are read and written (§3, sliding-window survival: no patch
+//                        is needed).
+//   relocate_patch_rows  m > 0, or any recall: rotation fused with the patch in one
+//                        HBM pass; the patch of a 16-token x 128-feature tile is 8
+//                        MFMA 16x16x32 bf16 tiles per 32 k.  The head launch covers
+//                        each 16-token group up to the end of its first chunk; a
+//                        tail launch (TAIL) covers the rest of groups that a chunk
+//                        boundary cuts.  OUT writes a destination cache.
 //   generic_rows         any shape, bf16 or fp32: one thread per (layer, token, head).
 //
 // Memory shape of the tuned kernels (what streams well on MI355X HBM3E): every load
