@@ -43,6 +43,12 @@
  *   - R(0) is the identity matrix: a chunk with delta 0 is not rotated at all.
  *   - The result is rounded once, from fp64, to the storage type (bf16 or fp32)
  *     with round-to-nearest-even.
+ *   - 8-bit KV (the pages report the method holding on FP8-quantised models, [N
+ *     closing summary]): elements are OCP FP8 E4M3 codes and channel c of layer l
+ *     carries one dequantisation scale s, value = s * code value.  The operator
+ *     acts on values: out = encode((R(delta) (s x) + U V^T) / s), where encode
+ *     rounds to the nearest code, ties to the even one, and saturates at +-448.
+ *     The factors stay bf16 (they are in value units).
  *   - With no patch (m = 0), elements the rotation does not move (channels with
  *     r = 0, dims >= r, chunks with delta = 0) keep their exact bits.
  *
@@ -59,6 +65,7 @@
 
 #define ORC_BF16 0
 #define ORC_F32 1
+#define ORC_FP8 2 /* OCP FP8 E4M3 codes with a per-layer scale; factors in bf16 */
 
 /* ---------------------------------------------------------------- numbers */
 
@@ -98,19 +105,61 @@ void orc_round_bf16_array(const double* y, uint16_t* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_from_double(y[i]);
 }
 
+/* OCP 8-bit floating point, E4M3 variant (the fp8 KV type): bit 7 sign, bits 6..3
+ * exponent with bias 7, bits 2..0 mantissa.  Exponent 0 holds the subnormals
+ * mantissa * 2^-9; exponent field 15 with mantissa 7 is NaN; there are no
+ * infinities, so exponent 15 with mantissa 0..6 is finite and 448 = 1.75 * 2^8 is
+ * the largest value.  Code -> exact double. */
+double orc_fp8_to_double(uint8_t b) {
+    int e = (b >> 3) & 15, mt = b & 7;
+    if (e == 15 && mt == 7) return NAN;
+    double v = e == 0 ? ldexp((double)mt, -9) : ldexp((double)(8 + mt), e - 10);
+    return (b & 0x80) ? -v : v;
+}
+
+/* Double -> E4M3 code: the nearest of the 127 finite magnitudes, a tie going to the
+ * even code (mantissa bit 0 clear); magnitudes of 448 and above give 448
+ * (saturation, no overflow to NaN); NaN gives NaN; the sign is kept, zero included.
+ * Found by brute force over the magnitudes. */
+uint8_t orc_fp8_from_double(double y) {
+    uint8_t sign = signbit(y) ? 0x80 : 0;
+    if (isnan(y)) return (uint8_t)(sign | 0x7F);
+    double a = fabs(y);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    int best = 0;
+    double bd = a;
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs(orc_fp8_to_double((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) { best = c; bd = d; }
+    }
+    return (uint8_t)(sign | best);
+}
+
+void orc_fp8_from_double_array(const double* y, uint8_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_fp8_from_double(y[i]);
+}
+
+/* Bytes of one element of the storage type, and the type of the patch factors. */
+static int elem_size(int dtype) { return dtype == ORC_BF16 ? 2 : dtype == ORC_FP8 ? 1 : 4; }
+static int factor_dtype(int dtype) { return dtype == ORC_FP8 ? ORC_BF16 : dtype; }
+
+/* Stored element -> double; an fp8 code gives its code value (the caller scales). */
 static double load_elem(int dtype, const void* base, int64_t i) {
     if (dtype == ORC_BF16) return orc_bf16_to_double(((const uint16_t*)base)[i]);
+    if (dtype == ORC_FP8) return orc_fp8_to_double(((const uint8_t*)base)[i]);
     return (double)((const float*)base)[i];
 }
 
+/* y (for fp8: already divided by the scale) -> stored element. */
 static void store_elem(int dtype, void* base, int64_t i, double y) {
     if (dtype == ORC_BF16) ((uint16_t*)base)[i] = orc_bf16_from_double(y);
+    else if (dtype == ORC_FP8) ((uint8_t*)base)[i] = orc_fp8_from_double(y);
     else ((float*)base)[i] = (float)y; /* C conversion: round to nearest even */
 }
 
 static void copy_elem(int dtype, void* dst, int64_t i, const void* src, int64_t k) {
-    if (dtype == ORC_BF16) ((uint16_t*)dst)[i] = ((const uint16_t*)src)[k];
-    else memcpy((float*)dst + i, (const float*)src + k, sizeof(float));
+    int es = elem_size(dtype);
+    memcpy((char*)dst + i * es, (const char*)src + k * es, (size_t)es);
 }
 
 /* ------------------------------------------------------------- relocation */
@@ -213,15 +262,18 @@ void orc_row_f64(const double* x, double* y, int heads, int dim, int r, double t
     orc_row_spec_f64(x, y, heads, dim, r, theta, &delta, NULL, m, u, V);
 }
 
-/* One token row in storage format (dtype 0 = bf16 bits, 1 = fp32): x_in and out
- * hold heads*dim contiguous elements, u holds m, V holds [heads*dim][m], all of
- * the same dtype.  out may equal x_in.  With m = 0, every element the rotation
- * does not move keeps its bits. Returns 0, or -1 on bad arguments. */
-int orc_row_spec(int dtype, const void* x_in, void* out, int heads, int dim, int r,
-                 double theta, const int64_t* delta, const orc_rope* q, int m, const void* u,
-                 const void* V) {
-    if ((dtype != ORC_BF16 && dtype != ORC_F32) || heads < 1 || dim < 1 || r < 0 ||
-        r > dim || (r & 1) || m < 0)
+/* One token row in storage format (dtype 0 = bf16 bits, 1 = fp32, 2 = fp8 E4M3
+ * codes with dequantisation scale `scale`): x_in and out hold heads*dim contiguous
+ * elements, u holds m, V holds [heads*dim][m], in the dtype's factor type (bf16 for
+ * fp8, else the dtype).  out may equal x_in.  The row's values are scale * x (scale
+ * is 1 but for fp8); the result is divided by the scale before it is stored.  With
+ * m = 0, every element the rotation does not move keeps its bits. Returns 0, or -1
+ * on bad arguments. */
+int orc_row_spec_scaled(int dtype, double scale, const void* x_in, void* out, int heads,
+                        int dim, int r, double theta, const int64_t* delta, const orc_rope* q,
+                        int m, const void* u, const void* V) {
+    if ((dtype != ORC_BF16 && dtype != ORC_F32 && dtype != ORC_FP8) || heads < 1 || dim < 1 ||
+        r < 0 || r > dim || (r & 1) || m < 0 || !(scale > 0) || !isfinite(scale))
         return -1;
     if (q && q->num_sections > 1) {
         int sum = 0;
@@ -238,18 +290,24 @@ int orc_row_spec(int dtype, const void* x_in, void* out, int heads, int dim, int
     double* ud = (double*)malloc(sizeof(double) * (m > 0 ? m : 1));
     double* vd = (double*)malloc(sizeof(double) * (m > 0 ? F * m : 1));
     if (!x || !y || !ud || !vd) { free(x); free(y); free(ud); free(vd); return -1; }
-    for (int64_t f = 0; f < F; ++f) x[f] = load_elem(dtype, x_in, f);
-    for (int k = 0; k < m; ++k) ud[k] = load_elem(dtype, u, k);
-    for (int64_t i = 0; i < F * m; ++i) vd[i] = load_elem(dtype, V, i);
+    for (int64_t f = 0; f < F; ++f) x[f] = scale * load_elem(dtype, x_in, f);
+    for (int k = 0; k < m; ++k) ud[k] = load_elem(factor_dtype(dtype), u, k);
+    for (int64_t i = 0; i < F * m; ++i) vd[i] = load_elem(factor_dtype(dtype), V, i);
     orc_row_spec_f64(x, y, heads, dim, r, theta, delta, q, m, ud, vd);
     for (int64_t f = 0; f < F; ++f) {
         int d = (int)(f % dim);
         int moved = m > 0 || dim_moves(q, r, d, delta);
-        if (moved) store_elem(dtype, out, f, y[f]);
+        if (moved) store_elem(dtype, out, f, y[f] / scale);
         else if (out != x_in) copy_elem(dtype, out, f, x_in, f);
     }
     free(x); free(y); free(ud); free(vd);
     return 0;
+}
+
+int orc_row_spec(int dtype, const void* x_in, void* out, int heads, int dim, int r,
+                 double theta, const int64_t* delta, const orc_rope* q, int m, const void* u,
+                 const void* V) {
+    return orc_row_spec_scaled(dtype, 1.0, x_in, out, heads, dim, r, theta, delta, q, m, u, V);
 }
 
 int orc_row(int dtype, const void* x_in, void* out, int heads, int dim, int r,
@@ -266,6 +324,7 @@ typedef struct {
     int64_t layer_stride, slot_stride, head_stride, page_stride; /* elements */
     const void* U;            /* [layers][total_tokens][m] or NULL when m = 0 */
     const void* V;            /* [layers][chunks][heads*dim][m] or NULL */
+    const float* scale;       /* fp8: [layers] dequantisation scales; else unused */
 } orc_channel;
 
 typedef struct {
@@ -338,14 +397,16 @@ void orc_row_magnitude_f64(const double* x, double* s, int heads, int dim, int r
  * (and s_out[c]) are given, they are fp64 arrays laid out exactly like channel c's
  * elements (same offsets from the channel's data pointer); every element the call
  * computes gets its unrounded value there (and its magnitude bound), every other
- * element is left as the caller filled it.  Returns 0, or -1 on bad arguments. */
+ * element is left as the caller filled it.  With fp8 codes both are divided by the
+ * layer's scale (code units, the grid the result is rounded on).  Returns 0, or -1
+ * on bad arguments. */
 int orc_relocate_patch_ex(const orc_problem* p, double* const* y_out, double* const* s_out) {
     if (!p || p->num_channels < 1 || p->num_channels > 2 || p->rank < 0 ||
-        (p->dtype != ORC_BF16 && p->dtype != ORC_F32))
+        (p->dtype != ORC_BF16 && p->dtype != ORC_F32 && p->dtype != ORC_FP8))
         return -1;
     int64_t T = p->total_tokens, L = p->num_layers;
     if (T == 0 || L == 0 || p->num_chunks == 0) return 0;
-    int es = p->dtype == ORC_BF16 ? 2 : 4;
+    int es = elem_size(p->dtype), fs = elem_size(factor_dtype(p->dtype));
     int m = p->rank;
     int bad = 0;
     for (int c = 0; c < p->num_channels; ++c) {
@@ -376,21 +437,23 @@ int orc_relocate_patch_ex(const orc_problem* p, double* const* y_out, double* co
                 }
                 const void* u = NULL;
                 const void* V = NULL;
+                double sc = p->dtype == ORC_FP8 ? (double)ch->scale[l] : 1.0;
                 if (m > 0) {
-                    u = (const char*)ch->U + ((l * T + t) * m) * es;
-                    V = (const char*)ch->V + ((l * p->num_chunks + j) * F * m) * es;
-                    for (int k = 0; k < m; ++k) ud[k] = load_elem(p->dtype, u, k);
-                    for (int64_t i = 0; i < F * m; ++i) vd[i] = load_elem(p->dtype, V, i);
+                    u = (const char*)ch->U + ((l * T + t) * m) * fs;
+                    V = (const char*)ch->V + ((l * p->num_chunks + j) * F * m) * fs;
+                    for (int k = 0; k < m; ++k) ud[k] = load_elem(factor_dtype(p->dtype), u, k);
+                    for (int64_t i = 0; i < F * m; ++i)
+                        vd[i] = load_elem(factor_dtype(p->dtype), V, i);
                 }
                 if (yo) {
-                    for (int64_t f = 0; f < F; ++f) x[f] = load_elem(p->dtype, row, f);
+                    for (int64_t f = 0; f < F; ++f) x[f] = sc * load_elem(p->dtype, row, f);
                     orc_row_spec_f64(x, y, ch->heads, ch->dim, ch->rope_dim, p->theta, dj, &p->rope,
                                      m, ud, vd);
                     orc_row_magnitude_spec_f64(x, s, ch->heads, ch->dim, ch->rope_dim, p->theta, dj,
                                                &p->rope, m, ud, vd);
                 }
-                if (orc_row_spec(p->dtype, row, row, ch->heads, ch->dim, ch->rope_dim, p->theta,
-                                 dj, &p->rope, m, u, V) != 0)
+                if (orc_row_spec_scaled(p->dtype, sc, row, row, ch->heads, ch->dim, ch->rope_dim,
+                                        p->theta, dj, &p->rope, m, u, V) != 0)
                     bad = 1;
                 for (int64_t h = 0; h < ch->heads; ++h) {
                     memcpy((char*)ch->data + offs[h] * es, row + h * ch->dim * es, (size_t)ch->dim * es);
@@ -398,8 +461,8 @@ int orc_relocate_patch_ex(const orc_problem* p, double* const* y_out, double* co
                         for (int d = 0; d < ch->dim; ++d) {
                             int moved = m > 0 || dim_moves(&p->rope, ch->rope_dim, d, dj);
                             if (!moved) continue;
-                            yo[offs[h] + d] = y[h * ch->dim + d];
-                            if (so) so[offs[h] + d] = s[h * ch->dim + d];
+                            yo[offs[h] + d] = y[h * ch->dim + d] / sc;
+                            if (so) so[offs[h] + d] = s[h * ch->dim + d] / sc;
                         }
                     }
                 }
@@ -419,13 +482,15 @@ int orc_relocate_patch(const orc_problem* p) { return orc_relocate_patch_ex(p, N
  * which only the channel data pointers, strides, page size and block table are read.
  * Every element of the row is written; elements that neither the rotation nor the
  * patch changes are copied bit for bit, so a chunk with delta 0 and no patch is a
- * plain copy.  src is never written.  y_out / s_out are laid out like dst; the
- * computed elements get their fp64 value and magnitude bound there.  Returns 0, or -1
- * on bad arguments. */
+ * plain copy.  src is never written.  With fp8 codes the destination keeps the
+ * source's scales (its own are not read).  y_out / s_out are laid out like dst; the
+ * computed elements get their fp64 value and magnitude bound there (fp8: divided by
+ * the scale, in code units).  Returns 0, or -1 on bad arguments. */
 int orc_recall_patch_ex(const orc_problem* src, const orc_problem* dst, double* const* y_out,
                         double* const* s_out) {
     if (!src || !dst || src->num_channels < 1 || src->num_channels > 2 || src->rank < 0 ||
-        (src->dtype != ORC_BF16 && src->dtype != ORC_F32) || dst->dtype != src->dtype ||
+        (src->dtype != ORC_BF16 && src->dtype != ORC_F32 && src->dtype != ORC_FP8) ||
+        dst->dtype != src->dtype ||
         dst->num_channels != src->num_channels || dst->num_layers != src->num_layers)
         return -1;
     for (int c = 0; c < src->num_channels; ++c)
@@ -433,7 +498,7 @@ int orc_recall_patch_ex(const orc_problem* src, const orc_problem* dst, double* 
             return -1;
     int64_t T = src->total_tokens, L = src->num_layers;
     if (T == 0 || L == 0 || src->num_chunks == 0) return 0;
-    int es = src->dtype == ORC_BF16 ? 2 : 4;
+    int es = elem_size(src->dtype), fs = elem_size(factor_dtype(src->dtype));
     int m = src->rank;
     int bad = 0;
     for (int c = 0; c < src->num_channels; ++c) {
@@ -461,21 +526,23 @@ int orc_recall_patch_ex(const orc_problem* src, const orc_problem* dst, double* 
                 }
                 const void* u = NULL;
                 const void* V = NULL;
+                double qs = src->dtype == ORC_FP8 ? (double)sc->scale[l] : 1.0;
                 if (m > 0) {
-                    u = (const char*)sc->U + ((l * T + t) * m) * es;
-                    V = (const char*)sc->V + ((l * src->num_chunks + j) * F * m) * es;
-                    for (int k = 0; k < m; ++k) ud[k] = load_elem(src->dtype, u, k);
-                    for (int64_t i = 0; i < F * m; ++i) vd[i] = load_elem(src->dtype, V, i);
+                    u = (const char*)sc->U + ((l * T + t) * m) * fs;
+                    V = (const char*)sc->V + ((l * src->num_chunks + j) * F * m) * fs;
+                    for (int k = 0; k < m; ++k) ud[k] = load_elem(factor_dtype(src->dtype), u, k);
+                    for (int64_t i = 0; i < F * m; ++i)
+                        vd[i] = load_elem(factor_dtype(src->dtype), V, i);
                 }
                 if (yo) {
-                    for (int64_t f = 0; f < F; ++f) x[f] = load_elem(src->dtype, row, f);
+                    for (int64_t f = 0; f < F; ++f) x[f] = qs * load_elem(src->dtype, row, f);
                     orc_row_spec_f64(x, y, sc->heads, sc->dim, sc->rope_dim, src->theta, dj,
                                      &src->rope, m, ud, vd);
                     orc_row_magnitude_spec_f64(x, s, sc->heads, sc->dim, sc->rope_dim, src->theta,
                                                dj, &src->rope, m, ud, vd);
                 }
-                if (orc_row_spec(src->dtype, row, out, sc->heads, sc->dim, sc->rope_dim, src->theta,
-                                 dj, &src->rope, m, u, V) != 0)
+                if (orc_row_spec_scaled(src->dtype, qs, row, out, sc->heads, sc->dim, sc->rope_dim,
+                                        src->theta, dj, &src->rope, m, u, V) != 0)
                     bad = 1;
                 for (int64_t h = 0; h < sc->heads; ++h) {
                     int64_t o = orc_row_offset(dc, dst->page_size, dst->block_table, l, t, h);
@@ -484,8 +551,8 @@ int orc_recall_patch_ex(const orc_problem* src, const orc_problem* dst, double* 
                         for (int d = 0; d < sc->dim; ++d) {
                             int moved = m > 0 || dim_moves(&src->rope, sc->rope_dim, d, dj);
                             if (!moved) continue;
-                            yo[o + d] = y[h * sc->dim + d];
-                            if (so) so[o + d] = s[h * sc->dim + d];
+                            yo[o + d] = y[h * sc->dim + d] / qs;
+                            if (so) so[o + d] = s[h * sc->dim + d] / qs;
                         }
                     }
                 }

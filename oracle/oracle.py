@@ -5,7 +5,8 @@ TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 the GPU library: it has its own C source, its own structs and its own loader.
 
 Every array argument is a numpy array in storage format: bf16 values travel as
-``uint16`` bit patterns, fp32 values as ``float32``.
+``uint16`` bit patterns, fp32 values as ``float32``, fp8 E4M3 codes as ``uint8``
+(with bf16 factors and a per-layer float32 scale per channel).
 """
 from __future__ import annotations
 
@@ -21,6 +22,7 @@ LIB = os.path.join(HERE, "libkamera_oracle.so")
 
 BF16 = 0
 F32 = 1
+FP8 = 2
 
 
 def build(force: bool = False) -> str:
@@ -39,7 +41,7 @@ class _Channel(C.Structure):
                 ("rope_dim", C.c_int32), ("pad_", C.c_int32),
                 ("layer_stride", C.c_int64), ("slot_stride", C.c_int64),
                 ("head_stride", C.c_int64), ("page_stride", C.c_int64),
-                ("U", C.c_void_p), ("V", C.c_void_p)]
+                ("U", C.c_void_p), ("V", C.c_void_p), ("scale", C.c_void_p)]
 
 
 class _Rope(C.Structure):
@@ -92,6 +94,15 @@ def lib():
         L.orc_bf16_to_double.restype = C.c_double
         L.orc_bf16_to_double.argtypes = [C.c_uint16]
         L.orc_round_bf16_array.argtypes = [C.c_void_p, C.c_void_p, C.c_int64]
+        L.orc_fp8_to_double.restype = C.c_double
+        L.orc_fp8_to_double.argtypes = [C.c_uint8]
+        L.orc_fp8_from_double.restype = C.c_uint8
+        L.orc_fp8_from_double.argtypes = [C.c_double]
+        L.orc_fp8_from_double_array.argtypes = [C.c_void_p, C.c_void_p, C.c_int64]
+        L.orc_row_spec_scaled.restype = C.c_int
+        L.orc_row_spec_scaled.argtypes = [C.c_int, C.c_double, C.c_void_p, C.c_void_p, C.c_int,
+                                          C.c_int, C.c_int, C.c_double, C.c_void_p,
+                                          C.POINTER(_Rope), C.c_int, C.c_void_p, C.c_void_p]
         L.orc_freq.restype = C.c_double
         L.orc_freq.argtypes = [C.c_double, C.c_int, C.c_int]
         L.orc_rotate_head_f64.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int,
@@ -146,7 +157,14 @@ def _dtype_code(a: np.ndarray) -> int:
         return BF16
     if a.dtype == np.float32:
         return F32
-    raise TypeError("storage arrays are uint16 (bf16 bits) or float32")
+    if a.dtype == np.uint8:
+        return FP8
+    raise TypeError("storage arrays are uint16 (bf16 bits), float32 or uint8 (fp8 codes)")
+
+
+def _factor_dtype(a: np.ndarray):
+    """numpy dtype of the patch factors for KV stored like `a` (bf16 bits for fp8)."""
+    return np.uint16 if a.dtype == np.uint8 else a.dtype
 
 
 # ----------------------------------------------------------------- numbers
@@ -163,6 +181,25 @@ def bf16_to_f64(bits) -> np.ndarray:
     """bf16 bits -> exact fp64 values."""
     b = np.ascontiguousarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def round_fp8(y) -> np.ndarray:
+    """fp64 -> E4M3 codes: nearest, ties to even, saturating at +-448."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib().orc_fp8_from_double_array(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+_fp8_table = None
+
+
+def fp8_to_f64(codes) -> np.ndarray:
+    """E4M3 codes -> exact fp64 values (NaN for the two NaN codes)."""
+    global _fp8_table
+    if _fp8_table is None:
+        _fp8_table = np.array([lib().orc_fp8_to_double(c) for c in range(256)])
+    return _fp8_table[np.asarray(codes, dtype=np.uint8)]
 
 
 def freq(theta: float, r: int, i: int) -> float:
@@ -219,18 +256,20 @@ def row_magnitude_f64(x, heads: int, dim: int, r: int, theta: float, delta,
 
 
 def row(x, heads: int, dim: int, r: int, theta: float, delta,
-        u=None, V=None, pairing: int = NEOX, sections=()) -> np.ndarray:
-    """One token row in storage format (uint16 bf16 bits or float32)."""
+        u=None, V=None, pairing: int = NEOX, sections=(), scale: float = 1.0) -> np.ndarray:
+    """One token row in storage format (uint16 bf16 bits, float32, or uint8 fp8 codes
+    whose values are `scale` * code value; fp8 factors are bf16 bits)."""
     x = np.ascontiguousarray(x)
     code = _dtype_code(x)
     out = np.empty_like(x)
     m = 0 if u is None else int(np.asarray(u).size)
-    uu = None if u is None else np.ascontiguousarray(u, dtype=x.dtype)
-    vv = None if V is None else np.ascontiguousarray(V, dtype=x.dtype)
+    fd = _factor_dtype(x)
+    uu = None if u is None else np.ascontiguousarray(u, dtype=fd)
+    vv = None if V is None else np.ascontiguousarray(V, dtype=fd)
     dv = _delta_vec(delta)
     q = _rope(pairing, sections)
-    rc = lib().orc_row_spec(code, _ptr(x), _ptr(out), heads, dim, r, theta, _ptr(dv),
-                            C.byref(q), m, _ptr(uu), _ptr(vv))
+    rc = lib().orc_row_spec_scaled(code, float(scale), _ptr(x), _ptr(out), heads, dim, r, theta,
+                                   _ptr(dv), C.byref(q), m, _ptr(uu), _ptr(vv))
     if rc != 0:
         raise ValueError("oracle rejected the row arguments")
     return out
@@ -280,9 +319,14 @@ def _problem(channels, *, num_layers, theta, offsets, delta, rank, page_size, bl
         if rank > 0 and shape_from is None:
             U = np.ascontiguousarray(ch["U"])
             V = np.ascontiguousarray(ch["V"])
-            assert U.dtype == data.dtype and V.dtype == data.dtype
+            assert U.dtype == _factor_dtype(data) and V.dtype == _factor_dtype(data)
             keep += [U, V]
             p.ch[i].U, p.ch[i].V = U.ctypes.data, V.ctypes.data
+        if c == FP8 and shape_from is None:
+            sc = np.ascontiguousarray(ch["scale"], dtype=np.float32)
+            assert sc.size >= num_layers and np.all(sc[:num_layers] > 0)
+            keep.append(sc)
+            p.ch[i].scale = sc.ctypes.data
     p.dtype = code
     p.num_layers = num_layers
     p.num_channels = len(channels)
@@ -320,11 +364,14 @@ def relocate_patch(channels, *, num_layers: int, theta: float, offsets, delta,
     ``offset`` (element offset of that first element inside ``data``, default
     0), ``heads``, ``dim``, ``rope_dim``, ``layer_stride``, ``slot_stride``,
     ``head_stride``, ``page_stride`` (elements) and, when ``rank > 0``, ``U``
-    ([layers][tokens][rank]) and ``V`` ([layers][chunks][heads*dim][rank]).
+    ([layers][tokens][rank]) and ``V`` ([layers][chunks][heads*dim][rank]).  With
+    fp8 codes (uint8 ``data``) the factors are bf16 bits and ``scale`` holds the
+    channel's per-layer float32 dequantisation scales.
 
     ``y_out`` / ``s_out``: optional lists (one per channel) of float64 buffers shaped
     like that channel's ``data``; every element the call computes receives its
-    unrounded fp64 value / its sum of term magnitudes, at the same element offset.
+    unrounded fp64 value / its sum of term magnitudes, at the same element offset
+    (fp8: divided by the layer's scale).
 
     ``pairing`` (NEOX or INTERLEAVED) and ``sections`` (M-RoPE pairs per section;
     then ``delta`` is [chunks][sections]) select the positional variant.
