@@ -33,6 +33,12 @@
  *   - delta == 0 means R = identity exactly.
  *   - Each output element is rounded once to the storage type (round to nearest even).
  *     Angles are formed and reduced in fp64; the sums run in fp32.
+ *   - 8-bit KV ("Modelos Tomam Notas no Prefill", closing summary: the method holds on
+ *     FP8-quantised models): KAMERA_FP8_E4M3 elements are OCP FP8 E4M3 codes and each
+ *     channel carries one dequantisation scale s per layer, value = s * code value.
+ *     The operator acts on values and stores encode(result / s): the nearest code,
+ *     ties to the even code, saturating at +-448 (NaN stays NaN).  The factors are
+ *     bf16, in value units.
  *
  * Conventions for every entry point:
  *   - In place: the KV buffers named by the descriptor are read and overwritten
@@ -67,7 +73,7 @@ extern "C" {
 #define KAMERA_API __attribute__((visibility("default")))
 #endif
 
-#define KAMERA_ABI_VERSION 2
+#define KAMERA_ABI_VERSION 3
 #define KAMERA_MAX_RANK 256   /* largest patch rank m accepted */
 
 typedef enum {
@@ -81,7 +87,11 @@ typedef enum {
   KAMERA_E_HIP = 6          /* the HIP runtime reported an error at launch */
 } kamera_status;
 
-typedef enum { KAMERA_BF16 = 0, KAMERA_F32 = 1 } kamera_dtype;
+typedef enum {
+  KAMERA_BF16 = 0,
+  KAMERA_F32 = 1,
+  KAMERA_FP8_E4M3 = 2  /* OCP E4M3 codes (1 byte) with per-layer scales; bf16 factors */
+} kamera_dtype;
 
 typedef enum {
   KAMERA_NEOX_HALF = 0,   /* rotary pair i is dims (i, i + rope_dim/2) */
@@ -110,10 +120,13 @@ typedef struct {
   int32_t rope_dim;    /* even, 0 <= rope_dim <= dim; 0 = this channel never rotates */
   int32_t reserved0;   /* must be 0 */
   int64_t layer_stride, slot_stride, head_stride, page_stride;
+  const float* scale;  /* KAMERA_FP8_E4M3: device [num_layers] dequantisation scales,
+                          precondition finite and > 0; ignored for other dtypes */
 } kamera_channel;
 
 typedef struct {
-  int32_t dtype;         /* kamera_dtype of the KV elements and of the factors */
+  int32_t dtype;         /* kamera_dtype of the KV elements (and of the factors, which
+                            are bf16 for KAMERA_FP8_E4M3) */
   int32_t num_layers;    /* >= 0 */
   int32_t num_channels;  /* 1 or 2 */
   int32_t pairing;       /* kamera_pairing */
@@ -143,7 +156,8 @@ typedef struct {
                               |delta| < 2^53 */
 } kamera_chunks;
 
-/* The rank-m patch, one factor pair per channel, in the KV dtype, dense row-major:
+/* The rank-m patch, one factor pair per channel, in the KV dtype (bf16 for
+ * KAMERA_FP8_E4M3), dense row-major:
  *   U[c]: [num_layers][total_tokens][rank]           token factor U_m, per layer
  *   V[c]: [num_layers][num_chunks][heads*dim][rank]  feature factor V_m, per layer and chunk
  * The same pointers may be passed for both channels when their shapes agree. */
@@ -184,8 +198,9 @@ KAMERA_API kamera_status kamera_relocate_patch(const kamera_kv_desc* kv, const k
  *   dst: the cache being filled.  dtype, num_layers, num_channels and each channel's
  *        heads, dim and rope_dim must equal src's; data, strides, page_size,
  *        num_pages and block_table are its own (destination tokens whose page id lies
- *        outside [0, num_pages) are skipped).  Its rope_theta, pairing and sections
- *        are not read: the source's apply.
+ *        outside [0, num_pages) are skipped).  Its rope_theta, pairing, sections and
+ *        (fp8) scales are not read: the source's apply, so an fp8 destination holds
+ *        codes in the source's scales.
  *        Its memory must not overlap the source or the factors (KAMERA_E_ALIAS).
  *   patch == NULL or rank 0: rotation and copy only.
  * chunks, stream and errors as for kamera_relocate_patch. */

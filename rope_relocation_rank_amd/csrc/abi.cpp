@@ -36,6 +36,15 @@ constexpr int64_t kMaxTunedTokens = (int64_t)1 << 30;  // token ids stay in 32 b
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Bytes of a KV element, and of a patch-factor element (bf16 for fp8 KV).
+int64_t elem_bytes(int32_t dtype) { return dtype == KAMERA_BF16 ? 2 : dtype == KAMERA_FP8_E4M3 ? 1 : 4; }
+int64_t factor_bytes(int32_t dtype) { return dtype == KAMERA_FP8_E4M3 ? 2 : elem_bytes(dtype); }
+
+// Dtypes of the tuned kernels, and the alignment their vector accesses need (a lane
+// moves 8 elements at once).
+bool tuned_dtype(int32_t dtype) { return dtype == KAMERA_BF16 || dtype == KAMERA_FP8_E4M3; }
+uintptr_t vec_align(int32_t dtype) { return dtype == KAMERA_FP8_E4M3 ? 8 : 16; }
+
 // Exclusive end (bytes) of the KV memory a channel can touch, from its base.
 // Returns false on int64 overflow.
 bool kv_extent(const kamera_channel& c, int64_t layers, int64_t slots, int32_t page_size,
@@ -89,16 +98,16 @@ __int128 layer_extent(const kamera_channel& c, int64_t T, int32_t page_size, int
   return last + 1;
 }
 
-// Rotation-only kernel: 16-byte lanes over the rotated dims of each row.
+// Rotation-only kernel: 8-element lanes over the rotated dims of each row.
 bool rotate_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, int64_t T) {
   const int r = c.rope_dim;
-  return kv.dtype == KAMERA_BF16 && !(kv.flags & KAMERA_FLAG_GENERIC) &&
+  return tuned_dtype(kv.dtype) && !(kv.flags & KAMERA_FLAG_GENERIC) &&
          (r == 16 || r == 32 || r == 64 || r == 128) && T < kMaxTunedTokens &&
-         aligned(c.data, 16) && strides_ok(c);
+         aligned(c.data, vec_align(kv.dtype)) && strides_ok(c);
 }
 
 // Rotate+patch kernel: 128-feature blocks hold whole heads (or whole blocks of one
-// head), a NeoX partner sits r/16 lanes away, rank <= 128.
+// head), a NeoX partner sits r/16 lanes away, rank <= 128 (fp8: a multiple of 8).
 bool mfma_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, const kamera_patch& p,
                    int ci, int64_t T) {
   const int r = c.rope_dim, D = c.dim;
@@ -106,10 +115,10 @@ bool mfma_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, const kame
   const bool dim_ok = D % 8 == 0 && (D % 128 == 0 || 128 % D == 0);
   // row offsets inside a layer are kept in 32 bits
   const bool extent_ok = layer_extent(c, T, kv.page_size, kv.num_pages) < ((__int128)1 << 31);
-  return kv.dtype == KAMERA_BF16 && !(kv.flags & KAMERA_FLAG_GENERIC) && p.rank <= kMfmaMaxRank &&
-         rope_ok && dim_ok && extent_ok && T < kMaxTunedTokens && aligned(c.data, 16) &&
-         aligned(p.U[ci], 16) && aligned(p.V[ci], 16) && strides_ok(c) &&
-         (int64_t)c.heads * D < (1 << 24);
+  return tuned_dtype(kv.dtype) && !(kv.flags & KAMERA_FLAG_GENERIC) && p.rank <= kMfmaMaxRank &&
+         (kv.dtype == KAMERA_BF16 || p.rank % 8 == 0) && rope_ok && dim_ok && extent_ok &&
+         T < kMaxTunedTokens && aligned(c.data, vec_align(kv.dtype)) && aligned(p.U[ci], 16) &&
+         aligned(p.V[ci], 16) && strides_ok(c) && (int64_t)c.heads * D < (1 << 24);
 }
 
 
@@ -144,8 +153,9 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
                        Plan* plan) {
   if (!kv) return fail(KAMERA_E_NULL, "kv descriptor is NULL");
   if (!ch) return fail(KAMERA_E_NULL, "chunks descriptor is NULL");
-  if (kv->dtype != KAMERA_BF16 && kv->dtype != KAMERA_F32)
-    return fail(KAMERA_E_UNSUPPORTED, "dtype %d is not bf16 (0) or fp32 (1)", kv->dtype);
+  if (kv->dtype != KAMERA_BF16 && kv->dtype != KAMERA_F32 && kv->dtype != KAMERA_FP8_E4M3)
+    return fail(KAMERA_E_UNSUPPORTED, "dtype %d is not bf16 (0), fp32 (1) or fp8 E4M3 (2)",
+                kv->dtype);
   if (kv->pairing != KAMERA_NEOX_HALF && kv->pairing != KAMERA_INTERLEAVED)
     return fail(KAMERA_E_UNSUPPORTED, "pairing %d is not NeoX half-split (0) or interleaved (1)",
                 kv->pairing);
@@ -167,7 +177,7 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
   if (p && p->reserved0 != 0) return fail(KAMERA_E_SHAPE, "patch.reserved0 must be 0");
   if (m < 0 || m > KAMERA_MAX_RANK)
     return fail(KAMERA_E_SHAPE, "rank %d outside [0, %d]", m, KAMERA_MAX_RANK);
-  const int64_t es = kv->dtype == KAMERA_BF16 ? 2 : 4;
+  const int64_t es = elem_bytes(kv->dtype), fs = factor_bytes(kv->dtype);
   const bool empty = kv->num_layers == 0 || ch->total_tokens == 0;
   bool any_rope = false;
   for (int c = 0; c < kv->num_channels; ++c) {
@@ -186,6 +196,10 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
     if (!empty && !k.data) return fail(KAMERA_E_NULL, "channel %d: data is NULL", c);
     if (!aligned(k.data, es))
       return fail(KAMERA_E_ALIGN, "channel %d: data not aligned to %d bytes", c, (int)es);
+    if (kv->dtype == KAMERA_FP8_E4M3) {
+      if (!empty && !k.scale) return fail(KAMERA_E_NULL, "channel %d: fp8 with no scales", c);
+      if (!aligned(k.scale, 4)) return fail(KAMERA_E_ALIGN, "channel %d: scales not 4-byte aligned", c);
+    }
   }
   if (any_rope && !(std::isfinite(kv->rope_theta) && kv->rope_theta > 0))
     return fail(KAMERA_E_SHAPE, "rope_theta must be finite and > 0");
@@ -217,8 +231,8 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
     for (int c = 0; c < kv->num_channels; ++c) {
       if (!empty && (!p->U[c] || !p->V[c]))
         return fail(KAMERA_E_NULL, "channel %d: rank %d with a NULL factor", c, m);
-      if (!aligned(p->U[c], es) || !aligned(p->V[c], es))
-        return fail(KAMERA_E_ALIGN, "channel %d: factor not aligned to %d bytes", c, (int)es);
+      if (!aligned(p->U[c], fs) || !aligned(p->V[c], fs))
+        return fail(KAMERA_E_ALIGN, "channel %d: factor not aligned to %d bytes", c, (int)fs);
     }
   }
   // Factors must not overlap any KV memory the call writes.
@@ -230,8 +244,8 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
         return fail(KAMERA_E_SHAPE, "channel %d: KV extent overflows", c);
       for (int f = 0; f < kv->num_channels; ++f) {
         const int64_t F = (int64_t)kv->ch[f].heads * kv->ch[f].dim;
-        const __int128 ub = (__int128)kv->num_layers * ch->total_tokens * m * es;
-        const __int128 vb = (__int128)kv->num_layers * ch->num_chunks * F * m * es;
+        const __int128 ub = (__int128)kv->num_layers * ch->total_tokens * m * fs;
+        const __int128 vb = (__int128)kv->num_layers * ch->num_chunks * F * m * fs;
         if (ub > INT64_MAX || vb > INT64_MAX) return fail(KAMERA_E_SHAPE, "factor size overflows");
         if (overlaps(kv->ch[c].data, kend, p->U[f], (int64_t)ub) ||
             overlaps(kv->ch[c].data, kend, p->V[f], (int64_t)vb))
@@ -253,9 +267,11 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
         // A workgroup covers 4 waves x `unroll` row groups of 64 / (rope_dim / 8) rows.
         // Interleaved rows keep more values live per row group: two groups fit the
         // register budget of four waves per SIMD, four would spill.
+        // fp8 rows hold half the registers and always take four.
         const int udflt = kv->pairing == KAMERA_INTERLEAVED ? 2 : 4;
         int unroll = env_int("KAMERA_ROTATE_UNROLL", udflt);
         if (unroll != 2 && unroll != 4) unroll = udflt;
+        if (kv->dtype == KAMERA_FP8_E4M3) unroll = 4;
         const int rows = 4 * unroll * (64 / (k.rope_dim / 8));
         const int bt = (int)std::min<int64_t>(kamera::kMaxBlockTokens,
                                               std::max<int64_t>(1, rows / k.heads));
@@ -296,6 +312,7 @@ kamera::CommonArgs common_args(const kamera_kv_desc& kv, const kamera_chunks& ch
     if (kv.page_size == (1 << sh)) a.page_shift = sh;
   a.out_page_shift = -1;
   a.pairing = kv.pairing;
+  a.dtype = kv.dtype;
   a.num_sections = kv.num_sections > 1 ? kv.num_sections : 1;
   int end = 0;
   for (int s = 0; s < 4; ++s) {
@@ -316,6 +333,7 @@ kamera::ChanArgs chan_args(const kamera_kv_desc& kv, int ci, const kamera_patch*
   a.page_stride = c.page_stride;
   a.U = p ? p->U[ci] : nullptr;
   a.V = p ? p->V[ci] : nullptr;
+  a.scale = kv.dtype == KAMERA_FP8_E4M3 ? c.scale : nullptr;
   a.heads = c.heads;
   a.dim = c.dim;
   a.rope_dim = c.rope_dim;
@@ -384,9 +402,10 @@ bool recall_tuned_ok(const kamera_kv_desc& src, const kamera_kv_desc& dst, const
       layer_extent(c, T, src.page_size, src.num_pages) < ((__int128)1 << 31) &&
       layer_extent(d, T, dst.page_size, dst.num_pages) < ((__int128)1 << 31);
   const bool factors_ok = m == 0 || (aligned(p->U[ci], 16) && aligned(p->V[ci], 16));
-  return src.dtype == KAMERA_BF16 && !((src.flags | dst.flags) & KAMERA_FLAG_GENERIC) &&
+  const uintptr_t va = vec_align(src.dtype);
+  return tuned_dtype(src.dtype) && !((src.flags | dst.flags) & KAMERA_FLAG_GENERIC) &&
          m <= kMfmaMaxRank && m % 8 == 0 && rope_ok && dim_ok && extent_ok &&
-         T < kMaxTunedTokens && aligned(c.data, 16) && aligned(d.data, 16) && factors_ok &&
+         T < kMaxTunedTokens && aligned(c.data, va) && aligned(d.data, va) && factors_ok &&
          strides_ok(c) && strides_ok(d) && (int64_t)c.heads * D < (1 << 24);
 }
 
@@ -406,7 +425,7 @@ kamera_status validate_recall(const kamera_kv_desc* src, const kamera_kv_desc* d
   if (dst->reserved1 != 0) return fail(KAMERA_E_SHAPE, "destination reserved1 must be 0");
   if (dst->flags & ~KAMERA_FLAG_GENERIC)
     return fail(KAMERA_E_SHAPE, "unknown destination flags 0x%x", dst->flags);
-  const int64_t es = src->dtype == KAMERA_BF16 ? 2 : 4;
+  const int64_t es = elem_bytes(src->dtype), fs = factor_bytes(src->dtype);
   const int m = p ? p->rank : 0;
   const int64_t T = ch->total_tokens;
   const bool empty = src->num_layers == 0 || T == 0;
@@ -444,8 +463,8 @@ kamera_status validate_recall(const kamera_kv_desc* src, const kamera_kv_desc* d
         return fail(KAMERA_E_ALIAS, "destination channel %d overlaps source channel %d", c, f);
       if (m > 0) {
         const int64_t F = (int64_t)src->ch[f].heads * src->ch[f].dim;
-        const int64_t ub = (int64_t)src->num_layers * T * m * es;
-        const int64_t vb = (int64_t)src->num_layers * ch->num_chunks * F * m * es;
+        const int64_t ub = (int64_t)src->num_layers * T * m * fs;
+        const int64_t vb = (int64_t)src->num_layers * ch->num_chunks * F * m * fs;
         if (overlaps(dst->ch[c].data, dend, p->U[f], ub) ||
             overlaps(dst->ch[c].data, dend, p->V[f], vb))
           return fail(KAMERA_E_ALIAS, "factors of channel %d overlap destination channel %d", f, c);

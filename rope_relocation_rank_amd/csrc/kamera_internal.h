@@ -20,6 +20,7 @@ struct ChanArgs {
   int64_t out_layer_stride, out_slot_stride, out_head_stride, out_page_stride;
   const void* U;  // [layers][tokens][rank]
   const void* V;  // [layers][chunks][heads*dim][rank]
+  const float* scale;  // fp8 E4M3: [layers] dequantisation scales; else unused
   int32_t heads, dim, rope_dim;
   int32_t fblocks;   // rotate+patch kernel: 128-feature blocks per token row
   int64_t blocks;    // tuned kernels: workgroups of this channel per layer
@@ -42,6 +43,7 @@ struct CommonArgs {
   int32_t block_tokens;     // tokens one workgroup covers (tuned kernels)
   int32_t page_shift;       // log2(page_size) when it is a power of two, else -1
   int32_t tail_mode;        // rotate+patch tail launch: 1 by boundary, 2 by token group
+  int32_t dtype;            // storage type: 0 bf16, 1 fp32, 2 fp8 E4M3 (factors bf16)
   // Positional variant: pairing 0 = NeoX half-split (i, i + r/2), 1 = interleaved
   // (2i, 2i + 1); delta holds num_sections values per chunk (M-RoPE when > 1), and
   // rotary pair i belongs to the first section s with i < sec_end[s].
@@ -79,12 +81,13 @@ hipError_t launch_form_batch(const FormArgs& a, int64_t p0, int count, hipStream
 // Gram matrices of every problem of one channel into G [problems][F][F].
 hipError_t launch_form_gram(const FormArgs& a, float* G, hipStream_t s);
 
-// Rotation only, bf16, 16-byte accesses: rope_dim in {16, 32, 64, 128}.
-// `unroll` row groups per wavefront (2 or 4).
+// Rotation only, bf16 (16-byte accesses) or fp8 (8-byte accesses): rope_dim in
+// {16, 32, 64, 128}.  `unroll` row groups per wavefront (2 or 4; fp8 always takes 4).
 hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unroll,
                               hipStream_t s);
 
-// Rotation + rank-m patch on MFMA, bf16: see kernels.hip for the shape conditions.
+// Rotation + rank-m patch on MFMA, bf16 or fp8 (fp8: rank % 8 == 0, tile_unroll 1):
+// see kernels.hip for the shape conditions.
 // With ChanArgs::out set it runs out of place (rank % 8 == 0; rank 0 allowed).
 // Covers nch (1 or 2) channels in one launch, plus a second launch for the token groups
 // that chunk boundaries cut when there is more than one chunk.
@@ -92,8 +95,8 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
 hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonArgs& cm,
                                       int tile_unroll, hipStream_t s);
 
-// Plain per-row kernel: any dim, even rope_dim, rank <= KAMERA_MAX_RANK, bf16 or fp32,
-// element-aligned pointers.  In place with rank 0 it only touches rotated dims; out of
+// Plain per-row kernel: any dim, even rope_dim, rank <= KAMERA_MAX_RANK, bf16, fp32 or
+// fp8, element-aligned pointers.  In place with rank 0 it only touches rotated dims; out of
 // place (ChanArgs::out set) it writes whole rows.
 hipError_t launch_generic(const ChanArgs& ch, const CommonArgs& cm, int dtype, hipStream_t s);
 

@@ -45,6 +45,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = 64 * kWavesPerBlock;
@@ -90,6 +91,61 @@ __device__ __forceinline__ void store_f(uint16_t* p, float y) {
 }
 __device__ __forceinline__ void store_f(float* p, float y) { *p = y; }
 
+// ------------------------------------------------------------------ fp8 (OCP E4M3)
+//
+// 8-bit KV elements are OCP FP8 E4M3 codes (the format gfx950's conversions use): a
+// lane's 8 elements are 8 bytes.  Code values become fp32 exactly; results go back
+// rounded to the nearest code, ties to the even one.  The conversion turns magnitudes
+// past the rounding range into NaN, so results are first clamped to +-448, the
+// largest finite code (saturation); NaN passes the clamp unchanged.
+
+// The two codes in the low (hi = false) or high 16 bits of w, as fp32.
+__device__ __forceinline__ float2 fp8_pair(uint32_t w, bool hi) {
+  const f32x2_t v = hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
+                       : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  return make_float2(v.x, v.y);
+}
+
+__device__ __forceinline__ float sat_fp8(float y) {
+  return fabsf(y) > 448.f ? copysignf(448.f, y) : y;
+}
+
+// `old` with its low (hi = false) or high 16 bits replaced by the codes of a and b.
+__device__ __forceinline__ uint32_t fp8_put(float a, float b, uint32_t old, bool hi) {
+  return hi ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_fp8(a), sat_fp8(b), (int)old, true)
+            : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_fp8(a), sat_fp8(b), (int)old, false);
+}
+
+__device__ __forceinline__ void unpack8(const u32x2_t& v, float (&x)[8]) {
+  float2 p = fp8_pair(v.x, false);
+  x[0] = p.x; x[1] = p.y;
+  p = fp8_pair(v.x, true);
+  x[2] = p.x; x[3] = p.y;
+  p = fp8_pair(v.y, false);
+  x[4] = p.x; x[5] = p.y;
+  p = fp8_pair(v.y, true);
+  x[6] = p.x; x[7] = p.y;
+}
+
+__device__ __forceinline__ u32x2_t pack8_fp8(const float (&y)[8]) {
+  u32x2_t r;
+  r.x = fp8_put(y[2], y[3], fp8_put(y[0], y[1], 0u, false), true);
+  r.y = fp8_put(y[6], y[7], fp8_put(y[4], y[5], 0u, false), true);
+  return r;
+}
+
+__device__ __forceinline__ u32x2_t load_nt(const uint8_t* p) {
+  return __builtin_nontemporal_load((const u32x2_t*)p);
+}
+__device__ __forceinline__ void store_nt(uint8_t* p, const u32x2_t& v) {
+  __builtin_nontemporal_store(v, (u32x2_t*)p);
+}
+
+__device__ __forceinline__ float load_f(const uint8_t* p) { return fp8_pair(*p, false).x; }
+__device__ __forceinline__ void store_f(uint8_t* p, float y) {
+  *p = (uint8_t)(fp8_put(y, 0.f, 0u, false) & 0xffu);
+}
+
 // Value of lane (l ^ X) within each 16-lane row, X in {1, 2, 4, 8}.  Every lane of the
 // wavefront must execute it.
 template <int X>
@@ -114,6 +170,14 @@ __device__ __forceinline__ u32x4_t lane_xor4(const u32x4_t& v) {
   return r;
 }
 
+template <int X>
+__device__ __forceinline__ u32x2_t lane_xor4(const u32x2_t& v) {
+  u32x2_t r;
+  r.x = lane_xor<X>(v.x);
+  r.y = lane_xor<X>(v.y);
+  return r;
+}
+
 // Word of results `y` with the halves flagged in `keep_lo` / `keep_hi` taken bit for
 // bit from `x` (pairs whose section delta is 0 do not move).
 __device__ __forceinline__ uint32_t keep_halves(uint32_t y, uint32_t x, bool keep_lo,
@@ -121,6 +185,69 @@ __device__ __forceinline__ uint32_t keep_halves(uint32_t y, uint32_t x, bool kee
   const uint32_t m = (keep_lo ? 0x0000ffffu : 0u) | (keep_hi ? 0xffff0000u : 0u);
   return (y & ~m) | (x & m);
 }
+
+// A lane's 8 results `o` with element e taken bit for bit from `x` where sn[e] == 0.
+__device__ __forceinline__ u32x4_t keep_elems(u32x4_t o, const u32x4_t& x, const float (&sn)[8]) {
+  o.x = keep_halves(o.x, x.x, sn[0] == 0.f, sn[1] == 0.f);
+  o.y = keep_halves(o.y, x.y, sn[2] == 0.f, sn[3] == 0.f);
+  o.z = keep_halves(o.z, x.z, sn[4] == 0.f, sn[5] == 0.f);
+  o.w = keep_halves(o.w, x.w, sn[6] == 0.f, sn[7] == 0.f);
+  return o;
+}
+
+__device__ __forceinline__ u32x2_t keep_elems(u32x2_t o, const u32x2_t& x, const float (&sn)[8]) {
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) m |= sn[4 * w + b] == 0.f ? 0xffu << (8 * b) : 0u;
+    o[w] = (o[w] & ~m) | (x[w] & m);
+  }
+  return o;
+}
+
+// Storage of the tuned kernels' elements: a lane holds 8 consecutive features of a
+// row, bf16 in a u32x4 (feature pair p in word p) or fp8 in a u32x2 (feature pair p in
+// half p & 1 of word p >> 1).  word / pair read feature pair pp; put and put_keep
+// write it (put_keep takes the features flagged k0 / k1 bit for bit from x).
+template <bool Q>
+struct Codec;
+
+template <>
+struct Codec<false> {
+  using E = uint16_t;
+  using XV = u32x4_t;
+  static __device__ __forceinline__ uint32_t word(const XV& x, int pp) { return x[pp]; }
+  static __device__ __forceinline__ float2 pair(uint32_t w, int) {
+    return make_float2(bf16_lo(w), bf16_hi(w));
+  }
+  static __device__ __forceinline__ void put(XV& o, int pp, float y0, float y1) {
+    o[pp] = pack2(y0, y1);
+  }
+  static __device__ __forceinline__ void put_keep(XV& o, const XV& x, int pp, float y0, float y1,
+                                                  bool k0, bool k1) {
+    o[pp] = keep_halves(pack2(y0, y1), x[pp], k0, k1);
+  }
+};
+
+template <>
+struct Codec<true> {
+  using E = uint8_t;
+  using XV = u32x2_t;
+  static __device__ __forceinline__ uint32_t word(const XV& x, int pp) { return x[pp >> 1]; }
+  static __device__ __forceinline__ float2 pair(uint32_t w, int pp) { return fp8_pair(w, pp & 1); }
+  static __device__ __forceinline__ void put(XV& o, int pp, float y0, float y1) {
+    const int k = pp >> 1;
+    o[k] = fp8_put(y0, y1, (pp & 1) ? o[k] : 0u, pp & 1);
+  }
+  static __device__ __forceinline__ void put_keep(XV& o, const XV& x, int pp, float y0, float y1,
+                                                  bool k0, bool k1) {
+    const int k = pp >> 1, sh = 16 * (pp & 1);
+    const uint32_t m = (k0 ? 0xffu : 0u) | (k1 ? 0xff00u : 0u);
+    const uint32_t v = (fp8_put(y0, y1, 0u, false) & 0xffffu & ~m) | ((x[k] >> sh) & m);
+    o[k] = (pp & 1) ? ((o[k] & 0xffffu) | (v << 16)) : v;
+  }
+};
 
 // ------------------------------------------------------------------ index helpers
 
@@ -309,7 +436,9 @@ __device__ __forceinline__ int32_t slot32(int page_size, int page_shift, const i
 }
 
 // Workgroup = `block_tokens` tokens of one layer, every head, taken as rows (token,
-// head) in order.  LPR lanes cover the rotated part of a row (8 dims each); one wave
+// head) in order.  LPR lanes cover the rotated part of a row (8 dims each: 16 bytes of
+// bf16, or 8 bytes of fp8 codes when Q; the rotation of code values needs no scale,
+// which cancels); one wave
 // instruction covers 64/LPR consecutive rows.  NeoX partner dims sit LPR/2 lanes away
 // and arrive by a lane exchange; interleaved (IL) partners are the other half of the
 // same 32-bit word.  Wave w takes row groups w, w + 4, ... (UNR of them per pass) and
@@ -319,9 +448,11 @@ __device__ __forceinline__ int32_t slot32(int page_size, int page_shift, const i
 // workgroup barrier, once, for the staged block table.  Dims >= rope_dim are never
 // touched; rows of chunks that do not move are not written; with M-RoPE sections, the
 // dims of pairs whose section delta is 0 keep their bits.
-template <int LPR, int UNR, bool PAGED, bool IL, bool SEC>
+template <bool Q, int LPR, int UNR, bool PAGED, bool IL, bool SEC>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(UNR == 4 ? 4 : 1)))
 void rotate_rows(ChanArgs ch, CommonArgs cm) {
+  using E = typename Codec<Q>::E;
+  using XV = typename Codec<Q>::XV;
   constexpr int RPI = 64 / LPR;
   constexpr int HX = LPR / 2;
   constexpr int HALF = 4 * LPR;  // rotary pairs of a head: rope_dim / 2
@@ -340,15 +471,15 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
   const float sgn = q < HX ? -1.f : 1.f;
   const int H = ch.heads;
   const int nrows = (int)(t1 - tb0) * H;
-  uint16_t* base = (uint16_t*)ch.data + layer * ch.layer_stride + 8 * q;
+  E* base = (E*)ch.data + layer * ch.layer_stride + 8 * q;
   int p0 = 0;
   if (PAGED) {
     p0 = stage_block_table(cm, tb0, t1, sbt);
     __syncthreads();
   }
   for (int rbase = 0; rbase < nrows; rbase += ROWS) {
-    u32x4_t xv[UNR];
-    uint16_t* ptr[UNR];
+    XV xv[UNR];
+    E* ptr[UNR];
     int64_t tok[UNR];
     bool ok[UNR];
 #pragma unroll
@@ -357,7 +488,7 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
       ok[k] = R < nrows;
       ptr[k] = base;
       tok[k] = tb0;
-      xv[k] = u32x4_t{0u, 0u, 0u, 0u};
+      xv[k] = (XV)(0u);
       if (ok[k]) {
         const int tl = R / H;
         const int h = R - tl * H;
@@ -404,13 +535,10 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
           }
 #pragma unroll
           for (int e = 0; e < 8; ++e) y[e] = fmaf(a[e], cs[e], b[e] * sn[e]);
-          u32x4_t o = pack8(y);
-          if constexpr (SEC) {
-            o.x = keep_halves(o.x, xv[k].x, sn[0] == 0.f, sn[1] == 0.f);
-            o.y = keep_halves(o.y, xv[k].y, sn[2] == 0.f, sn[3] == 0.f);
-            o.z = keep_halves(o.z, xv[k].z, sn[4] == 0.f, sn[5] == 0.f);
-            o.w = keep_halves(o.w, xv[k].w, sn[6] == 0.f, sn[7] == 0.f);
-          }
+          XV o;
+          if constexpr (Q) o = pack8_fp8(y);
+          else o = pack8(y);
+          if constexpr (SEC) o = keep_elems(o, xv[k], sn);
           if (ok[k] && tok[k] >= t0 && tok[k] < s1) store_nt(ptr[k], o);
         }
       }
@@ -439,9 +567,10 @@ __device__ __forceinline__ u32x4_t load_frag(const uint16_t* row, int k0, int m,
 }
 
 // Per-workgroup constants of the rotate+patch kernel that the tile loop reads.
+template <bool Q>
 struct PatchCtx {
-  uint16_t* base;       // lane's element (layer, slot 0, head h, dim d0)
-  uint16_t* obase;      // same element of the destination (out of place)
+  typename Codec<Q>::E* base;   // lane's element (layer, slot 0, head h, dim d0)
+  typename Codec<Q>::E* obase;  // same element of the destination (out of place)
   const uint16_t* Ul;   // U of this layer and channel
   const int* sbt;       // staged block table (paged)
   const int* osbt;      // staged destination block table (paged destination)
@@ -454,12 +583,13 @@ struct PatchCtx {
   float sgn;
   bool lane_on, rot_lane;
   bool mixed;           // M-RoPE sections: some pairs may not turn
+  float qs, qinv;       // fp8: the layer's dequantisation scale and its reciprocal
 };
 
 // KV, row offsets and U fragments of the TU tiles a wave loads together.
-template <int MK, int TU>
+template <bool Q, int MK, int TU>
 struct TileSet {
-  u32x4_t x[TU][4];
+  typename Codec<Q>::XV x[TU][4];
   // Element offset of the row to store, -1 = none: from the lane's base in place, from
   // the lane's destination base out of place.
   int32_t off[TU][4];
@@ -469,10 +599,10 @@ struct TileSet {
 // Loads tiles kt, kt + 4, ... (TU of them, those below k_hi), keeping tokens in [t0, s1).
 // OUT: 0 in place, 1 contiguous destination, 2 paged destination; a row is loaded
 // only when both its source and its destination slot exist.
-template <int MK, bool M8, bool PAGED, int TU, int OUT>
-__device__ __forceinline__ void load_tiles(const PatchCtx& c, const CommonArgs& cm, int kt,
+template <bool Q, int MK, bool M8, bool PAGED, int TU, int OUT>
+__device__ __forceinline__ void load_tiles(const PatchCtx<Q>& c, const CommonArgs& cm, int kt,
                                            int k_hi, int64_t t0, int64_t s1,
-                                           TileSet<MK, TU>& T) {
+                                           TileSet<Q, MK, TU>& T) {
 #pragma unroll
   for (int u = 0; u < TU; ++u) {
     const int64_t ts = c.tb0 + 16 * (int64_t)(kt + kWavesPerBlock * u);
@@ -481,7 +611,7 @@ __device__ __forceinline__ void load_tiles(const PatchCtx& c, const CommonArgs& 
     for (int i = 0; i < 4; ++i) {
       const int64_t t = ts + 4 * c.g + i;
       T.off[u][i] = -1;
-      T.x[u][i] = u32x4_t{0u, 0u, 0u, 0u};
+      T.x[u][i] = (typename Codec<Q>::XV)(0u);
       if (tile_on && c.lane_on && t >= t0 && t < s1) {
         int32_t so = slot32<PAGED>(cm.page_size, cm.page_shift, c.sbt, c.p0, c.page_stride,
                                    c.slot_stride, (int)t);
@@ -522,13 +652,18 @@ __device__ __forceinline__ void load_tiles(const PatchCtx& c, const CommonArgs& 
 //
 // Phases sit in LDS as (cos, sin) per rotary pair.  With M-RoPE sections a pair whose
 // section delta is 0 has sin exactly 0 and is not rotated.
-template <int MK, int HX, int TU, int OUT>
-__device__ __forceinline__ void finish_tiles(const PatchCtx& c, const u32x4_t* sV,
-                                             const float4* sph2, const TileSet<MK, TU>& T) {
+//
+// fp8 (Q): the rotation runs on code values; with a patch the accumulator starts at
+// s * (rotated codes), the MFMA adds the patch in value units, and the sum times 1/s
+// is encoded.
+template <bool Q, int MK, int HX, int TU, int OUT>
+__device__ __forceinline__ void finish_tiles(const PatchCtx<Q>& c, const u32x4_t* sV,
+                                             const float4* sph2, const TileSet<Q, MK, TU>& T) {
+  using P = Codec<Q>;
   const float2* sph = reinterpret_cast<const float2*>(sph2);
 #pragma unroll
   for (int u = 0; u < TU; ++u) {
-    u32x4_t out[4];
+    typename P::XV out[4];
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {  // features 2pp, 2pp + 1 of the lane's 8
       // (cos, sin) of the pairs of the two features, and whether each one turns.
@@ -543,13 +678,14 @@ __device__ __forceinline__ void finish_tiles(const PatchCtx& c, const u32x4_t* s
       float r0[4], r1[4];  // rotated (or unrotated) values of the two features
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t w = T.x[u][i][pp];
-        const float a0 = bf16_lo(w), a1 = bf16_hi(w);
+        const uint32_t w = P::word(T.x[u][i], pp);
+        const float2 av = P::pair(w, pp);
+        const float a0 = av.x, a1 = av.y;
         float y0 = a0, y1 = a1;
         if constexpr (HX > 0) {
-          const uint32_t pw = lane_xor<HX>(w);
-          y0 = fmaf(a0, ph.x, bf16_lo(pw) * (c.sgn * ph.y));
-          y1 = fmaf(a1, ph.z, bf16_hi(pw) * (c.sgn * ph.w));
+          const float2 bv = P::pair(lane_xor<HX>(w), pp);
+          y0 = fmaf(a0, ph.x, bv.x * (c.sgn * ph.y));
+          y1 = fmaf(a1, ph.z, bv.y * (c.sgn * ph.w));
         } else if constexpr (HX < 0) {
           y0 = fmaf(a0, ph.x, -(a1 * ph.y));
           y1 = fmaf(a1, ph.x, a0 * ph.y);
@@ -562,13 +698,13 @@ __device__ __forceinline__ void finish_tiles(const PatchCtx& c, const u32x4_t* s
         // element is copied bit for bit.
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          out[i][pp] = keep_halves(pack2(r0[i], r1[i]), T.x[u][i][pp], !turn0, !turn1);
+          P::put_keep(out[i], T.x[u][i], pp, r0[i], r1[i], !turn0, !turn1);
       } else {
         f32x4_t acc0, acc1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc0[i] = r0[i];
-          acc1[i] = r1[i];
+          acc0[i] = Q ? r0[i] * c.qs : r0[i];
+          acc1[i] = Q ? r1[i] * c.qs : r1[i];
         }
 #pragma unroll
         for (int ks = 0; ks < MK; ++ks) {
@@ -580,7 +716,8 @@ __device__ __forceinline__ void finish_tiles(const PatchCtx& c, const u32x4_t* s
           acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc1, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[i][pp] = pack2(acc0[i], acc1[i]);
+        for (int i = 0; i < 4; ++i)
+          P::put(out[i], pp, Q ? acc0[i] * c.qinv : acc0[i], Q ? acc1[i] * c.qinv : acc1[i]);
       }
       // Keep the scheduler from hoisting every feature pair's LDS reads at once (it
       // would hold all B fragments live and lower the occupancy).
@@ -595,22 +732,22 @@ __device__ __forceinline__ void finish_tiles(const PatchCtx& c, const u32x4_t* s
 // The wave's tiles (16-token tile kt with kt = wave mod 4) that meet [t0, s1), TU at a
 // time; only tokens in [t0, s1) are loaded and stored.  When `use_pre`, `pre` already
 // holds the wave's first group of tiles (loaded before the workgroup staged the chunk).
-template <int MK, bool M8, bool PAGED, int HX, int TU, int OUT>
-__device__ __forceinline__ void patch_tiles(const PatchCtx& c, const CommonArgs& cm,
+template <bool Q, int MK, bool M8, bool PAGED, int HX, int TU, int OUT>
+__device__ __forceinline__ void patch_tiles(const PatchCtx<Q>& c, const CommonArgs& cm,
                                             const u32x4_t* sV, const float4* sph2,
                                             int64_t t0, int64_t s1,
-                                            const TileSet<MK, TU>& pre, bool use_pre) {
+                                            const TileSet<Q, MK, TU>& pre, bool use_pre) {
   const int k_lo = (int)((t0 - c.tb0) >> 4);
   const int k_hi = (int)((s1 - c.tb0 + 15) >> 4);
   int kt = k_lo + ((c.wave - k_lo) % kWavesPerBlock + kWavesPerBlock) % kWavesPerBlock;
   if (use_pre) {
-    finish_tiles<MK, HX, TU, OUT>(c, sV, sph2, pre);
+    finish_tiles<Q, MK, HX, TU, OUT>(c, sV, sph2, pre);
     kt += kWavesPerBlock * TU;
   }
   for (; kt < k_hi; kt += kWavesPerBlock * TU) {
-    TileSet<MK, TU> T;
-    load_tiles<MK, M8, PAGED, TU, OUT>(c, cm, kt, k_hi, t0, s1, T);
-    finish_tiles<MK, HX, TU, OUT>(c, sV, sph2, T);
+    TileSet<Q, MK, TU> T;
+    load_tiles<Q, MK, M8, PAGED, TU, OUT>(c, cm, kt, k_hi, t0, s1, T);
+    finish_tiles<Q, MK, HX, TU, OUT>(c, sV, sph2, T);
   }
 }
 
@@ -631,8 +768,8 @@ __device__ __forceinline__ void patch_tiles(const PatchCtx& c, const CommonArgs&
 //
 // OUT != 0 is the out-of-place form (recall): rows are read through the source layout
 // and whole result rows written through the destination layout (OUT 1 contiguous, 2
-// paged); MK = 0 is its no-patch form.
-template <int MK, bool M8, bool PAGED, int TU, bool TAIL, int OUT>
+// paged); MK = 0 is its no-patch form.  Q: fp8 E4M3 elements (bf16 factors).
+template <bool Q, int MK, bool M8, bool PAGED, int TU, bool TAIL, int OUT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(!TAIL && TU == 1 && (MK <= 1 || (MK == 2 && OUT == 0)) ? 4 : 1)))
 void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t blocks_per_layer,
                          int xcd_group) {
@@ -664,7 +801,8 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
   const int64_t tg = b / fblocks;
   const int fbk = (int)(b - tg * fblocks);
 
-  PatchCtx c;
+  using E = typename Codec<Q>::E;
+  PatchCtx<Q> c;
   c.lane = lane;
   c.wave = threadIdx.x >> 6;
   c.c16 = lane & 15;
@@ -688,12 +826,17 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
 
   c.slot_stride = (int32_t)KAMERA_CH(slot_stride);
   c.page_stride = (int32_t)KAMERA_CH(page_stride);
-  c.base = (uint16_t*)KAMERA_CH(data) + layer * KAMERA_CH(layer_stride) +
+  c.base = (E*)KAMERA_CH(data) + layer * KAMERA_CH(layer_stride) +
            (int64_t)h * KAMERA_CH(head_stride) + d0;
+  c.qs = c.qinv = 1.f;
+  if constexpr (Q) {
+    c.qs = KAMERA_CH(scale)[layer];
+    c.qinv = 1.f / c.qs;
+  }
   c.obase = nullptr;
   c.opage_stride = c.oslot_stride = 0;
   if constexpr (OUT > 0) {
-    c.obase = (uint16_t*)KAMERA_CH(out) + layer * KAMERA_CH(out_layer_stride) +
+    c.obase = (E*)KAMERA_CH(out) + layer * KAMERA_CH(out_layer_stride) +
               (int64_t)h * KAMERA_CH(out_head_stride) + d0;
     c.oslot_stride = (int32_t)KAMERA_CH(out_slot_stride);
     c.opage_stride = (int32_t)KAMERA_CH(out_page_stride);
@@ -758,12 +901,12 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
   };
 #define KAMERA_PATCH_SWITCH(PRE, USE)                                                           \
   switch (rotate ? hx : 0) {                                                                    \
-    case 1: patch_tiles<MK, M8, PAGED, 1, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
-    case 2: patch_tiles<MK, M8, PAGED, 2, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
-    case 4: patch_tiles<MK, M8, PAGED, 4, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
-    case 8: patch_tiles<MK, M8, PAGED, 8, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;       \
-    case -1: patch_tiles<MK, M8, PAGED, -1, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;     \
-    default: patch_tiles<MK, M8, PAGED, 0, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;      \
+    case 1: patch_tiles<Q, MK, M8, PAGED, 1, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;    \
+    case 2: patch_tiles<Q, MK, M8, PAGED, 2, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;    \
+    case 4: patch_tiles<Q, MK, M8, PAGED, 4, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;    \
+    case 8: patch_tiles<Q, MK, M8, PAGED, 8, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;    \
+    case -1: patch_tiles<Q, MK, M8, PAGED, -1, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;  \
+    default: patch_tiles<Q, MK, M8, PAGED, 0, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;   \
   }
 
   if (PAGED || OUT == 2) __syncthreads();  // staged block tables
@@ -771,8 +914,8 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
     const int ntiles = (int)((c.t1 - c.tb0 + 15) >> 4);
     // The wave's first tiles are loaded before anything else, so their HBM latency
     // overlaps the chunk lookup, the LDS staging and the barrier.
-    TileSet<MK, TU> pre;
-    load_tiles<MK, M8, PAGED, TU, OUT>(c, cm, c.wave, ntiles, c.tb0, c.t1, pre);
+    TileSet<Q, MK, TU> pre;
+    load_tiles<Q, MK, M8, PAGED, TU, OUT>(c, cm, c.wave, ntiles, c.tb0, c.t1, pre);
     const ChunkRef ck = find_chunk_wave(cm, c.tb0);
     const int64_t t0 = c.tb0, s1 = min(c.t1, ck.end);
     if (s1 <= t0) return;  // offsets that do not cover the group: nothing here
@@ -788,7 +931,7 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
     KAMERA_PATCH_SWITCH(pre, true)
   } else {
     // The remaining chunks of the group, one after the other.
-    TileSet<MK, TU> none;
+    TileSet<Q, MK, TU> none;
     int64_t t0 = start;
     ChunkRef ck = find_chunk_wave(cm, t0, from);
     bool staged = false;
@@ -836,15 +979,18 @@ __device__ __forceinline__ bool slot_of(int64_t t, int page_size, const int32_t*
 
 template <typename T>
 __device__ __forceinline__ void copy_bits(T* dst, const T* src) {
-  if constexpr (sizeof(T) == 2) *(uint16_t*)dst = *(const uint16_t*)src;
+  if constexpr (sizeof(T) == 1) *(uint8_t*)dst = *(const uint8_t*)src;
+  else if constexpr (sizeof(T) == 2) *(uint16_t*)dst = *(const uint16_t*)src;
   else *(uint32_t*)dst = *(const uint32_t*)src;
 }
 
 // One thread per (layer, token, head) row; any dim, any even rope_dim, any rank.
 // OUT: the row is read through the channel's layout and written through its
 // destination layout, whole (elements the call leaves alone are copied bit for bit).
+// T = uint8_t: fp8 E4M3 codes of values scale * code, with bf16 factors.
 template <typename T, bool OUT>
 __global__ __launch_bounds__(kBlock) void generic_rows(ChanArgs ch, CommonArgs cm) {
+  using FT = std::conditional_t<sizeof(T) == 1, uint16_t, T>;  // factor type
   const int64_t H = ch.heads, Tt = cm.total_tokens;
   const int64_t nrows = (int64_t)cm.num_layers * Tt * H;
   const int m = cm.rank, D = ch.dim, r = ch.rope_dim, half = r >> 1;
@@ -872,8 +1018,10 @@ __global__ __launch_bounds__(kBlock) void generic_rows(ChanArgs ch, CommonArgs c
       for (int d = 0; d < D; ++d) copy_bits(dst + d, src + d);
       continue;
     }
-    const T* u = (const T*)ch.U + (layer * Tt + t) * m;
-    const T* vr = (const T*)ch.V + ((layer * cm.num_chunks + j) * F + h * D) * m;
+    const FT* u = (const FT*)ch.U + (layer * Tt + t) * m;
+    const FT* vr = (const FT*)ch.V + ((layer * cm.num_chunks + j) * F + h * D) * m;
+    const float qs = sizeof(T) == 1 ? ch.scale[layer] : 1.f;
+    const float qinv = sizeof(T) == 1 ? 1.f / qs : 1.f;
     for (int i = 0; i < half; ++i) {
       const int d0 = cm.pairing == 1 ? 2 * i : i;
       const int d1 = cm.pairing == 1 ? 2 * i + 1 : i + half;
@@ -887,7 +1035,7 @@ __global__ __launch_bounds__(kBlock) void generic_rows(ChanArgs ch, CommonArgs c
         }
         continue;
       }
-      float a = load_f(src + d0), b = load_f(src + d1);
+      float a = load_f(src + d0) * qs, b = load_f(src + d1) * qs;
       if (di != 0) {
         float c, s;
         phase_generic(cm.theta, r, i, di, c, s);
@@ -900,11 +1048,12 @@ __global__ __launch_bounds__(kBlock) void generic_rows(ChanArgs ch, CommonArgs c
         a += dot_patch(u, vr + (int64_t)d0 * m, m);
         b += dot_patch(u, vr + (int64_t)d1 * m, m);
       }
-      store_f(dst + d0, a);
-      store_f(dst + d1, b);
+      store_f(dst + d0, a * qinv);
+      store_f(dst + d1, b * qinv);
     }
     if (m > 0)
-      for (int d = r; d < D; ++d) store_f(dst + d, load_f(src + d) + dot_patch(u, vr + (int64_t)d * m, m));
+      for (int d = r; d < D; ++d)
+        store_f(dst + d, (load_f(src + d) * qs + dot_patch(u, vr + (int64_t)d * m, m)) * qinv);
     else if (OUT)
       for (int d = r; d < D; ++d) copy_bits(dst + d, src + d);
   }
@@ -920,10 +1069,12 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
   const dim3 grid((unsigned)blocks);
   const bool il = cm.pairing == 1;
   const bool sec = cm.num_sections > 1;
+  const bool q = cm.dtype == 2;
 #define KAMERA_LAUNCH_ROT4(LPR, PG, IL, SC)                                                          \
   do {                                                                                               \
-    if (unroll == 2) hipLaunchKernelGGL((rotate_rows<LPR, 2, PG, IL, SC>), grid, dim3(kBlock), 0, s, ch, cm); \
-    else hipLaunchKernelGGL((rotate_rows<LPR, 4, PG, IL, SC>), grid, dim3(kBlock), 0, s, ch, cm);   \
+    if (q) hipLaunchKernelGGL((rotate_rows<true, LPR, 4, PG, IL, SC>), grid, dim3(kBlock), 0, s, ch, cm); \
+    else if (unroll == 2) hipLaunchKernelGGL((rotate_rows<false, LPR, 2, PG, IL, SC>), grid, dim3(kBlock), 0, s, ch, cm); \
+    else hipLaunchKernelGGL((rotate_rows<false, LPR, 4, PG, IL, SC>), grid, dim3(kBlock), 0, s, ch, cm); \
   } while (0)
 #define KAMERA_LAUNCH_ROT3(LPR, PG, IL)                 \
   do {                                                  \
@@ -969,21 +1120,26 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
   const bool m8 = cm.rank % 8 == 0;
   // Out of place (recall): 1 contiguous destination, 2 paged destination.
   const int out = c0.out == nullptr ? 0 : (cm.out_page_size > 0 ? 2 : 1);
+  const bool q = cm.dtype == 2;
   if (out > 0 && (!m8 || (nch > 1 && c1.out == nullptr))) return hipErrorInvalidValue;
   if (out == 0 && mk == 0) return hipErrorInvalidValue;
-#define KAMERA_LAUNCH_K(MK, M8, PG, TU, TL, OUT, XG)                                           \
-  hipLaunchKernelGGL((relocate_patch_rows<MK, M8, PG, TU, TL, OUT>), grid, dim3(kBlock), 0, s, \
+  if (q && !m8) return hipErrorInvalidValue;
+#define KAMERA_LAUNCH_K(Q, MK, M8, PG, TU, TL, OUT, XG)                                           \
+  hipLaunchKernelGGL((relocate_patch_rows<Q, MK, M8, PG, TU, TL, OUT>), grid, dim3(kBlock), 0, s, \
                      c0, c1, cm, bpl, XG)
 #define KAMERA_LAUNCH_IN(MK, PG, TL, XG)                                                       \
   do {                                                                                         \
-    if (m8 && tile_unroll == 2 && !TL) KAMERA_LAUNCH_K(MK, true, PG, 2, false, 0, XG);         \
-    else if (m8) KAMERA_LAUNCH_K(MK, true, PG, 1, TL, 0, XG);                                  \
-    else KAMERA_LAUNCH_K(MK, false, PG, 1, TL, 0, XG);                                         \
+    if (q) KAMERA_LAUNCH_K(true, MK, true, PG, 1, TL, 0, XG);                                  \
+    else if (m8 && tile_unroll == 2 && !TL) KAMERA_LAUNCH_K(false, MK, true, PG, 2, false, 0, XG); \
+    else if (m8) KAMERA_LAUNCH_K(false, MK, true, PG, 1, TL, 0, XG);                           \
+    else KAMERA_LAUNCH_K(false, MK, false, PG, 1, TL, 0, XG);                                  \
   } while (0)
 #define KAMERA_LAUNCH_OUT(MK, PG, TL, XG)                                     \
   do {                                                                        \
-    if (out == 1) KAMERA_LAUNCH_K(MK, true, PG, 1, TL, 1, XG);                \
-    else KAMERA_LAUNCH_K(MK, true, PG, 1, TL, 2, XG);                         \
+    if (q && out == 1) KAMERA_LAUNCH_K(true, MK, true, PG, 1, TL, 1, XG);     \
+    else if (q) KAMERA_LAUNCH_K(true, MK, true, PG, 1, TL, 2, XG);            \
+    else if (out == 1) KAMERA_LAUNCH_K(false, MK, true, PG, 1, TL, 1, XG);    \
+    else KAMERA_LAUNCH_K(false, MK, true, PG, 1, TL, 2, XG);                  \
   } while (0)
 #define KAMERA_LAUNCH_PG(MK, TL, XG)                                          \
   do {                                                                        \
@@ -1032,7 +1188,11 @@ hipError_t launch_generic(const ChanArgs& ch, const CommonArgs& cm, int dtype, h
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
   const bool out = ch.out != nullptr;
-  if (dtype == 0 && out)
+  if (dtype == 2 && out)
+    hipLaunchKernelGGL((generic_rows<uint8_t, true>), dim3((unsigned)blocks), dim3(kBlock), 0, s, ch, cm);
+  else if (dtype == 2)
+    hipLaunchKernelGGL((generic_rows<uint8_t, false>), dim3((unsigned)blocks), dim3(kBlock), 0, s, ch, cm);
+  else if (dtype == 0 && out)
     hipLaunchKernelGGL((generic_rows<uint16_t, true>), dim3((unsigned)blocks), dim3(kBlock), 0, s, ch, cm);
   else if (dtype == 0)
     hipLaunchKernelGGL((generic_rows<uint16_t, false>), dim3((unsigned)blocks), dim3(kBlock), 0, s, ch, cm);

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(PKG, "libkamera.so")
 
 KAMERA_OK, KAMERA_E_NULL, KAMERA_E_SHAPE, KAMERA_E_UNSUPPORTED = 0, 1, 2, 3
 KAMERA_E_ALIGN, KAMERA_E_ALIAS, KAMERA_E_HIP = 4, 5, 6
-KAMERA_BF16, KAMERA_F32 = 0, 1
+KAMERA_BF16, KAMERA_F32, KAMERA_FP8_E4M3 = 0, 1, 2
+KAMERA_ABI_VERSION = 3
 KAMERA_NEOX_HALF = 0
 KAMERA_INTERLEAVED = 1
 KAMERA_FLAG_GENERIC = 1
@@ -34,7 +35,8 @@ class kamera_channel(C.Structure):
     _fields_ = [("data", C.c_void_p), ("heads", C.c_int32), ("dim", C.c_int32),
                 ("rope_dim", C.c_int32), ("reserved0", C.c_int32),
                 ("layer_stride", C.c_int64), ("slot_stride", C.c_int64),
-                ("head_stride", C.c_int64), ("page_stride", C.c_int64)]
+                ("head_stride", C.c_int64), ("page_stride", C.c_int64),
+                ("scale", C.c_void_p)]
 
 
 class kamera_kv_desc(C.Structure):
@@ -180,18 +182,22 @@ def _dtype_code(t) -> int:
         return KAMERA_BF16
     if t.dtype == torch.float32:
         return KAMERA_F32
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return KAMERA_FP8_E4M3
     raise TypeError(f"unsupported KV dtype {t.dtype}")
 
 
 def channel(data, *, heads: int, dim: int, rope_dim: int, layer_stride: int,
             slot_stride: int, head_stride: int, page_stride: int = 0,
-            element_offset: int = 0) -> kamera_channel:
-    """Channel view over a tensor's storage; strides in elements."""
+            element_offset: int = 0, scale=None) -> kamera_channel:
+    """Channel view over a tensor's storage; strides in elements.  `scale`: fp8 KV's
+    float32 [num_layers] dequantisation scales (a device tensor)."""
     c = kamera_channel()
     c.data = data.data_ptr() + element_offset * data.element_size()
     c.heads, c.dim, c.rope_dim, c.reserved0 = heads, dim, rope_dim, 0
     c.layer_stride, c.slot_stride = layer_stride, slot_stride
     c.head_stride, c.page_stride = head_stride, page_stride
+    c.scale = None if scale is None else scale.data_ptr()
     return c
 
 

@@ -8,16 +8,18 @@ from . import kamera as K
 def descriptors(buffers, layouts, *, dtype_code: int, num_layers: int, theta: float,
                 offsets_t, delta_t, total_tokens: int, rank: int = 0, U=(), V=(),
                 page_size: int = 0, num_pages: int = 0, block_table_t=None, flags: int = 0,
-                pairing: int = 0, sections=()):
+                pairing: int = 0, sections=(), scales=()):
     """Descriptors for channels laid out as `layouts` (dicts with buffer, offset,
-    heads, dim, rope_dim and element strides) over the KV tensors in `buffers`."""
+    heads, dim, rope_dim and element strides) over the KV tensors in `buffers`;
+    `scales`: fp8 per-channel [layers] float32 device tensors."""
     chans = []
-    for lay in layouts:
+    for c, lay in enumerate(layouts):
         chans.append(K.channel(buffers[lay["buffer"]], heads=lay["heads"], dim=lay["dim"],
                                rope_dim=lay["rope_dim"], layer_stride=lay["layer_stride"],
                                slot_stride=lay["slot_stride"], head_stride=lay["head_stride"],
                                page_stride=lay.get("page_stride", 0),
-                               element_offset=lay.get("offset", 0)))
+                               element_offset=lay.get("offset", 0),
+                               scale=scales[c] if c < len(scales) else None))
     kv = K.kv_desc(chans, dtype=dtype_code, num_layers=num_layers, rope_theta=theta,
                    page_size=page_size, num_pages=num_pages, block_table=block_table_t,
                    flags=flags, pairing=pairing, sections=sections)
@@ -30,15 +32,14 @@ def descriptors(buffers, layouts, *, dtype_code: int, num_layers: int, theta: fl
 
 def descriptors_for(inp, flags: int = 0):
     """Descriptors for a synth.Inputs instance."""
-    import torch
     w = inp.workload
-    code = K.KAMERA_BF16 if inp.buffers[0].dtype == torch.bfloat16 else K.KAMERA_F32
+    code = K._dtype_code(inp.buffers[0])
     return descriptors(inp.buffers, inp.layouts, dtype_code=code, num_layers=w.layers,
                        theta=w.theta, offsets_t=inp.offsets_t, delta_t=inp.delta_t,
                        total_tokens=inp.struct.total_tokens, rank=inp.rank, U=inp.U, V=inp.V,
                        page_size=w.page_size, num_pages=inp.pool_pages,
                        block_table_t=inp.block_table_t, flags=flags, pairing=w.pairing,
-                       sections=w.sections)
+                       sections=w.sections, scales=inp.scales)
 
 
 def run(inp, stream=None, flags: int = 0) -> None:
@@ -56,10 +57,9 @@ def plan(inp, flags: int = 0):
 
 def recall_descriptors(rinp, flags: int = 0):
     """(src, dst, chunks, patch) descriptors for a synth.RecallInputs instance."""
-    import torch
     src, ch, patch = descriptors_for(rinp.src, flags)
     w = rinp.workload
-    code = K.KAMERA_BF16 if rinp.dst_buffers[0].dtype == torch.bfloat16 else K.KAMERA_F32
+    code = K._dtype_code(rinp.dst_buffers[0])
     chans = []
     for lay in rinp.dst_layouts:
         chans.append(K.channel(rinp.dst_buffers[lay["buffer"]], heads=lay["heads"], dim=lay["dim"],

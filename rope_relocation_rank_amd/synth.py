@@ -13,6 +13,11 @@ channel) through numpy's SeedSequence; kind 0 = KV, 1 = U, 2 = V, 3 = structure,
 the block-table permutation, then outlier feature indices; the destination stream
 draws the destination block-table permutation.
 
+8-bit workloads (dtype "fp8") hold OCP FP8 E4M3 codes: the KV values are drawn as
+above in fp32, each (layer, channel) gets the scale s = max |value| / 224 (half the
+code range, so rotation and patch keep headroom), and the codes are PyTorch's E4M3
+encoding of value / s.  Their factors are bf16.
+
 Recall workloads (out of place) read a canonical store laid out as the workload says
 and write into a destination cache, paged with its own random block table or
 contiguous; destination slots are pre-filled with a NaN sentinel so that any slot the
@@ -28,6 +33,7 @@ import numpy as np
 
 KIND_KV, KIND_U, KIND_V, KIND_STRUCT, KIND_DST = 0, 1, 2, 3, 4
 DST_SENTINEL = 0x7FC1  # bf16 NaN with a payload the operator never produces
+DST_SENTINEL_FP8 = 0x7F  # E4M3 NaN: the operator never produces it from finite inputs
 
 
 @dataclass(frozen=True)
@@ -72,7 +78,12 @@ class Workload:
 
     @property
     def elem_size(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        return {"bf16": 2, "fp8": 1}.get(self.dtype, 4)
+
+    @property
+    def factor_size(self) -> int:
+        """Bytes of a patch-factor element (bf16 for fp8 KV)."""
+        return 2 if self.dtype == "fp8" else self.elem_size
 
 
 WORKLOADS = {
@@ -100,6 +111,19 @@ WORKLOADS = {
         theta=1e6, rank=64, tokens=32768, delta=65536, page_size=16, pool_pages=2048,
         note="72B-shaped long-video paged cache: 80 layers, 8 KV heads x 128, T=32768 in "
              "16-token pages scattered by a random block table, delta +65536, rank-64"),
+    "qwen25vl7b_segment_fp8": Workload(
+        key="qwen25vl7b_segment_fp8", wid=6, family="gqa", layers=28, heads=4, head_dim=128,
+        theta=1e6, rank=32, passes=(0, 32), tokens=4096, delta=-1536, outliers=4, dtype="fp8",
+        note="Qwen2.5-VL-7B-shaped video segment in an fp8 E4M3 cache (per-layer scales): "
+             "28 layers, 4 KV heads x 128, T=4096, delta -1536; rotation-only pass then "
+             "rank-32 patch pass"),
+    "long_video_72b_paged_fp8": Workload(
+        key="long_video_72b_paged_fp8", wid=7, family="gqa", layers=80, heads=8, head_dim=128,
+        theta=1e6, rank=64, tokens=32768, delta=65536, page_size=16, pool_pages=2048,
+        dtype="fp8",
+        note="72B-shaped long-video paged cache in fp8 E4M3 (per-layer scales): 80 layers, "
+             "8 KV heads x 128, T=32768 in 16-token pages under a random block table, "
+             "delta +65536, rank-64"),
     "recall_72b_paged": Workload(
         key="recall_72b_paged", wid=5, family="gqa", layers=80, heads=8, head_dim=128,
         theta=1e6, rank=64, tokens=32768, delta=65536, recall=True, dst_page_size=16,
@@ -262,14 +286,47 @@ class Inputs:
     layouts: list                  # per channel layout dicts
     U: list = field(default_factory=list)   # per channel [L][T][m] (torch) or []
     V: list = field(default_factory=list)   # per channel [L][n][F][m]
+    scales: list = field(default_factory=list)  # fp8: per channel float32 [L]; else []
     offsets_t: object = None
     delta_t: object = None
     block_table_t: object = None
 
 
 def _torch_dtype(w: Workload):
+    """Storage dtype of the KV buffers (fp8 codes travel as uint8)."""
     import torch
-    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return {"bf16": torch.bfloat16, "fp8": torch.uint8}.get(w.dtype, torch.float32)
+
+
+def _factor_dtype(w: Workload):
+    import torch
+    return torch.bfloat16 if w.dtype in ("bf16", "fp8") else torch.float32
+
+
+def _quantize_fp8(buffers, layouts, layers: int):
+    """fp32 value buffers -> (uint8 E4M3 code buffers, per channel [L] scales):
+    s = max |value| / 224 over each (layer, channel), codes = E4M3(value / s)."""
+    import torch
+    codes = [torch.empty(b.shape, dtype=torch.uint8, device=b.device) for b in buffers]
+    scales = []
+    for lay in layouts:
+        src = buffers[lay["buffer"]]
+        dst = codes[lay["buffer"]]
+        sl = slice(None)
+        if src.dim() == 3 and src.shape[-1] != lay["dim"] * lay["heads"]:  # MLA row slice
+            sl = slice(lay["offset"], lay["offset"] + lay["dim"])
+        sc = torch.empty(layers, dtype=torch.float32, device=src.device)
+        for l in range(layers):
+            v = src[l][..., sl] if sl != slice(None) else src[l]
+            amax = float(v.abs().max())
+            sc[l] = (amax if amax > 0 else 1.0) / 224.0
+            q = (v / sc[l]).to(torch.float8_e4m3fn).view(torch.uint8)
+            if sl != slice(None):
+                dst[l][..., sl] = q
+            else:
+                dst[l].copy_(q)
+        scales.append(sc)
+    return codes, scales
 
 
 def _normal(shape, seed: int, std: float, device, dtype):
@@ -291,7 +348,9 @@ def make_inputs(w: Workload, rank: int, device="cpu", pass_id: int = 0) -> Input
     pool = 0
     if w.page_size > 0:
         pool = max(w.pool_pages, -(-T // w.page_size))
-    dt = _torch_dtype(w)
+    q8 = w.dtype == "fp8"
+    dt = torch.float32 if q8 else _torch_dtype(w)
+    ft = _factor_dtype(w)
     wid = w.wid + 1000 * pass_id
     shapes = buffer_shapes(w, T, pool)
     buffers = []
@@ -306,18 +365,21 @@ def make_inputs(w: Workload, rank: int, device="cpu", pass_id: int = 0) -> Input
         for buf in buffers:
             flat = buf.view(w.layers, -1, w.heads * w.head_dim)
             flat[:, :, idx] = flat[:, :, idx] * w.outlier_scale
+    scales = []
+    if q8:
+        buffers, scales = _quantize_fp8(buffers, layouts, w.layers)
     U, V = [], []
     if rank > 0:
         s = factor_std(rank)
         for c, F in enumerate(feature_width(w)):
-            u = torch.empty((w.layers, T, rank), dtype=dt, device=device)
-            v = torch.empty((w.layers, st.num_chunks, F, rank), dtype=dt, device=device)
+            u = torch.empty((w.layers, T, rank), dtype=ft, device=device)
+            v = torch.empty((w.layers, st.num_chunks, F, rank), dtype=ft, device=device)
             for l in range(w.layers):
-                u[l] = _normal((T, rank), seed_of(wid, KIND_U, l, c), s, device, dt)
-                v[l] = _normal((st.num_chunks, F, rank), seed_of(wid, KIND_V, l, c), s, device, dt)
+                u[l] = _normal((T, rank), seed_of(wid, KIND_U, l, c), s, device, ft)
+                v[l] = _normal((st.num_chunks, F, rank), seed_of(wid, KIND_V, l, c), s, device, ft)
             U.append(u)
             V.append(v)
-    inp = Inputs(w, rank, st, pool, buffers, layouts, U, V)
+    inp = Inputs(w, rank, st, pool, buffers, layouts, U, V, scales=scales)
     inp.offsets_t = torch.as_tensor(st.offsets, device=device)
     inp.delta_t = torch.as_tensor(st.delta, device=device)
     if st.block_table is not None:
@@ -358,6 +420,8 @@ def make_recall_inputs(w: Workload, rank: int, device="cpu", pass_id: int = 0) -
     for shp in dst_buffer_shapes(w, T):
         if dt == torch.bfloat16:
             b = torch.full(shp, DST_SENTINEL, dtype=torch.int16, device=device).view(torch.bfloat16)
+        elif dt == torch.uint8:
+            b = torch.full(shp, DST_SENTINEL_FP8, dtype=torch.uint8, device=device)
         else:
             b = torch.full(shp, 0x7FC00001, dtype=torch.int32, device=device).view(torch.float32)
         bufs.append(b)
@@ -417,7 +481,7 @@ def algorithmic_bytes(w: Workload, rank: int, total_tokens: int | None = None,
     if total_tokens is None or num_chunks is None:
         st = structure(w)
         total_tokens, num_chunks = st.total_tokens, st.num_chunks
-    es = w.elem_size
+    es, fs = w.elem_size, w.factor_size
     T, L, n = total_tokens, w.layers, num_chunks
     lay = channel_layouts(w, T, 0)
     total = 0
@@ -428,7 +492,7 @@ def algorithmic_bytes(w: Workload, rank: int, total_tokens: int | None = None,
         elif rank == 0:
             total += 2 * es * c["heads"] * c["rope_dim"] * T * L
         else:
-            total += L * (2 * es * F * T + es * rank * T + es * F * rank * n)
+            total += L * (2 * es * F * T + fs * rank * T + fs * F * rank * n)
     return total
 
 
@@ -440,7 +504,7 @@ def patch_flops(w: Workload, rank: int) -> int:
 def patch_to_kv_ratio(w: Workload, rank: int) -> float:
     """Bytes of the stored patch (U and V) over bytes of the segment's KV."""
     st = structure(w)
-    es, T, n = w.elem_size, st.total_tokens, st.num_chunks
+    es, fs, T, n = w.elem_size, w.factor_size, st.total_tokens, st.num_chunks
     kv = sum(F * T * es for F in feature_width(w))
-    pat = sum(es * rank * (T + F * n) for F in feature_width(w))
+    pat = sum(fs * rank * (T + F * n) for F in feature_width(w))
     return pat / kv

@@ -11,6 +11,10 @@ within bf16 rounding):
     make it.  fp32 evaluation of the same terms in any order is off by at most
     about (m + 3) 2^-24 S, so when |y| is far below S that bound, not the ulp of
     y, limits any fp32 kernel.
+Acceptance for fp8 E4M3 output: the same two tests on the E4M3 grid, in code units
+(y and S divided by the layer's scale): at most 1 code (ordinal distance) from the
+oracle's code, or |g - y| <= ulp_fp8(y) + (m + 4) 2^-23 S.  The kernel forms
+(s x' + patch) / s in fp32, a few fp32 roundings of S, far inside that band.
 Acceptance for fp32 output: |g - y| <= 1e-5 max(|y|, S).
 NaN matches NaN.
 """
@@ -46,6 +50,33 @@ def bf16_ulp(y: np.ndarray) -> np.ndarray:
     return np.exp2(e - 7)
 
 
+def fp8_ordinal(codes: np.ndarray) -> np.ndarray:
+    b = codes.astype(np.int64)
+    mag = b & 0x7F
+    return np.where(b & 0x80, -mag, mag)
+
+
+def fp8_value(codes: np.ndarray) -> np.ndarray:
+    from oracle import oracle as orc
+    return orc.fp8_to_f64(codes)
+
+
+def fp8_ulp(y: np.ndarray) -> np.ndarray:
+    """Spacing of E4M3 codes around y: 2^(e - 3) for normal |y| >= 2^-6, else 2^-9."""
+    a = np.abs(y)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return np.exp2(e - 3)
+
+
+def storage_value(bits: np.ndarray) -> np.ndarray:
+    """Storage array -> fp64 values (fp8: code values, before the scale)."""
+    if bits.dtype == np.uint16:
+        return bf16_value(bits)
+    if bits.dtype == np.uint8:
+        return fp8_value(bits)
+    return bits.astype(np.float64)
+
+
 @dataclass
 class Report:
     elements: int = 0
@@ -76,22 +107,25 @@ def compare(g: np.ndarray, o: np.ndarray, y: np.ndarray, s: np.ndarray, rank: in
     rep.elements += g.size
     touched = s >= 0
     rep.computed += int(touched.sum())
-    if g.dtype == np.uint16:
+    if g.dtype in (np.uint16, np.uint8):
+        q8 = g.dtype == np.uint8
+        ordinal, value, ulp = ((fp8_ordinal, fp8_value, fp8_ulp) if q8
+                               else (bf16_ordinal, bf16_value, bf16_ulp))
         eq = g == o
-        gv = bf16_value(g)
-        nan_g, nan_o = np.isnan(gv), np.isnan(bf16_value(o))
+        gv = value(g)
+        nan_g, nan_o = np.isnan(gv), np.isnan(value(o))
         eq |= nan_g & nan_o
         rep.untouched_changed += int((~eq & ~touched).sum())
         rep.bit_equal += int((eq & touched).sum())
         idx = np.nonzero(~eq & touched)[0]
         if idx.size:
-            d = np.abs(bf16_ordinal(g[idx]) - bf16_ordinal(o[idx]))
+            d = np.abs(ordinal(g[idx]) - ordinal(o[idx]))
             near = (d <= 1) & ~nan_g[idx] & ~nan_o[idx]
             rep.within_1ulp += int(near.sum())
             rep.max_ulp = max(rep.max_ulp, int(d.max()))
             rest = idx[~near]
             if rest.size:
-                tol = bf16_ulp(y[rest]) + (rank + 4) * 2.0 ** -23 * s[rest]
+                tol = ulp(y[rest]) + (rank + 4) * 2.0 ** -23 * s[rest]
                 band = np.abs(gv[rest] - y[rest]) <= tol
                 rep.band_only += int(band.sum())
                 rep.failures += int((~band).sum())
@@ -118,10 +152,7 @@ def oracle_on_host(inp, before: list, factors: tuple | None = None):
     from oracle import oracle as orc
     w = inp.workload
     out = [b.copy() for b in before]
-    if before[0].dtype == np.uint16:
-        y = [bf16_value(b) for b in before]
-    else:
-        y = [b.astype(np.float64) for b in before]
+    y = [storage_value(b) for b in before]
     s = [np.full(b.size, -1.0) for b in before]
     if factors is None:
         factors = ([host_bits(u) for u in inp.U], [host_bits(v) for v in inp.V])
@@ -131,6 +162,8 @@ def oracle_on_host(inp, before: list, factors: tuple | None = None):
         d["data"] = out[lay["buffer"]]
         if inp.rank > 0:
             d["U"], d["V"] = factors[0][c], factors[1][c]
+        if inp.scales:
+            d["scale"] = host_bits(inp.scales[c])
         chans.append(d)
     orc.relocate_patch(chans, num_layers=w.layers, theta=w.theta, offsets=inp.struct.offsets,
                        delta=inp.struct.delta, rank=inp.rank, page_size=w.page_size,
@@ -214,6 +247,7 @@ def sampled_check(inp, run, n=1024, seed=0) -> Report:
         for c in chans:
             us[c] = host_bits(inp.U[c][li, ti]).reshape(len(rows), -1)
             vs[c] = host_bits(inp.V[c]).reshape(w.layers, st.num_chunks, -1, inp.rank)
+    scales = {c: host_bits(inp.scales[c]) for c in chans} if inp.scales else {}
     run(inp)
     torch.cuda.synchronize()
     after = {c: gather(c) for c in chans}
@@ -224,7 +258,8 @@ def sampled_check(inp, run, n=1024, seed=0) -> Report:
             j = int(np.searchsorted(st.offsets, t, side="right") - 1)
             compare(after[c][k], *_row_expect(w, lay, st.delta[j], before[c][k],
                                               us[c][k] if inp.rank > 0 else None,
-                                              vs[c][l, j] if inp.rank > 0 else None),
+                                              vs[c][l, j] if inp.rank > 0 else None,
+                                              float(scales[c][l]) if scales else 1.0),
                     inp.rank, rep)
     return rep
 
@@ -245,17 +280,20 @@ def moved_dims(lay, d, pairing=0, sections=()) -> np.ndarray:
     return np.tile(head, H)
 
 
-def _row_expect(w, lay, d, x, u, V):
-    """(oracle storage, fp64 value, magnitude or -1 where bits must match) of one row."""
+def _row_expect(w, lay, d, x, u, V, scale=1.0):
+    """(oracle storage, fp64 value, magnitude or -1 where bits must match) of one row;
+    fp8 rows (values scale * code) give value and magnitude in code units."""
     from oracle import oracle as orc
     kw = dict(pairing=w.pairing, sections=w.sections)
-    o = orc.row(x, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, u, V, **kw)
-    xf = bf16_value(x)
+    o = orc.row(x, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, u, V, scale=scale,
+                **kw)
+    xf = storage_value(x) * scale
     uf = None if u is None else bf16_value(u)
     Vf = None if V is None else bf16_value(V)
-    y = orc.row_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, uf, Vf, **kw)
+    y = orc.row_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, uf, Vf,
+                    **kw) / scale
     s = orc.row_magnitude_f64(xf, lay["heads"], lay["dim"], lay["rope_dim"], w.theta, d, uf,
-                              Vf, **kw)
+                              Vf, **kw) / scale
     if u is None:  # rank 0: only moved dims are computed
         s = np.where(moved_dims(lay, d, w.pairing, w.sections), s, -1.0)
     return o, y, s
@@ -263,13 +301,15 @@ def _row_expect(w, lay, d, x, u, V):
 
 # ----------------------------------------------------------------- recall (out of place)
 
-def _dicts(layouts, bufs, factors=None, rank=0):
+def _dicts(layouts, bufs, factors=None, rank=0, scales=()):
     out = []
     for c, lay in enumerate(layouts):
         d = dict(lay)
         d["data"] = bufs[lay["buffer"]]
         if factors is not None and rank > 0:
             d["U"], d["V"] = factors[0][c], factors[1][c]
+        if scales:
+            d["scale"] = host_bits(scales[c])
         out.append(d)
     return out
 
@@ -289,12 +329,10 @@ def check_recall(rinp, run) -> tuple:
     s_after = [host_bits(b) for b in src.buffers]
     d_after = [host_bits(b) for b in rinp.dst_buffers]
     out = [b.copy() for b in d_before]
-    if out[0].dtype == np.uint16:
-        y = [bf16_value(b) for b in d_before]
-    else:
-        y = [b.astype(np.float64) for b in d_before]
+    y = [storage_value(b) for b in d_before]
     s = [np.full(b.size, -1.0) for b in d_before]
-    orc.recall_patch(_dicts(src.layouts, [b.copy() for b in s_before], factors, src.rank),
+    orc.recall_patch(_dicts(src.layouts, [b.copy() for b in s_before], factors, src.rank,
+                            src.scales),
                      _dicts(rinp.dst_layouts, out), num_layers=w.layers, theta=w.theta,
                      offsets=src.struct.offsets, delta=src.struct.delta, rank=src.rank,
                      src_page_size=w.page_size, src_block_table=src.struct.block_table,
@@ -346,6 +384,7 @@ def sampled_check_recall(rinp, run, n=1024, seed=0) -> Report:
         for c in chans:
             us[c] = host_bits(src.U[c][li, ti]).reshape(len(rows), -1)
             vs[c] = host_bits(src.V[c]).reshape(w.layers, st.num_chunks, -1, src.rank)
+    scales = {c: host_bits(src.scales[c]) for c in chans} if src.scales else {}
     run(rinp)
     torch.cuda.synchronize()
     rep = Report()
@@ -358,6 +397,7 @@ def sampled_check_recall(rinp, run, n=1024, seed=0) -> Report:
             j = int(np.searchsorted(st.offsets, t, side="right") - 1)
             compare(got[k], *_row_expect(w, lay, st.delta[j], before[c][k],
                                          us[c][k] if src.rank > 0 else None,
-                                         vs[c][l, j] if src.rank > 0 else None),
+                                         vs[c][l, j] if src.rank > 0 else None,
+                                         float(scales[c][l]) if scales else 1.0),
                     src.rank, rep)
     return rep

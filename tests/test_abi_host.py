@@ -35,7 +35,7 @@ def test_library_loads_and_exports_every_declared_function():
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     assert set(names) <= exported
     assert not [e for e in exported if "launch" in e], "internal symbols leak"
-    assert K.kamera_abi_version() == 2
+    assert K.kamera_abi_version() == 3
 
 
 def test_struct_layout_matches_header():
@@ -84,14 +84,15 @@ class FakeTensor:
 
 def gqa(T=4096, L=28, H=4, D=128, r=128, m=32, dtype=K.KAMERA_BF16, kv_addr=FAKE,
         paged=False, pages=0, flags=0, n=1):
-    es = 2 if dtype == K.KAMERA_BF16 else 4
+    es = {K.KAMERA_BF16: 2, K.KAMERA_FP8_E4M3: 1}.get(dtype, 4)
     chans = []
     for c in range(2):
         base = kv_addr + c * (1 << 36)
+        scale = FakeTensor(FAKE + (7 << 40) + c * 4096) if dtype == K.KAMERA_FP8_E4M3 else None
         chans.append(K.channel(FakeTensor(base, es), heads=H, dim=D, rope_dim=r if c == 0 else 0,
                                layer_stride=(pages * 16 if paged else T) * H * D,
                                slot_stride=H * D, head_stride=D,
-                               page_stride=16 * H * D if paged else 0))
+                               page_stride=16 * H * D if paged else 0, scale=scale))
     kv = K.kv_desc(chans, dtype=dtype, num_layers=L, rope_theta=1e6,
                    page_size=16 if paged else 0, num_pages=pages,
                    block_table=FakeTensor(FAKE + (1 << 40)) if paged else None, flags=flags)
@@ -137,6 +138,8 @@ def test_null_descriptors():
 def test_bad_dtype_and_pairing():
     kv, ch, p = gqa()
     kv.dtype = 7
+    expect_status(K.KAMERA_E_UNSUPPORTED, kv, ch, p)
+    kv.dtype = 3
     expect_status(K.KAMERA_E_UNSUPPORTED, kv, ch, p)
     kv, ch, p = gqa()
     kv.pairing = 2
@@ -338,7 +341,7 @@ def test_chunk_boundary_tail_launch():
 
 def recall_dst(T=4096, L=28, H=4, D=128, r=128, pages=300, addr=FAKE + (5 << 40), dtype=None):
     """A paged destination cache matching gqa()'s source shape."""
-    es = 2 if dtype in (None, K.KAMERA_BF16) else 4
+    es = {None: 2, K.KAMERA_BF16: 2, K.KAMERA_FP8_E4M3: 1}.get(dtype, 4)
     chans = [K.channel(FakeTensor(addr + c * (1 << 36), es), heads=H, dim=D,
                        rope_dim=r if c == 0 else 0, layer_stride=pages * 16 * H * D,
                        slot_stride=H * D, head_stride=D, page_stride=16 * H * D)
@@ -374,6 +377,49 @@ def test_recall_kernel_choice():
     dst.ch[1].data = FAKE + (5 << 40) + (1 << 36) + 2  # element-aligned only
     names, info = recall_plan_names(src, dst, ch, p)
     assert names == ["rotate+patch mfma", "generic"] and info.launches == 2
+
+
+def test_fp8_kernel_choice_and_checks():
+    Q = K.KAMERA_FP8_E4M3
+    names, info = plan_names(*gqa(m=32, dtype=Q))
+    assert names == ["rotate+patch mfma"] * 2 and info.launches == 1
+    names, info = plan_names(*gqa(m=0, dtype=Q))
+    assert names == ["rotate", "none"]
+    names, _ = plan_names(*gqa(m=5, dtype=Q))  # the tuned fp8 kernel takes ranks % 8 == 0
+    assert names == ["generic", "generic"]
+    names, _ = plan_names(*gqa(m=128, dtype=Q, paged=True, pages=300))
+    assert names == ["rotate+patch mfma"] * 2
+    names, _ = plan_names(*gqa(m=8, dtype=Q, flags=K.KAMERA_FLAG_GENERIC))
+    assert names == ["generic", "generic"]
+    # 8-byte vector accesses: a row base on an 8-byte boundary is enough
+    kv, ch, p = gqa(m=8, dtype=Q)
+    kv.ch[0].data = FAKE + 8
+    assert plan_names(kv, ch, p)[0] == ["rotate+patch mfma"] * 2
+    kv.ch[0].data = FAKE + 4
+    assert plan_names(kv, ch, p)[0] == ["generic", "rotate+patch mfma"]
+    # scales are required and 4-byte aligned; factors are bf16 (2-byte aligned)
+    kv, ch, p = gqa(m=8, dtype=Q)
+    kv.ch[1].scale = None
+    expect_status(K.KAMERA_E_NULL, kv, ch, p)
+    kv, ch, p = gqa(m=8, dtype=Q)
+    kv.ch[0].scale = FAKE + (7 << 40) + 2
+    expect_status(K.KAMERA_E_ALIGN, kv, ch, p)
+    kv, ch, p = gqa(m=8, dtype=Q)
+    p.U[0] = FAKE + (1 << 39) + 1
+    expect_status(K.KAMERA_E_ALIGN, kv, ch, p)
+    # factor extents are counted in bf16 bytes: U right after the KV of channel 0
+    kv, ch, p = gqa(T=64, L=2, m=8, dtype=Q)
+    kv_bytes = 2 * 64 * 4 * 128  # layers * tokens * F, one byte each
+    p.U[0] = FAKE + kv_bytes
+    assert plan_names(kv, ch, p)[0] == ["rotate+patch mfma"] * 2
+    p.U[0] = FAKE + kv_bytes - 2
+    expect_status(K.KAMERA_E_ALIAS, kv, ch, p)
+    # recall: fp8 to fp8 only; the destination's scales are not read
+    src, ch, p = gqa(m=32, dtype=Q)
+    names, _ = recall_plan_names(src, recall_dst(dtype=Q), ch, p)
+    assert names == ["rotate+patch mfma"] * 2
+    st, _ = K.kamera_recall_plan(src, recall_dst(), ch, p)
+    assert st == K.KAMERA_E_SHAPE
 
 
 def test_recall_argument_errors():
