@@ -101,7 +101,8 @@ def main():
         c = synth.Inputs(base.workload, base.rank, base.struct, base.pool_pages,
                          [b.clone() for b in base.buffers], base.layouts,
                          [u.clone() for u in base.U], [v.clone() for v in base.V],
-                         base.offsets_t, base.delta_t, base.block_table_t)
+                         base.offsets_t, base.delta_t, base.block_table_t,
+                         scales=list(base.scales))
         return c
 
     insts = []
@@ -204,7 +205,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3"}.get(w.dtype, "f32"),
         "data": "synthetic",
         "config": {
             "workload": w.key,
@@ -366,7 +367,9 @@ def cpu_baseline(w, ranks, seconds: float):
     print("[bench] cpu baseline: oracle on host cores", file=sys.stderr, flush=True)
 
     def host(t):
-        return t.view(torch.int16).numpy().view(np.uint16)
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
 
     def prepare(ww):
         probs = []
@@ -381,6 +384,8 @@ def cpu_baseline(w, ranks, seconds: float):
                 if r > 0:
                     d["U"] = host(inp.U[c])
                     d["V"] = host(inp.V[c])
+                if inp.scales:
+                    d["scale"] = host(inp.scales[c])
                 chans.append(d)
             dchans = None
             if w.recall:

@@ -101,8 +101,10 @@ __int128 layer_extent(const kamera_channel& c, int64_t T, int32_t page_size, int
 // Rotation-only kernel: 8-element lanes over the rotated dims of each row.
 bool rotate_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, int64_t T) {
   const int r = c.rope_dim;
+  // row offsets inside a layer are kept in 32 bits
+  const bool extent_ok = layer_extent(c, T, kv.page_size, kv.num_pages) < ((__int128)1 << 31);
   return tuned_dtype(kv.dtype) && !(kv.flags & KAMERA_FLAG_GENERIC) &&
-         (r == 16 || r == 32 || r == 64 || r == 128) && T < kMaxTunedTokens &&
+         (r == 16 || r == 32 || r == 64 || r == 128) && T < kMaxTunedTokens && extent_ok &&
          aligned(c.data, vec_align(kv.dtype)) && strides_ok(c);
 }
 
@@ -129,8 +131,10 @@ void plan_mfma(const kamera_kv_desc& kv, const kamera_chunks& ch, int m, const b
   // Each of the 4 wavefronts of a workgroup streams `tpw` 16-token tiles.  The
   // workgroup stages 8 KB of feature factor per 32 ranks once per chunk, so larger
   // ranks take more tiles per wave (measured best: 2 tiles at rank <= 32, 4 at 64).
+  // fp8 rows carry half the bytes, so fp8 takes twice the tiles (measured best).
   const int mk = std::max(1, (m + 31) / 32);
-  const int dflt = std::min(8, 2 * (mk == 3 ? 4 : mk));
+  const int per_mk = 2 * (mk == 3 ? 4 : mk);
+  const int dflt = std::min(8, kv.dtype == KAMERA_FP8_E4M3 ? 2 * per_mk : per_mk);
   int tpw = env_int("KAMERA_TILES_PER_WAVE", dflt);
   if (tpw < 1 || tpw > kamera::kMaxBlockTokens / 64) tpw = dflt;
   plan->tiles_per_wave = tpw;
@@ -267,11 +271,11 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
         // A workgroup covers 4 waves x `unroll` row groups of 64 / (rope_dim / 8) rows.
         // Interleaved rows keep more values live per row group: two groups fit the
         // register budget of four waves per SIMD, four would spill.
-        // fp8 rows hold half the registers and always take four.
-        const int udflt = kv->pairing == KAMERA_INTERLEAVED ? 2 : 4;
+        // fp8 rows hold half the registers: four or eight groups (eight measured best).
+        const bool q8 = kv->dtype == KAMERA_FP8_E4M3;
+        const int udflt = q8 ? 8 : kv->pairing == KAMERA_INTERLEAVED ? 2 : 4;
         int unroll = env_int("KAMERA_ROTATE_UNROLL", udflt);
-        if (unroll != 2 && unroll != 4) unroll = udflt;
-        if (kv->dtype == KAMERA_FP8_E4M3) unroll = 4;
+        if (q8 ? (unroll != 4 && unroll != 8) : (unroll != 2 && unroll != 4)) unroll = udflt;
         const int rows = 4 * unroll * (64 / (k.rope_dim / 8));
         const int bt = (int)std::min<int64_t>(kamera::kMaxBlockTokens,
                                               std::max<int64_t>(1, rows / k.heads));

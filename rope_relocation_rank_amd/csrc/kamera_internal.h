@@ -82,11 +82,11 @@ hipError_t launch_form_batch(const FormArgs& a, int64_t p0, int count, hipStream
 hipError_t launch_form_gram(const FormArgs& a, float* G, hipStream_t s);
 
 // Rotation only, bf16 (16-byte accesses) or fp8 (8-byte accesses): rope_dim in
-// {16, 32, 64, 128}.  `unroll` row groups per wavefront (2 or 4; fp8 always takes 4).
+// {16, 32, 64, 128}.  `unroll` row groups per wavefront (bf16: 2 or 4; fp8: 4 or 8).
 hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unroll,
                               hipStream_t s);
 
-// Rotation + rank-m patch on MFMA, bf16 or fp8 (fp8: rank % 8 == 0, tile_unroll 1):
+// Rotation + rank-m patch on MFMA, bf16 or fp8 (fp8: rank % 8 == 0):
 // see kernels.hip for the shape conditions.
 // With ChanArgs::out set it runs out of place (rank % 8 == 0; rank 0 allowed).
 // Covers nch (1 or 2) channels in one launch, plus a second launch for the token groups

@@ -97,7 +97,8 @@ __device__ __forceinline__ void store_f(float* p, float y) { *p = y; }
 // lane's 8 elements are 8 bytes.  Code values become fp32 exactly; results go back
 // rounded to the nearest code, ties to the even one.  The conversion turns magnitudes
 // past the rounding range into NaN, so results are first clamped to +-448, the
-// largest finite code (saturation); NaN passes the clamp unchanged.
+// largest finite code (saturation), with the NaN-propagating maximum and minimum
+// (v_maximum3_f32 / v_minimum3_f32): NaN passes the clamp unchanged.
 
 // The two codes in the low (hi = false) or high 16 bits of w, as fp32.
 __device__ __forceinline__ float2 fp8_pair(uint32_t w, bool hi) {
@@ -107,7 +108,7 @@ __device__ __forceinline__ float2 fp8_pair(uint32_t w, bool hi) {
 }
 
 __device__ __forceinline__ float sat_fp8(float y) {
-  return fabsf(y) > 448.f ? copysignf(448.f, y) : y;
+  return __builtin_elementwise_minimum(__builtin_elementwise_maximum(y, -448.f), 448.f);
 }
 
 // `old` with its low (hi = false) or high 16 bits replaced by the codes of a and b.
@@ -127,10 +128,13 @@ __device__ __forceinline__ void unpack8(const u32x2_t& v, float (&x)[8]) {
   x[6] = p.x; x[7] = p.y;
 }
 
+// Both halves of each word are written, so the first conversion's tied operand is
+// seeded with the bits of its own first input (a register that dies there) rather
+// than a zero that would need a move.
 __device__ __forceinline__ u32x2_t pack8_fp8(const float (&y)[8]) {
   u32x2_t r;
-  r.x = fp8_put(y[2], y[3], fp8_put(y[0], y[1], 0u, false), true);
-  r.y = fp8_put(y[6], y[7], fp8_put(y[4], y[5], 0u, false), true);
+  r.x = fp8_put(y[2], y[3], fp8_put(y[0], y[1], __float_as_uint(y[0]), false), true);
+  r.y = fp8_put(y[6], y[7], fp8_put(y[4], y[5], __float_as_uint(y[4]), false), true);
   return r;
 }
 
@@ -209,7 +213,8 @@ __device__ __forceinline__ u32x2_t keep_elems(u32x2_t o, const u32x2_t& x, const
 // Storage of the tuned kernels' elements: a lane holds 8 consecutive features of a
 // row, bf16 in a u32x4 (feature pair p in word p) or fp8 in a u32x2 (feature pair p in
 // half p & 1 of word p >> 1).  word / pair read feature pair pp; put and put_keep
-// write it (put_keep takes the features flagged k0 / k1 bit for bit from x).
+// write it (put_keep takes the features flagged k0 / k1 bit for bit from the input
+// words x).
 template <bool Q>
 struct Codec;
 
@@ -236,9 +241,10 @@ struct Codec<true> {
   using XV = u32x2_t;
   static __device__ __forceinline__ uint32_t word(const XV& x, int pp) { return x[pp >> 1]; }
   static __device__ __forceinline__ float2 pair(uint32_t w, int pp) { return fp8_pair(w, pp & 1); }
+  // The low half's conversion is seeded with y0's bits (the word is written whole).
   static __device__ __forceinline__ void put(XV& o, int pp, float y0, float y1) {
     const int k = pp >> 1;
-    o[k] = fp8_put(y0, y1, (pp & 1) ? o[k] : 0u, pp & 1);
+    o[k] = fp8_put(y0, y1, (pp & 1) ? o[k] : __float_as_uint(y0), pp & 1);
   }
   static __device__ __forceinline__ void put_keep(XV& o, const XV& x, int pp, float y0, float y1,
                                                   bool k0, bool k1) {
@@ -380,8 +386,9 @@ __device__ __forceinline__ void phase_generic(double theta, int r, int i, int64_
 // untouched).  Returns p0.  The caller synchronises before reading `sbt`.
 __device__ __forceinline__ int stage_table(const int32_t* table, int64_t num_pages, int P,
                                            int64_t tb0, int64_t t1, int* sbt) {
-  const int p0 = (int)(tb0 / P);
-  const int n = (int)((t1 - 1) / P) + 1 - p0;
+  // tuned kernels keep token ids below 2^30: 32-bit division
+  const int p0 = (int)((uint32_t)tb0 / (uint32_t)P);
+  const int n = (int)((uint32_t)(t1 - 1) / (uint32_t)P) + 1 - p0;
   for (int k = threadIdx.x; k < n; k += kBlock) {
     const int64_t pg = table[p0 + k];
     sbt[k] = (pg >= 0 && pg < num_pages) ? (int)pg : -1;
@@ -448,8 +455,12 @@ __device__ __forceinline__ int32_t slot32(int page_size, int page_shift, const i
 // workgroup barrier, once, for the staged block table.  Dims >= rope_dim are never
 // touched; rows of chunks that do not move are not written; with M-RoPE sections, the
 // dims of pairs whose section delta is 0 keep their bits.
+//
+// Row offsets inside a layer are 32-bit (the host checks the extent) and advance from
+// one row group to the next by adds: the wave-uniform step of DR rows is dtl tokens and
+// dh heads, with a carry when the head index wraps.
 template <bool Q, int LPR, int UNR, bool PAGED, bool IL, bool SEC>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(UNR == 4 ? 4 : 1)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(UNR >= 4 ? 4 : 1)))
 void rotate_rows(ChanArgs ch, CommonArgs cm) {
   using E = typename Codec<Q>::E;
   using XV = typename Codec<Q>::XV;
@@ -460,9 +471,10 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
   __shared__ int sbt[kMaxBlockTokens + 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t layer = blockIdx.x / cm.token_groups;
-  const int64_t tg = blockIdx.x - layer * cm.token_groups;
-  const int64_t tb0 = tg * cm.block_tokens;
+  const uint32_t tgs = (uint32_t)cm.token_groups;  // grid = layers * tgs < 2^32
+  const uint32_t layer = blockIdx.x / tgs;
+  const uint32_t tg = blockIdx.x - layer * tgs;
+  const int64_t tb0 = (int64_t)tg * cm.block_tokens;
   const int64_t t1 = min(tb0 + (int64_t)cm.block_tokens, cm.total_tokens);
   const int q = lane % LPR;
   const int rr = lane / LPR;
@@ -471,7 +483,15 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
   const float sgn = q < HX ? -1.f : 1.f;
   const int H = ch.heads;
   const int nrows = (int)(t1 - tb0) * H;
-  E* base = (E*)ch.data + layer * ch.layer_stride + 8 * q;
+  E* base = (E*)ch.data + (int64_t)layer * ch.layer_stride + 8 * q;
+  // Offsets in uint32 arithmetic: every row the lane touches lies below 2^31, and rows
+  // past the block's end (never loaded) may wrap harmlessly.
+  const uint32_t ss = (uint32_t)ch.slot_stride, hs = (uint32_t)ch.head_stride;
+  const int32_t ps = (int32_t)ch.page_stride;
+  constexpr int DR = kWavesPerBlock * RPI;  // rows between a lane's row groups
+  const int dtl = DR / H, dh = DR - dtl * H;
+  const uint32_t dstep = (uint32_t)dtl * ss + (uint32_t)dh * hs;  // contiguous offset step
+  const uint32_t carry = ss - (uint32_t)H * hs;                    // and its head-wrap carry
   int p0 = 0;
   if (PAGED) {
     p0 = stage_block_table(cm, tb0, t1, sbt);
@@ -480,28 +500,38 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
   for (int rbase = 0; rbase < nrows; rbase += ROWS) {
     XV xv[UNR];
     E* ptr[UNR];
-    int64_t tok[UNR];
+    int tlk[UNR];  // token of each row group, relative to tb0
     bool ok[UNR];
+    const int R0 = rbase + wave * RPI + rr;
+    int tl = R0 / H;
+    int h = R0 - tl * H;
+    uint32_t off = PAGED ? 0u : ((uint32_t)tb0 + (uint32_t)tl) * ss + (uint32_t)h * hs;
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
-      const int R = rbase + (wave + kWavesPerBlock * k) * RPI + rr;
-      ok[k] = R < nrows;
-      ptr[k] = base;
-      tok[k] = tb0;
-      xv[k] = (XV)(0u);
-      if (ok[k]) {
-        const int tl = R / H;
-        const int h = R - tl * H;
-        tok[k] = tb0 + tl;
-        int64_t so;
-        if (PAGED) {
-          so = slot_staged(cm, sbt, p0, ch.page_stride, ch.slot_stride, tok[k]);
-          ok[k] = so >= 0;
-        } else {
-          so = tok[k] * ch.slot_stride;
+      if (k > 0) {
+        tl += dtl;
+        h += dh;
+        off += dstep;
+        if (h >= H) {
+          h -= H;
+          ++tl;
+          off += carry;
         }
-        ptr[k] = base + so + (int64_t)h * ch.head_stride;
       }
+      ok[k] = R0 + k * DR < nrows;
+      tlk[k] = tl;
+      uint32_t o = off;
+      if constexpr (PAGED) {
+        o = 0u;
+        if (ok[k]) {  // the staged table covers the block's own tokens only
+          const int32_t so = slot32<true>(cm.page_size, cm.page_shift, sbt, p0, ps, (int32_t)ss,
+                                          (int)tb0 + tl);
+          ok[k] = so >= 0;
+          o = (uint32_t)so + (uint32_t)h * hs;
+        }
+      }
+      ptr[k] = base + o;
+      xv[k] = (XV)(0u);
       if (ok[k]) xv[k] = load_nt(ptr[k]);
     }
     // Token span of this wave's rows in this pass.
@@ -514,6 +544,7 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
     while (true) {
       const int64_t s1 = min(tw1, c.end);
       if (s1 > t0 && c.delta != 0) {
+        const int lo = (int)(t0 - tb0), hi = (int)(s1 - tb0);  // rows' tokens to store
         float2 own = make_float2(1.f, 0.f);
         if (lane < HALF) own = phase_of(ch.omega[lane], SEC ? pair_delta(cm, c, lane) : c.delta);
         float cs[8], sn[8];
@@ -539,7 +570,7 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
           if constexpr (Q) o = pack8_fp8(y);
           else o = pack8(y);
           if constexpr (SEC) o = keep_elems(o, xv[k], sn);
-          if (ok[k] && tok[k] >= t0 && tok[k] < s1) store_nt(ptr[k], o);
+          if (ok[k] && tlk[k] >= lo && tlk[k] < hi) store_nt(ptr[k], o);
         }
       }
       t0 = max(t0, s1);
@@ -653,9 +684,11 @@ __device__ __forceinline__ void load_tiles(const PatchCtx<Q>& c, const CommonArg
 // Phases sit in LDS as (cos, sin) per rotary pair.  With M-RoPE sections a pair whose
 // section delta is 0 has sin exactly 0 and is not rotated.
 //
-// fp8 (Q): the rotation runs on code values; with a patch the accumulator starts at
-// s * (rotated codes), the MFMA adds the patch in value units, and the sum times 1/s
-// is encoded.
+// fp8 (Q): the rotation runs on code values and the result is rotated + patch * (1/s)
+// with the patch in value units.  At MK = 1 the MFMA starts from a zero accumulator and
+// one FMA finishes each element; at larger MK, where the rotated values cannot stay
+// live beside the accumulators without spilling, the accumulator starts at s * rotated
+// and the sum is multiplied by 1/s.
 template <bool Q, int MK, int HX, int TU, int OUT>
 __device__ __forceinline__ void finish_tiles(const PatchCtx<Q>& c, const u32x4_t* sV,
                                              const float4* sph2, const TileSet<Q, MK, TU>& T) {
@@ -700,11 +733,12 @@ __device__ __forceinline__ void finish_tiles(const PatchCtx<Q>& c, const u32x4_t
         for (int i = 0; i < 4; ++i)
           P::put_keep(out[i], T.x[u][i], pp, r0[i], r1[i], !turn0, !turn1);
       } else {
+        constexpr bool kFmaScale = Q && MK == 1;
         f32x4_t acc0, acc1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc0[i] = Q ? r0[i] * c.qs : r0[i];
-          acc1[i] = Q ? r1[i] * c.qs : r1[i];
+          acc0[i] = kFmaScale ? 0.f : Q ? r0[i] * c.qs : r0[i];
+          acc1[i] = kFmaScale ? 0.f : Q ? r1[i] * c.qs : r1[i];
         }
 #pragma unroll
         for (int ks = 0; ks < MK; ++ks) {
@@ -717,7 +751,9 @@ __device__ __forceinline__ void finish_tiles(const PatchCtx<Q>& c, const u32x4_t
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          P::put(out[i], pp, Q ? acc0[i] * c.qinv : acc0[i], Q ? acc1[i] * c.qinv : acc1[i]);
+          P::put(out[i], pp,
+                 kFmaScale ? fmaf(acc0[i], c.qinv, r0[i]) : Q ? acc0[i] * c.qinv : acc0[i],
+                 kFmaScale ? fmaf(acc1[i], c.qinv, r1[i]) : Q ? acc1[i] * c.qinv : acc1[i]);
       }
       // Keep the scheduler from hoisting every feature pair's LDS reads at once (it
       // would hold all B fragments live and lower the occupancy).
@@ -790,15 +826,17 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
       bid = bid - i + (i % 8) * xcd_group + i / 8;
     }
   }
-  const int64_t layer = bid / blocks_per_layer;
-  int64_t b = bid - layer * blocks_per_layer;
+  // grid < 2^32 workgroups: 32-bit division
+  const uint32_t bpl = (uint32_t)blocks_per_layer;
+  const int64_t layer = (uint32_t)bid / bpl;
+  int64_t b = (uint32_t)bid - (uint32_t)layer * bpl;
   const bool second = b >= ch0.blocks;
   if (second) b -= ch0.blocks;
   // Field-wise choice of the channel (a reference to either argument would copy both
   // to scratch memory).
 #define KAMERA_CH(f) (second ? ch1.f : ch0.f)
   const int fblocks = KAMERA_CH(fblocks);
-  const int64_t tg = b / fblocks;
+  const int64_t tg = (uint32_t)b / (uint32_t)fblocks;
   const int fbk = (int)(b - tg * fblocks);
 
   using E = typename Codec<Q>::E;
@@ -1072,7 +1110,8 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
   const bool q = cm.dtype == 2;
 #define KAMERA_LAUNCH_ROT4(LPR, PG, IL, SC)                                                          \
   do {                                                                                               \
-    if (q) hipLaunchKernelGGL((rotate_rows<true, LPR, 4, PG, IL, SC>), grid, dim3(kBlock), 0, s, ch, cm); \
+    if (q && unroll == 8) hipLaunchKernelGGL((rotate_rows<true, LPR, 8, PG, IL, SC>), grid, dim3(kBlock), 0, s, ch, cm); \
+    else if (q) hipLaunchKernelGGL((rotate_rows<true, LPR, 4, PG, IL, SC>), grid, dim3(kBlock), 0, s, ch, cm); \
     else if (unroll == 2) hipLaunchKernelGGL((rotate_rows<false, LPR, 2, PG, IL, SC>), grid, dim3(kBlock), 0, s, ch, cm); \
     else hipLaunchKernelGGL((rotate_rows<false, LPR, 4, PG, IL, SC>), grid, dim3(kBlock), 0, s, ch, cm); \
   } while (0)
@@ -1129,7 +1168,8 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
                      c0, c1, cm, bpl, XG)
 #define KAMERA_LAUNCH_IN(MK, PG, TL, XG)                                                       \
   do {                                                                                         \
-    if (q) KAMERA_LAUNCH_K(true, MK, true, PG, 1, TL, 0, XG);                                  \
+    if (q && tile_unroll == 2 && !TL) KAMERA_LAUNCH_K(true, MK, true, PG, 2, false, 0, XG);    \
+    else if (q) KAMERA_LAUNCH_K(true, MK, true, PG, 1, TL, 0, XG);                             \
     else if (m8 && tile_unroll == 2 && !TL) KAMERA_LAUNCH_K(false, MK, true, PG, 2, false, 0, XG); \
     else if (m8) KAMERA_LAUNCH_K(false, MK, true, PG, 1, TL, 0, XG);                           \
     else KAMERA_LAUNCH_K(false, MK, false, PG, 1, TL, 0, XG);                                  \

@@ -286,10 +286,10 @@ class Inputs:
     layouts: list                  # per channel layout dicts
     U: list = field(default_factory=list)   # per channel [L][T][m] (torch) or []
     V: list = field(default_factory=list)   # per channel [L][n][F][m]
-    scales: list = field(default_factory=list)  # fp8: per channel float32 [L]; else []
     offsets_t: object = None
     delta_t: object = None
     block_table_t: object = None
+    scales: list = field(default_factory=list)  # fp8: per channel float32 [L]; else []
 
 
 def _torch_dtype(w: Workload):

@@ -161,6 +161,27 @@ def test_encoder_bit_exact_on_exact_inputs():
         assert not bad.any(), f"{int(bad.sum())} codes differ, first at {np.argwhere(bad)[:4]}"
 
 
+@pytest.mark.parametrize("rank", [0, 8, 64])
+def test_nan_codes_and_saturation(rank):
+    # NaN codes (0x7F, 0xFF) must come out NaN, rotated together with their partner;
+    # codes at +-448 and a patch far past the range must saturate to +-448, not NaN.
+    w = _gqa(tokens=200, rank=max(rank, 8))
+    inp = synth.make_inputs(w, rank, device=DEV)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    for b in inp.buffers:
+        flat = b.view(-1)
+        n = flat.numel()
+        idx = torch.randperm(n, generator=g)[: n // 50].to(DEV)
+        vals = torch.tensor([0x7F, 0xFF, 0x7E, 0xFE], dtype=torch.uint8, device=DEV)
+        flat[idx] = vals[torch.arange(idx.numel(), device=DEV) % 4]
+    if rank:
+        for c in range(2):
+            inp.U[c][:, 50:60] *= 4000.0  # these tokens' patch overflows the E4M3 range
+    rep = parity.check_problem(inp, lambda i: ops.run(i))
+    print(f"[case] fp8 nan/saturation rank={rank} {rep}", flush=True)
+    assert rep.ok(), str(rep)
+
+
 # ----------------------------------------------------------------- recall (out of place)
 
 def _rw(**kw):
