@@ -563,6 +563,101 @@ int orc_recall_patch_ex(const orc_problem* src, const orc_problem* dst, double* 
     return bad ? -1 : 0;
 }
 
+/* Relocate-on-read decode attention, the use of the rebuilt cache that [K §3]
+ * describes as a hook in front of the attention kernel: the relocated and patched
+ * keys and values are consumed by attention instead of being written back.  For
+ * layer l and query head h (its KV head is g = h / (Hq / Hkv), grouped-query
+ * attention), over every token t of every chunk j whose slot exists:
+ *     K'_t = R(delta_j) K_t + U_K[l][t] V_K[l][j]^T    (head g's features)
+ *     V'_t = V_t           + U_V[l][t] V_V[l][j]^T
+ *     s_t  = scale * q[l][h] . K'_t
+ *     out[l][h] = sum_t softmax(s)_t V'_t,   lse[l][h] = log sum_t exp(s_t)
+ * K' and V' are the operator's values before rounding (the row function's fp64
+ * result): the attention reads them, nothing stores them.  Channel 0 is K and
+ * channel 1 is V, with equal heads and dim.  q and out are [L][Hq][dim] fp64, lse is
+ * [L][Hq] (may be NULL).  A head with no token gets out = 0 and lse = -inf.
+ * Returns 0, or -1 on bad arguments. */
+int orc_attend(const orc_problem* p, int num_q_heads, double scale, const double* q,
+               double* out, double* lse) {
+    if (!p || p->num_channels != 2 || p->rank < 0 || num_q_heads < 1 ||
+        (p->dtype != ORC_BF16 && p->dtype != ORC_F32 && p->dtype != ORC_FP8))
+        return -1;
+    const orc_channel* kc = &p->ch[0];
+    const orc_channel* vc = &p->ch[1];
+    if (kc->heads != vc->heads || kc->dim != vc->dim || num_q_heads % kc->heads) return -1;
+    int64_t T = p->total_tokens, L = p->num_layers;
+    int H = kc->heads, D = kc->dim, G = num_q_heads / H, m = p->rank;
+    int64_t F = (int64_t)H * D;
+    int fs = elem_size(factor_dtype(p->dtype));
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t l = 0; l < L; ++l) {
+        double* kp = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * F);
+        double* vp = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * F);
+        char* ok = (char*)calloc((size_t)(T > 0 ? T : 1), 1);
+        double* x = (double*)malloc(sizeof(double) * F);
+        double* ud = (double*)malloc(sizeof(double) * (m > 0 ? m : 1));
+        double* vd = (double*)malloc(sizeof(double) * (m > 0 ? F * m : 1));
+        double* sc = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+        /* the relocated rows, in fp64, of both channels */
+        for (int64_t t = 0; t < T; ++t) {
+            int64_t j = chunk_of(p, t);
+            if (j < 0) { bad = 1; continue; }
+            if (p->page_size > 0) {
+                int64_t pg = p->block_table[t / p->page_size];
+                if (pg < 0) continue; /* no slot: the token is not attended */
+            }
+            ok[t] = 1;
+            const int64_t* dj = p->delta + j * rope_sections(&p->rope);
+            for (int c = 0; c < 2; ++c) {
+                const orc_channel* ch = &p->ch[c];
+                double sl = p->dtype == ORC_FP8 ? (double)ch->scale[l] : 1.0;
+                for (int64_t h = 0; h < H; ++h) {
+                    int64_t o = orc_row_offset(ch, p->page_size, p->block_table, l, t, h);
+                    for (int d = 0; d < D; ++d) x[h * D + d] = sl * load_elem(p->dtype, ch->data, o + d);
+                }
+                if (m > 0) {
+                    const char* u = (const char*)ch->U + ((l * T + t) * m) * fs;
+                    const char* V = (const char*)ch->V + ((l * p->num_chunks + j) * F * m) * fs;
+                    for (int k = 0; k < m; ++k) ud[k] = load_elem(factor_dtype(p->dtype), u, k);
+                    for (int64_t i = 0; i < F * m; ++i)
+                        vd[i] = load_elem(factor_dtype(p->dtype), V, i);
+                }
+                orc_row_spec_f64(x, (c == 0 ? kp : vp) + t * F, H, D, ch->rope_dim, p->theta, dj,
+                                 &p->rope, m, ud, vd);
+            }
+        }
+        /* attention of every query head */
+        for (int hq = 0; hq < num_q_heads; ++hq) {
+            int g = hq / G;
+            const double* qh = q + (l * num_q_heads + hq) * D;
+            double mx = -INFINITY;
+            for (int64_t t = 0; t < T; ++t) {
+                if (!ok[t]) continue;
+                double s = 0.0;
+                for (int d = 0; d < D; ++d) s += qh[d] * kp[t * F + g * D + d];
+                sc[t] = scale * s;
+                if (sc[t] > mx) mx = sc[t];
+            }
+            double* oh = out + (l * num_q_heads + hq) * D;
+            for (int d = 0; d < D; ++d) oh[d] = 0.0;
+            double sum = 0.0;
+            if (mx > -INFINITY) {
+                for (int64_t t = 0; t < T; ++t) {
+                    if (!ok[t]) continue;
+                    double w = exp(sc[t] - mx);
+                    sum += w;
+                    for (int d = 0; d < D; ++d) oh[d] += w * vp[t * F + g * D + d];
+                }
+                for (int d = 0; d < D; ++d) oh[d] /= sum;
+            }
+            if (lse) lse[l * num_q_heads + hq] = mx > -INFINITY ? mx + log(sum) : -INFINITY;
+        }
+        free(kp); free(vp); free(ok); free(x); free(ud); free(vd); free(sc);
+    }
+    return bad ? -1 : 0;
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

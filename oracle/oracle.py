@@ -139,6 +139,9 @@ def lib():
         L.orc_row_offset.restype = C.c_int64
         L.orc_row_offset.argtypes = [C.POINTER(_Channel), C.c_int32, C.c_void_p,
                                      C.c_int64, C.c_int64, C.c_int64]
+        L.orc_attend.restype = C.c_int
+        L.orc_attend.argtypes = [C.POINTER(_Problem), C.c_int, C.c_double, C.c_void_p,
+                                 C.c_void_p, C.c_void_p]
         L.orc_num_threads.restype = C.c_int
         L.orc_struct_sizes.restype = C.c_int
         L.orc_struct_sizes.argtypes = [C.c_int]
@@ -412,6 +415,28 @@ def recall_patch(src_channels, dst_channels, *, num_layers: int, theta: float, o
     del keep, keep2
     if rc != 0:
         raise ValueError("oracle rejected the problem")
+
+
+def attend(channels, *, num_layers: int, theta: float, offsets, delta, q, scale: float,
+           rank: int = 0, page_size: int = 0, block_table=None, pairing: int = NEOX,
+           sections=()):
+    """Relocate-on-read decode attention over host arrays: ``channels`` = [K, V] dicts
+    as in ``relocate_patch`` (never written); ``q`` [L][Hq][D] float64.  Returns
+    (out [L][Hq][D], lse [L][Hq]) in float64.  Tokens whose block-table entry is
+    negative are not attended."""
+    p, keep = _problem(channels, num_layers=num_layers, theta=theta, offsets=offsets,
+                       delta=delta, rank=rank, page_size=page_size, block_table=block_table,
+                       pairing=pairing, sections=sections)
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    L, Hq, D = q.shape
+    assert L == num_layers and D == channels[0]["dim"]
+    out = np.empty_like(q)
+    lse = np.empty((L, Hq))
+    rc = lib().orc_attend(C.byref(p), Hq, float(scale), _ptr(q), _ptr(out), _ptr(lse))
+    del keep
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    return out, lse
 
 
 def num_threads() -> int:
