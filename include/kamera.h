@@ -208,6 +208,53 @@ KAMERA_API kamera_status kamera_recall_patch(const kamera_kv_desc* src, const ka
                                   const kamera_chunks* chunks, const kamera_patch* patch,
                                   hipStream_t stream);
 
+/* ------------------------------------------------------------------ relocate-on-read attention
+ *
+ * Kamera page §3, production deployment: the rebuild runs as a hook in front of the
+ * attention kernel.  This entry point is that use with nothing written back: decode
+ * attention (one query per layer and query head) reads the cached keys and values and
+ * consumes the relocated, patched ones directly,
+ *     K'_t = R(delta_j) K_t + sum_k U[0][l][t][k] V[0][l][j][f][k]
+ *     V'_t = V_t            + sum_k U[1][l][t][k] V[1][l][j][f][k]
+ *     out[l][h] = sum_t softmax_t(scale * q[l][h] . K'_t) V'_t
+ *     lse[l][h] = log sum_t exp(scale * q[l][h] . K'_t)
+ * over every token t of every chunk j, query head h reading KV head
+ * h / (num_q_heads / heads) (grouped-query attention).  K' and V' are the operator's
+ * values before rounding; the cache is not modified.  The library evaluates the same
+ * sums re-associated ((R(-delta) q) . K_t + (V_K^T q) . U[0][t], and V_V applied to
+ * sum_t p_t U[1][t]), in fp32.
+ *
+ * kv: MHA/GQA, bf16; channel 0 = K (its rope_dim, pairing and sections rotate),
+ *     channel 1 = V (rope_dim 0); equal heads; dim 128; contiguous or paged (tokens
+ *     whose block-table entry lies outside [0, num_pages) are not attended).  Row bases
+ *     8-byte aligned, strides multiples of 8 elements, per-layer extents below 2^31
+ *     elements, total_tokens below 2^30.  Other shapes: KAMERA_E_UNSUPPORTED.
+ * patch: NULL or rank 0 for plain attention; else rank <= 128, bf16 factors as for
+ *     kamera_relocate_patch.
+ * A head with no attended token gets out = 0 and lse = -inf. */
+typedef struct {
+  int32_t num_q_heads;   /* Hq: a multiple of kv.heads, at most 8 times it */
+  int32_t reserved0;     /* must be 0 */
+  float scale;           /* softmax scale (for example dim^-1/2); finite */
+  int32_t reserved1;     /* must be 0 */
+  const float* q;        /* device [num_layers][num_q_heads][dim] fp32, read only: the query of
+                            each layer, already rotated to its own position */
+  float* out;            /* device [num_layers][num_q_heads][dim] fp32, written */
+  float* lse;            /* device [num_layers][num_q_heads] fp32 (natural log), or NULL */
+} kamera_attend_desc;
+
+/* Bytes of workspace kamera_attend needs for this problem (0 when it is empty). */
+KAMERA_API kamera_status kamera_attend_workspace(const kamera_kv_desc* kv,
+                                      const kamera_chunks* chunks,
+                                      const kamera_attend_desc* attend, int64_t* bytes);
+
+/* Stream-ordered.  workspace: caller-owned device memory of at least the bytes
+ * kamera_attend_workspace reports, 16-byte aligned, overwritten.  out, lse and the
+ * workspace must not overlap each other, q or the cache (KAMERA_E_ALIAS). */
+KAMERA_API kamera_status kamera_attend(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                            const kamera_patch* patch, const kamera_attend_desc* attend,
+                            void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ patch formation
  *
  * The step before the reuse operator: Kamera page §2, "Aplicacao de Patch" forms the

@@ -575,10 +575,12 @@ int orc_recall_patch_ex(const orc_problem* src, const orc_problem* dst, double* 
  * K' and V' are the operator's values before rounding (the row function's fp64
  * result): the attention reads them, nothing stores them.  Channel 0 is K and
  * channel 1 is V, with equal heads and dim.  q and out are [L][Hq][dim] fp64, lse is
- * [L][Hq] (may be NULL).  A head with no token gets out = 0 and lse = -inf.
- * Returns 0, or -1 on bad arguments. */
+ * [L][Hq] (may be NULL).  A head with no token gets out = 0 and lse = -inf.  mag
+ * (may be NULL, [L][Hq][dim]) receives sum_t softmax(s)_t |V'_t|, the scale of the
+ * output's rounding error used by the parity tolerance.  Returns 0, or -1 on bad
+ * arguments. */
 int orc_attend(const orc_problem* p, int num_q_heads, double scale, const double* q,
-               double* out, double* lse) {
+               double* out, double* lse, double* mag) {
     if (!p || p->num_channels != 2 || p->rank < 0 || num_q_heads < 1 ||
         (p->dtype != ORC_BF16 && p->dtype != ORC_F32 && p->dtype != ORC_FP8))
         return -1;
@@ -640,7 +642,9 @@ int orc_attend(const orc_problem* p, int num_q_heads, double scale, const double
                 if (sc[t] > mx) mx = sc[t];
             }
             double* oh = out + (l * num_q_heads + hq) * D;
+            double* mh = mag ? mag + (l * num_q_heads + hq) * D : NULL;
             for (int d = 0; d < D; ++d) oh[d] = 0.0;
+            if (mh) for (int d = 0; d < D; ++d) mh[d] = 0.0;
             double sum = 0.0;
             if (mx > -INFINITY) {
                 for (int64_t t = 0; t < T; ++t) {
@@ -648,8 +652,10 @@ int orc_attend(const orc_problem* p, int num_q_heads, double scale, const double
                     double w = exp(sc[t] - mx);
                     sum += w;
                     for (int d = 0; d < D; ++d) oh[d] += w * vp[t * F + g * D + d];
+                    if (mh) for (int d = 0; d < D; ++d) mh[d] += w * fabs(vp[t * F + g * D + d]);
                 }
                 for (int d = 0; d < D; ++d) oh[d] /= sum;
+                if (mh) for (int d = 0; d < D; ++d) mh[d] /= sum;
             }
             if (lse) lse[l * num_q_heads + hq] = mx > -INFINITY ? mx + log(sum) : -INFINITY;
         }

@@ -86,8 +86,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
-            build()
+        build()  # rebuilds when the source is newer than the library
         L = C.CDLL(LIB)
         L.orc_bf16_from_double.restype = C.c_uint16
         L.orc_bf16_from_double.argtypes = [C.c_double]
@@ -141,7 +140,7 @@ def lib():
                                      C.c_int64, C.c_int64, C.c_int64]
         L.orc_attend.restype = C.c_int
         L.orc_attend.argtypes = [C.POINTER(_Problem), C.c_int, C.c_double, C.c_void_p,
-                                 C.c_void_p, C.c_void_p]
+                                 C.c_void_p, C.c_void_p, C.c_void_p]
         L.orc_num_threads.restype = C.c_int
         L.orc_struct_sizes.restype = C.c_int
         L.orc_struct_sizes.argtypes = [C.c_int]
@@ -419,11 +418,11 @@ def recall_patch(src_channels, dst_channels, *, num_layers: int, theta: float, o
 
 def attend(channels, *, num_layers: int, theta: float, offsets, delta, q, scale: float,
            rank: int = 0, page_size: int = 0, block_table=None, pairing: int = NEOX,
-           sections=()):
+           sections=(), with_mag: bool = False):
     """Relocate-on-read decode attention over host arrays: ``channels`` = [K, V] dicts
     as in ``relocate_patch`` (never written); ``q`` [L][Hq][D] float64.  Returns
-    (out [L][Hq][D], lse [L][Hq]) in float64.  Tokens whose block-table entry is
-    negative are not attended."""
+    (out [L][Hq][D], lse [L][Hq]) in float64, plus mag (sum_t p_t |V'_t|) when
+    ``with_mag``.  Tokens whose block-table entry is negative are not attended."""
     p, keep = _problem(channels, num_layers=num_layers, theta=theta, offsets=offsets,
                        delta=delta, rank=rank, page_size=page_size, block_table=block_table,
                        pairing=pairing, sections=sections)
@@ -432,11 +431,13 @@ def attend(channels, *, num_layers: int, theta: float, offsets, delta, q, scale:
     assert L == num_layers and D == channels[0]["dim"]
     out = np.empty_like(q)
     lse = np.empty((L, Hq))
-    rc = lib().orc_attend(C.byref(p), Hq, float(scale), _ptr(q), _ptr(out), _ptr(lse))
+    mag = np.empty_like(q) if with_mag else None
+    rc = lib().orc_attend(C.byref(p), Hq, float(scale), _ptr(q), _ptr(out), _ptr(lse),
+                          _ptr(mag))
     del keep
     if rc != 0:
         raise ValueError("oracle rejected the problem")
-    return out, lse
+    return (out, lse, mag) if with_mag else (out, lse)
 
 
 def num_threads() -> int:

@@ -10,8 +10,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkamera.so")
 SOURCES = [os.path.join(CSRC, "abi.cpp"), os.path.join(CSRC, "kernels.hip"),
-           os.path.join(CSRC, "form.hip")]
-HEADERS = [os.path.join(INCLUDE, "kamera.h"), os.path.join(CSRC, "kamera_internal.h")]
+           os.path.join(CSRC, "form.hip"), os.path.join(CSRC, "attend.hip")]
+HEADERS = [os.path.join(INCLUDE, "kamera.h"), os.path.join(CSRC, "kamera_internal.h"),
+           os.path.join(CSRC, "rope_device.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

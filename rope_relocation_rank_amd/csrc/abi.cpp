@@ -638,9 +638,181 @@ kamera_status run_form(const kamera_form_desc* d, const kamera_chunks* ch, void*
   return KAMERA_OK;
 }
 
+// ------------------------------------------------------------------ relocate-on-read attention
+
+struct AttendPlan {
+  int64_t splits = 0, split_tokens = 0, slots = 0, bytes = 0;
+};
+
+// Checks an attention call; no HIP call is made here.
+kamera_status validate_attend(const kamera_kv_desc* kv, const kamera_chunks* ch,
+                              const kamera_patch* p, const kamera_attend_desc* at,
+                              AttendPlan* plan) {
+  Plan ignored;
+  const kamera_status st = validate(kv, ch, p, &ignored);
+  if (st != KAMERA_OK) return st;
+  if (!at) return fail(KAMERA_E_NULL, "attend descriptor is NULL");
+  if (at->reserved0 != 0 || at->reserved1 != 0)
+    return fail(KAMERA_E_SHAPE, "attend reserved fields must be 0");
+  if (kv->num_channels != 2)
+    return fail(KAMERA_E_UNSUPPORTED, "attention takes an MHA/GQA cache: channels K and V");
+  const kamera_channel& K = kv->ch[0];
+  const kamera_channel& V = kv->ch[1];
+  if (kv->dtype != KAMERA_BF16) return fail(KAMERA_E_UNSUPPORTED, "attention takes bf16 KV");
+  if (K.heads != V.heads || K.dim != V.dim)
+    return fail(KAMERA_E_SHAPE, "K and V differ in heads or dim");
+  if (K.dim != kamera::kAttendDim)
+    return fail(KAMERA_E_UNSUPPORTED, "attention takes dim %d, not %d", kamera::kAttendDim, K.dim);
+  if (V.rope_dim != 0) return fail(KAMERA_E_SHAPE, "the V channel does not rotate (rope_dim 0)");
+  const int Hq = at->num_q_heads;
+  if (Hq < 1 || Hq % K.heads != 0)
+    return fail(KAMERA_E_SHAPE, "num_q_heads %d is not a multiple of the %d KV heads", Hq, K.heads);
+  if (Hq / K.heads > kamera::kAttendMaxGroup)
+    return fail(KAMERA_E_UNSUPPORTED, "more than %d query heads per KV head", kamera::kAttendMaxGroup);
+  if (!std::isfinite(at->scale)) return fail(KAMERA_E_SHAPE, "scale must be finite");
+  const int m = p ? p->rank : 0;
+  if (m > 128) return fail(KAMERA_E_UNSUPPORTED, "attention takes rank <= 128");
+  const int64_t T = ch->total_tokens, L = kv->num_layers, n = ch->num_chunks;
+  if (T >= kMaxTunedTokens) return fail(KAMERA_E_UNSUPPORTED, "total_tokens must be below 2^30");
+  for (int c = 0; c < 2; ++c) {
+    const kamera_channel& k = kv->ch[c];
+    if (!aligned(k.data, 8) || !strides_ok(k))
+      return fail(KAMERA_E_ALIGN, "channel %d: attention needs 8-byte rows (strides %% 8)", c);
+    if (layer_extent(k, T, kv->page_size, kv->num_pages) >= ((__int128)1 << 31))
+      return fail(KAMERA_E_UNSUPPORTED, "channel %d: per-layer extent of 2^31 elements or more", c);
+  }
+  if (L > 0 && (!at->q || !at->out)) return fail(KAMERA_E_NULL, "q and out are required");
+  if (!aligned(at->q, 4) || !aligned(at->out, 4) || !aligned(at->lse, 4))
+    return fail(KAMERA_E_ALIGN, "q, out and lse must be 4-byte aligned");
+  if (L == 0) return KAMERA_OK;
+  // Splits: enough workgroups to fill the chip, at least 64 tokens each.
+  const int64_t units = L * K.heads;
+  int64_t S = std::max<int64_t>(1, ceil_div(4096, units));
+  S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(T, 64)));
+  const int es = env_int("KAMERA_ATTEND_SPLITS", 0);
+  if (es > 0) S = es;
+  if (T > 0) {
+    int64_t TS = ceil_div(T, S);
+    TS = ceil_div(TS, 32) * 32;
+    S = ceil_div(T, TS);
+    plan->splits = S;
+    plan->split_tokens = TS;
+    plan->slots = S + std::max<int64_t>(n, 1) - 1;
+    plan->bytes = L * Hq * plan->slots * kamera::kAttendPartial * 4;
+  }
+  return KAMERA_OK;
+}
+
+kamera_status run_attend(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamera_patch* p,
+                         const kamera_attend_desc* at, void* ws, int64_t ws_bytes,
+                         hipStream_t stream) {
+  g_last_error.clear();
+  AttendPlan plan;
+  kamera_status st = validate_attend(kv, ch, p, at, &plan);
+  if (st != KAMERA_OK || kv->num_layers == 0) return st;
+  const int64_t L = kv->num_layers, T = ch->total_tokens, Hq = at->num_q_heads;
+  const int m = p ? p->rank : 0;
+  if (plan.bytes > 0) {
+    if (!ws) return fail(KAMERA_E_NULL, "workspace is NULL");
+    if (!aligned(ws, 16)) return fail(KAMERA_E_ALIGN, "workspace not 16-byte aligned");
+    if (ws_bytes < plan.bytes)
+      return fail(KAMERA_E_SHAPE, "workspace of %lld bytes is below the %lld needed",
+                  (long long)ws_bytes, (long long)plan.bytes);
+  }
+  // Written buffers must not overlap each other or anything read.
+  struct Range { const void* p; int64_t n; };
+  Range w[3] = {{at->out, L * Hq * kamera::kAttendDim * 4},
+                {at->lse, at->lse ? L * Hq * 4 : 0},
+                {ws, plan.bytes}};
+  Range r[7];
+  int nr = 0;
+  r[nr++] = {at->q, L * Hq * kamera::kAttendDim * 4};
+  for (int c = 0; c < 2; ++c) {
+    int64_t end = 0;
+    if (!kv_extent(kv->ch[c], L, T, kv->page_size, kv->num_pages, 2, &end))
+      return fail(KAMERA_E_SHAPE, "channel %d: KV extent overflows", c);
+    r[nr++] = {kv->ch[c].data, T > 0 ? end : 0};
+    if (m > 0) {
+      r[nr++] = {p->U[c], L * T * m * 2};
+      r[nr++] = {p->V[c], L * ch->num_chunks * (int64_t)kv->ch[c].heads * kv->ch[c].dim * m * 2};
+    }
+  }
+  for (int a = 0; a < 3; ++a) {
+    for (int b = a + 1; b < 3; ++b)
+      if (overlaps(w[a].p, w[a].n, w[b].p, w[b].n))
+        return fail(KAMERA_E_ALIAS, "out, lse and the workspace overlap");
+    for (int b = 0; b < nr; ++b)
+      if (overlaps(w[a].p, w[a].n, r[b].p, r[b].n))
+        return fail(KAMERA_E_ALIAS, "out, lse or the workspace overlaps q, the cache or the factors");
+  }
+  kamera::AttendArgs a;
+  memset(&a, 0, sizeof a);
+  for (int c = 0; c < 2; ++c) {
+    const kamera_channel& k = kv->ch[c];
+    a.data[c] = k.data;
+    a.layer_stride[c] = k.layer_stride;
+    a.slot_stride[c] = k.slot_stride;
+    a.head_stride[c] = k.head_stride;
+    a.page_stride[c] = k.page_stride;
+    a.U[c] = m > 0 ? p->U[c] : nullptr;
+    a.V[c] = m > 0 ? p->V[c] : nullptr;
+  }
+  a.block_table = kv->block_table;
+  a.num_pages = kv->num_pages;
+  a.offsets = ch->token_offsets;
+  a.delta = ch->delta;
+  a.q = at->q;
+  a.out = at->out;
+  a.lse = at->lse;
+  a.ws = (float*)ws;
+  a.total_tokens = T;
+  a.num_chunks = ch->num_chunks;
+  a.num_sections = kv->num_sections > 1 ? kv->num_sections : 1;
+  int end = 0;
+  for (int s = 0; s < 4; ++s) {
+    end += s < kv->num_sections ? kv->section_pairs[s] : 0;
+    a.sec_end[s] = kv->num_sections > 1 ? end : (1 << 30);
+  }
+  a.pairing = kv->pairing;
+  a.rope_dim = kv->ch[0].rope_dim;
+  a.page_size = kv->page_size;
+  a.num_layers = (int32_t)L;
+  a.heads = kv->ch[0].heads;
+  a.num_q_heads = (int32_t)Hq;
+  a.group = (int32_t)(Hq / a.heads);
+  a.rank = m;
+  a.splits = (int32_t)plan.splits;
+  a.split_tokens = (int32_t)plan.split_tokens;
+  a.slots = (int32_t)plan.slots;
+  a.scale_log2 = at->scale * 1.4426950408889634f;
+  for (int i = 0; i < a.rope_dim / 2 && i < 64; ++i)
+    a.omega[i] = pow(kv->rope_theta, -2.0 * (double)i / (double)a.rope_dim);
+  const hipError_t e = kamera::launch_attend(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return KAMERA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+kamera_status kamera_attend_workspace(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                                      const kamera_attend_desc* attend, int64_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(KAMERA_E_NULL, "bytes is NULL");
+  *bytes = 0;
+  AttendPlan plan;
+  const kamera_status st = validate_attend(kv, chunks, nullptr, attend, &plan);
+  if (st != KAMERA_OK) return st;
+  *bytes = plan.bytes;
+  return KAMERA_OK;
+}
+
+kamera_status kamera_attend(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                            const kamera_patch* patch, const kamera_attend_desc* attend,
+                            void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return run_attend(kv, chunks, patch, attend, workspace, workspace_bytes, stream);
+}
 
 kamera_status kamera_form_workspace(const kamera_form_desc* desc, const kamera_chunks* chunks,
                                     int64_t* bytes) {

@@ -74,6 +74,36 @@ struct FormArgs {
   int32_t num_layers;
 };
 
+// Relocate-on-read decode attention (attend.hip): K = channel 0, V = channel 1, bf16,
+// dim 128; tokens are cut into `splits` ranges of `split_tokens`, and each range into
+// segments at chunk boundaries; segment (split s, chunk j) writes partial slot s + j.
+struct AttendArgs {
+  const void* data[2];
+  int64_t layer_stride[2], slot_stride[2], head_stride[2], page_stride[2];
+  const void* U[2];           // [layers][tokens][rank] bf16, or nullptr at rank 0
+  const void* V[2];           // [layers][chunks][heads*128][rank] bf16
+  const int32_t* block_table;
+  int64_t num_pages;
+  const int64_t* offsets;     // [chunks + 1]
+  const int64_t* delta;       // [chunks][num_sections]
+  const float* q;             // [layers][num_q_heads][128]
+  float* out;                 // [layers][num_q_heads][128]
+  float* lse;                 // [layers][num_q_heads] or nullptr
+  float* ws;                  // [layers][num_q_heads][slots][130]: max, sum, 128 partial sums
+  int64_t total_tokens;
+  int32_t num_chunks, num_sections, sec_end[4], pairing, rope_dim;
+  int32_t page_size, num_layers, heads, num_q_heads, group, rank;
+  int32_t splits, split_tokens, slots;
+  float scale_log2;           // softmax scale * log2(e): scores are kept in base 2
+  double omega[64];           // theta^(-2i/rope_dim)
+};
+
+constexpr int kAttendDim = 128;
+constexpr int kAttendMaxGroup = 8;
+constexpr int kAttendPartial = kAttendDim + 2;  // floats per partial slot
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
 // Floats of workspace one problem needs.
 int64_t form_workspace_floats(int F, int k);
 // Problems [p0, p0 + count) of one channel (problem = layer * num_chunks + chunk).

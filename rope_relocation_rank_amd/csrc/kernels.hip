@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "kamera_internal.h"
+#include "rope_device.h"
 
 namespace kamera {
 namespace {
@@ -148,20 +149,6 @@ __device__ __forceinline__ void store_nt(uint8_t* p, const u32x2_t& v) {
 __device__ __forceinline__ float load_f(const uint8_t* p) { return fp8_pair(*p, false).x; }
 __device__ __forceinline__ void store_f(uint8_t* p, float y) {
   *p = (uint8_t)(fp8_put(y, 0.f, 0u, false) & 0xffu);
-}
-
-// Value of lane (l ^ X) within each 16-lane row, X in {1, 2, 4, 8}.  Every lane of the
-// wavefront must execute it.
-template <int X>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  if constexpr (X == 1)  // quad_perm [1,0,3,2]
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);
-  else if constexpr (X == 2)  // quad_perm [2,3,0,1]
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);
-  else if constexpr (X == 8)  // row_ror:8 swaps the two 8-lane halves of a row
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, true);
-  else  // swizzle bit mode: and 0x1f, or 0, xor 4
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);
 }
 
 template <int X>
@@ -335,39 +322,6 @@ __device__ __forceinline__ int find_chunk(const int64_t* off, int n, int64_t t) 
   return lo;
 }
 
-// cos and sin of phi = delta * omega, rounded to fp32.  phi is formed in fp64 and
-// reduced by pi/2 with the two-constant Cody-Waite method (inside the FMA the first
-// product is exact for |phi| < 2^53); on the reduced |r| <= pi/4 the Taylor series of
-// sin (through r^11) and cos (through r^12) are summed in fp64, whose truncation error
-// (< 2e-9 relative) stays far below fp32 rounding; the quadrant picks signs and order.
-__device__ __forceinline__ float2 phase_of(double omega, int64_t delta) {
-  const double kPio2a = 0x1.921fb54442d18p+0;    // pi/2 rounded to a double
-  const double kPio2b = 0x1.1a62633145c07p-54;   // pi/2 minus the above
-  const double kTwoOverPi = 0x1.45f306dc9c883p-1;
-  const double phi = (double)delta * omega;
-  const double k = rint(phi * kTwoOverPi);
-  double r = fma(-k, kPio2a, phi);
-  r = fma(-k, kPio2b, r);
-  const double r2 = r * r;
-  double sp = -1.0 / 39916800.0;
-  sp = fma(sp, r2, 1.0 / 362880.0);
-  sp = fma(sp, r2, -1.0 / 5040.0);
-  sp = fma(sp, r2, 1.0 / 120.0);
-  sp = fma(sp, r2, -1.0 / 6.0);
-  const double sr = fma(r * r2, sp, r);
-  double cp = 1.0 / 479001600.0;
-  cp = fma(cp, r2, -1.0 / 3628800.0);
-  cp = fma(cp, r2, 1.0 / 40320.0);
-  cp = fma(cp, r2, -1.0 / 720.0);
-  cp = fma(cp, r2, 1.0 / 24.0);
-  cp = fma(cp, r2, -0.5);
-  const double cr = fma(r2, cp, 1.0);
-  const int qd = (int)((int64_t)k & 3);
-  const double c = qd == 0 ? cr : qd == 1 ? -sr : qd == 2 ? -cr : sr;
-  const double s = qd == 0 ? sr : qd == 1 ? cr : qd == 2 ? -sr : -cr;
-  return make_float2((float)c, (float)s);
-}
-
 // Generic-kernel phase: plain fp64 pow and sincos per element pair.
 __device__ __forceinline__ void phase_generic(double theta, int r, int i, int64_t delta,
                                               float& c, float& s) {
@@ -401,28 +355,9 @@ __device__ __forceinline__ int stage_block_table(const CommonArgs& cm, int64_t t
   return stage_table(cm.block_table, cm.num_pages, cm.page_size, tb0, t1, sbt);
 }
 
-// Element offset, inside one layer, of the slot of token t (-1: token left untouched).
-__device__ __forceinline__ int64_t slot_staged(const CommonArgs& cm, const int* sbt, int p0,
-                                               int64_t page_stride, int64_t slot_stride,
-                                               int64_t t) {
-  if (cm.page_size > 0) {
-    const int tt = (int)t;
-    int pi, si;
-    if (cm.page_shift >= 0) {
-      pi = tt >> cm.page_shift;
-      si = tt & (cm.page_size - 1);
-    } else {
-      pi = tt / cm.page_size;
-      si = tt - pi * cm.page_size;
-    }
-    const int pg = sbt[pi - p0];
-    return pg < 0 ? -1 : (int64_t)pg * page_stride + (int64_t)si * slot_stride;
-  }
-  return t * slot_stride;
-}
-
-// Same as slot_staged in 32-bit arithmetic, for channels whose per-layer extent is
-// below 2^31 elements; PAGED selects the addressing at compile time.
+// Element offset, inside one layer, of the slot of token t (-1: token left untouched),
+// in 32-bit arithmetic: the tuned kernels take channels whose per-layer extent is below
+// 2^31 elements.  PAGED selects the addressing at compile time.
 template <bool PAGED>
 __device__ __forceinline__ int32_t slot32(int page_size, int page_shift, const int* sbt, int p0,
                                           int32_t page_stride, int32_t slot_stride, int t) {

@@ -27,6 +27,7 @@ KERNEL_NAMES = {0: "none", 1: "rotate", 2: "rotate+patch mfma", 3: "generic"}
 
 EXPORTED = ["kamera_relocate", "kamera_relocate_patch", "kamera_recall_patch", "kamera_plan",
             "kamera_recall_plan", "kamera_form_workspace", "kamera_form_patch", "kamera_form_gram",
+            "kamera_attend_workspace", "kamera_attend",
             "kamera_status_str", "kamera_last_error", "kamera_abi_version"]
 KAMERA_FORM_MAX_RANK = 112
 
@@ -63,6 +64,12 @@ class kamera_form_desc(C.Structure):
                 ("rank", C.c_int32), ("width", C.c_int32 * 2), ("iterations", C.c_int32),
                 ("reserved0", C.c_int32), ("delta", C.c_void_p * 2), ("U", C.c_void_p * 2),
                 ("V", C.c_void_p * 2), ("sigma", C.c_void_p * 2)]
+
+
+class kamera_attend_desc(C.Structure):
+    _fields_ = [("num_q_heads", C.c_int32), ("reserved0", C.c_int32), ("scale", C.c_float),
+                ("reserved1", C.c_int32), ("q", C.c_void_p), ("out", C.c_void_p),
+                ("lse", C.c_void_p)]
 
 
 class kamera_plan_info(C.Structure):
@@ -113,6 +120,13 @@ def lib():
         L.kamera_form_gram.restype = C.c_int
         L.kamera_form_gram.argtypes = [C.POINTER(kamera_form_desc), C.POINTER(kamera_chunks),
                                        C.POINTER(C.c_void_p), C.c_void_p]
+        L.kamera_attend_workspace.restype = C.c_int
+        L.kamera_attend_workspace.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
+                                              C.POINTER(kamera_attend_desc), C.POINTER(C.c_int64)]
+        L.kamera_attend.restype = C.c_int
+        L.kamera_attend.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
+                                    C.POINTER(kamera_patch), C.POINTER(kamera_attend_desc),
+                                    C.c_void_p, C.c_int64, C.c_void_p]
         L.kamera_status_str.restype = C.c_char_p
         L.kamera_status_str.argtypes = [C.c_int]
         L.kamera_last_error.restype = C.c_char_p
@@ -299,3 +313,33 @@ def form_gram(desc: kamera_form_desc, chunks: kamera_chunks, G, stream=None) -> 
     s = current_stream() if stream is None else stream
     arr = (C.c_void_p * 2)(*[g.data_ptr() for g in G] + [None] * (2 - len(G)))
     check(lib().kamera_form_gram(C.byref(desc), C.byref(chunks), arr, s))
+
+
+# ------------------------------------------------------------- relocate-on-read attention
+
+def attend_desc(q, out, *, scale: float, lse=None) -> kamera_attend_desc:
+    """Attention descriptor over torch tensors: q and out [L][Hq][128] fp32, lse [L][Hq]."""
+    d = kamera_attend_desc()
+    d.num_q_heads = q.shape[1]
+    d.reserved0 = d.reserved1 = 0
+    d.scale = float(scale)
+    d.q = q.data_ptr()
+    d.out = out.data_ptr()
+    d.lse = None if lse is None else lse.data_ptr()
+    return d
+
+
+def kamera_attend_workspace(kv, chunks, attend):
+    n = C.c_int64(0)
+    st = lib().kamera_attend_workspace(_ref(kv), _ref(chunks), _ref(attend), C.byref(n))
+    return st, n.value
+
+
+def attend(kv: kamera_kv_desc, chunks: kamera_chunks, patch, desc: kamera_attend_desc,
+           workspace, stream=None) -> None:
+    """Enqueue relocate-on-read decode attention; `workspace` is a torch uint8 tensor of
+    at least kamera_attend_workspace bytes (or None when that is 0)."""
+    s = current_stream() if stream is None else stream
+    ws = None if workspace is None else workspace.data_ptr()
+    nb = 0 if workspace is None else workspace.numel()
+    check(lib().kamera_attend(C.byref(kv), C.byref(chunks), _ref(patch), C.byref(desc), ws, nb, s))

@@ -84,3 +84,25 @@ def recall_plan(rinp, flags: int = 0):
     st, info = K.kamera_recall_plan(src, dst, ch, patch)
     K.check(st)
     return info
+
+
+def attend_buffers(inp, q, scale: float, flags: int = 0):
+    """(descriptors, out, lse, workspace) for relocate-on-read attention of query `q`
+    [L][Hq][128] fp32 over the cache of a synth.Inputs instance."""
+    import torch
+    kv, ch, patch = descriptors_for(inp, flags)
+    L, Hq, D = q.shape
+    out = torch.empty((L, Hq, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((L, Hq), dtype=torch.float32, device=q.device)
+    desc = K.attend_desc(q, out, scale=scale, lse=lse)
+    st, nbytes = K.kamera_attend_workspace(kv, ch, desc)
+    K.check(st)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device) if nbytes else None
+    return (kv, ch, patch, desc), out, lse, ws
+
+
+def attend(inp, q, scale: float, stream=None, flags: int = 0):
+    """Relocate-on-read decode attention: returns (out [L][Hq][128], lse [L][Hq])."""
+    (kv, ch, patch, desc), out, lse, ws = attend_buffers(inp, q, scale, flags)
+    K.attend(kv, ch, patch, desc, ws, stream)
+    return out, lse

@@ -32,6 +32,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 KIND_KV, KIND_U, KIND_V, KIND_STRUCT, KIND_DST = 0, 1, 2, 3, 4
+KIND_QUERY = 6
 DST_SENTINEL = 0x7FC1  # bf16 NaN with a payload the operator never produces
 DST_SENTINEL_FP8 = 0x7F  # E4M3 NaN: the operator never produces it from finite inputs
 
@@ -68,6 +69,7 @@ class Workload:
     recall: bool = False        # out of place: canonical store -> destination cache
     dst_page_size: int = 0      # recall destination: 0 contiguous, > 0 paged
     dst_pool_pages: int = 0     # recall destination pool pages per layer (paged)
+    q_heads: int = 0            # decode attention: query heads (0 = the KV heads)
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -93,12 +95,13 @@ WORKLOADS = {
         note="tiny MHA, 1 layer, T=256, 8 heads x 64, delta +37, rank-4 patch on K and V"),
     "qwen25vl7b_segment": Workload(
         key="qwen25vl7b_segment", wid=1, family="gqa", layers=28, heads=4, head_dim=128,
-        theta=1e6, rank=32, passes=(0, 32), tokens=4096, delta=-1536, outliers=4,
+        theta=1e6, rank=32, passes=(0, 32), tokens=4096, delta=-1536, outliers=4, q_heads=28,
         note="Qwen2.5-VL-7B-shaped video segment: 28 layers, 4 KV heads x 128, T=4096, "
              "delta -1536; rotation-only pass then rank-32 patch pass"),
     "llama3_8b_reorder": Workload(
         key="llama3_8b_reorder", wid=2, family="gqa", layers=32, heads=8, head_dim=128,
         theta=5e5, rank=16, n_chunks=64, chunk_len=(256, 2048), delta_range=(-32768, 32768),
+        q_heads=32,
         note="Llama-3-8B-shaped reorder batch: 32 layers, 8 KV heads x 128, 64 chunks of "
              "256..2048 tokens, per-chunk delta in [-32768, 32768], rank-16 per chunk"),
     "deepseek_v3_mla": Workload(
@@ -108,7 +111,7 @@ WORKLOADS = {
              "delta +100000, rank-64 on both channels"),
     "long_video_72b_paged": Workload(
         key="long_video_72b_paged", wid=4, family="gqa", layers=80, heads=8, head_dim=128,
-        theta=1e6, rank=64, tokens=32768, delta=65536, page_size=16, pool_pages=2048,
+        theta=1e6, rank=64, tokens=32768, delta=65536, page_size=16, pool_pages=2048, q_heads=64,
         note="72B-shaped long-video paged cache: 80 layers, 8 KV heads x 128, T=32768 in "
              "16-token pages scattered by a random block table, delta +65536, rank-64"),
     "qwen25vl7b_segment_fp8": Workload(
@@ -429,6 +432,20 @@ def make_recall_inputs(w: Workload, rank: int, device="cpu", pass_id: int = 0) -
     if table is not None:
         r.dst_block_table_t = torch.as_tensor(table, device=device)
     return r
+
+
+# ------------------------------------------------------------------ decode attention input
+
+def make_query(w: Workload, device="cpu", pass_id: int = 0):
+    """Decode queries [L][Hq][head_dim] fp32 ~ N(0, 1), Hq = w.q_heads (or the KV
+    heads): one new token's query per layer, already rotated to its own position."""
+    import torch
+    hq = w.q_heads or w.heads
+    q = torch.empty((w.layers, hq, w.head_dim), dtype=torch.float32, device=device)
+    for l in range(w.layers):
+        q[l] = _normal((hq, w.head_dim), seed_of(w.wid + 1000 * pass_id, KIND_QUERY, l), 1.0,
+                       device, torch.float32)
+    return q
 
 
 # ------------------------------------------------------------------ patch formation input

@@ -401,3 +401,136 @@ def sampled_check_recall(rinp, run, n=1024, seed=0) -> Report:
                                          float(scales[c][l]) if scales else 1.0),
                     src.rank, rep)
     return rep
+
+
+# ----------------------------------------------------------------- relocate-on-read attention
+
+@dataclass
+class AttendReport:
+    elements: int = 0
+    failures: int = 0
+    lse_failures: int = 0
+    max_err: float = 0.0     # max |g - y| / tol
+    max_rel: float = 0.0     # max |g - y| / mag
+
+    def ok(self) -> bool:
+        return self.failures == 0 and self.lse_failures == 0
+
+    def __str__(self) -> str:
+        return (f"elements={self.elements} failures={self.failures} "
+                f"lse_failures={self.lse_failures} max_err/tol={self.max_err:.3g} "
+                f"max_err/mag={self.max_rel:.3g}")
+
+
+def _channel_rows(inp, c, layer):
+    """Values [T][heads * dim] of channel c at one layer, through its layout."""
+    lay = inp.layouts[c]
+    w, st = inp.workload, inp.struct
+    T = st.total_tokens
+    t = np.arange(T)
+    if w.page_size > 0:
+        slot = (st.block_table[t // w.page_size].astype(np.int64) * lay["page_stride"] +
+                (t % w.page_size) * lay["slot_stride"])
+    else:
+        slot = t * lay["slot_stride"]
+    H, D = lay["heads"], lay["dim"]
+    cols = (np.arange(H)[:, None] * lay["head_stride"] + np.arange(D)[None, :]).ravel()
+    idx = lay.get("offset", 0) + layer * lay["layer_stride"] + slot[:, None] + cols[None, :]
+    vals = storage_value(host_bits(inp.buffers[lay["buffer"]]))
+    return vals[idx]
+
+
+def attend_bounds(inp, q, scale):
+    """Bound sm[l][h] on the summed magnitudes of the terms of any score, for an fp32
+    evaluation of the re-associated attention: sm = scale * max_t (sum_d (|q_d| +
+    |q_partner(d)|) |K_t,d| + sum_k |u_t,k| sum_d |q_d| |V_K[d][k]|), where the rotated
+    query's components are bounded by |q_d| + |q of d's rotary partner|."""
+    w, st = inp.workload, inp.struct
+    L, Hq, D = q.shape
+    H = w.heads
+    G = Hq // H
+    m = inp.rank
+    qa = np.abs(q.astype(np.float64))
+    r = inp.layouts[0]["rope_dim"]
+    qb = qa.copy()
+    if r:
+        half = r // 2
+        if w.pairing == 1:
+            qb[..., :r] += qa[..., :r].reshape(L, Hq, half, 2)[..., ::-1].reshape(L, Hq, r)
+        else:
+            qb[..., :half] += qa[..., half:r]
+            qb[..., half:r] += qa[..., :half]
+    sm = np.zeros((L, Hq))
+    T = st.total_tokens
+    if T == 0:
+        return sm
+    j_of_t = np.searchsorted(st.offsets, np.arange(T), side="right") - 1
+    U0 = V0 = None
+    if m > 0:
+        U0 = np.abs(bf16_value(host_bits(inp.U[0]))).reshape(L, T, m)
+        V0 = np.abs(bf16_value(host_bits(inp.V[0]))).reshape(L, st.num_chunks, H, D, m)
+    for l in range(L):
+        rows = np.abs(_channel_rows(inp, 0, l)).reshape(T, H, D)
+        for h in range(Hq):
+            g = h // G
+            s = rows[:, g, :] @ qb[l, h]
+            if m > 0:
+                wv = np.einsum("d,jdk->jk", qa[l, h], V0[l, :, g])  # [chunks][m]
+                s = s + (U0[l] * wv[j_of_t]).sum(axis=1)
+            sm[l, h] = s.max()
+    return sm * abs(scale)
+
+
+def check_attend(inp, q, scale, run) -> AttendReport:
+    """Run `run(inp, q, scale)` -> (out, lse) on the GPU and compare with the oracle's
+    attention element by element, within attend_tolerance."""
+    import torch
+    from oracle import oracle as orc
+    w = inp.workload
+    bufs = [host_bits(b) for b in inp.buffers]
+    chans = _dicts(inp.layouts, [b.copy() for b in bufs],
+                   ([host_bits(u) for u in inp.U], [host_bits(v) for v in inp.V]), inp.rank)
+    qh = q.detach().cpu().numpy().astype(np.float64)
+    out, lse = run(inp, q, scale)
+    if out.is_cuda:
+        torch.cuda.synchronize()
+    g = out.detach().cpu().numpy().astype(np.float64)
+    gl = lse.detach().cpu().numpy().astype(np.float64)
+    y, yl, mag = orc.attend(chans, num_layers=w.layers, theta=w.theta, offsets=inp.struct.offsets,
+                            delta=inp.struct.delta, q=qh, scale=scale, rank=inp.rank,
+                            page_size=w.page_size, block_table=inp.struct.block_table,
+                            pairing=w.pairing, sections=w.sections, with_mag=True)
+    # A score's fp32 error is below (D + m + 8) 2^-24 sm; each weight's relative error is
+    # below twice that (numerator and normaliser), and the sums over T tokens and m
+    # patch terms add (T + m + 32) 2^-24 relative, all scaling mag = sum_t p_t |V'_t|.
+    # lse carries the score error plus the normaliser's summation error.
+    eps = 2.0 ** -24
+    D, m, T = q.shape[2], inp.rank, inp.struct.total_tokens
+    sm = attend_bounds(inp, qh, scale)
+    ds = (D + m + 8) * eps * sm
+    rel = 2 * ds + (T + m + 32) * eps
+    tol = rel[..., None] * mag + 1e-30
+    err = np.abs(g - y)
+    rep = AttendReport(elements=int(g.size))
+    rep.failures = int((~(err <= tol)).sum())
+    rep.max_err = float(np.nan_to_num(err / tol, nan=np.inf).max()) if g.size else 0.0
+    rep.max_rel = float(np.nan_to_num(err / np.maximum(mag, 1e-30), nan=np.inf).max()) if g.size else 0.0
+    finite = np.isfinite(yl)
+    lse_tol = 2 * ds + (T + 32) * eps + 1e-6
+    rep.lse_failures = int((finite & ~(np.abs(gl - yl) <= lse_tol)).sum() +
+                           (~finite & ~(gl == yl)).sum())
+    return rep
+
+
+def layer_slice(inp, layer):
+    """A one-layer view of a synth.Inputs (same chunks, layout and table), on the same
+    device: buffers, factors and workload cut to `layer`."""
+    from rope_relocation_rank_amd import synth
+    w = inp.workload.with_(layers=1)
+    sub = synth.Inputs(w, inp.rank, inp.struct, inp.pool_pages,
+                       [b[layer:layer + 1].contiguous() for b in inp.buffers], inp.layouts,
+                       [u[layer:layer + 1].contiguous() for u in inp.U],
+                       [v[layer:layer + 1].contiguous() for v in inp.V],
+                       inp.offsets_t, inp.delta_t, inp.block_table_t,
+                       scales=[s[layer:layer + 1].contiguous() for s in inp.scales])
+    return sub

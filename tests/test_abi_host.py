@@ -45,6 +45,8 @@ def test_struct_layout_matches_header():
         "kamera_chunks": [f[0] for f in K.kamera_chunks._fields_],
         "kamera_patch": [f[0] for f in K.kamera_patch._fields_],
         "kamera_plan_info": [f[0] for f in K.kamera_plan_info._fields_],
+        "kamera_form_desc": [f[0] for f in K.kamera_form_desc._fields_],
+        "kamera_attend_desc": [f[0] for f in K.kamera_attend_desc._fields_],
     }
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "kamera.h"', "int main(void){"]
     for s, fs in fields.items():
@@ -516,3 +518,76 @@ def test_form_patch_checks_before_launch():
     assert st == K.KAMERA_E_ALIGN
     st = L_.kamera_form_patch(C.byref(d), C.byref(ch), C.c_void_p(FAKE + (7 << 40)), 1024, None)
     assert st == K.KAMERA_E_SHAPE  # workspace too small for one problem
+
+
+# ----------------------------------------------------------------- relocate-on-read attention
+
+def attend(Hq=28, L=28, T=4096, H=4, m=32, **kw):
+    kv, ch, p = gqa(T=T, L=L, H=H, m=m, **kw)
+    d = K.kamera_attend_desc()
+    d.num_q_heads, d.scale = Hq, 0.088
+    d.q = FAKE + (9 << 40)
+    d.out = FAKE + (10 << 40)
+    d.lse = FAKE + (11 << 40)
+    return kv, ch, p, d
+
+
+def attend_status(kv, ch, p, d):
+    st, _ = K.kamera_attend_workspace(kv, ch, d)
+    if st == K.KAMERA_OK:
+        # the launch call rejects before any HIP call too, through its workspace check
+        st2 = K.lib().kamera_attend(C.byref(kv), C.byref(ch), None if p is None else C.byref(p),
+                                    C.byref(d), None, 0, None)
+        return st, st2
+    return st, None
+
+
+def test_attend_workspace_and_checks():
+    kv, ch, p, d = attend()
+    st, nbytes = K.kamera_attend_workspace(kv, ch, d)
+    assert st == K.KAMERA_OK and nbytes > 0
+    # splits fill the chip: L * heads * splits workgroups, slots = splits + chunks - 1
+    assert nbytes % (28 * 28 * 130 * 4) == 0
+    st, st2 = attend_status(kv, ch, p, d)
+    assert st2 == K.KAMERA_E_NULL  # no workspace given
+    for mutate, status in [
+        (lambda kv, ch, p, d: setattr(d, "num_q_heads", 30), K.KAMERA_E_SHAPE),
+        (lambda kv, ch, p, d: setattr(d, "num_q_heads", 36), K.KAMERA_E_UNSUPPORTED),
+        (lambda kv, ch, p, d: setattr(d, "reserved0", 1), K.KAMERA_E_SHAPE),
+        (lambda kv, ch, p, d: setattr(d, "scale", float("inf")), K.KAMERA_E_SHAPE),
+        (lambda kv, ch, p, d: setattr(d, "q", None), K.KAMERA_E_NULL),
+        (lambda kv, ch, p, d: setattr(d, "out", FAKE + (10 << 40) + 2), K.KAMERA_E_ALIGN),
+        (lambda kv, ch, p, d: setattr(kv, "dtype", K.KAMERA_F32), K.KAMERA_E_UNSUPPORTED),
+        (lambda kv, ch, p, d: setattr(kv, "num_channels", 1), K.KAMERA_E_UNSUPPORTED),
+        (lambda kv, ch, p, d: setattr(kv.ch[1], "rope_dim", 128), K.KAMERA_E_SHAPE),
+    ]:
+        kv, ch, p, d = attend()
+        mutate(kv, ch, p, d)
+        st, _ = K.kamera_attend_workspace(kv, ch, d)
+        assert st == status, (st, K.kamera_last_error())
+    kv, ch, p, d = attend()
+    kv.ch[0].dim = kv.ch[1].dim = 64
+    kv.ch[0].rope_dim = 64
+    st, _ = K.kamera_attend_workspace(kv, ch, d)
+    assert st == K.KAMERA_E_UNSUPPORTED
+    # rank above 128 is refused at launch (the workspace does not depend on the rank)
+    kv, ch, p, d = attend(m=136)
+    assert K.lib().kamera_attend(C.byref(kv), C.byref(ch), C.byref(p), C.byref(d), None, 0,
+                                 None) == K.KAMERA_E_UNSUPPORTED
+
+
+def test_attend_aliasing():
+    kv, ch, p, d = attend(T=64, L=2)
+    _, nbytes = K.kamera_attend_workspace(kv, ch, d)
+    ws = FAKE + (12 << 40)
+    def call():
+        return K.lib().kamera_attend(C.byref(kv), C.byref(ch), C.byref(p), C.byref(d), ws,
+                                     nbytes, None)
+    d.out = d.q  # output on top of the query
+    assert call() == K.KAMERA_E_ALIAS
+    d.out = FAKE + (10 << 40)
+    d.lse = FAKE + (10 << 40) + 16  # lse inside out
+    assert call() == K.KAMERA_E_ALIAS
+    d.lse = FAKE + (11 << 40)
+    ws = FAKE  # workspace on the K cache
+    assert call() == K.KAMERA_E_ALIAS
