@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=1024)
     ap.add_argument("--form", action="store_true",
                     help="measure patch formation (kamera_form_patch) on the workload's shape")
+    ap.add_argument("--attend", action="store_true",
+                    help="measure relocate-on-read decode attention (kamera_attend) on the "
+                         "workload's cache, beside relocate + patch followed by attention")
     return ap.parse_args()
 
 
@@ -85,6 +88,8 @@ def main():
     w = synth.get(args.workload)
     if args.form:
         return bench_form(args, w, dev)
+    if args.attend:
+        return bench_attend(args, w, dev)
     ranks = w.rank_passes
     dominant = max(range(len(ranks)), key=lambda i: synth.algorithmic_bytes(w, ranks[i]))
     bytes_pass = [synth.algorithmic_bytes(w, r) for r in ranks]
@@ -319,6 +324,176 @@ def bench_form(args, w, dev):
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def attend_bytes(w, rank: int) -> int:
+    """Algorithmic bytes of one decode-attention call over the whole cache: K and V rows
+    read once, both U factors and both feature factors read once, queries read and
+    outputs (and lse) written.  The partial sums the split kernel exchanges with the
+    merge kernel are not counted."""
+    from rope_relocation_rank_amd import synth
+    st = synth.structure(w)
+    T, n, L = st.total_tokens, st.num_chunks, w.layers
+    F = w.heads * w.head_dim
+    hq = w.q_heads or w.heads
+    kv = 2 * L * T * F * w.elem_size
+    fac = 2 * L * (T * rank + n * F * rank) * 2
+    qo = L * hq * (2 * w.head_dim + 1) * 4
+    return kv + fac + qo
+
+
+def bench_attend(args, w, dev):
+    """Relocate-on-read decode attention (kamera_attend) over the workload's cache at
+    its patch rank, one query per layer and query head.  value = algorithmic GB/s over
+    whole calls (inputs cycled through copies so no call finds its cache in the MALL);
+    beside it, the same attention done the other way: relocate + patch in place
+    (kamera_relocate_patch), then plain attention over the rewritten cache."""
+    import ctypes as C
+
+    import torch
+
+    from rope_relocation_rank_amd import kamera as K
+    from rope_relocation_rank_amd import ops, synth
+
+    m = w.rank
+    st = synth.structure(w)
+    per = attend_bytes(w, m)
+    copies = args.copies or max(1, min(8, -(-2_000_000_000 // per)))
+    print(f"[bench] attend {w.key}: rank {m}, {w.q_heads or w.heads} query heads, "
+          f"{per} B per call, {copies} copies", file=sys.stderr, flush=True)
+    scale = w.head_dim ** -0.5
+    base = synth.make_inputs(w, m, device=dev)
+    q = synth.make_query(w, device=dev)
+    insts = [base]
+    for _ in range(copies - 1):
+        insts.append(synth.Inputs(base.workload, base.rank, base.struct, base.pool_pages,
+                                  [b.clone() for b in base.buffers], base.layouts,
+                                  [u.clone() for u in base.U], [v.clone() for v in base.V],
+                                  base.offsets_t, base.delta_t, base.block_table_t))
+    descs = [ops.attend_buffers(c, q, scale) for c in insts]
+    lib = K.lib()
+    stream = torch.cuda.current_stream(dev)
+    s_ptr = C.c_void_p(stream.cuda_stream)
+
+    def fused(i):
+        (kv, ch, p, d), _, _, ws = descs[i]
+        st_ = lib.kamera_attend(C.byref(kv), C.byref(ch), None if p is None else C.byref(p),
+                                C.byref(d), None if ws is None else ws.data_ptr(),
+                                0 if ws is None else ws.numel(), s_ptr)
+        if st_ != 0:
+            raise K.KameraError(st_, K.kamera_last_error())
+
+    # the other way: operator in place, then attention with no motion and no patch
+    zero = torch.zeros_like(base.delta_t)
+    plain = []
+    for c in insts:
+        kv, ch, p = ops.descriptors_for(c)
+        pc = K.chunks_desc(c.offsets_t, zero, st.total_tokens)
+        (kv2, _, _, d2), _, _, ws2 = ops.attend_buffers(c, q, scale)
+        plain.append((kv, ch, p, kv2, pc, d2, ws2))
+
+    def unfused(i):
+        kv, ch, p, kv2, pc, d2, ws2 = plain[i]
+        K.check(lib.kamera_relocate_patch(C.byref(kv), C.byref(ch), C.byref(p), s_ptr))
+        K.check(lib.kamera_attend(C.byref(kv2), C.byref(pc), None, C.byref(d2),
+                                  None if ws2 is None else ws2.data_ptr(),
+                                  0 if ws2 is None else ws2.numel(), s_ptr))
+
+    steps, warm = max(1, args.steps), max(1, args.warmup)
+    for i in range(warm):
+        fused(i % copies)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fused(i % copies)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    for i in range(min(warm, copies)):
+        unfused(i % copies)
+    torch.cuda.synchronize()
+    uv = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        uv[i][0].record(stream)
+        unfused(i % copies)
+        uv[i][1].record(stream)
+    torch.cuda.synchronize()
+    unfused_ms = sum(a.elapsed_time(b) for a, b in uv) / steps
+    achieved = per / (call_ms * 1e-3) / 1e9
+    cpu = None if args.no_cpu_baseline else cpu_baseline_attend(w, m, args.cpu_seconds)
+    line = {
+        "metric": "relocate-on-read decode attention: algorithmic GB/s (K, V and factors read once)",
+        "value": round(per * steps / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(wall * 1e3 / steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp32 compute",
+        "data": "synthetic",
+        "config": {"workload": w.key + " (decode attention)", "rank": m, "layers": w.layers,
+                   "kv_heads": w.heads, "q_heads": w.q_heads or w.heads,
+                   "head_dim": w.head_dim, "tokens": st.total_tokens, "chunks": st.num_chunks,
+                   "page_size": w.page_size, "bytes_per_call": per, "input_copies": copies,
+                   "parallelism": "single GPU"},
+        "call_ms_events": round(call_ms, 5),
+        "relocate_then_attend_ms": round(unfused_ms, 5),
+        "speedup_vs_relocate_then_attend": round(unfused_ms / call_ms, 3),
+        "roofline": {"bound": "hbm", "kernel": "attend_split + attend_combine",
+                     "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(achieved / 8000.0, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": per, "avg_launch_ms": round(call_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_attend(w, m, seconds: float):
+    """The oracle's attention (fp64: K', V' formed, then softmax) on the host, over the
+    leading layers of the same workload (the oracle spreads layers over host threads),
+    repeated until `seconds` have passed."""
+    import torch
+
+    from oracle import oracle as orc
+    from rope_relocation_rank_amd import synth
+
+    ww = w.with_(layers=min(w.layers, orc.num_threads()))
+    inp = synth.make_inputs(ww, m, device="cpu")
+    q = synth.make_query(ww, device="cpu").numpy().astype(np.float64)
+
+    def host(t):
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    chans = []
+    for c, lay in enumerate(inp.layouts):
+        d = dict(lay)
+        d["data"] = host(inp.buffers[lay["buffer"]]).ravel()
+        if m > 0:
+            d["U"], d["V"] = host(inp.U[c]), host(inp.V[c])
+        chans.append(d)
+    done, t = 0, 0.0
+    while t < seconds and done < 1000:
+        t0 = time.perf_counter()
+        orc.attend(chans, num_layers=ww.layers, theta=w.theta, offsets=inp.struct.offsets,
+                   delta=inp.struct.delta, q=q, scale=w.head_dim ** -0.5, rank=m,
+                   page_size=w.page_size, block_table=inp.struct.block_table,
+                   pairing=w.pairing, sections=w.sections)
+        t += time.perf_counter() - t0
+        done += 1
+    b = done * attend_bytes(ww, m)
+    return {"value": round(b / t / 1e9, 4), "unit": "GB/s",
+            "cores": min(orc.num_threads(), ww.layers), "kind": "oracle",
+            "sample": f"{done} x {ww.layers} of {w.layers} layers, every token; {t:.1f} s "
+                      "of compute, input generation excluded"}
 
 
 def cpu_baseline_form(w, m, seconds: float):

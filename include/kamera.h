@@ -229,8 +229,8 @@ KAMERA_API kamera_status kamera_recall_patch(const kamera_kv_desc* src, const ka
  *     whose block-table entry lies outside [0, num_pages) are not attended).  Row bases
  *     8-byte aligned, strides multiples of 8 elements, per-layer extents below 2^31
  *     elements, total_tokens below 2^30.  Other shapes: KAMERA_E_UNSUPPORTED.
- * patch: NULL or rank 0 for plain attention; else rank <= 128, bf16 factors as for
- *     kamera_relocate_patch.
+ * patch: NULL or rank 0 for plain attention; else a rank that is a multiple of 8, up
+ *     to 128, with 16-byte aligned bf16 factors as for kamera_relocate_patch.
  * A head with no attended token gets out = 0 and lse = -inf. */
 typedef struct {
   int32_t num_q_heads;   /* Hq: a multiple of kv.heads, at most 8 times it */
@@ -243,9 +243,10 @@ typedef struct {
   float* lse;            /* device [num_layers][num_q_heads] fp32 (natural log), or NULL */
 } kamera_attend_desc;
 
-/* Bytes of workspace kamera_attend needs for this problem (0 when it is empty). */
+/* Bytes of workspace kamera_attend needs for this problem (0 when it is empty); the
+ * prepared queries and the partial sums depend on the rank, so the patch is an input. */
 KAMERA_API kamera_status kamera_attend_workspace(const kamera_kv_desc* kv,
-                                      const kamera_chunks* chunks,
+                                      const kamera_chunks* chunks, const kamera_patch* patch,
                                       const kamera_attend_desc* attend, int64_t* bytes);
 
 /* Stream-ordered.  workspace: caller-owned device memory of at least the bytes

@@ -642,6 +642,7 @@ kamera_status run_form(const kamera_form_desc* d, const kamera_chunks* ch, void*
 
 struct AttendPlan {
   int64_t splits = 0, split_tokens = 0, slots = 0, bytes = 0;
+  int64_t qw_bytes = 0;  // prepared queries, first in the workspace (256-byte rounded)
 };
 
 // Checks an attention call; no HIP call is made here.
@@ -671,7 +672,11 @@ kamera_status validate_attend(const kamera_kv_desc* kv, const kamera_chunks* ch,
     return fail(KAMERA_E_UNSUPPORTED, "more than %d query heads per KV head", kamera::kAttendMaxGroup);
   if (!std::isfinite(at->scale)) return fail(KAMERA_E_SHAPE, "scale must be finite");
   const int m = p ? p->rank : 0;
-  if (m > 128) return fail(KAMERA_E_UNSUPPORTED, "attention takes rank <= 128");
+  if (m > 128 || m % 8 != 0)
+    return fail(KAMERA_E_UNSUPPORTED, "attention takes ranks that are multiples of 8, up to 128");
+  for (int c = 0; m > 0 && c < 2; ++c)
+    if (!aligned(p->U[c], 16) || !aligned(p->V[c], 16))
+      return fail(KAMERA_E_ALIGN, "channel %d: attention needs 16-byte aligned factors", c);
   const int64_t T = ch->total_tokens, L = kv->num_layers, n = ch->num_chunks;
   if (T >= kMaxTunedTokens) return fail(KAMERA_E_UNSUPPORTED, "total_tokens must be below 2^30");
   for (int c = 0; c < 2; ++c) {
@@ -698,7 +703,8 @@ kamera_status validate_attend(const kamera_kv_desc* kv, const kamera_chunks* ch,
     plan->splits = S;
     plan->split_tokens = TS;
     plan->slots = S + std::max<int64_t>(n, 1) - 1;
-    plan->bytes = L * Hq * plan->slots * kamera::kAttendPartial * 4;
+    plan->qw_bytes = ceil_div(L * std::max<int64_t>(n, 1) * Hq * (kamera::kAttendDim + m) * 4, 256) * 256;
+    plan->bytes = plan->qw_bytes + L * Hq * plan->slots * kamera::attend_slot_floats(m) * 4;
   }
   return KAMERA_OK;
 }
@@ -764,7 +770,8 @@ kamera_status run_attend(const kamera_kv_desc* kv, const kamera_chunks* ch, cons
   a.q = at->q;
   a.out = at->out;
   a.lse = at->lse;
-  a.ws = (float*)ws;
+  a.qw = (float*)ws;
+  a.ws = ws ? (float*)((char*)ws + plan.qw_bytes) : nullptr;
   a.total_tokens = T;
   a.num_chunks = ch->num_chunks;
   a.num_sections = kv->num_sections > 1 ? kv->num_sections : 1;
@@ -784,6 +791,7 @@ kamera_status run_attend(const kamera_kv_desc* kv, const kamera_chunks* ch, cons
   a.splits = (int32_t)plan.splits;
   a.split_tokens = (int32_t)plan.split_tokens;
   a.slots = (int32_t)plan.slots;
+  a.slot_floats = kamera::attend_slot_floats(m);
   a.scale_log2 = at->scale * 1.4426950408889634f;
   for (int i = 0; i < a.rope_dim / 2 && i < 64; ++i)
     a.omega[i] = pow(kv->rope_theta, -2.0 * (double)i / (double)a.rope_dim);
@@ -797,12 +805,13 @@ kamera_status run_attend(const kamera_kv_desc* kv, const kamera_chunks* ch, cons
 extern "C" {
 
 kamera_status kamera_attend_workspace(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                                      const kamera_patch* patch,
                                       const kamera_attend_desc* attend, int64_t* bytes) {
   g_last_error.clear();
   if (!bytes) return fail(KAMERA_E_NULL, "bytes is NULL");
   *bytes = 0;
   AttendPlan plan;
-  const kamera_status st = validate_attend(kv, chunks, nullptr, attend, &plan);
+  const kamera_status st = validate_attend(kv, chunks, patch, attend, &plan);
   if (st != KAMERA_OK) return st;
   *bytes = plan.bytes;
   return KAMERA_OK;

@@ -10,21 +10,22 @@
 // h / group.
 //
 // The products are re-associated so that no K' or V' element is ever formed:
-//     q . K'_t   = (R(-delta_j) q) . K_t + (V_K^T q) . U_K[t]
+//     q . K'_t       = (R(-delta_j) q) . K_t + (V_K^T q) . U_K[t]
 //     sum_t p_t V'_t = sum_t p_t V_t + V_V (sum_t p_t U_V[t])
-// The rotated query and V_K^T q are built once per (split, chunk) segment; per token the
-// kernel reads K_t, V_t and the two U rows once (the bytes an attention kernel reads
-// anyway plus 4m bytes), and the rank-m tail of the output is one V_V product per
-// segment.  The relocate + patch pass that would otherwise write K' and V' back to HBM
-// and the re-read of them disappear.  All arithmetic is fp32 on exactly converted bf16
-// inputs; scores are kept in base 2 (scale * log2 e folded into the query).
-//
-// Work split (flash-decoding): tokens are cut into `splits` ranges per (layer, KV head);
-// a workgroup (4 waves, 8 row groups of 32 lanes, lane c holding features 4c..4c+3)
-// streams its range, cut again at chunk boundaries, with an online softmax per row
-// group; the row groups are merged at the end of each segment, which writes one partial
-// (max, sum, 128 partial sums) per query head.  A second kernel merges the partials of
-// each (layer, query head).
+// so per token the kernels read K_t, V_t and the two U rows once, and the rank-m terms
+// cost one small product per chunk.  Three kernels:
+//   attend_prep   per (layer, chunk, KV head): the rotated query R(-delta_j) q and
+//                 V_K^T q of each query head, times scale * log2 e (scores in base 2).
+//   attend_tiles  per (layer, KV head, token range): 16-token tiles on MFMA.  Scores
+//                 S[t][h] = [K_t | U_K[t]] . [q~_h | w_h] with K rows as the A operand
+//                 and the prepared queries, split into bf16 high and low parts (|error|
+//                 <= 2^-17 relative), as B: 16x16x32 bf16 MFMA, fp32 accumulation.
+//                 Online softmax per query head.  Then O^T += V^T P^T and the U_V sums
+//                 on 16x16x16 bf16 MFMA, P split into high and low parts, V^T read
+//                 from a per-wave LDS copy of the tile.  Each (range, chunk) segment
+//                 writes one partial: max, sum, the 128 value sums and the m U_V sums.
+//   attend_merge  per (layer, query head): merges the partials, adding V_V times each
+//                 partial's U_V sums with that partial's chunk factor.
 #include <hip/hip_runtime.h>
 
 #include "kamera_internal.h"
@@ -33,18 +34,21 @@
 namespace kamera {
 namespace {
 
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowGroups = 2 * kWaves;  // 32 lanes per token row
 constexpr int kD = kAttendDim;
+constexpr int kRowPad = 8;                 // bf16 padding of an LDS tile row
+constexpr int kVRow = kD + kRowPad;        // LDS row of a V tile
+constexpr int kURow = 128 + kRowPad;       // LDS row of a U_V tile (rank <= 128)
 
 __device__ __forceinline__ float bf16_at(const uint16_t* p) {
   return __uint_as_float((uint32_t)*p << 16);
 }
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Last chunk j with offsets[j] <= t: the nonempty chunk holding t when the offsets
 // cover t (offsets[0] = 0 <= t).
@@ -58,36 +62,105 @@ __device__ __forceinline__ int chunk_at(const int64_t* off, int n, int64_t t) {
   return lo;
 }
 
-// Sum over the 32 lanes of each half-wave; every lane of the wavefront calls it.
-__device__ __forceinline__ float sum32(float v) {
-  v += __uint_as_float(lane_xor<1>(__float_as_uint(v)));
-  v += __uint_as_float(lane_xor<2>(__float_as_uint(v)));
-  v += __uint_as_float(lane_xor<4>(__float_as_uint(v)));
-  v += __uint_as_float(lane_xor<8>(__float_as_uint(v)));
-  v += __uint_as_float(lane_xor<16>(__float_as_uint(v)));
-  return v;
-}
-
 // 2^(x - m) for a running maximum m that may still be -inf (then nothing counts yet).
 __device__ __forceinline__ float weight(float x, float m) {
   return m == -INFINITY ? 0.f : exp2f(x - m);
 }
 
-// G: query heads per KV head the kernel is built for (the group may be smaller);
-// MU: U entries per lane (rank <= 32 MU); NB: token rows per row group per step;
-// PAGED: block-table addressing.
-template <int G, int MU, int NB, bool PAGED>
-__global__ __launch_bounds__(kThreads) void attend_split(AttendArgs a) {
+__device__ __forceinline__ float max_xor(float v, int x) {
+  return fmaxf(v, __shfl_xor(v, x));
+}
+
+// ------------------------------------------------------------------ prepared queries
+
+// One workgroup per (layer, chunk, KV head): V_K rows of the head staged in LDS, then
+// each query head's rotated query and V_K^T q.
+__global__ __launch_bounds__(kThreads) void attend_prep(AttendArgs a) {
+  __shared__ __align__(16) uint16_t svk[kD * 128];  // V_K[g * 128 + d][k], rank <= 128
+  __shared__ float sqh[kAttendMaxGroup][kD];
+  const int tid = threadIdx.x;
+  const int H = a.heads, n = a.num_chunks, m = a.rank, gq = a.group, Hq = a.num_q_heads;
+  const uint32_t bid = blockIdx.x;
+  const int g = (int)(bid % (uint32_t)H);
+  const uint32_t lj = bid / (uint32_t)H;
+  const int j = (int)(lj % (uint32_t)n);
+  const int l = (int)(lj / (uint32_t)n);
+  const int r = a.rope_dim, half = r >> 1;
+  const int64_t F = (int64_t)H * kD;
+  for (int idx = tid; idx < gq * kD; idx += kThreads) {
+    const int h = idx / kD, d = idx - h * kD;
+    sqh[h][d] = a.q[((int64_t)l * Hq + g * gq + h) * kD + d];
+  }
+  if (m > 0) {
+    // rows g*128 .. g*128+127 of V_K are one contiguous block of 128 * m elements
+    const uint16_t* vk = (const uint16_t*)a.V[0] + (((int64_t)l * n + j) * F + (int64_t)g * kD) * m;
+    for (int idx = tid; idx < kD * m / 8; idx += kThreads)
+      *(u32x4_t*)(svk + 8 * idx) = *(const u32x4_t*)(vk + 8 * idx);
+  }
+  __syncthreads();
+  const int W = kD + m;
+  float* out = a.qw + (((int64_t)l * n + j) * Hq + g * gq) * W;
+  for (int idx = tid; idx < gq * kD; idx += kThreads) {
+    const int h = idx / kD, d = idx - h * kD;
+    float v = sqh[h][d];
+    if (d < r) {
+      const bool il = a.pairing == 1;
+      const int i = il ? d >> 1 : (d < half ? d : d - half);
+      const bool first = il ? (d & 1) == 0 : d < half;
+      const int dp = il ? (d ^ 1) : (first ? d + half : d - half);
+      int sec = 0;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) sec += (k + 1 < a.num_sections && i >= a.sec_end[k]) ? 1 : 0;
+      const int64_t dl = a.delta[(int64_t)j * a.num_sections + sec];
+      if (dl != 0) {  // R(-delta): the phase of -delta in the rotation's own form
+        const float2 cs = phase_of(a.omega[i], -dl);
+        const float b = sqh[h][dp];
+        v = first ? fmaf(v, cs.x, -(b * cs.y)) : fmaf(v, cs.x, b * cs.y);
+      }
+    }
+    out[(int64_t)h * W + d] = v * a.scale_log2;
+  }
+  for (int idx = tid; idx < gq * m; idx += kThreads) {
+    const int h = idx / m, k = idx - h * m;
+    float w = 0.f;
+    for (int d = 0; d < kD; ++d) w = fmaf(sqh[h][d], bf16_at(svk + d * m + k), w);
+    out[(int64_t)h * W + kD + k] = w * a.scale_log2;
+  }
+}
+
+// ------------------------------------------------------------------ token tiles
+
+// Splits fp32 values into bf16 high and low parts (x - hi - lo <= 2^-17 |x|).
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = (__bf16)x[e];
+    lo[e] = (__bf16)(x[e] - (float)hi[e]);
+  }
+}
+
+// MK: 32-wide rank steps (ceil(m / 32)); PAGED: block-table addressing.
+template <int MK, bool PAGED>
+__global__ __launch_bounds__(kThreads) void attend_tiles(AttendArgs a) {
+  constexpr int MKX = MK > 0 ? MK : 1;
+  constexpr int MU = 2 * MK;               // 16-wide rank blocks of the U_V sums
   constexpr int MUX = MU > 0 ? MU : 1;
-  __shared__ float sq[G][kD];               // rotated query * scale * log2 e
-  __shared__ float sw[G][kD];               // V_K^T q * scale * log2 e (rank <= 128)
-  __shared__ float sred[kWaves][G][2 + 2 * kD];  // per wave: max, sum, 128 sums, U_V sums
-  __shared__ float sub[G][kD];              // merged U_V sums
+  // Per-wave V and U_V tiles; reused for the merge at the end of a segment.
+  constexpr int kTileBytes = 16 * (kVRow + kURow) * 2;
+  constexpr int kMergeFloats = kWaves * kAttendMaxGroup * (2 + kD + 128);
+  constexpr int kLds =
+      kWaves * kTileBytes > kMergeFloats * 4 ? kWaves * kTileBytes : kMergeFloats * 4;
+  __shared__ __align__(16) unsigned char lds[kLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int c = lane & 31;
-  const int rg = wave * 2 + (lane >> 5);
+  const int c16 = lane & 15;
+  const int grp = lane >> 4;
+  uint16_t* sv = (uint16_t*)(lds + wave * kTileBytes);
+  uint16_t* su = sv + 16 * kVRow;
+  typedef float MergeRow[kAttendMaxGroup][2 + kD + 128];
+  MergeRow* sred = (MergeRow*)lds;
+
   const uint32_t S = (uint32_t)a.splits;
   const uint32_t bid = blockIdx.x;
   const int s = (int)(bid % S);
@@ -99,208 +172,198 @@ __global__ __launch_bounds__(kThreads) void attend_split(AttendArgs a) {
   const int64_t t_hi = min(T, t_lo + (int64_t)a.split_tokens);
   if (t_lo >= t_hi) return;
   const int m = a.rank, gq = a.group, Hq = a.num_q_heads, n = a.num_chunks;
-  const int r = a.rope_dim, half = r >> 1;
-  const int64_t F = (int64_t)a.heads * kD;
+  const int W = kD + m;
+  const bool hv = c16 < gq;                // this lane's MFMA column is a real query head
   const uint16_t* kb = (const uint16_t*)a.data[0] + (int64_t)l * a.layer_stride[0] +
-                       (int64_t)g * a.head_stride[0] + 4 * c;
+                       (int64_t)g * a.head_stride[0] + 8 * grp;
   const uint16_t* vb = (const uint16_t*)a.data[1] + (int64_t)l * a.layer_stride[1] +
-                       (int64_t)g * a.head_stride[1] + 4 * c;
-  const uint16_t* ukb = MU > 0 ? (const uint16_t*)a.U[0] + (int64_t)l * T * m : nullptr;
-  const uint16_t* uvb = MU > 0 ? (const uint16_t*)a.U[1] + (int64_t)l * T * m : nullptr;
+                       (int64_t)g * a.head_stride[1] + 8 * grp;
+  const uint16_t* ukb = MK > 0 ? (const uint16_t*)a.U[0] + (int64_t)l * T * m + 8 * grp : nullptr;
+  const uint16_t* uvb = MK > 0 ? (const uint16_t*)a.U[1] + (int64_t)l * T * m + 8 * grp : nullptr;
   const uint32_t ss0 = (uint32_t)a.slot_stride[0], ss1 = (uint32_t)a.slot_stride[1];
   const uint32_t ps0 = (uint32_t)a.page_stride[0], ps1 = (uint32_t)a.page_stride[1];
   const uint32_t P = (uint32_t)a.page_size;
   const int psh = (P != 0u && (P & (P - 1u)) == 0u) ? __builtin_ctz(P) : -1;
+
+  // Row offsets of token t in the K and V channels inside the layer (32-bit: the host
+  // checks the extents); false when the token has no slot.
+  auto slot = [&](int64_t t, uint32_t& off_k, uint32_t& off_v) -> bool {
+    const uint32_t tt = (uint32_t)t;
+    if constexpr (PAGED) {
+      const uint32_t pi = psh >= 0 ? tt >> psh : tt / P, si = tt - pi * P;
+      const int32_t pg = a.block_table[pi];
+      if (pg < 0 || pg >= a.num_pages) return false;
+      off_k = (uint32_t)pg * ps0 + si * ss0;
+      off_v = (uint32_t)pg * ps1 + si * ss1;
+    } else {
+      off_k = tt * ss0;
+      off_v = tt * ss1;
+    }
+    return true;
+  };
 
   for (int64_t t0 = t_lo; t0 < t_hi;) {
     const int j = chunk_at(a.offsets, n, t0);
     const int64_t s1 = min(t_hi, a.offsets[j + 1]);
     if (s1 <= t0) break;  // offsets that do not cover the range: nothing more here
 
-    // ---- segment set-up: rotated query and V_K^T q of each query head
-    for (int idx = tid; idx < G * kD; idx += kThreads) {
-      const int h = idx / kD, d = idx - h * kD;
-      float v = 0.f;
-      if (h < gq) {
-        const float* qh = a.q + ((int64_t)l * Hq + g * gq + h) * kD;
-        v = qh[d];
-        if (d < r) {
-          const bool il = a.pairing == 1;
-          const int i = il ? d >> 1 : (d < half ? d : d - half);
-          const bool first = il ? (d & 1) == 0 : d < half;
-          const int dp = il ? (d ^ 1) : (first ? d + half : d - half);
-          int sec = 0;
+    // B operands: this lane's query head (column c16), features 32 ks + 8 grp ...
+    bf16x8_t qh[4], ql[4], wh[MKX], wl[MKX];
+    {
+      const float* qp = a.qw + (((int64_t)l * n + j) * Hq + g * gq + (hv ? c16 : 0)) * W;
 #pragma unroll
-          for (int k = 0; k < 3; ++k) sec += (k + 1 < a.num_sections && i >= a.sec_end[k]) ? 1 : 0;
-          const int64_t dl = a.delta[(int64_t)j * a.num_sections + sec];
-          if (dl != 0) {  // R(-delta): the phase of -delta in the rotation's own form
-            const float2 cs = phase_of(a.omega[i], -dl);
-            const float b = qh[dp];
-            v = first ? fmaf(v, cs.x, -(b * cs.y)) : fmaf(v, cs.x, b * cs.y);
-          }
-        }
-      }
-      sq[h][d] = v * a.scale_log2;
-    }
-    if constexpr (MU > 0) {
-      for (int idx = tid; idx < G * m; idx += kThreads) {
-        const int h = idx / m, k = idx - h * m;
-        float w = 0.f;
-        if (h < gq) {
-          const float* qh = a.q + ((int64_t)l * Hq + g * gq + h) * kD;
-          const uint16_t* vk =
-              (const uint16_t*)a.V[0] + (((int64_t)l * n + j) * F + (int64_t)g * kD) * m + k;
-          for (int d = 0; d < kD; ++d) w = fmaf(qh[d], bf16_at(vk + (int64_t)d * m), w);
-        }
-        sw[h][k] = w * a.scale_log2;
-      }
-    }
-    __syncthreads();
-    float qt[G][4], wk[G][MUX];
+      for (int ks = 0; ks < 4; ++ks) {
+        float x[8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qt[h][e] = sq[h][4 * c + e];
-#pragma unroll
-      for (int k = 0; k < MUX; ++k) wk[h][k] = (MU > 0 && c * MU + k < m) ? sw[h][c * MU + k] : 0.f;
-    }
-
-    // ---- stream the segment's tokens: row group rg takes tokens t0 + rg + 8 b + ...
-    float mr[G], lr[G], acc[G][4], ub[G][MUX];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      mr[h] = -INFINITY;
-      lr[h] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
-#pragma unroll
-      for (int k = 0; k < MUX; ++k) ub[h][k] = 0.f;
-    }
-    for (int64_t base = t0; base < s1; base += kRowGroups * NB) {
-      u32x2_t kx[NB], vx[NB];
-      float uk[NB][MUX], uv[NB][MUX];
-      bool ok[NB];
-      // Row offsets inside a layer fit in 32 bits (checked on the host); tokens < 2^30.
-      const uint32_t t_first = (uint32_t)(base + rg);
-      uint32_t ck = t_first * ss0, cv = t_first * ss1;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const uint32_t t = t_first + kRowGroups * b;
-        ok[b] = (int64_t)t < s1;
-        uint32_t sk = ck, sv = cv;
-        ck += kRowGroups * ss0;
-        cv += kRowGroups * ss1;
-        if constexpr (PAGED) {
-          sk = sv = 0u;
-          if (ok[b]) {
-            const uint32_t pi = psh >= 0 ? t >> psh : t / P, si = t - pi * P;
-            const int32_t pg = a.block_table[pi];
-            ok[b] = pg >= 0 && pg < a.num_pages;
-            sk = (uint32_t)pg * ps0 + si * ss0;
-            sv = (uint32_t)pg * ps1 + si * ss1;
-          }
-        }
-        kx[b] = u32x2_t{0u, 0u};
-        vx[b] = u32x2_t{0u, 0u};
-        if (ok[b]) {
-          kx[b] = __builtin_nontemporal_load((const u32x2_t*)(kb + sk));
-          vx[b] = __builtin_nontemporal_load((const u32x2_t*)(vb + sv));
-        }
-#pragma unroll
-        for (int k = 0; k < MUX; ++k) {
-          const bool uon = MU > 0 && ok[b] && c * MU + k < m;
-          uk[b][k] = uon ? bf16_at(ukb + (int64_t)t * m + c * MU + k) : 0.f;
-          uv[b][k] = uon ? bf16_at(uvb + (int64_t)t * m + c * MU + k) : 0.f;
-        }
-      }
-      float sc[NB][G];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float k0 = bf16_lo(kx[b].x), k1 = bf16_hi(kx[b].x);
-        const float k2 = bf16_lo(kx[b].y), k3 = bf16_hi(kx[b].y);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float p = qt[h][0] * k0;
-          p = fmaf(qt[h][1], k1, p);
-          p = fmaf(qt[h][2], k2, p);
-          p = fmaf(qt[h][3], k3, p);
-#pragma unroll
-          for (int k = 0; k < MUX; ++k) p = fmaf(wk[h][k], uk[b][k], p);
-          p = sum32(p);
-          sc[b][h] = ok[b] ? p : -INFINITY;
-        }
+        for (int e = 0; e < 8; ++e) x[e] = hv ? qp[32 * ks + 8 * grp + e] : 0.f;
+        split8(x, qh[ks], ql[ks]);
       }
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float mb = sc[0][h];
+      for (int ku = 0; ku < MKX; ++ku) {
+        float x[8];
 #pragma unroll
-        for (int b = 1; b < NB; ++b) mb = fmaxf(mb, sc[b][h]);
-        const float mn = fmaxf(mr[h], mb);
-        const float corr = weight(mr[h], mn);
-        lr[h] *= corr;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[h][e] *= corr;
-#pragma unroll
-        for (int k = 0; k < MUX; ++k) ub[h][k] *= corr;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float p = weight(sc[b][h], mn);
-          lr[h] += p;
-          acc[h][0] = fmaf(p, bf16_lo(vx[b].x), acc[h][0]);
-          acc[h][1] = fmaf(p, bf16_hi(vx[b].x), acc[h][1]);
-          acc[h][2] = fmaf(p, bf16_lo(vx[b].y), acc[h][2]);
-          acc[h][3] = fmaf(p, bf16_hi(vx[b].y), acc[h][3]);
-#pragma unroll
-          for (int k = 0; k < MUX; ++k) ub[h][k] = fmaf(p, uv[b][k], ub[h][k]);
+        for (int e = 0; e < 8; ++e) {
+          const int k = 32 * ku + 8 * grp + e;
+          x[e] = (MK > 0 && hv && k < m) ? qp[kD + k] : 0.f;
         }
-        mr[h] = mn;
+        split8(x, wh[ku], wl[ku]);
       }
     }
 
-    // ---- merge: the two row groups of a wave, then the four waves
+    float mrun = -INFINITY, lrun = 0.f;
+    f32x4_t acc[8], uacc[MUX];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(mr[h], 32);
-      const float M = fmaxf(mr[h], mo);
-      const float fs = weight(mr[h], M), fo = weight(mo, M);
-      lr[h] = lr[h] * fs + __shfl_xor(lr[h], 32) * fo;
+    for (int f = 0; f < 8; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[h][e] = acc[h][e] * fs + __shfl_xor(acc[h][e], 32) * fo;
+    for (int u = 0; u < MUX; ++u) uacc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int ntiles = (int)((s1 - t0 + 15) >> 4);
+    for (int ti = wave; ti < ntiles; ti += kWaves) {
+      const int64_t tb = t0 + 16 * (int64_t)ti;
+      // A operand rows: token tb + c16, 8 consecutive features per 32-wide step.
+      const int64_t tr = tb + c16;
+      uint32_t off_k = 0, off_v = 0;
+      const bool row_on = tr < s1 && slot(tr, off_k, off_v);
+      u32x4_t kx[4], vx[4], ukx[MKX], uvx[MKX];
 #pragma unroll
-      for (int k = 0; k < MUX; ++k) ub[h][k] = ub[h][k] * fs + __shfl_xor(ub[h][k], 32) * fo;
-      mr[h] = M;
-    }
-    if (lane < 32) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        if (c == 0) {
-          sred[wave][h][0] = mr[h];
-          sred[wave][h][1] = lr[h];
+      for (int ks = 0; ks < 4; ++ks) {
+        kx[ks] = u32x4_t{0u, 0u, 0u, 0u};
+        vx[ks] = u32x4_t{0u, 0u, 0u, 0u};
+        if (row_on) {
+          kx[ks] = __builtin_nontemporal_load((const u32x4_t*)(kb + off_k + 32 * ks));
+          vx[ks] = __builtin_nontemporal_load((const u32x4_t*)(vb + off_v + 32 * ks));
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sred[wave][h][2 + 4 * c + e] = acc[h][e];
-#pragma unroll
-        for (int k = 0; k < MUX; ++k)
-          if (MU > 0 && c * MU + k < m) sred[wave][h][2 + kD + c * MU + k] = ub[h][k];
       }
+#pragma unroll
+      for (int ku = 0; ku < MKX; ++ku) {
+        ukx[ku] = u32x4_t{0u, 0u, 0u, 0u};
+        uvx[ku] = u32x4_t{0u, 0u, 0u, 0u};
+        if (MK > 0 && tr < s1 && 32 * ku + 8 * grp < m) {
+          ukx[ku] = *(const u32x4_t*)(ukb + tr * m + 32 * ku);
+          uvx[ku] = *(const u32x4_t*)(uvb + tr * m + 32 * ku);
+        }
+      }
+      // Scores of tokens tb + 4 grp + i (i < 4) for query head c16.
+      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, kx[ks]);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qh[ks], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, ql[ks], sc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ku = 0; ku < MK; ++ku) {
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ukx[ku]);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wh[ku], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wl[ku], sc, 0, 0, 0);
+      }
+      // The V and U_V rows go to this wave's LDS tile (row c16) for the transposed reads.
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) *(u32x4_t*)(sv + c16 * kVRow + 32 * ks + 8 * grp) = vx[ks];
+#pragma unroll
+      for (int ku = 0; ku < MK; ++ku)
+        if (32 * ku + 8 * grp < m) *(u32x4_t*)(su + c16 * kURow + 32 * ku + 8 * grp) = uvx[ku];
+      // Mask tokens past the segment or without a slot.
+      float s4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = tb + 4 * grp + i;
+        uint32_t o0, o1;
+        const bool on = t < s1 && (!PAGED || slot(t, o0, o1));
+        s4[i] = on ? sc[i] : -INFINITY;
+      }
+      float mt = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+      mt = max_xor(mt, 16);
+      mt = max_xor(mt, 32);
+      const float mn = fmaxf(mrun, mt);
+      const float corr = weight(mrun, mn);
+      if (corr != 1.f) {
+        lrun *= corr;
+#pragma unroll
+        for (int f = 0; f < 8; ++f) acc[f] *= corr;
+#pragma unroll
+        for (int u = 0; u < MUX; ++u) uacc[u] *= corr;
+      }
+      mrun = mn;
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = weight(s4[i], mn);
+        lrun += p[i];
+      }
+      bf16x4_t ph, pl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ph[i] = (__bf16)p[i];
+        pl[i] = (__bf16)(p[i] - (float)ph[i]);
+      }
+      // O^T[f][h] += V^T[f][t] P^T[t][h]: A = V^T rows f = 16 fb + c16, tokens 4 grp + i.
+#pragma unroll
+      for (int fb = 0; fb < 8; ++fb) {
+        bf16x4_t A;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          A[i] = __builtin_bit_cast(__bf16, sv[(4 * grp + i) * kVRow + 16 * fb + c16]);
+        acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, acc[fb], 0, 0, 0);
+        acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, acc[fb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int ub = 0; ub < MU; ++ub) {
+        if (16 * ub >= m) break;
+        bf16x4_t A;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          A[i] = __builtin_bit_cast(__bf16, su[(4 * grp + i) * kURow + 16 * ub + c16]);
+        uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, uacc[ub], 0, 0, 0);
+        uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, uacc[ub], 0, 0, 0);
+      }
+    }
+    // The four lane groups of a column hold disjoint tokens' sums.
+    lrun += __shfl_xor(lrun, 16);
+    lrun += __shfl_xor(lrun, 32);
+
+    // ---- merge the four waves; lane (c16, grp) holds features 16 fb + 4 grp + i
+    __syncthreads();  // the tiles' LDS becomes the merge buffer
+    if (hv) {
+      if (grp == 0) {
+        sred[wave][c16][0] = mrun;
+        sred[wave][c16][1] = lrun;
+      }
+#pragma unroll
+      for (int fb = 0; fb < 8; ++fb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sred[wave][c16][2 + 16 * fb + 4 * grp + i] = acc[fb][i];
+#pragma unroll
+      for (int ub = 0; ub < MU; ++ub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = 16 * ub + 4 * grp + i;
+          if (k < m) sred[wave][c16][2 + kD + k] = uacc[ub][i];
+        }
     }
     __syncthreads();
-    if constexpr (MU > 0) {
-      for (int idx = tid; idx < G * m; idx += kThreads) {
-        const int h = idx / m, k = idx - h * m;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sred[w][h][0]);
-        float u = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) u = fmaf(weight(sred[w][h][0], M), sred[w][h][2 + kD + k], u);
-        sub[h][k] = u;
-      }
-      __syncthreads();
-    }
-    for (int idx = tid; idx < G * kD; idx += kThreads) {
-      const int h = idx / kD, d = idx - h * kD;
-      if (h >= gq) continue;
+    for (int idx = tid; idx < gq * W; idx += kThreads) {
+      const int h = idx / W, e = idx - h * W;
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sred[w][h][0]);
@@ -309,33 +372,34 @@ __global__ __launch_bounds__(kThreads) void attend_split(AttendArgs a) {
       for (int w = 0; w < kWaves; ++w) {
         const float f = weight(sred[w][h][0], M);
         L = fmaf(f, sred[w][h][1], L);
-        A = fmaf(f, sred[w][h][2 + d], A);
+        A = fmaf(f, sred[w][h][2 + e], A);
       }
-      if constexpr (MU > 0) {
-        const uint16_t* vv =
-            (const uint16_t*)a.V[1] + (((int64_t)l * n + j) * F + (int64_t)g * kD + d) * m;
-        for (int k = 0; k < m; ++k) A = fmaf(bf16_at(vv + k), sub[h][k], A);
+      float* sl = a.ws + (((int64_t)l * Hq + g * gq + h) * a.slots + (s + j)) * a.slot_floats;
+      if (e == 0) {
+        sl[0] = M;
+        sl[1] = L;
       }
-      float* slot = a.ws + (((int64_t)l * Hq + g * gq + h) * a.slots + (s + j)) * kAttendPartial;
-      if (d == 0) {
-        slot[0] = M;
-        slot[1] = L;
-      }
-      slot[2 + d] = A;
+      sl[2 + e] = A;
     }
-    __syncthreads();  // the next segment restages the shared arrays
+    __syncthreads();  // the next segment reuses the LDS for tiles
     t0 = s1;
   }
 }
 
-// One workgroup per (layer, query head), thread d: merges the partial slots the split
-// kernel wrote, walking the same (split, chunk) segments.
-__global__ __launch_bounds__(kD) void attend_combine(AttendArgs a) {
+// ------------------------------------------------------------------ merge
+
+// One workgroup per (layer, query head), thread d: merges the partial slots the tile
+// kernel wrote, walking the same (range, chunk) segments, and adds V_V times each
+// partial's U_V sums (with that partial's chunk factor).
+__global__ __launch_bounds__(kD) void attend_merge(AttendArgs a) {
   const int Hq = a.num_q_heads;
   const int hq = (int)(blockIdx.x % (uint32_t)Hq);
   const int l = (int)(blockIdx.x / (uint32_t)Hq);
+  const int g = hq / a.group;
   const int d = threadIdx.x;
-  const float* base = a.ws + ((int64_t)l * Hq + hq) * a.slots * kAttendPartial;
+  const int m = a.rank, n = a.num_chunks;
+  const int64_t F = (int64_t)a.heads * kD;
+  const float* base = a.ws + ((int64_t)l * Hq + hq) * a.slots * a.slot_floats;
   const int64_t T = a.total_tokens;
   float M = -INFINITY;
   for (int pass = 0; pass < 2; ++pass) {
@@ -344,18 +408,33 @@ __global__ __launch_bounds__(kD) void attend_combine(AttendArgs a) {
       const int64_t t_lo = (int64_t)s * a.split_tokens;
       const int64_t t_hi = min(T, t_lo + (int64_t)a.split_tokens);
       for (int64_t t0 = t_lo; t0 < t_hi;) {
-        const int j = chunk_at(a.offsets, a.num_chunks, t0);
+        const int j = chunk_at(a.offsets, n, t0);
         const int64_t s1 = min(t_hi, a.offsets[j + 1]);
         if (s1 <= t0) break;
-        const float* slot = base + (int64_t)(s + j) * kAttendPartial;
-        const float ls = slot[1];
+        const float* sl = base + (int64_t)(s + j) * a.slot_floats;
+        const float ls = sl[1];
         if (ls > 0.f) {
           if (pass == 0) {
-            M = fmaxf(M, slot[0]);
+            M = fmaxf(M, sl[0]);
           } else {
-            const float f = exp2f(slot[0] - M);
+            float v = sl[2 + d];
+            if (m > 0) {  // row d of V_V: m contiguous bf16, read 8 at a time
+              const u32x4_t* vv = (const u32x4_t*)((const uint16_t*)a.V[1] +
+                                                   (((int64_t)l * n + j) * F + (int64_t)g * kD + d) * m);
+              const float* us = sl + 2 + kD;
+#pragma unroll 4
+              for (int k8 = 0; k8 < m / 8; ++k8) {
+                const u32x4_t w = vv[k8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  v = fmaf(__uint_as_float(w[e] << 16), us[8 * k8 + 2 * e], v);
+                  v = fmaf(__uint_as_float(w[e] & 0xffff0000u), us[8 * k8 + 2 * e + 1], v);
+                }
+              }
+            }
+            const float f = exp2f(sl[0] - M);
             den = fmaf(f, ls, den);
-            num = fmaf(f, slot[2 + d], num);
+            num = fmaf(f, v, num);
           }
         }
         t0 = s1;
@@ -373,35 +452,28 @@ __global__ __launch_bounds__(kD) void attend_combine(AttendArgs a) {
 }  // namespace
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
-  const dim3 grid1((unsigned)((int64_t)a.num_layers * a.heads * a.splits));
-  const int mu = (a.rank + 31) / 32;
-  const int G = a.group <= 2 ? 2 : a.group <= 4 ? 4 : 8;
-#define KAMERA_ATT(GG, MM, PG)                                                                 \
-  hipLaunchKernelGGL((attend_split<GG, MM, (GG >= 8 ? 2 : 4), PG>), grid1, dim3(kThreads), 0, s, a)
-#define KAMERA_ATT_MU(GG, PG)                          \
-  do {                                                 \
-    if (mu == 0) KAMERA_ATT(GG, 0, PG);                \
-    else if (mu == 1) KAMERA_ATT(GG, 1, PG);           \
-    else if (mu == 2) KAMERA_ATT(GG, 2, PG);           \
-    else KAMERA_ATT(GG, 4, PG);                        \
-  } while (0)
-#define KAMERA_ATT_G(PG)                               \
-  do {                                                 \
-    if (G == 2) KAMERA_ATT_MU(2, PG);                  \
-    else if (G == 4) KAMERA_ATT_MU(4, PG);             \
-    else KAMERA_ATT_MU(8, PG);                         \
-  } while (0)
   if (a.splits > 0) {  // no tokens: only the merge runs, writing 0 and -inf
-    if (a.page_size > 0) KAMERA_ATT_G(true);
-    else KAMERA_ATT_G(false);
-  }
-#undef KAMERA_ATT_G
-#undef KAMERA_ATT_MU
+    const dim3 grid0((unsigned)((int64_t)a.num_layers * a.num_chunks * a.heads));
+    hipLaunchKernelGGL(attend_prep, grid0, dim3(kThreads), 0, s, a);
+    const dim3 grid1((unsigned)((int64_t)a.num_layers * a.heads * a.splits));
+    const int mk = (a.rank + 31) / 32;
+#define KAMERA_ATT(MK)                                                                          \
+  do {                                                                                          \
+    if (a.page_size > 0)                                                                        \
+      hipLaunchKernelGGL((attend_tiles<MK, true>), grid1, dim3(kThreads), 0, s, a);             \
+    else                                                                                        \
+      hipLaunchKernelGGL((attend_tiles<MK, false>), grid1, dim3(kThreads), 0, s, a);            \
+  } while (0)
+    if (mk == 0) KAMERA_ATT(0);
+    else if (mk == 1) KAMERA_ATT(1);
+    else if (mk == 2) KAMERA_ATT(2);
+    else KAMERA_ATT(4);
 #undef KAMERA_ATT
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid2((unsigned)((int64_t)a.num_layers * a.num_q_heads));
-  hipLaunchKernelGGL(attend_combine, grid2, dim3(kD), 0, s, a);
+  hipLaunchKernelGGL(attend_merge, grid2, dim3(kD), 0, s, a);
   return hipGetLastError();
 }
 

@@ -75,8 +75,12 @@ struct FormArgs {
 };
 
 // Relocate-on-read decode attention (attend.hip): K = channel 0, V = channel 1, bf16,
-// dim 128; tokens are cut into `splits` ranges of `split_tokens`, and each range into
-// segments at chunk boundaries; segment (split s, chunk j) writes partial slot s + j.
+// dim 128, rank a multiple of 8 up to 128.  The workspace holds the prepared queries
+// (qw: [layers][chunks][num_q_heads][128 + rank]: the rotated query and V_K^T q, both
+// times scale * log2 e) and the partial slots (ws: [layers][num_q_heads][slots]
+// [slot_floats]: max, sum, 128 value sums, rank U_V sums).  Tokens are cut into
+// `splits` ranges of `split_tokens`, and each range into segments at chunk
+// boundaries; segment (split s, chunk j) writes slot s + j.
 struct AttendArgs {
   const void* data[2];
   int64_t layer_stride[2], slot_stride[2], head_stride[2], page_stride[2];
@@ -89,18 +93,20 @@ struct AttendArgs {
   const float* q;             // [layers][num_q_heads][128]
   float* out;                 // [layers][num_q_heads][128]
   float* lse;                 // [layers][num_q_heads] or nullptr
-  float* ws;                  // [layers][num_q_heads][slots][130]: max, sum, 128 partial sums
+  float* qw;                  // prepared queries (see above)
+  float* ws;                  // partial slots (see above)
   int64_t total_tokens;
   int32_t num_chunks, num_sections, sec_end[4], pairing, rope_dim;
   int32_t page_size, num_layers, heads, num_q_heads, group, rank;
-  int32_t splits, split_tokens, slots;
+  int32_t splits, split_tokens, slots, slot_floats;
   float scale_log2;           // softmax scale * log2(e): scores are kept in base 2
   double omega[64];           // theta^(-2i/rope_dim)
 };
 
 constexpr int kAttendDim = 128;
 constexpr int kAttendMaxGroup = 8;
-constexpr int kAttendPartial = kAttendDim + 2;  // floats per partial slot
+// Floats of one partial slot at rank m: max, sum, 128 sums, m sums, padded to 4.
+constexpr int attend_slot_floats(int m) { return (kAttendDim + 2 + m + 3) & ~3; }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 

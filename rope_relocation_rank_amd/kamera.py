@@ -122,7 +122,8 @@ def lib():
                                        C.POINTER(C.c_void_p), C.c_void_p]
         L.kamera_attend_workspace.restype = C.c_int
         L.kamera_attend_workspace.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
-                                              C.POINTER(kamera_attend_desc), C.POINTER(C.c_int64)]
+                                              C.POINTER(kamera_patch), C.POINTER(kamera_attend_desc),
+                                              C.POINTER(C.c_int64)]
         L.kamera_attend.restype = C.c_int
         L.kamera_attend.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
                                     C.POINTER(kamera_patch), C.POINTER(kamera_attend_desc),
@@ -329,9 +330,10 @@ def attend_desc(q, out, *, scale: float, lse=None) -> kamera_attend_desc:
     return d
 
 
-def kamera_attend_workspace(kv, chunks, attend):
+def kamera_attend_workspace(kv, chunks, patch, attend):
     n = C.c_int64(0)
-    st = lib().kamera_attend_workspace(_ref(kv), _ref(chunks), _ref(attend), C.byref(n))
+    st = lib().kamera_attend_workspace(_ref(kv), _ref(chunks), _ref(patch), _ref(attend),
+                                       C.byref(n))
     return st, n.value
 
 

@@ -95,7 +95,7 @@ def attend_buffers(inp, q, scale: float, flags: int = 0):
     out = torch.empty((L, Hq, D), dtype=torch.float32, device=q.device)
     lse = torch.empty((L, Hq), dtype=torch.float32, device=q.device)
     desc = K.attend_desc(q, out, scale=scale, lse=lse)
-    st, nbytes = K.kamera_attend_workspace(kv, ch, desc)
+    st, nbytes = K.kamera_attend_workspace(kv, ch, patch, desc)
     K.check(st)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device) if nbytes else None
     return (kv, ch, patch, desc), out, lse, ws

@@ -533,7 +533,7 @@ def attend(Hq=28, L=28, T=4096, H=4, m=32, **kw):
 
 
 def attend_status(kv, ch, p, d):
-    st, _ = K.kamera_attend_workspace(kv, ch, d)
+    st, _ = K.kamera_attend_workspace(kv, ch, p, d)
     if st == K.KAMERA_OK:
         # the launch call rejects before any HIP call too, through its workspace check
         st2 = K.lib().kamera_attend(C.byref(kv), C.byref(ch), None if p is None else C.byref(p),
@@ -544,10 +544,11 @@ def attend_status(kv, ch, p, d):
 
 def test_attend_workspace_and_checks():
     kv, ch, p, d = attend()
-    st, nbytes = K.kamera_attend_workspace(kv, ch, d)
+    st, nbytes = K.kamera_attend_workspace(kv, ch, p, d)
     assert st == K.KAMERA_OK and nbytes > 0
-    # splits fill the chip: L * heads * splits workgroups, slots = splits + chunks - 1
-    assert nbytes % (28 * 28 * 130 * 4) == 0
+    # prepared queries [L][chunks][Hq][128 + m], then partial slots [L][Hq][slots][164]
+    # (max, sum, 128 + m sums, padded to 4); 32 splits of 128 tokens fill the chip
+    assert nbytes == 28 * 1 * 28 * (128 + 32) * 4 + 28 * 28 * 32 * 164 * 4
     st, st2 = attend_status(kv, ch, p, d)
     assert st2 == K.KAMERA_E_NULL  # no workspace given
     for mutate, status in [
@@ -563,22 +564,22 @@ def test_attend_workspace_and_checks():
     ]:
         kv, ch, p, d = attend()
         mutate(kv, ch, p, d)
-        st, _ = K.kamera_attend_workspace(kv, ch, d)
+        st, _ = K.kamera_attend_workspace(kv, ch, p, d)
         assert st == status, (st, K.kamera_last_error())
     kv, ch, p, d = attend()
     kv.ch[0].dim = kv.ch[1].dim = 64
     kv.ch[0].rope_dim = 64
-    st, _ = K.kamera_attend_workspace(kv, ch, d)
+    st, _ = K.kamera_attend_workspace(kv, ch, p, d)
     assert st == K.KAMERA_E_UNSUPPORTED
-    # rank above 128 is refused at launch (the workspace does not depend on the rank)
-    kv, ch, p, d = attend(m=136)
-    assert K.lib().kamera_attend(C.byref(kv), C.byref(ch), C.byref(p), C.byref(d), None, 0,
-                                 None) == K.KAMERA_E_UNSUPPORTED
+    # ranks above 128 or not a multiple of 8 are refused
+    for m in (136, 12):
+        kv, ch, p, d = attend(m=m)
+        assert K.kamera_attend_workspace(kv, ch, p, d)[0] == K.KAMERA_E_UNSUPPORTED
 
 
 def test_attend_aliasing():
     kv, ch, p, d = attend(T=64, L=2)
-    _, nbytes = K.kamera_attend_workspace(kv, ch, d)
+    _, nbytes = K.kamera_attend_workspace(kv, ch, p, d)
     ws = FAKE + (12 << 40)
     def call():
         return K.lib().kamera_attend(C.byref(kv), C.byref(ch), C.byref(p), C.byref(d), ws,
