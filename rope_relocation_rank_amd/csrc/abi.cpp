@@ -700,6 +700,8 @@ kamera_status validate_attend(const kamera_kv_desc* kv, const kamera_chunks* ch,
     int64_t TS = ceil_div(T, S);
     TS = ceil_div(TS, 32) * 32;
     S = ceil_div(T, TS);
+    if (ceil_div(L * S, 8) * 8 * K.heads >= ((int64_t)1 << 31))
+      return fail(KAMERA_E_UNSUPPORTED, "too many layers x heads x splits for one launch");
     plan->splits = S;
     plan->split_tokens = TS;
     plan->slots = S + std::max<int64_t>(n, 1) - 1;

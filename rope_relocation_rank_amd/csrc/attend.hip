@@ -126,6 +126,12 @@ __global__ __launch_bounds__(kThreads) void attend_prep(AttendArgs a) {
     for (int d = 0; d < kD; ++d) w = fmaf(sqh[h][d], bf16_at(svk + d * m + k), w);
     out[(int64_t)h * W + kD + k] = w * a.scale_log2;
   }
+  // The first chunk's workgroups mark every partial slot of their query heads empty;
+  // the tile kernel then fills the slots of the segments that exist.
+  if (j == 0) {
+    float* ws = a.ws + ((int64_t)l * Hq + g * gq) * a.slots * a.slot_floats;
+    for (int i = tid; i < gq * a.slots; i += kThreads) ws[(int64_t)i * a.slot_floats + 1] = 0.f;
+  }
 }
 
 // ------------------------------------------------------------------ token tiles
@@ -139,8 +145,18 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8_t& hi, bf16x8
   }
 }
 
-// MK: 32-wide rank steps (ceil(m / 32)); PAGED: block-table addressing.
-template <int MK, bool PAGED>
+// One 16-token tile's A-operand rows as loaded: lane (c16, grp) holds 8 consecutive
+// features of token tb + c16 per 32-wide step.
+template <int MKX>
+struct TileRows {
+  u32x4_t k[4], v[4], uk[MKX], uv[MKX];
+};
+
+// MK: 32-wide rank steps (ceil(m / 32)); PAGED: block-table addressing.  Each wave
+// streams the segment's tiles w, w + 4, ...; with PF it loads the next tile's rows
+// before it works on the current one (the second register tile lowers occupancy,
+// which pays at rank steps of one only).
+template <int MK, bool PAGED, bool PF>
 __global__ __launch_bounds__(kThreads) void attend_tiles(AttendArgs a) {
   constexpr int MKX = MK > 0 ? MK : 1;
   constexpr int MU = 2 * MK;               // 16-wide rank blocks of the U_V sums
@@ -237,32 +253,45 @@ __global__ __launch_bounds__(kThreads) void attend_tiles(AttendArgs a) {
 #pragma unroll
     for (int u = 0; u < MUX; ++u) uacc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int ntiles = (int)((s1 - t0 + 15) >> 4);
-    for (int ti = wave; ti < ntiles; ti += kWaves) {
-      const int64_t tb = t0 + 16 * (int64_t)ti;
-      // A operand rows: token tb + c16, 8 consecutive features per 32-wide step.
-      const int64_t tr = tb + c16;
+    // Loads the rows of tile ti (token tb + c16, 8 consecutive features per step).
+    auto load = [&](int ti, TileRows<MKX>& R) {
+      const int64_t tr = t0 + 16 * (int64_t)ti + c16;
       uint32_t off_k = 0, off_v = 0;
       const bool row_on = tr < s1 && slot(tr, off_k, off_v);
-      u32x4_t kx[4], vx[4], ukx[MKX], uvx[MKX];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        kx[ks] = u32x4_t{0u, 0u, 0u, 0u};
-        vx[ks] = u32x4_t{0u, 0u, 0u, 0u};
+        R.k[ks] = u32x4_t{0u, 0u, 0u, 0u};
+        R.v[ks] = u32x4_t{0u, 0u, 0u, 0u};
         if (row_on) {
-          kx[ks] = __builtin_nontemporal_load((const u32x4_t*)(kb + off_k + 32 * ks));
-          vx[ks] = __builtin_nontemporal_load((const u32x4_t*)(vb + off_v + 32 * ks));
+          R.k[ks] = __builtin_nontemporal_load((const u32x4_t*)(kb + off_k + 32 * ks));
+          R.v[ks] = __builtin_nontemporal_load((const u32x4_t*)(vb + off_v + 32 * ks));
         }
       }
 #pragma unroll
       for (int ku = 0; ku < MKX; ++ku) {
-        ukx[ku] = u32x4_t{0u, 0u, 0u, 0u};
-        uvx[ku] = u32x4_t{0u, 0u, 0u, 0u};
+        R.uk[ku] = u32x4_t{0u, 0u, 0u, 0u};
+        R.uv[ku] = u32x4_t{0u, 0u, 0u, 0u};
         if (MK > 0 && tr < s1 && 32 * ku + 8 * grp < m) {
-          ukx[ku] = *(const u32x4_t*)(ukb + tr * m + 32 * ku);
-          uvx[ku] = *(const u32x4_t*)(uvb + tr * m + 32 * ku);
+          R.uk[ku] = *(const u32x4_t*)(ukb + tr * m + 32 * ku);
+          R.uv[ku] = *(const u32x4_t*)(uvb + tr * m + 32 * ku);
         }
       }
+    };
+    const int ntiles = (int)((s1 - t0 + 15) >> 4);
+    TileRows<MKX> cur;
+    if (PF && wave < ntiles) load(wave, cur);
+    for (int ti = wave; ti < ntiles; ti += kWaves) {
+      const int64_t tb = t0 + 16 * (int64_t)ti;
+      TileRows<MKX> nxt;
+      if constexpr (PF) {
+        if (ti + kWaves < ntiles) load(ti + kWaves, nxt);
+      } else {
+        load(ti, cur);
+      }
+      const u32x4_t* kx = cur.k;
+      const u32x4_t* vx = cur.v;
+      const u32x4_t* ukx = cur.uk;
+      const u32x4_t* uvx = cur.uv;
       // Scores of tokens tb + 4 grp + i (i < 4) for query head c16.
       f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -337,6 +366,7 @@ __global__ __launch_bounds__(kThreads) void attend_tiles(AttendArgs a) {
         uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, uacc[ub], 0, 0, 0);
         uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, uacc[ub], 0, 0, 0);
       }
+      if constexpr (PF) cur = nxt;
     }
     // The four lane groups of a column hold disjoint tokens' sums.
     lrun += __shfl_xor(lrun, 16);
@@ -378,8 +408,9 @@ __global__ __launch_bounds__(kThreads) void attend_tiles(AttendArgs a) {
       if (e == 0) {
         sl[0] = M;
         sl[1] = L;
+        sl[2] = __int_as_float(j);
       }
-      sl[2 + e] = A;
+      sl[kAttendSlotHead + e] = A;
     }
     __syncthreads();  // the next segment reuses the LDS for tiles
     t0 = s1;
@@ -388,65 +419,93 @@ __global__ __launch_bounds__(kThreads) void attend_tiles(AttendArgs a) {
 
 // ------------------------------------------------------------------ merge
 
-// One workgroup per (layer, query head), thread d: merges the partial slots the tile
-// kernel wrote, walking the same (range, chunk) segments, and adds V_V times each
-// partial's U_V sums (with that partial's chunk factor).
+// One workgroup per (layer, query head), thread d.  Slots with a positive sum are the
+// segments' partials, in token order, so their chunks come in nondecreasing order:
+// the value sums are merged per thread, the U_V sums are merged per chunk and V_V of
+// that chunk is applied once when the chunk changes.  Slots are read 8 at a time so
+// their loads overlap.
 __global__ __launch_bounds__(kD) void attend_merge(AttendArgs a) {
+  __shared__ float smax[kD / 64];
+  __shared__ float su[128];
   const int Hq = a.num_q_heads;
   const int hq = (int)(blockIdx.x % (uint32_t)Hq);
   const int l = (int)(blockIdx.x / (uint32_t)Hq);
   const int g = hq / a.group;
   const int d = threadIdx.x;
-  const int m = a.rank, n = a.num_chunks;
+  const int m = a.rank, n = a.num_chunks, ns = a.slots, SF = a.slot_floats;
   const int64_t F = (int64_t)a.heads * kD;
-  const float* base = a.ws + ((int64_t)l * Hq + hq) * a.slots * a.slot_floats;
-  const int64_t T = a.total_tokens;
+  const float* base = a.ws + ((int64_t)l * Hq + hq) * ns * SF;
   float M = -INFINITY;
-  for (int pass = 0; pass < 2; ++pass) {
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const int64_t t_lo = (int64_t)s * a.split_tokens;
-      const int64_t t_hi = min(T, t_lo + (int64_t)a.split_tokens);
-      for (int64_t t0 = t_lo; t0 < t_hi;) {
-        const int j = chunk_at(a.offsets, n, t0);
-        const int64_t s1 = min(t_hi, a.offsets[j + 1]);
-        if (s1 <= t0) break;
-        const float* sl = base + (int64_t)(s + j) * a.slot_floats;
-        const float ls = sl[1];
-        if (ls > 0.f) {
-          if (pass == 0) {
-            M = fmaxf(M, sl[0]);
-          } else {
-            float v = sl[2 + d];
-            if (m > 0) {  // row d of V_V: m contiguous bf16, read 8 at a time
-              const u32x4_t* vv = (const u32x4_t*)((const uint16_t*)a.V[1] +
-                                                   (((int64_t)l * n + j) * F + (int64_t)g * kD + d) * m);
-              const float* us = sl + 2 + kD;
-#pragma unroll 4
-              for (int k8 = 0; k8 < m / 8; ++k8) {
-                const u32x4_t w = vv[k8];
+  for (int i = d; i < ns; i += kD) {
+    const float* sl = base + (int64_t)i * SF;
+    if (sl[1] > 0.f) M = fmaxf(M, sl[0]);
+  }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  v = fmaf(__uint_as_float(w[e] << 16), us[8 * k8 + 2 * e], v);
-                  v = fmaf(__uint_as_float(w[e] & 0xffff0000u), us[8 * k8 + 2 * e + 1], v);
-                }
-              }
-            }
-            const float f = exp2f(sl[0] - M);
-            den = fmaf(f, ls, den);
-            num = fmaf(f, v, num);
-          }
-        }
-        t0 = s1;
+  for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+  if ((d & 63) == 0) smax[d >> 6] = M;
+  __syncthreads();
+  M = smax[0];
+#pragma unroll
+  for (int w = 1; w < kD / 64; ++w) M = fmaxf(M, smax[w]);
+
+  float num = 0.f, den = 0.f, uk = 0.f;
+  int jcur = -1;
+  // Adds V_V[chunk jcur] times the chunk's merged U_V sums to this thread's value.
+  auto flush = [&]() {
+    __syncthreads();
+    if (d < m) su[d] = uk;
+    __syncthreads();
+    const u32x4_t* vv = (const u32x4_t*)((const uint16_t*)a.V[1] +
+                                         (((int64_t)l * n + jcur) * F + (int64_t)g * kD + d) * m);
+#pragma unroll 4
+    for (int k8 = 0; k8 < m / 8; ++k8) {
+      const u32x4_t w = vv[k8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        num = fmaf(__uint_as_float(w[e] << 16), su[8 * k8 + 2 * e], num);
+        num = fmaf(__uint_as_float(w[e] & 0xffff0000u), su[8 * k8 + 2 * e + 1], num);
       }
     }
-    if (pass == 1) {
-      const int64_t o = (int64_t)l * Hq + hq;
-      a.out[o * kD + d] = den > 0.f ? num / den : 0.f;
-      if (a.lse != nullptr && d == 0)
-        a.lse[o] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
+    uk = 0.f;
+  };
+  constexpr int kB = 8;
+  for (int i0 = 0; i0 < ns; i0 += kB) {
+    float ls[kB], ms[kB], av[kB], uv[kB];
+    int js[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      ls[u] = 0.f;
+      ms[u] = 0.f;
+      av[u] = 0.f;
+      uv[u] = 0.f;
+      js[u] = 0;
+      if (i0 + u < ns) {
+        const float* sl = base + (int64_t)(i0 + u) * SF;
+        ls[u] = sl[1];
+        ms[u] = sl[0];
+        js[u] = __float_as_int(sl[2]);
+        av[u] = sl[kAttendSlotHead + d];
+        if (d < m) uv[u] = sl[kAttendSlotHead + kD + d];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      if (!(ls[u] > 0.f)) continue;  // the same for every thread
+      if (m > 0 && js[u] != jcur) {
+        if (jcur >= 0) flush();
+        jcur = js[u];
+      }
+      const float f = exp2f(ms[u] - M);
+      den = fmaf(f, ls[u], den);
+      num = fmaf(f, av[u], num);
+      uk = fmaf(f, uv[u], uk);
     }
   }
+  if (m > 0 && jcur >= 0) flush();
+  const int64_t o = (int64_t)l * Hq + hq;
+  a.out[o * kD + d] = den > 0.f ? num / den : 0.f;
+  if (a.lse != nullptr && d == 0)
+    a.lse[o] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
 }
 
 }  // namespace
@@ -460,9 +519,9 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
 #define KAMERA_ATT(MK)                                                                          \
   do {                                                                                          \
     if (a.page_size > 0)                                                                        \
-      hipLaunchKernelGGL((attend_tiles<MK, true>), grid1, dim3(kThreads), 0, s, a);             \
+      hipLaunchKernelGGL((attend_tiles<MK, true, MK == 1>), grid1, dim3(kThreads), 0, s, a);             \
     else                                                                                        \
-      hipLaunchKernelGGL((attend_tiles<MK, false>), grid1, dim3(kThreads), 0, s, a);            \
+      hipLaunchKernelGGL((attend_tiles<MK, false, MK == 1>), grid1, dim3(kThreads), 0, s, a);            \
   } while (0)
     if (mk == 0) KAMERA_ATT(0);
     else if (mk == 1) KAMERA_ATT(1);

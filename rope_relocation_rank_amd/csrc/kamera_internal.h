@@ -78,9 +78,10 @@ struct FormArgs {
 // dim 128, rank a multiple of 8 up to 128.  The workspace holds the prepared queries
 // (qw: [layers][chunks][num_q_heads][128 + rank]: the rotated query and V_K^T q, both
 // times scale * log2 e) and the partial slots (ws: [layers][num_q_heads][slots]
-// [slot_floats]: max, sum, 128 value sums, rank U_V sums).  Tokens are cut into
-// `splits` ranges of `split_tokens`, and each range into segments at chunk
-// boundaries; segment (split s, chunk j) writes slot s + j.
+// [slot_floats]: max, sum, chunk index, 128 value sums, rank U_V sums).  Tokens are cut
+// into `splits` ranges of `split_tokens`, and each range into segments at chunk
+// boundaries; segment (split s, chunk j) writes slot s + j.  Slots no segment writes
+// keep the zero sum the prep kernel stores.
 struct AttendArgs {
   const void* data[2];
   int64_t layer_stride[2], slot_stride[2], head_stride[2], page_stride[2];
@@ -105,8 +106,9 @@ struct AttendArgs {
 
 constexpr int kAttendDim = 128;
 constexpr int kAttendMaxGroup = 8;
-// Floats of one partial slot at rank m: max, sum, 128 sums, m sums, padded to 4.
-constexpr int attend_slot_floats(int m) { return (kAttendDim + 2 + m + 3) & ~3; }
+// Floats of one partial slot at rank m: max, sum, chunk, 128 sums, m sums, padded to 4.
+constexpr int kAttendSlotHead = 3;
+constexpr int attend_slot_floats(int m) { return (kAttendSlotHead + kAttendDim + m + 3) & ~3; }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 
