@@ -448,7 +448,7 @@ def bench_attend(args, w, dev):
         "call_ms_events": round(call_ms, 5),
         "relocate_then_attend_ms": round(unfused_ms, 5),
         "speedup_vs_relocate_then_attend": round(unfused_ms / call_ms, 3),
-        "roofline": {"bound": "hbm", "kernel": "attend_split + attend_combine",
+        "roofline": {"bound": "hbm", "kernel": "attend_prep + attend_tiles + attend_merge (one call)",
                      "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(achieved / 8000.0, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": per, "avg_launch_ms": round(call_ms, 5)},
