@@ -690,18 +690,21 @@ kamera_status validate_attend(const kamera_kv_desc* kv, const kamera_chunks* ch,
   if (!aligned(at->q, 4) || !aligned(at->out, 4) || !aligned(at->lse, 4))
     return fail(KAMERA_E_ALIGN, "q, out and lse must be 4-byte aligned");
   if (L == 0) return KAMERA_OK;
-  // Splits: enough workgroups to fill the chip, at least 64 tokens each.
+  // Splits.  Contiguous caches run one wave per (layer, KV head, split): 8192 of them,
+  // at least 128 tokens each.  Paged caches run a 4-wave workgroup per (layer, KV head,
+  // split): 4096 of them, at least 64 tokens each.
+  const bool rows = kv->page_size == 0;
   const int64_t units = L * K.heads;
-  int64_t S = std::max<int64_t>(1, ceil_div(4096, units));
-  S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(T, 64)));
+  int64_t S = std::max<int64_t>(1, ceil_div(rows ? 8192 : 4096, units));
+  S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(T, rows ? 128 : 64)));
   const int es = env_int("KAMERA_ATTEND_SPLITS", 0);
   if (es > 0) S = es;
   if (T > 0) {
     int64_t TS = ceil_div(T, S);
     TS = ceil_div(TS, 32) * 32;
     S = ceil_div(T, TS);
-    if (ceil_div(L * S, 8) * 8 * K.heads >= ((int64_t)1 << 31))
-      return fail(KAMERA_E_UNSUPPORTED, "too many layers x heads x splits for one launch");
+    if (L * S * K.heads >= ((int64_t)1 << 31) || L * std::max<int64_t>(n, 1) * K.heads >= ((int64_t)1 << 31))
+      return fail(KAMERA_E_UNSUPPORTED, "too many layers x heads x splits (or chunks) for one launch");
     plan->splits = S;
     plan->split_tokens = TS;
     plan->slots = S + std::max<int64_t>(n, 1) - 1;

@@ -40,7 +40,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kThreads = 64 * kWaves;      // prep kernel
+constexpr int kTileWaves = 8;              // tile kernel: waves (KV heads) per workgroup
 constexpr int kD = kAttendDim;
 constexpr int kRowPad = 8;                 // bf16 padding of an LDS tile row
 constexpr int kVRow = kD + kRowPad;        // LDS row of a V tile
@@ -152,24 +153,35 @@ struct TileRows {
   u32x4_t k[4], v[4], uk[MKX], uv[MKX];
 };
 
-// MK: 32-wide rank steps (ceil(m / 32)); PAGED: block-table addressing.  Each wave
-// streams the segment's tiles w, w + 4, ...; with PF it loads the next tile's rows
-// before it works on the current one (the second register tile lowers occupancy,
-// which pays at rank steps of one only).
+// Two mappings of the work, chosen by what measured faster on each layout:
+//  - contiguous caches: one workgroup per (layer, token range), one wave per KV head
+//    (heads w, w + 8, ... beyond 8).  The waves read the same tokens' rows side by
+//    side, so the workgroup streams whole cache rows and the U rows all heads share are
+//    read by one CU.  Each wave walks the range tile by tile and writes its own
+//    partials.
+//  - paged caches: one 4-wave workgroup per (layer, KV head, token range); the waves
+//    take tiles w, w + 4, ... and merge through LDS at the end of each segment.
+// A segment is the part of the range inside one chunk; each writes one partial slot per
+// query head.  MK: 32-wide rank steps (ceil(m / 32)); PAGED: block-table addressing (and
+// the second mapping); PF: the next tile's rows are loaded before the current tile is
+// worked (the second register tile lowers occupancy, which pays at one rank step only).
 template <int MK, bool PAGED, bool PF>
-__global__ __launch_bounds__(kThreads) void attend_tiles(AttendArgs a) {
+__global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves) void attend_tiles(AttendArgs a) {
   constexpr int MKX = MK > 0 ? MK : 1;
   constexpr int MU = 2 * MK;               // 16-wide rank blocks of the U_V sums
   constexpr int MUX = MU > 0 ? MU : 1;
-  // Per-wave V and U_V tiles; reused for the merge at the end of a segment.
-  constexpr int kTileBytes = 16 * (kVRow + kURow) * 2;
+  constexpr bool ROWS = !PAGED;
+  constexpr int kTileBytes = 16 * (kVRow + kURow) * 2;  // per-wave V and U_V tiles
+  // Paged mapping: the tiles' LDS is reused for the merge of the four waves.
   constexpr int kMergeFloats = kWaves * kAttendMaxGroup * (2 + kD + 128);
-  constexpr int kLds =
-      kWaves * kTileBytes > kMergeFloats * 4 ? kWaves * kTileBytes : kMergeFloats * 4;
+  constexpr int kLds = ROWS ? kTileWaves * kTileBytes
+                            : (kWaves * kTileBytes > kMergeFloats * 4 ? kWaves * kTileBytes
+                                                                       : kMergeFloats * 4);
   __shared__ __align__(16) unsigned char lds[kLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int nw = blockDim.x >> 6;
   const int c16 = lane & 15;
   const int grp = lane >> 4;
   uint16_t* sv = (uint16_t*)(lds + wave * kTileBytes);
@@ -179,10 +191,15 @@ __global__ __launch_bounds__(kThreads) void attend_tiles(AttendArgs a) {
 
   const uint32_t S = (uint32_t)a.splits;
   const uint32_t bid = blockIdx.x;
-  const int s = (int)(bid % S);
-  const uint32_t rest = bid / S;
-  const int g = (int)(rest % (uint32_t)a.heads);
-  const int l = (int)(rest / (uint32_t)a.heads);
+  // Workgroup order: split fastest, then (paged) KV head, then layer.
+  const uint32_t lg = bid / S;
+  const int s = (int)(bid - lg * S);
+  const int l = ROWS ? (int)lg : (int)(lg / (uint32_t)a.heads);
+  // ROWS: wave w runs heads w, w + nw, ...; otherwise the workgroup runs one head.
+  const int g_first = ROWS ? wave : (int)(lg - (uint32_t)l * (uint32_t)a.heads);
+  const int g_step = ROWS ? nw : a.heads;
+  const int ti_first = ROWS ? 0 : wave;
+  const int ti_step = ROWS ? 1 : kWaves;
   const int64_t T = a.total_tokens;
   const int64_t t_lo = (int64_t)s * a.split_tokens;
   const int64_t t_hi = min(T, t_lo + (int64_t)a.split_tokens);
@@ -190,10 +207,6 @@ __global__ __launch_bounds__(kThreads) void attend_tiles(AttendArgs a) {
   const int m = a.rank, gq = a.group, Hq = a.num_q_heads, n = a.num_chunks;
   const int W = kD + m;
   const bool hv = c16 < gq;                // this lane's MFMA column is a real query head
-  const uint16_t* kb = (const uint16_t*)a.data[0] + (int64_t)l * a.layer_stride[0] +
-                       (int64_t)g * a.head_stride[0] + 8 * grp;
-  const uint16_t* vb = (const uint16_t*)a.data[1] + (int64_t)l * a.layer_stride[1] +
-                       (int64_t)g * a.head_stride[1] + 8 * grp;
   const uint16_t* ukb = MK > 0 ? (const uint16_t*)a.U[0] + (int64_t)l * T * m + 8 * grp : nullptr;
   const uint16_t* uvb = MK > 0 ? (const uint16_t*)a.U[1] + (int64_t)l * T * m + 8 * grp : nullptr;
   const uint32_t ss0 = (uint32_t)a.slot_stride[0], ss1 = (uint32_t)a.slot_stride[1];
@@ -218,202 +231,234 @@ __global__ __launch_bounds__(kThreads) void attend_tiles(AttendArgs a) {
     return true;
   };
 
-  for (int64_t t0 = t_lo; t0 < t_hi;) {
-    const int j = chunk_at(a.offsets, n, t0);
-    const int64_t s1 = min(t_hi, a.offsets[j + 1]);
-    if (s1 <= t0) break;  // offsets that do not cover the range: nothing more here
+  // All segments of head g over this workgroup's token range.
+  auto run_head = [&](const int g) {
+    const uint16_t* kb = (const uint16_t*)a.data[0] + (int64_t)l * a.layer_stride[0] +
+                         (int64_t)g * a.head_stride[0] + 8 * grp;
+    const uint16_t* vb = (const uint16_t*)a.data[1] + (int64_t)l * a.layer_stride[1] +
+                         (int64_t)g * a.head_stride[1] + 8 * grp;
+    for (int64_t t0 = t_lo; t0 < t_hi;) {
+      const int j = chunk_at(a.offsets, n, t0);
+      const int64_t s1 = min(t_hi, a.offsets[j + 1]);
+      if (s1 <= t0) break;  // offsets that do not cover the range: nothing more here
 
-    // B operands: this lane's query head (column c16), features 32 ks + 8 grp ...
-    bf16x8_t qh[4], ql[4], wh[MKX], wl[MKX];
-    {
-      const float* qp = a.qw + (((int64_t)l * n + j) * Hq + g * gq + (hv ? c16 : 0)) * W;
+      // Loads the rows of tile ti (token tb + c16, 8 consecutive features per step).
+      auto load = [&](int ti, TileRows<MKX>& R) {
+        const int64_t tr = t0 + 16 * (int64_t)ti + c16;
+        uint32_t off_k = 0, off_v = 0;
+        const bool row_on = tr < s1 && slot(tr, off_k, off_v);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = hv ? qp[32 * ks + 8 * grp + e] : 0.f;
-        split8(x, qh[ks], ql[ks]);
-      }
-#pragma unroll
-      for (int ku = 0; ku < MKX; ++ku) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = 32 * ku + 8 * grp + e;
-          x[e] = (MK > 0 && hv && k < m) ? qp[kD + k] : 0.f;
+        for (int ks = 0; ks < 4; ++ks) {
+          R.k[ks] = u32x4_t{0u, 0u, 0u, 0u};
+          R.v[ks] = u32x4_t{0u, 0u, 0u, 0u};
+          if (row_on) {
+            R.k[ks] = __builtin_nontemporal_load((const u32x4_t*)(kb + off_k + 32 * ks));
+            R.v[ks] = __builtin_nontemporal_load((const u32x4_t*)(vb + off_v + 32 * ks));
+          }
         }
-        split8(x, wh[ku], wl[ku]);
-      }
-    }
+#pragma unroll
+        for (int ku = 0; ku < MKX; ++ku) {
+          R.uk[ku] = u32x4_t{0u, 0u, 0u, 0u};
+          R.uv[ku] = u32x4_t{0u, 0u, 0u, 0u};
+          if (MK > 0 && tr < s1 && 32 * ku + 8 * grp < m) {
+            R.uk[ku] = *(const u32x4_t*)(ukb + tr * m + 32 * ku);
+            R.uv[ku] = *(const u32x4_t*)(uvb + tr * m + 32 * ku);
+          }
+        }
+      };
+      const int ntiles = (int)((s1 - t0 + 15) >> 4);
+      TileRows<MKX> cur;
+      if (PF && ti_first < ntiles) load(ti_first, cur);
 
-    float mrun = -INFINITY, lrun = 0.f;
-    f32x4_t acc[8], uacc[MUX];
+      // B operands: this lane's query head (column c16), features 32 ks + 8 grp ...
+      bf16x8_t qh[4], ql[4], wh[MKX], wl[MKX];
+      {
+        const float* qp = a.qw + (((int64_t)l * n + j) * Hq + g * gq + (hv ? c16 : 0)) * W;
 #pragma unroll
-    for (int f = 0; f < 8; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < 4; ++ks) {
+          float x[8];
 #pragma unroll
-    for (int u = 0; u < MUX; ++u) uacc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // Loads the rows of tile ti (token tb + c16, 8 consecutive features per step).
-    auto load = [&](int ti, TileRows<MKX>& R) {
-      const int64_t tr = t0 + 16 * (int64_t)ti + c16;
-      uint32_t off_k = 0, off_v = 0;
-      const bool row_on = tr < s1 && slot(tr, off_k, off_v);
+          for (int e = 0; e < 8; ++e) x[e] = hv ? qp[32 * ks + 8 * grp + e] : 0.f;
+          split8(x, qh[ks], ql[ks]);
+        }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        R.k[ks] = u32x4_t{0u, 0u, 0u, 0u};
-        R.v[ks] = u32x4_t{0u, 0u, 0u, 0u};
-        if (row_on) {
-          R.k[ks] = __builtin_nontemporal_load((const u32x4_t*)(kb + off_k + 32 * ks));
-          R.v[ks] = __builtin_nontemporal_load((const u32x4_t*)(vb + off_v + 32 * ks));
+        for (int ku = 0; ku < MKX; ++ku) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int k = 32 * ku + 8 * grp + e;
+            x[e] = (MK > 0 && hv && k < m) ? qp[kD + k] : 0.f;
+          }
+          split8(x, wh[ku], wl[ku]);
         }
       }
-#pragma unroll
-      for (int ku = 0; ku < MKX; ++ku) {
-        R.uk[ku] = u32x4_t{0u, 0u, 0u, 0u};
-        R.uv[ku] = u32x4_t{0u, 0u, 0u, 0u};
-        if (MK > 0 && tr < s1 && 32 * ku + 8 * grp < m) {
-          R.uk[ku] = *(const u32x4_t*)(ukb + tr * m + 32 * ku);
-          R.uv[ku] = *(const u32x4_t*)(uvb + tr * m + 32 * ku);
-        }
-      }
-    };
-    const int ntiles = (int)((s1 - t0 + 15) >> 4);
-    TileRows<MKX> cur;
-    if (PF && wave < ntiles) load(wave, cur);
-    for (int ti = wave; ti < ntiles; ti += kWaves) {
-      const int64_t tb = t0 + 16 * (int64_t)ti;
-      TileRows<MKX> nxt;
-      if constexpr (PF) {
-        if (ti + kWaves < ntiles) load(ti + kWaves, nxt);
-      } else {
-        load(ti, cur);
-      }
-      const u32x4_t* kx = cur.k;
-      const u32x4_t* vx = cur.v;
-      const u32x4_t* ukx = cur.uk;
-      const u32x4_t* uvx = cur.uv;
-      // Scores of tokens tb + 4 grp + i (i < 4) for query head c16.
-      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, kx[ks]);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qh[ks], sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, ql[ks], sc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int ku = 0; ku < MK; ++ku) {
-        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ukx[ku]);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wh[ku], sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wl[ku], sc, 0, 0, 0);
-      }
-      // The V and U_V rows go to this wave's LDS tile (row c16) for the transposed reads.
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) *(u32x4_t*)(sv + c16 * kVRow + 32 * ks + 8 * grp) = vx[ks];
-#pragma unroll
-      for (int ku = 0; ku < MK; ++ku)
-        if (32 * ku + 8 * grp < m) *(u32x4_t*)(su + c16 * kURow + 32 * ku + 8 * grp) = uvx[ku];
-      // Mask tokens past the segment or without a slot.
-      float s4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = tb + 4 * grp + i;
-        uint32_t o0, o1;
-        const bool on = t < s1 && (!PAGED || slot(t, o0, o1));
-        s4[i] = on ? sc[i] : -INFINITY;
-      }
-      float mt = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
-      mt = max_xor(mt, 16);
-      mt = max_xor(mt, 32);
-      const float mn = fmaxf(mrun, mt);
-      const float corr = weight(mrun, mn);
-      if (corr != 1.f) {
-        lrun *= corr;
-#pragma unroll
-        for (int f = 0; f < 8; ++f) acc[f] *= corr;
-#pragma unroll
-        for (int u = 0; u < MUX; ++u) uacc[u] *= corr;
-      }
-      mrun = mn;
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = weight(s4[i], mn);
-        lrun += p[i];
-      }
-      bf16x4_t ph, pl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ph[i] = (__bf16)p[i];
-        pl[i] = (__bf16)(p[i] - (float)ph[i]);
-      }
-      // O^T[f][h] += V^T[f][t] P^T[t][h]: A = V^T rows f = 16 fb + c16, tokens 4 grp + i.
-#pragma unroll
-      for (int fb = 0; fb < 8; ++fb) {
-        bf16x4_t A;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          A[i] = __builtin_bit_cast(__bf16, sv[(4 * grp + i) * kVRow + 16 * fb + c16]);
-        acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, acc[fb], 0, 0, 0);
-        acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, acc[fb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int ub = 0; ub < MU; ++ub) {
-        if (16 * ub >= m) break;
-        bf16x4_t A;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          A[i] = __builtin_bit_cast(__bf16, su[(4 * grp + i) * kURow + 16 * ub + c16]);
-        uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, uacc[ub], 0, 0, 0);
-        uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, uacc[ub], 0, 0, 0);
-      }
-      if constexpr (PF) cur = nxt;
-    }
-    // The four lane groups of a column hold disjoint tokens' sums.
-    lrun += __shfl_xor(lrun, 16);
-    lrun += __shfl_xor(lrun, 32);
 
-    // ---- merge the four waves; lane (c16, grp) holds features 16 fb + 4 grp + i
-    __syncthreads();  // the tiles' LDS becomes the merge buffer
-    if (hv) {
-      if (grp == 0) {
-        sred[wave][c16][0] = mrun;
-        sred[wave][c16][1] = lrun;
-      }
+      float mrun = -INFINITY, lrun = 0.f;
+      f32x4_t acc[8], uacc[MUX];
 #pragma unroll
-      for (int fb = 0; fb < 8; ++fb)
+      for (int f = 0; f < 8; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sred[wave][c16][2 + 16 * fb + 4 * grp + i] = acc[fb][i];
+      for (int u = 0; u < MUX; ++u) uacc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+      for (int ti = ti_first; ti < ntiles; ti += ti_step) {
+        const int64_t tb = t0 + 16 * (int64_t)ti;
+        TileRows<MKX> nxt;
+        if constexpr (PF) {
+          if (ti + ti_step < ntiles) load(ti + ti_step, nxt);
+        } else {
+          load(ti, cur);
+        }
+        // Scores of tokens tb + 4 grp + i (i < 4) for query head c16.
+        f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ub = 0; ub < MU; ++ub)
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, cur.k[ks]);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qh[ks], sc, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, ql[ks], sc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int ku = 0; ku < MK; ++ku) {
+          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, cur.uk[ku]);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wh[ku], sc, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wl[ku], sc, 0, 0, 0);
+        }
+        // The V and U_V rows go to this wave's LDS tile (row c16) for the transposed
+        // reads; the wave's previous reads of the tile come before these writes in
+        // program order, and LDS accesses of one wave complete in order.
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          *(u32x4_t*)(sv + c16 * kVRow + 32 * ks + 8 * grp) = cur.v[ks];
+#pragma unroll
+        for (int ku = 0; ku < MK; ++ku)
+          if (32 * ku + 8 * grp < m) *(u32x4_t*)(su + c16 * kURow + 32 * ku + 8 * grp) = cur.uv[ku];
+        // Mask tokens past the segment or without a slot.
+        float s4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int k = 16 * ub + 4 * grp + i;
-          if (k < m) sred[wave][c16][2 + kD + k] = uacc[ub][i];
+          const int64_t t = tb + 4 * grp + i;
+          uint32_t o0, o1;
+          const bool on = t < s1 && (!PAGED || slot(t, o0, o1));
+          s4[i] = on ? sc[i] : -INFINITY;
         }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < gq * W; idx += kThreads) {
-      const int h = idx / W, e = idx - h * W;
-      float M = -INFINITY;
+        float mt = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+        mt = max_xor(mt, 16);
+        mt = max_xor(mt, 32);
+        const float mn = fmaxf(mrun, mt);
+        const float corr = weight(mrun, mn);
+        if (corr != 1.f) {
+          lrun *= corr;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sred[w][h][0]);
-      float L = 0.f, A = 0.f;
+          for (int f = 0; f < 8; ++f) acc[f] *= corr;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = weight(sred[w][h][0], M);
-        L = fmaf(f, sred[w][h][1], L);
-        A = fmaf(f, sred[w][h][2 + e], A);
+          for (int u = 0; u < MUX; ++u) uacc[u] *= corr;
+        }
+        mrun = mn;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = weight(s4[i], mn);
+          lrun += p[i];
+        }
+        bf16x4_t ph, pl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ph[i] = (__bf16)p[i];
+          pl[i] = (__bf16)(p[i] - (float)ph[i]);
+        }
+        // O^T[f][h] += V^T[f][t] P^T[t][h]: A = V^T rows f = 16 fb + c16, tokens 4 grp + i.
+#pragma unroll
+        for (int fb = 0; fb < 8; ++fb) {
+          bf16x4_t A;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            A[i] = __builtin_bit_cast(__bf16, sv[(4 * grp + i) * kVRow + 16 * fb + c16]);
+          acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, acc[fb], 0, 0, 0);
+          acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, acc[fb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int ub = 0; ub < MU; ++ub) {
+          if (16 * ub >= m) break;
+          bf16x4_t A;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            A[i] = __builtin_bit_cast(__bf16, su[(4 * grp + i) * kURow + 16 * ub + c16]);
+          uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, uacc[ub], 0, 0, 0);
+          uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, uacc[ub], 0, 0, 0);
+        }
+        if constexpr (PF) cur = nxt;
       }
-      float* sl = a.ws + (((int64_t)l * Hq + g * gq + h) * a.slots + (s + j)) * a.slot_floats;
-      if (e == 0) {
-        sl[0] = M;
-        sl[1] = L;
-        sl[2] = __int_as_float(j);
+      // The four lane groups of a column hold disjoint tokens' sums.
+      lrun += __shfl_xor(lrun, 16);
+      lrun += __shfl_xor(lrun, 32);
+
+      // The segment's partial for query head c16: lane (c16, grp) holds features
+      // 16 fb + 4 grp + i of the value sums and 16 ub + 4 grp + i of the U_V sums.
+      if constexpr (ROWS) {
+        if (hv) {
+          float* sl = a.ws + (((int64_t)l * Hq + g * gq + c16) * a.slots + (s + j)) * a.slot_floats;
+          if (grp == 0) {
+            sl[0] = mrun;
+            sl[1] = lrun;
+            sl[2] = __int_as_float(j);
+          }
+#pragma unroll
+          for (int fb = 0; fb < 8; ++fb)
+            *(f32x4_t*)(sl + kAttendSlotHead + 16 * fb + 4 * grp) = acc[fb];
+#pragma unroll
+          for (int ub = 0; ub < MU; ++ub)
+            if (16 * ub + 4 * grp < m)
+              *(f32x4_t*)(sl + kAttendSlotHead + kD + 16 * ub + 4 * grp) = uacc[ub];
+        }
+      } else {
+        // Merge the four waves' partials through LDS first.
+        __syncthreads();  // the tiles' LDS becomes the merge buffer
+        if (hv) {
+          if (grp == 0) {
+            sred[wave][c16][0] = mrun;
+            sred[wave][c16][1] = lrun;
+          }
+#pragma unroll
+          for (int fb = 0; fb < 8; ++fb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sred[wave][c16][2 + 16 * fb + 4 * grp + i] = acc[fb][i];
+#pragma unroll
+          for (int ub = 0; ub < MU; ++ub)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int k = 16 * ub + 4 * grp + i;
+              if (k < m) sred[wave][c16][2 + kD + k] = uacc[ub][i];
+            }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < gq * W; idx += kThreads) {
+          const int h = idx / W, e = idx - h * W;
+          float M = -INFINITY;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sred[w][h][0]);
+          float L = 0.f, A = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            const float f = weight(sred[w][h][0], M);
+            L = fmaf(f, sred[w][h][1], L);
+            A = fmaf(f, sred[w][h][2 + e], A);
+          }
+          float* sl = a.ws + (((int64_t)l * Hq + g * gq + h) * a.slots + (s + j)) * a.slot_floats;
+          if (e == 0) {
+            sl[0] = M;
+            sl[1] = L;
+            sl[2] = __int_as_float(j);
+          }
+          sl[kAttendSlotHead + e] = A;
+        }
+        __syncthreads();  // the next segment reuses the LDS for tiles
       }
-      sl[kAttendSlotHead + e] = A;
+      t0 = s1;
     }
-    __syncthreads();  // the next segment reuses the LDS for tiles
-    t0 = s1;
+  };
+  if constexpr (ROWS) {
+    for (int g = g_first; g < a.heads; g += g_step) run_head(g);
+  } else {
+    run_head(g_first);
   }
 }
 
@@ -514,14 +559,18 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.splits > 0) {  // no tokens: only the merge runs, writing 0 and -inf
     const dim3 grid0((unsigned)((int64_t)a.num_layers * a.num_chunks * a.heads));
     hipLaunchKernelGGL(attend_prep, grid0, dim3(kThreads), 0, s, a);
-    const dim3 grid1((unsigned)((int64_t)a.num_layers * a.heads * a.splits));
+    // Contiguous: a workgroup per (layer, split), a wave per KV head; paged: a 4-wave
+    // workgroup per (layer, split, KV head).
+    const bool rows = a.page_size == 0;
+    const dim3 grid1((unsigned)((int64_t)a.num_layers * a.splits * (rows ? 1 : a.heads)));
+    const dim3 block1((unsigned)(rows ? 64 * (a.heads < kTileWaves ? a.heads : kTileWaves) : kThreads));
     const int mk = (a.rank + 31) / 32;
-#define KAMERA_ATT(MK)                                                                          \
-  do {                                                                                          \
-    if (a.page_size > 0)                                                                        \
-      hipLaunchKernelGGL((attend_tiles<MK, true, MK == 1>), grid1, dim3(kThreads), 0, s, a);             \
-    else                                                                                        \
-      hipLaunchKernelGGL((attend_tiles<MK, false, MK == 1>), grid1, dim3(kThreads), 0, s, a);            \
+#define KAMERA_ATT(MK)                                                                   \
+  do {                                                                                   \
+    if (a.page_size > 0)                                                                 \
+      hipLaunchKernelGGL((attend_tiles<MK, true, MK == 1>), grid1, block1, 0, s, a);   \
+    else                                                                                 \
+      hipLaunchKernelGGL((attend_tiles<MK, false, MK == 1>), grid1, block1, 0, s, a);  \
   } while (0)
     if (mk == 0) KAMERA_ATT(0);
     else if (mk == 1) KAMERA_ATT(1);

@@ -106,8 +106,9 @@ struct AttendArgs {
 
 constexpr int kAttendDim = 128;
 constexpr int kAttendMaxGroup = 8;
-// Floats of one partial slot at rank m: max, sum, chunk, 128 sums, m sums, padded to 4.
-constexpr int kAttendSlotHead = 3;
+// Floats of one partial slot at rank m: max, sum, chunk, one unused float (the sums
+// start 16-byte aligned), 128 value sums, m U_V sums; padded to a multiple of 4.
+constexpr int kAttendSlotHead = 4;
 constexpr int attend_slot_floats(int m) { return (kAttendSlotHead + kAttendDim + m + 3) & ~3; }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
