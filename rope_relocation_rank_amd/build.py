@@ -1,13 +1,20 @@
-"""Builds libkamera.so (gfx950 HIP kernels + C ABI) in place with hipcc."""
+"""Builds libkamera.so (gfx950 HIP kernels + C ABI) in place with hipcc.
+
+Each source compiles to its own object in parallel (every translation unit carries
+its own gfx950 code object; nothing is relocatable device code), then hipcc links
+the objects into the shared library.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
+OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkamera.so")
 SOURCES = [os.path.join(CSRC, "abi.cpp"), os.path.join(CSRC, "kernels.hip"),
            os.path.join(CSRC, "form.hip"), os.path.join(CSRC, "attend.hip")]
@@ -16,7 +23,7 @@ HEADERS = [os.path.join(INCLUDE, "kamera.h"), os.path.join(CSRC, "kamera_interna
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared", "-fvisibility=hidden",
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-fvisibility=hidden",
     # packed fp32 VALU ops stay off: the compiler must not form v_pk_* fp32 ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA accumulators stay in VGPRs (no AGPR copies around every MFMA)
@@ -25,10 +32,7 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into one shared library, always (no up-to-date check)."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -37,7 +41,20 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
-        print(out)
+        print(out, flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into one shared library, always (no up-to-date check)."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = [os.path.join(OBJDIR, os.path.basename(s) + ".o") for s in SOURCES]
+    cmds = [[HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", s, "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max_workers=len(cmds)) as pool:
+        for f in [pool.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
