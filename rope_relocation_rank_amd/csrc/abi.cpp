@@ -77,7 +77,6 @@ struct Plan {
   int block_tokens = 0;
   int tiles_per_wave = 0;
   int rotate_unroll = 2;
-  int tile_unroll = 1;
   int64_t units = 0;  // workgroups of the tuned launch(es)
 };
 
@@ -101,8 +100,9 @@ __int128 layer_extent(const kamera_channel& c, int64_t T, int32_t page_size, int
 // Rotation-only kernel: 8-element lanes over the rotated dims of each row.
 bool rotate_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, int64_t T) {
   const int r = c.rope_dim;
-  // row offsets inside a layer are kept in 32 bits
-  const bool extent_ok = layer_extent(c, T, kv.page_size, kv.num_pages) < ((__int128)1 << 31);
+  // one layer is reached through a buffer resource with 32-bit byte offsets
+  const bool extent_ok = layer_extent(c, T, kv.page_size, kv.num_pages) * elem_bytes(kv.dtype) <=
+                         kamera::kMaxBufferBytes;
   return tuned_dtype(kv.dtype) && !(kv.flags & KAMERA_FLAG_GENERIC) &&
          (r == 16 || r == 32 || r == 64 || r == 128) && T < kMaxTunedTokens && extent_ok &&
          aligned(c.data, vec_align(kv.dtype)) && strides_ok(c);
@@ -115,8 +115,12 @@ bool mfma_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, const kame
   const int r = c.rope_dim, D = c.dim;
   const bool rope_ok = r == 0 || ((r == 16 || r == 32 || r == 64 || r == 128) && D % r == 0);
   const bool dim_ok = D % 8 == 0 && (D % 128 == 0 || 128 % D == 0);
-  // row offsets inside a layer are kept in 32 bits
-  const bool extent_ok = layer_extent(c, T, kv.page_size, kv.num_pages) < ((__int128)1 << 31);
+  // one layer of the channel and one layer of U are each reached through a buffer
+  // resource with 32-bit byte offsets
+  const bool extent_ok =
+      layer_extent(c, T, kv.page_size, kv.num_pages) * elem_bytes(kv.dtype) <=
+          kamera::kMaxBufferBytes &&
+      (__int128)T * p.rank * factor_bytes(kv.dtype) <= kamera::kMaxBufferBytes;
   return tuned_dtype(kv.dtype) && !(kv.flags & KAMERA_FLAG_GENERIC) && p.rank <= kMfmaMaxRank &&
          (kv.dtype == KAMERA_BF16 || p.rank % 8 == 0) && rope_ok && dim_ok && extent_ok &&
          T < kMaxTunedTokens && aligned(c.data, vec_align(kv.dtype)) && aligned(p.U[ci], 16) &&
@@ -138,7 +142,6 @@ void plan_mfma(const kamera_kv_desc& kv, const kamera_chunks& ch, int m, const b
   int tpw = env_int("KAMERA_TILES_PER_WAVE", dflt);
   if (tpw < 1 || tpw > kamera::kMaxBlockTokens / 64) tpw = dflt;
   plan->tiles_per_wave = tpw;
-  plan->tile_unroll = env_int("KAMERA_TILE_UNROLL", 1) == 2 ? 2 : 1;
   plan->block_tokens = 64 * tpw;
   // A second launch covers the token groups that chunk boundaries cut.
   const int64_t T = ch.total_tokens;
@@ -363,7 +366,10 @@ kamera_status run(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamer
   if (m == 0) {
     for (int c = 0; c < kv->num_channels; ++c) {
       if (plan.kernel[c] == K_NONE) continue;
-      const kamera::ChanArgs a = chan_args(*kv, c, nullptr);
+      kamera::ChanArgs a = chan_args(*kv, c, nullptr);
+      a.layer_bytes = (uint32_t)(layer_extent(kv->ch[c], ch->total_tokens, kv->page_size,
+                                              kv->num_pages) *
+                                 elem_bytes(kv->dtype));
       const hipError_t e = plan.kernel[c] == K_ROTATE
                                ? kamera::launch_rotate_rows(a, cm, plan.rotate_unroll, stream)
                                                       : kamera::launch_generic(a, cm, kv->dtype, stream);
@@ -376,6 +382,10 @@ kamera_status run(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamer
   for (int c = 0; c < kv->num_channels; ++c) {
     kamera::ChanArgs a = chan_args(*kv, c, p);
     if (plan.kernel[c] == K_MFMA) {
+      const int64_t T = ch->total_tokens;
+      a.layer_bytes = (uint32_t)(layer_extent(kv->ch[c], T, kv->page_size, kv->num_pages) *
+                                 elem_bytes(kv->dtype));
+      a.u_layer_bytes = (uint32_t)(T * m * factor_bytes(kv->dtype));
       a.fblocks = (int)ceil_div((int64_t)a.heads * a.dim, 128);
       a.blocks = cm.token_groups * a.fblocks;
       tuned[ntuned++] = a;
@@ -386,7 +396,7 @@ kamera_status run(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamer
   }
   if (ntuned > 0) {
     const hipError_t e =
-        kamera::launch_relocate_patch_rows(tuned, ntuned, cm, plan.tile_unroll, stream);
+        kamera::launch_relocate_patch_rows(tuned, ntuned, cm, stream);
     if (e != hipSuccess) return hip_fail(e, "relocate+patch launch");
   }
   return KAMERA_OK;
@@ -402,9 +412,11 @@ bool recall_tuned_ok(const kamera_kv_desc& src, const kamera_kv_desc& dst, const
   const int r = c.rope_dim, D = c.dim;
   const bool rope_ok = r == 0 || ((r == 16 || r == 32 || r == 64 || r == 128) && D % r == 0);
   const bool dim_ok = D % 8 == 0 && (D % 128 == 0 || 128 % D == 0);
+  const int64_t es = elem_bytes(src.dtype);
   const bool extent_ok =
-      layer_extent(c, T, src.page_size, src.num_pages) < ((__int128)1 << 31) &&
-      layer_extent(d, T, dst.page_size, dst.num_pages) < ((__int128)1 << 31);
+      layer_extent(c, T, src.page_size, src.num_pages) * es <= kamera::kMaxBufferBytes &&
+      layer_extent(d, T, dst.page_size, dst.num_pages) * es <= kamera::kMaxBufferBytes &&
+      (__int128)T * m * factor_bytes(src.dtype) <= kamera::kMaxBufferBytes;
   const bool factors_ok = m == 0 || (aligned(p->U[ci], 16) && aligned(p->V[ci], 16));
   const uintptr_t va = vec_align(src.dtype);
   return tuned_dtype(src.dtype) && !((src.flags | dst.flags) & KAMERA_FLAG_GENERIC) &&
@@ -515,6 +527,11 @@ kamera_status run_recall(const kamera_kv_desc* src, const kamera_kv_desc* dst,
     a.out_head_stride = d.head_stride;
     a.out_page_stride = d.page_stride;
     if (plan.kernel[c] == K_MFMA) {
+      const int64_t T = ch->total_tokens, es = elem_bytes(src->dtype);
+      a.layer_bytes =
+          (uint32_t)(layer_extent(src->ch[c], T, src->page_size, src->num_pages) * es);
+      a.out_layer_bytes = (uint32_t)(layer_extent(d, T, dst->page_size, dst->num_pages) * es);
+      a.u_layer_bytes = (uint32_t)(T * m * factor_bytes(src->dtype));
       a.fblocks = (int)ceil_div((int64_t)a.heads * a.dim, 128);
       a.blocks = cm.token_groups * a.fblocks;
       tuned[ntuned++] = a;
@@ -524,7 +541,8 @@ kamera_status run_recall(const kamera_kv_desc* src, const kamera_kv_desc* dst,
     }
   }
   if (ntuned > 0) {
-    const hipError_t e = kamera::launch_relocate_patch_rows(tuned, ntuned, cm, 1, stream);
+    const hipError_t e =
+        kamera::launch_relocate_patch_rows(tuned, ntuned, cm, stream);
     if (e != hipSuccess) return hip_fail(e, "recall launch");
   }
   return KAMERA_OK;

@@ -8,6 +8,10 @@ namespace kamera {
 
 constexpr int kMaxTunedHalf = 64;     // tuned kernels rotate at most 128 dims per head
 constexpr int kMaxBlockTokens = 512;  // tokens one tuned workgroup covers, at most
+// The rotate+patch kernel addresses one layer of a channel (and one layer of U) through
+// a buffer resource with 32-bit byte offsets; byte offset 2^31 is its "no row" value,
+// so every range it covers ends at or below this.
+constexpr int64_t kMaxBufferBytes = ((int64_t)1 << 31) - 64;
 
 // One channel as the kernels see it.  Pointers are device pointers; strides are in
 // elements of the storage type.
@@ -21,6 +25,9 @@ struct ChanArgs {
   const void* U;  // [layers][tokens][rank]
   const void* V;  // [layers][chunks][heads*dim][rank]
   const float* scale;  // fp8 E4M3: [layers] dequantisation scales; else unused
+  // rotate+patch kernel: bytes one layer spans (largest element offset + 1, times the
+  // element size) in the source, the destination and U.
+  uint32_t layer_bytes, out_layer_bytes, u_layer_bytes;
   int32_t heads, dim, rope_dim;
   int32_t fblocks;   // rotate+patch kernel: 128-feature blocks per token row
   int64_t blocks;    // tuned kernels: workgroups of this channel per layer
@@ -130,9 +137,8 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
 // With ChanArgs::out set it runs out of place (rank % 8 == 0; rank 0 allowed).
 // Covers nch (1 or 2) channels in one launch, plus a second launch for the token groups
 // that chunk boundaries cut when there is more than one chunk.
-// `tile_unroll` 16-token tiles (1 or 2) are loaded together by each wavefront.
 hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonArgs& cm,
-                                      int tile_unroll, hipStream_t s);
+                                      hipStream_t s);
 
 // Plain per-row kernel: any dim, even rope_dim, rank <= KAMERA_MAX_RANK, bf16, fp32 or
 // fp8, element-aligned pointers.  In place with rank 0 it only touches rotated dims; out of

@@ -78,11 +78,33 @@ __device__ __forceinline__ u32x4_t pack8(const float (&y)[8]) {
   return r;
 }
 
-__device__ __forceinline__ u32x4_t load_nt(const uint16_t* p) {
-  return __builtin_nontemporal_load((const u32x4_t*)p);
+
+// Buffer addressing (gfx9 raw buffer: stride 0, dword data format in word 3).  A
+// resource covers `bytes` bytes from a wave-uniform base; every access is range checked
+// by the hardware, so a load at byte offset kOob reads zeros and a store there is
+// dropped: rows a lane must skip take that offset instead of a branch.  aux = 2 sets
+// the nontemporal bit.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
-__device__ __forceinline__ void store_nt(uint16_t* p, const u32x4_t& v) {
-  __builtin_nontemporal_store(v, (u32x4_t*)p);
+__device__ __forceinline__ void bload_nt(rsrc_t r, uint32_t off, u32x4_t& v) {
+  v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+}
+__device__ __forceinline__ void bload_nt(rsrc_t r, uint32_t off, u32x2_t& v) {
+  v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 2);
+}
+__device__ __forceinline__ void bstore_nt(rsrc_t r, uint32_t off, const u32x4_t& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 2);
+}
+__device__ __forceinline__ void bstore_nt(rsrc_t r, uint32_t off, const u32x2_t& v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 2);
+}
+// 16 bytes at `off` through a resource, cached (factor rows are re-read by other waves).
+__device__ __forceinline__ u32x4_t bload(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
 __device__ __forceinline__ float load_f(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
@@ -139,12 +161,6 @@ __device__ __forceinline__ u32x2_t pack8_fp8(const float (&y)[8]) {
   return r;
 }
 
-__device__ __forceinline__ u32x2_t load_nt(const uint8_t* p) {
-  return __builtin_nontemporal_load((const u32x2_t*)p);
-}
-__device__ __forceinline__ void store_nt(uint8_t* p, const u32x2_t& v) {
-  __builtin_nontemporal_store(v, (u32x2_t*)p);
-}
 
 __device__ __forceinline__ float load_f(const uint8_t* p) { return fp8_pair(*p, false).x; }
 __device__ __forceinline__ void store_f(uint8_t* p, float y) {
@@ -418,7 +434,8 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
   const float sgn = q < HX ? -1.f : 1.f;
   const int H = ch.heads;
   const int nrows = (int)(t1 - tb0) * H;
-  E* base = (E*)ch.data + (int64_t)layer * ch.layer_stride + 8 * q;
+  // One layer through a buffer resource: rows the lane skips take byte offset kOob.
+  const rsrc_t rkv = make_rsrc((E*)ch.data + (int64_t)layer * ch.layer_stride, ch.layer_bytes);
   // Offsets in uint32 arithmetic: every row the lane touches lies below 2^31, and rows
   // past the block's end (never loaded) may wrap harmlessly.
   const uint32_t ss = (uint32_t)ch.slot_stride, hs = (uint32_t)ch.head_stride;
@@ -434,9 +451,8 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
   }
   for (int rbase = 0; rbase < nrows; rbase += ROWS) {
     XV xv[UNR];
-    E* ptr[UNR];
+    uint32_t boff[UNR];  // byte offset of the lane's 8 elements, kOob = no row
     int tlk[UNR];  // token of each row group, relative to tb0
-    bool ok[UNR];
     const int R0 = rbase + wave * RPI + rr;
     int tl = R0 / H;
     int h = R0 - tl * H;
@@ -453,21 +469,20 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
           off += carry;
         }
       }
-      ok[k] = R0 + k * DR < nrows;
+      bool ok = R0 + k * DR < nrows;
       tlk[k] = tl;
       uint32_t o = off;
       if constexpr (PAGED) {
         o = 0u;
-        if (ok[k]) {  // the staged table covers the block's own tokens only
+        if (ok) {  // the staged table covers the block's own tokens only
           const int32_t so = slot32<true>(cm.page_size, cm.page_shift, sbt, p0, ps, (int32_t)ss,
                                           (int)tb0 + tl);
-          ok[k] = so >= 0;
+          ok = so >= 0;
           o = (uint32_t)so + (uint32_t)h * hs;
         }
       }
-      ptr[k] = base + o;
-      xv[k] = (XV)(0u);
-      if (ok[k]) xv[k] = load_nt(ptr[k]);
+      boff[k] = ok ? (o + 8u * (uint32_t)q) * (uint32_t)sizeof(E) : kOob;
+      bload_nt(rkv, boff[k], xv[k]);
     }
     // Token span of this wave's rows in this pass.
     const int r_first = rbase + wave * RPI;
@@ -505,7 +520,7 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
           if constexpr (Q) o = pack8_fp8(y);
           else o = pack8(y);
           if constexpr (SEC) o = keep_elems(o, xv[k], sn);
-          if (ok[k] && tlk[k] >= lo && tlk[k] < hi) store_nt(ptr[k], o);
+          bstore_nt(rkv, tlk[k] >= lo && tlk[k] < hi ? boff[k] : kOob, o);
         }
       }
       t0 = max(t0, s1);
@@ -535,8 +550,11 @@ __device__ __forceinline__ u32x4_t load_frag(const uint16_t* row, int k0, int m,
 // Per-workgroup constants of the rotate+patch kernel that the tile loop reads.
 template <bool Q>
 struct PatchCtx {
-  typename Codec<Q>::E* base;   // lane's element (layer, slot 0, head h, dim d0)
-  typename Codec<Q>::E* obase;  // same element of the destination (out of place)
+  rsrc_t rkv;           // this layer of the channel (in place: read and written)
+  rsrc_t rout;          // this layer of the destination (out of place)
+  rsrc_t ru;            // U of this layer and channel
+  uint32_t lane_b;      // byte offset of the lane's element (slot 0, head h, dim d0)
+  uint32_t olane_b;     // same in the destination
   const uint16_t* Ul;   // U of this layer and channel
   const int* sbt;       // staged block table (paged)
   const int* osbt;      // staged destination block table (paged destination)
@@ -552,59 +570,67 @@ struct PatchCtx {
   float qs, qinv;       // fp8: the layer's dequantisation scale and its reciprocal
 };
 
-// KV, row offsets and U fragments of the TU tiles a wave loads together.
-template <bool Q, int MK, int TU>
-struct TileSet {
-  typename Codec<Q>::XV x[TU][4];
-  // Element offset of the row to store, -1 = none: from the lane's base in place, from
-  // the lane's destination base out of place.
-  int32_t off[TU][4];
-  u32x4_t a[TU][MK > 0 ? MK : 1];
+// KV, row offsets and U fragments of one 16-token tile of a wave.
+template <bool Q, int MK>
+struct Tile {
+  typename Codec<Q>::XV x[4];
+  // Byte offset of the lane's 8 elements of the row to store, kOob = none: in the
+  // layer's source resource in place, in its destination resource out of place.
+  uint32_t off[4];
+  u32x4_t a[MK > 0 ? MK : 1];
 };
 
-// Loads tiles kt, kt + 4, ... (TU of them, those below k_hi), keeping tokens in [t0, s1).
-// OUT: 0 in place, 1 contiguous destination, 2 paged destination; a row is loaded
-// only when both its source and its destination slot exist.
-template <bool Q, int MK, bool M8, bool PAGED, int TU, int OUT>
-__device__ __forceinline__ void load_tiles(const PatchCtx<Q>& c, const CommonArgs& cm, int kt,
-                                           int k_hi, int64_t t0, int64_t s1,
-                                           TileSet<Q, MK, TU>& T) {
+// Loads tile kt (no rows when kt >= k_hi), keeping tokens in [t0, s1).  OUT: 0 in
+// place, 1 contiguous destination, 2 paged destination; a row is loaded only when both
+// its source and its destination slot exist.
+template <bool Q, int MK, bool M8, bool PAGED, int OUT>
+__device__ __forceinline__ void load_tile(const PatchCtx<Q>& c, const CommonArgs& cm, int kt,
+                                          int k_hi, int64_t t0, int64_t s1, Tile<Q, MK>& T) {
+  constexpr uint32_t es = sizeof(typename Codec<Q>::E);
+  const int64_t ts = c.tb0 + 16 * (int64_t)kt;
+  const bool tile_on = kt < k_hi;
 #pragma unroll
-  for (int u = 0; u < TU; ++u) {
-    const int64_t ts = c.tb0 + 16 * (int64_t)(kt + kWavesPerBlock * u);
-    const bool tile_on = kt + kWavesPerBlock * u < k_hi;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = ts + 4 * c.g + i;
-      T.off[u][i] = -1;
-      T.x[u][i] = (typename Codec<Q>::XV)(0u);
-      if (tile_on && c.lane_on && t >= t0 && t < s1) {
-        int32_t so = slot32<PAGED>(cm.page_size, cm.page_shift, c.sbt, c.p0, c.page_stride,
-                                   c.slot_stride, (int)t);
-        if constexpr (OUT > 0) {
-          const int32_t dso = slot32<OUT == 2>(cm.out_page_size, cm.out_page_shift, c.osbt, c.op0,
-                                               c.opage_stride, c.oslot_stride, (int)t);
-          if (dso < 0) so = -1;
-          if (so >= 0) T.x[u][i] = load_nt(c.base + so);
-          T.off[u][i] = so >= 0 ? dso : -1;
-        } else {
-          T.off[u][i] = so;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = ts + 4 * c.g + i;
+    // Offsets only (no memory access depends on a branch): rows the lane skips load
+    // zeros from and store nothing to offset kOob.
+    uint32_t so = kOob, dso = kOob;
+    if (tile_on && c.lane_on && t >= t0 && t < s1) {
+      const int32_t s = slot32<PAGED>(cm.page_size, cm.page_shift, c.sbt, c.p0, c.page_stride,
+                                      c.slot_stride, (int)t);
+      if constexpr (OUT > 0) {
+        const int32_t d = slot32<OUT == 2>(cm.out_page_size, cm.out_page_shift, c.osbt, c.op0,
+                                           c.opage_stride, c.oslot_stride, (int)t);
+        if (s >= 0 && d >= 0) {
+          so = (uint32_t)s * es + c.lane_b;
+          dso = (uint32_t)d * es + c.olane_b;
         }
+      } else if (s >= 0) {
+        so = (uint32_t)s * es + c.lane_b;
       }
-      if (OUT == 0 && T.off[u][i] >= 0) T.x[u][i] = load_nt(c.base + T.off[u][i]);
     }
-    const int64_t tu = ts + c.c16;
-    const bool uok = tile_on && tu < c.t1;
-    const uint16_t* urow = c.Ul + (uok ? tu : 0) * c.m;
+    T.off[i] = OUT > 0 ? dso : so;
+    bload_nt(c.rkv, so, T.x[i]);
+  }
+  const int64_t tu = ts + c.c16;
+  const bool uok = tile_on && tu < c.t1;
 #pragma unroll
-    for (int ks = 0; ks < (MK > 0 ? MK : 1); ++ks) {
-      T.a[u][ks] = u32x4_t{0u, 0u, 0u, 0u};
-      if (MK > 0 && uok) T.a[u][ks] = load_frag(urow, 32 * ks + 8 * c.g, c.m, M8);
+  for (int ks = 0; ks < (MK > 0 ? MK : 1); ++ks) {
+    T.a[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (MK > 0) {
+      const int k0 = 32 * ks + 8 * c.g;
+      if constexpr (M8) {
+        // rows are 16-byte aligned; ranks past m read zeros
+        const uint32_t uo = uok && k0 < c.m ? ((uint32_t)tu * c.m + k0) * 2u : kOob;
+        T.a[ks] = bload(c.ru, uo);
+      } else if (uok) {
+        T.a[ks] = load_frag(c.Ul + tu * c.m, k0, c.m, false);
+      }
     }
   }
 }
 
-// Rotates, patches and stores loaded tiles.  HX is the NeoX partner lane distance, -1
+// Rotates, patches and stores a loaded tile.  HX is the NeoX partner lane distance, -1
 // for interleaved pairs (partner in the other half of the same word), 0 for no
 // rotation.  Lane l holds features fb + 8c + n (c = l & 15, n < 8) of tokens
 // 4g .. 4g + 3 (g = l >> 4).
@@ -624,14 +650,17 @@ __device__ __forceinline__ void load_tiles(const PatchCtx<Q>& c, const CommonArg
 // one FMA finishes each element; at larger MK, where the rotated values cannot stay
 // live beside the accumulators without spilling, the accumulator starts at s * rotated
 // and the sum is multiplied by 1/s.
-template <bool Q, int MK, int HX, int TU, int OUT>
-__device__ __forceinline__ void finish_tiles(const PatchCtx<Q>& c, const u32x4_t* sV,
-                                             const float4* sph2, const TileSet<Q, MK, TU>& T) {
+template <bool Q, int MK, int HX, int OUT>
+__device__ __forceinline__ void finish_tile(const PatchCtx<Q>& c, const u32x4_t* sV,
+                                            const float4* sph2, Tile<Q, MK>& T) {
   using P = Codec<Q>;
   const float2* sph = reinterpret_cast<const float2*>(sph2);
-#pragma unroll
-  for (int u = 0; u < TU; ++u) {
-    typename P::XV out[4];
+  {
+    // bf16: feature pair pp of a row is one word, read (with the partner lane's word)
+    // before its result is written, so results overwrite the loaded words.  fp8 packs
+    // two pairs per word and keeps a separate result.
+    typename P::XV outq[4];
+    typename P::XV* out = Q ? outq : T.x;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {  // features 2pp, 2pp + 1 of the lane's 8
       // (cos, sin) of the pairs of the two features, and whether each one turns.
@@ -646,7 +675,7 @@ __device__ __forceinline__ void finish_tiles(const PatchCtx<Q>& c, const u32x4_t
       float r0[4], r1[4];  // rotated (or unrotated) values of the two features
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t w = P::word(T.x[u][i], pp);
+        const uint32_t w = P::word(T.x[i], pp);
         const float2 av = P::pair(w, pp);
         const float a0 = av.x, a1 = av.y;
         float y0 = a0, y1 = a1;
@@ -666,7 +695,7 @@ __device__ __forceinline__ void finish_tiles(const PatchCtx<Q>& c, const u32x4_t
         // element is copied bit for bit.
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          P::put_keep(out[i], T.x[u][i], pp, r0[i], r1[i], !turn0, !turn1);
+          P::put_keep(out[i], T.x[i], pp, r0[i], r1[i], !turn0, !turn1);
       } else {
         constexpr bool kFmaScale = Q && MK == 1;
         f32x4_t acc0, acc1;
@@ -677,7 +706,7 @@ __device__ __forceinline__ void finish_tiles(const PatchCtx<Q>& c, const u32x4_t
         }
 #pragma unroll
         for (int ks = 0; ks < MK; ++ks) {
-          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, T.a[u][ks]);
+          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, T.a[ks]);
           const bf16x8_t B0 = __builtin_bit_cast(bf16x8_t, sV[((2 * pp) * MK + ks) * 64 + c.lane]);
           const bf16x8_t B1 =
               __builtin_bit_cast(bf16x8_t, sV[((2 * pp + 1) * MK + ks) * 64 + c.lane]);
@@ -695,30 +724,29 @@ __device__ __forceinline__ void finish_tiles(const PatchCtx<Q>& c, const u32x4_t
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (T.off[u][i] >= 0) store_nt((OUT > 0 ? c.obase : c.base) + T.off[u][i], out[i]);
+    for (int i = 0; i < 4; ++i) bstore_nt(OUT > 0 ? c.rout : c.rkv, T.off[i], out[i]);
   }
 }
 
-// The wave's tiles (16-token tile kt with kt = wave mod 4) that meet [t0, s1), TU at a
-// time; only tokens in [t0, s1) are loaded and stored.  When `use_pre`, `pre` already
-// holds the wave's first group of tiles (loaded before the workgroup staged the chunk).
-template <bool Q, int MK, bool M8, bool PAGED, int HX, int TU, int OUT>
+// The wave's 16-token tiles (kt = wave mod 4, kt + 4, ...) that meet [t0, s1), one at a
+// time; only tokens in [t0, s1) are loaded and stored.  When `use_pre`, A already holds
+// the wave's first tile (loaded before the workgroup staged the chunk).
+template <bool Q, int MK, bool M8, bool PAGED, int HX, int OUT>
 __device__ __forceinline__ void patch_tiles(const PatchCtx<Q>& c, const CommonArgs& cm,
                                             const u32x4_t* sV, const float4* sph2,
-                                            int64_t t0, int64_t s1,
-                                            const TileSet<Q, MK, TU>& pre, bool use_pre) {
+                                            int64_t t0, int64_t s1, Tile<Q, MK>& A,
+                                            bool use_pre) {
+  constexpr int W = kWavesPerBlock;
   const int k_lo = (int)((t0 - c.tb0) >> 4);
   const int k_hi = (int)((s1 - c.tb0 + 15) >> 4);
-  int kt = k_lo + ((c.wave - k_lo) % kWavesPerBlock + kWavesPerBlock) % kWavesPerBlock;
+  int kt = k_lo + ((c.wave - k_lo) % W + W) % W;
   if (use_pre) {
-    finish_tiles<Q, MK, HX, TU, OUT>(c, sV, sph2, pre);
-    kt += kWavesPerBlock * TU;
+    finish_tile<Q, MK, HX, OUT>(c, sV, sph2, A);
+    kt += W;
   }
-  for (; kt < k_hi; kt += kWavesPerBlock * TU) {
-    TileSet<Q, MK, TU> T;
-    load_tiles<Q, MK, M8, PAGED, TU, OUT>(c, cm, kt, k_hi, t0, s1, T);
-    finish_tiles<Q, MK, HX, TU, OUT>(c, sV, sph2, T);
+  for (; kt < k_hi; kt += W) {
+    load_tile<Q, MK, M8, PAGED, OUT>(c, cm, kt, k_hi, t0, s1, A);
+    finish_tile<Q, MK, HX, OUT>(c, sV, sph2, A);
   }
 }
 
@@ -740,8 +768,8 @@ __device__ __forceinline__ void patch_tiles(const PatchCtx<Q>& c, const CommonAr
 // OUT != 0 is the out-of-place form (recall): rows are read through the source layout
 // and whole result rows written through the destination layout (OUT 1 contiguous, 2
 // paged); MK = 0 is its no-patch form.  Q: fp8 E4M3 elements (bf16 factors).
-template <bool Q, int MK, bool M8, bool PAGED, int TU, bool TAIL, int OUT>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(!TAIL && TU == 1 && (MK <= 1 || (MK == 2 && OUT == 0)) ? 4 : 1)))
+template <bool Q, int MK, bool M8, bool PAGED, bool TAIL, int OUT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAIL || MK > 2 || (MK == 2 && OUT != 0) ? 1 : 4)))
 void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t blocks_per_layer,
                          int xcd_group) {
   __shared__ u32x4_t sV[8 * (MK > 0 ? MK : 1) * 64];
@@ -799,22 +827,27 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
 
   c.slot_stride = (int32_t)KAMERA_CH(slot_stride);
   c.page_stride = (int32_t)KAMERA_CH(page_stride);
-  c.base = (E*)KAMERA_CH(data) + layer * KAMERA_CH(layer_stride) +
-           (int64_t)h * KAMERA_CH(head_stride) + d0;
+  c.rkv = make_rsrc((E*)KAMERA_CH(data) + layer * KAMERA_CH(layer_stride),
+                    KAMERA_CH(layer_bytes));
+  c.lane_b = (uint32_t)(((int64_t)h * KAMERA_CH(head_stride) + d0) * (int64_t)sizeof(E));
   c.qs = c.qinv = 1.f;
   if constexpr (Q) {
     c.qs = KAMERA_CH(scale)[layer];
     c.qinv = 1.f / c.qs;
   }
-  c.obase = nullptr;
+  c.rout = c.rkv;
+  c.olane_b = 0;
   c.opage_stride = c.oslot_stride = 0;
   if constexpr (OUT > 0) {
-    c.obase = (E*)KAMERA_CH(out) + layer * KAMERA_CH(out_layer_stride) +
-              (int64_t)h * KAMERA_CH(out_head_stride) + d0;
+    c.rout = make_rsrc((E*)KAMERA_CH(out) + layer * KAMERA_CH(out_layer_stride),
+                       KAMERA_CH(out_layer_bytes));
+    c.olane_b =
+        (uint32_t)(((int64_t)h * KAMERA_CH(out_head_stride) + d0) * (int64_t)sizeof(E));
     c.oslot_stride = (int32_t)KAMERA_CH(out_slot_stride);
     c.opage_stride = (int32_t)KAMERA_CH(out_page_stride);
   }
   c.Ul = (const uint16_t*)KAMERA_CH(U) + layer * cm.total_tokens * m;
+  c.ru = make_rsrc(c.Ul, KAMERA_CH(u_layer_bytes));
   const uint16_t* Vl = (const uint16_t*)KAMERA_CH(V) + layer * (int64_t)cm.num_chunks * F * m;
 
   // Token group and the first token this workgroup works on.
@@ -872,39 +905,37 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
       reinterpret_cast<float2*>(sph2)[threadIdx.x] =
           phase_of(KAMERA_CH(omega[threadIdx.x]), pair_delta(cm, ck, threadIdx.x));
   };
-#define KAMERA_PATCH_SWITCH(PRE, USE)                                                           \
-  switch (rotate ? hx : 0) {                                                                    \
-    case 1: patch_tiles<Q, MK, M8, PAGED, 1, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;    \
-    case 2: patch_tiles<Q, MK, M8, PAGED, 2, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;    \
-    case 4: patch_tiles<Q, MK, M8, PAGED, 4, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;    \
-    case 8: patch_tiles<Q, MK, M8, PAGED, 8, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;    \
-    case -1: patch_tiles<Q, MK, M8, PAGED, -1, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;  \
-    default: patch_tiles<Q, MK, M8, PAGED, 0, TU, OUT>(c, cm, sV, sph2, t0, s1, PRE, USE); break;   \
+#define KAMERA_PATCH_SWITCH(USE)                                                             \
+  switch (rotate ? hx : 0) {                                                                 \
+    case 1: patch_tiles<Q, MK, M8, PAGED, 1, OUT>(c, cm, sV, sph2, t0, s1, A, USE); break;   \
+    case 2: patch_tiles<Q, MK, M8, PAGED, 2, OUT>(c, cm, sV, sph2, t0, s1, A, USE); break;   \
+    case 4: patch_tiles<Q, MK, M8, PAGED, 4, OUT>(c, cm, sV, sph2, t0, s1, A, USE); break;   \
+    case 8: patch_tiles<Q, MK, M8, PAGED, 8, OUT>(c, cm, sV, sph2, t0, s1, A, USE); break;   \
+    case -1: patch_tiles<Q, MK, M8, PAGED, -1, OUT>(c, cm, sV, sph2, t0, s1, A, USE); break; \
+    default: patch_tiles<Q, MK, M8, PAGED, 0, OUT>(c, cm, sV, sph2, t0, s1, A, USE); break;  \
   }
 
   if (PAGED || OUT == 2) __syncthreads();  // staged block tables
   if constexpr (!TAIL) {
     const int ntiles = (int)((c.t1 - c.tb0 + 15) >> 4);
-    // The wave's first tiles are loaded before anything else, so their HBM latency
+    // The wave's first tile is loaded before anything else, so its HBM latency
     // overlaps the chunk lookup, the LDS staging and the barrier.
-    TileSet<Q, MK, TU> pre;
-    load_tiles<Q, MK, M8, PAGED, TU, OUT>(c, cm, c.wave, ntiles, c.tb0, c.t1, pre);
+    Tile<Q, MK> A;
+    load_tile<Q, MK, M8, PAGED, OUT>(c, cm, c.wave, ntiles, c.tb0, c.t1, A);
     const ChunkRef ck = find_chunk_wave(cm, c.tb0);
     const int64_t t0 = c.tb0, s1 = min(c.t1, ck.end);
     if (s1 <= t0) return;  // offsets that do not cover the group: nothing here
     // Tokens past the chunk's end belong to the tail kernel.
 #pragma unroll
-    for (int u = 0; u < TU; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (c.tb0 + 16 * (c.wave + kWavesPerBlock * u) + 4 * c.g + i >= s1) pre.off[u][i] = -1;
+    for (int i = 0; i < 4; ++i)
+      if (c.tb0 + 16 * c.wave + 4 * c.g + i >= s1) A.off[i] = kOob;
     const bool rotate = r > 0 && ck.delta != 0;
     stage(ck, rotate);
     __syncthreads();
-    KAMERA_PATCH_SWITCH(pre, true)
+    KAMERA_PATCH_SWITCH(true)
   } else {
     // The remaining chunks of the group, one after the other.
-    TileSet<Q, MK, TU> none;
+    Tile<Q, MK> A;
     int64_t t0 = start;
     ChunkRef ck = find_chunk_wave(cm, t0, from);
     bool staged = false;
@@ -916,7 +947,7 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
         staged = true;
         stage(ck, rotate);
         __syncthreads();
-        KAMERA_PATCH_SWITCH(none, false)
+        KAMERA_PATCH_SWITCH(false)
       }
       t0 = max(t0, s1);
       if (t0 >= c.t1 || ck.j + 1 >= cm.num_chunks) break;
@@ -1080,7 +1111,7 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
 }
 
 hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonArgs& cm_in,
-                                      int tile_unroll, hipStream_t s) {
+                                      hipStream_t s) {
   ChanArgs c0 = ch[0];
   ChanArgs c1 = nch > 1 ? ch[1] : ch[0];
   if (nch == 1) c1.blocks = 0;
@@ -1098,23 +1129,21 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
   if (out > 0 && (!m8 || (nch > 1 && c1.out == nullptr))) return hipErrorInvalidValue;
   if (out == 0 && mk == 0) return hipErrorInvalidValue;
   if (q && !m8) return hipErrorInvalidValue;
-#define KAMERA_LAUNCH_K(Q, MK, M8, PG, TU, TL, OUT, XG)                                           \
-  hipLaunchKernelGGL((relocate_patch_rows<Q, MK, M8, PG, TU, TL, OUT>), grid, dim3(kBlock), 0, s, \
+#define KAMERA_LAUNCH_K(Q, MK, M8, PG, TL, OUT, XG)                                           \
+  hipLaunchKernelGGL((relocate_patch_rows<Q, MK, M8, PG, TL, OUT>), grid, dim3(kBlock), 0, s, \
                      c0, c1, cm, bpl, XG)
-#define KAMERA_LAUNCH_IN(MK, PG, TL, XG)                                                       \
-  do {                                                                                         \
-    if (q && tile_unroll == 2 && !TL) KAMERA_LAUNCH_K(true, MK, true, PG, 2, false, 0, XG);    \
-    else if (q) KAMERA_LAUNCH_K(true, MK, true, PG, 1, TL, 0, XG);                             \
-    else if (m8 && tile_unroll == 2 && !TL) KAMERA_LAUNCH_K(false, MK, true, PG, 2, false, 0, XG); \
-    else if (m8) KAMERA_LAUNCH_K(false, MK, true, PG, 1, TL, 0, XG);                           \
-    else KAMERA_LAUNCH_K(false, MK, false, PG, 1, TL, 0, XG);                                  \
+#define KAMERA_LAUNCH_IN(MK, PG, TL, XG)                                      \
+  do {                                                                        \
+    if (q) KAMERA_LAUNCH_K(true, MK, true, PG, TL, 0, XG);                    \
+    else if (m8) KAMERA_LAUNCH_K(false, MK, true, PG, TL, 0, XG);             \
+    else KAMERA_LAUNCH_K(false, MK, false, PG, TL, 0, XG);                    \
   } while (0)
 #define KAMERA_LAUNCH_OUT(MK, PG, TL, XG)                                     \
   do {                                                                        \
-    if (q && out == 1) KAMERA_LAUNCH_K(true, MK, true, PG, 1, TL, 1, XG);     \
-    else if (q) KAMERA_LAUNCH_K(true, MK, true, PG, 1, TL, 2, XG);            \
-    else if (out == 1) KAMERA_LAUNCH_K(false, MK, true, PG, 1, TL, 1, XG);    \
-    else KAMERA_LAUNCH_K(false, MK, true, PG, 1, TL, 2, XG);                  \
+    if (q && out == 1) KAMERA_LAUNCH_K(true, MK, true, PG, TL, 1, XG);        \
+    else if (q) KAMERA_LAUNCH_K(true, MK, true, PG, TL, 2, XG);               \
+    else if (out == 1) KAMERA_LAUNCH_K(false, MK, true, PG, TL, 1, XG);       \
+    else KAMERA_LAUNCH_K(false, MK, true, PG, TL, 2, XG);                     \
   } while (0)
 #define KAMERA_LAUNCH_PG(MK, TL, XG)                                          \
   do {                                                                        \
