@@ -165,6 +165,19 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 2 * nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
+    # In-place elementwise reference of the same size: a framework kernel that reads and
+    # writes the same bytes, as the relocate kernels do.
+    x = torch.ones(nb // 2, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        x.mul_(1.0)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(10):
+        x.mul_(1.0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    inplace_gbps = 2 * nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x
 
     # Warmup.
     for s in range(args.warmup):
@@ -229,6 +242,7 @@ def main():
         "pass_gbps": [round(bytes_pass[i] / (pass_ms[i] * 1e-3) / 1e9, 1) for i in range(len(ranks))],
         "kernels": [[K.KERNEL_NAMES[k] for k in pi.kernel] for pi in plan_info],
         "copy_kernel_gbps": round(copy_gbps, 1),
+        "inplace_kernel_gbps": round(inplace_gbps, 1),
         "roofline": {
             "bound": "hbm",
             "kernel": "relocate_patch_rows" if ranks[dominant] > 0 else "rotate_rows",
