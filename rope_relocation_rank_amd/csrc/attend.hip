@@ -151,6 +151,7 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8_t& hi, bf16x8
 template <int MKX>
 struct TileRows {
   u32x4_t k[4], v[4], uk[MKX], uv[MKX];
+  bool on;  // the lane's token (tb + c16) has a row in the segment
 };
 
 // Two mappings of the work, chosen by what measured faster on each layout:
@@ -214,14 +215,24 @@ __global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves) void attend_til
   const uint32_t P = (uint32_t)a.page_size;
   const int psh = (P != 0u && (P & (P - 1u)) == 0u) ? __builtin_ctz(P) : -1;
 
+  // Block-table entry of token t (paged), -1 when t lies at or past `end` or its page
+  // id is out of range.  A tile's entries are read one tile ahead, so the row loads of
+  // a tile never wait on the table.
+  auto page_of = [&](int64_t t, int64_t end) -> int32_t {
+    if (!PAGED || t >= end) return -1;
+    const uint32_t tt = (uint32_t)t;
+    const uint32_t pi = psh >= 0 ? tt >> psh : tt / P;
+    const int32_t pg = a.block_table[pi];
+    return (pg < 0 || pg >= a.num_pages) ? -1 : pg;
+  };
   // Row offsets of token t in the K and V channels inside the layer (32-bit: the host
-  // checks the extents); false when the token has no slot.
-  auto slot = [&](int64_t t, uint32_t& off_k, uint32_t& off_v) -> bool {
+  // checks the extents), given its block-table entry pg when paged; false when the
+  // token has no slot.
+  auto slot = [&](int64_t t, int32_t pg, uint32_t& off_k, uint32_t& off_v) -> bool {
     const uint32_t tt = (uint32_t)t;
     if constexpr (PAGED) {
+      if (pg < 0) return false;
       const uint32_t pi = psh >= 0 ? tt >> psh : tt / P, si = tt - pi * P;
-      const int32_t pg = a.block_table[pi];
-      if (pg < 0 || pg >= a.num_pages) return false;
       off_k = (uint32_t)pg * ps0 + si * ss0;
       off_v = (uint32_t)pg * ps1 + si * ss1;
     } else {
@@ -242,11 +253,13 @@ __global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves) void attend_til
       const int64_t s1 = min(t_hi, a.offsets[j + 1]);
       if (s1 <= t0) break;  // offsets that do not cover the range: nothing more here
 
-      // Loads the rows of tile ti (token tb + c16, 8 consecutive features per step).
-      auto load = [&](int ti, TileRows<MKX>& R) {
+      // Loads the rows of tile ti (token tb + c16, 8 consecutive features per step);
+      // pg is that token's block-table entry when paged.
+      auto load = [&](int ti, int32_t pg, TileRows<MKX>& R) {
         const int64_t tr = t0 + 16 * (int64_t)ti + c16;
         uint32_t off_k = 0, off_v = 0;
-        const bool row_on = tr < s1 && slot(tr, off_k, off_v);
+        const bool row_on = tr < s1 && slot(tr, pg, off_k, off_v);
+        R.on = row_on;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           R.k[ks] = u32x4_t{0u, 0u, 0u, 0u};
@@ -267,8 +280,15 @@ __global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves) void attend_til
         }
       };
       const int ntiles = (int)((s1 - t0 + 15) >> 4);
+      auto tile_page = [&](int ti) -> int32_t {
+        return ti < ntiles ? page_of(t0 + 16 * (int64_t)ti + c16, s1) : -1;
+      };
       TileRows<MKX> cur;
-      if (PF && ti_first < ntiles) load(ti_first, cur);
+      int32_t pg_cur = tile_page(ti_first);
+      if (PF && ti_first < ntiles) {
+        load(ti_first, pg_cur, cur);
+        pg_cur = tile_page(ti_first + ti_step);
+      }
 
       // B operands: this lane's query head (column c16), features 32 ks + 8 grp ...
       bf16x8_t qh[4], ql[4], wh[MKX], wl[MKX];
@@ -303,10 +323,14 @@ __global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves) void attend_til
       for (int ti = ti_first; ti < ntiles; ti += ti_step) {
         const int64_t tb = t0 + 16 * (int64_t)ti;
         TileRows<MKX> nxt;
+        int32_t pg_nxt;
         if constexpr (PF) {
-          if (ti + ti_step < ntiles) load(ti + ti_step, nxt);
+          // pg_cur holds the entry of tile ti + ti_step here
+          if (ti + ti_step < ntiles) load(ti + ti_step, pg_cur, nxt);
+          pg_nxt = tile_page(ti + 2 * ti_step);
         } else {
-          load(ti, cur);
+          load(ti, pg_cur, cur);
+          pg_nxt = tile_page(ti + ti_step);
         }
         // Scores of tokens tb + 4 grp + i (i < 4) for query head c16.
         f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -331,14 +355,16 @@ __global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves) void attend_til
 #pragma unroll
         for (int ku = 0; ku < MK; ++ku)
           if (32 * ku + 8 * grp < m) *(u32x4_t*)(su + c16 * kURow + 32 * ku + 8 * grp) = cur.uv[ku];
-        // Mask tokens past the segment or without a slot.
+        // Mask tokens past the segment or without a slot.  Paged: bit c16 of the ballot
+        // (lanes 0..15) says whether token tb + c16 loaded a row.
         float s4[4];
+        if constexpr (PAGED) {
+          const uint32_t onm = (uint32_t)__ballot(cur.on) & 0xffffu;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t t = tb + 4 * grp + i;
-          uint32_t o0, o1;
-          const bool on = t < s1 && (!PAGED || slot(t, o0, o1));
-          s4[i] = on ? sc[i] : -INFINITY;
+          for (int i = 0; i < 4; ++i) s4[i] = (onm >> (4 * grp + i)) & 1u ? sc[i] : -INFINITY;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s4[i] = tb + 4 * grp + i < s1 ? sc[i] : -INFINITY;
         }
         float mt = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
         mt = max_xor(mt, 16);
@@ -386,6 +412,7 @@ __global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves) void attend_til
           uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, uacc[ub], 0, 0, 0);
         }
         if constexpr (PF) cur = nxt;
+        pg_cur = pg_nxt;
       }
       // The four lane groups of a column hold disjoint tokens' sums.
       lrun += __shfl_xor(lrun, 16);
