@@ -167,7 +167,8 @@ struct TileRows {
 // the second mapping); PF: the next tile's rows are loaded before the current tile is
 // worked (the second register tile lowers occupancy, which pays at one rank step only).
 template <int MK, bool PAGED, bool PF>
-__global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves) void attend_tiles(AttendArgs a) {
+__global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves)
+__attribute__((amdgpu_waves_per_eu(!PAGED ? 1 : MK == 0 ? 4 : MK == 2 ? 3 : 1))) void attend_tiles(AttendArgs a) {
   constexpr int MKX = MK > 0 ? MK : 1;
   constexpr int MU = 2 * MK;               // 16-wide rank blocks of the U_V sums
   constexpr int MUX = MU > 0 ? MU : 1;
@@ -175,10 +176,16 @@ __global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves) void attend_til
   constexpr int kTileBytes = 16 * (kVRow + kURow) * 2;  // per-wave V and U_V tiles
   // Paged mapping: the tiles' LDS is reused for the merge of the four waves.
   constexpr int kMergeFloats = kWaves * kAttendMaxGroup * (2 + kD + 128);
-  constexpr int kLds = ROWS ? kTileWaves * kTileBytes
-                            : (kWaves * kTileBytes > kMergeFloats * 4 ? kWaves * kTileBytes
-                                                                       : kMergeFloats * 4);
+  constexpr int kLdsTiles = ROWS ? kTileWaves * kTileBytes
+                                 : (kWaves * kTileBytes > kMergeFloats * 4 ? kWaves * kTileBytes
+                                                                            : kMergeFloats * 4);
+  // Paged mapping: the four waves run one KV head, so the query-side B operands (high
+  // and low parts of the rotated query and of V_K^T q) are the same for all of them and
+  // sit once in LDS after the tiles, read per tile instead of held in 48 registers.
+  constexpr int kBOps = 8 + 2 * MKX;  // 16-byte operands per lane
+  constexpr int kLds = kLdsTiles + (PAGED ? kBOps * 64 * 16 : 0);
   __shared__ __align__(16) unsigned char lds[kLds];
+  u32x4_t* sB = (u32x4_t*)(lds + kLdsTiles);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -292,6 +299,13 @@ __global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves) void attend_til
 
       // B operands: this lane's query head (column c16), features 32 ks + 8 grp ...
       bf16x8_t qh[4], ql[4], wh[MKX], wl[MKX];
+      // Operand o of this lane (paged: from LDS).  Every wave writes the same values
+      // for the segment, and reads only after its own writes; the previous segment's
+      // readers all passed the barrier that ends it.
+      auto bop = [&](int o, const bf16x8_t& r) -> bf16x8_t {
+        if constexpr (PAGED) return __builtin_bit_cast(bf16x8_t, sB[o * 64 + lane]);
+        return r;
+      };
       {
         const float* qp = a.qw + (((int64_t)l * n + j) * Hq + g * gq + (hv ? c16 : 0)) * W;
 #pragma unroll
@@ -310,6 +324,18 @@ __global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves) void attend_til
             x[e] = (MK > 0 && hv && k < m) ? qp[kD + k] : 0.f;
           }
           split8(x, wh[ku], wl[ku]);
+        }
+        if constexpr (PAGED) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            sB[ks * 64 + lane] = __builtin_bit_cast(u32x4_t, qh[ks]);
+            sB[(4 + ks) * 64 + lane] = __builtin_bit_cast(u32x4_t, ql[ks]);
+          }
+#pragma unroll
+          for (int ku = 0; ku < MKX; ++ku) {
+            sB[(8 + ku) * 64 + lane] = __builtin_bit_cast(u32x4_t, wh[ku]);
+            sB[(8 + MKX + ku) * 64 + lane] = __builtin_bit_cast(u32x4_t, wl[ku]);
+          }
         }
       }
 
@@ -337,14 +363,14 @@ __global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves) void attend_til
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const bf16x8_t A = __builtin_bit_cast(bf16x8_t, cur.k[ks]);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qh[ks], sc, 0, 0, 0);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, ql[ks], sc, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(ks, qh[ks]), sc, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(4 + ks, ql[ks]), sc, 0, 0, 0);
         }
 #pragma unroll
         for (int ku = 0; ku < MK; ++ku) {
           const bf16x8_t A = __builtin_bit_cast(bf16x8_t, cur.uk[ku]);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wh[ku], sc, 0, 0, 0);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wl[ku], sc, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(8 + ku, wh[ku]), sc, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(8 + MKX + ku, wl[ku]), sc, 0, 0, 0);
         }
         // The V and U_V rows go to this wave's LDS tile (row c16) for the transposed
         // reads; the wave's previous reads of the tile come before these writes in
