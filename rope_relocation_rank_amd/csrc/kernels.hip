@@ -1119,8 +1119,11 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
   cm.tail_mode = 0;
   int64_t bpl = c0.blocks + c1.blocks;
   dim3 grid((unsigned)((int64_t)cm.num_layers * bpl));
-  // XCD grouping needs one feature-block count for every channel of the launch.
-  const int xg = (nch == 1 || c0.fblocks == c1.fblocks) ? c0.fblocks : 0;
+  // XCD grouping by the larger feature-block count of the launch's channels: a token
+  // group's blocks of that channel land on one XCD; a channel with one block per group
+  // (MLA's k_rope beside c_KV) then gets runs of consecutive token groups per XCD.  The
+  // numbering is a bijection for any group size.
+  const int xg = nch == 1 ? c0.fblocks : (c0.fblocks > c1.fblocks ? c0.fblocks : c1.fblocks);
   const int mk = (cm.rank + 31) / 32;
   const bool m8 = cm.rank % 8 == 0;
   // Out of place (recall): 1 contiguous destination, 2 paged destination.
