@@ -310,6 +310,24 @@ def test_kernel_choice():
     assert names == ["rotate+patch mfma"] * 2
 
 
+def test_buffer_range_limits():
+    # The tuned kernels reach one layer of a channel, and one layer of U, through a
+    # buffer resource with 32-bit byte offsets: each may span at most 2^31 - 64 bytes.
+    # One head of 128 bf16 per token: a layer spans 256 * T bytes.
+    t_max = ((1 << 31) - 64) // 256
+    for m, tuned in ((32, "rotate+patch mfma"), (0, "rotate")):
+        names, _ = plan_names(*gqa(T=t_max, L=1, H=1, D=128, r=128, m=m))
+        assert names[0] == tuned
+        names, _ = plan_names(*gqa(T=t_max + 1, L=1, H=1, D=128, r=128, m=m))
+        assert names[0] == "generic"
+    # Small rows, large U: 2^25 tokens of 16 bf16 (1 GiB per layer) fit, but U fits only
+    # while 2^25 * m * 2 <= 2^31 - 64.
+    names, _ = plan_names(*gqa(T=1 << 25, L=1, H=1, D=16, r=16, m=8))
+    assert names == ["rotate+patch mfma"] * 2
+    names, _ = plan_names(*gqa(T=1 << 25, L=1, H=1, D=16, r=16, m=32))
+    assert names == ["generic", "generic"]
+
+
 def test_mfma_workgroup_count():
     # One workgroup = one 128-feature block of one channel and layer over
     # tokens_per_unit tokens (a multiple of the 64 tokens four 16-token tiles cover).
