@@ -10,8 +10,9 @@ before the timed region; steps cycle through `--copies` independent input copies
 Prints one JSON line.  value = algorithmic bytes moved per step (every touched KV
 element read once and written once, every factor element read once) x steps / wall
 time of the timed steps, in GB/s (1e9); no event is recorded between those launches.
-roofline = the dominant kernel (the relocate+patch launch): the same steps run again
-with HIP events bracketing every launch on its stream give its average launch time.
+roofline = the dominant kernel (the relocate+patch launch): its launches of the timed
+steps, run again back to back between two HIP events on its stream, give its average
+launch time.
 cpu_baseline = the fp64 CPU oracle on the host cores over a bounded sample of the same
 workload.
 
@@ -198,19 +199,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # Per-launch durations: the same steps again, with HIP events bracketing every
-    # launch of every pass on the launch stream (the roofline's average launch time).
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)] for _ in ranks]
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        for pi in range(len(ranks)):
-            a, b = ev[pi][s]
-            a.record(stream)
+    # Average launch time of each pass (the roofline's): the same launches again, each
+    # pass's `steps` launches back to back between one pair of HIP events on the launch
+    # stream.
+    pass_ms = []
+    for pi in range(len(ranks)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for s in range(args.steps):
             launch(pi, s % copies)
-            b.record(stream)
-    torch.cuda.synchronize()
-    pass_ms = [sum(a.elapsed_time(b) for a, b in ev[pi]) / args.steps for pi in range(len(ranks))]
+        b.record(stream)
+        torch.cuda.synchronize()
+        pass_ms.append(a.elapsed_time(b) / args.steps)
 
     ms_step = wall * 1e3 / args.steps
     value = bytes_step * args.steps / wall / 1e9
@@ -265,7 +266,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": bytes_pass[dominant],
             "avg_launch_ms": round(dom_ms, 5),
-            "timing": "HIP events around each launch, in a second pass over the same steps",
+            "timing": "HIP events around the pass's launches of the timed steps, rerun back to back",
         },
         "cpu_baseline": cpu,
     }
