@@ -77,6 +77,7 @@ struct Plan {
   int block_tokens = 0;
   int tiles_per_wave = 0;
   int rotate_unroll = 2;
+  int valu = 0;  // rotate+patch in place: patch on VALU (measurement variant)
   int64_t units = 0;  // workgroups of the tuned launch(es)
 };
 
@@ -143,6 +144,9 @@ void plan_mfma(const kamera_kv_desc& kv, const kamera_chunks& ch, int m, const b
   if (tpw < 1 || tpw > kamera::kMaxBlockTokens / 64) tpw = dflt;
   plan->tiles_per_wave = tpw;
   plan->block_tokens = 64 * tpw;
+  // KAMERA_PATCH_VALU=1 selects the VALU form of the patch (bf16 in place, rank <= 64)
+  // for the MFMA-versus-VALU comparison; the tuned default is MFMA.
+  plan->valu = env_int("KAMERA_PATCH_VALU", 0) != 0;
   // A second launch covers the token groups that chunk boundaries cut.
   const int64_t T = ch.total_tokens;
   const int64_t groups = ceil_div(T, plan->block_tokens);
@@ -396,7 +400,7 @@ kamera_status run(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamer
   }
   if (ntuned > 0) {
     const hipError_t e =
-        kamera::launch_relocate_patch_rows(tuned, ntuned, cm, stream);
+        kamera::launch_relocate_patch_rows(tuned, ntuned, cm, plan.valu, stream);
     if (e != hipSuccess) return hip_fail(e, "relocate+patch launch");
   }
   return KAMERA_OK;
@@ -542,7 +546,7 @@ kamera_status run_recall(const kamera_kv_desc* src, const kamera_kv_desc* dst,
   }
   if (ntuned > 0) {
     const hipError_t e =
-        kamera::launch_relocate_patch_rows(tuned, ntuned, cm, stream);
+        kamera::launch_relocate_patch_rows(tuned, ntuned, cm, plan.valu, stream);
     if (e != hipSuccess) return hip_fail(e, "recall launch");
   }
   return KAMERA_OK;

@@ -168,7 +168,7 @@ struct TileRows {
 // worked (the second register tile lowers occupancy, which pays at one rank step only).
 template <int MK, bool PAGED, bool PF>
 __global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves)
-__attribute__((amdgpu_waves_per_eu(!PAGED ? 1 : MK == 0 ? 4 : MK == 2 ? 3 : 1))) void attend_tiles(AttendArgs a) {
+__attribute__((amdgpu_waves_per_eu(PAGED && MK == 2 ? 3 : 1))) void attend_tiles(AttendArgs a) {
   constexpr int MKX = MK > 0 ? MK : 1;
   constexpr int MU = 2 * MK;               // 16-wide rank blocks of the U_V sums
   constexpr int MUX = MU > 0 ? MU : 1;

@@ -137,8 +137,10 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
 // With ChanArgs::out set it runs out of place (rank % 8 == 0; rank 0 allowed).
 // Covers nch (1 or 2) channels in one launch, plus a second launch for the token groups
 // that chunk boundaries cut when there is more than one chunk.
+// valu: the head launch of a bf16 in-place call with rank <= 64 (a multiple of 8) takes
+// the patch on VALU instead of MFMA (a measurement variant).
 hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonArgs& cm,
-                                      hipStream_t s);
+                                      int valu, hipStream_t s);
 
 // Plain per-row kernel: any dim, even rope_dim, rank <= KAMERA_MAX_RANK, bf16, fp32 or
 // fp8, element-aligned pointers.  In place with rank 0 it only touches rotated dims; out of

@@ -650,11 +650,48 @@ __device__ __forceinline__ void load_tile(const PatchCtx<Q>& c, const CommonArgs
 // one FMA finishes each element; at larger MK, where the rotated values cannot stay
 // live beside the accumulators without spilling, the accumulator starts at s * rotated
 // and the sum is multiplied by 1/s.
+// Rotated (or unrotated) values r0, r1 of features 2pp, 2pp + 1 of the lane's 4 tokens,
+// and whether each of the two features turns.  Phases sit in LDS as (cos, sin) per
+// rotary pair; with M-RoPE sections a pair whose section delta is 0 has sin exactly 0
+// and is not rotated.
+template <bool Q, int HX>
+__device__ __forceinline__ void rotate_pair(const PatchCtx<Q>& c, const float4* sph2,
+                                            const typename Codec<Q>::XV (&x)[4], int pp,
+                                            float (&r0)[4], float (&r1)[4], bool& turn0,
+                                            bool& turn1) {
+  using P = Codec<Q>;
+  const float2* sph = reinterpret_cast<const float2*>(sph2);
+  float4 ph = make_float4(1.f, 0.f, 1.f, 0.f);
+  if constexpr (HX > 0) ph = sph2[(c.fi0 >> 1) + pp];
+  if constexpr (HX < 0) {
+    const float2 q = sph[(c.fi0 >> 1) + pp];
+    ph = make_float4(q.x, q.y, q.x, q.y);
+  }
+  turn0 = HX != 0 && c.rot_lane && !(c.mixed && ph.y == 0.f);
+  turn1 = HX != 0 && c.rot_lane && !(c.mixed && ph.w == 0.f);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = P::word(x[i], pp);
+    const float2 av = P::pair(w, pp);
+    const float a0 = av.x, a1 = av.y;
+    float y0 = a0, y1 = a1;
+    if constexpr (HX > 0) {
+      const float2 bv = P::pair(lane_xor<HX>(w), pp);
+      y0 = fmaf(a0, ph.x, bv.x * (c.sgn * ph.y));
+      y1 = fmaf(a1, ph.z, bv.y * (c.sgn * ph.w));
+    } else if constexpr (HX < 0) {
+      y0 = fmaf(a0, ph.x, -(a1 * ph.y));
+      y1 = fmaf(a1, ph.x, a0 * ph.y);
+    }
+    r0[i] = turn0 ? y0 : a0;
+    r1[i] = turn1 ? y1 : a1;
+  }
+}
+
 template <bool Q, int MK, int HX, int OUT>
 __device__ __forceinline__ void finish_tile(const PatchCtx<Q>& c, const u32x4_t* sV,
                                             const float4* sph2, Tile<Q, MK>& T) {
   using P = Codec<Q>;
-  const float2* sph = reinterpret_cast<const float2*>(sph2);
   {
     // bf16: feature pair pp of a row is one word, read (with the partner lane's word)
     // before its result is written, so results overwrite the loaded words.  fp8 packs
@@ -663,33 +700,9 @@ __device__ __forceinline__ void finish_tile(const PatchCtx<Q>& c, const u32x4_t*
     typename P::XV* out = Q ? outq : T.x;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {  // features 2pp, 2pp + 1 of the lane's 8
-      // (cos, sin) of the pairs of the two features, and whether each one turns.
-      float4 ph = make_float4(1.f, 0.f, 1.f, 0.f);
-      if constexpr (HX > 0) ph = sph2[(c.fi0 >> 1) + pp];
-      if constexpr (HX < 0) {
-        const float2 q = sph[(c.fi0 >> 1) + pp];
-        ph = make_float4(q.x, q.y, q.x, q.y);
-      }
-      const bool turn0 = HX != 0 && c.rot_lane && !(c.mixed && ph.y == 0.f);
-      const bool turn1 = HX != 0 && c.rot_lane && !(c.mixed && ph.w == 0.f);
-      float r0[4], r1[4];  // rotated (or unrotated) values of the two features
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = P::word(T.x[i], pp);
-        const float2 av = P::pair(w, pp);
-        const float a0 = av.x, a1 = av.y;
-        float y0 = a0, y1 = a1;
-        if constexpr (HX > 0) {
-          const float2 bv = P::pair(lane_xor<HX>(w), pp);
-          y0 = fmaf(a0, ph.x, bv.x * (c.sgn * ph.y));
-          y1 = fmaf(a1, ph.z, bv.y * (c.sgn * ph.w));
-        } else if constexpr (HX < 0) {
-          y0 = fmaf(a0, ph.x, -(a1 * ph.y));
-          y1 = fmaf(a1, ph.x, a0 * ph.y);
-        }
-        r0[i] = turn0 ? y0 : a0;
-        r1[i] = turn1 ? y1 : a1;
-      }
+      float r0[4], r1[4];
+      bool turn0, turn1;
+      rotate_pair<Q, HX>(c, sph2, T.x, pp, r0, r1, turn0, turn1);
       if constexpr (MK == 0) {
         // No patch (out of place only): rotated dims are rounded once, every other
         // element is copied bit for bit.
@@ -728,25 +741,86 @@ __device__ __forceinline__ void finish_tile(const PatchCtx<Q>& c, const u32x4_t*
   }
 }
 
+// The same tile with the patch on VALU instead of MFMA (bf16 in place; a measurement
+// variant for the MFMA-versus-VALU comparison): the rank-m sum of the lane's 4 tokens x
+// 8 features is taken with v_dot2_f32_bf16 (two bf16 products per instruction, fp32
+// accumulation) from the tile's U rows, written per wave to LDS from the A fragments
+// (lane (c16, g) holds U[c16][32 ks + 8 g ...]), and the staged V rows (the B fragment
+// of feature n, rank step ks, lane group g holds V[n][32 ks + 8 g ...]).
+template <int MK, int HX>
+__device__ __forceinline__ void finish_tile_valu(const PatchCtx<false>& c, const u32x4_t* sV,
+                                                 const float4* sph2, u32x4_t* sUw,
+                                                 Tile<false, MK>& T) {
+  using P = Codec<false>;
+  constexpr int UR = 4 * MK + 1;  // 16-byte words per staged U row (+1 spreads banks)
+#pragma unroll
+  for (int ks = 0; ks < MK; ++ks) sUw[c.c16 * UR + 4 * ks + c.g] = T.a[ks];
+  float acc[4][8];  // token 4g + i, feature 8c16 + e
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    float r0[4], r1[4];
+    bool turn0, turn1;
+    rotate_pair<false, HX>(c, sph2, T.x, pp, r0, r1, turn0, turn1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i][2 * pp] = r0[i];
+      acc[i][2 * pp + 1] = r1[i];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4 * MK; ++q) {  // rank steps of 8
+    if (8 * q >= c.m) break;
+    u32x4_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = sUw[(4 * c.g + i) * UR + q];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const u32x4_t v = sV[(e * MK + (q >> 2)) * 64 + (q & 3) * 16 + c.c16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // Words go through scalars: a bit cast taken directly of a vector element
+          // (u[i][w]) reads element 0 for every w with this compiler.
+          const uint32_t uw = u[i][w], vw = v[w];
+          acc[i][e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, uw),
+                                                      __builtin_bit_cast(bf16x2_t, vw),
+                                                      acc[i][e], false);
+        }
+    }
+  }
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) P::put(T.x[i], pp, acc[i][2 * pp], acc[i][2 * pp + 1]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bstore_nt(c.rkv, T.off[i], T.x[i]);
+}
+
 // The wave's 16-token tiles (kt = wave mod 4, kt + 4, ...) that meet [t0, s1), one at a
 // time; only tokens in [t0, s1) are loaded and stored.  When `use_pre`, A already holds
 // the wave's first tile (loaded before the workgroup staged the chunk).
-template <bool Q, int MK, bool M8, bool PAGED, int HX, int OUT>
+// VALU: the patch on VALU (finish_tile_valu, with the wave's U staging area sUw).
+template <bool Q, int MK, bool M8, bool PAGED, int HX, int OUT, bool VALU>
 __device__ __forceinline__ void patch_tiles(const PatchCtx<Q>& c, const CommonArgs& cm,
                                             const u32x4_t* sV, const float4* sph2,
-                                            int64_t t0, int64_t s1, Tile<Q, MK>& A,
-                                            bool use_pre) {
+                                            u32x4_t* sUw, int64_t t0, int64_t s1,
+                                            Tile<Q, MK>& A, bool use_pre) {
   constexpr int W = kWavesPerBlock;
   const int k_lo = (int)((t0 - c.tb0) >> 4);
   const int k_hi = (int)((s1 - c.tb0 + 15) >> 4);
   int kt = k_lo + ((c.wave - k_lo) % W + W) % W;
+  auto finish = [&]() {
+    if constexpr (VALU) finish_tile_valu<MK, HX>(c, sV, sph2, sUw, A);
+    else finish_tile<Q, MK, HX, OUT>(c, sV, sph2, A);
+  };
   if (use_pre) {
-    finish_tile<Q, MK, HX, OUT>(c, sV, sph2, A);
+    finish();
     kt += W;
   }
   for (; kt < k_hi; kt += W) {
     load_tile<Q, MK, M8, PAGED, OUT>(c, cm, kt, k_hi, t0, s1, A);
-    finish_tile<Q, MK, HX, OUT>(c, sV, sph2, A);
+    finish();
   }
 }
 
@@ -767,8 +841,9 @@ __device__ __forceinline__ void patch_tiles(const PatchCtx<Q>& c, const CommonAr
 //
 // OUT != 0 is the out-of-place form (recall): rows are read through the source layout
 // and whole result rows written through the destination layout (OUT 1 contiguous, 2
-// paged); MK = 0 is its no-patch form.  Q: fp8 E4M3 elements (bf16 factors).
-template <bool Q, int MK, bool M8, bool PAGED, bool TAIL, int OUT>
+// paged); MK = 0 is its no-patch form.  Q: fp8 E4M3 elements (bf16 factors).  VALU
+// (bf16 in place, head launch): the patch on VALU instead of MFMA, for measurement.
+template <bool Q, int MK, bool M8, bool PAGED, bool TAIL, int OUT, bool VALU = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAIL || MK > 2 || (MK == 2 && OUT != 0) ? 1 : 4)))
 void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t blocks_per_layer,
                          int xcd_group) {
@@ -776,7 +851,9 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
   __shared__ float4 sph2[kMaxTunedHalf / 2];  // (cos, sin) of pairs 2p and 2p + 1
   __shared__ int sbt[kMaxBlockTokens + 1];
   __shared__ int osbt[OUT == 2 ? kMaxBlockTokens + 1 : 1];
+  __shared__ u32x4_t sUv[VALU ? kWavesPerBlock * 16 * (4 * MK + 1) : 1];
   const int lane = threadIdx.x & 63;
+  u32x4_t* sUw = sUv + (VALU ? (threadIdx.x >> 6) * 16 * (4 * MK + 1) : 0);
 
   // Logical workgroup index: groups of 8 * xcd_group ids are permuted so that XCD x
   // gets xcd_group consecutive logical blocks (one token group's feature blocks).
@@ -905,14 +982,14 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
       reinterpret_cast<float2*>(sph2)[threadIdx.x] =
           phase_of(KAMERA_CH(omega[threadIdx.x]), pair_delta(cm, ck, threadIdx.x));
   };
-#define KAMERA_PATCH_SWITCH(USE)                                                             \
-  switch (rotate ? hx : 0) {                                                                 \
-    case 1: patch_tiles<Q, MK, M8, PAGED, 1, OUT>(c, cm, sV, sph2, t0, s1, A, USE); break;   \
-    case 2: patch_tiles<Q, MK, M8, PAGED, 2, OUT>(c, cm, sV, sph2, t0, s1, A, USE); break;   \
-    case 4: patch_tiles<Q, MK, M8, PAGED, 4, OUT>(c, cm, sV, sph2, t0, s1, A, USE); break;   \
-    case 8: patch_tiles<Q, MK, M8, PAGED, 8, OUT>(c, cm, sV, sph2, t0, s1, A, USE); break;   \
-    case -1: patch_tiles<Q, MK, M8, PAGED, -1, OUT>(c, cm, sV, sph2, t0, s1, A, USE); break; \
-    default: patch_tiles<Q, MK, M8, PAGED, 0, OUT>(c, cm, sV, sph2, t0, s1, A, USE); break;  \
+#define KAMERA_PATCH_SWITCH(USE)                                                                   \
+  switch (rotate ? hx : 0) {                                                                       \
+    case 1: patch_tiles<Q, MK, M8, PAGED, 1, OUT, VALU>(c, cm, sV, sph2, sUw, t0, s1, A, USE); break;   \
+    case 2: patch_tiles<Q, MK, M8, PAGED, 2, OUT, VALU>(c, cm, sV, sph2, sUw, t0, s1, A, USE); break;   \
+    case 4: patch_tiles<Q, MK, M8, PAGED, 4, OUT, VALU>(c, cm, sV, sph2, sUw, t0, s1, A, USE); break;   \
+    case 8: patch_tiles<Q, MK, M8, PAGED, 8, OUT, VALU>(c, cm, sV, sph2, sUw, t0, s1, A, USE); break;   \
+    case -1: patch_tiles<Q, MK, M8, PAGED, -1, OUT, VALU>(c, cm, sV, sph2, sUw, t0, s1, A, USE); break; \
+    default: patch_tiles<Q, MK, M8, PAGED, 0, OUT, VALU>(c, cm, sV, sph2, sUw, t0, s1, A, USE); break;  \
   }
 
   if (PAGED || OUT == 2) __syncthreads();  // staged block tables
@@ -1111,7 +1188,7 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
 }
 
 hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonArgs& cm_in,
-                                      hipStream_t s) {
+                                      int valu, hipStream_t s) {
   ChanArgs c0 = ch[0];
   ChanArgs c1 = nch > 1 ? ch[1] : ch[0];
   if (nch == 1) c1.blocks = 0;
@@ -1138,6 +1215,10 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
 #define KAMERA_LAUNCH_IN(MK, PG, TL, XG)                                      \
   do {                                                                        \
     if (q) KAMERA_LAUNCH_K(true, MK, true, PG, TL, 0, XG);                    \
+    else if (m8 && valu && !TL && MK <= 2)                                    \
+      hipLaunchKernelGGL((relocate_patch_rows<false, MK, true, PG, false, 0,  \
+                                              (MK <= 2 && !TL)>),             \
+                         grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, XG);      \
     else if (m8) KAMERA_LAUNCH_K(false, MK, true, PG, TL, 0, XG);             \
     else KAMERA_LAUNCH_K(false, MK, false, PG, TL, 0, XG);                    \
   } while (0)
