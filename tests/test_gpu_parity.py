@@ -163,3 +163,36 @@ def test_delta_zero_rotation_only_is_untouched():
     after = [parity.host_bits(b) for b in inp.buffers]
     for a, b in zip(after, before):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("rank", [0, 64])
+def test_paged_skips_invalid_pages(rank):
+    # Tokens whose block-table entry is out of range (-1, or past the pool) are left
+    # untouched: the rows are skipped through the out-of-range buffer offset, so the
+    # pool pages the valid table gives those tokens keep their input bits, and every
+    # other token matches the oracle run with the valid table.
+    w = synth.get("long_video_72b_paged").with_(layers=2, tokens=300, pool_pages=40)
+    print(f"\n[case] paged, invalid page ids, rank={rank}", flush=True)
+    inp = synth.make_inputs(w, rank, device=DEV)
+    valid = np.asarray(inp.struct.block_table).copy()
+    bad = valid.copy()
+    bad[1], bad[4] = -1, 1 << 20
+    before = [parity.host_bits(b) for b in inp.buffers]
+    factors = ([parity.host_bits(u) for u in inp.U], [parity.host_bits(v) for v in inp.V])
+    inp.block_table_t = torch.as_tensor(bad, dtype=torch.int32, device=DEV)
+    ops.run(inp)
+    torch.cuda.synchronize()
+    got = [parity.host_bits(b) for b in inp.buffers]
+    out, y, s = parity.oracle_on_host(inp, before, factors)  # struct keeps the valid table
+    rep = parity.Report()
+    for c, lay in enumerate(inp.layouts):
+        b = lay["buffer"]
+        shape = (w.layers, 40, w.page_size, lay["heads"], lay["dim"])
+        for pg in (valid[1], valid[4]):  # skipped: input bits, compared bit for bit
+            out[b].reshape(shape)[:, pg] = before[b].reshape(shape)[:, pg]
+            s[b].reshape(shape)[:, pg] = -1.0
+            assert (got[b].reshape(shape)[:, pg] == before[b].reshape(shape)[:, pg]).all()
+    for g, o, yy, ss in zip(got, out, y, s):
+        parity.compare(g, o, yy, ss, inp.rank, rep)
+    print(f"[case] {rep}", flush=True)
+    assert rep.ok(), str(rep)
