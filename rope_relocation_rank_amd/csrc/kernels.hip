@@ -20,17 +20,23 @@
 //                        each 16-token group up to the end of its first chunk; a
 //                        tail launch (TAIL) covers the rest of groups that a chunk
 //                        boundary cuts.  OUT writes a destination cache.
+//                        Its VALU form (a measurement variant) sums the patch with
+//                        v_dot2_f32_bf16 instead.
 //   generic_rows         any shape, bf16 or fp32: one thread per (layer, token, head).
 //
-// Memory shape of the tuned kernels (what streams well on MI355X HBM3E): every load
-// and store is a 16-byte nontemporal access; 16 consecutive lanes cover one 256-byte
-// row of 128 features (or LPR lanes cover the rotated part of a row), so each wave
-// instruction touches whole 128-byte lines; a wavefront handles one or two 16-token
-// tiles and exits, so the lines in flight across the chip stay within a small
-// address window.  Per-chunk state (phases, feature factor V) is built once per
-// workgroup in LDS.  Angles: delta * omega_i is formed in fp64 with omega_i from the
-// host, reduced by 2 pi in fp64, and its cos and sin are rounded to fp32; all element
-// arithmetic is fp32 with one rounding to bf16 at the end.
+// Memory shape of the tuned kernels (what streams well on MI355X HBM3E): every KV load
+// and store is a 16-byte (fp8: 8-byte) nontemporal buffer access through a resource
+// over the current layer, with 32-bit byte offsets; a row a lane skips takes an offset
+// past the range, which the hardware turns into a zero load and a dropped store, so no
+// memory access sits behind a branch.  16 consecutive lanes cover one 256-byte row of
+// 128 features (or LPR lanes cover the rotated part of a row), so each wave
+// instruction touches whole 128-byte lines; a wavefront handles one to four 16-token
+// tiles and exits, and consecutive workgroups sweep one compact address range
+// together (the numbering keeps a token group's feature blocks on one XCD).  Per-chunk
+// state (phases, feature factor V) is built once per workgroup in LDS.  Angles:
+// delta * omega_i is formed in fp64 with omega_i from the host, reduced by pi/2 in
+// fp64, and its cos and sin are rounded to fp32; all element arithmetic is fp32 with
+// one rounding to bf16 at the end.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
