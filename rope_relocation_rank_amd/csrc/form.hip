@@ -606,6 +606,88 @@ __global__ __launch_bounds__(kThreads) void write_u(FormArgs P, int64_t p0, int6
   }
 }
 
+// U_m = Delta V_m on MFMA (v_mfma_f32_16x16x32_bf16): 64 tokens per workgroup
+// (blockIdx.x), wave w the 16-token tile w.  V_m (fp32, F x k at v_off) is split into
+// high and low bf16 parts (x - hi - lo <= 2^-17 |x|): the bf16 x bf16 products with
+// Delta are exact and accumulate in fp32, so the sums match the fp32 form above to
+// fp32 rounding.  Every 64 features the workgroup stages V_m's B fragments in LDS
+// (lane (c16, g) of column tile ct holds features 32 s + 8 g .. + 7 of column
+// 16 ct + c16); each lane loads its A fragment, 8 consecutive features of token c16 of
+// its wave's tile, straight from HBM (Delta rows 16-byte aligned).  Lane (c16, g) ends
+// with U rows 4 g .. 4 g + 3 of column 16 ct + c16.
+__global__ __launch_bounds__(kThreads) void write_u_mfma(FormArgs P, int64_t p0, int64_t v_off) {
+  constexpr int kSteps = 2;  // 32-feature MFMA steps per staged block
+  constexpr int kTiles = kMaxK / 16;
+  __shared__ u32x4_t sB[2][kSteps][kTiles][64];
+  const WsLayout W = ws_layout(P.F, P.k);
+  const float* Vm = P.ws + (int64_t)blockIdx.y * W.stride + v_off;
+  const int64_t p = p0 + blockIdx.y;
+  const int64_t layer = p / P.num_chunks;
+  const int j = (int)(p - layer * P.num_chunks);
+  const int64_t a = min(max(P.offsets[j], (int64_t)0), P.total_tokens);
+  const int64_t b = min(max(P.offsets[j + 1], a), P.total_tokens);
+  const int64_t t0 = a + (int64_t)blockIdx.x * 64;
+  if (t0 >= b) return;  // the whole workgroup
+  const uint16_t* D = P.delta + layer * P.total_tokens * P.F;
+  uint16_t* Uo = P.U_out + layer * P.total_tokens * P.m;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int k = P.k, m = P.m, F = P.F;
+  const int nct = (m + 15) / 16;
+  f32x4_t acc[kTiles];
+#pragma unroll
+  for (int ct = 0; ct < kTiles; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int64_t trow = t0 + 16 * wave + c16;  // this lane's A row
+  const bool row_ok = trow < b;
+  const uint16_t* drow = D + (row_ok ? trow : a) * F + 8 * g;
+  for (int f0 = 0; f0 < F; f0 += 32 * kSteps) {
+    for (int idx = tid; idx < kSteps * nct * 64; idx += kThreads) {
+      const int l = idx & 63, rest = idx >> 6;
+      const int ct = rest % nct, st = rest / nct;
+      const int col = 16 * ct + (l & 15);
+      const int fb = f0 + 32 * st + 8 * (l >> 4);
+      bf16x8_t hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int f = fb + e;
+        const float x = (col < m && col < k && f < F) ? Vm[(int64_t)f * k + col] : 0.f;
+        hi[e] = (__bf16)x;
+        lo[e] = (__bf16)(x - (float)hi[e]);
+      }
+      sB[0][st][ct][l] = __builtin_bit_cast(u32x4_t, hi);
+      sB[1][st][ct][l] = __builtin_bit_cast(u32x4_t, lo);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int f = f0 + 32 * st;
+      if (f >= F) break;
+      u32x4_t av = u32x4_t{0u, 0u, 0u, 0u};
+      if (row_ok) av = __builtin_nontemporal_load((const u32x4_t*)(drow + f));
+      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+      for (int ct = 0; ct < kTiles; ++ct) {
+        if (ct >= nct) break;
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            A, __builtin_bit_cast(bf16x8_t, sB[0][st][ct][lane]), acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            A, __builtin_bit_cast(bf16x8_t, sB[1][st][ct][lane]), acc[ct], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the next block's staging overwrites sB
+  }
+#pragma unroll
+  for (int ct = 0; ct < kTiles; ++ct) {
+    if (ct >= nct) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + 16 * wave + 4 * g + i;
+      const int c = 16 * ct + c16;
+      if (t < b && c < m) Uo[t * m + c] = f2bf16(acc[ct][i]);
+    }
+  }
+}
+
 }  // namespace
 
 int64_t form_workspace_floats(int F, int k) { return ws_layout(F, k).stride; }
@@ -658,7 +740,12 @@ hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream
   hipLaunchKernelGGL(write_v, dim3((F * P.m + kThreads - 1) / kThreads, count), blk, 0, s, P, p0,
                      tmp);
   const int64_t ttiles = (P.total_tokens + 63) / 64;
-  hipLaunchKernelGGL(write_u, dim3((unsigned)ttiles, count), blk, 0, s, P, p0, tmp);
+  // U on MFMA when Delta rows are 16-byte addressable (F is a multiple of 64); the
+  // fp32 VALU form otherwise.
+  if (((uintptr_t)P.delta & 15) == 0)
+    hipLaunchKernelGGL(write_u_mfma, dim3((unsigned)ttiles, count), blk, 0, s, P, p0, tmp);
+  else
+    hipLaunchKernelGGL(write_u, dim3((unsigned)ttiles, count), blk, 0, s, P, p0, tmp);
   return hipGetLastError();
 }
 
