@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void init_start(FormArgs P) {
 
 // C = op(A) B for every problem of the batch (blockIdx.z): op(A) is M x K (A row-major
 // M x K, or with TA row-major K x M), B row-major K x N, C row-major M x N; fp32 with
-// 64 x 64 output tiles, 16-deep LDS steps, 4 x 4 outputs per thread.  Offsets are
+// 64 x 64 output tiles, 16-deep LDS steps, fp32 MFMA (below).  Offsets are
 // element offsets inside each problem's workspace.
 template <bool TA>
 __global__ __launch_bounds__(kThreads) void gemm_ws(FormArgs P, int64_t a_off, int lda,
@@ -278,8 +278,18 @@ __global__ __launch_bounds__(kThreads) void gemm_ws(FormArgs P, int64_t a_off, i
   __shared__ float sB[16][64 + 4];
   const int tid = threadIdx.x;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  const int ty = tid >> 4, tx = tid & 15;
-  float acc[4][4] = {};
+  // fp32 MFMA (v_mfma_f32_16x16x4_f32): wave w computes rows 32 (w >> 1) .. + 31 and
+  // columns 32 (w & 1) .. + 31 of the 64 x 64 tile as 2 x 2 tiles of 16 x 16; lane l
+  // feeds A[row l & 15][k l >> 4] and B[k l >> 4][col l & 15] and holds
+  // C[4 (l >> 4) + q][l & 15], q < 4, of each tile.
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);
+  const int l16 = lane & 15, lk = lane >> 4;
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < K; k0 += 16) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -302,27 +312,30 @@ __global__ __launch_bounds__(kThreads) void gemm_ws(FormArgs P, int64_t a_off, i
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float av[4], bv[4];
+    for (int kk = 0; kk < 16; kk += 4) {
+      float av[2], bv[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        av[i] = sA[kk][ty * 4 + i];
-        bv[i] = sB[kk][tx * 4 + i];
+      for (int i = 0; i < 2; ++i) {
+        av[i] = sA[kk + lk][wr + 16 * i + l16];
+        bv[i] = sB[kk + lk][wc + 16 * i + l16];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = fmaf(av[i], bv[jj], acc[i][jj]);
+        for (int jj = 0; jj < 2; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[jj], acc[i][jj], 0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int gm = m0 + ty * 4 + i, gn = n0 + tx * 4 + jj;
-      if (gm < M && gn < N) C[(int64_t)gm * ldc + gn] = acc[i][jj];
-    }
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int gm = m0 + wr + 16 * i + 4 * lk + q, gn = n0 + wc + 16 * jj + l16;
+        if (gm < M && gn < N) C[(int64_t)gm * ldc + gn] = acc[i][jj][q];
+      }
 }
 
 // Block reduction of one float over the workgroup (result in every thread).
