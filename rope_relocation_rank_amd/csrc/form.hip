@@ -413,20 +413,30 @@ __global__ __launch_bounds__(kThreads) void chol_rinv(FormArgs P) {
     for (int i = j + 1 + tid; i < k; i += kThreads) L[i][j] *= inv;
     if (tid == 0) L[j][j] = keep ? sqrt(d) : 0.0;
     __syncthreads();
-    const int n = k - j - 1;  // trailing update: L[i][c] -= L[i][j] L[c][j], j < c <= i
-    for (int e = tid; e < n * n; e += kThreads) {
-      const int ii = j + 1 + e / n, cc = j + 1 + e % n;
-      if (cc <= ii) L[ii][cc] -= L[ii][j] * L[cc][j];
+    // Trailing update L[i][c] -= L[i][j] L[c][j], j < c <= i, on a 16 x 16 thread grid
+    // (rows by tid >> 4, columns by tid & 15).
+    const int n = k - j - 1;
+    for (int r = tid >> 4; r < n; r += 16) {
+      const int ii = j + 1 + r;
+      const double lij = L[ii][j];
+      for (int c = tid & 15; c <= r; c += 16) L[ii][j + 1 + c] -= lij * L[j + 1 + c][j];
     }
     __syncthreads();
   }
-  // In-place inverse of the lower-triangular L (dropped columns stay zero).
+  // In-place inverse of the lower-triangular L (dropped columns stay zero).  For column
+  // j, row i needs -(Linv[i][j+1..i] . L[j+1..i][j]) djj: four lanes share a row, each
+  // summing every fourth term, and two lane exchanges combine them.
   for (int j = k - 1; j >= 0; --j) {
     const double djj = L[j][j] > 0.0 ? 1.0 / L[j][j] : 0.0;
-    for (int i = j + 1 + tid; i < k; i += kThreads) {  // -(Linv[i][j+1..i] . L[j+1..i][j]) djj
+    const int n = k - j - 1;
+    for (int r0 = 0; r0 < n; r0 += kThreads / 4) {
+      const int r = r0 + (tid >> 2), q = tid & 3, i = j + 1 + r;
       double s = 0.0;
-      for (int p2 = j + 1; p2 <= i; ++p2) s += L[i][p2] * L[p2][j];
-      col[i] = -s * djj;
+      if (r < n)
+        for (int p2 = j + 1 + q; p2 <= i; p2 += 4) s += L[i][p2] * L[p2][j];
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      if (r < n && q == 0) col[i] = -s * djj;
     }
     __syncthreads();
     for (int i = j + 1 + tid; i < k; i += kThreads) L[i][j] = col[i];
