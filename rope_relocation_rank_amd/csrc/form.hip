@@ -29,6 +29,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kMaxK = 128;
@@ -58,6 +59,28 @@ __host__ __device__ inline WsLayout ws_layout(int F, int k) {
 
 // ------------------------------------------------------------------ 1. Gram on MFMA
 
+// Workgroups go to the 8 XCDs round-robin in launch order, and each XCD has its own
+// L2.  The tiles of one problem read the same data (columns of Delta, or the problem's
+// workspace matrices), so the linear block index L (x fastest, then y, then z) is
+// remapped to v such that each XCD takes a contiguous range of v, a bijection of
+// [0, N) for N blocks: XCD x = L % 8 takes its (L / 8)-th block from the range of x.
+// The kernels read their tile and problem from v in place of blockIdx.
+struct Blk {
+  uint32_t x, y, z;
+};
+__device__ __forceinline__ Blk xcd_block() {
+  const uint32_t gx = gridDim.x, gxy = gx * gridDim.y, N = gxy * gridDim.z;
+  const uint32_t L = blockIdx.x + blockIdx.y * gx + blockIdx.z * gxy;
+  const uint32_t x = L & 7u, s = L >> 3, Q = N >> 3, R = N & 7u;
+  uint32_t v = (x < R ? x * (Q + 1) : R * (Q + 1) + (x - R) * Q) + s;
+  Blk r;
+  r.z = v / gxy;
+  v -= r.z * gxy;
+  r.y = v / gx;
+  r.x = v - r.y * gx;
+  return r;
+}
+
 // One 64 x 64 tile (ti <= tj) of G = Delta_j^T Delta_j.  Per 32-token step the
 // workgroup stages both 64-feature column blocks of Delta transposed in LDS
 // ([feature][token]), so each lane reads the 8 consecutive tokens of one feature that
@@ -66,19 +89,21 @@ __host__ __device__ inline WsLayout ws_layout(int F, int k) {
 __global__ __launch_bounds__(kThreads) void gram_tiles(FormArgs P, int64_t p0, float* Gbase,
                                                        int64_t gstride) {
   const int ntile = P.F / 64;
-  int rem = blockIdx.x, ti = 0;
+  const Blk bk = xcd_block();
+  const int prob = (int)bk.y;
+  int rem = (int)bk.x, ti = 0;
   while (rem >= ntile - ti) {
     rem -= ntile - ti;
     ++ti;
   }
   const int tj = ti + rem;
-  const int64_t p = p0 + blockIdx.y;
+  const int64_t p = p0 + prob;
   const int64_t layer = p / P.num_chunks;
   const int j = (int)(p - layer * P.num_chunks);
   // Rows [a, b) of the chunk, kept inside [0, total_tokens) whatever the offsets hold.
   const int64_t a = min(max(P.offsets[j], (int64_t)0), P.total_tokens);
   const int64_t b = min(max(P.offsets[j + 1], a), P.total_tokens);
-  float* G = Gbase + (int64_t)blockIdx.y * gstride;
+  float* G = Gbase + (int64_t)prob * gstride;
 
   __shared__ __attribute__((aligned(16))) uint16_t sA[64][40];  // 32 tokens + 8 pad
   __shared__ __attribute__((aligned(16))) uint16_t sB[64][40];
@@ -144,18 +169,20 @@ __global__ __launch_bounds__(kThreads) void gram_tiles(FormArgs P, int64_t p0, f
 __global__ __launch_bounds__(kThreads) void gram_tiles128(FormArgs P, int64_t p0, float* Gbase,
                                                           int64_t gstride) {
   const int ntile = P.F / 128;
-  int rem = blockIdx.x, ti = 0;
+  const Blk bk = xcd_block();
+  const int prob = (int)bk.y;
+  int rem = (int)bk.x, ti = 0;
   while (rem >= ntile - ti) {
     rem -= ntile - ti;
     ++ti;
   }
   const int tj = ti + rem;
-  const int64_t p = p0 + blockIdx.y;
+  const int64_t p = p0 + prob;
   const int64_t layer = p / P.num_chunks;
   const int j = (int)(p - layer * P.num_chunks);
   const int64_t a = min(max(P.offsets[j], (int64_t)0), P.total_tokens);
   const int64_t b = min(max(P.offsets[j + 1], a), P.total_tokens);
-  float* G = Gbase + (int64_t)blockIdx.y * gstride;
+  float* G = Gbase + (int64_t)prob * gstride;
 
   constexpr int KS = 64;           // tokens per LDS step
   constexpr int RS = KS / 2 + 4;   // 32-bit words per LDS row (token pairs + pad)
@@ -164,31 +191,35 @@ __global__ __launch_bounds__(kThreads) void gram_tiles128(FormArgs P, int64_t p0
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = wave >> 1, wj = wave & 1;
   const uint16_t* D = P.delta + layer * P.total_tokens * P.F;
-  // Work item q (2 per thread): token pair tp = q & 31, feature group fg = q >> 5.
-  auto load = [&](int64_t t0, int col0, u32x4_t (&r)[2][2]) {
+  // Thread tid reads feature group fg = tid & 15 (8 features) of the 4 tokens
+  // 4 tq .. 4 tq + 3, tq = tid >> 4: 16 consecutive lanes read 256 contiguous bytes of
+  // one row, and a wave instruction touches 4 rows.  In LDS, the word of token pair tp
+  // of feature f sits at column tp ^ 4 ((f >> 4) & 7): the swizzle moves whole 16-byte
+  // groups, so an MFMA operand (4 words of one feature) stays one aligned 16-byte read,
+  // and a thread's two words per feature (token pairs 2 tq, 2 tq + 1) stay one aligned
+  // 8-byte store; a wave's stores spread evenly over the 64 banks.
+  const int fg = tid & 15, tq = tid >> 4;
+  const int col = (2 * tq) ^ (4 * ((fg >> 1) & 7));  // (f >> 4) & 7 for every f of the group
+  auto load = [&](int64_t t0, int col0, u32x4_t (&r)[4]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = tid + kThreads * h;
-      const int tp = q & 31, fg = q >> 5;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int64_t t = t0 + 2 * tp + u;
-        r[h][u] = u32x4_t{0u, 0u, 0u, 0u};
-        if (t < b) r[h][u] = *(const u32x4_t*)(D + t * P.F + col0 + fg * 8);
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int64_t t = t0 + 4 * tq + u;
+      r[u] = u32x4_t{0u, 0u, 0u, 0u};
+      if (t < b) r[u] = *(const u32x4_t*)(D + t * P.F + col0 + fg * 8);
     }
   };
-  auto store = [&](uint32_t (*S)[RS], const u32x4_t (&r)[2][2]) {
+  auto store = [&](uint32_t (*S)[RS], const u32x4_t (&r)[4]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = tid + kThreads * h;
-      const int tp = q & 31, fg = q >> 5;
+    for (int e = 0; e < 4; ++e) {  // features 2e, 2e + 1 of the group
+      u32x2_t lo, hi;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {  // features 2e, 2e + 1 of the group
-        const uint32_t w0 = r[h][0][e], w1 = r[h][1][e];
-        S[fg * 8 + 2 * e][tp] = (w0 & 0xffffu) | (w1 << 16);
-        S[fg * 8 + 2 * e + 1][tp] = (w0 >> 16) | (w1 & 0xffff0000u);
+      for (int pp = 0; pp < 2; ++pp) {
+        const uint32_t w0 = r[2 * pp][e], w1 = r[2 * pp + 1][e];
+        lo[pp] = (w0 & 0xffffu) | (w1 << 16);
+        hi[pp] = (w0 >> 16) | (w1 & 0xffff0000u);
       }
+      *(u32x2_t*)&S[fg * 8 + 2 * e][col] = lo;
+      *(u32x2_t*)&S[fg * 8 + 2 * e + 1][col] = hi;
     }
   };
   f32x4_t acc[4][4];
@@ -196,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void gram_tiles128(FormArgs P, int64_t p0
   for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  u32x4_t ra[2][2], rb[2][2];
+  u32x4_t ra[4], rb[4];
   if (a < b) {
     load(a, ti * 128, ra);
     load(a, tj * 128, rb);
@@ -215,11 +246,11 @@ __global__ __launch_bounds__(kThreads) void gram_tiles128(FormArgs P, int64_t p0
     for (int ks = 0; ks < KS / 32; ++ks) {
       bf16x8_t fa[4], fb[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        fa[x] = __builtin_bit_cast(bf16x8_t,
-                                   *(const u32x4_t*)&sA[wi * 64 + x * 16 + r16][ks * 16 + 4 * g]);
-        fb[x] = __builtin_bit_cast(bf16x8_t,
-                                   *(const u32x4_t*)&sB[wj * 64 + x * 16 + r16][ks * 16 + 4 * g]);
+      for (int x = 0; x < 4; ++x) {  // rows wi * 64 + x * 16 + r16: (row >> 4) & 7 = wi * 4 + x
+        const int ca = (ks * 16 + 4 * g) ^ (4 * (wi * 4 + x));
+        const int cb = (ks * 16 + 4 * g) ^ (4 * (wj * 4 + x));
+        fa[x] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)&sA[wi * 64 + x * 16 + r16][ca]);
+        fb[x] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)&sB[wj * 64 + x * 16 + r16][cb]);
       }
 #pragma unroll
       for (int x = 0; x < 4; ++x)
@@ -261,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void init_start(FormArgs P) {
   }
 }
 
-// C = op(A) B for every problem of the batch (blockIdx.z): op(A) is M x K (A row-major
+// C = op(A) B for every problem of the batch (grid z): op(A) is M x K (A row-major
 // M x K, or with TA row-major K x M), B row-major K x N, C row-major M x N; fp32 with
 // 64 x 64 output tiles, 16-deep LDS steps, fp32 MFMA (below).  Offsets are
 // element offsets inside each problem's workspace.
@@ -270,14 +301,15 @@ __global__ __launch_bounds__(kThreads) void gemm_ws(FormArgs P, int64_t a_off, i
                                                      int64_t b_off, int ldb, int64_t c_off,
                                                      int ldc, int M, int N, int K) {
   const WsLayout W = ws_layout(P.F, P.k);
-  float* base = P.ws + (int64_t)blockIdx.z * W.stride;
+  const Blk bk = xcd_block();
+  float* base = P.ws + (int64_t)bk.z * W.stride;
   const float* A = base + a_off;
   const float* B = base + b_off;
   float* C = base + c_off;
   __shared__ float sA[16][64 + 4];
   __shared__ float sB[16][64 + 4];
   const int tid = threadIdx.x;
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int m0 = (int)bk.y * 64, n0 = (int)bk.x * 64;
   // fp32 MFMA (v_mfma_f32_16x16x4_f32): wave w computes rows 32 (w >> 1) .. + 31 and
   // columns 32 (w & 1) .. + 31 of the 64 x 64 tile as 2 x 2 tiles of 16 x 16; lane l
   // feeds A[row l & 15][k l >> 4] and B[k l >> 4][col l & 15] and holds
@@ -353,11 +385,12 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // occupies the B and E regions of the workspace (2 k^2 floats = k^2 doubles).
 __global__ __launch_bounds__(kThreads) void gram64(FormArgs P, int64_t x_off) {
   const WsLayout W = ws_layout(P.F, P.k);
-  float* base = P.ws + (int64_t)blockIdx.z * W.stride;
+  const Blk bk = xcd_block();
+  float* base = P.ws + (int64_t)bk.z * W.stride;
   const float* X = base + x_off;
   double* Wd = reinterpret_cast<double*>(base + W.B);
   const int k = P.k, tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+  const int i0 = (int)bk.y * 32, j0 = (int)bk.x * 32;
   __shared__ float si[16][33], sj[16][33];
   double acc[2][2] = {};
   for (int f0 = 0; f0 < P.F; f0 += 16) {
