@@ -10,13 +10,15 @@
 //
 // Method, per problem (layer, chunk):
 //   1. G = Delta^T Delta (F x F, fp32) on MFMA 16x16x32 bf16: a dense contraction over
-//      the chunk's tokens, upper-triangular 64 x 64 tiles, mirrored.
+//      the chunk's tokens, upper-triangular 128 x 128 tiles (64 x 64 when F is not a
+//      multiple of 128), mirrored.
 //   2. Subspace iteration on G with k = m + 16 columns (at most 128, at most F):
 //      Q <- orth(G Q) from a fixed pseudo-random start, `iters` times (fp32 tiled GEMM;
 //      orth = Cholesky QR twice, Gram and Cholesky in fp64).
 //   3. Rayleigh-Ritz: B = Q^T G Q (k x k), eigenpairs of B by cyclic Jacobi in LDS,
 //      sorted; V_m = Q E[:, :m], s_i = sqrt(lambda_i).
-//   4. U_m = Delta V_m (= U_m diag(s) of the SVD), rounded to bf16 with V_m.
+//   4. U_m = Delta V_m (= U_m diag(s) of the SVD) on MFMA 16x16x32 bf16, V_m split
+//      into high and low bf16 parts once per problem; rounded to bf16 with V_m.
 // The top-m right singular vectors of Delta are the top-m eigenvectors of G; the error
 // of the subspace iteration shrinks like (lambda_{k+1} / lambda_i)^iters.
 #include <hip/hip_runtime.h>
@@ -34,7 +36,6 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kMaxK = 128;
 
-__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 __device__ __forceinline__ uint16_t f2bf16(float y) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(y));  // round to nearest even
 }
@@ -604,79 +605,57 @@ __global__ __launch_bounds__(kThreads) void write_v(FormArgs P, int64_t p0, int6
       P.sigma_out[p * P.m + c] = c < P.k ? sqrtf(fmaxf(base[W.lam + c], 0.f)) : 0.f;
 }
 
-// U_m = Delta V_m for the chunk's tokens: 64 tokens per workgroup (blockIdx.x), each
-// thread 4 tokens x 4 of the m columns; V_m (fp32, F x k at v_off) and Delta rows
-// staged in LDS 16 features at a time.  Rounded to bf16 into U [layer][t][m].
-__global__ __launch_bounds__(kThreads) void write_u(FormArgs P, int64_t p0, int64_t v_off) {
+// U_m = Delta V_m on MFMA (v_mfma_f32_16x16x32_bf16).  V_m (fp32, F x k at v_off) is
+// split into high and low bf16 parts (x - hi - lo <= 2^-17 |x|): the bf16 x bf16
+// products with Delta are exact and accumulate in fp32, so the sums match an fp32
+// product to fp32 rounding.
+
+constexpr int kUSteps = 2;  // 32-feature MFMA steps per staged 64-feature block
+
+// The split, once per problem, into the G region of the workspace, which is free once
+// the Rayleigh-Ritz products are done.  Only the first mu = min(m, k) columns of V_m can
+// be nonzero; they take nv = mu / 16 rounded up column tiles, and 16 nv <= F (k <= F,
+// and F is a multiple of 64), so the F * 16 nv floats fit in G's F^2.  For each
+// 64-feature block: 16-byte B fragments [part][step][column tile][lane], in the order
+// `write_u_mfma` stages them.  Lane (c16, g) of column tile ct, step st holds features
+// 64 fb + 32 st + 8 g .. + 7 of column 16 ct + c16 (zero from column mu on).
+__global__ __launch_bounds__(kThreads) void split_vm(FormArgs P, int64_t v_off) {
   const WsLayout W = ws_layout(P.F, P.k);
   const float* Vm = P.ws + (int64_t)blockIdx.y * W.stride + v_off;
-  const int64_t p = p0 + blockIdx.y;
-  const int64_t layer = p / P.num_chunks;
-  const int j = (int)(p - layer * P.num_chunks);
-  const int64_t a = min(max(P.offsets[j], (int64_t)0), P.total_tokens);
-  const int64_t b = min(max(P.offsets[j + 1], a), P.total_tokens);
-  const int64_t t0 = a + (int64_t)blockIdx.x * 64;
-  if (t0 >= b) return;
-  const uint16_t* D = P.delta + layer * P.total_tokens * P.F;
-  uint16_t* Uo = P.U_out + layer * P.total_tokens * P.m;
-  __shared__ float sD[16][64 + 4];
-  __shared__ float sV[16][kMaxK + 4];
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const int k = P.k, m = P.m;
-  for (int c0 = 0; c0 < m; c0 += 64) {
-    float acc[4][4] = {};
-    for (int f0 = 0; f0 < P.F; f0 += 16) {
+  u32x4_t* out = reinterpret_cast<u32x4_t*>(P.ws + (int64_t)blockIdx.y * W.stride + W.G);
+  const int k = P.k, mu = min(P.m, k), nct = (mu + 15) / 16;
+  const int n = (P.F / 64) * kUSteps * nct * 64;
+  for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < n; idx += gridDim.x * kThreads) {
+    const int l = idx & 63;
+    int rest = idx >> 6;
+    const int ct = rest % nct;
+    rest /= nct;
+    const int st = rest % kUSteps, fb = rest / kUSteps;
+    const int col = 16 * ct + (l & 15);
+    const int f8 = 64 * fb + 32 * st + 8 * (l >> 4);
+    bf16x8_t hi, lo;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int idx = tid + kThreads * q;
-        const int r = idx >> 4, ff = idx & 15;  // token r, feature ff
-        const int64_t t = t0 + r;
-        sD[ff][r] = (t < b) ? bf16f(D[t * P.F + f0 + ff]) : 0.f;
-        const int vf = idx >> 6, vc = idx & 63;  // feature vf, column vc
-        sV[vf][vc] = (c0 + vc < m && c0 + vc < k) ? Vm[(int64_t)(f0 + vf) * k + c0 + vc] : 0.f;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int ff = 0; ff < 16; ++ff) {
-        float dv[4], vv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dv[i] = sD[ff][ty * 4 + i];
-          vv[i] = sV[ff][tx * 4 + i];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc[i][jj] = fmaf(dv[i], vv[jj], acc[i][jj]);
-      }
-      __syncthreads();
+    for (int e = 0; e < 8; ++e) {
+      const float x = col < mu ? Vm[(int64_t)(f8 + e) * k + col] : 0.f;
+      hi[e] = (__bf16)x;
+      lo[e] = (__bf16)(x - (float)hi[e]);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int64_t t = t0 + ty * 4 + i;
-        const int c = c0 + tx * 4 + jj;
-        if (t < b && c < m) Uo[t * m + c] = f2bf16(acc[i][jj]);
-      }
+    const int64_t blk = (int64_t)fb * 2 * kUSteps * nct * 64;
+    out[blk + (st * nct + ct) * 64 + l] = __builtin_bit_cast(u32x4_t, hi);
+    out[blk + ((kUSteps + st) * nct + ct) * 64 + l] = __builtin_bit_cast(u32x4_t, lo);
   }
 }
 
-// U_m = Delta V_m on MFMA (v_mfma_f32_16x16x32_bf16): 64 tokens per workgroup
-// (blockIdx.x), wave w the 16-token tile w.  V_m (fp32, F x k at v_off) is split into
-// high and low bf16 parts (x - hi - lo <= 2^-17 |x|): the bf16 x bf16 products with
-// Delta are exact and accumulate in fp32, so the sums match the fp32 form above to
-// fp32 rounding.  Every 64 features the workgroup stages V_m's B fragments in LDS
-// (lane (c16, g) of column tile ct holds features 32 s + 8 g .. + 7 of column
-// 16 ct + c16); each lane loads its A fragment, 8 consecutive features of token c16 of
-// its wave's tile, straight from HBM (Delta rows 16-byte aligned).  Lane (c16, g) ends
-// with U rows 4 g .. 4 g + 3 of column 16 ct + c16.
-__global__ __launch_bounds__(kThreads) void write_u_mfma(FormArgs P, int64_t p0, int64_t v_off) {
-  constexpr int kSteps = 2;  // 32-feature MFMA steps per staged block
+// The product: 64 tokens per workgroup (blockIdx.x), wave w the 16-token tile w.  Every
+// 64 features the workgroup copies that block's fragments into LDS; each lane loads its
+// A fragment, 8 consecutive features of token c16 of its wave's tile, straight from HBM
+// (Delta rows 16-byte aligned), issued before the copy so that the load overlaps it.
+// Lane (c16, g) ends with U rows 4 g .. 4 g + 3 of column 16 ct + c16; column tiles
+// from nv on (columns past k) keep their zero sums.
+__global__ __launch_bounds__(kThreads) void write_u_mfma(FormArgs P, int64_t p0) {
   constexpr int kTiles = kMaxK / 16;
-  __shared__ u32x4_t sB[2][kSteps][kTiles][64];
+  __shared__ u32x4_t sB[2][kUSteps][kTiles][64];
   const WsLayout W = ws_layout(P.F, P.k);
-  const float* Vm = P.ws + (int64_t)blockIdx.y * W.stride + v_off;
   const int64_t p = p0 + blockIdx.y;
   const int64_t layer = p / P.num_chunks;
   const int j = (int)(p - layer * P.num_chunks);
@@ -688,49 +667,45 @@ __global__ __launch_bounds__(kThreads) void write_u_mfma(FormArgs P, int64_t p0,
   uint16_t* Uo = P.U_out + layer * P.total_tokens * P.m;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int k = P.k, m = P.m, F = P.F;
-  const int nct = (m + 15) / 16;
+  const int m = P.m, F = P.F;
+  const int nct = (m + 15) / 16;                     // column tiles of U
+  const int nv = (min(m, P.k) + 15) / 16;            // column tiles of the fragments
+  const int nfrag = 2 * kUSteps * nv * 64;  // fragments of one 64-feature block
+  const u32x4_t* frag =
+      reinterpret_cast<const u32x4_t*>(P.ws + (int64_t)blockIdx.y * W.stride + W.G);
   f32x4_t acc[kTiles];
 #pragma unroll
   for (int ct = 0; ct < kTiles; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int64_t trow = t0 + 16 * wave + c16;  // this lane's A row
   const bool row_ok = trow < b;
   const uint16_t* drow = D + (row_ok ? trow : a) * F + 8 * g;
-  for (int f0 = 0; f0 < F; f0 += 32 * kSteps) {
-    for (int idx = tid; idx < kSteps * nct * 64; idx += kThreads) {
-      const int l = idx & 63, rest = idx >> 6;
-      const int ct = rest % nct, st = rest / nct;
-      const int col = 16 * ct + (l & 15);
-      const int fb = f0 + 32 * st + 8 * (l >> 4);
-      bf16x8_t hi, lo;
+  for (int f0 = 0; f0 < F; f0 += 32 * kUSteps) {  // F is a multiple of 64
+    u32x4_t av[kUSteps];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int f = fb + e;
-        const float x = (col < m && col < k && f < F) ? Vm[(int64_t)f * k + col] : 0.f;
-        hi[e] = (__bf16)x;
-        lo[e] = (__bf16)(x - (float)hi[e]);
-      }
-      sB[0][st][ct][l] = __builtin_bit_cast(u32x4_t, hi);
-      sB[1][st][ct][l] = __builtin_bit_cast(u32x4_t, lo);
+    for (int st = 0; st < kUSteps; ++st) {
+      av[st] = u32x4_t{0u, 0u, 0u, 0u};
+      if (row_ok) av[st] = __builtin_nontemporal_load((const u32x4_t*)(drow + f0 + 32 * st));
+    }
+    const u32x4_t* src = frag + (int64_t)(f0 / 64) * nfrag;
+    for (int idx = tid; idx < nfrag; idx += kThreads) {
+      const int l = idx & 63, rest = idx >> 6;
+      const int ct = rest % nv, q = rest / nv;  // q = part * kUSteps + step
+      sB[q / kUSteps][q % kUSteps][ct][l] = src[idx];
     }
     __syncthreads();
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      const int f = f0 + 32 * st;
-      if (f >= F) break;
-      u32x4_t av = u32x4_t{0u, 0u, 0u, 0u};
-      if (row_ok) av = __builtin_nontemporal_load((const u32x4_t*)(drow + f));
-      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av);
+    for (int st = 0; st < kUSteps; ++st) {
+      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av[st]);
 #pragma unroll
       for (int ct = 0; ct < kTiles; ++ct) {
-        if (ct >= nct) break;
+        if (ct >= nv) break;
         acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             A, __builtin_bit_cast(bf16x8_t, sB[0][st][ct][lane]), acc[ct], 0, 0, 0);
         acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             A, __builtin_bit_cast(bf16x8_t, sB[1][st][ct][lane]), acc[ct], 0, 0, 0);
       }
     }
-    __syncthreads();  // the next block's staging overwrites sB
+    __syncthreads();  // the next block's copy overwrites sB
   }
 #pragma unroll
   for (int ct = 0; ct < kTiles; ++ct) {
@@ -796,12 +771,11 @@ hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream
   hipLaunchKernelGGL(write_v, dim3((F * P.m + kThreads - 1) / kThreads, count), blk, 0, s, P, p0,
                      tmp);
   const int64_t ttiles = (P.total_tokens + 63) / 64;
-  // U on MFMA when Delta rows are 16-byte addressable (F is a multiple of 64); the
-  // fp32 VALU form otherwise.
-  if (((uintptr_t)P.delta & 15) == 0)
-    hipLaunchKernelGGL(write_u_mfma, dim3((unsigned)ttiles, count), blk, 0, s, P, p0, tmp);
-  else
-    hipLaunchKernelGGL(write_u, dim3((unsigned)ttiles, count), blk, 0, s, P, p0, tmp);
+  // U on MFMA: Delta rows are 16-byte addressable (the host requires a 16-byte aligned
+  // deficit, and F is a multiple of 64).
+  const int nfr = (F / 64) * kUSteps * ((std::min(P.m, k) + 15) / 16) * 64;
+  hipLaunchKernelGGL(split_vm, dim3((nfr + kThreads - 1) / kThreads, count), blk, 0, s, P, tmp);
+  hipLaunchKernelGGL(write_u_mfma, dim3((unsigned)ttiles, count), blk, 0, s, P, p0);
   return hipGetLastError();
 }
 

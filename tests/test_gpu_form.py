@@ -119,6 +119,18 @@ def test_form_mla_widths():
     _check(w, 64, label="mla")
 
 
+def test_form_rank_above_width():
+    # m = 100 > F = 64 on k_rope: k = F, so only 64 columns can be nonzero; the rest of
+    # U_m and V_m must be exactly zero, and the first 64 columns are the exact SVD.
+    w = synth.get("deepseek_v3_mla").with_(layers=2, tokens=300)
+    _check(w, 100, label="mla m=100")
+    st, deltas, U, V, S = _form(w, 100)
+    c = [d.shape[-1] for d in deltas].index(64)
+    Ug = U[c].reshape(w.layers, -1, 100)
+    Vg = V[c].reshape(w.layers, st.num_chunks, 64, 100)
+    assert not Ug[..., 64:].any() and not Vg[..., 64:].any()
+
+
 def test_form_iterations_converge():
     # Fewer iterations leave the trailing singular values less converged (the error
     # falls like (lambda_{k+1} / lambda_i)^iterations); more meet the tight bounds.
