@@ -294,13 +294,16 @@ __global__ __launch_bounds__(kThreads) void init_start(FormArgs P) {
 }
 
 // C = op(A) B for every problem of the batch (grid z): op(A) is M x K (A row-major
-// M x K, or with TA row-major K x M), B row-major K x N, C row-major M x N; fp32 with
-// 64 x 64 output tiles, 16-deep LDS steps, fp32 MFMA (below).  Offsets are
-// element offsets inside each problem's workspace.
-template <bool TA>
+// M x K, or with TA row-major K x M), B row-major K x N, C row-major M x N, fp32.  Every
+// call has N = k <= 128, so one tile spans all columns: 64 rows x 16 NT columns,
+// NT = N / 16 rounded up (k = 80 computes 80 columns, not two 64-wide tiles), 16-deep
+// LDS steps, fp32 MFMA (below).  Offsets are element offsets inside each problem's
+// workspace.
+template <bool TA, int NT>
 __global__ __launch_bounds__(kThreads) void gemm_ws(FormArgs P, int64_t a_off, int lda,
                                                      int64_t b_off, int ldb, int64_t c_off,
                                                      int ldc, int M, int N, int K) {
+  constexpr int TN = 16 * NT;
   const WsLayout W = ws_layout(P.F, P.k);
   const Blk bk = xcd_block();
   float* base = P.ws + (int64_t)bk.z * W.stride;
@@ -308,24 +311,20 @@ __global__ __launch_bounds__(kThreads) void gemm_ws(FormArgs P, int64_t a_off, i
   const float* B = base + b_off;
   float* C = base + c_off;
   __shared__ float sA[16][64 + 4];
-  __shared__ float sB[16][64 + 4];
+  __shared__ float sB[16][TN + 4];
   const int tid = threadIdx.x;
-  const int m0 = (int)bk.y * 64, n0 = (int)bk.x * 64;
-  // fp32 MFMA (v_mfma_f32_16x16x4_f32): wave w computes rows 32 (w >> 1) .. + 31 and
-  // columns 32 (w & 1) .. + 31 of the 64 x 64 tile as 2 x 2 tiles of 16 x 16; lane l
-  // feeds A[row l & 15][k l >> 4] and B[k l >> 4][col l & 15] and holds
-  // C[4 (l >> 4) + q][l & 15], q < 4, of each tile.
+  const int m0 = (int)bk.y * 64;
+  // fp32 MFMA (v_mfma_f32_16x16x4_f32): wave w computes rows 16 w .. + 15 of the tile
+  // as NT tiles of 16 x 16; lane l feeds A[row l & 15][k l >> 4] and B[k l >> 4][col
+  // l & 15] and holds C[4 (l >> 4) + q][l & 15], q < 4, of each tile.
   const int lane = tid & 63, wave = tid >> 6;
-  const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);
   const int l16 = lane & 15, lk = lane >> 4;
-  f32x4_t acc[2][2];
+  f32x4_t acc[NT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < K; k0 += 16) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 4; ++q) {  // A: 64 x 16
       const int idx = tid + kThreads * q;
       int r, kk;
       if (TA) {
@@ -339,36 +338,56 @@ __global__ __launch_bounds__(kThreads) void gemm_ws(FormArgs P, int64_t a_off, i
       float v = 0.f;
       if (gm < M && gk < K) v = TA ? A[(int64_t)gk * lda + gm] : A[(int64_t)gm * lda + gk];
       sA[kk][r] = v;
-      const int bk = idx >> 6, bc = idx & 63;
-      const int gbk = k0 + bk, gn = n0 + bc;
-      sB[bk][bc] = (gbk < K && gn < N) ? B[(int64_t)gbk * ldb + gn] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {  // B: 16 x TN
+      const int idx = tid + kThreads * q;
+      const int bkk = idx / TN, bc = idx % TN;
+      const int gbk = k0 + bkk;
+      sB[bkk][bc] = (gbk < K && bc < N) ? B[(int64_t)gbk * ldb + bc] : 0.f;
     }
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 16; kk += 4) {
-      float av[2], bv[2];
+      const float av = sA[kk + lk][16 * wave + l16];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        av[i] = sA[kk + lk][wr + 16 * i + l16];
-        bv[i] = sB[kk + lk][wc + 16 * i + l16];
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[jj], acc[i][jj], 0, 0, 0);
+      for (int j = 0; j < NT; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, sB[kk + lk][16 * j + l16], acc[j], 0,
+                                                      0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < NT; ++j)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int gm = m0 + wr + 16 * i + 4 * lk + q, gn = n0 + wc + 16 * jj + l16;
-        if (gm < M && gn < N) C[(int64_t)gm * ldc + gn] = acc[i][jj][q];
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int gm = m0 + 16 * wave + 4 * lk + q, gn = 16 * j + l16;
+      if (gm < M && gn < N) C[(int64_t)gm * ldc + gn] = acc[j][q];
+    }
+}
+
+// Launch of gemm_ws for `count` problems, N <= 128.
+template <bool TA>
+void launch_gemm_ws(const FormArgs& P, int count, hipStream_t s, int64_t a_off, int lda,
+                    int64_t b_off, int ldb, int64_t c_off, int ldc, int M, int N, int K) {
+  const dim3 g(1, (M + 63) / 64, count), blk(kThreads);
+#define KAMERA_GEMM_WS(NT)                                                                   \
+  case NT:                                                                                   \
+    hipLaunchKernelGGL((gemm_ws<TA, NT>), g, blk, 0, s, P, a_off, lda, b_off, ldb, c_off, ldc, \
+                       M, N, K);                                                             \
+    break
+  switch ((N + 15) / 16) {
+    KAMERA_GEMM_WS(1);
+    KAMERA_GEMM_WS(2);
+    KAMERA_GEMM_WS(3);
+    KAMERA_GEMM_WS(4);
+    KAMERA_GEMM_WS(5);
+    KAMERA_GEMM_WS(6);
+    KAMERA_GEMM_WS(7);
+    KAMERA_GEMM_WS(8);
+    default: break;  // N <= k <= 128 (kMaxK)
+  }
+#undef KAMERA_GEMM_WS
 }
 
 // Block reduction of one float over the workgroup (result in every thread).
@@ -739,8 +758,6 @@ hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream
                        P.ws + W.G, W.stride);
   }
   hipLaunchKernelGGL(init_start, dim3((F * k + kThreads - 1) / kThreads, count), blk, 0, s, P);
-  const dim3 gFk((k + 63) / 64, (F + 63) / 64, count);
-  const dim3 gkk((k + 63) / 64, (k + 63) / 64, count);
   const dim3 g32((k + 31) / 32, (k + 31) / 32, count);
   // Z = G Q, Q = orth(Z), `iters` + 1 times (the first from the random start).  orth is
   // Cholesky QR; the last basis gets a second pass, which restores the orthogonality
@@ -750,10 +767,10 @@ hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream
   auto cholqr = [&](int64_t from, int64_t to) {  // to = from R^-1
     hipLaunchKernelGGL(gram64, g32, blk, 0, s, P, from);
     hipLaunchKernelGGL(chol_rinv, dim3(count), blk, 0, s, P);
-    hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, from, k, W.B, k, to, k, F, k, k);
+    launch_gemm_ws<false>(P, count, s, from, k, W.B, k, to, k, F, k, k);
   };
   for (int it = 0; it <= P.iters; ++it) {
-    hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, W.G, F, basis, k, tmp, k, F, k, F);
+    launch_gemm_ws<false>(P, count, s, W.G, F, basis, k, tmp, k, F, k, F);
     cholqr(tmp, basis);
     if (it == P.iters) {  // the basis Rayleigh-Ritz uses is orthonormalized twice
       cholqr(basis, tmp);
@@ -764,10 +781,10 @@ hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream
   }
   // Rayleigh-Ritz: tmp = G basis, B = basis^T tmp, eigenpairs of B, then tmp = basis E
   // (V_m in its first m columns).
-  hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, W.G, F, basis, k, tmp, k, F, k, F);
-  hipLaunchKernelGGL((gemm_ws<true>), gkk, blk, 0, s, P, basis, k, tmp, k, W.B, k, k, k, F);
+  launch_gemm_ws<false>(P, count, s, W.G, F, basis, k, tmp, k, F, k, F);
+  launch_gemm_ws<true>(P, count, s, basis, k, tmp, k, W.B, k, k, k, F);
   hipLaunchKernelGGL(jacobi_eig, dim3(count), blk, 0, s, P);
-  hipLaunchKernelGGL((gemm_ws<false>), gFk, blk, 0, s, P, basis, k, W.E, k, tmp, k, F, k, k);
+  launch_gemm_ws<false>(P, count, s, basis, k, W.E, k, tmp, k, F, k, k);
   hipLaunchKernelGGL(write_v, dim3((F * P.m + kThreads - 1) / kThreads, count), blk, 0, s, P, p0,
                      tmp);
   const int64_t ttiles = (P.total_tokens + 63) / 64;
