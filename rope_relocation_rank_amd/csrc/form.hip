@@ -295,44 +295,52 @@ __global__ __launch_bounds__(kThreads) void init_start(FormArgs P) {
 
 // C = op(A) B for every problem of the batch (grid z): op(A) is M x K (A row-major
 // M x K, or with TA row-major K x M), B row-major K x N, C row-major M x N, fp32.  Every
-// call has N = k <= 128, so one tile spans all columns: 64 rows x 16 NT columns,
-// NT = N / 16 rounded up (k = 80 computes 80 columns, not two 64-wide tiles), 16-deep
-// LDS steps, fp32 MFMA (below).  Offsets are element offsets inside each problem's
-// workspace.
-template <bool TA, int NT>
+// call has N = k <= 128, so one tile spans all columns, 16 NT of them with NT = N / 16
+// rounded up, on fp32 MFMA (below).  Two forms:
+//   - TM = 64 rows, 16-deep LDS steps, wave w the rows 16 w .. + 15 over all of K;
+//   - SPLIT: TM = 16 rows, 64-deep LDS steps, wave w the 16-deep slice w of each step
+//     (K split over the waves), the four partial tiles summed through LDS at the end.
+//     It runs 4x the workgroups and a quarter of the serial steps, for launches whose
+//     64-row grid cannot fill the chip; it re-reads B per 16 rows instead of per 64.
+// Offsets are element offsets inside each problem's workspace.
+template <bool TA, int NT, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void gemm_ws(FormArgs P, int64_t a_off, int lda,
                                                      int64_t b_off, int ldb, int64_t c_off,
                                                      int ldc, int M, int N, int K) {
   constexpr int TN = 16 * NT;
+  constexpr int TM = SPLIT ? 16 : 64;
+  constexpr int KS = SPLIT ? 64 : 16;  // K per LDS step
   const WsLayout W = ws_layout(P.F, P.k);
   const Blk bk = xcd_block();
   float* base = P.ws + (int64_t)bk.z * W.stride;
   const float* A = base + a_off;
   const float* B = base + b_off;
   float* C = base + c_off;
-  __shared__ float sA[16][64 + 4];
-  __shared__ float sB[16][TN + 4];
+  __shared__ float sA[KS][TM + (SPLIT ? 1 : 4)];  // [k][row]
+  __shared__ __attribute__((aligned(16))) float sB[KS][TN + 4];
   const int tid = threadIdx.x;
-  const int m0 = (int)bk.y * 64;
-  // fp32 MFMA (v_mfma_f32_16x16x4_f32): wave w computes rows 16 w .. + 15 of the tile
-  // as NT tiles of 16 x 16; lane l feeds A[row l & 15][k l >> 4] and B[k l >> 4][col
-  // l & 15] and holds C[4 (l >> 4) + q][l & 15], q < 4, of each tile.
+  const int m0 = (int)bk.y * TM;
+  // fp32 MFMA (v_mfma_f32_16x16x4_f32): lane l feeds A[row l & 15][k l >> 4] and
+  // B[k l >> 4][col l & 15] and holds C[4 (l >> 4) + q][l & 15], q < 4, of each of the
+  // NT 16 x 16 tiles.
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lk = lane >> 4;
+  const int wrow = SPLIT ? 0 : 16 * wave;  // the wave's rows in the tile
+  const int wk = SPLIT ? 16 * wave : 0;    // and its k slice in a step
   f32x4_t acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < K; k0 += 16) {
+  for (int k0 = 0; k0 < K; k0 += KS) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {  // A: 64 x 16
+    for (int q = 0; q < TM * KS / kThreads; ++q) {  // A: TM x KS
       const int idx = tid + kThreads * q;
       int r, kk;
       if (TA) {
-        kk = idx >> 6;
-        r = idx & 63;
+        kk = idx / TM;
+        r = idx % TM;
       } else {
-        r = idx >> 4;
-        kk = idx & 15;
+        r = idx / KS;
+        kk = idx % KS;
       }
       const int gm = m0 + r, gk = k0 + kk;
       float v = 0.f;
@@ -340,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void gemm_ws(FormArgs P, int64_t a_off, i
       sA[kk][r] = v;
     }
 #pragma unroll
-    for (int q = 0; q < NT; ++q) {  // B: 16 x TN
+    for (int q = 0; q < KS * TN / kThreads; ++q) {  // B: KS x TN
       const int idx = tid + kThreads * q;
       const int bkk = idx / TN, bc = idx % TN;
       const int gbk = k0 + bkk;
@@ -348,8 +356,8 @@ __global__ __launch_bounds__(kThreads) void gemm_ws(FormArgs P, int64_t a_off, i
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 16; kk += 4) {
-      const float av = sA[kk + lk][16 * wave + l16];
+    for (int kk = wk; kk < wk + 16; kk += 4) {
+      const float av = sA[kk + lk][wrow + l16];
 #pragma unroll
       for (int j = 0; j < NT; ++j)
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, sB[kk + lk][16 * j + l16], acc[j], 0,
@@ -357,24 +365,47 @@ __global__ __launch_bounds__(kThreads) void gemm_ws(FormArgs P, int64_t a_off, i
     }
     __syncthreads();
   }
+  if constexpr (SPLIT) {
+    // Waves 1..3 leave their partial tiles in sB's memory (3 NT x 64 x 16 bytes, within
+    // sB's 64 x (16 NT + 4) floats); wave 0 adds them.
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(&sB[0][0]);
+    if (wave > 0) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) red[((wave - 1) * NT + j) * 64 + lane] = acc[j];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int w = 0; w < 3; ++w) acc[j] += red[(w * NT + j) * 64 + lane];
+  }
 #pragma unroll
   for (int j = 0; j < NT; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int gm = m0 + 16 * wave + 4 * lk + q, gn = 16 * j + l16;
+      const int gm = m0 + wrow + 4 * lk + q, gn = 16 * j + l16;
       if (gm < M && gn < N) C[(int64_t)gm * ldc + gn] = acc[j][q];
     }
 }
 
-// Launch of gemm_ws for `count` problems, N <= 128.
+// Launch of gemm_ws for `count` problems, N <= 128: the K-split form when the 64-row
+// grid would leave CUs idle (fewer than 256 workgroups).  Measured on G Q products:
+// 224 workgroups (width 512, 28 problems) 55 -> 38 us with the split; 256 (width 1024,
+// 16 problems) slower with it; 1024 (width 1024, 64 problems) 254 -> 706 us.
 template <bool TA>
 void launch_gemm_ws(const FormArgs& P, int count, hipStream_t s, int64_t a_off, int lda,
                     int64_t b_off, int ldb, int64_t c_off, int ldc, int M, int N, int K) {
-  const dim3 g(1, (M + 63) / 64, count), blk(kThreads);
-#define KAMERA_GEMM_WS(NT)                                                                   \
-  case NT:                                                                                   \
-    hipLaunchKernelGGL((gemm_ws<TA, NT>), g, blk, 0, s, P, a_off, lda, b_off, ldb, c_off, ldc, \
-                       M, N, K);                                                             \
+  const bool split = (int64_t)((M + 63) / 64) * count < 256;
+  const dim3 g(1, split ? (M + 15) / 16 : (M + 63) / 64, count), blk(kThreads);
+#define KAMERA_GEMM_WS(NT)                                                                    \
+  case NT:                                                                                    \
+    if (split)                                                                                \
+      hipLaunchKernelGGL((gemm_ws<TA, NT, true>), g, blk, 0, s, P, a_off, lda, b_off, ldb,    \
+                         c_off, ldc, M, N, K);                                                \
+    else                                                                                      \
+      hipLaunchKernelGGL((gemm_ws<TA, NT, false>), g, blk, 0, s, P, a_off, lda, b_off, ldb,   \
+                         c_off, ldc, M, N, K);                                                \
     break
   switch ((N + 15) / 16) {
     KAMERA_GEMM_WS(1);
