@@ -432,42 +432,65 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // W = X^T X in fp64 for the F x k matrix X (Z or Q) of every problem: one 32 x 32 tile
-// of W per workgroup, 16 rows of X staged per step, 2 x 2 outputs per thread.  W
-// occupies the B and E regions of the workspace (2 k^2 floats = k^2 doubles).
+// of W per workgroup.  The F rows are split over the four waves (F is a multiple of 64):
+// wave w stages rows w F / 4 + 16 s .. + 15 of step s in its own LDS slice and
+// accumulates the whole tile over its quarter, 4 x 4 outputs per lane, so each wave
+// walks F / 64 steps; the four partial tiles are summed through LDS.  W occupies the B
+// and E regions of the workspace (2 k^2 floats = k^2 doubles).
 __global__ __launch_bounds__(kThreads) void gram64(FormArgs P, int64_t x_off) {
   const WsLayout W = ws_layout(P.F, P.k);
   const Blk bk = xcd_block();
   float* base = P.ws + (int64_t)bk.z * W.stride;
   const float* X = base + x_off;
   double* Wd = reinterpret_cast<double*>(base + W.B);
-  const int k = P.k, tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int k = P.k, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ty = lane >> 3, tx = lane & 7;  // outputs 4 ty + a, 4 tx + b
   const int i0 = (int)bk.y * 32, j0 = (int)bk.x * 32;
-  __shared__ float si[16][33], sj[16][33];
-  double acc[2][2] = {};
-  for (int f0 = 0; f0 < P.F; f0 += 16) {
+  const int quarter = P.F / 4, fw = wave * quarter;
+  __shared__ float si[4][16][33], sj[4][16][33];
+  __shared__ double red[3][16][64];
+  double acc[4][4] = {};
+  for (int f0 = 0; f0 < quarter; f0 += 16) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = tid + kThreads * q;
+    for (int q = 0; q < 8; ++q) {  // the wave's 16 x 32 slices of both column blocks
+      const int idx = lane + 64 * q;
       const int r = idx >> 5, c = idx & 31;
-      si[r][c] = (i0 + c < k) ? X[(int64_t)(f0 + r) * k + i0 + c] : 0.f;
-      sj[r][c] = (j0 + c < k) ? X[(int64_t)(f0 + r) * k + j0 + c] : 0.f;
+      const int64_t row = (int64_t)(fw + f0 + r) * k;
+      si[wave][r][c] = (i0 + c < k) ? X[row + i0 + c] : 0.f;
+      sj[wave][r][c] = (j0 + c < k) ? X[row + j0 + c] : 0.f;
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
+    for (int r = 0; r < 16; ++r) {
+      double xi[4], xj[4];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 4; ++a) {
+        xi[a] = (double)si[wave][r][4 * ty + a];
+        xj[a] = (double)sj[wave][r][4 * tx + a];
+      }
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = fma((double)si[r][2 * ty + a], (double)sj[r][2 * tx + b], acc[a][b]);
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fma(xi[a], xj[b], acc[a][b]);
+    }
     __syncthreads();
   }
+  if (wave > 0) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int i = i0 + 2 * ty + a, jj = j0 + 2 * tx + b;
-      if (i < k && jj < k) Wd[(int64_t)i * k + jj] = acc[a][b];
+      for (int b = 0; b < 4; ++b) red[wave - 1][4 * a + b][lane] = acc[a][b];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const double v = acc[a][b] + red[0][4 * a + b][lane] + red[1][4 * a + b][lane] +
+                       red[2][4 * a + b][lane];
+      const int i = i0 + 4 * ty + a, jj = j0 + 4 * tx + b;
+      if (i < k && jj < k) Wd[(int64_t)i * k + jj] = v;
     }
 }
 
