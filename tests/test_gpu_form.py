@@ -131,6 +131,14 @@ def test_form_rank_above_width():
     assert not Ug[..., 64:].any() and not Vg[..., 64:].any()
 
 
+def test_form_many_problems():
+    # 2 layers x 16 chunks = 32 problems per channel at F = 512: the workspace GEMMs run
+    # with 8 x 32 = 256 workgroups of 64 rows, the form used at or above one per CU (the
+    # smaller batches of the other cases take the form with K split over the waves).
+    lens = tuple(24 + 5 * i for i in range(16))
+    _check(_w(lens=lens, tokens=sum(lens)), 16, label="32 problems per channel")
+
+
 def test_form_iterations_converge():
     # Fewer iterations leave the trailing singular values less converged (the error
     # falls like (lambda_{k+1} / lambda_i)^iterations); more meet the tight bounds.
