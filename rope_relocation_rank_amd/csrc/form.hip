@@ -508,17 +508,20 @@ __global__ __launch_bounds__(kThreads) void chol_rinv(FormArgs P) {
   const int k = P.k, tid = threadIdx.x;
   __shared__ double L[kMaxK][kMaxK + 1];
   __shared__ double col[kMaxK];
+  __shared__ double dg[kMaxK];  // L's diagonal, moved into L once the factor is done
   for (int e = tid; e < k * k; e += kThreads) L[e / k][e % k] = Wd[e];
   __syncthreads();
   for (int i = tid; i < k; i += kThreads) col[i] = L[i][i];  // diagonal of W
   __syncthreads();
+  // Column j: every thread reads the pivot L[j][j], which no thread writes during the
+  // column (the scaling writes rows below j, the update columns right of j), so one
+  // barrier after the scaling and one after the update order the steps.
   for (int j = 0; j < k; ++j) {
     const double d = L[j][j];
     const bool keep = d > 1e-12 * col[j] && d > 0.0;
     const double inv = keep ? 1.0 / sqrt(d) : 0.0;
-    __syncthreads();
     for (int i = j + 1 + tid; i < k; i += kThreads) L[i][j] *= inv;
-    if (tid == 0) L[j][j] = keep ? sqrt(d) : 0.0;
+    if (tid == 0) dg[j] = keep ? sqrt(d) : 0.0;
     __syncthreads();
     // Trailing update L[i][c] -= L[i][j] L[c][j], j < c <= i, on a 16 x 16 thread grid
     // (rows by tid >> 4, columns by tid & 15).
@@ -530,6 +533,8 @@ __global__ __launch_bounds__(kThreads) void chol_rinv(FormArgs P) {
     }
     __syncthreads();
   }
+  for (int i = tid; i < k; i += kThreads) L[i][i] = dg[i];
+  __syncthreads();
   // In-place inverse of the lower-triangular L (dropped columns stay zero).  For column
   // j, row i needs -(Linv[i][j+1..i] . L[j+1..i][j]) djj: four lanes share a row, each
   // summing every fourth term, and two lane exchanges combine them.
