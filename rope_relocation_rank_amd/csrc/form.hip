@@ -587,6 +587,10 @@ __global__ __launch_bounds__(kThreads) void jacobi_eig(FormArgs P) {
   }
   __syncthreads();
   const int half = k / 2;
+  // The rotation loops take elements e = tid, tid + kThreads, ... of a half x k array as
+  // (pair e / k, index e % k); both advance by fixed steps, so no loop divides.
+  const int r_init = tid / k, j_init = tid - r_init * k;
+  const int dq = kThreads / k, dr = kThreads - dq * k;
   for (int sweep = 0; sweep < 30; ++sweep) {
     float off = 0.f, tot = 0.f;
     for (int e = tid; e < k * k; e += kThreads) {
@@ -623,18 +627,22 @@ __global__ __launch_bounds__(kThreads) void jacobi_eig(FormArgs P) {
       }
       __syncthreads();
       // rows p, q of A
-      for (int e = tid; e < half * k; e += kThreads) {
-        const int r = e / k, j = e % k;
+      for (int r = r_init, j = j_init; r < half;) {
         const int p = pp[r], q = qq[r];
         const float c = cs[r], s = sn[r];
         const float ap = A[p][j], aq = A[q][j];
         A[p][j] = c * ap - s * aq;
         A[q][j] = s * ap + c * aq;
+        j += dr;
+        r += dq;
+        if (j >= k) {
+          j -= k;
+          ++r;
+        }
       }
       __syncthreads();
       // columns p, q of A and of V
-      for (int e = tid; e < half * k; e += kThreads) {
-        const int r = e / k, i = e % k;
+      for (int r = r_init, i = j_init; r < half;) {
         const int p = pp[r], q = qq[r];
         const float c = cs[r], s = sn[r];
         const float ap = A[i][p], aq = A[i][q];
@@ -643,6 +651,12 @@ __global__ __launch_bounds__(kThreads) void jacobi_eig(FormArgs P) {
         const float vp = V[i][p], vq = V[i][q];
         V[i][p] = c * vp - s * vq;
         V[i][q] = s * vp + c * vq;
+        i += dr;
+        r += dq;
+        if (i >= k) {
+          i -= k;
+          ++r;
+        }
       }
       __syncthreads();
     }
