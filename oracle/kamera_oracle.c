@@ -672,6 +672,16 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Host threads the OpenMP loops use from now on (n >= 1); the arithmetic and its order
+ * per element do not depend on it. */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int orc_struct_sizes(int which) {
     return which == 0 ? (int)sizeof(orc_channel) : (int)sizeof(orc_problem);
 }

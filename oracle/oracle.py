@@ -142,6 +142,8 @@ def lib():
         L.orc_attend.argtypes = [C.POINTER(_Problem), C.c_int, C.c_double, C.c_void_p,
                                  C.c_void_p, C.c_void_p, C.c_void_p]
         L.orc_num_threads.restype = C.c_int
+        L.orc_set_num_threads.restype = None
+        L.orc_set_num_threads.argtypes = [C.c_int]
         L.orc_struct_sizes.restype = C.c_int
         L.orc_struct_sizes.argtypes = [C.c_int]
         assert L.orc_struct_sizes(0) == C.sizeof(_Channel)
@@ -442,3 +444,8 @@ def attend(channels, *, num_layers: int, theta: float, offsets, delta, q, scale:
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Host threads of the oracle's loops from now on (the results do not change)."""
+    lib().orc_set_num_threads(int(n))
