@@ -61,7 +61,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="qwen25vl7b_segment")
+    ap.add_argument("--workload", default="long_video_72b_paged")
+    ap.add_argument("--no-workspace", action="store_true",
+                    help="call kamera_relocate_patch (logical order) even where "
+                         "kamera_relocate_patch_ws would sweep a paged pool in pool order")
     ap.add_argument("--copies", type=int, default=0, help="input copies (0 = enough for >= 2 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -130,9 +133,23 @@ def main():
     if w.recall:
         descs = [[ops.recall_descriptors(c) for c in row] for row in insts]
         plan_info = [ops.recall_plan(row[0]) for row in insts]
+        wss = [[None] * copies for _ in insts]
     else:
         descs = [[ops.descriptors_for(c) for c in row] for row in insts]
         plan_info = [ops.plan(row[0]) for row in insts]
+        # Workspace of kamera_relocate_patch_ws (pool order), one per input copy,
+        # allocated before the timed region.
+        wss = [[None if args.no_workspace else ops.workspace_for(c) for c in row]
+               for row in insts]
+    entry = []
+    for pi, r in enumerate(ranks):
+        if w.recall:
+            entry.append("kamera_recall_patch")
+        elif r == 0:
+            entry.append("kamera_relocate")
+        else:
+            entry.append("kamera_relocate_patch_ws" if wss[pi][0] is not None
+                         else "kamera_relocate_patch")
     lib = K.lib()
     import ctypes as C
 
@@ -146,8 +163,12 @@ def main():
                                          None if p is None else C.byref(p), s_ptr)
         else:
             kv, ch, p = descs[pi][ci]
+            ws = wss[pi][ci]
             if p is None:
                 st = lib.kamera_relocate(C.byref(kv), C.byref(ch), s_ptr)
+            elif ws is not None:
+                st = lib.kamera_relocate_patch_ws(C.byref(kv), C.byref(ch), C.byref(p),
+                                                  ws.data_ptr(), ws.numel(), s_ptr)
             else:
                 st = lib.kamera_relocate_patch(C.byref(kv), C.byref(ch), C.byref(p), s_ptr)
         if st != 0:
@@ -244,7 +265,7 @@ def main():
             "layers": w.layers, "kv_heads": w.heads, "head_dim": w.head_dim,
             "tokens": st.total_tokens, "chunks": st.num_chunks,
             "theta": w.theta, "passes_rank": list(ranks), "page_size": w.page_size,
-            "entry_point": "kamera_recall_patch" if w.recall else "kamera_relocate_patch",
+            "entry_point": entry[dominant],
             "dst_page_size": w.dst_page_size if w.recall else None,
             "bytes_per_step": bytes_step, "input_copies": copies,
             "parallelism": "single GPU",
@@ -628,14 +649,61 @@ def cpu_baseline(w, ranks, seconds: float):
         t += step(ww, probs)
         reps += 1
     b = reps * sum(synth.algorithmic_bytes(ww, r) for r in ranks)
-    return {
+    out = {
         "value": round(b / t / 1e9, 4),
         "unit": "GB/s",
         "cores": orc.num_threads(),
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"{reps} x ({layers} of {w.layers} layers of every pass m={list(ranks)}, all "
                   f"tokens); {t:.1f} s of compute, input generation excluded",
     }
+    out["single_thread"] = cpu_single_thread(seconds / 3)
+    return out
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (the first one listed)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_single_thread(seconds: float):
+    """The oracle on one host thread, as a scale reference: the Qwen2.5-VL-7B-shaped
+    segment's rotation-only pass (keys only, m = 0), leading layers sized to about
+    `seconds` of compute, GB/s over the same algorithmic bytes."""
+    from oracle import oracle as orc
+    from rope_relocation_rank_amd import synth
+
+    w = synth.get("qwen25vl7b_segment")
+    threads = orc.num_threads()
+    orc.set_num_threads(1)
+    try:
+        def run(layers):
+            ww = w.with_(layers=layers)
+            inp = synth.make_inputs(ww, 0, device="cpu")
+            bufs = [b.view(__import__("torch").int16).numpy().view(np.uint16).ravel()
+                    for b in inp.buffers]
+            chans = [dict(lay, data=bufs[lay["buffer"]]) for lay in inp.layouts]
+            t0 = time.perf_counter()
+            orc.relocate_patch(chans, num_layers=layers, theta=w.theta,
+                               offsets=inp.struct.offsets, delta=inp.struct.delta, rank=0,
+                               page_size=0, block_table=None)
+            return ww, time.perf_counter() - t0
+
+        ww, t1 = run(1)
+        layers = int(max(1, min(w.layers, seconds / max(t1, 1e-6))))
+        ww, t = run(layers)
+        return {"value": round(synth.algorithmic_bytes(ww, 0) / t / 1e9, 4), "unit": "GB/s",
+                "cores": 1, "sample": f"{w.key} rotation-only pass, {layers} of {w.layers} "
+                                      f"layers; {t:.1f} s of compute"}
+    finally:
+        orc.set_num_threads(threads)
 
 
 if __name__ == "__main__":

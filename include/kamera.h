@@ -73,7 +73,7 @@ extern "C" {
 #define KAMERA_API __attribute__((visibility("default")))
 #endif
 
-#define KAMERA_ABI_VERSION 3
+#define KAMERA_ABI_VERSION 4
 #define KAMERA_MAX_RANK 256   /* largest patch rank m accepted */
 
 typedef enum {
@@ -181,6 +181,32 @@ KAMERA_API kamera_status kamera_relocate(const kamera_kv_desc* kv, const kamera_
  * reuse equation.  patch == NULL or patch->rank == 0 behaves as kamera_relocate. */
 KAMERA_API kamera_status kamera_relocate_patch(const kamera_kv_desc* kv, const kamera_chunks* chunks,
                                     const kamera_patch* patch, hipStream_t stream);
+
+/* Relocate and patch with a caller workspace: the same operation and results as
+ * kamera_relocate_patch (Kamera page §2, reuse equation), element for element; only the
+ * order of the work differs.  When the call moves one chunk (num_chunks == 1) of a paged
+ * cache whose page_size is a multiple of 16 and whose pool holds at most four times the
+ * pages the chunk uses, the library first writes the inverse of the block table into
+ * the workspace (pool page -> logical page; int32 per pool page) and then sweeps the
+ * pool in page order, so that concurrent work touches neighbouring pool memory instead
+ * of the table's scattered pages.  Other calls run exactly as kamera_relocate_patch and
+ * leave the workspace alone.
+ *   workspace: caller-owned device memory, 16-byte aligned, of at least the bytes
+ *     kamera_relocate_workspace reports, or NULL (then the call is kamera_relocate_patch).
+ *     Overwritten.  It must not overlap the cache, the factors, the block table, the
+ *     offsets or the deltas (KAMERA_E_ALIAS); fewer bytes than needed: KAMERA_E_SHAPE.
+ * Stream-ordered like every entry point: calls that share a workspace must be ordered. */
+KAMERA_API kamera_status kamera_relocate_patch_ws(const kamera_kv_desc* kv,
+                                       const kamera_chunks* chunks,
+                                       const kamera_patch* patch, void* workspace,
+                                       int64_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace kamera_relocate_patch_ws uses for this problem: 0 when it runs as
+ * kamera_relocate_patch, else 4 bytes per pool page rounded up to 256.  Checks the
+ * arguments as the call does (no HIP call). */
+KAMERA_API kamera_status kamera_relocate_workspace(const kamera_kv_desc* kv,
+                                        const kamera_chunks* chunks,
+                                        const kamera_patch* patch, int64_t* bytes);
 
 /* Recall, out of place: rebuild chunks from their canonical store into other cache
  * slots.  Kamera page §3, the three cheap window operations, recall (reversible

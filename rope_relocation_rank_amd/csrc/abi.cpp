@@ -79,6 +79,10 @@ struct Plan {
   int rotate_unroll = 2;
   int valu = 0;  // rotate+patch in place: patch on VALU (measurement variant)
   int64_t units = 0;  // workgroups of the tuned launch(es)
+  // Pool order: with a workspace of pool_bytes, the rotate+patch launch sweeps the paged
+  // pool in page order through the inverse of the block table (0: not applicable).
+  int64_t pool_bytes = 0;
+  int pool_block_tokens = 0;  // tokens (pool slots) one pool-order workgroup covers
 };
 
 bool strides_ok(const kamera_channel& c) {
@@ -121,7 +125,8 @@ bool mfma_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, const kame
   const bool extent_ok =
       layer_extent(c, T, kv.page_size, kv.num_pages) * elem_bytes(kv.dtype) <=
           kamera::kMaxBufferBytes &&
-      (__int128)T * p.rank * factor_bytes(kv.dtype) <= kamera::kMaxBufferBytes;
+      (__int128)T * p.rank * factor_bytes(kv.dtype) <= kamera::kMaxBufferBytes &&
+      (__int128)c.heads * D * p.rank * factor_bytes(kv.dtype) <= kamera::kMaxBufferBytes;
   return tuned_dtype(kv.dtype) && !(kv.flags & KAMERA_FLAG_GENERIC) && p.rank <= kMfmaMaxRank &&
          (kv.dtype == KAMERA_BF16 || p.rank % 8 == 0) && rope_ok && dim_ok && extent_ok &&
          T < kMaxTunedTokens && aligned(c.data, vec_align(kv.dtype)) && aligned(p.U[ci], 16) &&
@@ -144,6 +149,12 @@ void plan_mfma(const kamera_kv_desc& kv, const kamera_chunks& ch, int m, const b
   if (tpw < 1 || tpw > kamera::kMaxBlockTokens / 64) tpw = dflt;
   plan->tiles_per_wave = tpw;
   plan->block_tokens = 64 * tpw;
+  // The pool-order sweep needs no table lookup before its first loads, so its
+  // workgroups start streaming sooner and shorter ones measured best: half the tiles.
+  const int pdflt = std::max(1, dflt / 2);
+  int ptpw = env_int("KAMERA_TILES_PER_WAVE", pdflt);
+  if (ptpw < 1 || ptpw > kamera::kMaxBlockTokens / 64) ptpw = pdflt;
+  plan->pool_block_tokens = 64 * ptpw;
   // KAMERA_PATCH_VALU=1 selects the VALU form of the patch (bf16 in place, rank <= 64)
   // for the MFMA-versus-VALU comparison; the tuned default is MFMA.
   plan->valu = env_int("KAMERA_PATCH_VALU", 0) != 0;
@@ -299,7 +310,17 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
     plan->kernel[c] = use[c] ? K_MFMA : K_GENERIC;
     if (!use[c]) plan->launches++;
   }
-  if (use[0] || use[1]) plan_mfma(*kv, *ch, m, use, plan);
+  if (use[0] || use[1]) {
+    plan_mfma(*kv, *ch, m, use, plan);
+    // Pool order: one chunk over a paged cache whose pages are multiples of 16 slots
+    // (each 16-token tile lies in one page) and whose pool is at most four times the
+    // pages the chunk uses (the sweep visits every pool page).
+    const int P = kv->page_size;
+    const int64_t lpages = P > 0 ? ceil_div(T, P) : 0;
+    if (P > 0 && P % 16 == 0 && ch->num_chunks == 1 && kv->num_pages <= 4 * lpages &&
+        env_int("KAMERA_POOL_ORDER", 1) != 0 && plan->valu == 0)
+      plan->pool_bytes = (kv->num_pages * 4 + 255) / 256 * 256;
+  }
   return KAMERA_OK;
 }
 
@@ -359,14 +380,60 @@ kamera_status hip_fail(hipError_t e, const char* what) {
   return fail(KAMERA_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Checks a relocate workspace against the plan: big enough and aligned when the plan
+// uses one, and clear of every buffer the call reads or writes.
+kamera_status check_workspace(const kamera_kv_desc* kv, const kamera_chunks* ch,
+                              const kamera_patch* p, const Plan& plan, const void* ws,
+                              int64_t ws_bytes) {
+  if (!ws || plan.pool_bytes == 0) return KAMERA_OK;
+  if (ws_bytes < plan.pool_bytes)
+    return fail(KAMERA_E_SHAPE, "workspace of %lld bytes; this call needs %lld",
+                (long long)ws_bytes, (long long)plan.pool_bytes);
+  if (!aligned(ws, 16)) return fail(KAMERA_E_ALIGN, "workspace not 16-byte aligned");
+  const int m = p ? p->rank : 0;
+  const int64_t es = elem_bytes(kv->dtype), fs = factor_bytes(kv->dtype);
+  const int64_t T = ch->total_tokens, n = ch->num_chunks;
+  for (int c = 0; c < kv->num_channels; ++c) {
+    int64_t kend = 0;
+    if (kv_extent(kv->ch[c], kv->num_layers, T, kv->page_size, kv->num_pages, es, &kend) &&
+        overlaps(kv->ch[c].data, kend, ws, plan.pool_bytes))
+      return fail(KAMERA_E_ALIAS, "workspace overlaps KV of channel %d", c);
+    if (m > 0) {
+      const int64_t F = (int64_t)kv->ch[c].heads * kv->ch[c].dim;
+      if (overlaps(p->U[c], (int64_t)kv->num_layers * T * m * fs, ws, plan.pool_bytes) ||
+          overlaps(p->V[c], (int64_t)kv->num_layers * n * F * m * fs, ws, plan.pool_bytes))
+        return fail(KAMERA_E_ALIAS, "workspace overlaps the factors of channel %d", c);
+    }
+  }
+  const int S = kv->num_sections > 1 ? kv->num_sections : 1;
+  if (overlaps(kv->block_table, ceil_div(T, kv->page_size) * 4, ws, plan.pool_bytes) ||
+      overlaps(ch->token_offsets, (n + 1) * 8, ws, plan.pool_bytes) ||
+      overlaps(ch->delta, n * S * 8, ws, plan.pool_bytes))
+    return fail(KAMERA_E_ALIAS, "workspace overlaps the block table, offsets or deltas");
+  return KAMERA_OK;
+}
+
 kamera_status run(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamera_patch* p,
-                  hipStream_t stream) {
+                  void* ws, int64_t ws_bytes, hipStream_t stream) {
   g_last_error.clear();
   Plan plan;
   kamera_status st = validate(kv, ch, p, &plan);
+  if (st != KAMERA_OK) return st;
+  if (ws_bytes < 0) return fail(KAMERA_E_SHAPE, "workspace_bytes < 0");
+  st = check_workspace(kv, ch, p, plan, ws, ws_bytes);
   if (st != KAMERA_OK || plan.launches == 0) return st;
   const int m = p ? p->rank : 0;
-  const kamera::CommonArgs cm = common_args(*kv, *ch, m, plan.block_tokens);
+  const bool pool = ws != nullptr && plan.pool_bytes > 0;
+  kamera::CommonArgs cm = common_args(*kv, *ch, m, pool ? plan.pool_block_tokens : plan.block_tokens);
+  if (pool) {
+    cm.inv = (const int32_t*)ws;
+    cm.num_logical_pages = ceil_div(ch->total_tokens, kv->page_size);
+    cm.pool_slots = kv->num_pages * kv->page_size;
+    cm.token_groups = ceil_div(cm.pool_slots, cm.block_tokens);
+    const hipError_t e = kamera::launch_table_inverse(kv->block_table, cm.num_logical_pages,
+                                                      kv->num_pages, (int32_t*)ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "block-table inverse launch");
+  }
   if (m == 0) {
     for (int c = 0; c < kv->num_channels; ++c) {
       if (plan.kernel[c] == K_NONE) continue;
@@ -400,7 +467,7 @@ kamera_status run(const kamera_kv_desc* kv, const kamera_chunks* ch, const kamer
   }
   if (ntuned > 0) {
     const hipError_t e =
-        kamera::launch_relocate_patch_rows(tuned, ntuned, cm, plan.valu, stream);
+        kamera::launch_relocate_patch_rows(tuned, ntuned, cm, plan.valu, pool, stream);
     if (e != hipSuccess) return hip_fail(e, "relocate+patch launch");
   }
   return KAMERA_OK;
@@ -420,7 +487,8 @@ bool recall_tuned_ok(const kamera_kv_desc& src, const kamera_kv_desc& dst, const
   const bool extent_ok =
       layer_extent(c, T, src.page_size, src.num_pages) * es <= kamera::kMaxBufferBytes &&
       layer_extent(d, T, dst.page_size, dst.num_pages) * es <= kamera::kMaxBufferBytes &&
-      (__int128)T * m * factor_bytes(src.dtype) <= kamera::kMaxBufferBytes;
+      (__int128)T * m * factor_bytes(src.dtype) <= kamera::kMaxBufferBytes &&
+      (__int128)c.heads * D * m * factor_bytes(src.dtype) <= kamera::kMaxBufferBytes;
   const bool factors_ok = m == 0 || (aligned(p->U[ci], 16) && aligned(p->V[ci], 16));
   const uintptr_t va = vec_align(src.dtype);
   return tuned_dtype(src.dtype) && !((src.flags | dst.flags) & KAMERA_FLAG_GENERIC) &&
@@ -546,7 +614,7 @@ kamera_status run_recall(const kamera_kv_desc* src, const kamera_kv_desc* dst,
   }
   if (ntuned > 0) {
     const hipError_t e =
-        kamera::launch_relocate_patch_rows(tuned, ntuned, cm, plan.valu, stream);
+        kamera::launch_relocate_patch_rows(tuned, ntuned, cm, plan.valu, false, stream);
     if (e != hipSuccess) return hip_fail(e, "recall launch");
   }
   return KAMERA_OK;
@@ -928,12 +996,30 @@ kamera_status kamera_recall_plan(const kamera_kv_desc* src, const kamera_kv_desc
 
 kamera_status kamera_relocate(const kamera_kv_desc* kv, const kamera_chunks* chunks,
                               hipStream_t stream) {
-  return run(kv, chunks, nullptr, stream);
+  return run(kv, chunks, nullptr, nullptr, 0, stream);
 }
 
 kamera_status kamera_relocate_patch(const kamera_kv_desc* kv, const kamera_chunks* chunks,
                                     const kamera_patch* patch, hipStream_t stream) {
-  return run(kv, chunks, patch, stream);
+  return run(kv, chunks, patch, nullptr, 0, stream);
+}
+
+kamera_status kamera_relocate_workspace(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                                        const kamera_patch* patch, int64_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(KAMERA_E_NULL, "bytes is NULL");
+  *bytes = 0;
+  Plan plan;
+  const kamera_status st = validate(kv, chunks, patch, &plan);
+  if (st != KAMERA_OK) return st;
+  *bytes = plan.pool_bytes;
+  return KAMERA_OK;
+}
+
+kamera_status kamera_relocate_patch_ws(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                                       const kamera_patch* patch, void* workspace,
+                                       int64_t workspace_bytes, hipStream_t stream) {
+  return run(kv, chunks, patch, workspace, workspace_bytes, stream);
 }
 
 kamera_status kamera_plan(const kamera_kv_desc* kv, const kamera_chunks* chunks,

@@ -57,6 +57,11 @@ struct CommonArgs {
   int32_t pairing;
   int32_t num_sections;
   int32_t sec_end[4];
+  // Pool order (rotate+patch in place over one chunk of a paged cache): inv[p] is the
+  // logical page that pool page p holds, -1 for none; pool_slots = num_pages * page_size.
+  const int32_t* inv;
+  int64_t num_logical_pages;
+  int64_t pool_slots;
   // Destination paging (out of place only).
   const int32_t* out_block_table;
   int64_t out_num_pages;
@@ -139,8 +144,16 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
 // that chunk boundaries cut when there is more than one chunk.
 // valu: the head launch of a bf16 in-place call with rank <= 64 (a multiple of 8) takes
 // the patch on VALU instead of MFMA (a measurement variant).
+// pool: sweep a paged cache in pool order through cm.inv (in place, one chunk, page size a
+// multiple of 16; channel blocks counted over cm.pool_slots); no tail launch.
 hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonArgs& cm,
-                                      int valu, hipStream_t s);
+                                      int valu, bool pool, hipStream_t s);
+
+// inv[p] = the index k of the block-table entry that names pool page p (entries outside
+// [0, num_pages) name none), -1 for pool pages no entry names; inv has num_pages entries.
+// Two launches: fill, then scatter (entries are pairwise distinct by precondition).
+hipError_t launch_table_inverse(const int32_t* table, int64_t entries, int64_t num_pages,
+                                int32_t* inv, hipStream_t s);
 
 // Plain per-row kernel: any dim, even rope_dim, rank <= KAMERA_MAX_RANK, bf16, fp32 or
 // fp8, element-aligned pointers.  In place with rank 0 it only touches rotated dims; out of

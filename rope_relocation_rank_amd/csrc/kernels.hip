@@ -11,6 +11,7 @@
 // element (t, f) (§2, "Aplicacao de Patch").
 //
 // Kernels:
+//   table_inverse_*      pool page -> logical page, into the caller's workspace (pool order)
 //   rotate_rows          m = 0 in place: only the rotated dims of rotating channels
 //                        are read and written (§3, sliding-window survival: no patch
 //                        is needed).
@@ -37,6 +38,15 @@
 // delta * omega_i is formed in fp64 with omega_i from the host, reduced by pi/2 in
 // fp64, and its cos and sin are rounded to fp32; all element arithmetic is fp32 with
 // one rounding to bf16 at the end.
+//
+// Keeping HBM busy is a matter of bytes in flight per CU.  A launch over one chunk
+// therefore (a) reads its uniform state (chunk end and delta, pool pages) with scalar
+// loads before anything else, (b) requests the chunk's feature factor straight into LDS
+// (no registers, no wait behind row data), and (c) has each wave request its first two
+// 16-token tiles together (NT = 2: two tiles in flight per wave at three waves per SIMD).
+// A paged cache with a caller workspace is swept in pool order (POOL): workgroups cover
+// consecutive pool slots, the inverse block table gives each tile's logical page, and
+// the tile's rows are requested before that lookup returns.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -96,21 +106,28 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
+// An offset chosen by a condition (row or kOob) reaches the access through an empty asm
+// operand: otherwise the compiler may split the access into branches on that condition,
+// and a load behind such a branch made it wait for every earlier load.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 __device__ __forceinline__ void bload_nt(rsrc_t r, uint32_t off, u32x4_t& v) {
-  v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+  v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)opaque(off), 0, 2);
 }
 __device__ __forceinline__ void bload_nt(rsrc_t r, uint32_t off, u32x2_t& v) {
-  v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 2);
+  v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)opaque(off), 0, 2);
 }
 __device__ __forceinline__ void bstore_nt(rsrc_t r, uint32_t off, const u32x4_t& v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 2);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)opaque(off), 0, 2);
 }
 __device__ __forceinline__ void bstore_nt(rsrc_t r, uint32_t off, const u32x2_t& v) {
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 2);
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)opaque(off), 0, 2);
 }
 // 16 bytes at `off` through a resource, cached (factor rows are re-read by other waves).
 __device__ __forceinline__ u32x4_t bload(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)opaque(off), 0, 0);
 }
 
 __device__ __forceinline__ float load_f(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
@@ -574,6 +591,7 @@ struct PatchCtx {
   bool lane_on, rot_lane;
   bool mixed;           // M-RoPE sections: some pairs may not turn
   float qs, qinv;       // fp8: the layer's dequantisation scale and its reciprocal
+  int lend;             // pool order: end of the logical tokens the call covers
 };
 
 // KV, row offsets and U fragments of one 16-token tile of a wave.
@@ -586,6 +604,11 @@ struct Tile {
   u32x4_t a[MK > 0 ? MK : 1];
 };
 
+// Token, inside a 16-token tile, of accumulator row 4g + i (lane group g = lane >> 4
+// holds rows 4g .. 4g + 3 of its column): the A operand's row rho carries the U row of
+// token tile_token(rho >> 2, rho & 3), so any one-to-one choice keeps the product right.
+__device__ __forceinline__ int tile_token(int g, int i) { return g + 4 * i; }
+
 // Loads tile kt (no rows when kt >= k_hi), keeping tokens in [t0, s1).  OUT: 0 in
 // place, 1 contiguous destination, 2 paged destination; a row is loaded only when both
 // its source and its destination slot exist.
@@ -597,7 +620,7 @@ __device__ __forceinline__ void load_tile(const PatchCtx<Q>& c, const CommonArgs
   const bool tile_on = kt < k_hi;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t t = ts + 4 * c.g + i;
+    const int64_t t = ts + tile_token(c.g, i);
     // Offsets only (no memory access depends on a branch): rows the lane skips load
     // zeros from and store nothing to offset kOob.
     uint32_t so = kOob, dso = kOob;
@@ -618,7 +641,7 @@ __device__ __forceinline__ void load_tile(const PatchCtx<Q>& c, const CommonArgs
     T.off[i] = OUT > 0 ? dso : so;
     bload_nt(c.rkv, so, T.x[i]);
   }
-  const int64_t tu = ts + c.c16;
+  const int64_t tu = ts + tile_token(c.c16 >> 2, c.c16 & 3);
   const bool uok = tile_on && tu < c.t1;
 #pragma unroll
   for (int ks = 0; ks < (MK > 0 ? MK : 1); ++ks) {
@@ -634,6 +657,91 @@ __device__ __forceinline__ void load_tile(const PatchCtx<Q>& c, const CommonArgs
       }
     }
   }
+  // The tile's requests leave together: the scheduler would otherwise sink the later U
+  // loads below the first waits on row data, serialising their latency.
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Pool order (in place, one chunk, pages of a multiple of 16 slots): the workgroup's
+// "tokens" are pool slots, so a tile is 16 consecutive slots of one page.  sbt holds
+// the logical page of each of the workgroup's pool pages (-1: the page holds none of
+// the call's tokens).  Row addresses come straight from the slot; only validity and the
+// U rows depend on the logical page.
+// KV rows of tile kt, loaded by pool slot alone, before the logical pages are known:
+// every row of the tile is requested (past the tile range: none) and stored nowhere until
+// pool_validate has seen its page.
+template <bool Q, int MK>
+__device__ __forceinline__ void pool_rows(const PatchCtx<Q>& c, const CommonArgs& cm, int kt,
+                                          int k_hi, Tile<Q, MK>& T) {
+  constexpr uint32_t es = sizeof(typename Codec<Q>::E);
+  const int ps = (int)c.tb0 + 16 * kt;  // pool slot of the tile's first row
+  const int P = cm.page_size;
+  const int pg = cm.page_shift >= 0 ? ps >> cm.page_shift : ps / P;
+  const int si = ps - pg * P;
+  const uint32_t rowb = (uint32_t)pg * (uint32_t)c.page_stride + (uint32_t)si * c.slot_stride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t so = kt < k_hi && c.lane_on
+                            ? (rowb + (uint32_t)tile_token(c.g, i) * c.slot_stride) * es + c.lane_b
+                            : kOob;
+    T.off[i] = kOob;
+    bload_nt(c.rkv, so, T.x[i]);
+  }
+}
+
+// Logical page of the pool page that holds tile kt (-1: none of the call's tokens), read
+// with a wave-uniform load; in the prologue, before any store, that is a scalar load, which
+// waits on its own counter rather than behind the wave's row loads.
+template <bool Q>
+__device__ __forceinline__ int pool_lpage(const PatchCtx<Q>& c, const CommonArgs& cm, int kt,
+                                          int k_hi) {
+  if (kt >= k_hi) return -1;
+  const int ps = (int)c.tb0 + 16 * kt;
+  const int pg = cm.page_shift >= 0 ? ps >> cm.page_shift : ps / cm.page_size;
+  const int32_t* __restrict__ inv = cm.inv;
+  const int v = inv[__builtin_amdgcn_readfirstlane(pg)];
+  return v >= 0 && v < cm.num_logical_pages ? v : -1;
+}
+
+// Store offsets and U rows of tile kt, whose pool page holds logical page lp: rows of a
+// page that holds none of the call's tokens, or tokens at or past lend, are not stored.
+// With LOAD the KV rows are requested here as well, only for those rows.
+template <bool Q, int MK, bool M8, bool LOAD>
+__device__ __forceinline__ void pool_validate(const PatchCtx<Q>& c, const CommonArgs& cm, int kt,
+                                              int lp, Tile<Q, MK>& T) {
+  constexpr uint32_t es = sizeof(typename Codec<Q>::E);
+  const int ps = (int)c.tb0 + 16 * kt;
+  const int P = cm.page_size;
+  const int pg = cm.page_shift >= 0 ? ps >> cm.page_shift : ps / P;
+  const int si = ps - pg * P;
+  // Logical token of the first row (tuned kernels keep token ids below 2^30); a page no
+  // entry names gives lend, so that none of its rows is stored.
+  const int tl = lp >= 0 ? lp * P + si : c.lend;
+  const uint32_t rowb = (uint32_t)pg * (uint32_t)c.page_stride + (uint32_t)si * c.slot_stride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = tile_token(c.g, i);
+    uint32_t so = kOob;
+    if (c.lane_on && tl + r < c.lend) so = (rowb + (uint32_t)r * c.slot_stride) * es + c.lane_b;
+    T.off[i] = so;
+    if constexpr (LOAD) bload_nt(c.rkv, so, T.x[i]);
+  }
+  const int tu = tl + tile_token(c.c16 >> 2, c.c16 & 3);
+  const bool uok = tu < (int)cm.total_tokens;
+#pragma unroll
+  for (int ks = 0; ks < (MK > 0 ? MK : 1); ++ks) {
+    T.a[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (MK > 0) {
+      const int k0 = 32 * ks + 8 * c.g;
+      if constexpr (M8) {
+        const uint32_t uo = uok && k0 < c.m ? ((uint32_t)tu * c.m + k0) * 2u : kOob;
+        T.a[ks] = bload(c.ru, uo);
+      } else if (uok) {
+        T.a[ks] = load_frag(c.Ul + tu * c.m, k0, c.m, false);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the tile's requests leave together
 }
 
 // Rotates, patches and stores a loaded tile.  HX is the NeoX partner lane distance, -1
@@ -830,6 +938,37 @@ __device__ __forceinline__ void patch_tiles(const PatchCtx<Q>& c, const CommonAr
   }
 }
 
+// One chunk, logical order: the wave's tiles kt = wave, wave + 4, ... up to the chunk's
+// end s1; A holds the first NT of them already (in flight together), the rest follow one
+// at a time.
+template <bool Q, int MK, bool M8, bool PAGED, int HX, int OUT, int NT>
+__device__ __forceinline__ void patch_tiles_batch(const PatchCtx<Q>& c, const CommonArgs& cm,
+                                                  const u32x4_t* sV, const float4* sph2,
+                                                  int64_t s1, Tile<Q, MK> (&A)[NT]) {
+  const int k_hi = (int)((s1 - c.tb0 + 15) >> 4);
+#pragma unroll
+  for (int i = 0; i < NT; ++i) finish_tile<Q, MK, HX, OUT>(c, sV, sph2, A[i]);
+  for (int kt = c.wave + kWavesPerBlock * NT; kt < k_hi; kt += kWavesPerBlock) {
+    load_tile<Q, MK, M8, PAGED, OUT>(c, cm, kt, k_hi, c.tb0, s1, A[0]);
+    finish_tile<Q, MK, HX, OUT>(c, sV, sph2, A[0]);
+  }
+}
+
+// Pool order: the wave's tiles kt = wave, wave + 4, ... of the workgroup's slot range;
+// A holds the first NT of them already (in flight together), the rest follow one at a
+// time.
+template <bool Q, int MK, bool M8, int HX, int NT>
+__device__ __forceinline__ void patch_tiles_pool(const PatchCtx<Q>& c, const CommonArgs& cm,
+                                                 const u32x4_t* sV, const float4* sph2,
+                                                 int k_hi, Tile<Q, MK> (&A)[NT]) {
+#pragma unroll
+  for (int i = 0; i < NT; ++i) finish_tile<Q, MK, HX, 0>(c, sV, sph2, A[i]);
+  for (int kt = c.wave + kWavesPerBlock * NT; kt < k_hi; kt += kWavesPerBlock) {
+    pool_validate<Q, MK, M8, true>(c, cm, kt, pool_lpage(c, cm, kt, k_hi), A[0]);
+    finish_tile<Q, MK, HX, 0>(c, sV, sph2, A[0]);
+  }
+}
+
 // Workgroup = one 128-feature block of one channel and layer over `block_tokens` tokens;
 // wave w takes the 16-token tiles w, w + 4, ....  The chunk the workgroup works on is
 // staged once in LDS (the B fragments of its feature factor, the phases of its delta),
@@ -849,8 +988,9 @@ __device__ __forceinline__ void patch_tiles(const PatchCtx<Q>& c, const CommonAr
 // and whole result rows written through the destination layout (OUT 1 contiguous, 2
 // paged); MK = 0 is its no-patch form.  Q: fp8 E4M3 elements (bf16 factors).  VALU
 // (bf16 in place, head launch): the patch on VALU instead of MFMA, for measurement.
-template <bool Q, int MK, bool M8, bool PAGED, bool TAIL, int OUT, bool VALU = false>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAIL || MK > 2 || (MK == 2 && OUT != 0) ? 1 : 4)))
+template <bool Q, int MK, bool M8, bool PAGED, bool TAIL, int OUT, bool VALU = false,
+          bool POOL = false, int NT = 1>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAIL || MK > 2 || (MK == 2 && OUT != 0) ? 1 : NT > 1 ? 3 : 4)))
 void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t blocks_per_layer,
                          int xcd_group) {
   __shared__ u32x4_t sV[8 * (MK > 0 ? MK : 1) * 64];
@@ -888,7 +1028,7 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
   using E = typename Codec<Q>::E;
   PatchCtx<Q> c;
   c.lane = lane;
-  c.wave = threadIdx.x >> 6;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar tile indices
   c.c16 = lane & 15;
   c.g = lane >> 4;
   c.m = cm.rank;
@@ -956,37 +1096,64 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
       from = first.j + 1;
     }
   } else {
+    // Pool order: the workgroup covers pool slots [tb0, t1) of num_pages * page_size.
     c.tb0 = tg * cm.block_tokens;
-    c.t1 = min(c.tb0 + (int64_t)cm.block_tokens, cm.total_tokens);
+    c.t1 = min(c.tb0 + (int64_t)cm.block_tokens, POOL ? cm.pool_slots : cm.total_tokens);
     start = c.tb0;
   }
   c.p0 = 0;
   c.op0 = 0;
   c.sbt = sbt;
   c.osbt = osbt;
-  if (PAGED) c.p0 = stage_block_table(cm, c.tb0, c.t1, sbt);
-  if (OUT == 2)
-    c.op0 = stage_table(cm.out_block_table, cm.out_num_pages, cm.out_page_size, c.tb0, c.t1, osbt);
+  c.lend = (int)cm.total_tokens;
 
-  // Stages chunk j's B fragments (and, when rotating, its phases) in LDS.
-  auto stage = [&](const ChunkRef& ck, bool rotate) {
-    const uint16_t* Vj = Vl + (int64_t)ck.j * F * m;
+  // B fragments of chunk j's feature factor into sV: thread item u of 2 * MK is sV[u *
+  // kBlock + threadIdx.x], feature fb + 8 (lane & 15) + n, ranks 32 ks + 8 (lane >> 4) ..
+  // + 7 with n * MK + ks = 4 u + wave.  Rows 16-byte aligned (M8): each item is one
+  // 16-byte load straight into LDS (past the factor's range it reads zeros), no
+  // registers held; the workgroup barrier's release waits for them.  Otherwise through
+  // registers.
+  auto stage_factor = [&](int j) {
+    const uint16_t* Vj = Vl + (int64_t)j * F * m;
+    if constexpr (M8 && MK > 0) {
+      const rsrc_t rv = make_rsrc(Vj, (uint32_t)((int64_t)F * m * 2));
 #pragma unroll
-    for (int u = 0; u < 2 * MK; ++u) {  // none when MK == 0
-      const int it = threadIdx.x + kBlock * u;
-      const int l = it & 63;
-      const int nk = it >> 6;  // n * MK + ks
-      const int n = nk / (MK > 0 ? MK : 1);
-      const int ks = nk - n * MK;
-      const int f = fb + 8 * (l & 15) + n;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (f < F) v = load_frag(Vj + (int64_t)f * m, 32 * ks + 8 * (l >> 4), m, M8);
-      sV[it] = v;
+      for (int u = 0; u < 2 * MK; ++u) {
+        const int nk = 4 * u + c.wave;  // n * MK + ks
+        const int n = nk / MK;
+        const int ks = nk - n * MK;
+        const int f = fb + 8 * c.c16 + n;
+        const int k0 = 32 * ks + 8 * c.g;
+        const uint32_t off = f < F && k0 < m ? ((uint32_t)f * (uint32_t)m + (uint32_t)k0) * 2u : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(sV + kBlock * u + 64 * c.wave), 16, off,
+            0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2 * MK; ++u) {  // none when MK == 0
+        const int it = threadIdx.x + kBlock * u;
+        const int l = it & 63;
+        const int nk = it >> 6;  // n * MK + ks
+        const int n = nk / (MK > 0 ? MK : 1);
+        const int ks = nk - n * MK;
+        const int f = fb + 8 * (l & 15) + n;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (f < F) v = load_frag(Vj + (int64_t)f * m, 32 * ks + 8 * (l >> 4), m, M8);
+        sV[it] = v;
+      }
     }
-    // One pair frequency per thread; (cos, sin) of pairs 2p and 2p + 1 are adjacent.
-    if (rotate && threadIdx.x < (r >> 1))
+  };
+  // One pair frequency per thread; (cos, sin) of pairs 2p and 2p + 1 are adjacent.
+  auto phases = [&](const ChunkRef& ck) {
+    if (threadIdx.x < (r >> 1))
       reinterpret_cast<float2*>(sph2)[threadIdx.x] =
           phase_of(KAMERA_CH(omega[threadIdx.x]), pair_delta(cm, ck, threadIdx.x));
+  };
+  // Stages chunk j's B fragments (and, when rotating, its phases) in LDS.
+  auto stage = [&](const ChunkRef& ck, bool rotate) {
+    stage_factor(ck.j);
+    if (rotate) phases(ck);
   };
 #define KAMERA_PATCH_SWITCH(USE)                                                                   \
   switch (rotate ? hx : 0) {                                                                       \
@@ -998,27 +1165,131 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
     default: patch_tiles<Q, MK, M8, PAGED, 0, OUT, VALU>(c, cm, sV, sph2, sUw, t0, s1, A, USE); break;  \
   }
 
-  if (PAGED || OUT == 2) __syncthreads();  // staged block tables
+  // A head launch over one chunk needs no chunk lookup: the chunk's feature factor is
+  // requested before anything else (straight into LDS), so the workgroup's wait for it
+  // overlaps the table staging and the first tiles' loads instead of queueing behind them.
+  const bool one = !TAIL && cm.num_chunks == 1;
+  // Wave-uniform lookups first, while nothing has been written yet (the compiler then
+  // makes them scalar loads, which do not wait behind the row loads): chunk 0's end and
+  // motion, and in pool order the logical page of each of the wave's first NT tiles.
+  ChunkRef ck0{0, 0, 0};
+  int64_t sd[4] = {0, 0, 0, 0};  // M-RoPE: chunk 0's section deltas
+  if (one) {
+    ck0.end = cm.offsets[1];
+    ck0.delta = chunk_moves(cm, 0);
+    if (cm.num_sections > 1) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sd[k] = k < cm.num_sections ? cm.delta[k] : 0;
+    }
+    if (POOL) c.lend = (int)max(min(ck0.end, cm.total_tokens), (int64_t)0);
+  }
+  // This thread's pair frequency (a per-thread read of the argument block: issued before
+  // the row loads, so waiting for it does not wait for them).
+  double om = 0.0;
+  if (one && threadIdx.x < (r >> 1)) {
+    if (second) om = ch1.omega[threadIdx.x];
+    else om = ch0.omega[threadIdx.x];
+  }
+  int lps[NT];
+  if (POOL) {
+    const int k_hi = (int)((c.t1 - c.tb0 + 15) >> 4);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) lps[i] = pool_lpage(c, cm, c.wave + kWavesPerBlock * i, k_hi);
+  }
+  if (one && M8) stage_factor(0);
+  // Pool order: the first tile's rows are requested by pool slot right away, before the
+  // logical pages (needed only for validity and the U rows) arrive.
+  // The wave's first NT tiles, requested together (one chunk); A is the first.
+  Tile<Q, MK> TB[NT];
+  Tile<Q, MK>& A = TB[0];
+  if (POOL) {
+    const int k_hi = (int)((c.t1 - c.tb0 + 15) >> 4);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) pool_rows<Q, MK>(c, cm, c.wave + kWavesPerBlock * i, k_hi, TB[i]);
+  } else if (PAGED) {
+    c.p0 = stage_block_table(cm, c.tb0, c.t1, sbt);
+  }
+  if (OUT == 2)
+    c.op0 = stage_table(cm.out_block_table, cm.out_num_pages, cm.out_page_size, c.tb0, c.t1, osbt);
+  if (PAGED && !POOL || OUT == 2) __syncthreads();  // staged tables
+
   if constexpr (!TAIL) {
     const int ntiles = (int)((c.t1 - c.tb0 + 15) >> 4);
-    // The wave's first tile is loaded before anything else, so its HBM latency
-    // overlaps the chunk lookup, the LDS staging and the barrier.
-    Tile<Q, MK> A;
-    load_tile<Q, MK, M8, PAGED, OUT>(c, cm, c.wave, ntiles, c.tb0, c.t1, A);
-    const ChunkRef ck = find_chunk_wave(cm, c.tb0);
-    const int64_t t0 = c.tb0, s1 = min(c.t1, ck.end);
-    if (s1 <= t0) return;  // offsets that do not cover the group: nothing here
-    // Tokens past the chunk's end belong to the tail kernel.
+    if (one) {
+      if constexpr (POOL) {
+        // Rows of pool pages that hold none of the call's tokens are left alone.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (c.tb0 + 16 * c.wave + 4 * c.g + i >= s1) A.off[i] = kOob;
-    const bool rotate = r > 0 && ck.delta != 0;
-    stage(ck, rotate);
-    __syncthreads();
-    KAMERA_PATCH_SWITCH(true)
+        for (int i = 0; i < NT; ++i)
+          pool_validate<Q, MK, M8, false>(c, cm, c.wave + kWavesPerBlock * i, lps[i], TB[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+          load_tile<Q, MK, M8, PAGED, OUT>(c, cm, c.wave + kWavesPerBlock * i, ntiles, c.tb0,
+                                           c.t1, TB[i]);
+      }
+      const ChunkRef ck = ck0;
+      if constexpr (!POOL) {
+        if (min(c.t1, ck.end) <= c.tb0) return;  // offsets that do not cover the group
+#pragma unroll
+        for (int b = 0; b < NT; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (c.tb0 + 16 * (c.wave + kWavesPerBlock * b) + tile_token(c.g, i) >= ck.end)
+              TB[b].off[i] = kOob;
+      }
+      const bool rotate = r > 0 && ck.delta != 0;
+      if (!M8) stage_factor(0);
+      if (rotate && threadIdx.x < (r >> 1)) {
+        // chunk 0's phases from the uniform loads above
+        int64_t d = ck.delta;
+        if (cm.num_sections > 1) {
+          const int sec = section_of(cm, threadIdx.x);
+          d = sec == 0 ? sd[0] : sec == 1 ? sd[1] : sec == 2 ? sd[2] : sd[3];
+        }
+        reinterpret_cast<float2*>(sph2)[threadIdx.x] = phase_of(om, d);
+      }
+      __syncthreads();
+      if constexpr (POOL) {
+        switch (rotate ? hx : 0) {
+          case 1: patch_tiles_pool<Q, MK, M8, 1, NT>(c, cm, sV, sph2, ntiles, TB); break;
+          case 2: patch_tiles_pool<Q, MK, M8, 2, NT>(c, cm, sV, sph2, ntiles, TB); break;
+          case 4: patch_tiles_pool<Q, MK, M8, 4, NT>(c, cm, sV, sph2, ntiles, TB); break;
+          case 8: patch_tiles_pool<Q, MK, M8, 8, NT>(c, cm, sV, sph2, ntiles, TB); break;
+          case -1: patch_tiles_pool<Q, MK, M8, -1, NT>(c, cm, sV, sph2, ntiles, TB); break;
+          default: patch_tiles_pool<Q, MK, M8, 0, NT>(c, cm, sV, sph2, ntiles, TB); break;
+        }
+      } else if constexpr (NT > 1) {
+        const int64_t s1 = min(c.t1, ck.end);
+        switch (rotate ? hx : 0) {
+          case 1: patch_tiles_batch<Q, MK, M8, PAGED, 1, OUT, NT>(c, cm, sV, sph2, s1, TB); break;
+          case 2: patch_tiles_batch<Q, MK, M8, PAGED, 2, OUT, NT>(c, cm, sV, sph2, s1, TB); break;
+          case 4: patch_tiles_batch<Q, MK, M8, PAGED, 4, OUT, NT>(c, cm, sV, sph2, s1, TB); break;
+          case 8: patch_tiles_batch<Q, MK, M8, PAGED, 8, OUT, NT>(c, cm, sV, sph2, s1, TB); break;
+          case -1: patch_tiles_batch<Q, MK, M8, PAGED, -1, OUT, NT>(c, cm, sV, sph2, s1, TB); break;
+          default: patch_tiles_batch<Q, MK, M8, PAGED, 0, OUT, NT>(c, cm, sV, sph2, s1, TB); break;
+        }
+      } else {
+        const int64_t t0 = c.tb0, s1 = min(c.t1, ck.end);
+        KAMERA_PATCH_SWITCH(true)
+      }
+    } else if constexpr (!POOL) {
+      // The wave's first tile is loaded before anything else, so its HBM latency
+      // overlaps the chunk lookup, the LDS staging and the barrier.
+      load_tile<Q, MK, M8, PAGED, OUT>(c, cm, c.wave, ntiles, c.tb0, c.t1, A);
+      const ChunkRef ck = find_chunk_wave(cm, c.tb0);
+      const int64_t t0 = c.tb0, s1 = min(c.t1, ck.end);
+      if (s1 <= t0) return;  // offsets that do not cover the group: nothing here
+      // Tokens past the chunk's end belong to the tail kernel.
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (c.tb0 + 16 * c.wave + tile_token(c.g, i) >= s1) A.off[i] = kOob;
+      const bool rotate = r > 0 && ck.delta != 0;
+      stage(ck, rotate);
+      __syncthreads();
+      KAMERA_PATCH_SWITCH(true)
+    }
   } else {
     // The remaining chunks of the group, one after the other.
-    Tile<Q, MK> A;
     int64_t t0 = start;
     ChunkRef ck = find_chunk_wave(cm, t0, from);
     bool staged = false;
@@ -1146,9 +1417,41 @@ __global__ __launch_bounds__(kBlock) void generic_rows(ChanArgs ch, CommonArgs c
   }
 }
 
+// ------------------------------------------------------------------ block-table inverse
+
+__global__ __launch_bounds__(kBlock) void table_inverse_fill(int32_t* inv, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock)
+    inv[i] = -1;
+}
+
+__global__ __launch_bounds__(kBlock) void table_inverse_scatter(const int32_t* table,
+                                                                int64_t entries,
+                                                                int64_t num_pages,
+                                                                int32_t* inv) {
+  for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < entries;
+       k += (int64_t)gridDim.x * kBlock) {
+    const int32_t pg = table[k];
+    if (pg >= 0 && pg < num_pages) inv[pg] = (int32_t)k;
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
+
+hipError_t launch_table_inverse(const int32_t* table, int64_t entries, int64_t num_pages,
+                                int32_t* inv, hipStream_t s) {
+  auto grid = [](int64_t n) {
+    int64_t b = (n + kBlock - 1) / kBlock;
+    return dim3((unsigned)(b < 1 ? 1 : b > 4096 ? 4096 : b));
+  };
+  hipLaunchKernelGGL(table_inverse_fill, grid(num_pages), dim3(kBlock), 0, s, inv, num_pages);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || entries == 0) return e;
+  hipLaunchKernelGGL(table_inverse_scatter, grid(entries), dim3(kBlock), 0, s, table, entries,
+                     num_pages, inv);
+  return hipGetLastError();
+}
 
 hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unroll,
                               hipStream_t s) {
@@ -1194,7 +1497,7 @@ hipError_t launch_rotate_rows(const ChanArgs& ch, const CommonArgs& cm, int unro
 }
 
 hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonArgs& cm_in,
-                                      int valu, hipStream_t s) {
+                                      int valu, bool pool, hipStream_t s) {
   ChanArgs c0 = ch[0];
   ChanArgs c1 = nch > 1 ? ch[1] : ch[0];
   if (nch == 1) c1.blocks = 0;
@@ -1215,12 +1518,46 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
   if (out > 0 && (!m8 || (nch > 1 && c1.out == nullptr))) return hipErrorInvalidValue;
   if (out == 0 && mk == 0) return hipErrorInvalidValue;
   if (q && !m8) return hipErrorInvalidValue;
+  if (pool) {
+    if (out > 0 || mk == 0 || cm.num_chunks != 1 || cm.page_size <= 0 || cm.page_size % 16 != 0 ||
+        cm.inv == nullptr)
+      return hipErrorInvalidValue;
+    // Tiles each wave requests together: its whole share when that is 2 or 3 tiles.
+    const int tpw = cm.block_tokens / 64;
+    const int pool_nt = (tpw == 2 || tpw == 3) && cm.block_tokens % 64 == 0 ? tpw : 1;
+#define KAMERA_LAUNCH_POOL_NT(Q, MK, M8, NT)                                                  \
+  hipLaunchKernelGGL((relocate_patch_rows<Q, MK, M8, true, false, 0, false, true, NT>), grid,   \
+                     dim3(kBlock), 0, s, c0, c1, cm, bpl, xg)
+#define KAMERA_LAUNCH_POOL(Q, MK, M8)                                    \
+  do {                                                                   \
+    if (pool_nt == 3) KAMERA_LAUNCH_POOL_NT(Q, MK, M8, 3);               \
+    else if (pool_nt == 2) KAMERA_LAUNCH_POOL_NT(Q, MK, M8, 2);          \
+    else KAMERA_LAUNCH_POOL_NT(Q, MK, M8, 1);                            \
+  } while (0)
+    if (q && mk == 1) KAMERA_LAUNCH_POOL(true, 1, true);
+    else if (q && mk == 2) KAMERA_LAUNCH_POOL(true, 2, true);
+    else if (q && mk <= 4) KAMERA_LAUNCH_POOL(true, 4, true);
+    else if (mk == 1) { if (m8) KAMERA_LAUNCH_POOL(false, 1, true); else KAMERA_LAUNCH_POOL(false, 1, false); }
+    else if (mk == 2) { if (m8) KAMERA_LAUNCH_POOL(false, 2, true); else KAMERA_LAUNCH_POOL(false, 2, false); }
+    else if (mk <= 4) { if (m8) KAMERA_LAUNCH_POOL(false, 4, true); else KAMERA_LAUNCH_POOL(false, 4, false); }
+    else return hipErrorInvalidValue;
+#undef KAMERA_LAUNCH_POOL
+#undef KAMERA_LAUNCH_POOL_NT
+    return hipGetLastError();
+  }
 #define KAMERA_LAUNCH_K(Q, MK, M8, PG, TL, OUT, XG)                                           \
   hipLaunchKernelGGL((relocate_patch_rows<Q, MK, M8, PG, TL, OUT>), grid, dim3(kBlock), 0, s, \
                      c0, c1, cm, bpl, XG)
+#define KAMERA_LAUNCH_B(Q, MK, M8, PG, XG)                                                    \
+  hipLaunchKernelGGL((relocate_patch_rows<Q, (MK > 2 ? 1 : MK), M8, PG, false, 0, false, false, \
+                                          2>),                                                  \
+                     grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, XG)
 #define KAMERA_LAUNCH_IN(MK, PG, TL, XG)                                      \
   do {                                                                        \
-    if (q) KAMERA_LAUNCH_K(true, MK, true, PG, TL, 0, XG);                    \
+    if (!TL && MK <= 2 && batch && q) KAMERA_LAUNCH_B(true, MK, true, PG, XG); \
+    else if (!TL && MK <= 2 && batch && m8) KAMERA_LAUNCH_B(false, MK, true, PG, XG); \
+    else if (!TL && MK <= 2 && batch) KAMERA_LAUNCH_B(false, MK, false, PG, XG); \
+    else if (q) KAMERA_LAUNCH_K(true, MK, true, PG, TL, 0, XG);               \
     else if (m8 && valu && !TL && MK <= 2)                                    \
       hipLaunchKernelGGL((relocate_patch_rows<false, MK, true, PG, false, 0,  \
                                               (MK <= 2 && !TL)>),             \
@@ -1255,7 +1592,11 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
     else if (mk <= 4) KAMERA_LAUNCH_PG(4, TL, XG);                            \
     else return hipErrorInvalidValue;                                         \
   } while (0)
+  // One chunk, in place, at least two tiles per wave: each wave requests its first two
+  // tiles together (two tiles in flight per wave at 3 waves per SIMD).
+  bool batch = cm.num_chunks == 1 && out == 0 && !valu && cm.block_tokens >= 128;
   KAMERA_LAUNCH_MK(false, xg);
+  batch = false;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || cm.num_chunks < 2) return e;
   // Groups that a chunk boundary cuts: indexed by boundary, or by group when chunks
@@ -1269,6 +1610,7 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
   grid = dim3((unsigned)((int64_t)cm.num_layers * bpl));
   KAMERA_LAUNCH_MK(true, 0);
 #undef KAMERA_LAUNCH_MK
+#undef KAMERA_LAUNCH_B
 #undef KAMERA_LAUNCH_PG
 #undef KAMERA_LAUNCH_OUT
 #undef KAMERA_LAUNCH_IN

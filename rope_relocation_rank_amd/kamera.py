@@ -18,14 +18,15 @@ LIB_PATH = os.path.join(PKG, "libkamera.so")
 KAMERA_OK, KAMERA_E_NULL, KAMERA_E_SHAPE, KAMERA_E_UNSUPPORTED = 0, 1, 2, 3
 KAMERA_E_ALIGN, KAMERA_E_ALIAS, KAMERA_E_HIP = 4, 5, 6
 KAMERA_BF16, KAMERA_F32, KAMERA_FP8_E4M3 = 0, 1, 2
-KAMERA_ABI_VERSION = 3
+KAMERA_ABI_VERSION = 4
 KAMERA_NEOX_HALF = 0
 KAMERA_INTERLEAVED = 1
 KAMERA_FLAG_GENERIC = 1
 KAMERA_MAX_RANK = 256
 KERNEL_NAMES = {0: "none", 1: "rotate", 2: "rotate+patch mfma", 3: "generic"}
 
-EXPORTED = ["kamera_relocate", "kamera_relocate_patch", "kamera_recall_patch", "kamera_plan",
+EXPORTED = ["kamera_relocate", "kamera_relocate_patch", "kamera_relocate_patch_ws",
+            "kamera_relocate_workspace", "kamera_recall_patch", "kamera_plan",
             "kamera_recall_plan", "kamera_form_workspace", "kamera_form_patch", "kamera_form_gram",
             "kamera_attend_workspace", "kamera_attend",
             "kamera_status_str", "kamera_last_error", "kamera_abi_version"]
@@ -100,6 +101,13 @@ def lib():
         L.kamera_relocate_patch.restype = C.c_int
         L.kamera_relocate_patch.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
                                             C.POINTER(kamera_patch), C.c_void_p]
+        L.kamera_relocate_patch_ws.restype = C.c_int
+        L.kamera_relocate_patch_ws.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
+                                               C.POINTER(kamera_patch), C.c_void_p, C.c_int64,
+                                               C.c_void_p]
+        L.kamera_relocate_workspace.restype = C.c_int
+        L.kamera_relocate_workspace.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
+                                                C.POINTER(kamera_patch), C.POINTER(C.c_int64)]
         L.kamera_plan.restype = C.c_int
         L.kamera_plan.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
                                   C.POINTER(kamera_patch), C.POINTER(kamera_plan_info)]
@@ -147,6 +155,18 @@ def kamera_relocate(kv: kamera_kv_desc, chunks: kamera_chunks, stream) -> int:
 def kamera_relocate_patch(kv: kamera_kv_desc, chunks: kamera_chunks, patch, stream) -> int:
     return lib().kamera_relocate_patch(C.byref(kv), C.byref(chunks),
                                        None if patch is None else C.byref(patch), stream)
+
+
+def kamera_relocate_patch_ws(kv: kamera_kv_desc, chunks: kamera_chunks, patch, workspace,
+                             workspace_bytes: int, stream) -> int:
+    return lib().kamera_relocate_patch_ws(_ref(kv), _ref(chunks), _ref(patch), workspace,
+                                          workspace_bytes, stream)
+
+
+def kamera_relocate_workspace(kv, chunks, patch=None):
+    n = C.c_int64(0)
+    st = lib().kamera_relocate_workspace(_ref(kv), _ref(chunks), _ref(patch), C.byref(n))
+    return st, n.value
 
 
 def kamera_plan(kv, chunks, patch=None):
@@ -271,6 +291,15 @@ def relocate_patch_(kv: kamera_kv_desc, chunks: kamera_chunks, patch=None, strea
         check(kamera_relocate(kv, chunks, s))
     else:
         check(kamera_relocate_patch(kv, chunks, patch, s))
+
+
+def relocate_patch_ws_(kv: kamera_kv_desc, chunks: kamera_chunks, patch, workspace,
+                       stream=None) -> None:
+    """Enqueue kamera_relocate_patch_ws; `workspace` is a torch uint8 tensor (or None)."""
+    s = current_stream() if stream is None else stream
+    ws = None if workspace is None else workspace.data_ptr()
+    nb = 0 if workspace is None else workspace.numel()
+    check(kamera_relocate_patch_ws(kv, chunks, patch, ws, nb, s))
 
 
 def recall_patch(src: kamera_kv_desc, dst: kamera_kv_desc, chunks: kamera_chunks, patch=None,

@@ -48,6 +48,26 @@ def run(inp, stream=None, flags: int = 0) -> None:
     K.relocate_patch_(kv, ch, patch, stream)
 
 
+def workspace_for(inp, flags: int = 0):
+    """Workspace tensor for kamera_relocate_patch_ws on `inp` (None when it needs none)."""
+    import torch
+    kv, ch, patch = descriptors_for(inp, flags)
+    st, nbytes = K.kamera_relocate_workspace(kv, ch, patch)
+    K.check(st)
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=inp.buffers[0].device)
+
+
+def run_ws(inp, workspace=None, stream=None, flags: int = 0) -> None:
+    """Apply the operator in place through kamera_relocate_patch_ws (pool order when the
+    problem takes it); `workspace` from workspace_for, or None to size one here."""
+    kv, ch, patch = descriptors_for(inp, flags)
+    if workspace is None:
+        workspace = workspace_for(inp, flags)
+    K.relocate_patch_ws_(kv, ch, patch, workspace, stream)
+
+
 def plan(inp, flags: int = 0):
     kv, ch, patch = descriptors_for(inp, flags)
     st, info = K.kamera_plan(kv, ch, patch)

@@ -35,7 +35,7 @@ def test_library_loads_and_exports_every_declared_function():
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     assert set(names) <= exported
     assert not [e for e in exported if "launch" in e], "internal symbols leak"
-    assert K.kamera_abi_version() == 3
+    assert K.kamera_abi_version() == 4
 
 
 def test_struct_layout_matches_header():
@@ -355,6 +355,62 @@ def test_chunk_boundary_tail_launch():
     assert info.units == 28 * 2 * fb * (2 * groups)
     _, info = plan_names(*gqa(T=4096, m=0, n=5))  # rotation only: one kernel, no tail
     assert info.launches == 1
+
+
+# ----------------------------------------------------------------- pool order (workspace)
+
+def ws_bytes(kv, ch, p):
+    st, n = K.kamera_relocate_workspace(kv, ch, p)
+    assert st == K.KAMERA_OK, K.kamera_last_error()
+    return n
+
+
+def test_relocate_workspace_size():
+    # One chunk over a paged cache (pages of 16 slots): 4 bytes per pool page, rounded up
+    # to 256; the same problem contiguous, with several chunks, at rank 0 or with a pool
+    # far larger than the chunk's pages needs none.
+    assert ws_bytes(*gqa(T=32768, L=80, H=8, m=64, paged=True, pages=2048)) == 2048 * 4
+    assert ws_bytes(*gqa(T=1000, L=2, m=64, paged=True, pages=100)) == 512
+    assert ws_bytes(*gqa(T=1000, L=2, m=64, paged=True, pages=63 * 4)) == 1024
+    assert ws_bytes(*gqa(T=1000, L=2, m=64, paged=True, pages=63 * 4 + 1)) == 0
+    assert ws_bytes(*gqa(T=32768, m=64)) == 0
+    assert ws_bytes(*gqa(T=32768, L=2, m=64, paged=True, pages=2048, n=3)) == 0
+    assert ws_bytes(*gqa(T=32768, L=2, m=0, paged=True, pages=2048)) == 0
+    assert ws_bytes(*gqa(T=0, L=2, m=64, paged=True, pages=2048)) == 0
+    assert ws_bytes(*gqa(T=32768, L=2, m=64, paged=True, pages=2048,
+                         dtype=K.KAMERA_FP8_E4M3)) == 2048 * 4
+    kv, ch, p = gqa(T=32768, L=2, m=64, paged=True, pages=2048)
+    kv.page_size = 8  # a 16-token tile would span two pages
+    kv.ch[0].page_stride = kv.ch[1].page_stride = 8 * 4 * 128
+    assert ws_bytes(kv, ch, p) == 0
+    # the size query checks the arguments like the call
+    kv, ch, p = gqa(T=4096, m=64, paged=True, pages=256)
+    kv.ch[0].rope_dim = 3
+    st, n = K.kamera_relocate_workspace(kv, ch, p)
+    assert st == K.KAMERA_E_SHAPE and n == 0
+    assert K.lib().kamera_relocate_workspace(C.byref(kv), C.byref(ch), C.byref(p), None) == \
+        K.KAMERA_E_NULL
+
+
+def test_relocate_patch_ws_checks_before_launch():
+    kv, ch, p = gqa(T=4096, L=2, m=64, paged=True, pages=256)
+    need = ws_bytes(kv, ch, p)
+    assert need == 1024
+    ws = FAKE + (9 << 40)
+    # too small, misaligned, negative size: rejected before any HIP call
+    assert K.kamera_relocate_patch_ws(kv, ch, p, ws, need - 1, None) == K.KAMERA_E_SHAPE
+    assert "workspace" in K.kamera_last_error()
+    assert K.kamera_relocate_patch_ws(kv, ch, p, ws + 4, need, None) == K.KAMERA_E_ALIGN
+    assert K.kamera_relocate_patch_ws(kv, ch, p, ws, -1, None) == K.KAMERA_E_SHAPE
+    # overlapping the cache, the factors or the block table
+    for addr in (kv.ch[1].data + 64, p.U[0] + 256, p.V[1], kv.block_table):
+        assert K.kamera_relocate_patch_ws(kv, ch, p, addr, need, None) == K.KAMERA_E_ALIAS, addr
+    # argument errors of the operator itself come first
+    kv.ch[0].rope_dim = 3
+    assert K.kamera_relocate_patch_ws(kv, ch, p, ws, need, None) == K.KAMERA_E_SHAPE
+    # an empty problem with a workspace is fine and launches nothing
+    kv, ch, p = gqa(T=0, L=2, m=64, paged=True, pages=256)
+    assert K.kamera_relocate_patch_ws(kv, ch, p, ws, 1024, None) == K.KAMERA_OK
 
 
 # ----------------------------------------------------------------- recall (out of place)
