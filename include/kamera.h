@@ -201,6 +201,21 @@ KAMERA_API kamera_status kamera_relocate_patch_ws(const kamera_kv_desc* kv,
                                        const kamera_patch* patch, void* workspace,
                                        int64_t workspace_bytes, hipStream_t stream);
 
+/* kamera_relocate_patch_ws for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * results, with the inverse block table held in a library-owned device array instead of
+ * a caller workspace.  Nothing is allocated: the array (4 MiB, room for 1,048,576 pool
+ * pages) is part of the library's device code, one copy per GPU, kept until the process
+ * ends; the first call on a GPU looks its address up (a runtime query, no allocation).
+ * A problem that would use more pool pages than that returns KAMERA_E_SHAPE before any
+ * HIP call (kamera_relocate_patch_ws takes any size).  Every call on one GPU shares its
+ * array: calls on that GPU that may overlap in time (different streams, no ordering)
+ * race and must be ordered by the caller.  Problems that need no inverse table run as
+ * kamera_relocate_patch.  Errors as for kamera_relocate_patch. */
+KAMERA_API kamera_status kamera_relocate_patch_noalloc(const kamera_kv_desc* kv,
+                                            const kamera_chunks* chunks,
+                                            const kamera_patch* patch, hipStream_t stream);
+
 /* Bytes of workspace kamera_relocate_patch_ws uses for this problem: 0 when it runs as
  * kamera_relocate_patch, else 4 bytes per pool page rounded up to 256.  Checks the
  * arguments as the call does (no HIP call). */

@@ -1004,6 +1004,24 @@ kamera_status kamera_relocate_patch(const kamera_kv_desc* kv, const kamera_chunk
   return run(kv, chunks, patch, nullptr, 0, stream);
 }
 
+kamera_status kamera_relocate_patch_noalloc(const kamera_kv_desc* kv, const kamera_chunks* chunks,
+                                            const kamera_patch* patch, hipStream_t stream) {
+  g_last_error.clear();
+  Plan plan;
+  const kamera_status st = validate(kv, chunks, patch, &plan);
+  if (st != KAMERA_OK) return st;
+  if (plan.pool_bytes > kamera::kScratchPoolPages * 4)
+    return fail(KAMERA_E_SHAPE,
+                "pool of %lld pages exceeds the library scratch of %lld pages "
+                "(kamera_relocate_patch_ws takes any size)",
+                (long long)kv->num_pages, (long long)kamera::kScratchPoolPages);
+  if (plan.launches == 0 || plan.pool_bytes == 0) return run(kv, chunks, patch, nullptr, 0, stream);
+  int32_t* ws = nullptr;
+  const hipError_t e = kamera::scratch_inverse_table(stream, &ws);
+  if (e != hipSuccess) return hip_fail(e, "scratch address lookup");
+  return run(kv, chunks, patch, ws, plan.pool_bytes, stream);
+}
+
 kamera_status kamera_relocate_workspace(const kamera_kv_desc* kv, const kamera_chunks* chunks,
                                         const kamera_patch* patch, int64_t* bytes) {
   g_last_error.clear();

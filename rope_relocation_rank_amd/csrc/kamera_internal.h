@@ -155,6 +155,12 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
 hipError_t launch_table_inverse(const int32_t* table, int64_t entries, int64_t num_pages,
                                 int32_t* inv, hipStream_t s);
 
+// Pool pages whose inverse table fits the library-held scratch array (4 MiB per GPU).
+constexpr int64_t kScratchPoolPages = (int64_t)1 << 20;
+// Device address of the scratch array on the GPU that `s` belongs to (looked up once per
+// GPU; no allocation).
+hipError_t scratch_inverse_table(hipStream_t s, int32_t** out);
+
 // Plain per-row kernel: any dim, even rope_dim, rank <= KAMERA_MAX_RANK, bf16, fp32 or
 // fp8, element-aligned pointers.  In place with rank 0 it only touches rotated dims; out of
 // place (ChanArgs::out set) it writes whole rows.

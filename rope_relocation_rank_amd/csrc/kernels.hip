@@ -49,6 +49,7 @@
 // the tile's rows are requested before that lookup returns.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "kamera_internal.h"
@@ -1211,7 +1212,7 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
   }
   if (OUT == 2)
     c.op0 = stage_table(cm.out_block_table, cm.out_num_pages, cm.out_page_size, c.tb0, c.t1, osbt);
-  if (PAGED && !POOL || OUT == 2) __syncthreads();  // staged tables
+  if ((PAGED && !POOL) || OUT == 2) __syncthreads();  // staged tables
 
   if constexpr (!TAIL) {
     const int ntiles = (int)((c.t1 - c.tb0 + 15) >> 4);
@@ -1435,7 +1436,46 @@ __global__ __launch_bounds__(kBlock) void table_inverse_scatter(const int32_t* t
   }
 }
 
+// ------------------------------------------------------------------ library-held scratch
+
+// The inverse block table of the no-allocation entry point: one array per GPU the
+// library runs on, kept until the process ends.  Host code never names it except to look
+// its address up (scratch_inverse_table); kernels get that address as an argument.
+static __device__ __align__(256) int32_t scratch[kScratchPoolPages];
+
 }  // namespace
+
+// ------------------------------------------------------------------ library-held scratch
+
+hipError_t scratch_inverse_table(hipStream_t s, int32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  hipDevice_t dev = 0;
+  hipError_t e = hipStreamGetDevice(s, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // Each GPU holds its own copy of the array; its address is looked up once, with that
+    // GPU current.
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = static_cast<int32_t*>(addr[dev]);
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------ launchers
 

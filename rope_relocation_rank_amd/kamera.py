@@ -26,6 +26,7 @@ KAMERA_MAX_RANK = 256
 KERNEL_NAMES = {0: "none", 1: "rotate", 2: "rotate+patch mfma", 3: "generic"}
 
 EXPORTED = ["kamera_relocate", "kamera_relocate_patch", "kamera_relocate_patch_ws",
+            "kamera_relocate_patch_noalloc",
             "kamera_relocate_workspace", "kamera_recall_patch", "kamera_plan",
             "kamera_recall_plan", "kamera_form_workspace", "kamera_form_patch", "kamera_form_gram",
             "kamera_attend_workspace", "kamera_attend",
@@ -105,6 +106,10 @@ def lib():
         L.kamera_relocate_patch_ws.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
                                                C.POINTER(kamera_patch), C.c_void_p, C.c_int64,
                                                C.c_void_p]
+        L.kamera_relocate_patch_noalloc.restype = C.c_int
+        L.kamera_relocate_patch_noalloc.argtypes = [C.POINTER(kamera_kv_desc),
+                                                    C.POINTER(kamera_chunks),
+                                                    C.POINTER(kamera_patch), C.c_void_p]
         L.kamera_relocate_workspace.restype = C.c_int
         L.kamera_relocate_workspace.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
                                                 C.POINTER(kamera_patch), C.POINTER(C.c_int64)]
@@ -161,6 +166,11 @@ def kamera_relocate_patch_ws(kv: kamera_kv_desc, chunks: kamera_chunks, patch, w
                              workspace_bytes: int, stream) -> int:
     return lib().kamera_relocate_patch_ws(_ref(kv), _ref(chunks), _ref(patch), workspace,
                                           workspace_bytes, stream)
+
+
+def kamera_relocate_patch_noalloc(kv: kamera_kv_desc, chunks: kamera_chunks, patch,
+                                  stream) -> int:
+    return lib().kamera_relocate_patch_noalloc(_ref(kv), _ref(chunks), _ref(patch), stream)
 
 
 def kamera_relocate_workspace(kv, chunks, patch=None):

@@ -413,6 +413,25 @@ def test_relocate_patch_ws_checks_before_launch():
     assert K.kamera_relocate_patch_ws(kv, ch, p, ws, 1024, None) == K.KAMERA_OK
 
 
+def test_relocate_patch_noalloc_size_limit():
+    # The library-held inverse table has room for 2^20 pool pages; a pool-order problem
+    # with more is rejected before any HIP call, one that fits reports 4 MiB of workspace.
+    T = (1 << 20) * 4  # tokens of 16-slot pages: a pool of 2^20 pages is within 4x
+    kv, ch, p = gqa(T=T, L=1, H=1, D=16, r=16, m=8, paged=True, pages=1 << 20)
+    assert ws_bytes(kv, ch, p) == (1 << 20) * 4
+    kv, ch, p = gqa(T=T + 1024, L=1, H=1, D=16, r=16, m=8, paged=True, pages=(1 << 20) + 16)
+    assert ws_bytes(kv, ch, p) > (1 << 20) * 4
+    assert K.kamera_relocate_patch_noalloc(kv, ch, p, None) == K.KAMERA_E_SHAPE
+    assert "scratch" in K.kamera_last_error()
+    # argument errors come first, as for the other entry points
+    kv.ch[0].rope_dim = 3
+    assert K.kamera_relocate_patch_noalloc(kv, ch, p, None) == K.KAMERA_E_SHAPE
+    assert "rope_dim" in K.kamera_last_error()
+    # an empty problem launches nothing
+    kv, ch, p = gqa(T=0, L=1, m=8, paged=True, pages=4)
+    assert K.kamera_relocate_patch_noalloc(kv, ch, p, None) == K.KAMERA_OK
+
+
 # ----------------------------------------------------------------- recall (out of place)
 
 def recall_dst(T=4096, L=28, H=4, D=128, r=128, pages=300, addr=FAKE + (5 << 40), dtype=None):
