@@ -990,7 +990,7 @@ __device__ __forceinline__ void patch_tiles_pool(const PatchCtx<Q>& c, const Com
 // paged); MK = 0 is its no-patch form.  Q: fp8 E4M3 elements (bf16 factors).  VALU
 // (bf16 in place, head launch): the patch on VALU instead of MFMA, for measurement.
 template <bool Q, int MK, bool M8, bool PAGED, bool TAIL, int OUT, bool VALU = false,
-          bool POOL = false, int NT = 1>
+          bool POOL = false, int NT = 1, int CH = 0>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAIL || MK > 2 || (MK == 2 && OUT != 0) ? 1 : NT > 1 ? 3 : 4)))
 void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t blocks_per_layer,
                          int xcd_group) {
@@ -1169,7 +1169,9 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
   // A head launch over one chunk needs no chunk lookup: the chunk's feature factor is
   // requested before anything else (straight into LDS), so the workgroup's wait for it
   // overlaps the table staging and the first tiles' loads instead of queueing behind them.
-  const bool one = !TAIL && cm.num_chunks == 1;
+  // CH: 1 the launch moves one chunk, 2 several, 0 decided here (the batched head
+  // launches are compiled for one case each, so neither path's registers burden the other).
+  const bool one = CH == 1 ? true : CH == 2 ? false : !TAIL && cm.num_chunks == 1;
   // Wave-uniform lookups first, while nothing has been written yet (the compiler then
   // makes them scalar loads, which do not wait behind the row loads): chunk 0's end and
   // motion, and in pool order the logical page of each of the wave's first NT tiles.
@@ -1187,7 +1189,7 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
   // This thread's pair frequency (a per-thread read of the argument block: issued before
   // the row loads, so waiting for it does not wait for them).
   double om = 0.0;
-  if (one && threadIdx.x < (r >> 1)) {
+  if (!TAIL && threadIdx.x < (r >> 1)) {
     if (second) om = ch1.omega[threadIdx.x];
     else om = ch0.omega[threadIdx.x];
   }
@@ -1274,20 +1276,61 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
         KAMERA_PATCH_SWITCH(true)
       }
     } else if constexpr (!POOL) {
-      // The wave's first tile is loaded before anything else, so its HBM latency
-      // overlaps the chunk lookup, the LDS staging and the barrier.
-      load_tile<Q, MK, M8, PAGED, OUT>(c, cm, c.wave, ntiles, c.tb0, c.t1, A);
-      const ChunkRef ck = find_chunk_wave(cm, c.tb0);
+      // Several chunks.  The chunk lookup's loads go out first (lane k reads chunk k's end
+      // and motion), then the wave's first NT tiles up to the group's end, so resolving
+      // the chunk waits for the lookup alone; rows past the chunk's end are then dropped
+      // (the tail launch covers them).
+      const int n = cm.num_chunks;
+      int64_t e0 = INT64_MAX, d0 = 0;
+      if (lane < n) {
+        e0 = cm.offsets[lane + 1];
+        d0 = chunk_moves(cm, lane);
+      }
+#pragma unroll
+      for (int b = 0; b < NT; ++b)
+        load_tile<Q, MK, M8, PAGED, OUT>(c, cm, c.wave + kWavesPerBlock * b, ntiles, c.tb0, c.t1,
+                                         TB[b]);
+      ChunkRef ck{0, 0, 0};
+      const int cnt = __popcll(__ballot(e0 <= c.tb0));  // chunks that end at or before tb0
+      if (cnt < 64 || n <= 64) {
+        const int src = cnt < 64 ? cnt : 63;
+        ck.j = min(src, n - 1);
+        ck.end = __shfl(e0, src);
+        ck.delta = __shfl(d0, src);
+        if (src >= n) {  // past the last chunk: clamp to it
+          ck.j = n - 1;
+          ck.end = cm.offsets[n];
+          ck.delta = chunk_moves(cm, n - 1);
+        }
+      } else {
+        ck = find_chunk_wave(cm, c.tb0, 64);
+      }
       const int64_t t0 = c.tb0, s1 = min(c.t1, ck.end);
       if (s1 <= t0) return;  // offsets that do not cover the group: nothing here
-      // Tokens past the chunk's end belong to the tail kernel.
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (c.tb0 + 16 * c.wave + tile_token(c.g, i) >= s1) A.off[i] = kOob;
+      for (int b = 0; b < NT; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (c.tb0 + 16 * (c.wave + kWavesPerBlock * b) + tile_token(c.g, i) >= s1)
+            TB[b].off[i] = kOob;
       const bool rotate = r > 0 && ck.delta != 0;
-      stage(ck, rotate);
+      stage_factor(ck.j);
+      if (rotate && threadIdx.x < (r >> 1))
+        reinterpret_cast<float2*>(sph2)[threadIdx.x] =
+            phase_of(om, pair_delta(cm, ck, threadIdx.x));
       __syncthreads();
-      KAMERA_PATCH_SWITCH(true)
+      if constexpr (NT > 1) {
+        switch (rotate ? hx : 0) {
+          case 1: patch_tiles_batch<Q, MK, M8, PAGED, 1, OUT, NT>(c, cm, sV, sph2, s1, TB); break;
+          case 2: patch_tiles_batch<Q, MK, M8, PAGED, 2, OUT, NT>(c, cm, sV, sph2, s1, TB); break;
+          case 4: patch_tiles_batch<Q, MK, M8, PAGED, 4, OUT, NT>(c, cm, sV, sph2, s1, TB); break;
+          case 8: patch_tiles_batch<Q, MK, M8, PAGED, 8, OUT, NT>(c, cm, sV, sph2, s1, TB); break;
+          case -1: patch_tiles_batch<Q, MK, M8, PAGED, -1, OUT, NT>(c, cm, sV, sph2, s1, TB); break;
+          default: patch_tiles_batch<Q, MK, M8, PAGED, 0, OUT, NT>(c, cm, sV, sph2, s1, TB); break;
+        }
+      } else {
+        KAMERA_PATCH_SWITCH(true)
+      }
     }
   } else {
     // The remaining chunks of the group, one after the other.
@@ -1588,10 +1631,15 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
 #define KAMERA_LAUNCH_K(Q, MK, M8, PG, TL, OUT, XG)                                           \
   hipLaunchKernelGGL((relocate_patch_rows<Q, MK, M8, PG, TL, OUT>), grid, dim3(kBlock), 0, s, \
                      c0, c1, cm, bpl, XG)
-#define KAMERA_LAUNCH_B(Q, MK, M8, PG, XG)                                                    \
+#define KAMERA_LAUNCH_B2(Q, MK, M8, PG, XG, CHS)                                               \
   hipLaunchKernelGGL((relocate_patch_rows<Q, (MK > 2 ? 1 : MK), M8, PG, false, 0, false, false, \
-                                          2>),                                                  \
+                                          2, CHS>),                                             \
                      grid, dim3(kBlock), 0, s, c0, c1, cm, bpl, XG)
+#define KAMERA_LAUNCH_B(Q, MK, M8, PG, XG)                                   \
+  do {                                                                       \
+    if (cm.num_chunks == 1) KAMERA_LAUNCH_B2(Q, MK, M8, PG, XG, 1);          \
+    else KAMERA_LAUNCH_B2(Q, MK, M8, PG, XG, 2);                             \
+  } while (0)
 #define KAMERA_LAUNCH_IN(MK, PG, TL, XG)                                      \
   do {                                                                        \
     if (!TL && MK <= 2 && batch && q) KAMERA_LAUNCH_B(true, MK, true, PG, XG); \
@@ -1632,9 +1680,9 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
     else if (mk <= 4) KAMERA_LAUNCH_PG(4, TL, XG);                            \
     else return hipErrorInvalidValue;                                         \
   } while (0)
-  // One chunk, in place, at least two tiles per wave: each wave requests its first two
-  // tiles together (two tiles in flight per wave at 3 waves per SIMD).
-  bool batch = cm.num_chunks == 1 && out == 0 && !valu && cm.block_tokens >= 128;
+  // In place, at least two tiles per wave: each wave of the head launch requests its first
+  // two tiles together (two tiles in flight per wave).
+  bool batch = out == 0 && !valu && cm.block_tokens >= 128;
   KAMERA_LAUNCH_MK(false, xg);
   batch = false;
   hipError_t e = hipGetLastError();
@@ -1651,6 +1699,7 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
   KAMERA_LAUNCH_MK(true, 0);
 #undef KAMERA_LAUNCH_MK
 #undef KAMERA_LAUNCH_B
+#undef KAMERA_LAUNCH_B2
 #undef KAMERA_LAUNCH_PG
 #undef KAMERA_LAUNCH_OUT
 #undef KAMERA_LAUNCH_IN
