@@ -468,12 +468,32 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
   const int dtl = DR / H, dh = DR - dtl * H;
   const uint32_t dstep = (uint32_t)dtl * ss + (uint32_t)dh * hs;  // contiguous offset step
   const uint32_t carry = ss - (uint32_t)H * hs;                    // and its head-wrap carry
+  // One chunk: its end, motion and (M-RoPE) section deltas through wave-uniform loads,
+  // and this lane's pair frequency, all requested before the row loads, so the phases are
+  // formed while the rows are in flight.
+  const bool one = cm.num_chunks == 1;
+  ChunkRef c1{0, 0, 0};
+  int64_t sd[4] = {0, 0, 0, 0};
+  if (one) {
+    c1.end = cm.offsets[1];
+    c1.delta = SEC ? chunk_moves(cm, 0) : cm.delta[0];
+    if constexpr (SEC) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sd[k] = k < cm.num_sections ? cm.delta[k] : 0;
+    }
+  }
+  // More rows than one pass covers (only with more heads than a pass has rows): the
+  // general loop, kept apart so that the common single pass below is straight-line code
+  // (its row loads would otherwise wait on the frequency read at a loop header).
+  const double om = lane < HALF ? ch.omega[lane] : 0.0;
   int p0 = 0;
   if (PAGED) {
     p0 = stage_block_table(cm, tb0, t1, sbt);
     __syncthreads();
   }
-  for (int rbase = 0; rbase < nrows; rbase += ROWS) {
+  // One pass over ROWS rows of the block (a lambda so that the common single-pass case
+  // is straight-line code: a loop header makes the first row loads wait for earlier loads).
+  auto pass = [&](int rbase, double om) {
     XV xv[UNR];
     uint32_t boff[UNR];  // byte offset of the lane's 8 elements, kOob = no row
     int tlk[UNR];  // token of each row group, relative to tb0
@@ -510,17 +530,28 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
     }
     // Token span of this wave's rows in this pass.
     const int r_first = rbase + wave * RPI;
-    if (r_first >= nrows) continue;
+    if (r_first >= nrows) return;
     const int r_last = min(nrows - 1, rbase + (wave + kWavesPerBlock * (UNR - 1)) * RPI + RPI - 1);
     int64_t t0 = tb0 + r_first / H;
     const int64_t tw1 = tb0 + r_last / H + 1;
-    ChunkRef c = find_chunk_wave<SEC ? 1 : 0>(cm, t0);
+    ChunkRef c = one ? c1 : find_chunk_wave<SEC ? 1 : 0>(cm, t0);
     while (true) {
       const int64_t s1 = min(tw1, c.end);
       if (s1 > t0 && c.delta != 0) {
         const int lo = (int)(t0 - tb0), hi = (int)(s1 - tb0);  // rows' tokens to store
         float2 own = make_float2(1.f, 0.f);
-        if (lane < HALF) own = phase_of(ch.omega[lane], SEC ? pair_delta(cm, c, lane) : c.delta);
+        if (lane < HALF) {
+          int64_t d = c.delta;
+          if constexpr (SEC) {
+            if (one) {
+              const int sec = section_of(cm, lane);
+              d = sec == 0 ? sd[0] : sec == 1 ? sd[1] : sec == 2 ? sd[2] : sd[3];
+            } else {
+              d = pair_delta(cm, c, lane);
+            }
+          }
+          own = phase_of(om, d);
+        }
         float cs[8], sn[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -551,7 +582,12 @@ void rotate_rows(ChanArgs ch, CommonArgs cm) {
       if (t0 >= tw1 || c.j + 1 >= cm.num_chunks) break;
       c = find_chunk_wave<SEC ? 1 : 0>(cm, t0, c.j + 1);
     }
+  };
+  if (nrows > ROWS) {
+    for (int rbase = 0; rbase < nrows; rbase += ROWS) pass(rbase, ch.omega[lane < HALF ? lane : 0]);
+    return;
   }
+  pass(0, om);
 }
 
 // ------------------------------------------------------------------ rotation + patch (MFMA)
