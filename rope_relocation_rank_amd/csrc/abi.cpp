@@ -150,8 +150,10 @@ void plan_mfma(const kamera_kv_desc& kv, const kamera_chunks& ch, int m, const b
   plan->tiles_per_wave = tpw;
   plan->block_tokens = 64 * tpw;
   // The pool-order sweep needs no table lookup before its first loads, so its
-  // workgroups start streaming sooner and shorter ones measured best: half the tiles.
-  const int pdflt = std::max(1, dflt / 2);
+  // workgroups start streaming sooner and shorter ones measured best: two tiles per wave
+  // for bf16, three for fp8 (rows of half the bytes), each wave's whole share requested
+  // together.
+  const int pdflt = kv.dtype == KAMERA_FP8_E4M3 ? 3 : std::max(1, std::min(2, dflt));
   int ptpw = env_int("KAMERA_TILES_PER_WAVE", pdflt);
   if (ptpw < 1 || ptpw > kamera::kMaxBlockTokens / 64) ptpw = pdflt;
   plan->pool_block_tokens = 64 * ptpw;

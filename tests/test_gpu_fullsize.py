@@ -12,7 +12,8 @@ import parity  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 CASES = [("tiny_mha", 4), ("qwen25vl7b_segment", 0), ("qwen25vl7b_segment", 32),
-         ("llama3_8b_reorder", 16), ("deepseek_v3_mla", 64), ("long_video_72b_paged", 64)]
+         ("llama3_8b_reorder", 16), ("deepseek_v3_mla", 64), ("long_video_72b_paged", 64),
+         ("long_video_72b_paged_fp8", 64), ("qwen25vl7b_segment_fp8", 32)]
 
 
 @pytest.mark.parametrize("key,rank", CASES)
@@ -24,10 +25,14 @@ def test_full_size_sampled(key, rank):
     untouched = None
     if rank == 0:
         untouched = [b.clone() for c, b in enumerate(inp.buffers) if inp.layouts[c]["rope_dim"] == 0]
-    rep = parity.sampled_check(inp, ops.run, n=1024 if w.layers > 1 else 256)
+    # bench.py's launch configuration: the workspace entry point wherever the problem
+    # takes a workspace (pool order), else kamera_relocate_patch / kamera_relocate.
+    ws = ops.workspace_for(inp) if rank > 0 else None
+    run = (lambda i: ops.run_ws(i, ws)) if ws is not None else ops.run
+    rep = parity.sampled_check(inp, run, n=1024 if w.layers > 1 else 256)
     print(f"[full] kernels={[kamera.KERNEL_NAMES[k] for k in info.kernel]} {rep}", flush=True)
     assert rep.ok(), str(rep)
-    assert rep.band_only <= max(2, rep.computed // 10000), str(rep)
+    assert rep.band_only <= max(2, rep.computed // 100000), str(rep)
     if untouched:  # rotation only: the value channel is bit-for-bit unchanged
         vb = [b for c, b in enumerate(inp.buffers) if inp.layouts[c]["rope_dim"] == 0]
         for a, b in zip(untouched, vb):

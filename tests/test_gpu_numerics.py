@@ -70,6 +70,75 @@ def test_ties_round_to_even(flags):
     assert np.all((got.reshape(T, D)[ties] & 1) == 0)
 
 
+def test_rne_large_seeded_sample():
+    # A million fp32 values the kernel forms exactly, then rounds to bf16 itself: with
+    # delta = 0 and a rank-8 patch whose U row is (2^e, 2^e, 0, ...) and whose V row holds
+    # two 8-bit integers scaled by 2^-15 and 2^-23, element (t, f) is x + mid + low with
+    # x the bf16 input (exponent e) and mid, low filling the next 16 mantissa bits, so
+    # every partial sum is exact in fp32 whatever the accumulation order.  The kernel's
+    # round to nearest even must give the oracle's rounding of the exact value, bit for
+    # bit: random patterns, exact ties (mid = 0x80, low = 0) either way, one unit either
+    # side of a tie, a carry into the exponent, and NaN rows.
+    rng = np.random.default_rng(2024)
+    D, T, m = 128, 8192, 8
+    e = rng.integers(-60, 60, size=T)
+    sign = np.where(rng.integers(0, 2, size=(T, D)) == 1, -1.0, 1.0)
+    mant = rng.integers(128, 256, size=(T, D))           # 8 significant bits
+    # features 0, 1 hold exact ties: keep |y| in x's binade for negative x too
+    mant[:, :2] = rng.integers(129, 256, size=(T, 2))
+    mant[:, 8] = 255  # feature 8: all-ones mantissa, so rounding up carries into e + 1
+    x = sign * mant * 2.0 ** (e[:, None] - 7)
+    mid = rng.integers(0, 256, size=D).astype(np.float64)
+    low = rng.integers(0, 256, size=D).astype(np.float64)
+    special = [(128, 0), (128, 0), (128, 1), (127, 255), (0, 0), (255, 255), (128, 255), (0, 1),
+               (200, 0)]
+    for k, (a, b) in enumerate(special):  # ties, near-ties and the carry feature
+        mid[k], low[k] = a, b
+    nan_rows = rng.choice(T, size=16, replace=False)
+    x[nan_rows, 9] = np.nan
+    xb = orc.round_bf16(x.ravel())
+    assert np.array_equal(parity.bf16_value(xb)[~np.isnan(x.ravel())], x.ravel()[~np.isnan(x.ravel())])
+    U = np.zeros((T, m))
+    U[:, 0] = U[:, 1] = 2.0 ** e
+    Vm = np.zeros((D, m))
+    Vm[:, 0], Vm[:, 1] = mid * 2.0 ** -15, low * 2.0 ** -23
+    ub, vb = orc.round_bf16(U.ravel()), orc.round_bf16(Vm.ravel())
+    assert np.array_equal(parity.bf16_value(ub), U.ravel())
+    assert np.array_equal(parity.bf16_value(vb), Vm.ravel())
+    K = _bits_to_bf16_tensor(xb, (1, T, 1, D))
+    Vc = K.clone()
+    Ut = _bits_to_bf16_tensor(ub, (1, T, m))
+    Vt = _bits_to_bf16_tensor(vb, (1, 1, D, m))
+    lay = [dict(buffer=0, offset=0, heads=1, dim=D, rope_dim=D, layer_stride=T * D,
+                slot_stride=D, head_stride=D),
+           dict(buffer=1, offset=0, heads=1, dim=D, rope_dim=0, layer_stride=T * D,
+                slot_stride=D, head_stride=D)]
+    offs = torch.tensor([0, T], dtype=torch.int64, device=DEV)
+    dl = torch.tensor([0], dtype=torch.int64, device=DEV)
+    kv, ch, p = ops.descriptors([K, Vc], lay, dtype_code=kamera.KAMERA_BF16, num_layers=1,
+                                theta=1e4, offsets_t=offs, delta_t=dl, total_tokens=T, rank=m,
+                                U=(Ut, Ut), V=(Vt, Vt))
+    st, info = kamera.kamera_plan(kv, ch, p)
+    assert st == 0 and info.kernel[0] == 2  # the tuned rotate+patch kernel
+    kamera.relocate_patch_(kv, ch, p)
+    torch.cuda.synchronize()
+    got = parity.host_bits(K)
+    yv = x + (mid * 2.0 ** -15)[None, :] * 2.0 ** e[:, None] + (low * 2.0 ** -23)[None, :] * 2.0 ** e[:, None]
+    want = orc.round_bf16(yv.ravel())  # RNE of the exact value (exact in fp32 as well)
+    nan = np.isnan(yv.ravel())
+    assert np.array_equal(np.isnan(parity.bf16_value(got)), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # the sample holds the cases it claims: exact ties, both resolutions, and carries
+    ties = (mid == 128) & (low == 0)
+    assert ties.sum() == 2
+    tie_bits = got.reshape(T, D)[:, ties]
+    assert np.all((tie_bits & 1) == 0)  # ties went to the even neighbour
+    carried = np.abs(parity.bf16_value(got.reshape(T, D)[:, 8])) == 2.0 ** (e + 1)
+    assert carried.mean() > 0.4  # positive rows round 255 + 0.78 up to the next binade
+    print(f"[rne] {T * D} values, {int(ties.sum()) * T} exact ties, {len(nan_rows)} NaN",
+          flush=True)
+
+
 def test_nan_inf_overflow():
     D = 128
     vals = np.array([np.inf, -np.inf, np.nan, 3.38e38, -3.38e38, 0.0, -0.0, 1e-40] * 16)[:D]

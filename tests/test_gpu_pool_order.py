@@ -29,7 +29,7 @@ def _case(w, rank, label):
     rep = parity.check_problem(inp, lambda i: ops.run_ws(i, ws))
     print(f"[pool] {rep}", flush=True)
     assert rep.ok(), str(rep)
-    assert rep.band_only <= max(2, rep.computed // 10000), str(rep)
+    assert rep.band_only <= max(2, rep.computed // 100000), str(rep)
     return inp
 
 

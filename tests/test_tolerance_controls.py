@@ -73,7 +73,7 @@ def run_model(rows=600, D=128, H=8, m=64, theta=1e6, delta=65536, r=None, seed=0
 def test_correct_fp32_model_passes(theta, delta, m):
     rep = run_model(theta=theta, delta=delta, m=m)
     assert rep.ok(), str(rep)
-    assert rep.band_only <= rep.computed // 10000
+    assert rep.band_only <= max(2, rep.computed // 100000)
 
 
 @pytest.mark.parametrize("theta,delta", [(1e6, 65536), (1e4, 100000)])
