@@ -1641,15 +1641,16 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
     if (out > 0 || mk == 0 || cm.num_chunks != 1 || cm.page_size <= 0 || cm.page_size % 16 != 0 ||
         cm.inv == nullptr)
       return hipErrorInvalidValue;
-    // Tiles each wave requests together: its whole share when that is 2 or 3 tiles.
+    // Tiles each wave requests together: its whole share when that is 2 tiles, or 3 of
+    // fp8 (three bf16 tiles exceed the register budget of 3 waves per SIMD and spill).
     const int tpw = cm.block_tokens / 64;
-    const int pool_nt = (tpw == 2 || tpw == 3) && cm.block_tokens % 64 == 0 ? tpw : 1;
+    const int pool_nt = (tpw == 2 || (tpw == 3 && q)) && cm.block_tokens % 64 == 0 ? tpw : 1;
 #define KAMERA_LAUNCH_POOL_NT(Q, MK, M8, NT)                                                  \
   hipLaunchKernelGGL((relocate_patch_rows<Q, MK, M8, true, false, 0, false, true, NT>), grid,   \
                      dim3(kBlock), 0, s, c0, c1, cm, bpl, xg)
 #define KAMERA_LAUNCH_POOL(Q, MK, M8)                                    \
   do {                                                                   \
-    if (pool_nt == 3) KAMERA_LAUNCH_POOL_NT(Q, MK, M8, 3);               \
+    if (pool_nt == 3) KAMERA_LAUNCH_POOL_NT(Q, MK, M8, (Q ? 3 : 1));     \
     else if (pool_nt == 2) KAMERA_LAUNCH_POOL_NT(Q, MK, M8, 2);          \
     else KAMERA_LAUNCH_POOL_NT(Q, MK, M8, 1);                            \
   } while (0)
