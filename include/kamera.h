@@ -360,7 +360,7 @@ typedef struct {
                               3 generic */
   int32_t launches;        /* kernel launches the call would make (the rotate+patch kernel
                               takes a second launch for the token groups that chunk
-                              boundaries cut when num_chunks > 1) */
+                              boundaries cut when boundaries outnumber token groups) */
   int32_t tokens_per_unit; /* tokens one workgroup of a tuned kernel covers */
   int64_t units;           /* workgroups of the tuned launches */
 } kamera_plan_info;

@@ -136,7 +136,7 @@ bool mfma_tuned_ok(const kamera_kv_desc& kv, const kamera_channel& c, const kame
 
 // Launch shape of the rotate+patch kernel for the channels in `use`.
 void plan_mfma(const kamera_kv_desc& kv, const kamera_chunks& ch, int m, const bool* use,
-               Plan* plan) {
+               bool out_of_place, Plan* plan) {
   plan->launches++;
   // Each of the 4 wavefronts of a workgroup streams `tpw` 16-token tiles.  The
   // workgroup stages 8 KB of feature factor per 32 ranks once per chunk, so larger
@@ -160,12 +160,13 @@ void plan_mfma(const kamera_kv_desc& kv, const kamera_chunks& ch, int m, const b
   // KAMERA_PATCH_VALU=1 selects the VALU form of the patch (bf16 in place, rank <= 64)
   // for the MFMA-versus-VALU comparison; the tuned default is MFMA.
   plan->valu = env_int("KAMERA_PATCH_VALU", 0) != 0;
-  // A second launch covers the token groups that chunk boundaries cut.
+  // Token groups that chunk boundaries cut: in place, one more unit per boundary in the
+  // same launch; out of place, or with more boundaries than groups, a second launch.
   const int64_t T = ch.total_tokens;
   const int64_t groups = ceil_div(T, plan->block_tokens);
   const int64_t tail_units =
       ch.num_chunks < 2 ? 0 : std::min<int64_t>((int64_t)ch.num_chunks - 1, groups);
-  if (tail_units > 0) plan->launches++;
+  if (tail_units > 0 && (out_of_place || (int64_t)ch.num_chunks - 1 > groups)) plan->launches++;
   for (int c = 0; c < kv.num_channels; ++c)
     if (use[c])
       plan->units += (int64_t)kv.num_layers * (groups + tail_units) *
@@ -313,7 +314,7 @@ kamera_status validate(const kamera_kv_desc* kv, const kamera_chunks* ch, const 
     if (!use[c]) plan->launches++;
   }
   if (use[0] || use[1]) {
-    plan_mfma(*kv, *ch, m, use, plan);
+    plan_mfma(*kv, *ch, m, use, false, plan);
     // Pool order: one chunk over a paged cache whose pages are multiples of 16 slots
     // (each 16-token tile lies in one page) and whose pool is at most four times the
     // pages the chunk uses (the sweep visits every pool page).
@@ -568,7 +569,7 @@ kamera_status validate_recall(const kamera_kv_desc* src, const kamera_kv_desc* d
     plan->kernel[c] = use[c] ? K_MFMA : K_GENERIC;
     if (!use[c]) plan->launches++;
   }
-  if (use[0] || use[1]) plan_mfma(*src, *ch, m, use, plan);
+  if (use[0] || use[1]) plan_mfma(*src, *ch, m, use, true, plan);
   return KAMERA_OK;
 }
 

@@ -738,7 +738,8 @@ __global__ __launch_bounds__(kThreads) void split_vm(FormArgs P, int64_t v_off) 
   }
 }
 
-// The product: 64 tokens per workgroup (blockIdx.x), wave w the 16-token tile w.  Every
+// The product: 64-token tiles of the chunk, tile blockIdx.x + i * gridDim.x for
+// i = 0, 1, ... in workgroup x; wave w takes the 16-token slice w of a tile.  Every
 // 64 features the workgroup copies that block's fragments into LDS; each lane loads its
 // A fragment, 8 consecutive features of token c16 of its wave's tile, straight from HBM
 // (Delta rows 16-byte aligned), issued before the copy so that the load overlaps it.
@@ -753,8 +754,6 @@ __global__ __launch_bounds__(kThreads) void write_u_mfma(FormArgs P, int64_t p0)
   const int j = (int)(p - layer * P.num_chunks);
   const int64_t a = min(max(P.offsets[j], (int64_t)0), P.total_tokens);
   const int64_t b = min(max(P.offsets[j + 1], a), P.total_tokens);
-  const int64_t t0 = a + (int64_t)blockIdx.x * 64;
-  if (t0 >= b) return;  // the whole workgroup
   const uint16_t* D = P.delta + layer * P.total_tokens * P.F;
   uint16_t* Uo = P.U_out + layer * P.total_tokens * P.m;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -765,48 +764,51 @@ __global__ __launch_bounds__(kThreads) void write_u_mfma(FormArgs P, int64_t p0)
   const int nfrag = 2 * kUSteps * nv * 64;  // fragments of one 64-feature block
   const u32x4_t* frag =
       reinterpret_cast<const u32x4_t*>(P.ws + (int64_t)blockIdx.y * W.stride + W.G);
-  f32x4_t acc[kTiles];
+  // t0 is uniform over the workgroup, so every thread takes the loop's barriers.
+  for (int64_t t0 = a + (int64_t)blockIdx.x * 64; t0 < b; t0 += (int64_t)gridDim.x * 64) {
+    f32x4_t acc[kTiles];
 #pragma unroll
-  for (int ct = 0; ct < kTiles; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int64_t trow = t0 + 16 * wave + c16;  // this lane's A row
-  const bool row_ok = trow < b;
-  const uint16_t* drow = D + (row_ok ? trow : a) * F + 8 * g;
-  for (int f0 = 0; f0 < F; f0 += 32 * kUSteps) {  // F is a multiple of 64
-    u32x4_t av[kUSteps];
+    for (int ct = 0; ct < kTiles; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int64_t trow = t0 + 16 * wave + c16;  // this lane's A row
+    const bool row_ok = trow < b;
+    const uint16_t* drow = D + (row_ok ? trow : a) * F + 8 * g;
+    for (int f0 = 0; f0 < F; f0 += 32 * kUSteps) {  // F is a multiple of 64
+      u32x4_t av[kUSteps];
 #pragma unroll
-    for (int st = 0; st < kUSteps; ++st) {
-      av[st] = u32x4_t{0u, 0u, 0u, 0u};
-      if (row_ok) av[st] = __builtin_nontemporal_load((const u32x4_t*)(drow + f0 + 32 * st));
-    }
-    const u32x4_t* src = frag + (int64_t)(f0 / 64) * nfrag;
-    for (int idx = tid; idx < nfrag; idx += kThreads) {
-      const int l = idx & 63, rest = idx >> 6;
-      const int ct = rest % nv, q = rest / nv;  // q = part * kUSteps + step
-      sB[q / kUSteps][q % kUSteps][ct][l] = src[idx];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int st = 0; st < kUSteps; ++st) {
-      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av[st]);
-#pragma unroll
-      for (int ct = 0; ct < kTiles; ++ct) {
-        if (ct >= nv) break;
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            A, __builtin_bit_cast(bf16x8_t, sB[0][st][ct][lane]), acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            A, __builtin_bit_cast(bf16x8_t, sB[1][st][ct][lane]), acc[ct], 0, 0, 0);
+      for (int st = 0; st < kUSteps; ++st) {
+        av[st] = u32x4_t{0u, 0u, 0u, 0u};
+        if (row_ok) av[st] = __builtin_nontemporal_load((const u32x4_t*)(drow + f0 + 32 * st));
       }
+      const u32x4_t* src = frag + (int64_t)(f0 / 64) * nfrag;
+      for (int idx = tid; idx < nfrag; idx += kThreads) {
+        const int l = idx & 63, rest = idx >> 6;
+        const int ct = rest % nv, q = rest / nv;  // q = part * kUSteps + step
+        sB[q / kUSteps][q % kUSteps][ct][l] = src[idx];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int st = 0; st < kUSteps; ++st) {
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av[st]);
+#pragma unroll
+        for (int ct = 0; ct < kTiles; ++ct) {
+          if (ct >= nv) break;
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              A, __builtin_bit_cast(bf16x8_t, sB[0][st][ct][lane]), acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              A, __builtin_bit_cast(bf16x8_t, sB[1][st][ct][lane]), acc[ct], 0, 0, 0);
+        }
+      }
+      __syncthreads();  // the next block's copy overwrites sB
     }
-    __syncthreads();  // the next block's copy overwrites sB
-  }
 #pragma unroll
-  for (int ct = 0; ct < kTiles; ++ct) {
-    if (ct >= nct) break;
+    for (int ct = 0; ct < kTiles; ++ct) {
+      if (ct >= nct) break;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = t0 + 16 * wave + 4 * g + i;
-      const int c = 16 * ct + c16;
-      if (t < b && c < m) Uo[t * m + c] = f2bf16(acc[ct][i]);
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = t0 + 16 * wave + 4 * g + i;
+        const int c = 16 * ct + c16;
+        if (t < b && c < m) Uo[t * m + c] = f2bf16(acc[ct][i]);
+      }
     }
   }
 }
@@ -860,12 +862,19 @@ hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream
   launch_gemm_ws<false>(P, count, s, basis, k, W.E, k, tmp, k, F, k, k);
   hipLaunchKernelGGL(write_v, dim3((F * P.m + kThreads - 1) / kThreads, count), blk, 0, s, P, p0,
                      tmp);
+  // Tiles of the longest chunk bound the work of one problem; the host does not read the
+  // offsets, so the grid takes the average tiles per chunk (twice over, for ragged
+  // chunks), or enough workgroups to fill the chip, and each workgroup loops over
+  // every gx-th tile of its chunk.
   const int64_t ttiles = (P.total_tokens + 63) / 64;
+  const int64_t gx = std::min<int64_t>(
+      ttiles, std::max<int64_t>({(int64_t)1, 2 * ((ttiles + P.num_chunks - 1) / P.num_chunks),
+                                 (2048 + count - 1) / count}));
   // U on MFMA: Delta rows are 16-byte addressable (the host requires a 16-byte aligned
   // deficit, and F is a multiple of 64).
   const int nfr = (F / 64) * kUSteps * ((std::min(P.m, k) + 15) / 16) * 64;
   hipLaunchKernelGGL(split_vm, dim3((nfr + kThreads - 1) / kThreads, count), blk, 0, s, P, tmp);
-  hipLaunchKernelGGL(write_u_mfma, dim3((unsigned)ttiles, count), blk, 0, s, P, p0);
+  hipLaunchKernelGGL(write_u_mfma, dim3((unsigned)gx, count), blk, 0, s, P, p0);
   return hipGetLastError();
 }
 

@@ -18,9 +18,11 @@
 //   relocate_patch_rows  m > 0, or any recall: rotation fused with the patch in one
 //                        HBM pass; the patch of a 16-token x 128-feature tile is 8
 //                        MFMA 16x16x32 bf16 tiles per 32 k.  The head launch covers
-//                        each 16-token group up to the end of its first chunk; a
-//                        tail launch (TAIL) covers the rest of groups that a chunk
-//                        boundary cuts.  OUT writes a destination cache.
+//                        each token group up to the end of its first chunk, and in
+//                        place, with no more chunk boundaries than groups, one unit
+//                        per boundary covers each further chunk's part of a cut group;
+//                        otherwise a tail launch (TAIL) covers the rest of the cut
+//                        groups.  OUT writes a destination cache.
 //                        Its VALU form (a measurement variant) sums the patch with
 //                        v_dot2_f32_bf16 instead.
 //   generic_rows         any shape, bf16 or fp32: one thread per (layer, token, head).
@@ -1014,11 +1016,13 @@ __device__ __forceinline__ void patch_tiles_pool(const PatchCtx<Q>& c, const Com
 // to consecutive XCDs), where they share the token group's U rows in that XCD's L2.
 //
 // TAIL = false covers every token group from its first token to the end of the chunk
-// that holds it (all of it in the common case of a group inside one chunk).  TAIL =
-// true covers the rest of the groups that a chunk boundary cuts: the grid then runs
-// over boundaries (cm.tail_mode == 1: unit k handles boundary offsets[k + 1] when it is
-// the first boundary inside its group) or over groups (cm.tail_mode == 2, when chunks
-// outnumber groups).  Keeping that rarer loop over chunks in its own kernel keeps the
+// that holds it (all of it in the common case of a group inside one chunk); in place,
+// when the grid holds units past the token groups, unit k - 1 covers chunk k's part of
+// the group that chunk k's first token cuts, so one launch covers the call.  TAIL =
+// true covers the rest of the groups that a chunk boundary cuts otherwise: the grid
+// runs over boundaries (cm.tail_mode == 1: unit k handles boundary offsets[k + 1] when
+// it is the first boundary inside its group) or over groups (cm.tail_mode == 2, when
+// chunks outnumber groups).  Keeping that loop over chunks in its own kernel keeps the
 // common kernel's register count (and so its occupancy) down.
 //
 // OUT != 0 is the out-of-place form (recall): rows are read through the source layout
@@ -1132,6 +1136,19 @@ void relocate_patch_rows(ChanArgs ch0, ChanArgs ch1, CommonArgs cm, int64_t bloc
       start = first.end;
       from = first.j + 1;
     }
+  } else if (!POOL && CH != 1 && OUT == 0 && tg >= cm.token_groups) {
+    // A boundary unit of a head launch over several chunks: unit k - 1 covers chunk k's
+    // part of the token group that its first token offsets[k] cuts, [offsets[k],
+    // min(offsets[k + 1], group end)).  Boundaries on a group's first token and empty
+    // chunks leave it idle; the group's head unit covers its part up to its first chunk
+    // end, so the units of a group cover it once.
+    const int k = (int)(tg - cm.token_groups) + 1;  // 1 <= k < num_chunks
+    const int64_t o = cm.offsets[k];
+    const int64_t g0 = o / cm.block_tokens * cm.block_tokens;
+    c.tb0 = o;
+    c.t1 = min(g0 + (int64_t)cm.block_tokens, cm.total_tokens);
+    if (o <= g0 || o >= c.t1 || cm.offsets[k + 1] <= o) return;
+    start = o;
   } else {
     // Pool order: the workgroup covers pool slots [tb0, t1) of num_pages * page_size.
     c.tb0 = tg * cm.block_tokens;
@@ -1720,13 +1737,24 @@ hipError_t launch_relocate_patch_rows(const ChanArgs* ch, int nch, const CommonA
   // In place, at least two tiles per wave: each wave of the head launch requests its first
   // two tiles together (two tiles in flight per wave).
   bool batch = out == 0 && !valu && cm.block_tokens >= 128;
+  // Groups that a chunk boundary cuts.  In place, with no more boundaries than groups,
+  // the head launch takes one unit per boundary after its token groups (each covers one
+  // chunk's part of a cut group), so one launch covers the call.  Otherwise a second
+  // launch walks the cut groups chunk by chunk, indexed by boundary (out of place:
+  // the boundary units would raise the head kernel's register count past 128) or, when
+  // boundaries outnumber groups, by group.
+  const int64_t nb = (int64_t)cm.num_chunks - 1;
+  const bool fold = out == 0 && nb > 0 && nb <= cm.token_groups;
+  if (fold) {
+    c0.blocks += nb * c0.fblocks;
+    if (nch > 1) c1.blocks += nb * c1.fblocks;
+    bpl = c0.blocks + c1.blocks;
+    grid = dim3((unsigned)((int64_t)cm.num_layers * bpl));
+  }
   KAMERA_LAUNCH_MK(false, xg);
   batch = false;
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || cm.num_chunks < 2) return e;
-  // Groups that a chunk boundary cuts: indexed by boundary, or by group when chunks
-  // outnumber groups.
-  const int64_t nb = (int64_t)cm.num_chunks - 1;
+  if (e != hipSuccess || cm.num_chunks < 2 || fold) return e;
   cm.tail_mode = nb <= cm.token_groups ? 1 : 2;
   const int64_t units = cm.tail_mode == 1 ? nb : cm.token_groups;
   c0.blocks = units * c0.fblocks;

@@ -339,17 +339,19 @@ def test_mfma_workgroup_count():
 
 
 def test_chunk_boundary_tail_launch():
-    # With more than one chunk a second launch covers the token groups that chunk
-    # boundaries cut: one unit per boundary, or per token group when chunks outnumber
-    # the groups.
+    # Token groups that chunk boundaries cut: one more unit per boundary in the same
+    # launch, or a second launch over the token groups when boundaries outnumber them.
     _, info1 = plan_names(*gqa(T=4096, m=32, n=1))
     assert info1.launches == 1
     bt = info1.tokens_per_unit
     groups = -(-4096 // bt)
     fb = 4 * 128 // 128
     _, info = plan_names(*gqa(T=4096, m=32, n=5))
-    assert info.launches == 2
+    assert info.launches == 1
     assert info.units == 28 * 2 * fb * (groups + 4)
+    _, info = plan_names(*gqa(T=4096, m=32, n=groups + 1))  # as many boundaries as groups
+    assert info.launches == 1
+    assert info.units == 28 * 2 * fb * (2 * groups)
     _, info = plan_names(*gqa(T=4096, m=32, n=groups + 100))
     assert info.launches == 2
     assert info.units == 28 * 2 * fb * (2 * groups)
@@ -458,7 +460,7 @@ def test_recall_kernel_choice():
         src, ch, p = gqa(m=m)
         names, info = recall_plan_names(src, recall_dst(), ch, p)
         assert names == ["rotate+patch mfma"] * 2 and info.launches == 1, m
-    src, ch, p = gqa(m=32, n=3)
+    src, ch, p = gqa(m=32, n=3)  # out of place, boundaries take a second launch
     _, info = recall_plan_names(src, recall_dst(), ch, p)
     assert info.launches == 2
     src, ch, p = gqa(m=12)  # rank not a multiple of 8

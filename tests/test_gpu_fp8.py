@@ -64,7 +64,7 @@ def test_paged_rotation_only():
 
 
 def test_llama_reorder_reduced():
-    # many chunks: the tail launch covers the token groups chunk boundaries cut
+    # many chunks: boundary units cover the token groups chunk boundaries cut
     w = _q("llama3_8b_reorder", layers=2, n_chunks=9, chunk_len=(1, 300))
     _run_case(w, w.rank, expect=["rotate+patch mfma"] * 2)
 

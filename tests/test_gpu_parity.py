@@ -131,9 +131,10 @@ def test_chunk_edges(rank):
 
 @pytest.mark.parametrize("rank", [8, 64, 100])
 def test_chunk_boundary_groups(rank):
-    # Token groups that chunk boundaries cut go to a second launch.  Boundaries here:
-    # one on a group start (512 is a multiple of every group size), several inside one
-    # group, an empty chunk; then many tiny chunks, so that boundaries outnumber groups.
+    # Token groups that chunk boundaries cut: one unit per boundary in the head launch,
+    # or a second launch when boundaries outnumber groups.  Boundaries here: one on a
+    # group start (512 is a multiple of every group size), several inside one group, an
+    # empty chunk; then many tiny chunks, so that boundaries outnumber groups.
     lens = (512, 3, 0, 250, 1, 1, 700, 40)
     deltas = (3, -5, 9, 0, 1 << 16, -7, 11, 2)
     _run_case(_gqa(lens=lens, deltas=deltas, rank=rank), rank,
