@@ -16,10 +16,21 @@ Reading (stated, not printed on the pages): Sigma is folded into the token facto
 U_m = U[:, :m] diag(s[:m]) and V_m = V[:, :m], so that U_m V_m^T is the best rank-m
 approximation of Delta (Eckart-Young) and the reuse operator adds exactly that product.
 numpy's LAPACK SVD in fp64 is the library step.
+
+[K] §3, "Tres Operacoes de Janela Baratas", item 1 ("Reordenacao"): one orbit patch,
+averaged over permutations, serves every order of a cached set.  Reading (stated, not
+printed on the pages): the caller supplies the deficit of the chunk under each of P
+orders of the set (each measured in the chunk's canonical frame), the orbit deficit is
+their mean, rounded once to bf16 (the deficits' own type) so that it enters patch
+formation like any deficit, and the orbit patch is its top-m factorization.  The
+factorization of the exact mean is the rank-m P that minimizes the summed squared error
+over the orbit, sum_p ||Delta_p - P||^2 = sum_p ||Delta_p - mean||^2 + P ||mean - P||^2.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from . import oracle as _orc
 
 
 def top_m_factors(delta: np.ndarray, m: int):
@@ -56,3 +67,19 @@ def form_patch(delta, offsets, m: int):
             V[l, j] = Vj
             S[l][j] = s
     return U, V, S
+
+
+def orbit_mean(deltas) -> np.ndarray:
+    """Deficits [P][...] as bf16 bit patterns -> their mean as bf16 bits: the fp64 sum in
+    order p = 0 .. P-1, divided by P in fp64, rounded once to bf16 (ties to even)."""
+    d = np.asarray(deltas, dtype=np.uint16)
+    acc = np.zeros(d.shape[1:], dtype=np.float64)
+    for p in range(d.shape[0]):
+        acc = acc + _orc.bf16_to_f64(d[p])
+    return _orc.round_bf16(acc / d.shape[0])
+
+
+def orbit_patch(deltas, offsets, m: int):
+    """The orbit patch: form_patch of the rounded mean deficit (deltas [P][L][T][F] bf16
+    bits)."""
+    return form_patch(_orc.bf16_to_f64(orbit_mean(deltas)), offsets, m)
