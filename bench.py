@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=1024)
     ap.add_argument("--form", action="store_true",
                     help="measure patch formation (kamera_form_patch) on the workload's shape")
+    ap.add_argument("--orbit", type=int, default=0,
+                    help="measure the orbit deficit (kamera_orbit_mean) over this many orders "
+                         "of the workload's first-channel deficit")
     ap.add_argument("--attend", action="store_true",
                     help="measure relocate-on-read decode attention (kamera_attend) on the "
                          "workload's cache, beside relocate + patch followed by attention")
@@ -92,6 +95,8 @@ def main():
     K.lib()
     dev = torch.device("cuda:0")
     w = synth.get(args.workload)
+    if args.orbit:
+        return bench_orbit(args, w, dev)
     if args.form:
         return bench_form(args, w, dev)
     if args.attend:
@@ -371,6 +376,71 @@ def bench_form(args, w, dev):
                      "traffic": None, "algorithmic_flops_per_launch": gram_flops,
                      "avg_launch_ms": round(gram_ms, 4)},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_orbit(args, w, dev):
+    """The orbit deficit on the workload's first channel: `args.orbit` orders of its
+    [L][T][F] deficit (seeded Gaussian bf16 values), averaged into one.  value = GB/s of
+    algorithmic traffic (every order read once, the mean written once) over whole
+    kamera_orbit_mean calls; the kernel is HBM-bound."""
+    import torch
+
+    from rope_relocation_rank_amd import kamera as K
+    from rope_relocation_rank_amd import synth
+
+    P = args.orbit
+    st = synth.structure(w)
+    L, T = w.layers, st.total_tokens
+    F = synth.feature_width(w)[0]
+    n = L * T * F
+    print(f"[bench] orbit {w.key}: {P} orders of {L} x {T} x {F}", file=sys.stderr, flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    d = torch.empty((P, n), dtype=torch.bfloat16, device=dev)
+    for p in range(P):
+        d[p] = (torch.randn(n, generator=g, device=dev) * 0.05).to(torch.bfloat16)
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    steps, warm = max(1, min(args.steps, 50)), max(1, min(args.warmup, 5))
+    for _ in range(warm):
+        K.orbit_mean(d, out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        K.orbit_mean(d, out)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        K.orbit_mean(d, out)
+    b.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = a.elapsed_time(b) / steps
+    nbytes = (P + 1) * n * 2
+    gbps = nbytes / (launch_ms * 1e-3) / 1e9
+    line = {
+        "metric": "orbit deficit (mean over orders): GB/s of algorithmic traffic",
+        "value": round(nbytes * steps / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(wall * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, f64 sum",
+        "data": "synthetic",
+        "config": {"workload": w.key + " (orbit deficit)", "orders": P, "layers": L,
+                   "tokens": T, "width": F, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "orbit_mean_bf16", "achieved": round(gbps, 1),
+                     "peak": 8000.0, "unit": "GB/s", "frac": round(gbps / 8000.0, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_ms": round(launch_ms, 4)},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

@@ -73,7 +73,7 @@ extern "C" {
 #define KAMERA_API __attribute__((visibility("default")))
 #endif
 
-#define KAMERA_ABI_VERSION 4
+#define KAMERA_ABI_VERSION 5
 #define KAMERA_MAX_RANK 256   /* largest patch rank m accepted */
 
 typedef enum {
@@ -352,6 +352,24 @@ KAMERA_API kamera_status kamera_form_patch(const kamera_form_desc* desc, const k
  * overlap a deficit.  desc.rank, U, V, sigma and iterations are not read. */
 KAMERA_API kamera_status kamera_form_gram(const kamera_form_desc* desc, const kamera_chunks* chunks,
                                float* const G[2], hipStream_t stream);
+
+/* Orbit deficit: Kamera page §3, "Tres Operacoes de Janela Baratas", item 1
+ * ("Reordenacao"): one patch averaged over permutations serves every order of a cached
+ * set.  Given the deficit of a channel under each of num_orders orders of the set (each
+ * in the chunks' canonical frames, laid out as kamera_form_desc.delta), this writes
+ * their mean, out[i] = bf16(sum_p deltas[p * order_stride + i] / num_orders): the sum
+ * in fp64 in order p = 0, 1, ..., one fp64 division, one rounding to nearest even.
+ * kamera_form_patch on `out` then gives the orbit patch, the top-m factorization of the
+ * mean deficit (among rank-m matrices it minimizes the squared error summed over the
+ * orbit).
+ *   deltas: device bf16, order p's deficit at element p * order_stride; read only.
+ *   out: device bf16 [elements]; must not overlap any order's deficit (KAMERA_E_ALIAS).
+ *   deltas and out 16-byte aligned, order_stride a multiple of 8 (KAMERA_E_ALIGN);
+ *   1 <= num_orders <= 2^20, elements >= 0, order_stride >= elements (KAMERA_E_SHAPE).
+ * A NaN input gives a NaN (sign unspecified); infinities follow fp64 arithmetic.
+ * Stream-ordered; allocates nothing. */
+KAMERA_API kamera_status kamera_orbit_mean(const void* deltas, int32_t num_orders, int64_t elements,
+                                int64_t order_stride, void* out, hipStream_t stream);
 
 /* Which kernels a call would launch, without launching anything (no HIP call).
  * Fills `out` and returns the status the call itself would return before launching. */

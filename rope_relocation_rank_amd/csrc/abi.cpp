@@ -973,6 +973,32 @@ kamera_status kamera_form_gram(const kamera_form_desc* desc, const kamera_chunks
 }
 
 
+kamera_status kamera_orbit_mean(const void* deltas, int32_t num_orders, int64_t elements,
+                                int64_t order_stride, void* out, hipStream_t stream) {
+  g_last_error.clear();
+  if (num_orders < 1 || num_orders > (1 << 20))
+    return fail(KAMERA_E_SHAPE, "num_orders %d outside [1, 2^20]", num_orders);
+  if (elements < 0) return fail(KAMERA_E_SHAPE, "elements %lld < 0", (long long)elements);
+  if (order_stride < elements)
+    return fail(KAMERA_E_SHAPE, "order_stride %lld < elements %lld", (long long)order_stride,
+                (long long)elements);
+  if (order_stride > (INT64_MAX / 2) / num_orders)
+    return fail(KAMERA_E_SHAPE, "num_orders * order_stride overflows");
+  if (elements == 0) return KAMERA_OK;
+  if (!deltas) return fail(KAMERA_E_NULL, "deltas is NULL");
+  if (!out) return fail(KAMERA_E_NULL, "out is NULL");
+  if (!aligned(deltas, 16) || !aligned(out, 16) || order_stride % 8 != 0)
+    return fail(KAMERA_E_ALIGN, "deltas and out must be 16-byte aligned and order_stride a "
+                                "multiple of 8");
+  for (int64_t p = 0; p < num_orders; ++p)
+    if (overlaps(out, elements * 2, (const uint16_t*)deltas + p * order_stride, elements * 2))
+      return fail(KAMERA_E_ALIAS, "out overlaps the deficit of order %lld", (long long)p);
+  const hipError_t e = kamera::launch_orbit_mean((const uint16_t*)deltas, num_orders, elements,
+                                                 order_stride, (uint16_t*)out, stream);
+  if (e != hipSuccess) return hip_fail(e, "orbit mean launch");
+  return KAMERA_OK;
+}
+
 kamera_status kamera_recall_patch(const kamera_kv_desc* src, const kamera_kv_desc* dst,
                                   const kamera_chunks* chunks, const kamera_patch* patch,
                                   hipStream_t stream) {

@@ -878,6 +878,112 @@ hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ orbit mean
+
+namespace {
+
+// fp64 -> bf16 bits, nearest with ties to even, as one rounding: first to fp32 with
+// round-to-odd (the nearest-even fp32 value, stepped toward zero when it rounded away,
+// with its last bit set when inexact), then to bf16 with ties to even.  Rounding to odd
+// at 24 bits and then to nearest at 8 gives the nearest 8-bit value of x itself, since
+// 24 >= 8 + 2 (in the subnormal ranges too: fp32 keeps 16 bits below bf16's quantum).
+// A NaN stays a NaN (quiet); past the largest finite bf16 the result is infinity.
+__device__ __forceinline__ uint16_t bf16_rne_f64(double x) {
+  const float f = (float)x;
+  const double back = (double)f;
+  const bool inexact = back != x;
+  uint32_t u = __float_as_uint(f);
+  u -= (inexact && fabs(back) > fabs(x)) ? 1u : 0u;
+  u |= inexact ? 1u : 0u;
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ double bf16_f64(uint32_t h) { return (double)__uint_as_float(h << 16); }
+
+// Adds the eight bf16 values of w to acc.
+__device__ __forceinline__ void add8(double (&acc)[8], const u32x4_t& w) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc[2 * e] += bf16_f64(w[e] & 0xffffu);
+    acc[2 * e + 1] += bf16_f64(w[e] >> 16);
+  }
+}
+
+// out[i] = bf16(sum_p in[p * stride + i] / num): eight values per thread and step, the
+// sum in fp64 in order p = 0, 1, ..., then one division and one rounding.  HBM-bound:
+// (num + 1) * 2 bytes per value.  NUM > 0: num == NUM, all of a step's loads issued
+// together; NUM == 0: any num, four loads at a time.
+template <int NUM>
+__global__ __launch_bounds__(256) void orbit_mean_bf16(const uint16_t* in, int num, int64_t n,
+                                                       int64_t stride, uint16_t* out) {
+  const int64_t n8 = n >> 3;
+  const int64_t step = (int64_t)gridDim.x * 256;
+  if constexpr (NUM > 0) num = NUM;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n8; v += step) {
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    if constexpr (NUM > 0) {
+      u32x4_t w[NUM];
+#pragma unroll
+      for (int p = 0; p < NUM; ++p)
+        w[p] = __builtin_nontemporal_load((const u32x4_t*)(in + (int64_t)p * stride) + v);
+#pragma unroll
+      for (int p = 0; p < NUM; ++p) add8(acc, w[p]);
+    } else {
+      int p = 0;
+      for (; p + 4 <= num; p += 4) {
+        u32x4_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          w[u] = __builtin_nontemporal_load((const u32x4_t*)(in + (int64_t)(p + u) * stride) + v);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) add8(acc, w[u]);
+      }
+      for (; p < num; ++p)
+        add8(acc, __builtin_nontemporal_load((const u32x4_t*)(in + (int64_t)p * stride) + v));
+    }
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (uint32_t)bf16_rne_f64(acc[2 * e] / (double)num) |
+             ((uint32_t)bf16_rne_f64(acc[2 * e + 1] / (double)num) << 16);
+    __builtin_nontemporal_store(o, (u32x4_t*)out + v);
+  }
+  // The last n % 8 values: one thread each in the first workgroup.
+  const int64_t i = (n8 << 3) + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x < 8 && i < n) {
+    double acc = 0.0;
+    for (int p = 0; p < num; ++p) acc += bf16_f64(in[(int64_t)p * stride + i]);
+    out[i] = bf16_rne_f64(acc / (double)num);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_orbit_mean(const uint16_t* in, int num, int64_t n, int64_t stride,
+                             uint16_t* out, hipStream_t s) {
+  const int64_t n8 = n >> 3;
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n8 + 255) / 256, 8192));
+#define KAMERA_ORBIT(N)                                                                        \
+  hipLaunchKernelGGL(orbit_mean_bf16<N>, dim3((unsigned)blocks), dim3(256), 0, s, in, num, n,   \
+                     stride, out)
+  switch (num) {
+    case 1: KAMERA_ORBIT(1); break;
+    case 2: KAMERA_ORBIT(2); break;
+    case 3: KAMERA_ORBIT(3); break;
+    case 4: KAMERA_ORBIT(4); break;
+    case 5: KAMERA_ORBIT(5); break;
+    case 6: KAMERA_ORBIT(6); break;
+    case 7: KAMERA_ORBIT(7); break;
+    case 8: KAMERA_ORBIT(8); break;
+    default: KAMERA_ORBIT(0); break;
+  }
+#undef KAMERA_ORBIT
+  return hipGetLastError();
+}
+
 hipError_t launch_form_gram(const FormArgs& P, float* G, hipStream_t s) {
   const int nt = P.F / 64;
   const int64_t problems = (int64_t)P.num_layers * P.num_chunks;

@@ -131,6 +131,10 @@ int64_t form_workspace_floats(int F, int k);
 hipError_t launch_form_batch(const FormArgs& a, int64_t p0, int count, hipStream_t s);
 // Gram matrices of every problem of one channel into G [problems][F][F].
 hipError_t launch_form_gram(const FormArgs& a, float* G, hipStream_t s);
+// Orbit deficit: out[i] = bf16(sum_p in[p * stride + i] / num), fp64 sum and division,
+// one rounding (in, out 16-byte aligned, stride a multiple of 8).
+hipError_t launch_orbit_mean(const uint16_t* in, int num, int64_t n, int64_t stride,
+                             uint16_t* out, hipStream_t s);
 
 // Rotation only, bf16 (16-byte accesses) or fp8 (8-byte accesses): rope_dim in
 // {16, 32, 64, 128}.  `unroll` row groups per wavefront (bf16: 2 or 4; fp8: 4 or 8).

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG, "libkamera.so")
 KAMERA_OK, KAMERA_E_NULL, KAMERA_E_SHAPE, KAMERA_E_UNSUPPORTED = 0, 1, 2, 3
 KAMERA_E_ALIGN, KAMERA_E_ALIAS, KAMERA_E_HIP = 4, 5, 6
 KAMERA_BF16, KAMERA_F32, KAMERA_FP8_E4M3 = 0, 1, 2
-KAMERA_ABI_VERSION = 4
+KAMERA_ABI_VERSION = 5
 KAMERA_NEOX_HALF = 0
 KAMERA_INTERLEAVED = 1
 KAMERA_FLAG_GENERIC = 1
@@ -29,7 +29,7 @@ EXPORTED = ["kamera_relocate", "kamera_relocate_patch", "kamera_relocate_patch_w
             "kamera_relocate_patch_noalloc",
             "kamera_relocate_workspace", "kamera_recall_patch", "kamera_plan",
             "kamera_recall_plan", "kamera_form_workspace", "kamera_form_patch", "kamera_form_gram",
-            "kamera_attend_workspace", "kamera_attend",
+            "kamera_orbit_mean", "kamera_attend_workspace", "kamera_attend",
             "kamera_status_str", "kamera_last_error", "kamera_abi_version"]
 KAMERA_FORM_MAX_RANK = 112
 
@@ -133,6 +133,9 @@ def lib():
         L.kamera_form_gram.restype = C.c_int
         L.kamera_form_gram.argtypes = [C.POINTER(kamera_form_desc), C.POINTER(kamera_chunks),
                                        C.POINTER(C.c_void_p), C.c_void_p]
+        L.kamera_orbit_mean.restype = C.c_int
+        L.kamera_orbit_mean.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int64, C.c_void_p,
+                                        C.c_void_p]
         L.kamera_attend_workspace.restype = C.c_int
         L.kamera_attend_workspace.argtypes = [C.POINTER(kamera_kv_desc), C.POINTER(kamera_chunks),
                                               C.POINTER(kamera_patch), C.POINTER(kamera_attend_desc),
@@ -353,6 +356,16 @@ def form_gram(desc: kamera_form_desc, chunks: kamera_chunks, G, stream=None) -> 
     s = current_stream() if stream is None else stream
     arr = (C.c_void_p * 2)(*[g.data_ptr() for g in G] + [None] * (2 - len(G)))
     check(lib().kamera_form_gram(C.byref(desc), C.byref(chunks), arr, s))
+
+
+def orbit_mean(deltas, out, stream=None) -> None:
+    """Enqueue the orbit mean: deltas a torch bf16 tensor [P][...] (contiguous), out a
+    bf16 tensor with deltas[0]'s elements."""
+    s = current_stream() if stream is None else stream
+    P = deltas.shape[0]
+    n = out.numel()
+    stride = deltas[0].numel() if P > 0 else 0
+    check(lib().kamera_orbit_mean(deltas.data_ptr(), P, n, stride, out.data_ptr(), s))
 
 
 # ------------------------------------------------------------- relocate-on-read attention

@@ -35,7 +35,7 @@ def test_library_loads_and_exports_every_declared_function():
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     assert set(names) <= exported
     assert not [e for e in exported if "launch" in e], "internal symbols leak"
-    assert K.kamera_abi_version() == 4
+    assert K.kamera_abi_version() == 5
 
 
 def test_struct_layout_matches_header():
@@ -689,3 +689,26 @@ def test_attend_aliasing():
     d.lse = FAKE + (11 << 40)
     ws = FAKE  # workspace on the K cache
     assert call() == K.KAMERA_E_ALIAS
+
+
+# ----------------------------------------------------------------- orbit mean
+
+def test_orbit_mean_checks_before_launch():
+    # Every argument error returns before any HIP call (fake addresses, no GPU); an
+    # empty problem returns OK without a launch.
+    L = K.lib()
+    A, O = FAKE, FAKE + (1 << 36)
+    assert L.kamera_orbit_mean(A, 3, 0, 0, O, None) == K.KAMERA_OK
+    assert L.kamera_orbit_mean(A, 0, 64, 64, O, None) == K.KAMERA_E_SHAPE
+    assert L.kamera_orbit_mean(A, 3, -1, 64, O, None) == K.KAMERA_E_SHAPE
+    assert L.kamera_orbit_mean(A, 3, 64, 32, O, None) == K.KAMERA_E_SHAPE
+    assert L.kamera_orbit_mean(A, (1 << 20) + 1, 64, 64, O, None) == K.KAMERA_E_SHAPE
+    assert L.kamera_orbit_mean(None, 3, 64, 64, O, None) == K.KAMERA_E_NULL
+    assert L.kamera_orbit_mean(A, 3, 64, 64, None, None) == K.KAMERA_E_NULL
+    assert L.kamera_orbit_mean(A + 2, 3, 64, 64, O, None) == K.KAMERA_E_ALIGN
+    assert L.kamera_orbit_mean(A, 3, 64, 68, O, None) == K.KAMERA_E_ALIGN
+    assert L.kamera_orbit_mean(A, 3, 64, 64, O + 8, None) == K.KAMERA_E_ALIGN
+    # out overlapping an order's deficit (order p holds bytes [2 p stride, 2 p stride + 128))
+    assert L.kamera_orbit_mean(A, 3, 64, 64, A + 128 + 16, None) == K.KAMERA_E_ALIAS
+    assert L.kamera_orbit_mean(A, 3, 64, 128, A + 256 - 64, None) == K.KAMERA_E_ALIAS
+    assert L.kamera_orbit_mean(A, 3, 64, 128, A + 2 * 256 + 64, None) == K.KAMERA_E_ALIAS
