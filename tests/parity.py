@@ -477,8 +477,11 @@ def attend_bounds(inp, q, scale):
     if m > 0:
         U0 = np.abs(bf16_value(host_bits(inp.U[0]))).reshape(L, T, m)
         V0 = np.abs(bf16_value(host_bits(inp.V[0]))).reshape(L, st.num_chunks, H, D, m)
+    ks = host_bits(inp.scales[0]).astype(np.float64) if inp.scales else None
     for l in range(L):
         rows = np.abs(_channel_rows(inp, 0, l)).reshape(T, H, D)
+        if ks is not None:  # fp8: values are scale * code
+            rows = rows * abs(ks[l])
         for h in range(Hq):
             g = h // G
             s = rows[:, g, :] @ qb[l, h]
@@ -497,7 +500,8 @@ def check_attend(inp, q, scale, run) -> AttendReport:
     w = inp.workload
     bufs = [host_bits(b) for b in inp.buffers]
     chans = _dicts(inp.layouts, [b.copy() for b in bufs],
-                   ([host_bits(u) for u in inp.U], [host_bits(v) for v in inp.V]), inp.rank)
+                   ([host_bits(u) for u in inp.U], [host_bits(v) for v in inp.V]), inp.rank,
+                   inp.scales)
     qh = q.detach().cpu().numpy().astype(np.float64)
     out, lse = run(inp, q, scale)
     if out.is_cuda:

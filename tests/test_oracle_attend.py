@@ -206,3 +206,43 @@ def test_token_order_does_not_matter():
                        delta=delta[::-1].copy(), q=q, scale=0.5, rank=m)
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(la, lb, rtol=1e-13)
+
+
+def test_fp8_cache_matches_the_same_values_in_bf16():
+    # An fp8 E4M3 cache (codes and per-layer scales of each channel) and a bf16 cache
+    # holding exactly the same values attend to the same result, bit for bit: with
+    # power-of-two scales every scale * code is a bf16 value.  The scales differ per
+    # layer and per channel, so a scale taken from the wrong layer or channel, or left
+    # out, changes the result.
+    L, T, H, D, m, n = 3, 29, 2, 16, 8, 2
+    rng = np.random.default_rng(9)
+    codes = []
+    for _ in range(2):
+        c = rng.integers(0, 0x7F, size=(L, T, H, D)) | (rng.integers(0, 2, size=(L, T, H, D)) << 7)
+        codes.append(np.ascontiguousarray(c, dtype=np.uint8))
+    scales = [np.array([2.0 ** -3, 2.0, 2.0 ** 4], np.float32),
+              np.array([4.0, 2.0 ** -5, 1.0], np.float32)]
+    bf = [orc.round_bf16(orc.fp8_to_f64(codes[c]) * scales[c].astype(np.float64)[:, None, None, None])
+          for c in range(2)]
+    for c in range(2):  # exact: the values are bf16 numbers
+        assert np.array_equal(orc.bf16_to_f64(bf[c]),
+                              orc.fp8_to_f64(codes[c]) * scales[c].astype(np.float64)[:, None, None, None])
+    f = lambda x: orc.round_bf16(x)  # noqa: E731  bf16 factors
+    U = [f(0.3 * rng.standard_normal((L, T, m))) for _ in range(2)]
+    VK, VV = f(0.3 * rng.standard_normal((L, n, H * D, m))), f(0.3 * rng.standard_normal((L, n, H * D, m)))
+    offs, delta = np.array([0, 11, T]), np.array([7, -300])
+    q = rng.standard_normal((L, 2 * H, D))
+
+    def run(data, with_scales):
+        ch = _chans(data[0], data[1], D, U, VK, VV)
+        if with_scales is not None:
+            for c in range(2):
+                ch[c]["scale"] = with_scales[c]
+        return orc.attend(ch, num_layers=L, theta=1e4, offsets=offs, delta=delta, q=q,
+                          scale=0.25, rank=m)
+
+    out8, lse8 = run(codes, scales)
+    out16, lse16 = run(bf, None)
+    assert np.array_equal(out8, out16) and np.array_equal(lse8, lse16)
+    swapped, _ = run(codes, scales[::-1])
+    assert not np.allclose(swapped, out16)
