@@ -268,10 +268,12 @@ KAMERA_API kamera_status kamera_recall_patch(const kamera_kv_desc* src, const ka
  * kv: MHA/GQA, bf16; channel 0 = K (its rope_dim, pairing and sections rotate),
  *     channel 1 = V (rope_dim 0); equal heads; dim 128; contiguous or paged (tokens
  *     whose block-table entry lies outside [0, num_pages) are not attended).  Row bases
- *     8-byte aligned, strides multiples of 8 elements, per-layer extents below 2^31
- *     elements, total_tokens below 2^30.  Other shapes: KAMERA_E_UNSUPPORTED.
+ *     16-byte aligned (KAMERA_E_ALIGN), strides multiples of 8 elements, one layer of a
+ *     channel spanning less than 2^31 - 64 bytes, total_tokens below 2^30, a block
+ *     table below 2^29 entries.  Other shapes: KAMERA_E_UNSUPPORTED.
  * patch: NULL or rank 0 for plain attention; else a rank that is a multiple of 8, up
- *     to 128, with 16-byte aligned bf16 factors as for kamera_relocate_patch.
+ *     to 128, with 16-byte aligned bf16 factors as for kamera_relocate_patch, one
+ *     layer of U spanning less than 2^31 - 64 bytes.
  * A head with no attended token gets out = 0 and lse = -inf. */
 typedef struct {
   int32_t num_q_heads;   /* Hq: a multiple of kv.heads, at most 8 times it */

@@ -774,22 +774,25 @@ kamera_status validate_attend(const kamera_kv_desc* kv, const kamera_chunks* ch,
   if (T >= kMaxTunedTokens) return fail(KAMERA_E_UNSUPPORTED, "total_tokens must be below 2^30");
   for (int c = 0; c < 2; ++c) {
     const kamera_channel& k = kv->ch[c];
-    if (!aligned(k.data, 8) || !strides_ok(k))
-      return fail(KAMERA_E_ALIGN, "channel %d: attention needs 8-byte rows (strides %% 8)", c);
-    if (layer_extent(k, T, kv->page_size, kv->num_pages) >= ((__int128)1 << 31))
-      return fail(KAMERA_E_UNSUPPORTED, "channel %d: per-layer extent of 2^31 elements or more", c);
+    if (!aligned(k.data, 16) || !strides_ok(k))
+      return fail(KAMERA_E_ALIGN, "channel %d: attention needs 16-byte rows (strides %% 8)", c);
+    // rows are reached through buffer resources with 32-bit byte offsets
+    if (layer_extent(k, T, kv->page_size, kv->num_pages) * 2 > kamera::kMaxBufferBytes)
+      return fail(KAMERA_E_UNSUPPORTED, "channel %d: one layer spans 2^31 - 64 bytes or more", c);
   }
+  if ((__int128)T * m * 2 > kamera::kMaxBufferBytes)
+    return fail(KAMERA_E_UNSUPPORTED, "one layer of U spans 2^31 - 64 bytes or more");
+  if (kv->page_size > 0 && ceil_div(T, kv->page_size) * 4 > kamera::kMaxBufferBytes)
+    return fail(KAMERA_E_UNSUPPORTED, "block table of 2^29 entries or more");
   if (L > 0 && (!at->q || !at->out)) return fail(KAMERA_E_NULL, "q and out are required");
   if (!aligned(at->q, 4) || !aligned(at->out, 4) || !aligned(at->lse, 4))
     return fail(KAMERA_E_ALIGN, "q, out and lse must be 4-byte aligned");
   if (L == 0) return KAMERA_OK;
-  // Splits.  Contiguous caches run one wave per (layer, KV head, split): 8192 of them,
-  // at least 128 tokens each.  Paged caches run a 4-wave workgroup per (layer, KV head,
-  // split): 4096 of them, at least 64 tokens each.
-  const bool rows = kv->page_size == 0;
+  // Splits: a 4-wave workgroup per (layer, KV head, split), 4096 of them, at least 64
+  // tokens each.
   const int64_t units = L * K.heads;
-  int64_t S = std::max<int64_t>(1, ceil_div(rows ? 8192 : 4096, units));
-  S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(T, rows ? 128 : 64)));
+  int64_t S = std::max<int64_t>(1, ceil_div(4096, units));
+  S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(T, 64)));
   const int es = env_int("KAMERA_ATTEND_SPLITS", 0);
   if (es > 0) S = es;
   if (T > 0) {
@@ -890,6 +893,12 @@ kamera_status run_attend(const kamera_kv_desc* kv, const kamera_chunks* ch, cons
   a.split_tokens = (int32_t)plan.split_tokens;
   a.slots = (int32_t)plan.slots;
   a.slot_floats = kamera::attend_slot_floats(m);
+  for (int c = 0; c < 2; ++c)
+    a.layer_bytes[c] = (uint32_t)(layer_extent(kv->ch[c], T, kv->page_size, kv->num_pages) * 2);
+  // The next tile's V rows go to a second LDS tile (more bytes in flight per wave, fewer
+  // workgroups per CU): measured best at ranks 33-64, and no better or slower below;
+  // KAMERA_ATTEND_DB=0/1 overrides.
+  a.double_buffer = env_int("KAMERA_ATTEND_DB", m > 32 && m <= 64 ? 1 : 0) != 0;
   a.scale_log2 = at->scale * 1.4426950408889634f;
   for (int i = 0; i < a.rope_dim / 2 && i < 64; ++i)
     a.omega[i] = pow(kv->rope_theta, -2.0 * (double)i / (double)a.rope_dim);

@@ -22,11 +22,15 @@
 //                 <= 2^-17 relative), as B: 16x16x32 bf16 MFMA, fp32 accumulation.
 //                 Online softmax per query head.  Then O^T += V^T P^T and the U_V sums
 //                 on 16x16x16 bf16 MFMA, P split into high and low parts, V^T read
-//                 from a per-wave LDS copy of the tile.  Each (range, chunk) segment
-//                 writes one partial: max, sum, the 128 value sums and the m U_V sums.
+//                 transposed from the wave's LDS tile, which the V and U_V rows reach
+//                 straight from memory (no registers), one tile ahead.  Each (range,
+//                 chunk) segment writes one partial: max, sum, the 128 value sums and
+//                 the m U_V sums.
 //   attend_merge  per (layer, query head): merges the partials, adding V_V times each
 //                 partial's U_V sums with that partial's chunk factor.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kamera_internal.h"
 #include "rope_device.h"
@@ -40,12 +44,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;      // prep kernel
-constexpr int kTileWaves = 8;              // tile kernel: waves (KV heads) per workgroup
+constexpr int kThreads = 64 * kWaves;      // prep and tile kernels
 constexpr int kD = kAttendDim;
-constexpr int kRowPad = 8;                 // bf16 padding of an LDS tile row
-constexpr int kVRow = kD + kRowPad;        // LDS row of a V tile
-constexpr int kURow = 128 + kRowPad;       // LDS row of a U_V tile (rank <= 128)
 
 __device__ __forceinline__ float bf16_at(const uint16_t* p) {
   return __uint_as_float((uint32_t)*p << 16);
@@ -146,372 +146,442 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8_t& hi, bf16x8
   }
 }
 
-// One 16-token tile's A-operand rows as loaded: lane (c16, grp) holds 8 consecutive
-// features of token tb + c16 per 32-wide step.
+// Buffer addressing (gfx9 raw buffer, stride 0): a resource covers `bytes` bytes from a
+// wave-uniform base and range-checks every access, so a load at byte offset kOob reads
+// zeros; rows a lane skips take that offset instead of a branch.  The offset passes an
+// empty asm operand so that the compiler does not split the access into branches (a
+// load behind such a branch waits for every earlier load).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+// 16 bytes into registers (aux 2: nontemporal, for rows read once).
+template <int AUX>
+__device__ __forceinline__ u32x4_t bload(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)opaque(off), 0, AUX);
+}
+// 16 bytes per lane straight into LDS: lane i's bytes land at dst + 16 i (dst is
+// wave-uniform).  No registers are held while the request is in flight.
+__device__ __forceinline__ void bload_lds(rsrc_t r, uint32_t off, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           (int)opaque(off), 0, 0, 2);
+}
+
+// One wave's LDS tile: the V rows of its 16 tokens as four blocks of four 256-byte rows
+// (token 4 b + i in block b, row i), the blocks 64 bytes apart so that the transposed
+// reads of the four lane groups fall in different banks; and, in an array of its own,
+// the U_V rows of the 16 tokens as they lie in memory (16 x 2m bytes, m <= 32 MK).
+// Separate arrays let the compiler wait for exactly the request a read depends on.
+constexpr int kVBlk = 4 * 2 * kD + 64;
+constexpr int kVTile = 4 * kVBlk;
+
+// The K-side rows of one tile as loaded: lane (c16, grp) holds features 32 ks + 8 grp ..
+// + 7 of token c16 (k), and ranks 32 ku + 8 grp .. + 7 of its U_K row (uk).
 template <int MKX>
-struct TileRows {
-  u32x4_t k[4], v[4], uk[MKX], uv[MKX];
-  bool on;  // the lane's token (tb + c16) has a row in the segment
+struct KRows {
+  u32x4_t k[4], uk[MKX];
+};
+// Where the lane's token of a tile lives: byte offsets of its K and V rows inside the
+// layer (kOob when the token lies past the segment or its page is out of range).
+struct RowAt {
+  uint32_t k, v;
+};
+// Block-table entries of one tile with pages of at least 16 slots: the tile's tokens
+// lie in at most two pages, entries p0 (of its first token) and p1 (of its last), and
+// its first token sits at slot r0 of the first page.  Wave-uniform: scalar loads.
+struct TilePages {
+  int32_t p0, p1, r0;
 };
 
-// Two mappings of the work, chosen by what measured faster on each layout:
-//  - contiguous caches: one workgroup per (layer, token range), one wave per KV head
-//    (heads w, w + 8, ... beyond 8).  The waves read the same tokens' rows side by
-//    side, so the workgroup streams whole cache rows and the U rows all heads share are
-//    read by one CU.  Each wave walks the range tile by tile and writes its own
-//    partials.
-//  - paged caches: one 4-wave workgroup per (layer, KV head, token range); the waves
-//    take tiles w, w + 4, ... and merge through LDS at the end of each segment.
-// A segment is the part of the range inside one chunk; each writes one partial slot per
-// query head.  MK: 32-wide rank steps (ceil(m / 32)); PAGED: block-table addressing (and
-// the second mapping); PF: the next tile's rows are loaded before the current tile is
-// worked (the second register tile lowers occupancy, which pays at one rank step only).
-template <int MK, bool PAGED, bool PF>
-__global__ __launch_bounds__(PAGED ? kThreads : 64 * kTileWaves)
-__attribute__((amdgpu_waves_per_eu(PAGED && MK == 2 ? 3 : 1))) void attend_tiles(AttendArgs a) {
+// One 4-wave workgroup per (layer, KV head, token range); the waves take the range's
+// 16-token tiles w, w + 4, ... and merge through LDS at the end of each segment (the
+// part of the range inside one chunk), which writes one partial slot per query head.
+// The query-side B operands (high and low parts of the rotated query and of V_K^T q)
+// are the same for the four waves and sit once in LDS.  Per tile, a wave requests the
+// K and U_K rows into registers and the V and U_V rows straight into its LDS tile (the
+// P V products read them transposed from there), one tile ahead of the one it works
+// on: DB, the next tile's V and U_V go to a second LDS tile at once; otherwise they go
+// to the one LDS tile after the current tile's reads.  Block-table entries are read two
+// tiles ahead, before the rows that precede their use, so no wait for them waits for
+// rows.  MK: 32-wide rank steps (ceil(m / 32)).  PG: 0 contiguous; 1 paged with pages
+// of at least 16 slots, a tile's two block-table entries read by scalar loads (which
+// count apart from the row requests); 2 paged with smaller pages, each lane reading its
+// token's entry.
+template <int MK, int PG, bool DB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MK >= 4 && DB ? 1 : MK >= 2 ? 2 : 3)))
+void attend_tiles(AttendArgs a) {
   constexpr int MKX = MK > 0 ? MK : 1;
-  constexpr int MU = 2 * MK;               // 16-wide rank blocks of the U_V sums
+  constexpr int MU = 2 * MK;  // 16-wide rank blocks of the U_V sums
   constexpr int MUX = MU > 0 ? MU : 1;
-  constexpr bool ROWS = !PAGED;
-  constexpr int kTileBytes = 16 * (kVRow + kURow) * 2;  // per-wave V and U_V tiles
-  // Paged mapping: the tiles' LDS is reused for the merge of the four waves.
-  constexpr int kMergeFloats = kWaves * kAttendMaxGroup * (2 + kD + 128);
-  constexpr int kLdsTiles = ROWS ? kTileWaves * kTileBytes
-                                 : (kWaves * kTileBytes > kMergeFloats * 4 ? kWaves * kTileBytes
-                                                                            : kMergeFloats * 4);
-  // Paged mapping: the four waves run one KV head, so the query-side B operands (high
-  // and low parts of the rotated query and of V_K^T q) are the same for all of them and
-  // sit once in LDS after the tiles, read per tile instead of held in 48 registers.
-  constexpr int kBOps = 8 + 2 * MKX;  // 16-byte operands per lane
-  constexpr int kLds = kLdsTiles + (PAGED ? kBOps * 64 * 16 : 0);
-  __shared__ __align__(16) unsigned char lds[kLds];
-  u32x4_t* sB = (u32x4_t*)(lds + kLdsTiles);
+  constexpr int kUTile = 1024 * MKX;
+  constexpr int kMergeBytes = kWaves * kAttendMaxGroup * (2 + kD + 32 * MK) * 4;
+  constexpr int kBuf0 = kWaves * kVTile > kMergeBytes ? kWaves * kVTile : kMergeBytes;
+  constexpr int kBOps = 8 + 2 * MKX;  // 16-byte query-side operands per lane
+  __shared__ __align__(16) unsigned char lds0[kBuf0];  // V tiles, then the merge
+  __shared__ __align__(16) unsigned char lds1[DB ? kWaves * kVTile : 16];
+  __shared__ __align__(16) unsigned char ldu0[kWaves * kUTile];  // U_V tiles
+  __shared__ __align__(16) unsigned char ldu1[DB ? kWaves * kUTile : 16];
+  __shared__ __align__(16) u32x4_t sB[kBOps * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int nw = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15;
   const int grp = lane >> 4;
-  uint16_t* sv = (uint16_t*)(lds + wave * kTileBytes);
-  uint16_t* su = sv + 16 * kVRow;
-  typedef float MergeRow[kAttendMaxGroup][2 + kD + 128];
-  MergeRow* sred = (MergeRow*)lds;
+  // LDS tiles are addressed as one byte offset into the array itself (buffer 0 or 1, a
+  // compile-time tag), so that the compiler keeps track of which array every read and
+  // every request touches and waits for exactly the requests a read depends on.
+  using Buf0 = std::integral_constant<int, 0>;
+  using Buf1 = std::integral_constant<int, 1>;
+  const int vwave = wave * kVTile, uwave = wave * kUTile;
+  typedef float MergeRow[kAttendMaxGroup][2 + kD + 32 * MK];
+  MergeRow* sred = (MergeRow*)lds0;
 
   const uint32_t S = (uint32_t)a.splits;
+  const uint32_t H = (uint32_t)a.heads;
   const uint32_t bid = blockIdx.x;
-  // Workgroup order: split fastest, then (paged) KV head, then layer.
+  // Workgroup order: split fastest, then KV head, then layer.  (Placing the KV heads of
+  // one (layer, split) on one XCD, so that they read the range's U rows from one L2,
+  // measured 3-4% slower.)
   const uint32_t lg = bid / S;
   const int s = (int)(bid - lg * S);
-  const int l = ROWS ? (int)lg : (int)(lg / (uint32_t)a.heads);
-  // ROWS: wave w runs heads w, w + nw, ...; otherwise the workgroup runs one head.
-  const int g_first = ROWS ? wave : (int)(lg - (uint32_t)l * (uint32_t)a.heads);
-  const int g_step = ROWS ? nw : a.heads;
-  const int ti_first = ROWS ? 0 : wave;
-  const int ti_step = ROWS ? 1 : kWaves;
+  const int l = (int)(lg / H);
+  const int g = (int)(lg - (uint32_t)l * H);
   const int64_t T = a.total_tokens;
   const int64_t t_lo = (int64_t)s * a.split_tokens;
   const int64_t t_hi = min(T, t_lo + (int64_t)a.split_tokens);
   if (t_lo >= t_hi) return;
   const int m = a.rank, gq = a.group, Hq = a.num_q_heads, n = a.num_chunks;
   const int W = kD + m;
-  const bool hv = c16 < gq;                // this lane's MFMA column is a real query head
-  const uint16_t* ukb = MK > 0 ? (const uint16_t*)a.U[0] + (int64_t)l * T * m + 8 * grp : nullptr;
-  const uint16_t* uvb = MK > 0 ? (const uint16_t*)a.U[1] + (int64_t)l * T * m + 8 * grp : nullptr;
-  const uint32_t ss0 = (uint32_t)a.slot_stride[0], ss1 = (uint32_t)a.slot_stride[1];
-  const uint32_t ps0 = (uint32_t)a.page_stride[0], ps1 = (uint32_t)a.page_stride[1];
+  const bool hv = c16 < gq;  // this lane's MFMA column is a real query head
+  const uint32_t ss0 = (uint32_t)a.slot_stride[0] * 2u, ss1 = (uint32_t)a.slot_stride[1] * 2u;
+  const uint32_t ps0 = (uint32_t)a.page_stride[0] * 2u, ps1 = (uint32_t)a.page_stride[1] * 2u;
   const uint32_t P = (uint32_t)a.page_size;
   const int psh = (P != 0u && (P & (P - 1u)) == 0u) ? __builtin_ctz(P) : -1;
+  // One resource per (layer, head) row set, from the head's first element to the end of
+  // the layer; one per layer of each U factor; one over the block table.
+  const rsrc_t rk = make_rsrc((const uint16_t*)a.data[0] + (int64_t)l * a.layer_stride[0] +
+                                  (int64_t)g * a.head_stride[0],
+                              a.layer_bytes[0] - (uint32_t)(g * a.head_stride[0] * 2));
+  const rsrc_t rv = make_rsrc((const uint16_t*)a.data[1] + (int64_t)l * a.layer_stride[1] +
+                                  (int64_t)g * a.head_stride[1],
+                              a.layer_bytes[1] - (uint32_t)(g * a.head_stride[1] * 2));
+  const uint32_t ubytes = (uint32_t)(T * m * 2);
+  const rsrc_t ruk = make_rsrc(MK > 0 ? (const void*)((const uint16_t*)a.U[0] + (int64_t)l * T * m)
+                                      : (const void*)a.q, MK > 0 ? ubytes : 0u);
+  const rsrc_t ruv = make_rsrc(MK > 0 ? (const void*)((const uint16_t*)a.U[1] + (int64_t)l * T * m)
+                                      : (const void*)a.q, MK > 0 ? ubytes : 0u);
+  const rsrc_t rbt = make_rsrc(PG == 2 ? (const void*)a.block_table : (const void*)a.q,
+                               PG == 2 ? (uint32_t)(((T + P - 1) / P) * 4) : 0u);
+  // Restricted copies: the slot stores cannot clobber the table, so uniform reads of it
+  // become scalar loads.
+  const int32_t* __restrict__ bt = a.block_table;
+  float* __restrict__ wsp = a.ws;
 
-  // Block-table entry of token t (paged), -1 when t lies at or past `end` or its page
-  // id is out of range.  A tile's entries are read one tile ahead, so the row loads of
-  // a tile never wait on the table.
-  auto page_of = [&](int64_t t, int64_t end) -> int32_t {
-    if (!PAGED || t >= end) return -1;
-    const uint32_t tt = (uint32_t)t;
-    const uint32_t pi = psh >= 0 ? tt >> psh : tt / P;
-    const int32_t pg = a.block_table[pi];
-    return (pg < 0 || pg >= a.num_pages) ? -1 : pg;
-  };
-  // Row offsets of token t in the K and V channels inside the layer (32-bit: the host
-  // checks the extents), given its block-table entry pg when paged; false when the
-  // token has no slot.
-  auto slot = [&](int64_t t, int32_t pg, uint32_t& off_k, uint32_t& off_v) -> bool {
-    const uint32_t tt = (uint32_t)t;
-    if constexpr (PAGED) {
-      if (pg < 0) return false;
-      const uint32_t pi = psh >= 0 ? tt >> psh : tt / P, si = tt - pi * P;
-      off_k = (uint32_t)pg * ps0 + si * ss0;
-      off_v = (uint32_t)pg * ps1 + si * ss1;
-    } else {
-      off_k = tt * ss0;
-      off_v = tt * ss1;
-    }
-    return true;
-  };
+  for (int64_t t0 = t_lo; t0 < t_hi;) {
+    const int j = chunk_at(a.offsets, n, t0);
+    const int64_t s1 = min(t_hi, a.offsets[j + 1]);
+    if (s1 <= t0) break;  // offsets that do not cover the range: nothing more here
+    const int ntiles = (int)((s1 - t0 + 15) >> 4);
 
-  // All segments of head g over this workgroup's token range.
-  auto run_head = [&](const int g) {
-    const uint16_t* kb = (const uint16_t*)a.data[0] + (int64_t)l * a.layer_stride[0] +
-                         (int64_t)g * a.head_stride[0] + 8 * grp;
-    const uint16_t* vb = (const uint16_t*)a.data[1] + (int64_t)l * a.layer_stride[1] +
-                         (int64_t)g * a.head_stride[1] + 8 * grp;
-    for (int64_t t0 = t_lo; t0 < t_hi;) {
-      const int j = chunk_at(a.offsets, n, t0);
-      const int64_t s1 = min(t_hi, a.offsets[j + 1]);
-      if (s1 <= t0) break;  // offsets that do not cover the range: nothing more here
-
-      // Loads the rows of tile ti (token tb + c16, 8 consecutive features per step);
-      // pg is that token's block-table entry when paged.
-      auto load = [&](int ti, int32_t pg, TileRows<MKX>& R) {
-        const int64_t tr = t0 + 16 * (int64_t)ti + c16;
-        uint32_t off_k = 0, off_v = 0;
-        const bool row_on = tr < s1 && slot(tr, pg, off_k, off_v);
-        R.on = row_on;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          R.k[ks] = u32x4_t{0u, 0u, 0u, 0u};
-          R.v[ks] = u32x4_t{0u, 0u, 0u, 0u};
-          if (row_on) {
-            R.k[ks] = __builtin_nontemporal_load((const u32x4_t*)(kb + off_k + 32 * ks));
-            R.v[ks] = __builtin_nontemporal_load((const u32x4_t*)(vb + off_v + 32 * ks));
-          }
-        }
-#pragma unroll
-        for (int ku = 0; ku < MKX; ++ku) {
-          R.uk[ku] = u32x4_t{0u, 0u, 0u, 0u};
-          R.uv[ku] = u32x4_t{0u, 0u, 0u, 0u};
-          if (MK > 0 && tr < s1 && 32 * ku + 8 * grp < m) {
-            R.uk[ku] = *(const u32x4_t*)(ukb + tr * m + 32 * ku);
-            R.uv[ku] = *(const u32x4_t*)(uvb + tr * m + 32 * ku);
-          }
-        }
-      };
-      const int ntiles = (int)((s1 - t0 + 15) >> 4);
-      auto tile_page = [&](int ti) -> int32_t {
-        return ti < ntiles ? page_of(t0 + 16 * (int64_t)ti + c16, s1) : -1;
-      };
-      TileRows<MKX> cur;
-      int32_t pg_cur = tile_page(ti_first);
-      if (PF && ti_first < ntiles) {
-        load(ti_first, pg_cur, cur);
-        pg_cur = tile_page(ti_first + ti_step);
-      }
-
-      // B operands: this lane's query head (column c16), features 32 ks + 8 grp ...
-      bf16x8_t qh[4], ql[4], wh[MKX], wl[MKX];
-      // Operand o of this lane (paged: from LDS).  Every wave writes the same values
-      // for the segment, and reads only after its own writes; the previous segment's
-      // readers all passed the barrier that ends it.
-      auto bop = [&](int o, const bf16x8_t& r) -> bf16x8_t {
-        if constexpr (PAGED) return __builtin_bit_cast(bf16x8_t, sB[o * 64 + lane]);
-        return r;
-      };
-      {
-        const float* qp = a.qw + (((int64_t)l * n + j) * Hq + g * gq + (hv ? c16 : 0)) * W;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = hv ? qp[32 * ks + 8 * grp + e] : 0.f;
-          split8(x, qh[ks], ql[ks]);
-        }
-#pragma unroll
-        for (int ku = 0; ku < MKX; ++ku) {
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int k = 32 * ku + 8 * grp + e;
-            x[e] = (MK > 0 && hv && k < m) ? qp[kD + k] : 0.f;
-          }
-          split8(x, wh[ku], wl[ku]);
-        }
-        if constexpr (PAGED) {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            sB[ks * 64 + lane] = __builtin_bit_cast(u32x4_t, qh[ks]);
-            sB[(4 + ks) * 64 + lane] = __builtin_bit_cast(u32x4_t, ql[ks]);
-          }
-#pragma unroll
-          for (int ku = 0; ku < MKX; ++ku) {
-            sB[(8 + ku) * 64 + lane] = __builtin_bit_cast(u32x4_t, wh[ku]);
-            sB[(8 + MKX + ku) * 64 + lane] = __builtin_bit_cast(u32x4_t, wl[ku]);
-          }
-        }
-      }
-
-      float mrun = -INFINITY, lrun = 0.f;
-      f32x4_t acc[8], uacc[MUX];
-#pragma unroll
-      for (int f = 0; f < 8; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < MUX; ++u) uacc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-      for (int ti = ti_first; ti < ntiles; ti += ti_step) {
+    // Page lookups of tile ti: PG 1, the tile's two entries (uniform); PG 2, the entry
+    // of the lane's token (-1: past the segment or out of the pool); PG 0, none.
+    auto lookup = [&](int ti) {
+      if constexpr (PG == 1) {
+        // Tiles past the segment read the entries of its last token (their rows are
+        // dropped anyway): no branch around the loads.
+        TilePages q;
         const int64_t tb = t0 + 16 * (int64_t)ti;
-        TileRows<MKX> nxt;
-        int32_t pg_nxt;
-        if constexpr (PF) {
-          // pg_cur holds the entry of tile ti + ti_step here
-          if (ti + ti_step < ntiles) load(ti + ti_step, pg_cur, nxt);
-          pg_nxt = tile_page(ti + 2 * ti_step);
-        } else {
-          load(ti, pg_cur, cur);
-          pg_nxt = tile_page(ti + ti_step);
-        }
-        // Scores of tokens tb + 4 grp + i (i < 4) for query head c16.
-        f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, cur.k[ks]);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(ks, qh[ks]), sc, 0, 0, 0);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(4 + ks, ql[ks]), sc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int ku = 0; ku < MK; ++ku) {
-          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, cur.uk[ku]);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(8 + ku, wh[ku]), sc, 0, 0, 0);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(8 + MKX + ku, wl[ku]), sc, 0, 0, 0);
-        }
-        // The V and U_V rows go to this wave's LDS tile (row c16) for the transposed
-        // reads; the wave's previous reads of the tile come before these writes in
-        // program order, and LDS accesses of one wave complete in order.
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          *(u32x4_t*)(sv + c16 * kVRow + 32 * ks + 8 * grp) = cur.v[ks];
-#pragma unroll
-        for (int ku = 0; ku < MK; ++ku)
-          if (32 * ku + 8 * grp < m) *(u32x4_t*)(su + c16 * kURow + 32 * ku + 8 * grp) = cur.uv[ku];
-        // Mask tokens past the segment or without a slot.  Paged: bit c16 of the ballot
-        // (lanes 0..15) says whether token tb + c16 loaded a row.
-        float s4[4];
-        if constexpr (PAGED) {
-          const uint32_t onm = (uint32_t)__ballot(cur.on) & 0xffffu;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s4[i] = (onm >> (4 * grp + i)) & 1u ? sc[i] : -INFINITY;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s4[i] = tb + 4 * grp + i < s1 ? sc[i] : -INFINITY;
-        }
-        float mt = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
-        mt = max_xor(mt, 16);
-        mt = max_xor(mt, 32);
-        const float mn = fmaxf(mrun, mt);
-        const float corr = weight(mrun, mn);
-        if (corr != 1.f) {
-          lrun *= corr;
-#pragma unroll
-          for (int f = 0; f < 8; ++f) acc[f] *= corr;
-#pragma unroll
-          for (int u = 0; u < MUX; ++u) uacc[u] *= corr;
-        }
-        mrun = mn;
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = weight(s4[i], mn);
-          lrun += p[i];
-        }
-        bf16x4_t ph, pl;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ph[i] = (__bf16)p[i];
-          pl[i] = (__bf16)(p[i] - (float)ph[i]);
-        }
-        // O^T[f][h] += V^T[f][t] P^T[t][h]: A = V^T rows f = 16 fb + c16, tokens 4 grp + i.
-#pragma unroll
-        for (int fb = 0; fb < 8; ++fb) {
-          bf16x4_t A;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            A[i] = __builtin_bit_cast(__bf16, sv[(4 * grp + i) * kVRow + 16 * fb + c16]);
-          acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, acc[fb], 0, 0, 0);
-          acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, acc[fb], 0, 0, 0);
-        }
-#pragma unroll
-        for (int ub = 0; ub < MU; ++ub) {
-          if (16 * ub >= m) break;
-          bf16x4_t A;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            A[i] = __builtin_bit_cast(__bf16, su[(4 * grp + i) * kURow + 16 * ub + c16]);
-          uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, uacc[ub], 0, 0, 0);
-          uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, uacc[ub], 0, 0, 0);
-        }
-        if constexpr (PF) cur = nxt;
-        pg_cur = pg_nxt;
-      }
-      // The four lane groups of a column hold disjoint tokens' sums.
-      lrun += __shfl_xor(lrun, 16);
-      lrun += __shfl_xor(lrun, 32);
-
-      // The segment's partial for query head c16: lane (c16, grp) holds features
-      // 16 fb + 4 grp + i of the value sums and 16 ub + 4 grp + i of the U_V sums.
-      if constexpr (ROWS) {
-        if (hv) {
-          float* sl = a.ws + (((int64_t)l * Hq + g * gq + c16) * a.slots + (s + j)) * a.slot_floats;
-          if (grp == 0) {
-            sl[0] = mrun;
-            sl[1] = lrun;
-            sl[2] = __int_as_float(j);
-          }
-#pragma unroll
-          for (int fb = 0; fb < 8; ++fb)
-            *(f32x4_t*)(sl + kAttendSlotHead + 16 * fb + 4 * grp) = acc[fb];
-#pragma unroll
-          for (int ub = 0; ub < MU; ++ub)
-            if (16 * ub + 4 * grp < m)
-              *(f32x4_t*)(sl + kAttendSlotHead + kD + 16 * ub + 4 * grp) = uacc[ub];
-        }
+        const uint32_t tt = (uint32_t)min(tb, s1 - 1), last = (uint32_t)(min(s1, tb + 16) - 1);
+        const uint32_t i0 = psh >= 0 ? tt >> psh : tt / P;
+        const uint32_t i1 = psh >= 0 ? last >> psh : last / P;
+        q.r0 = (int32_t)(tt - i0 * P);
+        q.p0 = bt[__builtin_amdgcn_readfirstlane(i0)];
+        q.p1 = bt[__builtin_amdgcn_readfirstlane(i1)];
+        return q;
+      } else if constexpr (PG == 2) {
+        const int64_t t = t0 + 16 * (int64_t)ti + c16;
+        const uint32_t tt = (uint32_t)t;
+        const uint32_t off = t < s1 ? (psh >= 0 ? tt >> psh : tt / P) * 4u : kOob;
+        const int32_t pg = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rbt, (int)opaque(off), 0, 0);
+        return (off == kOob || pg < 0 || pg >= a.num_pages) ? (int32_t)-1 : pg;
       } else {
-        // Merge the four waves' partials through LDS first.
-        __syncthreads();  // the tiles' LDS becomes the merge buffer
-        if (hv) {
-          if (grp == 0) {
-            sred[wave][c16][0] = mrun;
-            sred[wave][c16][1] = lrun;
-          }
-#pragma unroll
-          for (int fb = 0; fb < 8; ++fb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sred[wave][c16][2 + 16 * fb + 4 * grp + i] = acc[fb][i];
-#pragma unroll
-          for (int ub = 0; ub < MU; ++ub)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int k = 16 * ub + 4 * grp + i;
-              if (k < m) sred[wave][c16][2 + kD + k] = uacc[ub][i];
-            }
-        }
-        __syncthreads();
-        for (int idx = tid; idx < gq * W; idx += kThreads) {
-          const int h = idx / W, e = idx - h * W;
-          float M = -INFINITY;
-#pragma unroll
-          for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sred[w][h][0]);
-          float L = 0.f, A = 0.f;
-#pragma unroll
-          for (int w = 0; w < kWaves; ++w) {
-            const float f = weight(sred[w][h][0], M);
-            L = fmaf(f, sred[w][h][1], L);
-            A = fmaf(f, sred[w][h][2 + e], A);
-          }
-          float* sl = a.ws + (((int64_t)l * Hq + g * gq + h) * a.slots + (s + j)) * a.slot_floats;
-          if (e == 0) {
-            sl[0] = M;
-            sl[1] = L;
-            sl[2] = __int_as_float(j);
-          }
-          sl[kAttendSlotHead + e] = A;
-        }
-        __syncthreads();  // the next segment reuses the LDS for tiles
+        return 0;
       }
-      t0 = s1;
+    };
+    using Pages = decltype(lookup(0));
+    auto row_at = [&](int ti, const Pages& pq) -> RowAt {
+      const int64_t t = t0 + 16 * (int64_t)ti + c16;
+      const uint32_t tt = (uint32_t)t;
+      RowAt r{kOob, kOob};
+      if constexpr (PG == 1) {
+        const int32_t rr = pq.r0 + c16;
+        const bool second = rr >= (int32_t)P;
+        const int32_t pg = second ? pq.p1 : pq.p0;
+        const uint32_t si = (uint32_t)(second ? rr - (int32_t)P : rr);
+        const bool ok = t < s1 && pg >= 0 && pg < a.num_pages;
+        r.k = ok ? (uint32_t)pg * ps0 + si * ss0 : kOob;
+        r.v = ok ? (uint32_t)pg * ps1 + si * ss1 : kOob;
+      } else if constexpr (PG == 2) {
+        const uint32_t pi = psh >= 0 ? tt >> psh : tt / P, si = tt - pi * P;
+        const bool ok = t < s1 && pq >= 0;
+        r.k = ok ? (uint32_t)pq * ps0 + si * ss0 : kOob;
+        r.v = ok ? (uint32_t)pq * ps1 + si * ss1 : kOob;
+      } else {
+        r.k = t < s1 ? tt * ss0 : kOob;
+        r.v = t < s1 ? tt * ss1 : kOob;
+      }
+      return r;
+    };
+    // K and U_K rows of tile ti into registers.
+    auto issue_k = [&](int ti, const RowAt& r, KRows<MKX>& R) {
+      const uint32_t tt = (uint32_t)(t0 + 16 * (int64_t)ti + c16);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        R.k[ks] = bload<2>(rk, r.k == kOob ? kOob : r.k + 64u * ks + 16u * grp);
+#pragma unroll
+      for (int ku = 0; ku < MKX; ++ku) {
+        const int k0 = 32 * ku + 8 * grp;
+        R.uk[ku] = u32x4_t{0u, 0u, 0u, 0u};
+        if (MK > 0) R.uk[ku] = bload<0>(ruk, k0 < m ? (tt * (uint32_t)m + k0) * 2u : kOob);
+      }
+    };
+    // V and U_V rows of tile ti straight into an LDS tile: request b copies tokens
+    // 4 b .. 4 b + 3 (lane i: token 4 b + i / 16, bytes 16 (i % 16) of its row, whose
+    // offset the lane of that token holds); the U_V rows of the 16 tokens are one
+    // contiguous run of 32 m bytes, copied 1 KB per request (tokens past the segment
+    // read zeros).
+    auto issue_v = [&](int ti, const RowAt& r, auto buf) {
+      constexpr bool one = decltype(buf)::value == 1;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t vr = (uint32_t)__shfl((int)r.v, 4 * b + grp);
+        bload_lds(rv, vr == kOob ? kOob : vr + 16u * c16,
+                  one ? lds1 + (vwave + b * kVBlk) : lds0 + (vwave + b * kVBlk));
+      }
+      const int64_t tb = t0 + 16 * (int64_t)ti;
+#pragma unroll
+      for (int b = 0; b < MK; ++b) {
+        const int u = 64 * b + lane;  // 16-byte unit of the run; token tb + 8 u / m
+        const bool ok = u < 2 * m && tb + (8 * u) / m < s1;
+        bload_lds(ruv, ok ? (uint32_t)(tb * m * 2) + 16u * u : kOob,
+                  one ? ldu1 + (uwave + 1024 * b) : ldu0 + (uwave + 1024 * b));
+      }
+    };
+
+    // B operands: this lane's query head (column c16), features 32 ks + 8 grp ...  Every
+    // wave writes the same values for the segment; the previous segment's readers all
+    // passed the barrier that ends it.
+    {
+      const float* qp = a.qw + (((int64_t)l * n + j) * Hq + g * gq + (hv ? c16 : 0)) * W;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = hv ? qp[32 * ks + 8 * grp + e] : 0.f;
+        bf16x8_t hi, lo;
+        split8(x, hi, lo);
+        sB[ks * 64 + lane] = __builtin_bit_cast(u32x4_t, hi);
+        sB[(4 + ks) * 64 + lane] = __builtin_bit_cast(u32x4_t, lo);
+      }
+#pragma unroll
+      for (int ku = 0; ku < MKX; ++ku) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = 32 * ku + 8 * grp + e;
+          x[e] = (MK > 0 && hv && k < m) ? qp[kD + k] : 0.f;
+        }
+        bf16x8_t hi, lo;
+        split8(x, hi, lo);
+        sB[(8 + ku) * 64 + lane] = __builtin_bit_cast(u32x4_t, hi);
+        sB[(8 + MKX + ku) * 64 + lane] = __builtin_bit_cast(u32x4_t, lo);
+      }
     }
-  };
-  if constexpr (ROWS) {
-    for (int g = g_first; g < a.heads; g += g_step) run_head(g);
-  } else {
-    run_head(g_first);
+    auto bop = [&](int o) -> bf16x8_t { return __builtin_bit_cast(bf16x8_t, sB[o * 64 + lane]); };
+
+    float mrun = -INFINITY, lrun = 0.f;
+    f32x4_t acc[8], uacc[MUX];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < MUX; ++u) uacc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Scores, online softmax and the P V and P U_V products of tile ti.
+    auto work = [&](const RowAt& r, const KRows<MKX>& R, auto buf) {
+      constexpr bool one = decltype(buf)::value == 1;
+      const unsigned char* vs = one ? lds1 : lds0;
+      const unsigned char* us = one ? ldu1 : ldu0;
+      // Scores of tokens tb + 4 grp + i (i < 4) for query head c16.
+      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, R.k[ks]);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(ks), sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(4 + ks), sc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ku = 0; ku < MK; ++ku) {
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, R.uk[ku]);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(8 + ku), sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(8 + MKX + ku), sc, 0, 0, 0);
+      }
+      // Tokens without a row (past the segment, or out of the pool) get weight 0: bit
+      // c16 of the ballot over lanes 0..15 says whether token tb + c16 has one.
+      const uint32_t onm = (uint32_t)__ballot(r.k != kOob) & 0xffffu;
+      float s4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s4[i] = (onm >> (4 * grp + i)) & 1u ? sc[i] : -INFINITY;
+      float mt = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+      mt = max_xor(mt, 16);
+      mt = max_xor(mt, 32);
+      const float mn = fmaxf(mrun, mt);
+      const float corr = weight(mrun, mn);
+      if (corr != 1.f) {
+        lrun *= corr;
+#pragma unroll
+        for (int f = 0; f < 8; ++f) acc[f] *= corr;
+#pragma unroll
+        for (int u = 0; u < MUX; ++u) uacc[u] *= corr;
+      }
+      mrun = mn;
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = weight(s4[i], mn);
+        lrun += p[i];
+      }
+      bf16x4_t ph, pl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ph[i] = (__bf16)p[i];
+        pl[i] = (__bf16)(p[i] - (float)ph[i]);
+      }
+      // O^T[f][h] += V^T[f][t] P^T[t][h]: A = V^T rows f = 16 fb + c16, tokens 4 grp + i
+      // (block grp, row i of the LDS tile).
+      const int vo = vwave + grp * kVBlk + 2 * c16;
+#pragma unroll
+      for (int fb = 0; fb < 8; ++fb) {
+        bf16x4_t A;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          A[i] = __builtin_bit_cast(__bf16, *(const uint16_t*)(vs + (vo + 2 * (i * kD + 16 * fb))));
+        acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, acc[fb], 0, 0, 0);
+        acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, acc[fb], 0, 0, 0);
+      }
+      // Every rank block is worked, also past m (their sums are never written): a
+      // branch on m here would make the reads after it wait for every request.  Those
+      // reads stay inside the tile's U_V area (30 m + 64 MK - 2 < 1024 MK bytes).
+      const int uo = uwave + 2 * (4 * grp * m + c16);
+#pragma unroll
+      for (int ub = 0; ub < MU; ++ub) {
+        bf16x4_t A;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          A[i] = __builtin_bit_cast(__bf16, *(const uint16_t*)(us + (uo + 2 * (i * m + 16 * ub))));
+        uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, uacc[ub], 0, 0, 0);
+        uacc[ub] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, uacc[ub], 0, 0, 0);
+      }
+    };
+    // The tile's LDS reads are done before a later request overwrites the tile.
+    auto lds_reads_done = [&]() { __builtin_amdgcn_s_waitcnt(0xc07f); };  // lgkmcnt(0)
+
+    // The wave's tiles, two per loop pass (registers ra / rb alternate; LDS tile 0 / 1
+    // with DB).
+    int ti = wave;
+    if (ti < ntiles) {
+      KRows<MKX> ra, rb;
+      Pages pg_n = lookup(ti + 4);
+      RowAt ra_at = row_at(ti, lookup(ti)), rb_at{kOob, kOob};
+      issue_k(ti, ra_at, ra);
+      issue_v(ti, ra_at, Buf0{});
+      while (true) {
+        // tile ti: ra, LDS tile 0.  The next tile's requests go out whether or not it
+        // exists (past the segment they read zeros): a request under a branch would
+        // leave the join after it unsure which LDS tile is in flight, and the reads of
+        // the current tile would then wait for every request.
+        const Pages pg_nn = lookup(ti + 8);
+        const bool more = ti + 4 < ntiles;
+        rb_at = row_at(ti + 4, pg_n);
+        issue_k(ti + 4, rb_at, rb);
+        if constexpr (DB) issue_v(ti + 4, rb_at, Buf1{});
+        work(ra_at, ra, Buf0{});
+        if (!more) break;
+        if (!DB) {
+          lds_reads_done();
+          issue_v(ti + 4, rb_at, Buf0{});
+        }
+        ti += 4;
+        // tile ti: rb, LDS tile 1 (DB) or 0
+        const Pages pg_n3 = lookup(ti + 8);
+        const bool more2 = ti + 4 < ntiles;
+        ra_at = row_at(ti + 4, pg_nn);
+        issue_k(ti + 4, ra_at, ra);
+        if constexpr (DB) issue_v(ti + 4, ra_at, Buf0{});
+        if constexpr (DB) work(rb_at, rb, Buf1{});
+        else work(rb_at, rb, Buf0{});
+        if (!more2) break;
+        if (!DB) {
+          lds_reads_done();
+          issue_v(ti + 4, ra_at, Buf0{});
+        }
+        ti += 4;
+        pg_n = pg_n3;
+      }
+    }
+    // The four lane groups of a column hold disjoint tokens' sums.
+    lrun += __shfl_xor(lrun, 16);
+    lrun += __shfl_xor(lrun, 32);
+
+    // Merge the four waves' partials through LDS, then write the segment's slot: lane
+    // (c16, grp) holds features 16 fb + 4 grp + i of the value sums and 16 ub + 4 grp + i
+    // of the U_V sums of query head c16.
+    __syncthreads();  // every wave's tile reads are done: the tiles' LDS holds the merge
+    if (hv) {
+      if (grp == 0) {
+        sred[wave][c16][0] = mrun;
+        sred[wave][c16][1] = lrun;
+      }
+#pragma unroll
+      for (int fb = 0; fb < 8; ++fb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sred[wave][c16][2 + 16 * fb + 4 * grp + i] = acc[fb][i];
+#pragma unroll
+      for (int ub = 0; ub < MU; ++ub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = 16 * ub + 4 * grp + i;
+          if (k < m) sred[wave][c16][2 + kD + k] = uacc[ub][i];
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < gq * W; idx += kThreads) {
+      const int h = idx / W, e = idx - h * W;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sred[w][h][0]);
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = weight(sred[w][h][0], M);
+        L = fmaf(f, sred[w][h][1], L);
+        A = fmaf(f, sred[w][h][2 + e], A);
+      }
+      float* sl = wsp + (((int64_t)l * Hq + g * gq + h) * a.slots + (s + j)) * a.slot_floats;
+      if (e == 0) {
+        sl[0] = M;
+        sl[1] = L;
+        sl[2] = __int_as_float(j);
+      }
+      sl[kAttendSlotHead + e] = A;
+    }
+    __syncthreads();  // the next segment reuses the LDS for tiles and operands
+    t0 = s1;
   }
 }
 
@@ -612,24 +682,27 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.splits > 0) {  // no tokens: only the merge runs, writing 0 and -inf
     const dim3 grid0((unsigned)((int64_t)a.num_layers * a.num_chunks * a.heads));
     hipLaunchKernelGGL(attend_prep, grid0, dim3(kThreads), 0, s, a);
-    // Contiguous: a workgroup per (layer, split), a wave per KV head; paged: a 4-wave
-    // workgroup per (layer, split, KV head).
-    const bool rows = a.page_size == 0;
-    const dim3 grid1((unsigned)((int64_t)a.num_layers * a.splits * (rows ? 1 : a.heads)));
-    const dim3 block1((unsigned)(rows ? 64 * (a.heads < kTileWaves ? a.heads : kTileWaves) : kThreads));
+    // A 4-wave workgroup per (layer, split, KV head).
+    const dim3 grid1((unsigned)((int64_t)a.num_layers * a.splits * a.heads));
     const int mk = (a.rank + 31) / 32;
-#define KAMERA_ATT(MK)                                                                   \
+    const bool db = a.double_buffer != 0 && mk <= 2;
+#define KAMERA_ATT2(MK, PG)                                                              \
   do {                                                                                   \
-    if (a.page_size > 0)                                                                 \
-      hipLaunchKernelGGL((attend_tiles<MK, true, MK == 1>), grid1, block1, 0, s, a);   \
-    else                                                                                 \
-      hipLaunchKernelGGL((attend_tiles<MK, false, MK == 1>), grid1, block1, 0, s, a);  \
+    if (db) hipLaunchKernelGGL((attend_tiles<MK, PG, true>), grid1, dim3(kThreads), 0, s, a);  \
+    else hipLaunchKernelGGL((attend_tiles<MK, PG, false>), grid1, dim3(kThreads), 0, s, a);    \
+  } while (0)
+#define KAMERA_ATT(MK)                              \
+  do {                                              \
+    if (a.page_size >= 16) KAMERA_ATT2(MK, 1);      \
+    else if (a.page_size > 0) KAMERA_ATT2(MK, 2);   \
+    else KAMERA_ATT2(MK, 0);                        \
   } while (0)
     if (mk == 0) KAMERA_ATT(0);
     else if (mk == 1) KAMERA_ATT(1);
     else if (mk == 2) KAMERA_ATT(2);
     else KAMERA_ATT(4);
 #undef KAMERA_ATT
+#undef KAMERA_ATT2
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

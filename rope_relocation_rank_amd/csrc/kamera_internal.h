@@ -112,6 +112,8 @@ struct AttendArgs {
   int32_t num_chunks, num_sections, sec_end[4], pairing, rope_dim;
   int32_t page_size, num_layers, heads, num_q_heads, group, rank;
   int32_t splits, split_tokens, slots, slot_floats;
+  uint32_t layer_bytes[2];    // bytes of one layer of each channel (below 2^31 - 64)
+  int32_t double_buffer;      // tile kernel: the next tile's V rows go to a second LDS tile
   float scale_log2;           // softmax scale * log2(e): scores are kept in base 2
   double omega[64];           // theta^(-2i/rope_dim)
 };
