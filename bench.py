@@ -488,7 +488,8 @@ def bench_attend(args, w, dev):
         insts.append(synth.Inputs(base.workload, base.rank, base.struct, base.pool_pages,
                                   [b.clone() for b in base.buffers], base.layouts,
                                   [u.clone() for u in base.U], [v.clone() for v in base.V],
-                                  base.offsets_t, base.delta_t, base.block_table_t))
+                                  base.offsets_t, base.delta_t, base.block_table_t,
+                                  scales=base.scales))
     descs = [ops.attend_buffers(c, q, scale) for c in insts]
     lib = K.lib()
     stream = torch.cuda.current_stream(dev)
@@ -562,7 +563,7 @@ def bench_attend(args, w, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, fp32 compute",
+        "dtype": ("fp8 e4m3" if w.dtype == "fp8" else "bf16") + " in, fp32 compute",
         "data": "synthetic",
         "config": {"workload": w.key + " (decode attention)", "rank": m, "layers": w.layers,
                    "kv_heads": w.heads, "q_heads": w.q_heads or w.heads,
@@ -603,6 +604,8 @@ def cpu_baseline_attend(w, m, seconds: float):
         d["data"] = host(inp.buffers[lay["buffer"]]).ravel()
         if m > 0:
             d["U"], d["V"] = host(inp.U[c]), host(inp.V[c])
+        if inp.scales:  # fp8: each channel's per-layer scales
+            d["scale"] = inp.scales[c].numpy()
         chans.append(d)
     done, t = 0, 0.0
     while t < seconds and done < 1000:

@@ -265,10 +265,12 @@ KAMERA_API kamera_status kamera_recall_patch(const kamera_kv_desc* src, const ka
  * sums re-associated ((R(-delta) q) . K_t + (V_K^T q) . U[0][t], and V_V applied to
  * sum_t p_t U[1][t]), in fp32.
  *
- * kv: MHA/GQA, bf16; channel 0 = K (its rope_dim, pairing and sections rotate),
+ * kv: MHA/GQA, bf16 or fp8 E4M3 (values scale * code with each channel's per-layer
+ *     scale, as for kamera_relocate_patch); channel 0 = K (its rope_dim, pairing and sections rotate),
  *     channel 1 = V (rope_dim 0); equal heads; dim 128; contiguous or paged (tokens
  *     whose block-table entry lies outside [0, num_pages) are not attended).  Row bases
- *     16-byte aligned (KAMERA_E_ALIGN), strides multiples of 8 elements, one layer of a
+ *     16-byte aligned (KAMERA_E_ALIGN: data 16-byte aligned, strides multiples of 8
+ *     elements, of 16 for fp8), one layer of a
  *     channel spanning less than 2^31 - 64 bytes, total_tokens below 2^30, a block
  *     table below 2^29 entries.  Other shapes: KAMERA_E_UNSUPPORTED.
  * patch: NULL or rank 0 for plain attention; else a rank that is a multiple of 8, up

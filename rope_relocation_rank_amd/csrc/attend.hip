@@ -42,6 +42,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;      // prep and tile kernels
@@ -101,6 +103,9 @@ __global__ __launch_bounds__(kThreads) void attend_prep(AttendArgs a) {
   __syncthreads();
   const int W = kD + m;
   float* out = a.qw + (((int64_t)l * n + j) * Hq + g * gq) * W;
+  // fp8 keys are scale * code: the rotated query carries K's scale of the layer, so the
+  // tile kernel multiplies codes by it.
+  const float kscale = a.scale_log2 * (a.kv_scale[0] ? a.kv_scale[0][l] : 1.f);
   for (int idx = tid; idx < gq * kD; idx += kThreads) {
     const int h = idx / kD, d = idx - h * kD;
     float v = sqh[h][d];
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void attend_prep(AttendArgs a) {
         v = first ? fmaf(v, cs.x, -(b * cs.y)) : fmaf(v, cs.x, b * cs.y);
       }
     }
-    out[(int64_t)h * W + d] = v * a.scale_log2;
+    out[(int64_t)h * W + d] = v * kscale;
   }
   for (int idx = tid; idx < gq * m; idx += kThreads) {
     const int h = idx / m, k = idx - h * m;
@@ -173,6 +178,26 @@ __device__ __forceinline__ void bload_lds(rsrc_t r, uint32_t off, void* dst) {
                                            (int)opaque(off), 0, 0, 2);
 }
 
+// 8-byte loads and fp8 E4M3 codes.  Every E4M3 value is a bf16 value (3 mantissa bits),
+// so a code becomes bf16 exactly: to fp32 by the hardware conversion, then the upper
+// half of the fp32 pattern (NaN stays NaN).
+template <int AUX>
+__device__ __forceinline__ u32x2_t bload8(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)opaque(off), 0, AUX);
+}
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  const f32x2_t v = hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
+                       : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  return (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xffff0000u);
+}
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t w) {
+  return u32x4_t{fp8x2_to_bf16x2(w[0], false), fp8x2_to_bf16x2(w[0], true),
+                 fp8x2_to_bf16x2(w[1], false), fp8x2_to_bf16x2(w[1], true)};
+}
+__device__ __forceinline__ uint16_t fp8_to_bf16(uint32_t code) {
+  return (uint16_t)(__float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)code, 0)) >> 16);
+}
+
 // One wave's LDS tile: the V rows of its 16 tokens as four blocks of four 256-byte rows
 // (token 4 b + i in block b, row i), the blocks 64 bytes apart so that the transposed
 // reads of the four lane groups fall in different banks; and, in an array of its own,
@@ -180,12 +205,16 @@ __device__ __forceinline__ void bload_lds(rsrc_t r, uint32_t off, void* dst) {
 // Separate arrays let the compiler wait for exactly the request a read depends on.
 constexpr int kVBlk = 4 * 2 * kD + 64;
 constexpr int kVTile = 4 * kVBlk;
+// fp8 (rows of 128 bytes): two blocks of eight rows (token 8 b + i in block b, row i).
+constexpr int kVBlkQ = 8 * kD + 64;
+constexpr int kVTileQ = 2 * kVBlkQ;
 
 // The K-side rows of one tile as loaded: lane (c16, grp) holds features 32 ks + 8 grp ..
 // + 7 of token c16 (k), and ranks 32 ku + 8 grp .. + 7 of its U_K row (uk).
-template <int MKX>
+template <int MKX, bool Q>
 struct KRows {
-  u32x4_t k[4], uk[MKX];
+  u32x4_t k[Q ? 1 : 4], uk[MKX];
+  u32x2_t k8[Q ? 4 : 1];  // fp8: 8 codes per step, converted when used
 };
 // Where the lane's token of a tile lives: byte offsets of its K and V rows inside the
 // layer (kOob when the token lies past the segment or its page is out of range).
@@ -213,18 +242,22 @@ struct TilePages {
 // of at least 16 slots, a tile's two block-table entries read by scalar loads (which
 // count apart from the row requests); 2 paged with smaller pages, each lane reading its
 // token's entry.
-template <int MK, int PG, bool DB>
+// Q: fp8 E4M3 keys and values (per-layer scales); K rows are converted to bf16 in
+// registers, V rows read from LDS as codes.
+template <int MK, int PG, bool DB, bool Q>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MK >= 4 && DB ? 1 : MK >= 2 ? 2 : 3)))
 void attend_tiles(AttendArgs a) {
   constexpr int MKX = MK > 0 ? MK : 1;
+  constexpr uint32_t ES = Q ? 1 : 2;  // bytes per KV element
+  constexpr int kVT = Q ? kVTileQ : kVTile;
   constexpr int MU = 2 * MK;  // 16-wide rank blocks of the U_V sums
   constexpr int MUX = MU > 0 ? MU : 1;
   constexpr int kUTile = 1024 * MKX;
   constexpr int kMergeBytes = kWaves * kAttendMaxGroup * (2 + kD + 32 * MK) * 4;
-  constexpr int kBuf0 = kWaves * kVTile > kMergeBytes ? kWaves * kVTile : kMergeBytes;
+  constexpr int kBuf0 = kWaves * kVT > kMergeBytes ? kWaves * kVT : kMergeBytes;
   constexpr int kBOps = 8 + 2 * MKX;  // 16-byte query-side operands per lane
   __shared__ __align__(16) unsigned char lds0[kBuf0];  // V tiles, then the merge
-  __shared__ __align__(16) unsigned char lds1[DB ? kWaves * kVTile : 16];
+  __shared__ __align__(16) unsigned char lds1[DB ? kWaves * kVT : 16];
   __shared__ __align__(16) unsigned char ldu0[kWaves * kUTile];  // U_V tiles
   __shared__ __align__(16) unsigned char ldu1[DB ? kWaves * kUTile : 16];
   __shared__ __align__(16) u32x4_t sB[kBOps * 64];
@@ -238,7 +271,7 @@ void attend_tiles(AttendArgs a) {
   // every request touches and waits for exactly the requests a read depends on.
   using Buf0 = std::integral_constant<int, 0>;
   using Buf1 = std::integral_constant<int, 1>;
-  const int vwave = wave * kVTile, uwave = wave * kUTile;
+  const int vwave = wave * kVT, uwave = wave * kUTile;
   typedef float MergeRow[kAttendMaxGroup][2 + kD + 32 * MK];
   MergeRow* sred = (MergeRow*)lds0;
 
@@ -259,18 +292,21 @@ void attend_tiles(AttendArgs a) {
   const int m = a.rank, gq = a.group, Hq = a.num_q_heads, n = a.num_chunks;
   const int W = kD + m;
   const bool hv = c16 < gq;  // this lane's MFMA column is a real query head
-  const uint32_t ss0 = (uint32_t)a.slot_stride[0] * 2u, ss1 = (uint32_t)a.slot_stride[1] * 2u;
-  const uint32_t ps0 = (uint32_t)a.page_stride[0] * 2u, ps1 = (uint32_t)a.page_stride[1] * 2u;
+  const uint32_t ss0 = (uint32_t)a.slot_stride[0] * ES, ss1 = (uint32_t)a.slot_stride[1] * ES;
+  const uint32_t ps0 = (uint32_t)a.page_stride[0] * ES, ps1 = (uint32_t)a.page_stride[1] * ES;
+  // fp8: the value sums are sums of p * code; V's scale of the layer turns them into
+  // values when the partial is written.
+  const float vscale = Q ? a.kv_scale[1][l] : 1.f;
   const uint32_t P = (uint32_t)a.page_size;
   const int psh = (P != 0u && (P & (P - 1u)) == 0u) ? __builtin_ctz(P) : -1;
   // One resource per (layer, head) row set, from the head's first element to the end of
   // the layer; one per layer of each U factor; one over the block table.
-  const rsrc_t rk = make_rsrc((const uint16_t*)a.data[0] + (int64_t)l * a.layer_stride[0] +
-                                  (int64_t)g * a.head_stride[0],
-                              a.layer_bytes[0] - (uint32_t)(g * a.head_stride[0] * 2));
-  const rsrc_t rv = make_rsrc((const uint16_t*)a.data[1] + (int64_t)l * a.layer_stride[1] +
-                                  (int64_t)g * a.head_stride[1],
-                              a.layer_bytes[1] - (uint32_t)(g * a.head_stride[1] * 2));
+  const rsrc_t rk = make_rsrc((const unsigned char*)a.data[0] +
+                                  ((int64_t)l * a.layer_stride[0] + (int64_t)g * a.head_stride[0]) * ES,
+                              a.layer_bytes[0] - (uint32_t)(g * a.head_stride[0] * ES));
+  const rsrc_t rv = make_rsrc((const unsigned char*)a.data[1] +
+                                  ((int64_t)l * a.layer_stride[1] + (int64_t)g * a.head_stride[1]) * ES,
+                              a.layer_bytes[1] - (uint32_t)(g * a.head_stride[1] * ES));
   const uint32_t ubytes = (uint32_t)(T * m * 2);
   const rsrc_t ruk = make_rsrc(MK > 0 ? (const void*)((const uint16_t*)a.U[0] + (int64_t)l * T * m)
                                       : (const void*)a.q, MK > 0 ? ubytes : 0u);
@@ -339,11 +375,14 @@ void attend_tiles(AttendArgs a) {
       return r;
     };
     // K and U_K rows of tile ti into registers.
-    auto issue_k = [&](int ti, const RowAt& r, KRows<MKX>& R) {
+    auto issue_k = [&](int ti, const RowAt& r, KRows<MKX, Q>& R) {
       const uint32_t tt = (uint32_t)(t0 + 16 * (int64_t)ti + c16);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        R.k[ks] = bload<2>(rk, r.k == kOob ? kOob : r.k + 64u * ks + 16u * grp);
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t off = r.k == kOob ? kOob : r.k + ES * (32u * ks + 8u * grp);
+        if constexpr (Q) R.k8[ks] = bload8<2>(rk, off);
+        else R.k[ks] = bload<2>(rk, off);
+      }
 #pragma unroll
       for (int ku = 0; ku < MKX; ++ku) {
         const int k0 = 32 * ku + 8 * grp;
@@ -358,11 +397,20 @@ void attend_tiles(AttendArgs a) {
     // read zeros).
     auto issue_v = [&](int ti, const RowAt& r, auto buf) {
       constexpr bool one = decltype(buf)::value == 1;
+      if constexpr (Q) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t vr = (uint32_t)__shfl((int)r.v, 4 * b + grp);
-        bload_lds(rv, vr == kOob ? kOob : vr + 16u * c16,
-                  one ? lds1 + (vwave + b * kVBlk) : lds0 + (vwave + b * kVBlk));
+        for (int b = 0; b < 2; ++b) {  // tokens 8 b + lane / 8, bytes 16 (lane % 8)
+          const uint32_t vr = (uint32_t)__shfl((int)r.v, 8 * b + (lane >> 3));
+          bload_lds(rv, vr == kOob ? kOob : vr + 16u * (lane & 7),
+                    one ? lds1 + (vwave + b * kVBlkQ) : lds0 + (vwave + b * kVBlkQ));
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t vr = (uint32_t)__shfl((int)r.v, 4 * b + grp);
+          bload_lds(rv, vr == kOob ? kOob : vr + 16u * c16,
+                    one ? lds1 + (vwave + b * kVBlk) : lds0 + (vwave + b * kVBlk));
+        }
       }
       const int64_t tb = t0 + 16 * (int64_t)ti;
 #pragma unroll
@@ -413,7 +461,7 @@ void attend_tiles(AttendArgs a) {
     for (int u = 0; u < MUX; ++u) uacc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // Scores, online softmax and the P V and P U_V products of tile ti.
-    auto work = [&](const RowAt& r, const KRows<MKX>& R, auto buf) {
+    auto work = [&](const RowAt& r, const KRows<MKX, Q>& R, auto buf) {
       constexpr bool one = decltype(buf)::value == 1;
       const unsigned char* vs = one ? lds1 : lds0;
       const unsigned char* us = one ? ldu1 : ldu0;
@@ -421,7 +469,10 @@ void attend_tiles(AttendArgs a) {
       f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, R.k[ks]);
+        u32x4_t kw;
+        if constexpr (Q) kw = fp8x8_to_bf16x8(R.k8[ks]);
+        else kw = R.k[ks];
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, kw);
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(ks), sc, 0, 0, 0);
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bop(4 + ks), sc, 0, 0, 0);
       }
@@ -464,13 +515,20 @@ void attend_tiles(AttendArgs a) {
       }
       // O^T[f][h] += V^T[f][t] P^T[t][h]: A = V^T rows f = 16 fb + c16, tokens 4 grp + i
       // (block grp, row i of the LDS tile).
-      const int vo = vwave + grp * kVBlk + 2 * c16;
+      // bf16: token 4 grp + i is row i of block grp; fp8: row 4 (grp % 2) + i of block
+      // grp / 2.
+      const int vo = Q ? vwave + (grp >> 1) * kVBlkQ + (grp & 1) * 4 * kD + c16
+                       : vwave + grp * kVBlk + 2 * c16;
 #pragma unroll
       for (int fb = 0; fb < 8; ++fb) {
         bf16x4_t A;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          A[i] = __builtin_bit_cast(__bf16, *(const uint16_t*)(vs + (vo + 2 * (i * kD + 16 * fb))));
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (Q)
+            A[i] = __builtin_bit_cast(__bf16, fp8_to_bf16(vs[vo + i * kD + 16 * fb]));
+          else
+            A[i] = __builtin_bit_cast(__bf16, *(const uint16_t*)(vs + (vo + 2 * (i * kD + 16 * fb))));
+        }
         acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, acc[fb], 0, 0, 0);
         acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, pl, acc[fb], 0, 0, 0);
       }
@@ -495,7 +553,7 @@ void attend_tiles(AttendArgs a) {
     // with DB).
     int ti = wave;
     if (ti < ntiles) {
-      KRows<MKX> ra, rb;
+      KRows<MKX, Q> ra, rb;
       Pages pg_n = lookup(ti + 4);
       RowAt ra_at = row_at(ti, lookup(ti)), rb_at{kOob, kOob};
       issue_k(ti, ra_at, ra);
@@ -578,7 +636,7 @@ void attend_tiles(AttendArgs a) {
         sl[1] = L;
         sl[2] = __int_as_float(j);
       }
-      sl[kAttendSlotHead + e] = A;
+      sl[kAttendSlotHead + e] = e < kD ? A * vscale : A;
     }
     __syncthreads();  // the next segment reuses the LDS for tiles and operands
     t0 = s1;
@@ -686,10 +744,15 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     const dim3 grid1((unsigned)((int64_t)a.num_layers * a.splits * a.heads));
     const int mk = (a.rank + 31) / 32;
     const bool db = a.double_buffer != 0 && mk <= 2;
-#define KAMERA_ATT2(MK, PG)                                                              \
-  do {                                                                                   \
-    if (db) hipLaunchKernelGGL((attend_tiles<MK, PG, true>), grid1, dim3(kThreads), 0, s, a);  \
-    else hipLaunchKernelGGL((attend_tiles<MK, PG, false>), grid1, dim3(kThreads), 0, s, a);    \
+#define KAMERA_ATT3(MK, PG, Q)                                                                  \
+  do {                                                                                          \
+    if (db) hipLaunchKernelGGL((attend_tiles<MK, PG, true, Q>), grid1, dim3(kThreads), 0, s, a);  \
+    else hipLaunchKernelGGL((attend_tiles<MK, PG, false, Q>), grid1, dim3(kThreads), 0, s, a);    \
+  } while (0)
+#define KAMERA_ATT2(MK, PG)                    \
+  do {                                         \
+    if (a.fp8) KAMERA_ATT3(MK, PG, true);      \
+    else KAMERA_ATT3(MK, PG, false);           \
   } while (0)
 #define KAMERA_ATT(MK)                              \
   do {                                              \
@@ -703,6 +766,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     else KAMERA_ATT(4);
 #undef KAMERA_ATT
 #undef KAMERA_ATT2
+#undef KAMERA_ATT3
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

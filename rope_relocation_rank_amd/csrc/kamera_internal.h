@@ -114,6 +114,8 @@ struct AttendArgs {
   int32_t splits, split_tokens, slots, slot_floats;
   uint32_t layer_bytes[2];    // bytes of one layer of each channel (below 2^31 - 64)
   int32_t double_buffer;      // tile kernel: the next tile's V rows go to a second LDS tile
+  int32_t fp8;                // KV elements are fp8 E4M3 codes with per-layer scales
+  const float* kv_scale[2];   // fp8: [layers] scale of K and of V; else nullptr
   float scale_log2;           // softmax scale * log2(e): scores are kept in base 2
   double omega[64];           // theta^(-2i/rope_dim)
 };

@@ -117,13 +117,14 @@ WORKLOADS = {
     "qwen25vl7b_segment_fp8": Workload(
         key="qwen25vl7b_segment_fp8", wid=6, family="gqa", layers=28, heads=4, head_dim=128,
         theta=1e6, rank=32, passes=(0, 32), tokens=4096, delta=-1536, outliers=4, dtype="fp8",
+        q_heads=28,
         note="Qwen2.5-VL-7B-shaped video segment in an fp8 E4M3 cache (per-layer scales): "
              "28 layers, 4 KV heads x 128, T=4096, delta -1536; rotation-only pass then "
              "rank-32 patch pass"),
     "long_video_72b_paged_fp8": Workload(
         key="long_video_72b_paged_fp8", wid=7, family="gqa", layers=80, heads=8, head_dim=128,
         theta=1e6, rank=64, tokens=32768, delta=65536, page_size=16, pool_pages=2048,
-        dtype="fp8",
+        dtype="fp8", q_heads=64,
         note="72B-shaped long-video paged cache in fp8 E4M3 (per-layer scales): 80 layers, "
              "8 KV heads x 128, T=32768 in 16-token pages under a random block table, "
              "delta +65536, rank-64"),

@@ -642,10 +642,10 @@ def test_attend_workspace_and_checks():
     st, nbytes = K.kamera_attend_workspace(kv, ch, p, d)
     assert st == K.KAMERA_OK and nbytes > 0
     # prepared queries [L][chunks][Hq][128 + m], then partial slots [L][Hq][slots][164]
-    # (max, sum, chunk, one unused float, 128 + m sums); contiguous: one wave per
-    # (layer, KV head, split), 8192 waves would take 74 splits, capped at 32 splits of
-    # 128 tokens
-    assert nbytes == 28 * 1 * 28 * (128 + 32) * 4 + 28 * 28 * 32 * 164 * 4
+    # (max, sum, chunk, one unused float, 128 + m sums); one 4-wave workgroup per (layer,
+    # KV head, split): 4096 workgroups would take 37 splits, capped at 4 splits of 1024
+    # tokens
+    assert nbytes == 28 * 1 * 28 * (128 + 32) * 4 + 28 * 28 * 4 * 164 * 4
     st, st2 = attend_status(kv, ch, p, d)
     assert st2 == K.KAMERA_E_NULL  # no workspace given
     for mutate, status in [

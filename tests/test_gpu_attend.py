@@ -147,9 +147,45 @@ def test_cache_untouched_and_matches_relocate_then_attend():
     assert diff <= 2e-2 * ref
 
 
+@pytest.mark.parametrize("P", [1, 4, 8, 32, 64])
+def test_page_sizes(P):
+    # pages of 16 slots or more: a tile's two block-table entries by scalar reads; below
+    # 16, each lane reads its token's entry
+    w = synth.get("long_video_72b_paged").with_(layers=2, tokens=333, page_size=P,
+                                                pool_pages=-(-333 // P) + 5)
+    _case(w, 32, label=f"pages of {P}")
+
+
+# ----------------------------------------------------------------- fp8 E4M3 caches
+
+@pytest.mark.parametrize("rank", [0, 32])
+def test_fp8_qwen_segment_reduced(rank):
+    # codes with per-layer scales of K and V; a group of 7 query heads per KV head
+    _case(synth.get("qwen25vl7b_segment_fp8").with_(layers=3, tokens=1000), rank)
+
+
+def test_fp8_paged_reduced_with_spare_pages():
+    _case(synth.get("long_video_72b_paged_fp8").with_(layers=2, tokens=1000, pool_pages=100), 64)
+
+
+def test_fp8_chunks_and_variants():
+    # many ragged chunks (splits cut at chunk boundaries), interleaved pairing, rank 16
+    w = synth.get("qwen25vl7b_segment_fp8").with_(layers=2, n_chunks=7, chunk_len=(1, 200),
+                                                  pairing=1)
+    _case(w, 16, label="fp8 chunks interleaved")
+
+
+def test_fp8_small_pages():
+    # pages of 4 slots: each lane reads its token's block-table entry
+    w = synth.get("long_video_72b_paged_fp8").with_(layers=2, tokens=300, page_size=4,
+                                                    pool_pages=90)
+    _case(w, 32, label="fp8 pages of 4")
+
+
 @pytest.mark.parametrize("key,layers", [("qwen25vl7b_segment", (0, 13, 27)),
                                         ("long_video_72b_paged", (0, 79)),
-                                        ("llama3_8b_reorder", (0, 31))])
+                                        ("llama3_8b_reorder", (0, 31)),
+                                        ("long_video_72b_paged_fp8", (0, 79))])
 def test_full_size_sampled_layers(key, layers):
     w = synth.get(key)
     rank = w.rank
