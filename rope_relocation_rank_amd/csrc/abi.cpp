@@ -736,6 +736,7 @@ kamera_status run_form(const kamera_form_desc* d, const kamera_chunks* ch, void*
 struct AttendPlan {
   int64_t splits = 0, split_tokens = 0, slots = 0, bytes = 0;
   int64_t qw_bytes = 0;  // prepared queries, first in the workspace (256-byte rounded)
+  bool heads_mapping = false;  // one wave per KV head, a workgroup per (layer, split)
 };
 
 // Checks an attention call; no HIP call is made here.
@@ -797,8 +798,15 @@ kamera_status validate_attend(const kamera_kv_desc* kv, const kamera_chunks* ch,
   // tokens each (a workgroup's setup and merge cost about as much as 16 tiles; measured:
   // fewer, longer splits on the Qwen-shaped call, 0.098 -> 0.076 ms, and no change on
   // the large calls).
+  // With one wave per KV head a workgroup holds all heads of a split: 16384 waves, at
+  // least 1024 tokens each.  Measured faster with 8 KV heads at ranks up to 32 (the
+  // Llama-shaped call, 2.33 -> 2.25 ms) and slower on the 72B- and Qwen-shaped calls;
+  // KAMERA_ATTEND_HM=0/1 overrides (up to 8 heads).
+  const bool hm_default = K.heads == kamera::kAttendMaxHeadsPerGroup && m <= 32;
+  plan->heads_mapping = K.heads <= kamera::kAttendMaxHeadsPerGroup &&
+                        env_int("KAMERA_ATTEND_HM", hm_default ? 1 : 0) != 0;
   const int64_t units = L * K.heads;
-  int64_t S = std::max<int64_t>(1, ceil_div(4096, units));
+  int64_t S = std::max<int64_t>(1, ceil_div(plan->heads_mapping ? 16384 : 4096, units));
   S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(T, 1024)));
   const int env_splits = env_int("KAMERA_ATTEND_SPLITS", 0);
   if (env_splits > 0) S = env_splits;
@@ -911,6 +919,7 @@ kamera_status run_attend(const kamera_kv_desc* kv, const kamera_chunks* ch, cons
   // workgroups per CU): measured best at ranks 33-64, and no better or slower below;
   // KAMERA_ATTEND_DB=0/1 overrides.
   a.double_buffer = env_int("KAMERA_ATTEND_DB", m > 32 && m <= 64 ? 1 : 0) != 0;
+  a.heads_mapping = plan.heads_mapping;
   a.scale_log2 = at->scale * 1.4426950408889634f;
   for (int i = 0; i < a.rope_dim / 2 && i < 64; ++i)
     a.omega[i] = pow(kv->rope_theta, -2.0 * (double)i / (double)a.rope_dim);

@@ -171,8 +171,17 @@ template <int AUX>
 __device__ __forceinline__ u32x4_t bload(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)opaque(off), 0, AUX);
 }
+// Waits until at most n vector-memory requests of this wave are outstanding (vmcnt;
+// the export and LDS counters are left alone).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 // 16 bytes per lane straight into LDS: lane i's bytes land at dst + 16 i (dst is
-// wave-uniform).  No registers are held while the request is in flight.
+// wave-uniform).  No registers are held while the request is in flight.  The compiler
+// does not reliably wait for these before later LDS reads of the same bytes, so the
+// tile loop waits for them itself (wait_vm), with the requests kept in program order.
 __device__ __forceinline__ void bload_lds(rsrc_t r, uint32_t off, void* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
                                            (int)opaque(off), 0, 0, 2);
@@ -243,24 +252,30 @@ struct TilePages {
 // count apart from the row requests); 2 paged with smaller pages, each lane reading its
 // token's entry.
 // Q: fp8 E4M3 keys and values (per-layer scales); K rows are converted to bf16 in
-// registers, V rows read from LDS as codes.
-template <int MK, int PG, bool DB, bool Q>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MK >= 4 && DB ? 1 : MK >= 2 ? 2 : 3)))
+// registers, V rows read from LDS as codes.  HM: one workgroup per (layer, token
+// range) with one wave per KV head (heads <= 8), each wave walking every tile of the
+// range and writing its own partials; the waves request the same U rows at about the
+// same time from one CU, so those are fetched once per range instead of once per head.
+template <int MK, int PG, bool DB, bool Q, bool HM>
+__global__ __launch_bounds__(HM ? 64 * kAttendMaxHeadsPerGroup : kThreads)
+__attribute__((amdgpu_waves_per_eu(MK >= 4 && DB ? 1 : MK >= 2 || HM ? 2 : 3)))
 void attend_tiles(AttendArgs a) {
   constexpr int MKX = MK > 0 ? MK : 1;
+  constexpr int NW = HM ? kAttendMaxHeadsPerGroup : kWaves;  // waves per workgroup (at most)
+  constexpr int TSTEP = HM ? 1 : kWaves;                      // a wave's tile stride
   constexpr uint32_t ES = Q ? 1 : 2;  // bytes per KV element
   constexpr int kVT = Q ? kVTileQ : kVTile;
   constexpr int MU = 2 * MK;  // 16-wide rank blocks of the U_V sums
   constexpr int MUX = MU > 0 ? MU : 1;
   constexpr int kUTile = 1024 * MKX;
-  constexpr int kMergeBytes = kWaves * kAttendMaxGroup * (2 + kD + 32 * MK) * 4;
-  constexpr int kBuf0 = kWaves * kVT > kMergeBytes ? kWaves * kVT : kMergeBytes;
+  constexpr int kMergeBytes = HM ? 0 : kWaves * kAttendMaxGroup * (2 + kD + 32 * MK) * 4;
+  constexpr int kBuf0 = NW * kVT > kMergeBytes ? NW * kVT : kMergeBytes;
   constexpr int kBOps = 8 + 2 * MKX;  // 16-byte query-side operands per lane
   __shared__ __align__(16) unsigned char lds0[kBuf0];  // V tiles, then the merge
-  __shared__ __align__(16) unsigned char lds1[DB ? kWaves * kVT : 16];
-  __shared__ __align__(16) unsigned char ldu0[kWaves * kUTile];  // U_V tiles
-  __shared__ __align__(16) unsigned char ldu1[DB ? kWaves * kUTile : 16];
-  __shared__ __align__(16) u32x4_t sB[kBOps * 64];
+  __shared__ __align__(16) unsigned char lds1[DB ? NW * kVT : 16];
+  __shared__ __align__(16) unsigned char ldu0[NW * kUTile];  // U_V tiles
+  __shared__ __align__(16) unsigned char ldu1[DB ? NW * kUTile : 16];
+  __shared__ __align__(16) u32x4_t sB[HM ? 1 : kBOps * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -278,13 +293,21 @@ void attend_tiles(AttendArgs a) {
   const uint32_t S = (uint32_t)a.splits;
   const uint32_t H = (uint32_t)a.heads;
   const uint32_t bid = blockIdx.x;
-  // Workgroup order: split fastest, then KV head, then layer.  (Placing the KV heads of
-  // one (layer, split) on one XCD, so that they read the range's U rows from one L2,
-  // measured 3-4% slower.)
-  const uint32_t lg = bid / S;
-  const int s = (int)(bid - lg * S);
-  const int l = (int)(lg / H);
-  const int g = (int)(lg - (uint32_t)l * H);
+  int s, l, g;
+  if constexpr (HM) {
+    // Split fastest, then layer; wave w runs KV head w.
+    l = (int)(bid / S);
+    s = (int)(bid - (uint32_t)l * S);
+    g = wave;
+  } else {
+    // Split fastest, then KV head, then layer.  (Placing the KV heads of one (layer,
+    // split) on one XCD, so that they read the range's U rows from one L2, measured 3-4%
+    // slower.)
+    const uint32_t lg = bid / S;
+    s = (int)(bid - lg * S);
+    l = (int)(lg / H);
+    g = (int)(lg - (uint32_t)l * H);
+  }
   const int64_t T = a.total_tokens;
   const int64_t t_lo = (int64_t)s * a.split_tokens;
   const int64_t t_hi = min(T, t_lo + (int64_t)a.split_tokens);
@@ -422,9 +445,11 @@ void attend_tiles(AttendArgs a) {
       }
     };
 
-    // B operands: this lane's query head (column c16), features 32 ks + 8 grp ...  Every
-    // wave writes the same values for the segment; the previous segment's readers all
-    // passed the barrier that ends it.
+    // B operands: this lane's query head (column c16), features 32 ks + 8 grp ...  HM:
+    // in registers (each wave its own head).  Otherwise every wave writes the same values
+    // to LDS for the segment; the previous segment's readers all passed the barrier that
+    // ends it.
+    bf16x8_t bq[HM ? kBOps : 1];
     {
       const float* qp = a.qw + (((int64_t)l * n + j) * Hq + g * gq + (hv ? c16 : 0)) * W;
 #pragma unroll
@@ -434,8 +459,13 @@ void attend_tiles(AttendArgs a) {
         for (int e = 0; e < 8; ++e) x[e] = hv ? qp[32 * ks + 8 * grp + e] : 0.f;
         bf16x8_t hi, lo;
         split8(x, hi, lo);
-        sB[ks * 64 + lane] = __builtin_bit_cast(u32x4_t, hi);
-        sB[(4 + ks) * 64 + lane] = __builtin_bit_cast(u32x4_t, lo);
+        if constexpr (HM) {
+          bq[ks] = hi;
+          bq[4 + ks] = lo;
+        } else {
+          sB[ks * 64 + lane] = __builtin_bit_cast(u32x4_t, hi);
+          sB[(4 + ks) * 64 + lane] = __builtin_bit_cast(u32x4_t, lo);
+        }
       }
 #pragma unroll
       for (int ku = 0; ku < MKX; ++ku) {
@@ -447,11 +477,19 @@ void attend_tiles(AttendArgs a) {
         }
         bf16x8_t hi, lo;
         split8(x, hi, lo);
-        sB[(8 + ku) * 64 + lane] = __builtin_bit_cast(u32x4_t, hi);
-        sB[(8 + MKX + ku) * 64 + lane] = __builtin_bit_cast(u32x4_t, lo);
+        if constexpr (HM) {
+          bq[8 + ku] = hi;
+          bq[8 + MKX + ku] = lo;
+        } else {
+          sB[(8 + ku) * 64 + lane] = __builtin_bit_cast(u32x4_t, hi);
+          sB[(8 + MKX + ku) * 64 + lane] = __builtin_bit_cast(u32x4_t, lo);
+        }
       }
     }
-    auto bop = [&](int o) -> bf16x8_t { return __builtin_bit_cast(bf16x8_t, sB[o * 64 + lane]); };
+    auto bop = [&](int o) -> bf16x8_t {
+      if constexpr (HM) return bq[o];
+      else return __builtin_bit_cast(bf16x8_t, sB[o * 64 + lane]);
+    };
 
     float mrun = -INFINITY, lrun = 0.f;
     f32x4_t acc[8], uacc[MUX];
@@ -461,6 +499,9 @@ void attend_tiles(AttendArgs a) {
     for (int u = 0; u < MUX; ++u) uacc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // Scores, online softmax and the P V and P U_V products of tile ti.
+    // Requests per tile: K and U_K rows into registers, V and U_V rows into LDS, and
+    // with small pages one block-table read per lane.
+    constexpr int kReqK = 4 + MK, kReqV = (Q ? 2 : 4) + MK, kReqPg = PG == 2 ? 1 : 0;
     auto work = [&](const RowAt& r, const KRows<MKX, Q>& R, auto buf) {
       constexpr bool one = decltype(buf)::value == 1;
       const unsigned char* vs = one ? lds1 : lds0;
@@ -515,6 +556,11 @@ void attend_tiles(AttendArgs a) {
       }
       // O^T[f][h] += V^T[f][t] P^T[t][h]: A = V^T rows f = 16 fb + c16, tokens 4 grp + i
       // (block grp, row i of the LDS tile).
+      // This tile's V and U_V requests are done once no more than the requests issued
+      // after them are outstanding: the next tile's block-table read, K and U_K rows
+      // and (DB) V and U_V rows.
+      wait_vm<kReqPg + kReqK + (DB ? kReqV : 0)>();
+      __builtin_amdgcn_sched_barrier(0);
       // bf16: token 4 grp + i is row i of block grp; fp8: row 4 (grp % 2) + i of block
       // grp / 2.
       const int vo = Q ? vwave + (grp >> 1) * kVBlkQ + (grp & 1) * 4 * kD + c16
@@ -551,10 +597,10 @@ void attend_tiles(AttendArgs a) {
 
     // The wave's tiles, two per loop pass (registers ra / rb alternate; LDS tile 0 / 1
     // with DB).
-    int ti = wave;
+    int ti = HM ? 0 : wave;
     if (ti < ntiles) {
       KRows<MKX, Q> ra, rb;
-      Pages pg_n = lookup(ti + 4);
+      Pages pg_n = lookup(ti + TSTEP);
       RowAt ra_at = row_at(ti, lookup(ti)), rb_at{kOob, kOob};
       issue_k(ti, ra_at, ra);
       issue_v(ti, ra_at, Buf0{});
@@ -563,42 +609,66 @@ void attend_tiles(AttendArgs a) {
         // exists (past the segment they read zeros): a request under a branch would
         // leave the join after it unsure which LDS tile is in flight, and the reads of
         // the current tile would then wait for every request.
-        const Pages pg_nn = lookup(ti + 8);
-        const bool more = ti + 4 < ntiles;
-        rb_at = row_at(ti + 4, pg_n);
-        issue_k(ti + 4, rb_at, rb);
-        if constexpr (DB) issue_v(ti + 4, rb_at, Buf1{});
+        __builtin_amdgcn_sched_barrier(0);
+        const Pages pg_nn = lookup(ti + 2 * TSTEP);
+        const bool more = ti + TSTEP < ntiles;
+        rb_at = row_at(ti + TSTEP, pg_n);
+        issue_k(ti + TSTEP, rb_at, rb);
+        if constexpr (DB) issue_v(ti + TSTEP, rb_at, Buf1{});
+        __builtin_amdgcn_sched_barrier(0);
         work(ra_at, ra, Buf0{});
         if (!more) break;
         if (!DB) {
           lds_reads_done();
-          issue_v(ti + 4, rb_at, Buf0{});
+          issue_v(ti + TSTEP, rb_at, Buf0{});
         }
-        ti += 4;
+        ti += TSTEP;
+        __builtin_amdgcn_sched_barrier(0);
         // tile ti: rb, LDS tile 1 (DB) or 0
-        const Pages pg_n3 = lookup(ti + 8);
-        const bool more2 = ti + 4 < ntiles;
-        ra_at = row_at(ti + 4, pg_nn);
-        issue_k(ti + 4, ra_at, ra);
-        if constexpr (DB) issue_v(ti + 4, ra_at, Buf0{});
+        const Pages pg_n3 = lookup(ti + 2 * TSTEP);
+        const bool more2 = ti + TSTEP < ntiles;
+        ra_at = row_at(ti + TSTEP, pg_nn);
+        issue_k(ti + TSTEP, ra_at, ra);
+        if constexpr (DB) issue_v(ti + TSTEP, ra_at, Buf0{});
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (DB) work(rb_at, rb, Buf1{});
         else work(rb_at, rb, Buf0{});
         if (!more2) break;
         if (!DB) {
           lds_reads_done();
-          issue_v(ti + 4, ra_at, Buf0{});
+          issue_v(ti + TSTEP, ra_at, Buf0{});
         }
-        ti += 4;
+        ti += TSTEP;
         pg_n = pg_n3;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // The four lane groups of a column hold disjoint tokens' sums.
     lrun += __shfl_xor(lrun, 16);
     lrun += __shfl_xor(lrun, 32);
 
-    // Merge the four waves' partials through LDS, then write the segment's slot: lane
-    // (c16, grp) holds features 16 fb + 4 grp + i of the value sums and 16 ub + 4 grp + i
-    // of the U_V sums of query head c16.
+    // Lane (c16, grp) holds features 16 fb + 4 grp + i of the value sums and 16 ub +
+    // 4 grp + i of the U_V sums of query head c16.  HM: the wave writes its head's slot.
+    if constexpr (HM) {
+      if (hv) {
+        float* sl = wsp + (((int64_t)l * Hq + g * gq + c16) * a.slots + (s + j)) * a.slot_floats;
+        if (grp == 0) {
+          sl[0] = mrun;
+          sl[1] = lrun;
+          sl[2] = __int_as_float(j);
+        }
+#pragma unroll
+        for (int fb = 0; fb < 8; ++fb)
+          *(f32x4_t*)(sl + kAttendSlotHead + 16 * fb + 4 * grp) = acc[fb] * vscale;
+#pragma unroll
+        for (int ub = 0; ub < MU; ++ub)
+          if (16 * ub + 4 * grp < m)
+            *(f32x4_t*)(sl + kAttendSlotHead + kD + 16 * ub + 4 * grp) = uacc[ub];
+      }
+      t0 = s1;
+      continue;
+    }
+    // Otherwise merge the four waves' partials through LDS, then write the segment's slot.
     __syncthreads();  // every wave's tile reads are done: the tiles' LDS holds the merge
     if (hv) {
       if (grp == 0) {
@@ -740,14 +810,22 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.splits > 0) {  // no tokens: only the merge runs, writing 0 and -inf
     const dim3 grid0((unsigned)((int64_t)a.num_layers * a.num_chunks * a.heads));
     hipLaunchKernelGGL(attend_prep, grid0, dim3(kThreads), 0, s, a);
-    // A 4-wave workgroup per (layer, split, KV head).
-    const dim3 grid1((unsigned)((int64_t)a.num_layers * a.splits * a.heads));
+    // A 4-wave workgroup per (layer, split, KV head), or (HM) one wave per KV head in a
+    // workgroup per (layer, split).
+    const bool hm = a.heads_mapping != 0;
+    const dim3 grid1((unsigned)((int64_t)a.num_layers * a.splits * (hm ? 1 : a.heads)));
+    const dim3 block1((unsigned)(hm ? 64 * a.heads : kThreads));
     const int mk = (a.rank + 31) / 32;
     const bool db = a.double_buffer != 0 && mk <= 2;
-#define KAMERA_ATT3(MK, PG, Q)                                                                  \
-  do {                                                                                          \
-    if (db) hipLaunchKernelGGL((attend_tiles<MK, PG, true, Q>), grid1, dim3(kThreads), 0, s, a);  \
-    else hipLaunchKernelGGL((attend_tiles<MK, PG, false, Q>), grid1, dim3(kThreads), 0, s, a);    \
+#define KAMERA_ATT4(MK, PG, Q, HM)                                                             \
+  do {                                                                                         \
+    if (db) hipLaunchKernelGGL((attend_tiles<MK, PG, true, Q, HM>), grid1, block1, 0, s, a);   \
+    else hipLaunchKernelGGL((attend_tiles<MK, PG, false, Q, HM>), grid1, block1, 0, s, a);     \
+  } while (0)
+#define KAMERA_ATT3(MK, PG, Q)                  \
+  do {                                          \
+    if (hm) KAMERA_ATT4(MK, PG, Q, true);       \
+    else KAMERA_ATT4(MK, PG, Q, false);         \
   } while (0)
 #define KAMERA_ATT2(MK, PG)                    \
   do {                                         \
@@ -767,6 +845,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
 #undef KAMERA_ATT
 #undef KAMERA_ATT2
 #undef KAMERA_ATT3
+#undef KAMERA_ATT4
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

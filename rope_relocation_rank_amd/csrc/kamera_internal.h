@@ -115,6 +115,7 @@ struct AttendArgs {
   uint32_t layer_bytes[2];    // bytes of one layer of each channel (below 2^31 - 64)
   int32_t double_buffer;      // tile kernel: the next tile's V rows go to a second LDS tile
   int32_t fp8;                // KV elements are fp8 E4M3 codes with per-layer scales
+  int32_t heads_mapping;      // tile kernel: one wave per KV head, a workgroup per range
   const float* kv_scale[2];   // fp8: [layers] scale of K and of V; else nullptr
   float scale_log2;           // softmax scale * log2(e): scores are kept in base 2
   double omega[64];           // theta^(-2i/rope_dim)
@@ -122,6 +123,7 @@ struct AttendArgs {
 
 constexpr int kAttendDim = 128;
 constexpr int kAttendMaxGroup = 8;
+constexpr int kAttendMaxHeadsPerGroup = 8;  // KV heads of the one-wave-per-head mapping
 // Floats of one partial slot at rank m: max, sum, chunk, one unused float (the sums
 // start 16-byte aligned), 128 value sums, m U_V sums; padded to a multiple of 4.
 constexpr int kAttendSlotHead = 4;

@@ -202,3 +202,15 @@ def test_full_size_sampled_layers(key, layers):
         assert rep.ok(), str(rep)
     del inp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("hm", ["0", "1"])
+@pytest.mark.parametrize("key,rank", [("llama3_8b_reorder", 16), ("long_video_72b_paged", 64),
+                                      ("long_video_72b_paged_fp8", 64)])
+def test_both_work_mappings(monkeypatch, hm, key, rank):
+    # The tile kernel's two mappings (a 4-wave workgroup per KV head and range, or one
+    # wave per KV head in a workgroup per range), each forced on a reduced shape.
+    monkeypatch.setenv("KAMERA_ATTEND_HM", hm)
+    w = synth.get(key).with_(layers=2)
+    w = w.with_(n_chunks=5, chunk_len=(1, 400)) if w.n_chunks > 1 else w.with_(tokens=900, pool_pages=80 if w.page_size else 0)
+    _case(w, rank, label=f"{key} mapping hm={hm}")
