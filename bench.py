@@ -509,7 +509,11 @@ def bench_attend(args, w, dev):
     for c in insts:
         kv, ch, p = ops.descriptors_for(c)
         pc = K.chunks_desc(c.offsets_t, zero, st.total_tokens)
-        (kv2, _, _, d2), _, _, ws2 = ops.attend_buffers(c, q, scale)
+        (kv2, _, _, d2), _, _, _ = ops.attend_buffers(c, q, scale)
+        # sized for this call: with no patch the planner may pick another mapping
+        st2, nb2 = K.kamera_attend_workspace(kv2, pc, None, d2)
+        K.check(st2)
+        ws2 = torch.empty(max(nb2, 16), dtype=torch.uint8, device=dev) if nb2 else None
         plain.append((kv, ch, p, kv2, pc, d2, ws2))
 
     def unfused(i):
