@@ -23,6 +23,7 @@
 // of the subspace iteration shrinks like (lambda_{k+1} / lambda_i)^iters.
 #include <hip/hip_runtime.h>
 
+
 #include "kamera_internal.h"
 
 namespace kamera {
@@ -33,8 +34,21 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
 constexpr int kThreads = 256;
 constexpr int kMaxK = 128;
+
+// A raw buffer resource over [base, base + bytes): loads at offsets past the end return
+// zeros.  `opaque` keeps an offset in a vector register as computed.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 __device__ __forceinline__ uint16_t f2bf16(float y) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(y));  // round to nearest even
@@ -167,6 +181,8 @@ __global__ __launch_bounds__(kThreads) void gram_tiles(FormArgs P, int64_t p0, f
 // MFMAs per wave between barriers.  The next step's rows are loaded into registers
 // before the current step's MFMAs; rows go to LDS transposed two tokens at a time
 // (one 32-bit word holds a feature's pair of tokens).
+// Used where a chunk's rows span 2^31 - 64 bytes or more (the buffer resources of
+// gram_tr cannot reach them).
 __global__ __launch_bounds__(kThreads) void gram_tiles128(FormArgs P, int64_t p0, float* Gbase,
                                                           int64_t gstride) {
   const int ntile = P.F / 128;
@@ -260,6 +276,176 @@ __global__ __launch_bounds__(kThreads) void gram_tiles128(FormArgs P, int64_t p0
           acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
     }
   }
+  const int c = lane & 15;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gi = ti * 128 + wi * 64 + x * 16 + 4 * g + r;
+        const int gj = tj * 128 + wj * 64 + y * 16 + c;
+        G[(int64_t)gi * P.F + gj] = acc[x][y][r];
+        if (ti != tj) G[(int64_t)gj * P.F + gi] = acc[x][y][r];
+      }
+}
+
+// The same 128 x 128 tiles with the rows staged in LDS as they lie in memory.  Each
+// 64-token step's rows of both 128-feature column blocks go straight from memory into
+// one of two LDS stages (16 bytes per lane per request, no registers held), one step
+// ahead of the MFMAs; deeper rings measured slower (each wave's requests run further
+// ahead of the other tiles of its problem, whose reads of the same rows then miss the
+// L2 more often).  The MFMA operands come from the untransposed rows through the
+// gfx950 transposing LDS read: within each 16-lane group, lane i receives as its
+// element e element i & 3 of the 8 bytes that lane 4 e + (i >> 2) addressed.  So when
+// lane s of group g addresses row 8 g + 4 h + (s >> 2) at features f + 4 (s & 3),
+// lane i holds feature f + i of rows 8 g + 4 h .. 8 g + 4 h + 3: half of its MFMA
+// operand (the tokens are the contraction index).  A row is 256 bytes, all 64 banks;
+// its 32-byte slot q sits at slot q ^ sw(r), sw(r) = (r & 3) | ((r >> 3) & 1) << 2, so
+// the eight rows a half-wave reads fall in eight different slots.  One barrier per
+// step: the stage a step's requests overwrite was read in the step before.
+constexpr uint32_t kGramOob = 0x80000000u;  // past every chunk: such requests read zeros
+
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint32_t off, unsigned char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           (int)opaque(off), 0, 0, 0);
+}
+// Waits until at most n vector-memory requests of this wave are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2_t lds_tr16(const unsigned char* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) i16x4_t*)p));
+}
+
+__global__ __launch_bounds__(kThreads) void gram_tr(FormArgs P, int64_t p0, float* Gbase,
+                                                    int64_t gstride) {
+  constexpr int KS = 64;                  // tokens per step
+  constexpr int kStage = KS * 256;        // bytes of one block's rows in one step
+  constexpr int kSeg = kStage / 4096;     // 1 KB requests per wave, per block and step
+  const int ntile = P.F / 128;
+  const Blk bk = xcd_block();
+  const int prob = (int)bk.y;
+  int rem = (int)bk.x, ti = 0;
+  while (rem >= ntile - ti) {
+    rem -= ntile - ti;
+    ++ti;
+  }
+  const int tj = ti + rem;
+  const int64_t p = p0 + prob;
+  const int64_t layer = p / P.num_chunks;
+  const int j = (int)(p - layer * P.num_chunks);
+  const int64_t a = min(max(P.offsets[j], (int64_t)0), P.total_tokens);
+  const int64_t b = min(max(P.offsets[j + 1], a), P.total_tokens);
+  float* G = Gbase + (int64_t)prob * gstride;
+  const uint16_t* D = P.delta + layer * P.total_tokens * P.F;
+  const int64_t nrows = b - a;
+  const rsrc_t rd = make_rsrc(D + a * P.F, (uint32_t)(nrows * P.F * 2));
+
+  // Stage k: block ti's rows at bytes [0, kStage), block tj's at [kStage, 2 kStage).  A
+  // diagonal tile (ti == tj) reads both operands from the first half; its requests for
+  // the second go past the chunk (no memory traffic, zeros) to keep the count uniform.
+  // One array per stage: the compiler then waits for exactly the requests a read needs.
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[2 * kStage], st1[2 * kStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = wave >> 1, wj = wave & 1;
+  const bool diag = ti == tj;
+
+  // Requests: this wave's segment jj = wave * kSeg + i of a block (bytes 1024 jj ..)
+  // holds rows 4 jj .. 4 jj + 3; lane l writes 16-byte group l & 15 of row
+  // 4 jj + (l >> 4), which holds the row's logical group (l & 15) ^ 2 sw(row).
+  const int rq = lane >> 4, gp = lane & 15;
+  uint32_t colA[kSeg], colB[kSeg];
+#pragma unroll
+  for (int i = 0; i < kSeg; ++i) {
+    const int jj = wave * kSeg + i;
+    const int sw = rq | (((jj >> 1) & 1) << 2);
+    const int lg = gp ^ (2 * sw);
+    colA[i] = 2u * (uint32_t)(ti * 128 + 8 * lg);
+    colB[i] = 2u * (uint32_t)(tj * 128 + 8 * lg);
+  }
+  auto issue = [&](unsigned char* dst, int64_t st) {
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) {
+      const int jj = wave * kSeg + i;
+      const int64_t row = st * KS + 4 * jj + rq;
+      const uint32_t ro = row < nrows ? (uint32_t)(row * P.F * 2) : kGramOob;
+      lds_dma16(rd, ro + colA[i], dst + 1024 * jj);
+      lds_dma16(rd, diag ? kGramOob : ro + colB[i], dst + kStage + 1024 * jj);
+    }
+  };
+  // Operand reads: lane (s, g), s = lane & 15, g = lane >> 4.  Row 32 ks + 8 g + 4 h +
+  // (s >> 2) has sw = (s >> 2) | (g & 1) << 2 whatever ks and h are.
+  const int s16 = lane & 15, g = lane >> 4;
+  const int swr = (s16 >> 2) | ((g & 1) << 2);
+  const int rbase = (8 * g + (s16 >> 2)) * 256 + 8 * (s16 & 3);
+  const int bhalf = diag ? 0 : kStage;
+  int offA[4], offB[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    offA[x] = rbase + 32 * ((wi * 4 + x) ^ swr);
+    offB[x] = bhalf + rbase + 32 * ((wj * 4 + x) ^ swr);
+  }
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const unsigned char* src) {
+#pragma unroll
+    for (int ks = 0; ks < KS / 32; ++ks) {
+      bf16x8_t fa[4], fb[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const u32x2_t a0 = lds_tr16(src + ks * 32 * 256 + offA[x]);
+        const u32x2_t a1 = lds_tr16(src + ks * 32 * 256 + 4 * 256 + offA[x]);
+        const u32x2_t b0 = lds_tr16(src + ks * 32 * 256 + offB[x]);
+        const u32x2_t b1 = lds_tr16(src + ks * 32 * 256 + 4 * 256 + offB[x]);
+        fa[x] = __builtin_bit_cast(bf16x8_t, u32x4_t{a0[0], a0[1], a1[0], a1[1]});
+        fb[x] = __builtin_bit_cast(bf16x8_t, u32x4_t{b0[0], b0[1], b1[0], b1[1]});
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    }
+  };
+  // Step st reads stage st % 2.  Before it, this wave's requests of that stage are done
+  // (vmcnt 0: the other stage's were issued after the previous step's reads); the
+  // barrier makes every wave's done, and every wave has read the other stage, which the
+  // next step's requests then refill.
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int64_t nsteps = (nrows + KS - 1) / KS;
+  issue(st0, 0);
+  int64_t st = 0;
+  while (st < nsteps) {
+    wait_vm<0>();
+    barrier();
+    issue(st1, st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(st0);
+    if (++st >= nsteps) break;
+    wait_vm<0>();
+    barrier();
+    issue(st0, st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(st1);
+    ++st;
+  }
+  // Requests past the last step (zeros) are still in flight: done before the wave ends.
+  wait_vm<0>();
   const int c = lane & 15;
 #pragma unroll
   for (int x = 0; x < 4; ++x)
@@ -817,6 +1003,21 @@ __global__ __launch_bounds__(kThreads) void write_u_mfma(FormArgs P, int64_t p0)
 
 int64_t form_workspace_floats(int F, int k) { return ws_layout(F, k).stride; }
 
+namespace {
+// 128 x 128 Gram tiles of problems [p0, p0 + count): rows staged by direct LDS loads
+// when a chunk's rows stay below 2^31 - 64 bytes (whatever the offsets hold, a chunk
+// lies inside [0, total_tokens)), else through registers.
+void launch_gram128(const FormArgs& P, int64_t p0, int count, float* G, int64_t gstride,
+                    hipStream_t s) {
+  const int n2 = P.F / 128;
+  const dim3 grid(n2 * (n2 + 1) / 2, count), blk(kThreads);
+  if (P.total_tokens * P.F * 2 <= kMaxBufferBytes)
+    hipLaunchKernelGGL(gram_tr, grid, blk, 0, s, P, p0, G, gstride);
+  else
+    hipLaunchKernelGGL(gram_tiles128, grid, blk, 0, s, P, p0, G, gstride);
+}
+}  // namespace
+
 // One channel's problems [p0, p0 + count) (problem = layer * num_chunks + chunk), with
 // the workspace holding `count` problems.
 hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream_t s) {
@@ -825,9 +1026,7 @@ hipError_t launch_form_batch(const FormArgs& P, int64_t p0, int count, hipStream
   const int nt = F / 64;
   const dim3 blk(kThreads);
   if (F % 128 == 0) {
-    const int n2 = F / 128;
-    hipLaunchKernelGGL(gram_tiles128, dim3(n2 * (n2 + 1) / 2, count), blk, 0, s, P, p0,
-                       P.ws + W.G, W.stride);
+    launch_gram128(P, p0, count, P.ws + W.G, W.stride, s);
   } else {
     hipLaunchKernelGGL(gram_tiles, dim3(nt * (nt + 1) / 2, count), blk, 0, s, P, p0,
                        P.ws + W.G, W.stride);
@@ -991,9 +1190,7 @@ hipError_t launch_form_gram(const FormArgs& P, float* G, hipStream_t s) {
   for (int64_t p0 = 0; p0 < problems; p0 += 65535) {
     const int count = (int)min(problems - p0, (int64_t)65535);
     if (P.F % 128 == 0) {
-      const int n2 = P.F / 128;
-      hipLaunchKernelGGL(gram_tiles128, dim3(n2 * (n2 + 1) / 2, count), dim3(kThreads), 0, s, P,
-                         p0, G + p0 * gs, gs);
+      launch_gram128(P, p0, count, G + p0 * gs, gs, s);
     } else {
       hipLaunchKernelGGL(gram_tiles, dim3(nt * (nt + 1) / 2, count), dim3(kThreads), 0, s, P, p0,
                          G + p0 * gs, gs);

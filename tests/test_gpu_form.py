@@ -179,10 +179,12 @@ def test_form_full_size_qwen():
     print(f"\n[case] form full size qwen ok", flush=True)
 
 
-def test_form_gram_stage():
+@pytest.mark.parametrize("heads,lens", [(2, (100, 0, 37, 300)), (8, (700, 5, 0, 1300))])
+def test_form_gram_stage(heads, lens):
     # G_j = Delta_j^T Delta_j on MFMA: bf16 products are exact in fp32, so every entry is
     # within the fp32 summation bound T_j 2^-24 sum_t |Delta_ti Delta_tj| of the exact sum.
-    w = _w(lens=(100, 0, 37, 300), heads=2)
+    # Chunks of many 64-token steps cycle through every LDS stage; F = 1024 has 36 tiles.
+    w = _w(lens=lens, heads=heads)
     st = synth.structure(w)
     deltas = synth.make_deficit(w, device=DEV)
     L, n = w.layers, st.num_chunks
