@@ -77,9 +77,11 @@ __device__ __forceinline__ float max_xor(float v, int x) {
 // ------------------------------------------------------------------ prepared queries
 
 // One workgroup per (layer, chunk, KV head): V_K rows of the head staged in LDS, then
-// each query head's rotated query and V_K^T q.
+// each query head's rotated query and V_K^T q.  The V_K rows take 256 rank bytes of
+// dynamic LDS, so that small ranks leave room for more workgroups per CU (each one
+// waits on two rounds of loads).
 __global__ __launch_bounds__(kThreads) void attend_prep(AttendArgs a) {
-  __shared__ __align__(16) uint16_t svk[kD * 128];  // V_K[g * 128 + d][k], rank <= 128
+  extern __shared__ __align__(16) uint16_t svk[];  // V_K[g * 128 + d][k], kD * rank
   __shared__ float sqh[kAttendMaxGroup][kD];
   const int tid = threadIdx.x;
   const int H = a.heads, n = a.num_chunks, m = a.rank, gq = a.group, Hq = a.num_q_heads;
@@ -347,6 +349,26 @@ void attend_tiles(AttendArgs a) {
     const int64_t s1 = min(t_hi, a.offsets[j + 1]);
     if (s1 <= t0) break;  // offsets that do not cover the range: nothing more here
     const int ntiles = (int)((s1 - t0 + 15) >> 4);
+
+    // HM: the wave applies V_V of the segment's chunk to its U_V sums itself (then the
+    // merge has no per-chunk work).  Lane (c16, grp) takes, for each 16-feature block fb
+    // and 16-rank block ub, ranks 16 ub + 4 grp .. + 3 of V_V row 16 fb + c16: the A
+    // operand of a 16x16x16 product whose B operand is uacc[ub] as the lane holds it.
+    // With one 32-rank step, ranks 0 .. 15 are requested here, to arrive during the
+    // tiles (ranks 16 .. 31, if m has them, in the epilogue); ranks past m read the
+    // row's start and count zero.
+    const uint16_t* vvseg = (const uint16_t*)a.V[1] + (((int64_t)l * n + j) * H + g) * kD * m;
+    auto vv_load = [&](int fb, int ub) -> u32x2_t {
+      const int k0 = 16 * ub + 4 * grp;
+      const u32x2_t w = *(const u32x2_t*)(vvseg + (16 * fb + c16) * m + (k0 < m ? k0 : 0));
+      return k0 < m ? w : u32x2_t{0u, 0u};
+    };
+    constexpr bool kVVPre = HM && MK == 1;
+    u32x2_t vvr[kVVPre ? 8 : 1];
+    if constexpr (kVVPre) {
+#pragma unroll
+      for (int fb = 0; fb < 8; ++fb) vvr[fb] = vv_load(fb, 0);
+    }
 
     // Page lookups of tile ti: PG 1, the tile's two entries (uniform); PG 2, the entry
     // of the lane's token (-1: past the segment or out of the pool); PG 0, none.
@@ -650,6 +672,33 @@ void attend_tiles(AttendArgs a) {
     // Lane (c16, grp) holds features 16 fb + 4 grp + i of the value sums and 16 ub +
     // 4 grp + i of the U_V sums of query head c16.  HM: the wave writes its head's slot.
     if constexpr (HM) {
+      // value sums times V's scale, plus V_V times the U_V sums (hi and lo bf16 parts of
+      // the fp32 sums, so the products keep fp32 accuracy); ranks past m count zero.
+#pragma unroll
+      for (int fb = 0; fb < 8; ++fb) acc[fb] *= vscale;
+      if constexpr (MK > 0) {
+#pragma unroll
+        for (int ub = 0; ub < MU; ++ub) {
+          if (16 * ub >= m) break;  // uniform
+          const bool kok = 16 * ub + 4 * grp < m;
+          bf16x4_t uh, ul;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = kok ? uacc[ub][i] : 0.f;
+            uh[i] = (__bf16)x;
+            ul[i] = (__bf16)(x - (float)uh[i]);
+          }
+#pragma unroll
+          for (int fb = 0; fb < 8; ++fb) {
+            u32x2_t w;
+            if (kVVPre && ub == 0) w = vvr[kVVPre ? fb : 0];
+            else w = vv_load(fb, ub);
+            const bf16x4_t A = __builtin_bit_cast(bf16x4_t, w);
+            acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, uh, acc[fb], 0, 0, 0);
+            acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ul, acc[fb], 0, 0, 0);
+          }
+        }
+      }
       if (hv) {
         float* sl = wsp + (((int64_t)l * Hq + g * gq + c16) * a.slots + (s + j)) * a.slot_floats;
         if (grp == 0) {
@@ -659,11 +708,7 @@ void attend_tiles(AttendArgs a) {
         }
 #pragma unroll
         for (int fb = 0; fb < 8; ++fb)
-          *(f32x4_t*)(sl + kAttendSlotHead + 16 * fb + 4 * grp) = acc[fb] * vscale;
-#pragma unroll
-        for (int ub = 0; ub < MU; ++ub)
-          if (16 * ub + 4 * grp < m)
-            *(f32x4_t*)(sl + kAttendSlotHead + kD + 16 * ub + 4 * grp) = uacc[ub];
+          *(f32x4_t*)(sl + kAttendSlotHead + 16 * fb + 4 * grp) = acc[fb];
       }
       t0 = s1;
       continue;
@@ -729,6 +774,9 @@ __global__ __launch_bounds__(kD) void attend_merge(AttendArgs a) {
   const int g = hq / a.group;
   const int d = threadIdx.x;
   const int m = a.rank, n = a.num_chunks, ns = a.slots, SF = a.slot_floats;
+  // With one wave per KV head the tile kernel has applied V_V already: the slots' value
+  // sums are complete and their U_V sums unused.
+  const int mv = a.heads_mapping ? 0 : m;
   const int64_t F = (int64_t)a.heads * kD;
   const float* base = a.ws + ((int64_t)l * Hq + hq) * ns * SF;
   float M = -INFINITY;
@@ -781,13 +829,13 @@ __global__ __launch_bounds__(kD) void attend_merge(AttendArgs a) {
         ms[u] = sl[0];
         js[u] = __float_as_int(sl[2]);
         av[u] = sl[kAttendSlotHead + d];
-        if (d < m) uv[u] = sl[kAttendSlotHead + kD + d];
+        if (d < mv) uv[u] = sl[kAttendSlotHead + kD + d];
       }
     }
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
       if (!(ls[u] > 0.f)) continue;  // the same for every thread
-      if (m > 0 && js[u] != jcur) {
+      if (mv > 0 && js[u] != jcur) {
         if (jcur >= 0) flush();
         jcur = js[u];
       }
@@ -797,7 +845,7 @@ __global__ __launch_bounds__(kD) void attend_merge(AttendArgs a) {
       uk = fmaf(f, uv[u], uk);
     }
   }
-  if (m > 0 && jcur >= 0) flush();
+  if (mv > 0 && jcur >= 0) flush();
   const int64_t o = (int64_t)l * Hq + hq;
   a.out[o * kD + d] = den > 0.f ? num / den : 0.f;
   if (a.lse != nullptr && d == 0)
@@ -809,7 +857,7 @@ __global__ __launch_bounds__(kD) void attend_merge(AttendArgs a) {
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.splits > 0) {  // no tokens: only the merge runs, writing 0 and -inf
     const dim3 grid0((unsigned)((int64_t)a.num_layers * a.num_chunks * a.heads));
-    hipLaunchKernelGGL(attend_prep, grid0, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(attend_prep, grid0, dim3(kThreads), (size_t)kD * a.rank * 2, s, a);
     // A 4-wave workgroup per (layer, split, KV head), or (HM) one wave per KV head in a
     // workgroup per (layer, split).
     const bool hm = a.heads_mapping != 0;
