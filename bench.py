@@ -509,15 +509,16 @@ def bench_attend(args, w, dev):
     for c in insts:
         kv, ch, p = ops.descriptors_for(c)
         pc = K.chunks_desc(c.offsets_t, zero, st.total_tokens)
-        (kv2, _, _, d2), _, _, _ = ops.attend_buffers(c, q, scale)
+        # out2 and lse2 stay referenced: the descriptor d2 holds their raw pointers
+        (kv2, _, _, d2), out2, lse2, _ = ops.attend_buffers(c, q, scale)
         # sized for this call: with no patch the planner may pick another mapping
         st2, nb2 = K.kamera_attend_workspace(kv2, pc, None, d2)
         K.check(st2)
         ws2 = torch.empty(max(nb2, 16), dtype=torch.uint8, device=dev) if nb2 else None
-        plain.append((kv, ch, p, kv2, pc, d2, ws2))
+        plain.append((kv, ch, p, kv2, pc, d2, ws2, out2, lse2))
 
     def unfused(i):
-        kv, ch, p, kv2, pc, d2, ws2 = plain[i]
+        kv, ch, p, kv2, pc, d2, ws2 = plain[i][:7]
         K.check(lib.kamera_relocate_patch(C.byref(kv), C.byref(ch), C.byref(p), s_ptr))
         K.check(lib.kamera_attend(C.byref(kv2), C.byref(pc), None, C.byref(d2),
                                   None if ws2 is None else ws2.data_ptr(),

@@ -798,15 +798,27 @@ kamera_status validate_attend(const kamera_kv_desc* kv, const kamera_chunks* ch,
   // tokens each (a workgroup's setup and merge cost about as much as 16 tiles; measured:
   // fewer, longer splits on the Qwen-shaped call, 0.098 -> 0.076 ms, and no change on
   // the large calls).
-  // With one wave per KV head a workgroup holds all heads of a split: 16384 waves, at
-  // least 1024 tokens each.  Measured faster with 8 KV heads at ranks up to 32 (the
-  // Llama-shaped call, 2.33 -> 2.25 ms) and slower on the 72B- and Qwen-shaped calls;
-  // KAMERA_ATTEND_HM=0/1 overrides (up to 8 heads).
-  const bool hm_default = K.heads == kamera::kAttendMaxHeadsPerGroup && m <= 32;
+  // With one wave per KV head a workgroup holds all heads of a split, and one such
+  // workgroup fills a CU (8 waves of about 230 registers, two per SIMD), so
+  // kAttendCus * (8 / heads) of them run at once.  The splits are as many as one round
+  // of those holds: every workgroup then starts at once and walks a long range.
+  // Measured with 8 KV heads: Llama-shaped call (32 layers) 2.15 ms at 64 splits, 2.12
+  // at 24, 2.07 at 16, 2.05 at 8 (one round); 72B-shaped call (80 layers) 2.46 ms at 26
+  // splits, 2.47 at 48, 2.20 at 16, 2.18 at 6, 2.17 at 3 (one round, 240 workgroups),
+  // against 2.33 ms with 4-wave workgroups, so the mapping is the default with 8 KV
+  // heads at ranks up to 64.  KAMERA_ATTEND_HM=0/1 overrides (up to 8 heads).
+  const bool hm_default = K.heads == kamera::kAttendMaxHeadsPerGroup && m <= 64;
   plan->heads_mapping = K.heads <= kamera::kAttendMaxHeadsPerGroup &&
                         env_int("KAMERA_ATTEND_HM", hm_default ? 1 : 0) != 0;
   const int64_t units = L * K.heads;
-  int64_t S = std::max<int64_t>(1, ceil_div(plan->heads_mapping ? 16384 : 4096, units));
+  int64_t S;
+  if (plan->heads_mapping) {
+    const int64_t at_once = (int64_t)kamera::kAttendCus *
+                            std::max<int64_t>(1, kamera::kAttendMaxHeadsPerGroup / K.heads);
+    S = std::max<int64_t>(1, at_once / L);
+  } else {
+    S = std::max<int64_t>(1, ceil_div(4096, units));
+  }
   S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(T, 1024)));
   const int env_splits = env_int("KAMERA_ATTEND_SPLITS", 0);
   if (env_splits > 0) S = env_splits;

@@ -123,7 +123,10 @@ struct AttendArgs {
 
 constexpr int kAttendDim = 128;
 constexpr int kAttendMaxGroup = 8;
-constexpr int kAttendMaxHeadsPerGroup = 8;  // KV heads of the one-wave-per-head mapping
+constexpr int kAttendMaxHeadsPerGroup = 8;
+// Compute units of the part (MI355X): the attention planner sizes one round of
+// one-wave-per-KV-head workgroups by it.
+constexpr int kAttendCus = 256;  // KV heads of the one-wave-per-head mapping
 // Floats of one partial slot at rank m: max, sum, chunk, one unused float (the sums
 // start 16-byte aligned), 128 value sums, m U_V sums; padded to a multiple of 4.
 constexpr int kAttendSlotHead = 4;

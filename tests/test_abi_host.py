@@ -637,6 +637,21 @@ def attend_status(kv, ch, p, d):
     return st, None
 
 
+@pytest.mark.parametrize("L,T,m,splits", [(80, 32768, 64, 3), (32, 73728, 16, 8), (2, 4096, 32, 4),
+                                           (300, 8192, 8, 1)])
+def test_attend_one_wave_per_head_splits(L, T, m, splits):
+    # 8 KV heads at ranks up to 64 take one workgroup per (layer, split) with a wave per
+    # head, one workgroup per CU: as many splits as one round of 256 workgroups holds
+    # (floor(256 / L), at least 1), at most one per 1024 tokens.  The slots per query
+    # head are the splits (one chunk): workspace = prepared queries + slots.
+    kv, ch, p, d = attend(Hq=64, L=L, T=T, H=8, m=m)
+    st, nbytes = K.kamera_attend_workspace(kv, ch, p, d)
+    assert st == K.KAMERA_OK, K.kamera_last_error()
+    qw = -(-(L * 1 * 64 * (128 + m) * 4) // 256) * 256
+    slot_floats = (4 + 128 + m + 3) & ~3
+    assert nbytes == qw + L * 64 * splits * slot_floats * 4
+
+
 def test_attend_workspace_and_checks():
     kv, ch, p, d = attend()
     st, nbytes = K.kamera_attend_workspace(kv, ch, p, d)
