@@ -806,20 +806,27 @@ kamera_status validate_attend(const kamera_kv_desc* kv, const kamera_chunks* ch,
   // at 24, 2.07 at 16, 2.05 at 8 (one round); 72B-shaped call (80 layers) 2.46 ms at 26
   // splits, 2.47 at 48, 2.20 at 16, 2.18 at 6, 2.17 at 3 (one round, 240 workgroups),
   // against 2.33 ms with 4-wave workgroups, so the mapping is the default with 8 KV
-  // heads at ranks up to 64.  KAMERA_ATTEND_HM=0/1 overrides (up to 8 heads).
-  const bool hm_default = K.heads == kamera::kAttendMaxHeadsPerGroup && m <= 64;
+  // heads at ranks up to 64.  With 4 KV heads a workgroup is 4 waves and two fit a CU:
+  // the Qwen-shaped call (28 layers, 4096 tokens) took 0.076 ms with 4-wave workgroups
+  // per head (4 splits of 1024 tokens), 0.069 with this mapping at 18 splits and 0.064
+  // at 9 (one workgroup per CU); with fp8 0.065, 0.061 at 18 and 0.072 at 9.  So bf16
+  // counts one workgroup per CU and fp8 as many as fit; splits go down to 128 tokens.
+  // KAMERA_ATTEND_HM=0/1 overrides (up to 8 heads).
+  const bool hm_default = K.heads >= 4 && K.heads <= kamera::kAttendMaxHeadsPerGroup && m <= 64;
   plan->heads_mapping = K.heads <= kamera::kAttendMaxHeadsPerGroup &&
                         env_int("KAMERA_ATTEND_HM", hm_default ? 1 : 0) != 0;
   const int64_t units = L * K.heads;
   int64_t S;
   if (plan->heads_mapping) {
-    const int64_t at_once = (int64_t)kamera::kAttendCus *
-                            std::max<int64_t>(1, kamera::kAttendMaxHeadsPerGroup / K.heads);
-    S = std::max<int64_t>(1, at_once / L);
+    const int64_t per_cu = kv->dtype == KAMERA_FP8_E4M3
+                               ? std::max<int64_t>(1, kamera::kAttendMaxHeadsPerGroup / K.heads)
+                               : 1;
+    S = std::max<int64_t>(1, (int64_t)kamera::kAttendCus * per_cu / L);
+    S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(T, 128)));
   } else {
     S = std::max<int64_t>(1, ceil_div(4096, units));
+    S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(T, 1024)));
   }
-  S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(T, 1024)));
   const int env_splits = env_int("KAMERA_ATTEND_SPLITS", 0);
   if (env_splits > 0) S = env_splits;
   if (T > 0) {

@@ -637,19 +637,22 @@ def attend_status(kv, ch, p, d):
     return st, None
 
 
-@pytest.mark.parametrize("L,T,m,splits", [(80, 32768, 64, 3), (32, 73728, 16, 8), (2, 4096, 32, 4),
-                                           (300, 8192, 8, 1)])
-def test_attend_one_wave_per_head_splits(L, T, m, splits):
-    # 8 KV heads at ranks up to 64 take one workgroup per (layer, split) with a wave per
-    # head, one workgroup per CU: as many splits as one round of 256 workgroups holds
-    # (floor(256 / L), at least 1), at most one per 1024 tokens.  The slots per query
-    # head are the splits (one chunk): workspace = prepared queries + slots.
-    kv, ch, p, d = attend(Hq=64, L=L, T=T, H=8, m=m)
+@pytest.mark.parametrize("H,L,T,m,splits", [(8, 80, 32768, 64, 3), (8, 32, 73728, 16, 8),
+                                             (8, 2, 4096, 32, 32), (8, 300, 8192, 8, 1),
+                                             (4, 28, 4096, 32, 9), (4, 2, 1000, 32, 8)])
+def test_attend_one_wave_per_head_splits(H, L, T, m, splits):
+    # 4 to 8 KV heads at ranks up to 64 take one workgroup per (layer, split) with a
+    # wave per head, bf16 one workgroup per CU: as many splits as one round of 256
+    # workgroups holds (floor(256 / L), at least 1), at most one per 128 tokens.  The
+    # slots per query head are the splits (one chunk): workspace = prepared queries +
+    # slots.
+    kv, ch, p, d = attend(Hq=8 * H, L=L, T=T, H=H, m=m)
     st, nbytes = K.kamera_attend_workspace(kv, ch, p, d)
     assert st == K.KAMERA_OK, K.kamera_last_error()
-    qw = -(-(L * 1 * 64 * (128 + m) * 4) // 256) * 256
+    Hq = 8 * H
+    qw = -(-(L * 1 * Hq * (128 + m) * 4) // 256) * 256
     slot_floats = (4 + 128 + m + 3) & ~3
-    assert nbytes == qw + L * 64 * splits * slot_floats * 4
+    assert nbytes == qw + L * Hq * splits * slot_floats * 4
 
 
 def test_attend_workspace_and_checks():
@@ -657,10 +660,14 @@ def test_attend_workspace_and_checks():
     st, nbytes = K.kamera_attend_workspace(kv, ch, p, d)
     assert st == K.KAMERA_OK and nbytes > 0
     # prepared queries [L][chunks][Hq][128 + m], then partial slots [L][Hq][slots][164]
-    # (max, sum, chunk, one unused float, 128 + m sums); one 4-wave workgroup per (layer,
-    # KV head, split): 4096 workgroups would take 37 splits, capped at 4 splits of 1024
-    # tokens
-    assert nbytes == 28 * 1 * 28 * (128 + 32) * 4 + 28 * 28 * 4 * 164 * 4
+    # (max, sum, chunk, one unused float, 128 + m sums); 4 KV heads: a workgroup per
+    # (layer, split) with a wave per head, floor(256 / 28) = 9 splits
+    assert nbytes == 28 * 1 * 28 * (128 + 32) * 4 + 28 * 28 * 9 * 164 * 4
+    # 2 KV heads: one 4-wave workgroup per (layer, KV head, split): 4096 workgroups would
+    # take 74 splits, capped at 4 splits of 1024 tokens
+    kv2, ch2, p2, d2 = attend(Hq=14, H=2)
+    st, nb2 = K.kamera_attend_workspace(kv2, ch2, p2, d2)
+    assert st == K.KAMERA_OK and nb2 == 28 * 1 * 14 * (128 + 32) * 4 + 28 * 14 * 4 * 164 * 4
     st, st2 = attend_status(kv, ch, p, d)
     assert st2 == K.KAMERA_E_NULL  # no workspace given
     for mutate, status in [
