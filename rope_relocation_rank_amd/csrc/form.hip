@@ -958,12 +958,19 @@ __global__ __launch_bounds__(kThreads) void write_u_mfma(FormArgs P, int64_t p0)
     const int64_t trow = t0 + 16 * wave + c16;  // this lane's A row
     const bool row_ok = trow < b;
     const uint16_t* drow = D + (row_ok ? trow : a) * F + 8 * g;
+    // The next 64-feature block's rows are requested before this block's fragment copy
+    // and products, so their latency overlaps them (rows past the chunk read row a).
+    u32x4_t avn[kUSteps];
+#pragma unroll
+    for (int st = 0; st < kUSteps; ++st)
+      avn[st] = __builtin_nontemporal_load((const u32x4_t*)(drow + 32 * st));
     for (int f0 = 0; f0 < F; f0 += 32 * kUSteps) {  // F is a multiple of 64
       u32x4_t av[kUSteps];
 #pragma unroll
       for (int st = 0; st < kUSteps; ++st) {
-        av[st] = u32x4_t{0u, 0u, 0u, 0u};
-        if (row_ok) av[st] = __builtin_nontemporal_load((const u32x4_t*)(drow + f0 + 32 * st));
+        av[st] = row_ok ? avn[st] : u32x4_t{0u, 0u, 0u, 0u};
+        const int fn = f0 + 32 * kUSteps < F ? f0 + 32 * kUSteps : f0;
+        avn[st] = __builtin_nontemporal_load((const u32x4_t*)(drow + fn + 32 * st));
       }
       const u32x4_t* src = frag + (int64_t)(f0 / 64) * nfrag;
       for (int idx = tid; idx < nfrag; idx += kThreads) {
