@@ -139,12 +139,16 @@ void plan_mfma(const kamera_kv_desc& kv, const kamera_chunks& ch, int m, const b
                bool out_of_place, Plan* plan) {
   plan->launches++;
   // Each of the 4 wavefronts of a workgroup streams `tpw` 16-token tiles.  The
-  // workgroup stages 8 KB of feature factor per 32 ranks once per chunk, so larger
-  // ranks take more tiles per wave (measured best: 2 tiles at rank <= 32, 4 at 64).
-  // fp8 rows carry half the bytes, so fp8 takes twice the tiles (measured best).
+  // workgroup stages 8 KB of feature factor per 32 ranks once per chunk (and, paged, its
+  // block-table entries), so larger ranks take more tiles per wave: 2 tiles at rank
+  // <= 32, 4 at 64 with a paged cache, 2 at 64 with a contiguous one (the MLA-shaped
+  // call: 0.212 ms with 4, 0.203 with 2; paged recall 4.11 ms with 4, 4.41 with 2; the
+  // 72B paged call in logical order 4.22 with 4, 4.29 with 2).  fp8 rows carry half
+  // the bytes, so fp8 takes twice the tiles (measured best).
   const int mk = std::max(1, (m + 31) / 32);
   const int per_mk = 2 * (mk == 3 ? 4 : mk);
-  const int dflt = std::min(8, kv.dtype == KAMERA_FP8_E4M3 ? 2 * per_mk : per_mk);
+  const bool fp8 = kv.dtype == KAMERA_FP8_E4M3;
+  const int dflt = std::min(8, fp8 ? 2 * per_mk : (mk == 2 && kv.page_size == 0 ? 2 : per_mk));
   int tpw = env_int("KAMERA_TILES_PER_WAVE", dflt);
   if (tpw < 1 || tpw > kamera::kMaxBlockTokens / 64) tpw = dflt;
   plan->tiles_per_wave = tpw;
