@@ -63,6 +63,18 @@ def test_groups_and_ranks(hq, rank):
     _case(w, rank, label=f"hq={hq} m={rank}", q_heads=hq)
 
 
+@pytest.mark.parametrize("heads,rank,pages", [(4, 32, 0), (5, 16, 0), (6, 64, 60), (7, 8, 0),
+                                               (8, 48, 60)])
+def test_kv_head_counts(heads, rank, pages):
+    # 4 to 8 KV heads at ranks up to 64 take one wave per KV head by default, any count
+    # of them per workgroup; groups of 2 query heads, contiguous and paged caches, three
+    # chunks so that splits cut at chunk boundaries too.
+    w = synth.Workload(key="att", wid=82, family="gqa", layers=2, heads=heads, head_dim=128,
+                       theta=1e4, rank=max(rank, 8), lens=(300, 5, 395), deltas=(11, -3, 700),
+                       q_heads=2 * heads, page_size=16 if pages else 0, pool_pages=pages)
+    _case(w, rank, label=f"kv heads={heads} m={rank} pages={pages}")
+
+
 @pytest.mark.parametrize("rank", [0, 16])
 def test_chunk_edges(rank):
     w = synth.Workload(key="att", wid=81, family="gqa", layers=2, heads=2, head_dim=128,
