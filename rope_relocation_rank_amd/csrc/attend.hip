@@ -44,6 +44,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;      // prep and tile kernels
@@ -268,6 +269,10 @@ void attend_tiles(AttendArgs a) {
   constexpr uint32_t ES = Q ? 1 : 2;  // bytes per KV element
   constexpr int kVT = Q ? kVTileQ : kVTile;
   constexpr int MU = 2 * MK;  // 16-wide rank blocks of the U_V sums
+  // fp8 V codes through transposing LDS reads: measured faster with one 32-rank step
+  // (Qwen-shaped fp8 call 0.0615 -> 0.0587 ms) and slower with two (72B-shaped fp8 call
+  // 1.630 -> 1.671 ms, double-buffered tiles).
+  constexpr bool kTr8 = Q && MK <= 1;
   constexpr int MUX = MU > 0 ? MU : 1;
   constexpr int kUTile = 1024 * MKX;
   constexpr int kMergeBytes = HM ? 0 : kWaves * kAttendMaxGroup * (2 + kD + 32 * MK) * 4;
@@ -443,10 +448,14 @@ void attend_tiles(AttendArgs a) {
     auto issue_v = [&](int ti, const RowAt& r, auto buf) {
       constexpr bool one = decltype(buf)::value == 1;
       if constexpr (Q) {
+        // tokens 8 b + lane / 8; with transposing reads (kTr8) row i of a block holds the
+        // row's 16-byte chunk q at place q ^ ((i >> 1) & 3), so that the reads of the
+        // eight rows of a block fall in different banks.
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {  // tokens 8 b + lane / 8, bytes 16 (lane % 8)
+        for (int b = 0; b < 2; ++b) {
           const uint32_t vr = (uint32_t)__shfl((int)r.v, 8 * b + (lane >> 3));
-          bload_lds(rv, vr == kOob ? kOob : vr + 16u * (lane & 7),
+          const uint32_t q16 = kTr8 ? (uint32_t)((lane & 7) ^ ((lane >> 4) & 3)) : (uint32_t)(lane & 7);
+          bload_lds(rv, vr == kOob ? kOob : vr + 16u * q16,
                     one ? lds1 + (vwave + b * kVBlkQ) : lds0 + (vwave + b * kVBlkQ));
         }
       } else {
@@ -584,17 +593,30 @@ void attend_tiles(AttendArgs a) {
       wait_vm<kReqPg + kReqK + (DB ? kReqV : 0)>();
       __builtin_amdgcn_sched_barrier(0);
       // bf16: token 4 grp + i is row i of block grp; fp8: row 4 (grp % 2) + i of block
-      // grp / 2.
-      const int vo = Q ? vwave + (grp >> 1) * kVBlkQ + (grp & 1) * 4 * kD + c16
+      // grp / 2.  kTr8 reads fp8 codes with the gfx950 transposing 8-bit LDS read: within
+      // a 16-lane group, lane i receives as its byte e byte i & 7 of the 8 bytes lane
+      // 2 e + (i >> 3) addressed.  Lane s addresses row 4 (grp % 2) + ((s >> 1) & 3)
+      // (rows 4 .. 7 of the read repeat rows 0 .. 3) at features 16 fb + 8 (s & 1), so
+      // lane c16 receives feature 16 fb + c16 of the group's four tokens in its low 4
+      // bytes.  Otherwise one byte read per token.
+      const int vrow = kTr8 ? 4 * (grp & 1) + ((c16 >> 1) & 3) : 4 * (grp & 1);
+      const int vo = Q ? vwave + (grp >> 1) * kVBlkQ + vrow * kD + (kTr8 ? 8 * (c16 & 1) : c16)
                        : vwave + grp * kVBlk + 2 * c16;
+      const int vsw = (vrow >> 1) & 3;
 #pragma unroll
       for (int fb = 0; fb < 8; ++fb) {
         bf16x4_t A;
+        if constexpr (kTr8) {
+          const uint32_t w = (uint32_t)__builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) v2i32_t*)(vs + vo + 16 * (fb ^ vsw)))[0];
+          A = __builtin_bit_cast(bf16x4_t, u32x2_t{fp8x2_to_bf16x2(w, false), fp8x2_to_bf16x2(w, true)});
+        } else if constexpr (Q) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (Q)
+          for (int i = 0; i < 4; ++i)
             A[i] = __builtin_bit_cast(__bf16, fp8_to_bf16(vs[vo + i * kD + 16 * fb]));
-          else
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
             A[i] = __builtin_bit_cast(__bf16, *(const uint16_t*)(vs + (vo + 2 * (i * kD + 16 * fb))));
         }
         acc[fb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, ph, acc[fb], 0, 0, 0);
