@@ -45,6 +45,7 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef int v2i32_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;      // prep and tile kernels
@@ -211,12 +212,11 @@ __device__ __forceinline__ uint16_t fp8_to_bf16(uint32_t code) {
 }
 
 // One wave's LDS tile: the V rows of its 16 tokens as four blocks of four 256-byte rows
-// (token 4 b + i in block b, row i), the blocks 64 bytes apart so that the transposed
-// reads of the four lane groups fall in different banks; and, in an array of its own,
-// the U_V rows of the 16 tokens as they lie in memory (16 x 2m bytes, m <= 32 MK).
-// Separate arrays let the compiler wait for exactly the request a read depends on.
-constexpr int kVBlk = 4 * 2 * kD + 64;
-constexpr int kVTile = 4 * kVBlk;
+// (token 4 b + i in block b, row i), the blocks padded so that the reads of the four
+// lane groups fall in different banks (the kernel's kVB: 64 bytes for per-element reads,
+// 128 with transposing reads); and, in an array of its own, the U_V rows of the 16
+// tokens as they lie in memory (16 x 2m bytes, m <= 32 MK).  Separate arrays let the
+// compiler wait for exactly the request a read depends on.
 // fp8 (rows of 128 bytes): two blocks of eight rows (token 8 b + i in block b, row i).
 constexpr int kVBlkQ = 8 * kD + 64;
 constexpr int kVTileQ = 2 * kVBlkQ;
@@ -267,12 +267,16 @@ void attend_tiles(AttendArgs a) {
   constexpr int NW = HM ? kAttendMaxHeadsPerGroup : kWaves;  // waves per workgroup (at most)
   constexpr int TSTEP = HM ? 1 : kWaves;                      // a wave's tile stride
   constexpr uint32_t ES = Q ? 1 : 2;  // bytes per KV element
-  constexpr int kVT = Q ? kVTileQ : kVTile;
+  constexpr int kVT = Q ? kVTileQ : 4 * (4 * 2 * kD + (MK <= 1 ? 128 : 64));
   constexpr int MU = 2 * MK;  // 16-wide rank blocks of the U_V sums
   // fp8 V codes through transposing LDS reads: measured faster with one 32-rank step
   // (Qwen-shaped fp8 call 0.0615 -> 0.0587 ms) and slower with two (72B-shaped fp8 call
   // 1.630 -> 1.671 ms, double-buffered tiles).
   constexpr bool kTr8 = Q && MK <= 1;
+  // bf16 with one 32-rank step: V through the transposing 16-bit LDS read, rows' 32-byte
+  // slots XOR-placed by row and blocks 128 bytes apart (64 for the per-element reads).
+  constexpr bool kTr16 = !Q && MK <= 1;
+  constexpr int kVB = 4 * 2 * kD + (kTr16 ? 128 : 64);
   constexpr int MUX = MU > 0 ? MU : 1;
   constexpr int kUTile = 1024 * MKX;
   constexpr int kMergeBytes = HM ? 0 : kWaves * kAttendMaxGroup * (2 + kD + 32 * MK) * 4;
@@ -462,8 +466,10 @@ void attend_tiles(AttendArgs a) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const uint32_t vr = (uint32_t)__shfl((int)r.v, 4 * b + grp);
-          bload_lds(rv, vr == kOob ? kOob : vr + 16u * c16,
-                    one ? lds1 + (vwave + b * kVBlk) : lds0 + (vwave + b * kVBlk));
+          // kTr16: row grp of the block holds the row's 16-byte chunk q at q ^ 2 grp
+          const uint32_t q16 = kTr16 ? (uint32_t)(c16 ^ (2 * grp)) : (uint32_t)c16;
+          bload_lds(rv, vr == kOob ? kOob : vr + 16u * q16,
+                    one ? lds1 + (vwave + b * kVB) : lds0 + (vwave + b * kVB));
         }
       }
       const int64_t tb = t0 + 16 * (int64_t)ti;
@@ -600,8 +606,13 @@ void attend_tiles(AttendArgs a) {
       // lane c16 receives feature 16 fb + c16 of the group's four tokens in its low 4
       // bytes.  Otherwise one byte read per token.
       const int vrow = kTr8 ? 4 * (grp & 1) + ((c16 >> 1) & 3) : 4 * (grp & 1);
+      // kTr16: the 16-bit transposing read gives lane i, as its element e, element i & 3
+      // of the 8 bytes lane 4 e + (i >> 2) of its group addressed; lane s addresses row
+      // s >> 2 of block grp at features 16 fb + 4 (s & 3), so lane c16 receives feature
+      // 16 fb + c16 of the block's four tokens.
       const int vo = Q ? vwave + (grp >> 1) * kVBlkQ + vrow * kD + (kTr8 ? 8 * (c16 & 1) : c16)
-                       : vwave + grp * kVBlk + 2 * c16;
+                       : kTr16 ? vwave + grp * kVB + (c16 >> 2) * 2 * kD + 8 * (c16 & 3)
+                               : vwave + grp * kVB + 2 * c16;
       const int vsw = (vrow >> 1) & 3;
 #pragma unroll
       for (int fb = 0; fb < 8; ++fb) {
@@ -614,6 +625,9 @@ void attend_tiles(AttendArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             A[i] = __builtin_bit_cast(__bf16, fp8_to_bf16(vs[vo + i * kD + 16 * fb]));
+        } else if constexpr (kTr16) {
+          A = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) i16x4_t*)(vs + vo + 32 * (fb ^ (c16 >> 2)))));
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
